@@ -1,0 +1,306 @@
+"""Oracle: balanced optimal assignment (the LP of "MoE环游记：6") and its duals.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+Follows [MoE tour 6]:
+* "선형계획" eq. (3)/(4): maximise Σ_ij x_ij s_ij subject to Σ_j x_ij = k and
+  Σ_i x_ij = mk/n (= q), with x in {0,1} (eq. 3) or [0,1] (eq. 4).
+* "극대-극소" eq. (5)-(7): the Lagrangian swap; x*_ij = 1 where
+  s_ij − α_i − β_j > 0, so the relaxation has the integer optimum.
+* "분할정복" eq. (8)-(11): the reduced dual
+  g(α, β) = Σ_ij max(0, s_ij − α_i − β_j) + k Σ α_i + q Σ β_j; for fixed β the
+  best α_i is any value between the k-th and (k+1)-th largest of s_i − β,
+  conventionally the (k+1)-th.
+* "교대 반복" (Quantile Balancing): β = 0; repeat T times
+  α_i ← (k+1)-th largest of s_i − β, β_j ← (q+1)-th largest of s_·j − α;
+  output x_i = top-k of s_i − β.  The page's text of the β step names
+  s_ij − β_j, its algorithm box s − α; the box is followed.
+* "함정에 주의": the online form routes with the old β first, then makes one
+  α update and one β update.
+
+Precision: the Quantile-Balancing duals are exact order statistics of fp32
+differences (fl32(s − β), fl32(s − α)), so ``qb_*`` work in fp32 and are
+bit-reproducible.  ``qb_*`` take the exact order statistic of the algorithm
+box, not the linearly interpolated quantile of the page's demo code.
+
+Exact balance (reading): the alternating iteration stalls short of exact
+column counts on skewed scores, while the pages' target is exactly q per
+expert.  ``ssp_complete`` therefore finishes from the QB result with
+successive shortest paths (min-cost flow) on the expert graph, in float64,
+until every expert holds q tokens; the result is the LP optimum.  It is
+checked against ``lp_highs`` (scipy's HiGHS on eq. (4)), against brute force
+(``brute_force_*``) and against the dual objective eq. (8).
+"""
+from __future__ import annotations
+
+import heapq
+import itertools
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+# ------------------------------------------------------------------ QB (fp32, exact order statistics)
+def _kth_largest_rows(v: np.ndarray, k: int) -> np.ndarray:
+    """0-based k: the (k+1)-th largest of each row (des_sort(v, axis=1)[:, k])."""
+    return -np.sort(-v, axis=1)[:, k]
+
+
+def qb_alpha(s: np.ndarray, beta: np.ndarray, k: int) -> np.ndarray:
+    v = (s.astype(np.float32) - beta.astype(np.float32)[None, :]).astype(np.float32)
+    return _kth_largest_rows(v, k).astype(np.float32)
+
+
+def qb_beta(s: np.ndarray, alpha: np.ndarray, q: int) -> np.ndarray:
+    w = (s.astype(np.float32) - alpha.astype(np.float32)[:, None]).astype(np.float32)
+    return (-np.sort(-w, axis=0)[q, :]).astype(np.float32)
+
+
+def topk_biased(s: np.ndarray, beta: np.ndarray, k: int) -> np.ndarray:
+    """x_i = top-k of fl32(s_i − β), lower expert index first on ties, by descending key."""
+    v = (s.astype(np.float32) - beta.astype(np.float32)[None, :]).astype(np.float32)
+    return np.argsort(-v, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def qb_solve(s: np.ndarray, k: int, iters: int, beta0: Optional[np.ndarray] = None):
+    """Quantile Balancing, solve form.  Returns (idx [m,k], beta [n], alpha [m])."""
+    m, n = s.shape
+    q = m * k // n
+    beta = np.zeros(n, np.float32) if beta0 is None else np.asarray(beta0, np.float32).copy()
+    alpha = np.zeros(m, np.float32)
+    for _ in range(iters):
+        alpha = qb_alpha(s, beta, k)
+        beta = qb_beta(s, alpha, q)
+    return topk_biased(s, beta, k), beta, alpha
+
+
+def qb_online(s: np.ndarray, k: int, beta_old: np.ndarray):
+    """Online form: route with the old β, then one α and one β update."""
+    m, n = s.shape
+    q = m * k // n
+    idx = topk_biased(s, beta_old, k)
+    alpha = qb_alpha(s, beta_old, k)
+    beta = qb_beta(s, alpha, q)
+    return idx, beta, alpha
+
+
+# ------------------------------------------------------------------ assignments
+def idx_to_x(idx: np.ndarray, n: int) -> np.ndarray:
+    m = idx.shape[0]
+    x = np.zeros((m, n), dtype=bool)
+    x[np.arange(m)[:, None], idx] = True
+    return x
+
+
+def x_to_idx(x: np.ndarray, key: Optional[np.ndarray] = None) -> np.ndarray:
+    """Selected experts per row; ordered by descending key (lower index on ties) if given."""
+    m, n = x.shape
+    k = int(x[0].sum())
+    if key is None:
+        key = np.zeros((m, n))
+    k2 = np.where(x, key, -np.inf)
+    return np.argsort(-k2, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def objective(s: np.ndarray, x: np.ndarray) -> float:
+    return float(np.sum(np.where(x, s.astype(np.float64), 0.0)))
+
+
+def dual_objective(s: np.ndarray, alpha: np.ndarray, beta: np.ndarray, k: int) -> float:
+    """eq. (8): Σ max(0, s − α − β) + k Σ α + q Σ β, float64."""
+    m, n = s.shape
+    q = m * k // n
+    s64 = s.astype(np.float64)
+    a = np.asarray(alpha, np.float64)
+    b = np.asarray(beta, np.float64)
+    r = np.maximum(0.0, s64 - a[:, None] - b[None, :])
+    return float(r.sum() + k * a.sum() + q * b.sum())
+
+
+def best_alpha(s: np.ndarray, beta: np.ndarray, k: int) -> np.ndarray:
+    """eq. (11) in float64: α_i = (k+1)-th largest of s_i − β."""
+    v = s.astype(np.float64) - np.asarray(beta, np.float64)[None, :]
+    return _kth_largest_rows(v, k)
+
+
+# ------------------------------------------------------------------ exact completion (SSP)
+@dataclass
+class Completion:
+    x: np.ndarray          # [m, n] bool, column sums exactly q
+    beta: np.ndarray       # [n] float64 potentials (an optimal dual)
+    augmentations: int
+
+
+def _move_costs(s64: np.ndarray, x: np.ndarray):
+    """M[a, j] = min over tokens i with x_ia = 1, x_ij = 0 of s_ia − s_ij, and the token."""
+    m, n = x.shape
+    M = np.full((n, n), np.inf)
+    arg = np.full((n, n), -1, dtype=np.int64)
+    for a in range(n):
+        toks = np.nonzero(x[:, a])[0]
+        if toks.size == 0:
+            continue
+        cost = s64[toks, a][:, None] - s64[toks, :]
+        cost[x[toks]] = np.inf
+        best = np.argmin(cost, axis=0)          # first (lowest token index) on ties
+        M[a] = cost[best, np.arange(n)]
+        arg[a] = np.where(np.isfinite(M[a]), toks[best], -1)
+    return M, arg
+
+
+def ssp_complete(s: np.ndarray, k: int, beta: np.ndarray) -> Completion:
+    """Exact LP optimum by successive shortest paths from x = top-k(s − β).
+
+    Expert graph: an edge a → j moves one token from expert a to expert j at
+    cost s_ia − s_ij (the cheapest such token).  Potentials start at β, for
+    which x = top-k(s − β) gives non-negative reduced costs
+    M(a,j) − π_a + π_j.  Each round runs Dijkstra from every over-full expert,
+    stops at the first under-full expert reached, moves the tokens along that
+    path and lowers the potentials by min(d, d_target).
+    """
+    m, n = s.shape
+    q = m * k // n
+    s64 = s.astype(np.float64)
+    pi = np.asarray(beta, np.float64).copy()
+    key = s64 - pi[None, :]
+    x = idx_to_x(np.argsort(-key, axis=1, kind="stable")[:, :k], n)
+    c = x.sum(axis=0).astype(np.int64)
+    aug = 0
+    while np.any(c > q):
+        M, arg = _move_costs(s64, x)
+        W = np.maximum(M - pi[:, None] + pi[None, :], 0.0)     # reduced costs (clip rounding)
+        dist = np.full(n, np.inf)
+        pred = np.full(n, -1, dtype=np.int64)
+        done = np.zeros(n, dtype=bool)
+        dist[c > q] = 0.0
+        target = -1
+        while True:
+            cand = np.where(done, np.inf, dist)
+            u = int(np.argmin(cand))
+            if not np.isfinite(cand[u]):
+                raise RuntimeError("no augmenting path")
+            done[u] = True
+            if c[u] < q:
+                target = u
+                break
+            nd = dist[u] + W[u]
+            better = (~done) & (nd < dist)
+            dist[better] = nd[better]
+            pred[better] = u
+        D = dist[target]
+        pi -= np.where(done, np.minimum(dist, D), D)
+        # move one token along each edge of the path
+        j = target
+        while pred[j] >= 0:
+            a = int(pred[j])
+            i = int(arg[a, j])
+            x[i, a] = False
+            x[i, j] = True
+            j = a
+        c[j] -= 1
+        c[target] += 1
+        aug += 1
+    return Completion(x, pi, aug)
+
+
+# ------------------------------------------------------------------ LP via HiGHS
+def lp_highs(s: np.ndarray, k: int):
+    """eq. (4) solved by scipy's HiGHS.  Returns the (fractional) x and the objective."""
+    from scipy.optimize import linprog
+    from scipy.sparse import coo_matrix, vstack
+
+    m, n = s.shape
+    q = m * k // n
+    rows = np.repeat(np.arange(m), n)
+    cols = np.arange(m * n)
+    A_row = coo_matrix((np.ones(m * n), (rows, cols)), shape=(m, m * n))
+    rows2 = np.tile(np.arange(n), m)
+    A_col = coo_matrix((np.ones(m * n), (rows2, cols)), shape=(n, m * n))
+    A = vstack([A_row, A_col]).tocsr()
+    b = np.concatenate([np.full(m, k, np.float64), np.full(n, q, np.float64)])
+    res = linprog(-s.astype(np.float64).reshape(-1), A_eq=A, b_eq=b, bounds=(0.0, 1.0),
+                  method="highs")
+    if res.status != 0:
+        raise RuntimeError(res.message)
+    return res.x.reshape(m, n), -res.fun
+
+
+# ------------------------------------------------------------------ brute force (tiny m, n)
+def _choices(n: int, k: int):
+    return [np.array(c, dtype=np.int64) for c in itertools.combinations(range(n), k)]
+
+
+def brute_force_dp(s: np.ndarray, k: int) -> Tuple[int, float]:
+    """Count of feasible {0,1} assignments and their best objective, by a DP over
+    per-expert count vectors (exhaustive; tiny m, n only)."""
+    m, n = s.shape
+    q = m * k // n
+    s64 = s.astype(np.float64)
+    ch = _choices(n, k)
+    states = {tuple([0] * n): (1, 0.0)}
+    for i in range(m):
+        nxt = {}
+        for st, (cnt, best) in states.items():
+            for c in ch:
+                ns = list(st)
+                ok = True
+                for j in c:
+                    ns[j] += 1
+                    if ns[j] > q:
+                        ok = False
+                if not ok:
+                    continue
+                ns = tuple(ns)
+                val = best + float(s64[i, c].sum())
+                if ns in nxt:
+                    c0, b0 = nxt[ns]
+                    nxt[ns] = (c0 + cnt, max(b0, val))
+                else:
+                    nxt[ns] = (cnt, val)
+        states = nxt
+    cnt, best = states[tuple([q] * n)]
+    return cnt, best
+
+
+def brute_force_mitm(s: np.ndarray, k: int) -> Tuple[int, float, np.ndarray]:
+    """Same count and optimum by meet-in-the-middle enumeration over the two halves of
+    the tokens; also returns one optimal x."""
+    m, n = s.shape
+    q = m * k // n
+    s64 = s.astype(np.float64)
+    ch = _choices(n, k)
+    h = m // 2
+
+    def enum(lo, hi):
+        table = {}
+        for combo in itertools.product(range(len(ch)), repeat=hi - lo):
+            cnt = np.zeros(n, dtype=np.int64)
+            val = 0.0
+            for t, ci in enumerate(combo):
+                cnt[ch[ci]] += 1
+                val += float(s64[lo + t, ch[ci]].sum())
+            key = tuple(cnt)
+            if key in table:
+                c0, b0, a0 = table[key]
+                table[key] = (c0 + 1, val, combo) if val > b0 else (c0 + 1, b0, a0)
+            else:
+                table[key] = (1, val, combo)
+        return table
+
+    A = enum(0, h)
+    B = enum(h, m)
+    total = 0
+    best = -np.inf
+    arg = None
+    for key, (ca, ba, aa) in A.items():
+        comp = tuple(q - v for v in key)
+        if comp in B:
+            cb, bb, ab = B[comp]
+            total += ca * cb
+            if ba + bb > best:
+                best, arg = ba + bb, aa + ab
+    x = np.zeros((m, n), dtype=bool)
+    for i, ci in enumerate(arg):
+        x[i, ch[ci]] = True
+    return total, best, x

@@ -1,0 +1,162 @@
+"""Pins of the balanced-assignment oracle (QB duals, exact completion) — CPU only."""
+import numpy as np
+import pytest
+from scipy.optimize import linear_sum_assignment
+
+import workloads as W
+from oracle import balance as B
+from oracle import stats as S
+
+
+def tiny_scores(seed, m=12, n=4):
+    return W.balanced_scores(W.BalancedSpec(m=m, n=n, k=2), seed)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_tiny_lp(seed):
+    """m=12, n=4, k=2: both exhaustive methods count the feasible assignments
+    (12x4 binary matrices with row sums 2 and column sums 6) and find the
+    optimum; the LP (eq. 4), the exact completion and QB+completion agree."""
+    s = tiny_scores(seed)
+    cnt_dp, best_dp = B.brute_force_dp(s, 2)
+    cnt_mm, best_mm, x_mm = B.brute_force_mitm(s, 2)
+    assert cnt_dp == cnt_mm == 32496156
+    assert best_dp == pytest.approx(best_mm, abs=1e-9)
+    xl, obj = B.lp_highs(s, 2)
+    assert obj == pytest.approx(best_dp, abs=1e-7)
+    comp = B.ssp_complete(s, 2, np.zeros(4, np.float32))
+    assert np.array_equal(comp.x, x_mm)
+    assert B.objective(s, comp.x) == pytest.approx(best_dp, abs=1e-9)
+    _, beta, _ = B.qb_solve(s, 2, 3)
+    comp2 = B.ssp_complete(s, 2, beta)
+    assert np.array_equal(comp2.x, x_mm)
+
+
+def test_lp_relaxation_is_integral_and_matches_completion():
+    """"극대-극소": the relaxation's optimum is a 0/1 assignment."""
+    spec = W.BalancedSpec(m=256, n=16, k=2)
+    s = W.balanced_scores(spec, 3)
+    xl, obj = B.lp_highs(s, 2)
+    frac = np.minimum(np.abs(xl), np.abs(1 - xl))
+    assert frac.max() < 1e-7
+    comp = B.ssp_complete(s, 2, np.zeros(16, np.float32))
+    assert np.array_equal(comp.x, xl > 0.5)
+    assert comp.x.sum(axis=0).tolist() == [spec.q] * 16
+    assert comp.x.sum(axis=1).tolist() == [2] * 256
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_k1_reduces_to_linear_sum_assignment(seed):
+    """k = 1, n | m: replicate each expert q times -> an m x m assignment problem."""
+    m, n = 64, 8
+    s = W.balanced_scores(W.BalancedSpec(m=m, n=n, k=1), seed)
+    q = m // n
+    big = np.repeat(s.astype(np.float64), q, axis=1)
+    r, c = linear_sum_assignment(big, maximize=True)
+    lsa_obj = big[r, c].sum()
+    x_lsa = np.zeros((m, n), bool)
+    x_lsa[r, c // q] = True
+    comp = B.ssp_complete(s, 1, np.zeros(n, np.float32))
+    assert B.objective(s, comp.x) == pytest.approx(lsa_obj, abs=1e-9)
+    assert np.array_equal(comp.x, x_lsa)
+
+
+@pytest.mark.parametrize("iters", [0, 1, 5])
+def test_dual_certificate(iters):
+    """eq. (8) at the completion's potentials equals the primal optimum (strong duality)."""
+    spec = W.BalancedSpec(m=512, n=16, k=4)
+    s = W.balanced_scores(spec, 4)
+    _, beta, _ = B.qb_solve(s, spec.k, iters)
+    comp = B.ssp_complete(s, spec.k, beta)
+    primal = B.objective(s, comp.x)
+    a = B.best_alpha(s, comp.beta, spec.k)
+    dual = B.dual_objective(s, a, comp.beta, spec.k)
+    assert dual == pytest.approx(primal, rel=1e-12)
+    # weak duality at arbitrary duals
+    assert B.dual_objective(s, B.best_alpha(s, beta, spec.k), beta, spec.k) >= primal - 1e-9
+    # complementary slackness: chosen entries have s - beta >= alpha
+    r = s.astype(np.float64) - comp.beta[None, :] - a[:, None]
+    assert np.all(r[comp.x] >= -1e-9) and np.all(r[~comp.x] <= 1e-9)
+
+
+def test_alpha_closed_form_by_scanning_eq10():
+    """eq. (10): k·α + Σ_j max(0, v_j − α) is minimal exactly on [v_(k+1), v_(k)]."""
+    g = np.random.default_rng(5)
+    for k in (1, 2, 3):
+        v = g.standard_normal(6)
+        srt = -np.sort(-v)
+        grid = np.linspace(srt[-1] - 1, srt[0] + 1, 20001)
+        f = k * grid + np.maximum(0, v[None, :] - grid[:, None]).sum(axis=1)
+        fmin = f.min()
+        flat = grid[f <= fmin + 1e-12]
+        assert flat.min() >= srt[k] - 1e-3 and flat.max() <= srt[k - 1] + 1e-3
+        fa = k * srt[k] + np.maximum(0, v - srt[k]).sum()     # QB's convention: (k+1)-th
+        assert fa == pytest.approx(fmin, abs=1e-9)
+        a = B.qb_alpha(v[None, :].astype(np.float32), np.zeros(6, np.float32), k)
+        assert a[0] == np.float32(srt[k])
+
+
+def test_qb_order_statistics_are_exact():
+    spec = W.BalancedSpec(m=256, n=16, k=3)
+    s = W.balanced_scores(spec, 6)
+    idx, beta, _ = B.qb_solve(s, spec.k, 2)
+    alpha = B.qb_alpha(s, beta, spec.k)
+    v = (s - beta[None, :]).astype(np.float32)
+    assert np.all((v > alpha[:, None]).sum(axis=1) <= spec.k)
+    assert np.all((v >= alpha[:, None]).sum(axis=1) >= spec.k + 1)
+    assert np.all(np.any(v == alpha[:, None], axis=1))
+    beta2 = B.qb_beta(s, alpha, spec.q)
+    w = (s - alpha[:, None]).astype(np.float32)
+    assert np.all((w > beta2[None, :]).sum(axis=0) <= spec.q)
+    assert np.all((w >= beta2[None, :]).sum(axis=0) >= spec.q + 1)
+    assert np.all(np.any(w == beta2[None, :], axis=0))
+    assert np.array_equal(idx, np.argsort(-v, axis=1, kind="stable")[:, :spec.k])
+
+
+def test_qb_online_routes_with_old_beta():
+    spec = W.BalancedSpec(m=128, n=8, k=2)
+    s = W.balanced_scores(spec, 7)
+    beta_old = np.linspace(-1, 1, 8).astype(np.float32)
+    idx, beta_new, _ = B.qb_online(s, 2, beta_old)
+    assert np.array_equal(idx, B.topk_biased(s, beta_old, 2))
+    assert not np.array_equal(idx, B.topk_biased(s, beta_new, 2))
+    _, b1, _ = B.qb_solve(s, 2, 1, beta0=beta_old)
+    assert np.array_equal(beta_new, b1)
+
+
+def test_qb_fixed_point_is_lp_optimal():
+    """"교대 반복": once QB's x meets both constraint sets it is the LP optimum."""
+    hits = 0
+    for seed in range(40):
+        spec = W.BalancedSpec(m=32, n=4, k=1, offset_std=0.1)
+        s = W.balanced_scores(spec, seed)
+        idx, beta, _ = B.qb_solve(s, 1, 30)
+        x = B.idx_to_x(idx, 4)
+        if np.all(x.sum(axis=0) == spec.q):
+            hits += 1
+            comp = B.ssp_complete(s, 1, np.zeros(4, np.float32))
+            assert np.array_equal(x, comp.x)
+    assert hits >= 2
+
+
+def test_qb_improves_balance_on_demo_workload():
+    """"데모 코드": subtracting the QB bias lowers the max violation."""
+    s = W.uniform_offset_scores(4000, 64, 0)
+    k = 4
+    top = np.argsort(-s, axis=1)[:, :k]
+    before = S.max_min_avg_vio(np.bincount(top.ravel(), minlength=64))
+    idx, beta, _ = B.qb_solve(s, k, 5)
+    after = S.max_min_avg_vio(np.bincount(idx.ravel(), minlength=64))
+    assert after[0] < 0.25 * before[0] and after[2] < 0.25 * before[2]
+
+
+@pytest.mark.slow
+def test_full_size_completion_matches_highs():
+    """The balanced-LP workload at full size (m=4096, n=64, k=4)."""
+    spec = W.BALANCED
+    s = W.balanced_scores(spec, 0)
+    _, beta, _ = B.qb_solve(s, spec.k, 20)
+    comp = B.ssp_complete(s, spec.k, beta)
+    xl, obj = B.lp_highs(s, spec.k)
+    assert np.array_equal(comp.x, xl > 0.5)
+    assert B.objective(s, comp.x) == pytest.approx(obj, rel=1e-12)
