@@ -1,0 +1,284 @@
+/*
+ * moe.h — C ABI of libmoe.so: the Mixture-of-Experts routing, load-balance and
+ * dispatch path on AMD Instinct MI355X (gfx950).
+ *
+ * Page references (title, then section / equation):
+ *   [Switch review] "Switch Transformers 논문 리뷰: 1.6조 파라미터 MoE 모델의 Sparse
+ *                   Routing 기법 완전 분석" (tildalice.io)
+ *   [Switch impl]   "Switch Transformer를 구현 관점에서 읽기: Top-1 라우팅과 Expert 병렬
+ *                   처리" (molayo1419.me)
+ *   [MoE tour 6]    "MoE环游记：6、最优分配促均衡" (kexue.fm/archives/11619)
+ *   [Qwen global]   "Qwen 글로벌-배치 로드 밸런스 MoE LLM 훈련" (agentlenshq.com)
+ *
+ * Conventions shared by every call
+ *   - Arrays are DEVICE pointers (HIP global memory), row-major and contiguous,
+ *     owned by the caller.  The library allocates no device memory: scratch
+ *     space is the caller's workspace `ws` of at least moe_workspace_size()
+ *     bytes, 256-byte aligned.
+ *   - The first 65536 bytes of a workspace are control words that must be
+ *     zero before the workspace is first used (moe_workspace_init(), or any
+ *     zero fill).  Every call leaves them zero again.  Two calls that run at
+ *     the same time (different streams) must not share a workspace.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work; they never synchronise with the host.  Results are ready
+ *     when the stream reaches that point.
+ *   - Every call validates its arguments on the host before any HIP call and
+ *     returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE
+ *     without touching device memory.  MOE_ERR_HIP reports a failed launch
+ *     (hipGetLastError); device faults surface at the caller's next sync.
+ *   - Integer outputs are deterministic and bit-reproducible.  Float
+ *     reductions use fixed-order trees or exact fixed-point integer sums, so
+ *     repeated calls give bit-identical results.
+ *   - NaN / Inf inputs are outside the contract; indices stay in [0, n).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* bad size, null required pointer, inconsistent options */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but beyond this build's limits (e.g. n > 4096) */
+  MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4            /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Router score: softmax p_i = e^{h_i}/Σ_j e^{h_j} ([Switch review] "Switch Routing
+ * 메커니즘" Step 1) or sigmoid ρ_i = σ(h_i) ([MoE tour 6] "방법 회고"). */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* Gate of a chosen expert: its score (Switch: [Switch review] Step 3; Loss-Free:
+ * [MoE tour 6] eq. (1), the bias never enters the gate), or the score divided by
+ * the sum over the token's k choices (top-k softmax gating, [Switch review]
+ * "Shazeer et al. (2017)의 MoE Layer"). */
+typedef enum { MOE_GATE_PROB = 0, MOE_GATE_RENORM = 1 } moe_gate;
+
+/* Balanced-assignment modes ([MoE tour 6] "교대 반복" and "함정에 주의"). */
+typedef enum { MOE_QB_SOLVE = 0, MOE_QB_ONLINE = 1 } moe_qb_mode;
+
+typedef enum { MOE_EXPERT_IDENTITY = 0, MOE_EXPERT_RELU_FFN = 1 } moe_expert_kind;
+
+/* Problem shape, following the pages' problem statement: m tokens (batch x
+ * sequence flattened), d = d_model, n experts, k experts per token. */
+typedef struct {
+  int64_t m;
+  int32_t d;
+  int32_t n;
+  int32_t k;
+  int32_t score;    /* moe_score */
+  int32_t gate;     /* moe_gate */
+  int32_t x_dtype;  /* moe_dtype of the hidden states x */
+} moe_shape;
+
+/* ------------------------------------------------------------------ host helpers */
+
+/* Workspace bytes that every call below needs for this shape (the maximum
+ * over calls), with `capacity` the per-expert capacity used by dispatch
+ * (-1: no limit) and `d_ff` the expert hidden width (0: no FFN).  Returns 0
+ * for an invalid shape. */
+size_t moe_workspace_size(const moe_shape* shape, int32_t capacity, int32_t d_ff);
+
+/* Zero-fills the control words of a fresh workspace (asynchronous on stream). */
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_balance_duals (exact != 0: with the completion);
+ * 0 for invalid sizes. */
+size_t moe_balance_workspace_size(int64_t m, int32_t n, int32_t k, int32_t exact);
+
+/* Workspace bytes for moe_expert_ffn with at most rows_max rows per expert;
+ * 0 for invalid sizes. */
+size_t moe_expert_ffn_workspace_size(int32_t n, int32_t rows_max, int32_t d_ff);
+
+/* Expert capacity floor(m · cf / n) on the exact binary value of cf
+ * ([Switch review] "Expert Capacity와 토큰 드롭": (tokens per batch / number of
+ * experts) x capacity factor).  Returns -1 if m < 0, n < 1, cf < 0 or not
+ * finite, or the result exceeds INT32_MAX. */
+int32_t moe_capacity(int64_t m, int32_t n, double capacity_factor);
+
+const char* moe_status_str(int32_t status);
+
+/* Library version string and the GPU architecture its kernels target. */
+const char* moe_build_info(void);
+
+/* ------------------------------------------------------------------ router */
+
+/* moe_route — router projection, score, top-k selection and load histogram.
+ *   h = x · W_r with x upcast exactly to fp32 and fp32-accurate accumulation
+ *   ([Switch review] "Switch Routing 메커니즘" Step 1, "선택적 정밀도 캐스팅":
+ *   the router runs in fp32 on bf16 hidden states).  For bf16 x the product
+ *   is formed on bf16 matrix cores from an exact three-way bf16 split of W_r.
+ *   Selection key: h (no bias; the same order as p or σ(h)), or score + bias
+ *   (Loss-Free, [MoE tour 6] eq. (1)).  Ties go to the lower expert index; a
+ *   token's k choices are written by descending key.
+ * x        [m, d]   fp32 or bf16 (shape->x_dtype)
+ * w_r      [d, n]   fp32 router weight
+ * bias     [n]      fp32 or NULL (ranks only; never part of the gate)
+ * idx      [m, k]   int32 out: chosen experts
+ * gate     [m, k]   fp32 out: gate values (moe_gate)
+ * counts   [n]      int32 out: c_j = number of (token, choice) pairs on expert j
+ * prob_sum [n]      fp32 out or NULL: Σ_t score_j(t) (softmax p or sigmoid ρ),
+ *                   the numerator of P_j ([Switch review] "로드 밸런싱 손실")
+ * Limits: 1 <= k <= n <= 4096, d >= 1, m >= 1. */
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* bias,
+                     int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ statistics */
+
+/* moe_stats — load statistics of one (micro-)batch, optional global-batch
+ * accumulation and optional Loss-Free bias update.
+ *   f_j = c_j / m; P_j = prob_sum_j / m; aux = α · n · Σ_j f_j P_j
+ *   ([Switch review] "로드 밸런싱 손실"; for k > 1, f_j still counts the pairs
+ *   on expert j per token).  Σ is taken in fp64 in a fixed order.
+ *   global_counts[j] += c_j and global_tokens[0] += m ([Qwen global]
+ *   "글로벌-배치 로드 밸런스 구현": expert frequencies are gathered over the
+ *   global batch).
+ *   bias[j] ← fl32(bias[j] − fl32(γ) · sign(c_j · n − m · k)), i.e. the sign of
+ *   F_j − 1/n with F_j = c_j/(m·k), evaluated exactly in 64-bit integers
+ *   ([MoE tour 6] eq. (2)).  Call this AFTER routing the batch with the old
+ *   bias ([MoE tour 6] "함정에 주의").
+ * counts [n] int32 in; prob_sum [n] fp32 in or NULL (then P and aux are skipped);
+ * f [n] fp32 out or NULL; P [n] fp32 out or NULL; aux [1] fp32 out or NULL;
+ * global_counts [n] int64 in/out or NULL; global_tokens [1] int64 in/out or NULL
+ * (both or neither); bias [n] fp32 in/out or NULL. */
+moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, const float* prob_sum,
+                     float alpha, float* f, float* P, float* aux,
+                     int64_t* global_counts, int64_t* global_tokens,
+                     float* bias, float gamma, void* stream);
+
+/* moe_global_aux — the global-batch balance loss ([Qwen global] "글로벌-배치 로드
+ * 밸런스 구현": synchronise f over the global batch, form each micro-batch's loss
+ * with it, aggregate).  f^g_j = global_counts_j / global_tokens;
+ * losses[t] = α · n · Σ_j f^g_j · P[t, j]; loss_mean = mean_t losses[t].
+ * P [nb, n] fp32 (each row a micro-batch's P); f_global [n], losses [nb],
+ * loss_mean [1] fp32 out (each may be NULL). */
+moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t* global_tokens,
+                          const float* P, int32_t nb, float alpha,
+                          float* f_global, float* losses, float* loss_mean, void* stream);
+
+/* ------------------------------------------------------------------ balanced assignment */
+
+/* moe_balance_duals — balanced optimal assignment ([MoE tour 6] "선형계획" eq. (3)/(4):
+ * every token takes k experts, every expert exactly q = m·k/n tokens).
+ *   QB step ("교대 반복"): α_i ← (k+1)-th largest of fl32(s_i − β);
+ *   β_j ← (q+1)-th largest of fl32(s_·j − α) — exact order statistics of fp32
+ *   differences, bit-reproducible.
+ *   mode SOLVE: start from the given beta, run `iters` QB steps, then
+ *     idx = top-k of fl32(s_i − β) (ties: lower index).
+ *   mode ONLINE ("함정에 주의"): idx = top-k of fl32(s_i − β_old) FIRST, then one
+ *     QB step updates beta (iters must be 1, exact must be 0).
+ *   exact = 1 (SOLVE only): finish with successive shortest paths (min-cost
+ *     flow on the expert graph, fp64) from x = top-k(s − β) until every expert
+ *     holds exactly q tokens; idx is then the LP optimum (eq. (4), which has an
+ *     integral optimum, "극대-극소") and beta the final potentials, an optimal
+ *     dual of eq. (8) rounded to fp32.  Requires n <= 64.
+ * s [m, n] fp32; beta [n] fp32 in/out; idx [m, k] int32 out; counts [n] int32 out;
+ * alpha [m] fp32 out or NULL (the last α computed); info [4] int32 out or NULL:
+ * {QB steps run, augmentations, 1 if every count == q else 0, 0}.
+ * Requires (m·k) % n == 0 and 1 <= k < n. */
+moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, float* beta,
+                             int32_t iters, int32_t mode, int32_t exact,
+                             int32_t* idx, int32_t* counts, float* alpha, int32_t* info,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ capacity + dispatch */
+
+/* moe_dispatch — capacity slots in token order and permute-dispatch.
+ *   slot(t, r) = number of earlier pairs (t', r') < (t, r) in token-major order
+ *   with the same expert; kept ⇔ slot < capacity ([Switch review] "Expert
+ *   Capacity와 토큰 드롭": overflow tokens skip the expert and reach the next
+ *   layer through the residual).  Kept pairs are gathered expert-major and
+ *   contiguous ([Switch impl] "forward pass에서는 토큰 순서를 두 번 변경한다").
+ * capacity: -1 = unlimited, else >= 0.
+ * x [m, d] (x_dtype) or NULL when dispatched is NULL; idx [m, k] int32 in;
+ * token_to_row [m, k] int32 out (-1 = dropped); drop_mask [m, k] uint8 out or NULL;
+ * expert_offsets [n + 1] int32 out: rows of expert j are
+ *   [expert_offsets[j], expert_offsets[j+1]);
+ * row_to_token [m·k] int32 out or NULL (entries >= expert_offsets[n] untouched);
+ * dispatched [m·k, d] (x_dtype) out or NULL: row r = x[row_to_token[r]], bit copy. */
+moe_status moe_dispatch(const moe_shape* shape, int32_t capacity, const void* x, const int32_t* idx,
+                        int32_t* token_to_row, uint8_t* drop_mask, int32_t* expert_offsets,
+                        int32_t* row_to_token, void* dispatched,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ expert FFN */
+
+/* moe_expert_ffn — per-expert ReLU FFN on the dispatched rows ([Switch review]
+ * "Switch Layer의 구조": FFN(x) = max(0, x·W1)·W2, one weight set per expert;
+ * no biases).  bf16 operands, fp32 accumulation, the hidden activation and
+ * the output rounded to bf16 (nearest even).
+ * rows_max: a host-known bound on any expert's row count (e.g. the capacity).
+ * expert_offsets [n + 1] int32 (device, from moe_dispatch);
+ * dispatched [rows, d] bf16; w1 [n, d_ff, d] bf16 (row f feeds hidden unit f);
+ * w2 [n, d, d_ff] bf16 (row c feeds output channel c); y [rows, d] bf16 out.
+ * Limits: d and d_ff multiples of 32. */
+moe_status moe_expert_ffn(int32_t n, int32_t d, int32_t d_ff, int32_t rows_max,
+                          const int32_t* expert_offsets, const void* dispatched,
+                          const void* w1, const void* w2, void* y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ combine */
+
+/* moe_combine — inverse permute, gate scaling and residual:
+ *   out[t] = residual[t] + Σ_{r kept} gate[t, r] · y[token_to_row[t, r]]
+ *   in fp32, r in increasing order, rounded once to the output dtype
+ *   ([Switch review] Step 3; [Switch impl] pipeline list: restore token order,
+ *   multiply by the gate, join the residual path).  A token with no kept pair
+ *   gets out[t] = residual[t] bit-exactly.  residual = NULL gives the expert
+ *   branch alone.
+ * y [rows, d] (y_dtype); gate [m, k] fp32; token_to_row [m, k] int32;
+ * residual [m, d] (x_dtype) or NULL; out [m, d] (x_dtype). */
+moe_status moe_combine(const moe_shape* shape, const void* y, int32_t y_dtype, const float* gate,
+                       const int32_t* token_to_row, const void* residual, void* out, void* stream);
+
+/* ------------------------------------------------------------------ whole layer */
+
+typedef struct {
+  int32_t capacity;      /* per-expert capacity, -1 = unlimited */
+  int32_t expert_kind;   /* moe_expert_kind */
+  int32_t d_ff;          /* FFN hidden width (relu_ffn) */
+  float alpha;           /* aux-loss weight */
+} moe_layer_params;
+
+/* Device output pointers of moe_switch_layer.  `out` is required; every other
+ * field may be NULL (then the workspace holds it). */
+typedef struct {
+  int32_t* idx;            /* [m, k] */
+  float* gate;             /* [m, k] */
+  int32_t* counts;         /* [n] */
+  float* prob_sum;         /* [n] */
+  float* f;                /* [n] */
+  float* P;                /* [n] */
+  float* aux;              /* [1] */
+  int32_t* token_to_row;   /* [m, k] */
+  uint8_t* drop_mask;      /* [m, k] */
+  int32_t* expert_offsets; /* [n + 1] */
+  int32_t* row_to_token;   /* [m·k] */
+  void* dispatched;        /* [m·k, d] x_dtype */
+  void* y;                 /* [m·k, d] bf16 expert outputs (relu_ffn; ignored for
+                              the identity expert, whose output is `dispatched`) */
+  void* out;               /* [m, d] x_dtype */
+} moe_layer_outputs;
+
+/* moe_switch_layer — route → stats → capacity + dispatch → expert → combine on one
+ * stream, the Switch layer of [Switch impl] (pipeline list) and [Switch review]
+ * ("Switch Layer의 구조", "Switch Routing 메커니즘", "Expert Capacity와 토큰
+ * 드롭", "로드 밸런싱 손실").  Results equal those of the individual calls.
+ * relu_ffn needs bf16 x; identity accepts fp32 or bf16. */
+moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* params,
+                            const void* x, const float* w_r, const void* w1, const void* w2,
+                            const float* bias, const moe_layer_outputs* outputs,
+                            void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,73 @@
+"""ctypes view of libmoe.so (declared in include/moe.h).  Loading needs the HIP
+runtime library, not a GPU; every compute call needs the GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+SCORES = {"softmax": 0, "sigmoid": 1}
+GATES = {"prob": 0, "renorm": 1}
+QB_MODES = {"solve": 0, "online": 1}
+EXPERTS = {"identity": 0, "relu_ffn": 1}
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("m", c_int64), ("d", c_int32), ("n", c_int32), ("k", c_int32),
+                ("score", c_int32), ("gate", c_int32), ("x_dtype", c_int32)]
+
+
+class LayerParams(ctypes.Structure):
+    _fields_ = [("capacity", c_int32), ("expert_kind", c_int32), ("d_ff", c_int32), ("alpha", c_float)]
+
+
+class LayerOutputs(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in (
+        "idx", "gate", "counts", "prob_sum", "f", "P", "aux", "token_to_row", "drop_mask",
+        "expert_offsets", "row_to_token", "dispatched", "y", "out")]
+
+
+_P = c_void_p
+SIGNATURES = {
+    "moe_workspace_size": (c_size_t, [POINTER(MoeShape), c_int32, c_int32]),
+    "moe_workspace_init": (c_int32, [_P, c_size_t, _P]),
+    "moe_balance_workspace_size": (c_size_t, [c_int64, c_int32, c_int32, c_int32]),
+    "moe_expert_ffn_workspace_size": (c_size_t, [c_int32, c_int32, c_int32]),
+    "moe_capacity": (c_int32, [c_int64, c_int32, c_double]),
+    "moe_status_str": (c_char_p, [c_int32]),
+    "moe_build_info": (c_char_p, []),
+    "moe_route": (c_int32, [POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_stats": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_float, _P, _P, _P, _P, _P, _P, c_float, _P]),
+    "moe_global_aux": (c_int32, [c_int32, _P, _P, _P, c_int32, c_float, _P, _P, _P, _P]),
+    "moe_balance_duals": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_int32, c_int32, c_int32,
+                                    _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_dispatch": (c_int32, [POINTER(MoeShape), c_int32, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_expert_ffn": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_combine": (c_int32, [POINTER(MoeShape), _P, c_int32, _P, _P, _P, _P, _P]),
+    "moe_switch_layer": (c_int32, [POINTER(MoeShape), POINTER(LayerParams), _P, _P, _P, _P, _P,
+                                   POINTER(LayerOutputs), _P, c_size_t, _P]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libmoe.so and declares every entry point; fails loudly if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m load_balanced_expert_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,297 @@
+"""Thin Python binding over libmoe's C ABI (include/moe.h).
+
+Argument marshalling only: torch tensors provide device memory and the HIP
+stream; every step of the path runs in libmoe's HIP kernels.  Names follow
+the C entry points (moe_route -> route, ...).  Outputs are allocated here
+with torch.empty on the input's device; errors raise MoeError.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def _lib():
+    return L.load()
+
+
+def _check(status: int, what: str):
+    if status != L.MOE_OK:
+        msg = _lib().moe_status_str(status).decode()
+        raise MoeError(f"{what}: {msg} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoeError("libmoe takes device tensors only")
+    if not t.is_contiguous():
+        raise MoeError("libmoe takes contiguous tensors only")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _on_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise MoeError("libmoe takes device tensors only")
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.MOE_BF16
+    if t.dtype == torch.float32:
+        return L.MOE_F32
+    raise MoeError(f"hidden states must be bf16 or fp32, got {t.dtype}")
+
+
+def shape(m, d, n, k, score="softmax", gate="prob", x_dtype=L.MOE_BF16) -> L.MoeShape:
+    return L.MoeShape(int(m), int(d), int(n), int(k), L.SCORES[score], L.GATES[gate], int(x_dtype))
+
+
+# ------------------------------------------------------------------ workspace
+_ws = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-initialised uint8 device buffer of at least nbytes, cached per device.
+    Calls on one stream may share it (the library leaves its control words zero)."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(int(nbytes), 1 << 16) + 256, dtype=torch.uint8, device=dev)
+        _ws[key] = buf
+    return buf
+
+
+def _ws_args(nbytes: int, device):
+    buf = workspace(nbytes, device)
+    base = buf.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    return ctypes.c_void_p(aligned), ctypes.c_size_t(buf.numel() - (aligned - base))
+
+
+def capacity(m: int, n: int, cf: float) -> int:
+    return int(_lib().moe_capacity(int(m), int(n), float(cf)))
+
+
+def workspace_size(sh: L.MoeShape, capacity: int = -1, d_ff: int = 0) -> int:
+    return int(_lib().moe_workspace_size(ctypes.byref(sh), int(capacity), int(d_ff)))
+
+
+# ------------------------------------------------------------------ router
+@dataclass
+class RouteOut:
+    idx: torch.Tensor
+    gate: torch.Tensor
+    counts: torch.Tensor
+    prob_sum: Optional[torch.Tensor]
+
+
+def route(x: torch.Tensor, w_r: torch.Tensor, k: int, score: str = "softmax", gate: str = "prob",
+          bias: Optional[torch.Tensor] = None, prob_sum: bool = True) -> RouteOut:
+    _on_device(x, w_r, bias)
+    m, d = x.shape
+    n = w_r.shape[1]
+    dev = x.device
+    sh = shape(m, d, n, k, score, gate, _dtype_code(x))
+    idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    g = torch.empty((m, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    ps = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum else None
+    ws, wsb = _ws_args(workspace_size(sh), dev)
+    _check(_lib().moe_route(ctypes.byref(sh), _ptr(x), _ptr(w_r), _ptr(bias), _ptr(idx), _ptr(g), _ptr(counts),
+                            _ptr(ps), ws, wsb, _stream(dev)), "moe_route")
+    return RouteOut(idx, g, counts, ps)
+
+
+# ------------------------------------------------------------------ statistics
+@dataclass
+class StatsOut:
+    f: torch.Tensor
+    P: Optional[torch.Tensor]
+    aux: Optional[torch.Tensor]
+
+
+def stats(m: int, k: int, counts: torch.Tensor, prob_sum: Optional[torch.Tensor], alpha: float = 1e-2,
+          global_counts: Optional[torch.Tensor] = None, global_tokens: Optional[torch.Tensor] = None,
+          bias: Optional[torch.Tensor] = None, gamma: float = 1e-3) -> StatsOut:
+    _on_device(counts, prob_sum, global_counts, global_tokens, bias)
+    n = counts.shape[0]
+    dev = counts.device
+    f = torch.empty(n, dtype=torch.float32, device=dev)
+    P = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum is not None else None
+    aux = torch.empty(1, dtype=torch.float32, device=dev) if prob_sum is not None else None
+    _check(_lib().moe_stats(int(m), int(n), int(k), _ptr(counts), _ptr(prob_sum), float(alpha), _ptr(f), _ptr(P),
+                            _ptr(aux), _ptr(global_counts), _ptr(global_tokens), _ptr(bias), float(gamma),
+                            _stream(dev)), "moe_stats")
+    return StatsOut(f, P, aux)
+
+
+def global_aux(global_counts: torch.Tensor, global_tokens: torch.Tensor, P_rows: torch.Tensor, alpha: float = 1e-2):
+    n = global_counts.shape[0]
+    nb = P_rows.shape[0]
+    dev = global_counts.device
+    fg = torch.empty(n, dtype=torch.float32, device=dev)
+    losses = torch.empty(max(nb, 1), dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(_lib().moe_global_aux(int(n), _ptr(global_counts), _ptr(global_tokens), _ptr(P_rows), int(nb),
+                                 float(alpha), _ptr(fg), _ptr(losses), _ptr(mean), _stream(dev)), "moe_global_aux")
+    return fg, losses[:nb], mean
+
+
+# ------------------------------------------------------------------ balanced assignment
+@dataclass
+class BalanceOut:
+    idx: torch.Tensor
+    counts: torch.Tensor
+    alpha: torch.Tensor
+    info: torch.Tensor
+
+
+def balance_duals(s: torch.Tensor, k: int, beta: torch.Tensor, iters: int = 5, mode: str = "solve",
+                  exact: bool = False) -> BalanceOut:
+    """beta is updated in place."""
+    _on_device(s, beta)
+    m, n = s.shape
+    dev = s.device
+    idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    alpha = torch.empty(m, dtype=torch.float32, device=dev)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    need = int(_lib().moe_balance_workspace_size(int(m), int(n), int(k), int(exact)))
+    ws, wsb = _ws_args(need, dev)
+    _check(_lib().moe_balance_duals(int(m), int(n), int(k), _ptr(s), _ptr(beta), int(iters), L.QB_MODES[mode],
+                                    int(exact), _ptr(idx), _ptr(counts), _ptr(alpha), _ptr(info), ws, wsb,
+                                    _stream(dev)), "moe_balance_duals")
+    return BalanceOut(idx, counts, alpha, info)
+
+
+# ------------------------------------------------------------------ dispatch
+@dataclass
+class DispatchOut:
+    token_to_row: torch.Tensor
+    drop_mask: torch.Tensor
+    expert_offsets: torch.Tensor
+    row_to_token: torch.Tensor
+    dispatched: Optional[torch.Tensor]
+
+
+def dispatch(x: Optional[torch.Tensor], idx: torch.Tensor, n: int, capacity: int = -1, d: Optional[int] = None,
+             copy_rows: bool = True) -> DispatchOut:
+    _on_device(x, idx)
+    m, k = idx.shape
+    dev = idx.device
+    if x is not None:
+        d = x.shape[1]
+        xd = _dtype_code(x)
+    else:
+        xd = L.MOE_BF16
+    sh = shape(m, d or 1, n, k, x_dtype=xd)
+    t2r = torch.empty((m, k), dtype=torch.int32, device=dev)
+    drop = torch.empty((m, k), dtype=torch.uint8, device=dev)
+    offs = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    r2t = torch.full((m * k,), -1, dtype=torch.int32, device=dev)
+    rows_bound = m * k if capacity < 0 else min(m * k, capacity * n)
+    disp = (torch.empty((rows_bound, d), dtype=x.dtype, device=dev)
+            if (x is not None and copy_rows) else None)
+    ws, wsb = _ws_args(workspace_size(sh, capacity), dev)
+    _check(_lib().moe_dispatch(ctypes.byref(sh), int(capacity), _ptr(x), _ptr(idx), _ptr(t2r), _ptr(drop),
+                               _ptr(offs), _ptr(r2t), _ptr(disp), ws, wsb, _stream(dev)), "moe_dispatch")
+    return DispatchOut(t2r, drop, offs, r2t, disp)
+
+
+# ------------------------------------------------------------------ expert FFN
+def expert_ffn(dispatched: torch.Tensor, expert_offsets: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+               rows_max: int) -> torch.Tensor:
+    _on_device(dispatched, expert_offsets, w1, w2)
+    n, d_ff, d = w1.shape
+    dev = dispatched.device
+    y = torch.empty((dispatched.shape[0], d), dtype=torch.bfloat16, device=dev)
+    need = int(_lib().moe_expert_ffn_workspace_size(int(n), int(rows_max), int(d_ff)))
+    ws, wsb = _ws_args(need, dev)
+    _check(_lib().moe_expert_ffn(int(n), int(d), int(d_ff), int(rows_max), _ptr(expert_offsets), _ptr(dispatched),
+                                 _ptr(w1), _ptr(w2), _ptr(y), ws, wsb, _stream(dev)), "moe_expert_ffn")
+    return y
+
+
+# ------------------------------------------------------------------ combine
+def combine(y: torch.Tensor, gate: torch.Tensor, token_to_row: torch.Tensor, residual: Optional[torch.Tensor],
+            out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    _on_device(y, gate, token_to_row, residual)
+    m, k = token_to_row.shape
+    dev = y.device
+    d = y.shape[1]
+    odt = residual.dtype if residual is not None else (out_dtype or torch.float32)
+    sh = shape(m, d, k, k, x_dtype=L.MOE_BF16 if odt == torch.bfloat16 else L.MOE_F32)
+    out = torch.empty((m, d), dtype=odt, device=dev)
+    _check(_lib().moe_combine(ctypes.byref(sh), _ptr(y), _dtype_code(y), _ptr(gate), _ptr(token_to_row),
+                              _ptr(residual), _ptr(out), _stream(dev)), "moe_combine")
+    return out
+
+
+# ------------------------------------------------------------------ whole layer
+@dataclass
+class LayerOut:
+    idx: torch.Tensor
+    gate: torch.Tensor
+    counts: torch.Tensor
+    prob_sum: torch.Tensor
+    f: torch.Tensor
+    P: torch.Tensor
+    aux: torch.Tensor
+    token_to_row: torch.Tensor
+    drop_mask: torch.Tensor
+    expert_offsets: torch.Tensor
+    row_to_token: torch.Tensor
+    dispatched: torch.Tensor
+    y: Optional[torch.Tensor]
+    out: torch.Tensor
+
+
+def allocate_layer_outputs(m, d, n, k, rows_bound, x_dtype, ffn: bool, device) -> LayerOut:
+    e = lambda *s, dt: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+    return LayerOut(
+        idx=e(m, k, dt=torch.int32), gate=e(m, k, dt=torch.float32), counts=e(n, dt=torch.int32),
+        prob_sum=e(n, dt=torch.float32), f=e(n, dt=torch.float32), P=e(n, dt=torch.float32),
+        aux=e(1, dt=torch.float32), token_to_row=e(m, k, dt=torch.int32), drop_mask=e(m, k, dt=torch.uint8),
+        expert_offsets=e(n + 1, dt=torch.int32),
+        row_to_token=torch.full((m * k,), -1, dtype=torch.int32, device=device),
+        dispatched=e(rows_bound, d, dt=x_dtype), y=e(rows_bound, d, dt=torch.bfloat16) if ffn else None,
+        out=e(m, d, dt=x_dtype))
+
+
+def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int = -1, alpha: float = 1e-2,
+                 w1: Optional[torch.Tensor] = None, w2: Optional[torch.Tensor] = None,
+                 bias: Optional[torch.Tensor] = None, score: str = "softmax", gate: str = "prob",
+                 outputs: Optional[LayerOut] = None) -> LayerOut:
+    _on_device(x, w_r, w1, w2, bias)
+    m, d = x.shape
+    n = w_r.shape[1]
+    dev = x.device
+    ffn = w1 is not None
+    d_ff = w1.shape[1] if ffn else 0
+    sh = shape(m, d, n, k, score, gate, _dtype_code(x))
+    rows_bound = m * k if capacity < 0 else min(m * k, capacity * n)
+    o = outputs or allocate_layer_outputs(m, d, n, k, rows_bound, x.dtype, ffn, dev)
+    lo = L.LayerOutputs(*[(_ptr(getattr(o, f)) if getattr(o, f) is not None else None)
+                          for f, _ in L.LayerOutputs._fields_])
+    params = L.LayerParams(int(capacity), L.EXPERTS["relu_ffn" if ffn else "identity"], int(d_ff), float(alpha))
+    ws, wsb = _ws_args(workspace_size(sh, capacity, d_ff), dev)
+    _check(_lib().moe_switch_layer(ctypes.byref(sh), ctypes.byref(params), _ptr(x), _ptr(w_r), _ptr(w1), _ptr(w2),
+                                   _ptr(bias), ctypes.byref(lo), ws, wsb, _stream(dev)), "moe_switch_layer")
+    return o

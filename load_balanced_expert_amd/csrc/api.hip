@@ -1,0 +1,338 @@
+// C ABI of libmoe: host-side validation, workspace carve-up and launch
+// sequencing.  Every argument check runs before the first HIP call.
+#include <math.h>
+#include <string.h>
+
+#include "moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+using namespace moe;
+
+size_t al(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t planes, logits, chunks, r2t, hidden;
+  size_t idx, gate, counts, psum, f, P, aux, t2r, drop, offs, disp, y;
+  size_t route_end, dispatch_end, total;
+  RoutePlan rp;
+  int64_t pairs, rows_bound;
+};
+
+bool shape_valid(const moe_shape* s) {
+  return s && s->m >= 1 && s->d >= 1 && s->n >= 1 && s->k >= 1 && s->k <= s->n &&
+         (s->score == MOE_SCORE_SOFTMAX || s->score == MOE_SCORE_SIGMOID) &&
+         (s->gate == MOE_GATE_PROB || s->gate == MOE_GATE_RENORM) &&
+         (s->x_dtype == MOE_F32 || s->x_dtype == MOE_BF16);
+}
+
+bool shape_supported(const moe_shape* s) {
+  return s->n <= kMaxExperts && s->m <= 0x7FFFFFFFll && s->m * s->k <= 0x7FFFFFFFll;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!shape_valid(s)) return MOE_ERR_INVALID_ARG;
+  if (!shape_supported(s)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t x_esz(const moe_shape& s) { return s.x_dtype == MOE_BF16 ? 2 : 4; }
+
+Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
+  Layout L{};
+  L.rp = route_plan(s.m, s.d, s.n, s.x_dtype == MOE_BF16);
+  L.pairs = s.m * s.k;
+  L.rows_bound = capacity < 0 ? L.pairs : std::min<int64_t>(L.pairs, int64_t(capacity) * s.n);
+  const size_t esz = x_esz(s);
+  size_t o = kControlBytes;
+  L.planes = o; o += al(L.rp.planes_bytes);
+  L.logits = o; o += al(L.rp.logits_bytes);
+  L.route_end = o;
+  L.chunks = o; o += al(dispatch_ws_bytes(L.pairs, s.n));
+  L.r2t = o; o += al(size_t(L.pairs) * 4);
+  L.dispatch_end = o;
+  L.hidden = o; o += al(d_ff > 0 ? ffn_ws_bytes(L.rows_bound, d_ff) : 0);
+  L.idx = o; o += al(size_t(L.pairs) * 4);
+  L.gate = o; o += al(size_t(L.pairs) * 4);
+  L.counts = o; o += al(size_t(s.n) * 4);
+  L.psum = o; o += al(size_t(s.n) * 4);
+  L.f = o; o += al(size_t(s.n) * 4);
+  L.P = o; o += al(size_t(s.n) * 4);
+  L.aux = o; o += al(4);
+  L.t2r = o; o += al(size_t(L.pairs) * 4);
+  L.drop = o; o += al(size_t(L.pairs));
+  L.offs = o; o += al(size_t(s.n + 1) * 4);
+  L.disp = o; o += al(size_t(L.rows_bound) * s.d * esz);
+  L.y = o; o += al(size_t(L.rows_bound) * s.d * (d_ff > 0 ? 2 : esz));
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool ws_ok(const void* ws, size_t have, size_t need) {
+  return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) % 256) == 0 && have >= need;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int32_t effective_capacity(int32_t capacity, int64_t pairs) {
+  return capacity < 0 ? int32_t(std::min<int64_t>(pairs, 0x7FFFFFFF)) : capacity;
+}
+
+moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const float* w_r, const float* bias,
+                    int32_t* idx, float* gate, int32_t* counts, float* prob_sum, void* ws, hipStream_t st) {
+  RouteArgs a{};
+  a.x = x;
+  a.m = s.m;
+  a.d = s.d;
+  a.n = s.n;
+  a.npad = L.rp.npad;
+  a.dpad = L.rp.dpad;
+  a.k = s.k;
+  a.score = s.score;
+  a.gate = s.gate;
+  a.x_bf16 = s.x_dtype == MOE_BF16;
+  a.w_r = w_r;
+  a.bias = bias;
+  a.planes = at<uint16_t>(ws, L.planes);
+  a.logits = at<float>(ws, L.logits);
+  a.idx = idx;
+  a.gate_out = gate;
+  a.counts = counts;
+  a.prob_sum = prob_sum;
+  a.psum_acc = ctl_psum(ws);
+  a.cnt_acc = ctl_cnt(ws);
+  a.done = ctl_ticket(ws, kTicketRoute);
+  RoutePlan rp = L.rp;
+  if (rp.mfma && (reinterpret_cast<uintptr_t>(x) % 16) != 0) rp.mfma = false;
+  return hip_status(launch_route(rp, a, st));
+}
+
+moe_status do_dispatch(const moe_shape& s, const Layout& L, int32_t capacity, const void* x, const int32_t* idx,
+                       int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* r2t, void* disp, void* ws,
+                       hipStream_t st) {
+  DispatchArgs a{};
+  a.idx = idx;
+  a.pairs = L.pairs;
+  a.k = s.k;
+  a.n = s.n;
+  a.nbits = bits_for(s.n);
+  a.capacity = effective_capacity(capacity, L.pairs);
+  a.chunk_counts = at<int32_t>(ws, L.chunks);
+  a.token_to_row = t2r;
+  a.drop_mask = drop;
+  a.expert_offsets = offs;
+  a.row_to_token = r2t ? r2t : (disp ? at<int32_t>(ws, L.r2t) : nullptr);
+  a.x = x;
+  a.dispatched = disp;
+  a.row_bytes = int64_t(s.d) * x_esz(s);
+  a.max_rows = L.rows_bound;
+  a.done = ctl_ticket(ws, kTicketDispatch);
+  return hip_status(launch_dispatch(a, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_shape* shape, int32_t capacity, int32_t d_ff) {
+  if (check_shape(shape) != MOE_OK || capacity < -1 || d_ff < 0) return 0;
+  return layout(*shape, capacity, d_ff).total;
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws_ok(ws, ws_bytes, kControlBytes)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return hip_status(hipMemsetAsync(ws, 0, kControlBytes, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_capacity(int64_t m, int32_t n, double cf) {
+  if (m < 0 || n < 1 || !(cf >= 0) || !isfinite(cf)) return -1;
+  if (cf == 0.0 || m == 0) return 0;
+  int e = 0;
+  const double fr = frexp(cf, &e);                 // cf = fr * 2^e, fr in [0.5, 1)
+  const int64_t mant = int64_t(ldexp(fr, 53));     // cf = mant * 2^(e-53), exact
+  int sh = e - 53;
+  __int128 num = (__int128)m * mant;               // < 2^116
+  __int128 q;
+  if (sh >= 0) {
+    if (sh > 60) return -1;
+    q = (num << sh) / n;
+  } else {
+    q = num / n;                                   // floor(floor(a/b)/c) == floor(a/(b c))
+    const int r = -sh;
+    q = r >= 127 ? 0 : (q >> r);
+  }
+  if (q > 0x7FFFFFFF) return -1;
+  return int32_t(q);
+}
+
+const char* moe_status_str(int32_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or option";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_build_info(void) { return "libmoe 0.1 gfx950"; }
+
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* bias, int32_t* idx,
+                     float* gate, int32_t* counts, float* prob_sum, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !w_r || !idx || !gate || !counts) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(*shape, -1, 0);
+  if (!ws_ok(ws, ws_bytes, L.route_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return do_route(*shape, L, x, w_r, bias, idx, gate, counts, prob_sum, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, const float* prob_sum, float alpha,
+                     float* f, float* P, float* aux, int64_t* global_counts, int64_t* global_tokens, float* bias,
+                     float gamma, void* stream) {
+  if (m < 1 || n < 1 || k < 1 || k > n || !counts) return MOE_ERR_INVALID_ARG;
+  if ((global_counts == nullptr) != (global_tokens == nullptr)) return MOE_ERR_INVALID_ARG;
+  if ((P || aux) && !prob_sum) return MOE_ERR_INVALID_ARG;
+  if (n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (m > (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;  // c*n and m*k stay inside int64
+  return hip_status(launch_stats(m, n, k, counts, prob_sum, alpha, f, P, aux, global_counts, global_tokens, bias,
+                                 gamma, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t* global_tokens, const float* P,
+                          int32_t nb, float alpha, float* f_global, float* losses, float* loss_mean, void* stream) {
+  if (n < 1 || nb < 0 || !global_counts || !global_tokens) return MOE_ERR_INVALID_ARG;
+  if (nb > 0 && !P) return MOE_ERR_INVALID_ARG;
+  if (n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_global_aux(n, global_counts, global_tokens, P, nb, alpha, f_global, losses, loss_mean,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_balance_workspace_size(int64_t m, int32_t n, int32_t k, int32_t exact) {
+  if (m < 1 || n < 2 || k < 1 || k >= n) return 0;
+  return kControlBytes + balance_ws_bytes(m, n, k, exact != 0);
+}
+
+moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, float* beta, int32_t iters,
+                             int32_t mode, int32_t exact, int32_t* idx, int32_t* counts, float* alpha,
+                             int32_t* info, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 1 || n < 2 || k < 1 || k >= n || !s || !beta || !idx || !counts) return MOE_ERR_INVALID_ARG;
+  if ((m * int64_t(k)) % n != 0) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_QB_SOLVE && mode != MOE_QB_ONLINE) return MOE_ERR_INVALID_ARG;
+  if (iters < 0 || (mode == MOE_QB_ONLINE && (iters != 1 || exact))) return MOE_ERR_INVALID_ARG;
+  if (n > kMaxExperts || m > 0x7FFFFFFFll || m * k > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
+  if (exact && n > 64) return MOE_ERR_UNSUPPORTED;
+  if (!ws_ok(ws, ws_bytes, moe_balance_workspace_size(m, n, k, exact))) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  BalanceArgs a{};
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.q = m * k / n;
+  a.s = s;
+  a.beta = beta;
+  a.iters = mode == MOE_QB_ONLINE ? 1 : iters;
+  a.mode = mode;
+  a.exact = exact;
+  a.idx = idx;
+  a.counts = counts;
+  a.alpha_out = alpha;
+  a.info = info;
+  a.ws = static_cast<char*>(ws) + kControlBytes;
+  a.done = ctl_ticket(ws, kTicketBalance);
+  a.cnt_acc = ctl_cnt(ws);
+  return hip_status(launch_balance(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_dispatch(const moe_shape* shape, int32_t capacity, const void* x, const int32_t* idx,
+                        int32_t* token_to_row, uint8_t* drop_mask, int32_t* expert_offsets, int32_t* row_to_token,
+                        void* dispatched, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (capacity < -1 || !idx || !token_to_row || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (dispatched && !x) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(*shape, capacity, 0);
+  if (!ws_ok(ws, ws_bytes, L.dispatch_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return do_dispatch(*shape, L, capacity, x, idx, token_to_row, drop_mask, expert_offsets, row_to_token, dispatched,
+                     ws, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_expert_ffn_workspace_size(int32_t n, int32_t rows_max, int32_t d_ff) {
+  if (n < 1 || rows_max < 0 || d_ff < 1) return 0;
+  return kControlBytes + al(ffn_ws_bytes(int64_t(n) * rows_max, d_ff));
+}
+
+moe_status moe_expert_ffn(int32_t n, int32_t d, int32_t d_ff, int32_t rows_max, const int32_t* expert_offsets,
+                          const void* dispatched, const void* w1, const void* w2, void* y, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (n < 1 || d < 1 || d_ff < 1 || rows_max < 0 || !expert_offsets || !dispatched || !w1 || !w2 || !y)
+    return MOE_ERR_INVALID_ARG;
+  if (d % 32 != 0 || d_ff % 32 != 0 || n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (!ws_ok(ws, ws_bytes, moe_expert_ffn_workspace_size(n, rows_max, d_ff)))
+    return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return hip_status(launch_expert_ffn(n, d, d_ff, rows_max, expert_offsets, static_cast<const uint16_t*>(dispatched),
+                                      static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
+                                      at<uint16_t>(ws, kControlBytes), static_cast<uint16_t*>(y),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* y, int32_t y_dtype, const float* gate,
+                       const int32_t* token_to_row, const void* residual, void* out, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!y || !gate || !token_to_row || !out || (y_dtype != MOE_F32 && y_dtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(shape->m, shape->d, shape->k, y, y_dtype == MOE_BF16, gate, token_to_row, residual,
+                                   out, shape->x_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, const void* x, const float* w_r,
+                            const void* w1, const void* w2, const float* bias, const moe_layer_outputs* o, void* ws,
+                            size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!p || !o || !x || !w_r || !o->out || p->capacity < -1) return MOE_ERR_INVALID_ARG;
+  const bool ffn = p->expert_kind == MOE_EXPERT_RELU_FFN;
+  if (!ffn && p->expert_kind != MOE_EXPERT_IDENTITY) return MOE_ERR_INVALID_ARG;
+  if (ffn && (!w1 || !w2 || p->d_ff < 1 || shape->x_dtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
+  if (ffn && (shape->d % 32 != 0 || p->d_ff % 32 != 0)) return MOE_ERR_UNSUPPORTED;
+  const Layout L = layout(*shape, p->capacity, ffn ? p->d_ff : 0);
+  if (!ws_ok(ws, ws_bytes, L.total)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_shape& sh = *shape;
+  int32_t* idx = o->idx ? o->idx : at<int32_t>(ws, L.idx);
+  float* gate = o->gate ? o->gate : at<float>(ws, L.gate);
+  int32_t* counts = o->counts ? o->counts : at<int32_t>(ws, L.counts);
+  float* psum = o->prob_sum ? o->prob_sum : at<float>(ws, L.psum);
+  float* f = o->f ? o->f : at<float>(ws, L.f);
+  float* P = o->P ? o->P : at<float>(ws, L.P);
+  float* aux = o->aux ? o->aux : at<float>(ws, L.aux);
+  int32_t* t2r = o->token_to_row ? o->token_to_row : at<int32_t>(ws, L.t2r);
+  uint8_t* drop = o->drop_mask ? o->drop_mask : at<uint8_t>(ws, L.drop);
+  int32_t* offs = o->expert_offsets ? o->expert_offsets : at<int32_t>(ws, L.offs);
+  int32_t* r2t = o->row_to_token ? o->row_to_token : at<int32_t>(ws, L.r2t);
+  void* disp = o->dispatched ? o->dispatched : at<void>(ws, L.disp);
+  void* y = ffn ? (o->y ? o->y : at<void>(ws, L.y)) : disp;
+
+  if ((st = do_route(sh, L, x, w_r, bias, idx, gate, counts, psum, ws, s)) != MOE_OK) return st;
+  if ((st = hip_status(launch_stats(sh.m, sh.n, sh.k, counts, psum, p->alpha, f, P, aux, nullptr, nullptr, nullptr,
+                                    0.f, s))) != MOE_OK)
+    return st;
+  if ((st = do_dispatch(sh, L, p->capacity, x, idx, t2r, drop, offs, r2t, disp, ws, s)) != MOE_OK) return st;
+  if (ffn) {
+    const int32_t rows_max = effective_capacity(p->capacity, L.pairs);
+    if ((st = hip_status(launch_expert_ffn(sh.n, sh.d, p->d_ff, rows_max, offs, static_cast<const uint16_t*>(disp),
+                                           static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
+                                           at<uint16_t>(ws, L.hidden), static_cast<uint16_t*>(y), s))) != MOE_OK)
+      return st;
+  }
+  return hip_status(launch_combine(sh.m, sh.d, sh.k, y, ffn ? true : sh.x_dtype == MOE_BF16, gate, t2r, x, o->out,
+                                   sh.x_dtype == MOE_BF16, s));
+}
+
+}  // extern "C"

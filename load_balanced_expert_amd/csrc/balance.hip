@@ -1,0 +1,415 @@
+// Balanced optimal assignment ([MoE tour 6]):
+//   "선형계획" eq. (3)/(4): maximise Σ x_ij s_ij with Σ_j x_ij = k and
+//   Σ_i x_ij = q = mk/n;
+//   "교대 반복" (Quantile Balancing): α_i ← (k+1)-th largest of s_i − β,
+//   β_j ← (q+1)-th largest of s_·j − α, x_i = top-k of s_i − β;
+//   "함정에 주의": the online form routes with the old β, then updates it.
+//
+// Kernels
+//  * row kernel: one wave per token row; k+1 rounds of a wave-wide arg-best
+//    over fl32(s_i − β) give the top-k (idx) and the (k+1)-th value (α).
+//  * column kernel: one workgroup per expert; the (q+1)-th largest of
+//    fl32(s_·j − α) by an exact 4-pass radix select (8 bits per pass) over
+//    order-preserving uint32 keys, on a transposed copy of s so that each
+//    column is contiguous.
+//  * exact completion: one persistent workgroup runs successive shortest
+//    paths on the expert graph in fp64 (the move cost a -> j is the cheapest
+//    s_ia − s_ij over tokens holding a but not j, kept in LDS; Dijkstra runs
+//    on one wave with one expert per lane) until every expert has q tokens.
+//    Requires n <= 64.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kQbRowsPerBlock = 16;
+constexpr int kCompleteMaxN = 64;
+
+static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t balance_ws_bytes(int64_t m, int n, int k, bool exact) {
+  size_t b = al256(size_t(m) * n * sizeof(float));   // s transposed
+  b += al256(size_t(m) * sizeof(float));              // alpha
+  if (exact) b += 2 * al256(size_t(m) * k * sizeof(int32_t));  // assignment, per-expert token lists
+  return b;
+}
+
+// ------------------------------------------------------------------ transpose
+__global__ __launch_bounds__(256) void k_qb_transpose(const float* __restrict__ s, float* __restrict__ sT, int64_t m,
+                                                      int n) {
+  __shared__ float tile[64][65];
+  const int64_t ib = int64_t(blockIdx.x) * 64;
+  const int jb = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t i = ib + r;
+    const int j = jb + tx;
+    tile[r][tx] = (i < m && j < n) ? s[i * n + j] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int j = jb + r;
+    const int64_t i = ib + tx;
+    if (j < n && i < m) sT[int64_t(j) * m + i] = tile[tx][r];
+  }
+}
+
+// ------------------------------------------------------------------ rows: top-k and α
+template <bool IDX, bool ALPHA>
+__global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __restrict__ beta,
+                                                 float* __restrict__ alpha, uint32_t* __restrict__ cnt_acc) {
+  extern __shared__ int hist[];
+  const int n = a.n, k = a.k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (IDX) {
+    for (int j = threadIdx.x; j < n; j += 256) hist[j] = 0;
+    __syncthreads();
+  }
+  for (int rr = wave; rr < kQbRowsPerBlock; rr += 4) {
+    const int64_t i = int64_t(blockIdx.x) * kQbRowsPerBlock + rr;
+    if (i >= a.m) break;
+    const float* row = a.s + i * n;
+    float last_key = INFINITY;
+    int last_j = -1, my_j = 0;
+    const int rounds = ALPHA ? k + 1 : k;
+    for (int r = 0; r < rounds; ++r) {
+      float bk = -INFINITY;
+      int bj = 0x7FFFFFFF;
+      for (int j = lane; j < n; j += 64) {
+        const float v = row[j] - beta[j];
+        if (better(last_key, last_j, v, j) && better(v, j, bk, bj)) {
+          bk = v;
+          bj = j;
+        }
+      }
+      wave_argbest(bk, bj);
+      last_key = bk;
+      last_j = bj;
+      if (IDX && r < k) {
+        if (lane == r) my_j = bj;
+        if (lane == 0) atomicAdd(&hist[bj], 1);
+      }
+    }
+    if (ALPHA && lane == 0) alpha[i] = last_key;
+    if (IDX && lane < k) a.idx[i * k + lane] = my_j;
+  }
+  if (!IDX) return;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += 256)
+    if (hist[j]) atomicAdd(cnt_acc + j, uint32_t(hist[j]));
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  __shared__ int s_bal;
+  if (threadIdx.x == 0) s_bal = 1;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const uint32_t c = atomicExch(cnt_acc + j, 0u);
+    a.counts[j] = int32_t(c);
+    if (int64_t(c) != a.q) atomicAnd(&s_bal, 0);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicExch(a.done, 0u);
+    if (a.info) a.info[2] = s_bal;
+  }
+}
+
+// ------------------------------------------------------------------ columns: (q+1)-th largest
+__global__ __launch_bounds__(256) void k_qb_cols(const float* __restrict__ sT, const float* __restrict__ alpha,
+                                                 float* __restrict__ beta, int64_t m, int64_t q) {
+  __shared__ int hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int64_t s_rank;
+  const int j = blockIdx.x;
+  const float* col = sT + int64_t(j) * m;
+  uint32_t prefix = 0, mask = 0;
+  int64_t rank = q;  // 0-based rank in descending order
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < m; i += 256) {
+      const uint32_t u = f32_key(col[i] - alpha[i]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l holds digits 255-4l .. 252-4l (descending digit order across lanes)
+      const int lane = threadIdx.x;
+      int hv[4], tot = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        hv[u] = hist[255 - 4 * lane - u];
+        tot += hv[u];
+      }
+      int incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      int64_t cum = incl - tot;  // count of keys in higher digits
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (cum <= rank && rank < cum + hv[u]) {
+          s_prefix = prefix | (uint32_t(255 - 4 * lane - u) << shift);
+          s_rank = rank - cum;
+        }
+        cum += hv[u];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    rank = s_rank;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) beta[j] = key_f32(prefix);
+}
+
+// ------------------------------------------------------------------ exact completion (n <= 64)
+__device__ __forceinline__ uint64_t f64_key(double d) {
+  const uint64_t u = __double_as_longlong(d);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double key_f64(uint64_t k) {
+  if (k == ~0ull) return INFINITY;
+  return __longlong_as_double((k & 0x8000000000000000ull) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k);
+}
+__device__ __forceinline__ bool better64(double ka, int ia, double kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+__device__ __forceinline__ void wave_argbest64(double& key, int& ix) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double ok = __shfl_xor(key, off, 64);
+    const int oi = __shfl_xor(ix, off, 64);
+    if (better64(ok, oi, key, ix)) {
+      key = ok;
+      ix = oi;
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __restrict__ xi) {
+  __shared__ unsigned long long Mk[kCompleteMaxN * kCompleteMaxN];
+  __shared__ int arg[kCompleteMaxN * kCompleteMaxN];
+  __shared__ double pi[kCompleteMaxN], dist[kCompleteMaxN];
+  __shared__ int cnt[kCompleteMaxN], pred[kCompleteMaxN], vis[kCompleteMaxN];
+  __shared__ int s_go, s_target, s_fail;
+  __shared__ double s_D;
+  const int n = a.n, k = a.k;
+  const int64_t m = a.m, q = a.q;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* s = a.s;
+
+  for (int j = tid; j < n; j += 1024) {
+    pi[j] = double(a.beta[j]);
+    cnt[j] = 0;
+  }
+  __syncthreads();
+  // initial assignment: top-k of the exact keys s_ij − β_j (lower index on ties)
+  for (int64_t i = wave; i < m; i += 16) {
+    double last = INFINITY;
+    int lj = -1;
+    for (int r = 0; r < k; ++r) {
+      double bk = -INFINITY;
+      int bj = 0x7FFFFFFF;
+      if (lane < n) {
+        const double v = double(s[i * n + lane]) - pi[lane];
+        if (better64(last, lj, v, lane)) {
+          bk = v;
+          bj = lane;
+        }
+      }
+      wave_argbest64(bk, bj);
+      last = bk;
+      lj = bj;
+      if (lane == 0) {
+        xi[i * k + r] = bj;
+        atomicAdd(&cnt[bj], 1);
+      }
+    }
+  }
+  int aug = 0;
+  const int max_aug = int(min<int64_t>(m * k, 0x7FFFFFFF));
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) {
+      int go = 0;
+      for (int j = 0; j < n; ++j) go |= cnt[j] > q;
+      s_go = go && aug < max_aug;
+      s_fail = 0;
+    }
+    __syncthreads();
+    if (!s_go) break;
+    for (int e = tid; e < n * n; e += 1024) {
+      Mk[e] = ~0ull;
+      arg[e] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    // move costs: token i holding a but not j offers s_ia − s_ij for a -> j
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int64_t c = tid; c < m * n; c += 1024) {
+        const int64_t i = c / n;
+        const int j = int(c - i * n);
+        const int32_t* xr = xi + i * k;
+        bool has = false;
+        for (int r = 0; r < k; ++r) has |= xr[r] == j;
+        if (has) continue;
+        const double sij = double(s[i * n + j]);
+        for (int r = 0; r < k; ++r) {
+          const int aa = xr[r];
+          const uint64_t key = f64_key(double(s[i * n + aa]) - sij);
+          if (pass == 0)
+            atomicMin(&Mk[aa * n + j], (unsigned long long)key);
+          else if (Mk[aa * n + j] == key)
+            atomicMin(&arg[aa * n + j], int(i));
+        }
+      }
+      __syncthreads();
+    }
+    // Dijkstra from every over-full expert to the first under-full one reached
+    if (wave == 0) {
+      double dv = (lane < n && cnt[lane] > q) ? 0.0 : INFINITY;
+      int pv = -1;
+      bool done = lane >= n;
+      int target = -1;
+      double D = 0.0;
+      for (int it = 0; it < n; ++it) {
+        double bk = done ? -INFINITY : -dv;   // arg-best of -dist == arg-min of dist
+        int bj = done ? 0x7FFFFFFF : lane;
+        wave_argbest64(bk, bj);
+        if (bj == 0x7FFFFFFF || bk == -INFINITY) break;
+        const int u = bj;
+        const double du = -bk;
+        if (lane == u) done = true;
+        if (cnt[u] < q) {
+          target = u;
+          D = du;
+          break;
+        }
+        if (!done) {
+          double w = key_f64(Mk[u * n + lane]) - pi[u] + pi[lane];
+          w = fmax(w, 0.0);
+          const double nd = du + w;
+          if (nd < dv) {
+            dv = nd;
+            pv = u;
+          }
+        }
+      }
+      if (lane < n) {
+        dist[lane] = dv;
+        pred[lane] = pv;
+        vis[lane] = done;
+      }
+      if (lane == 0) {
+        s_target = target;
+        s_D = D;
+        s_fail = target < 0;
+      }
+    }
+    __syncthreads();
+    if (s_fail) break;
+    if (tid < n) {
+      const double D = s_D;
+      pi[tid] -= vis[tid] ? fmin(dist[tid], D) : D;
+    }
+    if (tid == 0) {
+      int j = s_target;
+      while (pred[j] >= 0) {
+        const int aa = pred[j];
+        const int i = arg[aa * n + j];
+        int32_t* xr = xi + int64_t(i) * k;
+        for (int r = 0; r < k; ++r)
+          if (xr[r] == aa) xr[r] = j;
+        j = aa;
+      }
+      cnt[j] -= 1;
+      cnt[s_target] += 1;
+    }
+    ++aug;
+  }
+  __syncthreads();
+  // outputs: idx by descending s_ij − π_j (lower index on ties), counts, β, info
+  for (int64_t i = wave; i < m; i += 16) {
+    const int32_t* xr = xi + i * k;
+    double v = -INFINITY;
+    int jj = 0x7FFFFFFF;
+    if (lane < k) {
+      jj = xr[lane];
+      v = double(s[i * n + jj]) - pi[jj];
+    }
+    // rank of lane's element among the k (k <= 64)
+    int rank = 0;
+    for (int r = 0; r < k; ++r) {
+      const double ov = __shfl(v, r, 64);
+      const int oj = __shfl(jj, r, 64);
+      if (lane < k && better64(ov, oj, v, jj)) ++rank;
+    }
+    if (lane < k) a.idx[i * k + rank] = jj;
+  }
+  int bal = 1;
+  for (int j = tid; j < n; j += 1024) {
+    a.counts[j] = cnt[j];
+    a.beta[j] = float(pi[j]);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int j = 0; j < n; ++j) bal &= cnt[j] == q;
+    if (a.info) {
+      a.info[1] = aug;
+      a.info[2] = bal && !s_fail;
+      a.info[3] = s_fail;
+    }
+  }
+}
+
+__global__ void k_qb_info(int32_t* info, int iters) {
+  if (threadIdx.x == 0) {
+    info[0] = iters;
+    info[1] = 0;
+    info[2] = 0;
+    info[3] = 0;
+  }
+}
+
+// ------------------------------------------------------------------ launcher
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
+  char* ws = static_cast<char*>(a.ws);
+  float* sT = reinterpret_cast<float*>(ws);
+  ws += al256(size_t(a.m) * a.n * sizeof(float));
+  float* alpha_int = reinterpret_cast<float*>(ws);
+  ws += al256(size_t(a.m) * sizeof(float));
+  int32_t* xi = reinterpret_cast<int32_t*>(ws);
+  float* alpha = a.alpha_out ? a.alpha_out : alpha_int;
+  uint32_t* cnt_acc = a.cnt_acc;
+
+  if (a.info) hipLaunchKernelGGL(k_qb_info, dim3(1), dim3(64), 0, s, a.info, a.iters);
+  const unsigned rblocks = unsigned(ceil_div64(a.m, kQbRowsPerBlock));
+  const size_t rlds = a.n * sizeof(int);
+  hipLaunchKernelGGL(k_qb_transpose, dim3(unsigned(ceil_div64(a.m, 64)), ceil_div(a.n, 64)), dim3(256), 0, s, a.s,
+                     sT, a.m, a.n);
+  if (a.mode == 1) {  // online: route with the old β, then one α and one β step
+    hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, cnt_acc);
+    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q);
+    return hipGetLastError();
+  }
+  for (int it = 0; it < a.iters; ++it) {
+    hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, a.beta, alpha, cnt_acc);
+    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q);
+  }
+  if (a.exact)
+    hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi);
+  else
+    hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, cnt_acc);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+// Combine: inverse permute, gate scaling and residual.
+//   out[t] = residual[t] + Σ_{r kept} gate[t, r] · y[token_to_row[t, r]]
+// ([Switch review] "Switch Routing 메커니즘" Step 3: the expert output is scaled
+// by the router probability; [Switch impl] pipeline list: restore the token
+// order, multiply by the gate and join the residual path; dropped tokens take
+// the residual path alone.)  fp32 arithmetic, r in increasing order, one
+// rounding to the output dtype; HBM-bound, so every thread moves 8 elements
+// with 16-byte (bf16) or 2x16-byte (fp32) accesses.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+template <bool BF16>
+__device__ __forceinline__ void load_vec(const void* p, int64_t i, float (&v)[8]) {
+  if constexpr (BF16) {
+    const u32x4 w = reinterpret_cast<const u32x4*>(p)[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[2 * i];
+    const f32x4 b = reinterpret_cast<const f32x4*>(p)[2 * i + 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = a[q];
+      v[4 + q] = b[q];
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_vec(void* p, int64_t i, const float (&v)[8]) {
+  if constexpr (BF16) {
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = uint32_t(f32_to_bf16(v[2 * q])) | (uint32_t(f32_to_bf16(v[2 * q + 1])) << 16);
+    reinterpret_cast<u32x4*>(p)[i] = w;
+  } else {
+    f32x4 a, b;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q] = v[q];
+      b[q] = v[4 + q];
+    }
+    reinterpret_cast<f32x4*>(p)[2 * i] = a;
+    reinterpret_cast<f32x4*>(p)[2 * i + 1] = b;
+  }
+}
+
+template <bool XB, bool YB>
+__global__ __launch_bounds__(256) void k_combine_vec(int64_t m, int d, int k, const void* __restrict__ y,
+                                                     const float* __restrict__ gate,
+                                                     const int32_t* __restrict__ t2r, const void* __restrict__ res,
+                                                     void* __restrict__ out) {
+  const int64_t vpr = d / 8;
+  const int64_t items = m * vpr;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < items; i += int64_t(gridDim.x) * 256) {
+    const int64_t t = i / vpr, v = i - t * vpr;
+    float acc[8];
+    if (res) {
+      load_vec<XB>(res, i, acc);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    }
+    for (int r = 0; r < k; ++r) {
+      const int32_t row = t2r[t * k + r];
+      if (row >= 0) {
+        const float g = gate[t * k + r];
+        float yv[8];
+        load_vec<YB>(y, int64_t(row) * vpr + v, yv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, yv[q], acc[q]);
+      }
+    }
+    store_vec<XB>(out, i, acc);
+  }
+}
+
+// Any d: one element per thread.
+__global__ __launch_bounds__(256) void k_combine_scalar(int64_t m, int d, int k, const void* __restrict__ y, int yb,
+                                                        const float* __restrict__ gate,
+                                                        const int32_t* __restrict__ t2r,
+                                                        const void* __restrict__ res, void* __restrict__ out, int xb) {
+  const int64_t items = m * d;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < items; i += int64_t(gridDim.x) * 256) {
+    const int64_t t = i / d, c = i - t * d;
+    float acc = 0.f;
+    if (res) acc = xb ? bf16_to_f32(static_cast<const uint16_t*>(res)[i]) : static_cast<const float*>(res)[i];
+    for (int r = 0; r < k; ++r) {
+      const int32_t row = t2r[t * k + r];
+      if (row >= 0) {
+        const int64_t o = int64_t(row) * d + c;
+        const float yv = yb ? bf16_to_f32(static_cast<const uint16_t*>(y)[o]) : static_cast<const float*>(y)[o];
+        acc = fmaf(gate[t * k + r], yv, acc);
+      }
+    }
+    if (xb)
+      static_cast<uint16_t*>(out)[i] = f32_to_bf16(acc);
+    else
+      static_cast<float*>(out)[i] = acc;
+  }
+}
+
+hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, const float* gate,
+                          const int32_t* t2r, const void* residual, void* out, bool x_bf16, hipStream_t s) {
+  const uintptr_t al = reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(out) |
+                       reinterpret_cast<uintptr_t>(residual);
+  if (d % 8 == 0 && (al % 16) == 0) {
+    const int64_t items = m * (d / 8);
+    const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(items, 256), 65536));
+    if (x_bf16 && y_bf16)
+      hipLaunchKernelGGL((k_combine_vec<true, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+    else if (x_bf16)
+      hipLaunchKernelGGL((k_combine_vec<true, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+    else if (y_bf16)
+      hipLaunchKernelGGL((k_combine_vec<false, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+    else
+      hipLaunchKernelGGL((k_combine_vec<false, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+  } else {
+    const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(m * d, 256), 65536));
+    hipLaunchKernelGGL(k_combine_scalar, dim3(blocks), dim3(256), 0, s, m, d, k, y, int(y_bf16), gate, t2r, residual,
+                       out, int(x_bf16));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,113 @@
+// Device helpers shared by the gfx950 kernels of libmoe.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 4096;
+
+// Control region at the start of every workspace (zero before first use;
+// every kernel that uses a word leaves it zero again).
+//   [0, 256)            completion tickets of last-block-done kernels
+//   [256, 33024)        uint64 fixed-point score sums, one per expert
+//   [33024, 49408)      uint32 expert counters, one per expert
+constexpr size_t kControlBytes = 65536;
+constexpr size_t kCtlPsumOffset = 256;
+constexpr size_t kCtlCntOffset = kCtlPsumOffset + sizeof(uint64_t) * kMaxExperts;
+enum CtlTicket { kTicketRoute = 0, kTicketDispatch = 1, kTicketBalance = 2 };
+inline uint32_t* ctl_ticket(void* ws, int which) { return static_cast<uint32_t*>(ws) + which; }
+inline uint64_t* ctl_psum(void* ws) { return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kCtlPsumOffset); }
+inline uint32_t* ctl_cnt(void* ws) { return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCtlCntOffset); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float <-> larger key).
+__device__ __forceinline__ uint32_t f32_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// (key, index) ordering used by every top-k: larger key first, lower index on ties.
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Wave-wide arg-best of (key, index) by the order above; every lane gets the result.
+__device__ __forceinline__ void wave_argbest(float& key, int& ix) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float ok = __shfl_xor(key, off, kWave);
+    int oi = __shfl_xor(ix, off, kWave);
+    if (better(ok, oi, key, ix)) { key = ok; ix = oi; }
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Butterfly sum: every lane ends with the same value, and the association order
+// depends only on lane positions, so the result is reproducible.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Lanes of the wave whose `key` equals this lane's (a "match any" built from
+// one ballot per key bit), restricted to `active`.
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t active) {
+  uint64_t peers = active;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  return peers;
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int round_up(int a, int b) { return ceil_div(a, b) * b; }
+
+inline int bits_for(int n) {  // bits needed for values 0..n-1
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+}  // namespace moe

@@ -1,0 +1,102 @@
+// Internal launchers of libmoe (host side, C++ linkage).  Arguments are
+// validated by the C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+struct RoutePlan {
+  bool fused;      // logits tile kept in LDS (n <= kFusedMaxN)
+  bool mfma;       // bf16 x on matrix cores (exact 3-way bf16 split of W_r)
+  int npad;        // experts padded (fused: multiple of 32, else of 128)
+  int dpad;        // d padded to a multiple of 32 (mfma)
+  size_t planes_bytes;
+  size_t logits_bytes;
+};
+constexpr int kFusedMaxN = 256;
+RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16);
+
+struct RouteArgs {
+  const void* x;
+  int64_t m;
+  int d, n, npad, dpad, k;
+  int score;       // 0 softmax, 1 sigmoid
+  int gate;        // 0 prob, 1 renorm
+  int x_bf16;      // storage dtype of x
+  const float* w_r;
+  const float* bias;
+  const uint16_t* planes;
+  float* logits;   // big-n path only
+  int32_t* idx;
+  float* gate_out;
+  int32_t* counts;
+  float* prob_sum;
+  uint64_t* psum_acc;  // [n] zero, left zero
+  uint32_t* cnt_acc;   // [n] zero, left zero
+  uint32_t* done;      // zero, left zero
+};
+hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- stats
+hipError_t launch_stats(int64_t m, int n, int k, const int32_t* counts, const float* prob_sum,
+                        float alpha, float* f, float* P, float* aux, int64_t* gcounts,
+                        int64_t* gtokens, float* bias, float gamma, hipStream_t s);
+hipError_t launch_global_aux(int n, const int64_t* gcounts, const int64_t* gtokens, const float* P,
+                             int nb, float alpha, float* fg, float* losses, float* loss_mean,
+                             hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch
+constexpr int kDispChunk = 1024;  // (token, choice) pairs per histogram / rank block
+struct DispatchArgs {
+  const int32_t* idx;
+  int64_t pairs;        // m * k
+  int k, n, nbits;
+  int32_t capacity;     // >= 0 (unlimited is passed as pairs)
+  int32_t* chunk_counts;  // [nch, n] workspace
+  int32_t* token_to_row;
+  uint8_t* drop_mask;
+  int32_t* expert_offsets;
+  int32_t* row_to_token;
+  const void* x;
+  void* dispatched;
+  int64_t row_bytes;    // d * element size
+  int64_t max_rows;     // host bound on rows
+  uint32_t* done;
+};
+size_t dispatch_ws_bytes(int64_t pairs, int n);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- expert FFN
+size_t ffn_ws_bytes(int64_t rows_bound, int d_ff);
+hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets,
+                             const uint16_t* D, const uint16_t* w1, const uint16_t* w2,
+                             uint16_t* hidden, uint16_t* y, hipStream_t s);
+
+// ---------------------------------------------------------------- combine
+hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, const float* gate,
+                          const int32_t* token_to_row, const void* residual, void* out,
+                          bool x_bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- balanced assignment
+size_t balance_ws_bytes(int64_t m, int n, int k, bool exact);
+struct BalanceArgs {
+  int64_t m;
+  int n, k;
+  int64_t q;
+  const float* s;
+  float* beta;
+  int iters, mode, exact;
+  int32_t* idx;
+  int32_t* counts;
+  float* alpha_out;
+  int32_t* info;
+  void* ws;          // after the control words
+  uint32_t* done;    // completion ticket (control region)
+  uint32_t* cnt_acc; // [n] expert counters (control region)
+};
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
+
+}  // namespace moe

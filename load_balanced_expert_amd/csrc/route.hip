@@ -1,0 +1,399 @@
+// Router: h = x · W_r, softmax / sigmoid score, top-k selection, gates, the
+// expert histogram and Σ_t score_j(t).
+//
+// [Switch review] "Switch Routing 메커니즘" Step 1-3 (h = x·W_r, p = softmax(h),
+// i* = argmax p, gate = p_{i*}); "선택적 정밀도 캐스팅" (router in fp32 on bf16
+// hidden states); [MoE tour 6] "방법 회고" eq. (1) (Loss-Free: top-k of ρ + b,
+// gate ρ); [Switch review] "로드 밸런싱 손실" (counts for f_i, Σ p for P_i).
+//
+// gfx950 design
+//  * bf16 x: W_r is split once per call into three bf16 planes hi + mid + lo
+//    that sum exactly to the fp32 weight; three bf16 MFMAs with fp32
+//    accumulation then give an fp32-accurate product (every bf16 x bf16
+//    product is exact in fp32).  v_mfma_f32_32x32x16_bf16, 64-lane waves.
+//  * n <= 256: one workgroup owns 32 tokens x all experts; the logits tile
+//    stays in LDS and the epilogue (softmax statistics, top-k, gates, block
+//    histogram, per-expert score sums) runs in the same kernel.
+//  * n > 256: a tiled MFMA GEMM writes fp32 logits to the workspace, then a
+//    row kernel runs the same epilogue from global memory.
+//  * Σ_t score_j(t) is accumulated as 2^-32 fixed point in uint64 atomics, so
+//    the total is exact integer arithmetic and independent of block order;
+//    counts use integer atomics.  The last block to finish converts the
+//    totals, writes the outputs and clears the accumulators.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kRouteBM = 32;      // tokens per route workgroup
+constexpr int kRouteThreads = 256;
+constexpr double kFix = 4294967296.0;  // 2^32
+
+RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
+  RoutePlan p{};
+  p.fused = n <= kFusedMaxN;
+  p.mfma = x_bf16 && (d % 8 == 0);
+  p.npad = p.fused ? round_up(n, 32) : round_up(n, 128);
+  p.dpad = round_up(d, 32);
+  p.planes_bytes = p.mfma ? size_t(3) * p.npad * p.dpad * sizeof(uint16_t) : 0;
+  p.logits_bytes = p.fused ? 0 : size_t(m) * p.npad * sizeof(float);
+  return p;
+}
+
+// ------------------------------------------------------------------ W_r split
+// planes[p][j][k], p = 0 (hi), 1 (mid), 2 (lo); zero for j >= n or k >= d.
+__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ w,
+                                                       uint16_t* __restrict__ planes, int d, int n,
+                                                       int npad, int dpad) {
+  __shared__ float tile[64][65];
+  const int kb = blockIdx.x * 64, jb = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int k = kb + r, j = jb + tx;
+    tile[r][tx] = (k < d && j < n) ? w[size_t(k) * n + j] : 0.f;
+  }
+  __syncthreads();
+  const size_t plane = size_t(npad) * dpad;
+  for (int r = ty; r < 64; r += 4) {
+    const int j = jb + r, k = kb + tx;
+    if (j < npad && k < dpad) {
+      const float v = tile[tx][r];
+      const uint16_t hi = f32_to_bf16(v);
+      const float r1 = v - bf16_to_f32(hi);     // exact: |r1| <= half a bf16 ulp of v
+      const uint16_t mid = f32_to_bf16(r1);
+      const float r2 = r1 - bf16_to_f32(mid);   // exact, at most 8 significant bits
+      const uint16_t lo = f32_to_bf16(r2);      // exact
+      const size_t o = size_t(j) * dpad + k;
+      planes[o] = hi;
+      planes[plane + o] = mid;
+      planes[2 * plane + o] = lo;
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+// One 32-token x (tiles of 32 experts) block product on bf16 MFMA.  Lane l
+// holds row (l & 31) and the k-slice [kb + 16*(l>>5), +16) of each 32-wide
+// K block; substep s uses its elements [8s, 8s+8).  A and B use the same
+// lane -> k mapping, so every k is paired with itself exactly once.
+template <int TPW>
+__device__ __forceinline__ void gemm_tile_bf16x3(const uint16_t* __restrict__ xrow, int d, int dpad,
+                                                 const uint16_t* __restrict__ planes, int npad,
+                                                 int wave, int lane, f32x16 (&acc)[TPW]) {
+  const int h = lane >> 5, r32 = lane & 31;
+  const size_t plane = size_t(npad) * dpad;
+  const int ntiles = npad / 32;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+  for (int kb = 0; kb < dpad; kb += 32) {
+    const int k0 = kb + 16 * h;
+    const bf16x8 a0 = (k0 + 8 <= d) ? load8(xrow + k0) : zero8();
+    const bf16x8 a1 = (k0 + 16 <= d) ? load8(xrow + k0 + 8) : zero8();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tile = wave + 4 * t;
+      if (tile < ntiles) {
+        const uint16_t* b = planes + size_t(tile * 32 + r32) * dpad + k0;
+        const bf16x8 h0 = load8(b), h1 = load8(b + 8);
+        const bf16x8 m0 = load8(b + plane), m1 = load8(b + plane + 8);
+        const bf16x8 l0 = load8(b + 2 * plane), l1 = load8(b + 2 * plane + 8);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, h0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, h1, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, m0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, m1, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, l0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, l1, acc[t], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// 32x32 accumulator layout: lane l, element i -> row 8*(i/4) + 4*(l/32) + (i%4), col l%32.
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// ------------------------------------------------------------------ epilogue
+struct EpiArgs {
+  int n, k, score, gate;
+  const float* bias;
+};
+
+__device__ __forceinline__ float sigm(float h) { return 1.0f / (1.0f + expf(-h)); }
+
+// Score of expert j for a token with softmax statistics (mx, sum).
+__device__ __forceinline__ float score_of(int score, float h, float mx, float sum) {
+  return score == 0 ? expf(h - mx) / sum : sigm(h);
+}
+
+// Per-token selection for the `rows` tokens of one block, wave w taking
+// tokens w, w+4, ...; writes idx/gate, per-token softmax statistics to
+// tok_mx/tok_sum (shared) and counts selections into hist (shared).
+__device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows, int64_t t0,
+                                           const EpiArgs& e, int32_t* __restrict__ idx,
+                                           float* __restrict__ gate_out, float* tok_mx,
+                                           float* tok_sum, int* hist) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = e.n;
+  for (int tl = wave; tl < rows; tl += kRouteThreads / 64) {
+    const float* row = lg + int64_t(tl) * ld;
+    float mx = -INFINITY, sum = 1.0f;
+    if (e.score == 0) {
+      for (int j = lane; j < n; j += 64) mx = fmaxf(mx, row[j]);
+      mx = wave_max(mx);
+      float s = 0.f;
+      for (int j = lane; j < n; j += 64) s += expf(row[j] - mx);
+      sum = wave_sum(s);
+    }
+    if (lane == 0) {
+      tok_mx[tl] = mx;
+      tok_sum[tl] = sum;
+    }
+    // k rounds: each picks the best (key, j) strictly after the previous pick
+    float last_key = INFINITY;
+    int last_j = -1;
+    int my_j = 0;
+    float my_score = 0.f, score_total = 0.f;
+    for (int r = 0; r < e.k; ++r) {
+      float bk = -INFINITY;
+      int bj = 0x7FFFFFFF;
+      for (int j = lane; j < n; j += 64) {
+        const float h = row[j];
+        const float key = e.bias ? score_of(e.score, h, mx, sum) + e.bias[j] : h;
+        if (better(last_key, last_j, key, j) && better(key, j, bk, bj)) {
+          bk = key;
+          bj = j;
+        }
+      }
+      wave_argbest(bk, bj);
+      last_key = bk;
+      last_j = bj;
+      const float sc = score_of(e.score, row[bj], mx, sum);
+      score_total += sc;
+      if (lane == r) {
+        my_j = bj;
+        my_score = sc;
+      }
+      if (lane == 0) atomicAdd(&hist[bj], 1);
+    }
+    if (lane < e.k) {
+      const int64_t o = (t0 + tl) * e.k + lane;
+      idx[o] = my_j;
+      gate_out[o] = e.gate == 1 ? my_score / score_total : my_score;
+    }
+  }
+}
+
+// Per-expert Σ over the block's tokens of score_j(t), folded into 2^-32 fixed
+// point, and the block histogram; then the last block publishes the totals.
+__device__ __forceinline__ void route_block_tail(const float* lg, int64_t ld, int rows, const EpiArgs& e,
+                                                 const float* tok_mx, const float* tok_sum, int* hist,
+                                                 const RouteArgs& a) {
+  for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
+    if (a.prob_sum) {
+      float acc = 0.f;
+      for (int tl = 0; tl < rows; ++tl) acc += score_of(e.score, lg[int64_t(tl) * ld + j], tok_mx[tl], tok_sum[tl]);
+      const unsigned long long fx = __double2ull_rn(double(acc) * kFix);
+      if (fx) atomicAdd(reinterpret_cast<unsigned long long*>(a.psum_acc + j), fx);
+    }
+    const int c = hist[j];
+    if (c) atomicAdd(a.cnt_acc + j, uint32_t(c));
+  }
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1u) == gridDim.x * gridDim.y - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
+    const unsigned long long v = atomicExch(reinterpret_cast<unsigned long long*>(a.psum_acc + j), 0ull);
+    const uint32_t c = atomicExch(a.cnt_acc + j, 0u);
+    a.counts[j] = int32_t(c);
+    if (a.prob_sum) a.prob_sum[j] = float(double(v) / kFix);
+  }
+  if (threadIdx.x == 0) atomicExch(a.done, 0u);
+}
+
+__device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
+  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i]) : static_cast<const float*>(x)[i];
+}
+
+// ------------------------------------------------------------------ fused route (n <= 256)
+template <int TPW, bool MFMA>
+__global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
+  extern __shared__ float smem[];
+  const int ldl = a.npad + 1;
+  float* lg = smem;
+  float* tok_mx = lg + kRouteBM * ldl;
+  float* tok_sum = tok_mx + kRouteBM;
+  int* hist = reinterpret_cast<int*>(tok_sum + kRouteBM);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t t0 = int64_t(blockIdx.x) * kRouteBM;
+  const int rows = int(min<int64_t>(kRouteBM, a.m - t0));
+  for (int j = tid; j < a.npad; j += kRouteThreads) hist[j] = 0;
+
+  if constexpr (MFMA) {
+    const int r = min(lane & 31, rows - 1);  // rows past the end repeat the last token; discarded
+    const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (t0 + r) * a.d;
+    f32x16 acc[TPW];
+    gemm_tile_bf16x3<TPW>(xrow, a.d, a.dpad, a.planes, a.npad, wave, lane, acc);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tile = wave + 4 * t;
+      if (tile < a.npad / 32) {
+        const int col = tile * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lg[acc_row(i, lane) * ldl + col] = acc[t][i];
+      }
+    }
+  } else {
+    // fp32 product on the vector ALUs: thread (token, expert group), fma over k in order.
+    const int tl = tid >> 3, jg = tid & 7;
+    if (tl < rows) {
+      const int64_t xo = (t0 + tl) * a.d;
+      for (int j = jg; j < a.npad; j += 8) {
+        float h = 0.f;
+        if (j < a.n)
+          for (int kk = 0; kk < a.d; ++kk) h = fmaf(load_x(a.x, a.x_bf16, xo + kk), a.w_r[int64_t(kk) * a.n + j], h);
+        lg[tl * ldl + j] = h;
+      }
+    }
+  }
+  __syncthreads();
+  EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
+  route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
+  __syncthreads();
+  route_block_tail(lg, ldl, rows, e, tok_mx, tok_sum, hist, a);
+}
+
+// ------------------------------------------------------------------ big-n route: logits GEMM
+// Workgroup: 128 tokens x 128 experts; wave (wm, wn) owns 64 x 64 = 2 x 2 MFMA tiles.
+__global__ __launch_bounds__(256) void k_route_logits_mfma(RouteArgs a) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  const int64_t tb = int64_t(blockIdx.x) * 128 + 64 * wm;
+  const int jb = blockIdx.y * 128 + 64 * wn;
+  const size_t plane = size_t(a.npad) * a.dpad;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* xr[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) xr[mt] = x + min<int64_t>(tb + 32 * mt + r32, a.m - 1) * a.d;
+  const uint16_t* br[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) br[nt] = a.planes + size_t(jb + 32 * nt + r32) * a.dpad;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
+  for (int kb = 0; kb < a.dpad; kb += 32) {
+    const int k0 = kb + 16 * h;
+    bf16x8 av[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      av[mt][0] = (k0 + 8 <= a.d) ? load8(xr[mt] + k0) : zero8();
+      av[mt][1] = (k0 + 16 <= a.d) ? load8(xr[mt] + k0 + 8) : zero8();
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8 b0 = load8(br[nt] + p * plane + k0), b1 = load8(br[nt] + p * plane + k0 + 8);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt][0], b0, acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt][1], b1, acc[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int col = jb + 32 * nt + r32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t t = tb + 32 * mt + acc_row(i, lane);
+        if (t < a.m) a.logits[t * a.npad + col] = acc[mt][nt][i];
+      }
+    }
+}
+
+// fp32 vector-ALU logits for the big-n path (fp32 x, or bf16 x with d % 8 != 0).
+// Workgroup: 32 tokens x 64 experts.
+__global__ __launch_bounds__(256) void k_route_logits_valu(RouteArgs a) {
+  const int tid = threadIdx.x, tl = tid >> 3, jg = tid & 7;
+  const int64_t t = int64_t(blockIdx.x) * 32 + tl;
+  const int jb = blockIdx.y * 64;
+  if (t >= a.m) return;
+  for (int u = 0; u < 8; ++u) {
+    const int j = jb + jg + 8 * u;
+    float h = 0.f;
+    if (j < a.n)
+      for (int kk = 0; kk < a.d; ++kk) h = fmaf(load_x(a.x, a.x_bf16, t * a.d + kk), a.w_r[int64_t(kk) * a.n + j], h);
+    a.logits[t * a.npad + j] = h;
+  }
+}
+
+// big-n route epilogue: kRowsBM tokens per workgroup from the logits in global memory.
+constexpr int kRowsBM = 256;
+__global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
+  extern __shared__ float smem[];
+  float* tok_mx = smem;
+  float* tok_sum = tok_mx + kRowsBM;
+  int* hist = reinterpret_cast<int*>(tok_sum + kRowsBM);
+  const int64_t t0 = int64_t(blockIdx.x) * kRowsBM;
+  const int rows = int(min<int64_t>(kRowsBM, a.m - t0));
+  for (int j = threadIdx.x; j < a.npad; j += kRouteThreads) hist[j] = 0;
+  __syncthreads();
+  const float* lg = a.logits + t0 * a.npad;
+  EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
+  route_rows(lg, a.npad, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
+  __syncthreads();
+  route_block_tail(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a);
+}
+
+// ------------------------------------------------------------------ launcher
+hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s) {
+  if (plan.mfma) {
+    dim3 g(ceil_div(plan.dpad, 64), ceil_div(plan.npad, 64));
+    hipLaunchKernelGGL(k_router_split, g, dim3(256), 0, s, a.w_r, const_cast<uint16_t*>(a.planes), a.d, a.n,
+                       plan.npad, plan.dpad);
+  }
+  const int nblk_fused = int(ceil_div64(a.m, kRouteBM));
+  if (plan.fused) {
+    const size_t lds = (size_t(kRouteBM) * (plan.npad + 1) + 2 * kRouteBM) * sizeof(float) + plan.npad * sizeof(int);
+    const int tiles = plan.npad / 32;
+    if (plan.mfma) {
+      if (tiles <= 4)
+        hipLaunchKernelGGL((k_route_fused<1, true>), dim3(nblk_fused), dim3(kRouteThreads), lds, s, a);
+      else
+        hipLaunchKernelGGL((k_route_fused<2, true>), dim3(nblk_fused), dim3(kRouteThreads), lds, s, a);
+    } else {
+      hipLaunchKernelGGL((k_route_fused<1, false>), dim3(nblk_fused), dim3(kRouteThreads), lds, s, a);
+    }
+  } else {
+    if (plan.mfma)
+      hipLaunchKernelGGL(k_route_logits_mfma, dim3(unsigned(ceil_div64(a.m, 128)), plan.npad / 128), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_route_logits_valu, dim3(unsigned(ceil_div64(a.m, 32)), plan.npad / 64), dim3(256), 0, s, a);
+    const size_t lds = 2 * kRowsBM * sizeof(float) + plan.npad * sizeof(int);
+    hipLaunchKernelGGL(k_route_rows, dim3(unsigned(ceil_div64(a.m, kRowsBM))), dim3(kRouteThreads), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

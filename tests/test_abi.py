@@ -1,0 +1,183 @@
+"""C-ABI contract of libmoe.so, checked on the host (no GPU needed).
+
+Loads the library, checks that it exports every entry point declared in
+include/moe.h, and that argument validation rejects bad calls before any
+HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import load_balanced_expert_amd as M
+from load_balanced_expert_amd import _lib as L
+from oracle import dispatch as OD
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from load_balanced_expert_amd import build
+        build.build()
+    return L.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"libmoe.so does not export {n}"
+    assert set(names) == set(L.SIGNATURES), "binding signatures out of sync with include/moe.h"
+
+
+def test_build_info(lib):
+    assert b"gfx950" in lib.moe_build_info()
+
+
+@pytest.mark.parametrize("m,n,cf", [(1024, 8, 1.25), (8192, 128, 1.0), (8192, 128, 1.25), (65536, 2048, 1.25),
+                                    (10, 1, 0.3), (7, 3, 0.1), (1000, 7, 1.1), (16, 4, 2.0), (5, 5, 0.0),
+                                    (123456, 37, 3.3333333)])
+def test_capacity_matches_oracle(lib, m, n, cf):
+    assert lib.moe_capacity(m, n, cf) == OD.capacity(m, n, cf)
+
+
+def test_capacity_rejects_invalid(lib):
+    assert lib.moe_capacity(-1, 4, 1.0) == -1
+    assert lib.moe_capacity(10, 0, 1.0) == -1
+    assert lib.moe_capacity(10, 4, -1.0) == -1
+    assert lib.moe_capacity(10, 4, float("nan")) == -1
+    assert lib.moe_capacity(10, 4, float("inf")) == -1
+    assert lib.moe_capacity(2 ** 40, 1, 1.0) == -1      # exceeds int32
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_str(s)
+    assert b"unknown" in lib.moe_status_str(99)
+
+
+def _sh(m=64, d=32, n=8, k=1, score=0, gate=0, xd=1):
+    return L.MoeShape(m, d, n, k, score, gate, xd)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("bad", [dict(m=0), dict(d=0), dict(n=0), dict(k=0), dict(k=9), dict(score=2),
+                                 dict(gate=5), dict(xd=3)])
+def test_invalid_shapes(lib, bad):
+    sh = _sh(**bad)
+    assert lib.moe_workspace_size(ctypes.byref(sh), -1, 0) == 0
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == L.MOE_ERR_INVALID_ARG
+
+
+def test_unsupported_sizes(lib):
+    sh = _sh(n=5000)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == L.MOE_ERR_UNSUPPORTED
+    sh = _sh(m=2 ** 31, k=1)
+    assert lib.moe_workspace_size(ctypes.byref(sh), -1, 0) == 0
+
+
+def test_null_pointers_rejected(lib):
+    sh = _sh()
+    assert lib.moe_route(ctypes.byref(sh), None, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.moe_dispatch(ctypes.byref(sh), -1, FAKE, None, FAKE, None, FAKE, None, None, FAKE, 1 << 30,
+                            None) == 1
+    assert lib.moe_dispatch(ctypes.byref(sh), -2, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, 1 << 30,
+                            None) == 1
+    # dispatched rows requested without x
+    assert lib.moe_dispatch(ctypes.byref(sh), -1, None, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 30,
+                            None) == 1
+    assert lib.moe_combine(ctypes.byref(sh), None, 1, FAKE, FAKE, None, FAKE, None) == 1
+    assert lib.moe_combine(ctypes.byref(sh), FAKE, 7, FAKE, FAKE, None, FAKE, None) == 1
+
+
+def test_workspace_too_small_or_misaligned(lib):
+    sh = _sh(m=1024, d=768, n=128)
+    need = lib.moe_workspace_size(ctypes.byref(sh), -1, 0)
+    assert need >= 65536
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1024, None)
+    assert st == L.MOE_ERR_WORKSPACE
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x1010),
+                       1 << 40, None)
+    assert st == L.MOE_ERR_WORKSPACE
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 1 << 40, None)
+    assert st == L.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_grows_with_capacity_and_ffn(lib):
+    sh = _sh(m=8192, d=768, n=128)
+    a = lib.moe_workspace_size(ctypes.byref(sh), 64, 0)
+    b = lib.moe_workspace_size(ctypes.byref(sh), 80, 0)
+    c = lib.moe_workspace_size(ctypes.byref(sh), 80, 3072)
+    assert 0 < a <= b < c
+    assert lib.moe_workspace_size(ctypes.byref(sh), -2, 0) == 0
+
+
+def test_stats_validation(lib):
+    assert lib.moe_stats(0, 8, 1, FAKE, None, 0.01, None, None, None, None, None, None, 0.001, None) == 1
+    assert lib.moe_stats(8, 8, 9, FAKE, None, 0.01, None, None, None, None, None, None, 0.001, None) == 1
+    assert lib.moe_stats(8, 8, 1, None, None, 0.01, None, None, None, None, None, None, 0.001, None) == 1
+    # global counts without global tokens
+    assert lib.moe_stats(8, 8, 1, FAKE, None, 0.01, None, None, None, FAKE, None, None, 0.001, None) == 1
+    # aux requested without prob_sum
+    assert lib.moe_stats(8, 8, 1, FAKE, None, 0.01, None, None, FAKE, None, None, None, 0.001, None) == 1
+    assert lib.moe_stats(8, 5000, 1, FAKE, None, 0.01, None, None, None, None, None, None, 0.001, None) == 2
+    assert lib.moe_global_aux(8, None, FAKE, FAKE, 1, 0.01, None, None, None, None) == 1
+    assert lib.moe_global_aux(8, FAKE, FAKE, None, 2, 0.01, None, None, None, None) == 1
+
+
+def test_balance_validation(lib):
+    big = 1 << 40
+    args = lambda m, n, k, it=1, mode=0, ex=0, ws=FAKE, wsb=big: (m, n, k, FAKE, FAKE, it, mode, ex, FAKE, FAKE,  # noqa
+                                                                   None, None, ws, wsb, None)
+    assert lib.moe_balance_duals(*args(10, 4, 1)) == 1          # (m*k) % n != 0
+    assert lib.moe_balance_duals(*args(8, 4, 4)) == 1           # k == n
+    assert lib.moe_balance_duals(*args(8, 4, 1, mode=2)) == 1
+    assert lib.moe_balance_duals(*args(8, 4, 1, it=2, mode=1)) == 1   # online takes one step
+    assert lib.moe_balance_duals(*args(8, 4, 1, mode=1, ex=1)) == 1   # exact is solve-only
+    assert lib.moe_balance_duals(*args(128, 128, 1, ex=1)) == 2      # completion limited to n <= 64
+    assert lib.moe_balance_duals(*args(64, 8, 1, wsb=100)) == 3
+    assert lib.moe_balance_workspace_size(64, 8, 8, 0) == 0
+    assert lib.moe_balance_workspace_size(4096, 64, 4, 1) > lib.moe_balance_workspace_size(4096, 64, 4, 0)
+
+
+def test_expert_ffn_validation(lib):
+    big = 1 << 40
+    assert lib.moe_expert_ffn(8, 48, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 2
+    assert lib.moe_expert_ffn(8, 64, 64, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 1
+    assert lib.moe_expert_ffn(8, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == 3
+
+
+def test_switch_layer_validation(lib):
+    sh = _sh(m=64, d=64, n=8, xd=0)
+    out = L.LayerOutputs()
+    out.out = FAKE
+    p = L.LayerParams(16, 1, 64, 0.01)                       # relu_ffn needs bf16 x
+    assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None,
+                                ctypes.byref(out), FAKE, 1 << 40, None) == 1
+    p = L.LayerParams(16, 7, 0, 0.01)
+    assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, None, None, None,
+                                ctypes.byref(out), FAKE, 1 << 40, None) == 1
+    out.out = None
+    p = L.LayerParams(16, 0, 0, 0.01)
+    assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, None, None, None,
+                                ctypes.byref(out), FAKE, 1 << 40, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(M.MoeError):
+        M.route(torch.zeros(4, 8), torch.zeros(8, 2), 1)

@@ -1,0 +1,155 @@
+"""GPU parity: moe_route (router GEMM, scores, top-k, gates, counts, score sums)
+against the float64 oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import router as OR
+from tests.gpu_util import DEV, assert_rel, check_selection, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+M = pytest.importorskip("load_balanced_expert_amd")
+
+
+def run_route(x, w_r, k, score="softmax", gate="prob", bias=None):
+    r = M.route(to_dev(x), to_dev(w_r), k, score=score, gate=gate,
+                bias=None if bias is None else to_dev(bias))
+    torch.cuda.synchronize()
+    return to_host(r.idx), to_host(r.gate), to_host(r.counts), to_host(r.prob_sum)
+
+
+def check_route(x, w_r, k, what, score="softmax", gate="prob", bias=None):
+    say(f"[route] {what}: m={x.shape[0]} d={x.shape[1]} n={w_r.shape[1]} k={k} {score} {gate} "
+        f"bias={'yes' if bias is not None else 'no'}")
+    idx, g, counts, psum = run_route(x, w_r, k, score, gate, bias)
+    ref = OR.route(x, w_r, k, score=score, bias=bias, gate=gate)
+    n = w_r.shape[1]
+    assert idx.min() >= 0 and idx.max() < n
+    flips = check_selection(idx, ref, what)
+    same = np.array([t not in flips for t in range(x.shape[0])])
+    assert_rel(g[same], ref.gate[same], 1e-5, f"{what} gates")
+    assert np.array_equal(counts, np.bincount(idx.reshape(-1), minlength=n)), f"{what}: counts != histogram of idx"
+    if not flips:
+        assert np.array_equal(counts, ref.counts)
+    assert_rel(psum, ref.prob_sum, 1e-5, f"{what} prob_sum", floor=1e-6 * x.shape[0] / n)
+    return idx, g, counts, psum, ref
+
+
+def test_tiny_switch_fp32():
+    inp = W.switch_inputs(W.TINY_SWITCH, 0)
+    check_route(inp.x, inp.w_r, 1, "tiny switch (fp32 x, vector-ALU product)")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_switch_base_ragged(seed):
+    spec = W.SWITCH_BASE.scaled(T=1000)
+    inp = W.switch_inputs(spec, seed)
+    check_route(inp.x, inp.w_r, 1, "switch-base ragged T=1000 (bf16x3 MFMA)")
+
+
+def test_switch_base_full():
+    inp = W.switch_inputs(W.SWITCH_BASE, 0)
+    check_route(inp.x, inp.w_r, 1, "switch-base T=8192 d=768 N=128")
+
+
+def test_padded_expert_count_and_odd_tokens():
+    spec = W.SwitchSpec("odd", T=333, d=96, N=40, w_r_std=0.05)
+    inp = W.switch_inputs(spec, 3)
+    check_route(inp.x, inp.w_r, 3, "N=40 k=3 T=333")
+
+
+def test_topk_renorm_gate():
+    spec = W.SwitchSpec("renorm", T=512, d=128, N=64, w_r_std=0.05)
+    inp = W.switch_inputs(spec, 4)
+    check_route(inp.x, inp.w_r, 4, "top-4 renormalised softmax gate", gate="renorm")
+
+
+def test_lossfree_micro_batch_with_bias():
+    spec = W.LOSSFREE
+    inp = W.lossfree_inputs(spec, 0)
+    x = inp.micro_batch(1)
+    g = np.random.default_rng(0)
+    bias = (g.integers(-5, 6, spec.N) * np.float32(1e-3)).astype(np.float32)
+    check_route(x, inp.w_r, spec.k, "loss-free micro-batch (sigmoid, top-8 of 256, bias)", score="sigmoid",
+                bias=bias)
+
+
+def test_sigmoid_without_bias():
+    spec = W.LOSSFREE.scaled(T=700, d=256)
+    inp = W.lossfree_inputs(spec, 1)
+    check_route(inp.micro_batch(0), inp.w_r, 8, "sigmoid top-8 no bias T=700", score="sigmoid")
+
+
+def test_softmax_with_bias():
+    spec = W.SwitchSpec("sbias", T=256, d=64, N=32, w_r_std=0.2)
+    inp = W.switch_inputs(spec, 5)
+    bias = np.linspace(-0.02, 0.02, 32).astype(np.float32)
+    check_route(inp.x, inp.w_r, 2, "softmax + bias (key = p + b)", bias=bias)
+
+
+def test_bf16_x_with_d_not_multiple_of_8():
+    spec = W.SwitchSpec("oddd", T=200, d=36, N=16, w_r_std=0.1)
+    inp = W.switch_inputs(spec, 6)
+    check_route(inp.x, inp.w_r, 2, "bf16 x, d=36 (vector-ALU product)")
+
+
+def test_large_expert_count_path():
+    spec = W.SwitchSpec("bign", T=777, d=256, N=600, w_r_std=0.05)
+    inp = W.switch_inputs(spec, 7)
+    check_route(inp.x, inp.w_r, 2, "N=600 (logits GEMM + row kernel)")
+
+
+def test_large_expert_count_fp32():
+    spec = W.SwitchSpec("bignf", T=100, d=40, N=300, x_dtype="f32", w_r_std=0.05)
+    inp = W.switch_inputs(spec, 8)
+    check_route(inp.x, inp.w_r, 1, "N=300 fp32 x (vector-ALU logits)")
+
+
+def test_ties_go_to_lower_index():
+    # duplicated router columns: every token sees equal logits for experts 2j and 2j+1
+    spec = W.SwitchSpec("ties", T=256, d=64, N=16, w_r_std=0.1)
+    inp = W.switch_inputs(spec, 9)
+    w = inp.w_r.copy()
+    w[:, 1::2] = w[:, 0::2]
+    idx, g, counts, _, ref = check_route(inp.x, w, 2, "exact ties")
+    assert np.all(idx[:, 0] % 2 == 0) and np.all(idx[:, 1] == idx[:, 0] + 1)
+
+
+def test_zero_router_uniform():
+    x = W.switch_inputs(W.TINY_SWITCH.scaled(x_dtype="bf16"), 0).x
+    idx, g, counts, psum = run_route(x, np.zeros((64, 8), np.float32), 1)
+    assert np.all(idx == 0) and np.all(g == np.float32(1 / 8))
+    assert counts.tolist() == [1024, 0, 0, 0, 0, 0, 0, 0]
+    assert np.all(psum == np.float32(1024 / 8))
+
+
+def test_repeat_is_bitwise_deterministic():
+    inp = W.switch_inputs(W.SWITCH_BASE.scaled(T=2048), 11)
+    a = run_route(inp.x, inp.w_r, 1)
+    b = run_route(inp.x, inp.w_r, 1)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("sample", [4096])
+def test_switch_c_full_size_sampled(sample):
+    """T=65536, d=1024, N=2048 at full size: every output checked on a token sample,
+    counts against the GPU's own indices, score sums against the full oracle."""
+    spec = W.SWITCH_C
+    inp = W.switch_inputs(spec, 0)
+    say("[route] switch-C full size on GPU")
+    idx, g, counts, psum = run_route(inp.x, inp.w_r, 1)
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(spec.T, sample, replace=False))
+    ref = OR.route(inp.x[toks], inp.w_r, 1)
+    flips = check_selection(idx[toks], ref, "switch-C sampled")
+    same = np.array([t not in flips for t in range(sample)])
+    assert_rel(g[toks][same], ref.gate[same], 1e-5, "switch-C gates")
+    assert np.array_equal(counts, np.bincount(idx.reshape(-1), minlength=spec.N))
+    assert counts.sum() == spec.T
+    psum_ref = np.zeros(spec.N)
+    for lo in range(0, spec.T, 8192):
+        psum_ref += OR.route(inp.x[lo:lo + 8192], inp.w_r, 1).prob_sum
+    assert_rel(psum, psum_ref, 1e-5, "switch-C prob_sum")
