@@ -110,6 +110,17 @@ const char* moe_build_info(void);
 
 /* ------------------------------------------------------------------ router */
 
+/* Bytes of the prepared router weight for moe_router_prepare (0 if invalid). */
+size_t moe_router_planes_bytes(int32_t d, int32_t n);
+
+/* moe_router_prepare — re-lays the fp32 router weight W_r [d, n] for the bf16
+ * matrix-core product of moe_route: three bf16 planes hi, mid, lo with
+ * hi + mid + lo == W_r exactly (each plane [n_pad, d_pad], expert-major, zero
+ * padded).  Prepare once per weight update and pass the planes to every
+ * moe_route call that uses this W_r (for example all micro-batches of a
+ * global batch).  planes: device buffer of moe_router_planes_bytes(d, n). */
+moe_status moe_router_prepare(int32_t d, int32_t n, const float* w_r, void* planes, void* stream);
+
 /* moe_route — router projection, score, top-k selection and load histogram.
  *   h = x · W_r with x upcast exactly to fp32 and fp32-accurate accumulation
  *   ([Switch review] "Switch Routing 메커니즘" Step 1, "선택적 정밀도 캐스팅":
@@ -120,6 +131,8 @@ const char* moe_build_info(void);
  *   token's k choices are written by descending key.
  * x        [m, d]   fp32 or bf16 (shape->x_dtype)
  * w_r      [d, n]   fp32 router weight
+ * w_planes moe_router_prepare(w_r) output, or NULL (then moe_route prepares it
+ *          in the workspace on every call)
  * bias     [n]      fp32 or NULL (ranks only; never part of the gate)
  * idx      [m, k]   int32 out: chosen experts
  * gate     [m, k]   fp32 out: gate values (moe_gate)
@@ -127,8 +140,8 @@ const char* moe_build_info(void);
  * prob_sum [n]      fp32 out or NULL: Σ_t score_j(t) (softmax p or sigmoid ρ),
  *                   the numerator of P_j ([Switch review] "로드 밸런싱 손실")
  * Limits: 1 <= k <= n <= 4096, d >= 1, m >= 1. */
-moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* bias,
-                     int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
+                     const float* bias, int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ statistics */
@@ -246,6 +259,11 @@ typedef struct {
   int32_t expert_kind;   /* moe_expert_kind */
   int32_t d_ff;          /* FFN hidden width (relu_ffn) */
   float alpha;           /* aux-loss weight */
+  /* NULL, or 6 hipEvent_t recorded on the stream at the stage boundaries:
+   * [0] start, [1] router weight prepared, [2] routed (with statistics and
+   * capacity prefix sums), [3] dispatched, [4] expert done, [5] combined.
+   * Any entry may be NULL. */
+  void* const* stage_events;
 } moe_layer_params;
 
 /* Device output pointers of moe_switch_layer.  `out` is required; every other

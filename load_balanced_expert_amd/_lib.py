@@ -23,7 +23,8 @@ class MoeShape(ctypes.Structure):
 
 
 class LayerParams(ctypes.Structure):
-    _fields_ = [("capacity", c_int32), ("expert_kind", c_int32), ("d_ff", c_int32), ("alpha", c_float)]
+    _fields_ = [("capacity", c_int32), ("expert_kind", c_int32), ("d_ff", c_int32), ("alpha", c_float),
+                ("stage_events", POINTER(c_void_p))]
 
 
 class LayerOutputs(ctypes.Structure):
@@ -41,7 +42,9 @@ SIGNATURES = {
     "moe_capacity": (c_int32, [c_int64, c_int32, c_double]),
     "moe_status_str": (c_char_p, [c_int32]),
     "moe_build_info": (c_char_p, []),
-    "moe_route": (c_int32, [POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_router_planes_bytes": (c_size_t, [c_int32, c_int32]),
+    "moe_router_prepare": (c_int32, [c_int32, c_int32, _P, _P, _P]),
+    "moe_route": (c_int32, [POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_stats": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_float, _P, _P, _P, _P, _P, _P, c_float, _P]),
     "moe_global_aux": (c_int32, [c_int32, _P, _P, _P, c_int32, c_float, _P, _P, _P, _P]),
     "moe_balance_duals": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_int32, c_int32, c_int32,

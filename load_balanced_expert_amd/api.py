@@ -102,20 +102,37 @@ class RouteOut:
     prob_sum: Optional[torch.Tensor]
 
 
+def router_prepare(w_r: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Exact three-way bf16 split of the fp32 router weight, reusable by route(w_planes=...)."""
+    _on_device(w_r, out)
+    d, n = w_r.shape
+    nbytes = int(_lib().moe_router_planes_bytes(int(d), int(n)))
+    planes = out if out is not None else torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w_r.device)
+    if planes.numel() * planes.element_size() < nbytes:
+        raise MoeError("router planes buffer too small")
+    _check(_lib().moe_router_prepare(int(d), int(n), _ptr(w_r), _ptr(planes), _stream(w_r.device)),
+           "moe_router_prepare")
+    return planes
+
+
 def route(x: torch.Tensor, w_r: torch.Tensor, k: int, score: str = "softmax", gate: str = "prob",
-          bias: Optional[torch.Tensor] = None, prob_sum: bool = True) -> RouteOut:
-    _on_device(x, w_r, bias)
+          bias: Optional[torch.Tensor] = None, prob_sum: bool = True, out: Optional[RouteOut] = None,
+          w_planes: Optional[torch.Tensor] = None) -> RouteOut:
+    _on_device(x, w_r, bias, w_planes)
     m, d = x.shape
     n = w_r.shape[1]
     dev = x.device
     sh = shape(m, d, n, k, score, gate, _dtype_code(x))
-    idx = torch.empty((m, k), dtype=torch.int32, device=dev)
-    g = torch.empty((m, k), dtype=torch.float32, device=dev)
-    counts = torch.empty(n, dtype=torch.int32, device=dev)
-    ps = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum else None
+    if out is not None:
+        idx, g, counts, ps = out.idx, out.gate, out.counts, out.prob_sum
+    else:
+        idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+        g = torch.empty((m, k), dtype=torch.float32, device=dev)
+        counts = torch.empty(n, dtype=torch.int32, device=dev)
+        ps = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum else None
     ws, wsb = _ws_args(workspace_size(sh), dev)
-    _check(_lib().moe_route(ctypes.byref(sh), _ptr(x), _ptr(w_r), _ptr(bias), _ptr(idx), _ptr(g), _ptr(counts),
-                            _ptr(ps), ws, wsb, _stream(dev)), "moe_route")
+    _check(_lib().moe_route(ctypes.byref(sh), _ptr(x), _ptr(w_r), _ptr(w_planes), _ptr(bias), _ptr(idx), _ptr(g),
+                            _ptr(counts), _ptr(ps), ws, wsb, _stream(dev)), "moe_route")
     return RouteOut(idx, g, counts, ps)
 
 
@@ -129,13 +146,16 @@ class StatsOut:
 
 def stats(m: int, k: int, counts: torch.Tensor, prob_sum: Optional[torch.Tensor], alpha: float = 1e-2,
           global_counts: Optional[torch.Tensor] = None, global_tokens: Optional[torch.Tensor] = None,
-          bias: Optional[torch.Tensor] = None, gamma: float = 1e-3) -> StatsOut:
+          bias: Optional[torch.Tensor] = None, gamma: float = 1e-3, out: Optional[StatsOut] = None) -> StatsOut:
     _on_device(counts, prob_sum, global_counts, global_tokens, bias)
     n = counts.shape[0]
     dev = counts.device
-    f = torch.empty(n, dtype=torch.float32, device=dev)
-    P = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum is not None else None
-    aux = torch.empty(1, dtype=torch.float32, device=dev) if prob_sum is not None else None
+    if out is not None:
+        f, P, aux = out.f, out.P, out.aux
+    else:
+        f = torch.empty(n, dtype=torch.float32, device=dev)
+        P = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum is not None else None
+        aux = torch.empty(1, dtype=torch.float32, device=dev) if prob_sum is not None else None
     _check(_lib().moe_stats(int(m), int(n), int(k), _ptr(counts), _ptr(prob_sum), float(alpha), _ptr(f), _ptr(P),
                             _ptr(aux), _ptr(global_counts), _ptr(global_tokens), _ptr(bias), float(gamma),
                             _stream(dev)), "moe_stats")
@@ -192,7 +212,7 @@ class DispatchOut:
 
 
 def dispatch(x: Optional[torch.Tensor], idx: torch.Tensor, n: int, capacity: int = -1, d: Optional[int] = None,
-             copy_rows: bool = True) -> DispatchOut:
+             copy_rows: bool = True, out: Optional[DispatchOut] = None) -> DispatchOut:
     _on_device(x, idx)
     m, k = idx.shape
     dev = idx.device
@@ -202,13 +222,17 @@ def dispatch(x: Optional[torch.Tensor], idx: torch.Tensor, n: int, capacity: int
     else:
         xd = L.MOE_BF16
     sh = shape(m, d or 1, n, k, x_dtype=xd)
-    t2r = torch.empty((m, k), dtype=torch.int32, device=dev)
-    drop = torch.empty((m, k), dtype=torch.uint8, device=dev)
-    offs = torch.empty(n + 1, dtype=torch.int32, device=dev)
-    r2t = torch.full((m * k,), -1, dtype=torch.int32, device=dev)
     rows_bound = m * k if capacity < 0 else min(m * k, capacity * n)
-    disp = (torch.empty((rows_bound, d), dtype=x.dtype, device=dev)
-            if (x is not None and copy_rows) else None)
+    if out is not None:
+        t2r, drop, offs, r2t, disp = (out.token_to_row, out.drop_mask, out.expert_offsets, out.row_to_token,
+                                      out.dispatched)
+    else:
+        t2r = torch.empty((m, k), dtype=torch.int32, device=dev)
+        drop = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        offs = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        r2t = torch.full((m * k,), -1, dtype=torch.int32, device=dev)
+        disp = (torch.empty((rows_bound, d), dtype=x.dtype, device=dev)
+                if (x is not None and copy_rows) else None)
     ws, wsb = _ws_args(workspace_size(sh, capacity), dev)
     _check(_lib().moe_dispatch(ctypes.byref(sh), int(capacity), _ptr(x), _ptr(idx), _ptr(t2r), _ptr(drop),
                                _ptr(offs), _ptr(r2t), _ptr(disp), ws, wsb, _stream(dev)), "moe_dispatch")
@@ -217,11 +241,11 @@ def dispatch(x: Optional[torch.Tensor], idx: torch.Tensor, n: int, capacity: int
 
 # ------------------------------------------------------------------ expert FFN
 def expert_ffn(dispatched: torch.Tensor, expert_offsets: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
-               rows_max: int) -> torch.Tensor:
+               rows_max: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     _on_device(dispatched, expert_offsets, w1, w2)
     n, d_ff, d = w1.shape
     dev = dispatched.device
-    y = torch.empty((dispatched.shape[0], d), dtype=torch.bfloat16, device=dev)
+    y = out if out is not None else torch.empty((dispatched.shape[0], d), dtype=torch.bfloat16, device=dev)
     need = int(_lib().moe_expert_ffn_workspace_size(int(n), int(rows_max), int(d_ff)))
     ws, wsb = _ws_args(need, dev)
     _check(_lib().moe_expert_ffn(int(n), int(d), int(d_ff), int(rows_max), _ptr(expert_offsets), _ptr(dispatched),
@@ -231,14 +255,15 @@ def expert_ffn(dispatched: torch.Tensor, expert_offsets: torch.Tensor, w1: torch
 
 # ------------------------------------------------------------------ combine
 def combine(y: torch.Tensor, gate: torch.Tensor, token_to_row: torch.Tensor, residual: Optional[torch.Tensor],
-            out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+            out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     _on_device(y, gate, token_to_row, residual)
     m, k = token_to_row.shape
     dev = y.device
     d = y.shape[1]
     odt = residual.dtype if residual is not None else (out_dtype or torch.float32)
     sh = shape(m, d, k, k, x_dtype=L.MOE_BF16 if odt == torch.bfloat16 else L.MOE_F32)
-    out = torch.empty((m, d), dtype=odt, device=dev)
+    if out is None:
+        out = torch.empty((m, d), dtype=odt, device=dev)
     _check(_lib().moe_combine(ctypes.byref(sh), _ptr(y), _dtype_code(y), _ptr(gate), _ptr(token_to_row),
                               _ptr(residual), _ptr(out), _stream(dev)), "moe_combine")
     return out
@@ -278,7 +303,9 @@ def allocate_layer_outputs(m, d, n, k, rows_bound, x_dtype, ffn: bool, device) -
 def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int = -1, alpha: float = 1e-2,
                  w1: Optional[torch.Tensor] = None, w2: Optional[torch.Tensor] = None,
                  bias: Optional[torch.Tensor] = None, score: str = "softmax", gate: str = "prob",
-                 outputs: Optional[LayerOut] = None) -> LayerOut:
+                 outputs: Optional[LayerOut] = None, stage_events=None) -> LayerOut:
+    """stage_events: optional list of 6 torch.cuda.Event (timing enabled) recorded at the stage
+    boundaries (start, router prepared, routed, dispatched, expert done, combined)."""
     _on_device(x, w_r, w1, w2, bias)
     m, d = x.shape
     n = w_r.shape[1]
@@ -290,7 +317,14 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
     o = outputs or allocate_layer_outputs(m, d, n, k, rows_bound, x.dtype, ffn, dev)
     lo = L.LayerOutputs(*[(_ptr(getattr(o, f)) if getattr(o, f) is not None else None)
                           for f, _ in L.LayerOutputs._fields_])
-    params = L.LayerParams(int(capacity), L.EXPERTS["relu_ffn" if ffn else "identity"], int(d_ff), float(alpha))
+    evs = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise MoeError("stage_events takes 6 events")
+        evs = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None
+                                      for e in stage_events])
+    params = L.LayerParams(int(capacity), L.EXPERTS["relu_ffn" if ffn else "identity"], int(d_ff), float(alpha),
+                           ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p)) if evs is not None else None)
     ws, wsb = _ws_args(workspace_size(sh, capacity, d_ff), dev)
     _check(_lib().moe_switch_layer(ctypes.byref(sh), ctypes.byref(params), _ptr(x), _ptr(w_r), _ptr(w1), _ptr(w2),
                                    _ptr(bias), ctypes.byref(lo), ws, wsb, _stream(dev)), "moe_switch_layer")

@@ -18,6 +18,7 @@ struct Layout {
   size_t route_end, dispatch_end, total;
   RoutePlan rp;
   int64_t pairs, rows_bound;
+  int route_ct, disp_ct, nch, sup;
 };
 
 bool shape_valid(const moe_shape* s) {
@@ -49,7 +50,11 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   L.planes = o; o += al(L.rp.planes_bytes);
   L.logits = o; o += al(L.rp.logits_bytes);
   L.route_end = o;
-  L.chunks = o; o += al(dispatch_ws_bytes(L.pairs, s.n));
+  L.route_ct = route_chunk_tokens(L.rp);
+  L.disp_ct = dispatch_chunk_tokens(L.route_ct, s.k);
+  L.nch = int(ceil_div64(s.m, L.disp_ct));
+  L.sup = super_chunk(L.nch);
+  L.chunks = o; o += al(dispatch_ws_bytes(s.m, s.k, s.n, L.disp_ct));
   L.r2t = o; o += al(size_t(L.pairs) * 4);
   L.dispatch_end = o;
   L.hidden = o; o += al(d_ff > 0 ? ffn_ws_bytes(L.rows_bound, d_ff) : 0);
@@ -84,8 +89,18 @@ int32_t effective_capacity(int32_t capacity, int64_t pairs) {
   return capacity < 0 ? int32_t(std::min<int64_t>(pairs, 0x7FFFFFFF)) : capacity;
 }
 
-moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const float* w_r, const float* bias,
-                    int32_t* idx, float* gate, int32_t* counts, float* prob_sum, void* ws, hipStream_t st) {
+// Work the route kernel's last workgroup can do for the stages after it.
+struct RouteExtras {
+  float* f = nullptr;
+  float* P = nullptr;
+  float* aux = nullptr;
+  float alpha = 0.f;
+  const DispatchArgs* disp = nullptr;   // capacity prefix sums for this dispatch
+};
+
+moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const float* w_r, const void* w_planes,
+                    const float* bias, int32_t* idx, float* gate, int32_t* counts, float* prob_sum, void* ws,
+                    hipStream_t st, const RouteExtras& ex = RouteExtras()) {
   RouteArgs a{};
   a.x = x;
   a.m = s.m;
@@ -99,12 +114,23 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
   a.x_bf16 = s.x_dtype == MOE_BF16;
   a.w_r = w_r;
   a.bias = bias;
-  a.planes = at<uint16_t>(ws, L.planes);
+  a.planes = w_planes ? static_cast<const uint16_t*>(w_planes) : at<uint16_t>(ws, L.planes);
+  a.planes_ready = w_planes != nullptr;
   a.logits = at<float>(ws, L.logits);
   a.idx = idx;
   a.gate_out = gate;
   a.counts = counts;
   a.prob_sum = prob_sum;
+  a.want_psum = prob_sum != nullptr || ex.P != nullptr || ex.aux != nullptr;
+  a.f = ex.f;
+  a.P = ex.P;
+  a.aux = ex.aux;
+  a.alpha = ex.alpha;
+  if (ex.disp) {
+    a.chunk_counts = ex.disp->chunk_counts;
+    a.prefix = PrefixArgs{ex.disp->chunk_counts, ex.disp->nch, ex.disp->sup, s.n, ex.disp->capacity,
+                          ex.disp->expert_offsets, ex.disp->super_prefix};
+  }
   a.psum_acc = ctl_psum(ws);
   a.cnt_acc = ctl_cnt(ws);
   a.done = ctl_ticket(ws, kTicketRoute);
@@ -113,9 +139,8 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
   return hip_status(launch_route(rp, a, st));
 }
 
-moe_status do_dispatch(const moe_shape& s, const Layout& L, int32_t capacity, const void* x, const int32_t* idx,
-                       int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* r2t, void* disp, void* ws,
-                       hipStream_t st) {
+DispatchArgs dispatch_args(const moe_shape& s, const Layout& L, int32_t capacity, const void* x, const int32_t* idx,
+                           int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* r2t, void* disp, void* ws) {
   DispatchArgs a{};
   a.idx = idx;
   a.pairs = L.pairs;
@@ -123,17 +148,28 @@ moe_status do_dispatch(const moe_shape& s, const Layout& L, int32_t capacity, co
   a.n = s.n;
   a.nbits = bits_for(s.n);
   a.capacity = effective_capacity(capacity, L.pairs);
+  a.chunk_tokens = L.disp_ct;
+  a.nch = L.nch;
+  a.sup = L.sup;
   a.chunk_counts = at<int32_t>(ws, L.chunks);
+  a.super_prefix = at<int32_t>(ws, L.chunks + al(size_t(L.nch) * s.n * sizeof(int32_t)));
   a.token_to_row = t2r;
   a.drop_mask = drop;
   a.expert_offsets = offs;
-  a.row_to_token = r2t ? r2t : (disp ? at<int32_t>(ws, L.r2t) : nullptr);
+  a.row_to_token = r2t;
   a.x = x;
   a.dispatched = disp;
   a.row_bytes = int64_t(s.d) * x_esz(s);
-  a.max_rows = L.rows_bound;
   a.done = ctl_ticket(ws, kTicketDispatch);
-  return hip_status(launch_dispatch(a, st));
+  a.cnt_acc = ctl_cnt(ws);
+  return a;
+}
+
+moe_status do_dispatch(const moe_shape& s, const Layout& L, int32_t capacity, const void* x, const int32_t* idx,
+                       int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* r2t, void* disp, void* ws,
+                       bool prefix_ready, hipStream_t st) {
+  const DispatchArgs a = dispatch_args(s, L, capacity, x, idx, t2r, drop, offs, r2t, disp, ws);
+  return hip_status(launch_dispatch(a, prefix_ready, st));
 }
 
 }  // namespace
@@ -184,14 +220,29 @@ const char* moe_status_str(int32_t st) {
 
 const char* moe_build_info(void) { return "libmoe 0.1 gfx950"; }
 
-moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* bias, int32_t* idx,
-                     float* gate, int32_t* counts, float* prob_sum, void* ws, size_t ws_bytes, void* stream) {
+size_t moe_router_planes_bytes(int32_t d, int32_t n) {
+  if (d < 1 || n < 1 || n > kMaxExperts) return 0;
+  return route_plan(1, d, n, true).planes_bytes;
+}
+
+moe_status moe_router_prepare(int32_t d, int32_t n, const float* w_r, void* planes, void* stream) {
+  if (d < 1 || n < 1 || !w_r || !planes) return MOE_ERR_INVALID_ARG;
+  if (n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  const RoutePlan rp = route_plan(1, d, n, true);
+  return hip_status(launch_router_prepare(rp, d, n, w_r, static_cast<uint16_t*>(planes),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes, const float* bias,
+                     int32_t* idx, float* gate, int32_t* counts, float* prob_sum, void* ws, size_t ws_bytes,
+                     void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!x || !w_r || !idx || !gate || !counts) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape, -1, 0);
   if (!ws_ok(ws, ws_bytes, L.route_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
-  return do_route(*shape, L, x, w_r, bias, idx, gate, counts, prob_sum, ws, static_cast<hipStream_t>(stream));
+  return do_route(*shape, L, x, w_r, w_planes, bias, idx, gate, counts, prob_sum, ws,
+                  static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, const float* prob_sum, float alpha,
@@ -260,7 +311,7 @@ moe_status moe_dispatch(const moe_shape* shape, int32_t capacity, const void* x,
   const Layout L = layout(*shape, capacity, 0);
   if (!ws_ok(ws, ws_bytes, L.dispatch_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
   return do_dispatch(*shape, L, capacity, x, idx, token_to_row, drop_mask, expert_offsets, row_to_token, dispatched,
-                     ws, static_cast<hipStream_t>(stream));
+                     ws, false, static_cast<hipStream_t>(stream));
 }
 
 size_t moe_expert_ffn_workspace_size(int32_t n, int32_t rows_max, int32_t d_ff) {
@@ -315,15 +366,34 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   int32_t* t2r = o->token_to_row ? o->token_to_row : at<int32_t>(ws, L.t2r);
   uint8_t* drop = o->drop_mask ? o->drop_mask : at<uint8_t>(ws, L.drop);
   int32_t* offs = o->expert_offsets ? o->expert_offsets : at<int32_t>(ws, L.offs);
-  int32_t* r2t = o->row_to_token ? o->row_to_token : at<int32_t>(ws, L.r2t);
   void* disp = o->dispatched ? o->dispatched : at<void>(ws, L.disp);
   void* y = ffn ? (o->y ? o->y : at<void>(ws, L.y)) : disp;
 
-  if ((st = do_route(sh, L, x, w_r, bias, idx, gate, counts, psum, ws, s)) != MOE_OK) return st;
-  if ((st = hip_status(launch_stats(sh.m, sh.n, sh.k, counts, psum, p->alpha, f, P, aux, nullptr, nullptr, nullptr,
-                                    0.f, s))) != MOE_OK)
-    return st;
-  if ((st = do_dispatch(sh, L, p->capacity, x, idx, t2r, drop, offs, r2t, disp, ws, s)) != MOE_OK) return st;
+  auto mark = [&](int i) {
+    if (p->stage_events && p->stage_events[i]) hipEventRecord(static_cast<hipEvent_t>(p->stage_events[i]), s);
+  };
+  // route (+ load statistics + per-chunk counts and capacity prefix sums in its last workgroup), then
+  // slots + permute-dispatch in one kernel
+  const DispatchArgs da = dispatch_args(sh, L, p->capacity, x, idx, t2r, drop, offs, o->row_to_token, disp, ws);
+  RouteExtras ex;
+  ex.f = f;
+  ex.P = P;
+  ex.aux = aux;
+  ex.alpha = p->alpha;
+  const bool fused_prefix = L.disp_ct == L.route_ct;
+  if (fused_prefix) ex.disp = &da;
+  mark(0);
+  const void* planes = nullptr;
+  if (L.rp.mfma && (reinterpret_cast<uintptr_t>(x) % 16) == 0) {
+    if ((st = hip_status(launch_router_prepare(L.rp, sh.d, sh.n, w_r, at<uint16_t>(ws, L.planes), s))) != MOE_OK)
+      return st;
+    planes = at<void>(ws, L.planes);
+  }
+  mark(1);
+  if ((st = do_route(sh, L, x, w_r, planes, bias, idx, gate, counts, psum, ws, s, ex)) != MOE_OK) return st;
+  mark(2);
+  if ((st = hip_status(launch_dispatch(da, fused_prefix, s))) != MOE_OK) return st;
+  mark(3);
   if (ffn) {
     const int32_t rows_max = effective_capacity(p->capacity, L.pairs);
     if ((st = hip_status(launch_expert_ffn(sh.n, sh.d, p->d_ff, rows_max, offs, static_cast<const uint16_t*>(disp),
@@ -331,8 +401,11 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
                                            at<uint16_t>(ws, L.hidden), static_cast<uint16_t*>(y), s))) != MOE_OK)
       return st;
   }
-  return hip_status(launch_combine(sh.m, sh.d, sh.k, y, ffn ? true : sh.x_dtype == MOE_BF16, gate, t2r, x, o->out,
-                                   sh.x_dtype == MOE_BF16, s));
+  mark(4);
+  st = hip_status(launch_combine(sh.m, sh.d, sh.k, y, ffn ? true : sh.x_dtype == MOE_BF16, gate, t2r, x, o->out,
+                                 sh.x_dtype == MOE_BF16, s));
+  mark(5);
+  return st;
 }
 
 }  // extern "C"

@@ -8,26 +8,28 @@
 //
 // The slot of pair p = (t, r) is its rank among earlier pairs (token-major)
 // with the same expert.  Atomic return order is not deterministic, so ranks
-// come from counting instead:
-//   1. histogram kernel: per-chunk (1024 pairs) expert counts in LDS; the
-//      last block turns them into per-chunk exclusive bases (scan over chunks
-//      for each expert), clamps totals at the capacity and scans those into
-//      the expert offsets;
-//   2. rank kernel: inside a chunk, each wave ranks its 64-pair groups with a
-//      match-any built from ballots over the expert-id bits; per-wave counts
-//      in LDS give the offset of each wave inside the chunk;
-//   3. copy kernel: every kept row is copied with 16-byte loads and stores.
+// come from counting instead.  Tokens are cut into chunks of `chunk_tokens`
+// (the route workgroup size, so the route kernel can produce the counts):
+//   1. per-chunk dense expert counts and totals (from the route kernel, or
+//      from the histogram kernel here); the last workgroup turns them into
+//      expert offsets and super-chunk prefix sums (prefix.hpp);
+//   2. one workgroup per chunk: wave 0 ranks the chunk's pairs in order with
+//      a match-any built from ballots over the expert-id bits and per-expert
+//      LDS counters; every pair adds its chunk base (a super-chunk prefix plus
+//      at most sup-1 chunk counts) and, if kept, its expert offset; then the
+//      whole workgroup copies the chunk's kept rows with 16-byte accesses.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "prefix.hpp"
 
 namespace moe {
 
 constexpr int kDispThreads = 256;
-constexpr int kPairsPerWave = kDispChunk / (kDispThreads / 64);  // 256
 
-size_t dispatch_ws_bytes(int64_t pairs, int n) {
-  const int64_t nch = ceil_div64(pairs, kDispChunk);
-  return size_t(nch) * n * sizeof(int32_t);
+size_t dispatch_ws_bytes(int64_t m, int k, int n, int chunk_tokens) {
+  const int64_t nch = ceil_div64(m, chunk_tokens);
+  (void)k;
+  return size_t(nch) * n * sizeof(int32_t) + size_t(16) * n * sizeof(int32_t) + 256;
 }
 
 __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
@@ -35,168 +37,107 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
   int* hist = lds;                  // [n]
   const int n = a.n;
   const int64_t c = blockIdx.x;
-  const int nch = gridDim.x;
   for (int j = threadIdx.x; j < n; j += kDispThreads) hist[j] = 0;
   __syncthreads();
-  const int64_t p0 = c * kDispChunk;
-  for (int u = 0; u < kDispChunk / kDispThreads; ++u) {
-    const int64_t p = p0 + u * kDispThreads + threadIdx.x;
-    if (p < a.pairs) {
-      const int e = a.idx[p];
-      if (unsigned(e) < unsigned(n)) atomicAdd(&hist[e], 1);   // ids outside [0, n) are dropped
-    }
+  const int64_t p0 = c * a.chunk_tokens * a.k;
+  const int64_t p1 = min<int64_t>(a.pairs, p0 + int64_t(a.chunk_tokens) * a.k);
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += kDispThreads) {
+    const int e = a.idx[p];
+    if (unsigned(e) < unsigned(n)) atomicAdd(&hist[e], 1);   // ids outside [0, n) are dropped
   }
   __syncthreads();
-  int32_t* cc = a.chunk_counts + c * n;
-  for (int j = threadIdx.x; j < n; j += kDispThreads) cc[j] = hist[j];
-
-  // last block: exclusive scan over chunks per expert, capacity clamp, offsets
+  for (int j = threadIdx.x; j < n; j += kDispThreads) {
+    const int v = hist[j];
+    a.chunk_counts[c * n + j] = v;
+    if (v) atomicAdd(a.cnt_acc + j, uint32_t(v));
+  }
   __shared__ int s_last;
+  __shared__ int part[kDispThreads / 64];
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1u) == unsigned(nch) - 1;
+  if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1u) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  int* kept = lds;  // reuse: [n]
-  for (int j = threadIdx.x; j < n; j += kDispThreads) {
-    int run = 0;
-    for (int cc2 = 0; cc2 < nch; ++cc2) {
-      int32_t* q = a.chunk_counts + int64_t(cc2) * n + j;
-      const int v = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *q = run;
-      run += v;
-    }
-    kept[j] = min(run, a.capacity);
-  }
+  for (int j = threadIdx.x; j < n; j += kDispThreads) hist[j] = int(atomicExch(a.cnt_acc + j, 0u));
   __syncthreads();
-  // exclusive scan of kept[0..n) into expert_offsets (n <= 4096: 16 per thread)
-  __shared__ int part[kDispThreads];
-  const int per = ceil_div(n, kDispThreads);
-  const int j0 = threadIdx.x * per;
-  int s = 0;
-  for (int j = j0; j < min(j0 + per, n); ++j) s += kept[j];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int t = 0; t < kDispThreads; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
-    }
-    a.expert_offsets[n] = run;
-  }
-  __syncthreads();
-  int run = part[threadIdx.x];
-  for (int j = j0; j < min(j0 + per, n); ++j) {
-    a.expert_offsets[j] = run;
-    run += kept[j];
-  }
+  PrefixArgs pa{a.chunk_counts, a.nch, a.sup, n, a.capacity, a.expert_offsets, a.super_prefix};
+  dispatch_prefix(pa, hist, part, kDispThreads);
   if (threadIdx.x == 0) atomicExch(a.done, 0u);
 }
 
-__global__ __launch_bounds__(kDispThreads) void k_disp_rank(DispatchArgs a) {
-  extern __shared__ uint16_t whist[];   // [4][n] per-wave counts, then per-wave bases
-  const int n = a.n;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int j = threadIdx.x; j < 4 * n; j += kDispThreads) whist[j] = 0;
-  __syncthreads();
-  const int64_t pw = int64_t(blockIdx.x) * kDispChunk + int64_t(wave) * kPairsPerWave;
-  uint16_t* wh = whist + wave * n;
-  uint64_t peers[kPairsPerWave / 64];
-  int ex[kPairsPerWave / 64];
-#pragma unroll
-  for (int it = 0; it < kPairsPerWave / 64; ++it) {
-    const int64_t p = pw + it * 64 + lane;
-    const bool inside = p < a.pairs;
-    const int e0 = inside ? a.idx[p] : 0;
-    const bool valid = inside && unsigned(e0) < unsigned(n);
-    const int e = valid ? e0 : 0;
-    const uint64_t active = __ballot(valid);
-    const uint64_t pr = match_any(uint32_t(e), a.nbits, active);
-    ex[it] = e;
-    peers[it] = pr;
-    if (valid && (pr & lanemask_lt()) == 0) wh[e] = uint16_t(wh[e] + __popcll(pr));
-  }
-  __syncthreads();
-  for (int j = threadIdx.x; j < n; j += kDispThreads) {
-    int run = 0;
-    for (int w = 0; w < 4; ++w) {
-      const int v = whist[w * n + j];
-      whist[w * n + j] = uint16_t(run);
-      run += v;
-    }
-  }
-  __syncthreads();
-  const int32_t* base = a.chunk_counts + int64_t(blockIdx.x) * n;
-#pragma unroll
-  for (int it = 0; it < kPairsPerWave / 64; ++it) {
-    const int64_t p = pw + it * 64 + lane;
-    const uint64_t pr = peers[it];
-    const bool inside = p < a.pairs;
-    const bool valid = inside && (pr >> lane) & 1;
-    const int e = ex[it];
-    int slot = 0;
-    if (valid) slot = base[e] + wh[e] + __popcll(pr & lanemask_lt());
-    // every lane has read wh[e] above before the group leader advances it
-    __builtin_amdgcn_wave_barrier();
-    if (valid && (pr & lanemask_lt()) == 0) wh[e] = uint16_t(wh[e] + __popcll(pr));
-    if (inside && !valid) {
-      a.token_to_row[p] = -1;
-      if (a.drop_mask) a.drop_mask[p] = 1;
-    }
-    if (valid) {
-      const bool kept = slot < a.capacity;
-      const int row = kept ? a.expert_offsets[e] + slot : -1;
-      a.token_to_row[p] = row;
-      if (a.drop_mask) a.drop_mask[p] = kept ? 0 : 1;
-      if (kept && a.row_to_token) a.row_to_token[row] = int32_t(p / a.k);
-    }
-  }
-}
-
 template <typename V>
-__global__ __launch_bounds__(256) void k_disp_copy(const char* __restrict__ x, char* __restrict__ out,
-                                                   const int32_t* __restrict__ row_to_token,
-                                                   const int32_t* __restrict__ offsets_end, int64_t vpr,
-                                                   int64_t items) {
-  const int64_t total_rows = *offsets_end;
-  const int64_t limit = min<int64_t>(items, total_rows * vpr);
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < limit; i += int64_t(gridDim.x) * 256) {
-    const int64_t row = i / vpr, v = i - row * vpr;
-    const int64_t t = row_to_token[row];
-    reinterpret_cast<V*>(out)[row * vpr + v] = reinterpret_cast<const V*>(x)[t * vpr + v];
+__global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a) {
+  extern __shared__ int lds[];
+  const int n = a.n;
+  const int cp = a.chunk_tokens * a.k;          // pairs per chunk
+  int* cnt = lds;                                // [n] running counts inside the chunk
+  int* lslot = cnt + n;                          // [cp] slot inside the chunk (-1: invalid id)
+  int* lrow = lslot + cp;                        // [cp] dispatched row (-1: dropped)
+  const int c = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t p0 = int64_t(c) * cp;
+  const int np = int(min<int64_t>(cp, a.pairs - p0));
+  for (int j = threadIdx.x; j < n; j += kDispThreads) cnt[j] = 0;
+  __syncthreads();
+  if (wave == 0) {
+    for (int g = 0; g < np; g += 64) {
+      const bool inside = g + lane < np;
+      const int e0 = inside ? a.idx[p0 + g + lane] : 0;
+      const bool valid = inside && unsigned(e0) < unsigned(n);
+      const int e = valid ? e0 : 0;
+      const uint64_t active = __ballot(valid);
+      const uint64_t pr = match_any(uint32_t(e), a.nbits, active);
+      const int before = valid ? cnt[e] : 0;
+      // every lane has read cnt[e] before the group's first lane advances it
+      __builtin_amdgcn_wave_barrier();
+      if (valid && (pr & lanemask_lt()) == 0) cnt[e] = before + __popcll(pr);
+      if (inside) lslot[g + lane] = valid ? before + __popcll(pr & lanemask_lt()) : -1;
+    }
+  }
+  __syncthreads();
+  const int s = c / a.sup;
+  for (int q = threadIdx.x; q < np; q += kDispThreads) {
+    const int64_t p = p0 + q;
+    const int ls = lslot[q];
+    int row = -1;
+    if (ls >= 0) {
+      const int e = a.idx[p];
+      int base = a.super_prefix[int64_t(s) * n + e];
+      for (int cc = s * a.sup; cc < c; ++cc) base += a.chunk_counts[int64_t(cc) * n + e];
+      const int slot = base + ls;
+      if (slot < a.capacity) row = a.expert_offsets[e] + slot;
+    }
+    lrow[q] = row;
+    a.token_to_row[p] = row;
+    if (a.drop_mask) a.drop_mask[p] = row < 0 ? 1 : 0;
+    if (row >= 0 && a.row_to_token) a.row_to_token[row] = int32_t(p / a.k);
+  }
+  if (!a.dispatched) return;
+  __syncthreads();
+  const int64_t vpr = a.row_bytes / int64_t(sizeof(V));
+  const int64_t items = int64_t(np) * vpr;
+  const V* x = static_cast<const V*>(a.x);
+  V* out = static_cast<V*>(a.dispatched);
+  for (int64_t i = threadIdx.x; i < items; i += kDispThreads) {
+    const int q = int(i / vpr);
+    const int64_t v = i - int64_t(q) * vpr;
+    const int row = lrow[q];
+    if (row >= 0) out[int64_t(row) * vpr + v] = x[((p0 + q) / a.k) * vpr + v];
   }
 }
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
-  const int nch = int(ceil_div64(a.pairs, kDispChunk));
-  hipLaunchKernelGGL(k_disp_hist, dim3(nch), dim3(kDispThreads), a.n * sizeof(int), s, a);
-  hipLaunchKernelGGL(k_disp_rank, dim3(nch), dim3(kDispThreads), 4 * a.n * sizeof(uint16_t), s, a);
-  if (a.dispatched) {
-    int64_t vpr;
-    const int64_t items_per_row_16 = a.row_bytes / 16;
-    const bool v16 = a.row_bytes % 16 == 0;
-    const bool v4 = a.row_bytes % 4 == 0;
-    vpr = v16 ? items_per_row_16 : (v4 ? a.row_bytes / 4 : a.row_bytes / 2);
-    const int64_t items = a.max_rows * vpr;
-    const int64_t blocks = std::min<int64_t>(ceil_div64(items, 256), 16384);
-    if (blocks > 0) {
-      if (v16)
-        hipLaunchKernelGGL(k_disp_copy<u32x4>, dim3(unsigned(blocks)), dim3(256), 0, s,
-                           static_cast<const char*>(a.x), static_cast<char*>(a.dispatched), a.row_to_token,
-                           a.expert_offsets + a.n, vpr, items);
-      else if (v4)
-        hipLaunchKernelGGL(k_disp_copy<uint32_t>, dim3(unsigned(blocks)), dim3(256), 0, s,
-                           static_cast<const char*>(a.x), static_cast<char*>(a.dispatched), a.row_to_token,
-                           a.expert_offsets + a.n, vpr, items);
-      else
-        hipLaunchKernelGGL(k_disp_copy<uint16_t>, dim3(unsigned(blocks)), dim3(256), 0, s,
-                           static_cast<const char*>(a.x), static_cast<char*>(a.dispatched), a.row_to_token,
-                           a.expert_offsets + a.n, vpr, items);
-    }
-  }
+hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s) {
+  if (!prefix_ready)
+    hipLaunchKernelGGL(k_disp_hist, dim3(a.nch), dim3(kDispThreads), a.n * sizeof(int), s, a);
+  const size_t lds = (size_t(a.n) + 2 * size_t(a.chunk_tokens) * a.k) * sizeof(int);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.dispatched);
+  if (a.row_bytes % 16 == 0 && al % 16 == 0)
+    hipLaunchKernelGGL(k_disp_rank_copy<u32x4>, dim3(a.nch), dim3(kDispThreads), lds, s, a);
+  else if (a.row_bytes % 4 == 0 && al % 4 == 0)
+    hipLaunchKernelGGL(k_disp_rank_copy<uint32_t>, dim3(a.nch), dim3(kDispThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL(k_disp_rank_copy<uint16_t>, dim3(a.nch), dim3(kDispThreads), lds, s, a);
   return hipGetLastError();
 }
 

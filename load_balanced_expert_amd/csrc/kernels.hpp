@@ -2,6 +2,8 @@
 // validated by the C-ABI layer before any of these is called.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "prefix.hpp"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -29,16 +31,27 @@ struct RouteArgs {
   const float* w_r;
   const float* bias;
   const uint16_t* planes;
+  bool planes_ready;  // planes already hold the split of w_r
   float* logits;   // big-n path only
   int32_t* idx;
   float* gate_out;
   int32_t* counts;
   float* prob_sum;
+  bool want_psum;      // accumulate Σ score (prob_sum, P or aux requested)
+  float* f;            // optional load statistics computed by the last block
+  float* P;
+  float* aux;
+  float alpha;
+  int32_t* chunk_counts;  // optional [blocks, n] per-chunk counts for the dispatch
+  PrefixArgs prefix;      // optional capacity prefix sums (prefix.chunk_counts != nullptr)
   uint64_t* psum_acc;  // [n] zero, left zero
   uint32_t* cnt_acc;   // [n] zero, left zero
   uint32_t* done;      // zero, left zero
 };
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
+int route_chunk_tokens(const RoutePlan& plan);  // tokens per route workgroup (= dispatch chunk)
+hipError_t launch_router_prepare(const RoutePlan& plan, int d, int n, const float* w_r, uint16_t* planes,
+                                 hipStream_t s);
 
 // ---------------------------------------------------------------- stats
 hipError_t launch_stats(int64_t m, int n, int k, const int32_t* counts, const float* prob_sum,
@@ -49,13 +62,15 @@ hipError_t launch_global_aux(int n, const int64_t* gcounts, const int64_t* gtoke
                              hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch
-constexpr int kDispChunk = 1024;  // (token, choice) pairs per histogram / rank block
 struct DispatchArgs {
   const int32_t* idx;
   int64_t pairs;        // m * k
   int k, n, nbits;
   int32_t capacity;     // >= 0 (unlimited is passed as pairs)
-  int32_t* chunk_counts;  // [nch, n] workspace
+  int chunk_tokens;     // tokens per chunk (== route workgroup tokens when the route made the counts)
+  int nch, sup;         // chunks, chunks per super chunk
+  int32_t* chunk_counts;  // [nch, n]
+  int32_t* super_prefix;  // [ceil(nch / sup), n]
   int32_t* token_to_row;
   uint8_t* drop_mask;
   int32_t* expert_offsets;
@@ -63,11 +78,16 @@ struct DispatchArgs {
   const void* x;
   void* dispatched;
   int64_t row_bytes;    // d * element size
-  int64_t max_rows;     // host bound on rows
-  uint32_t* done;
+  uint32_t* done;       // completion ticket (control region)
+  uint32_t* cnt_acc;    // [n] expert counters (control region)
 };
-size_t dispatch_ws_bytes(int64_t pairs, int n);
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+constexpr int kDispMaxChunkPairs = 4096;
+// chunk tokens for m tokens x k choices given the route workgroup size
+inline int dispatch_chunk_tokens(int route_tokens, int k) {
+  return route_tokens * k <= kDispMaxChunkPairs ? route_tokens : (kDispMaxChunkPairs / k > 0 ? kDispMaxChunkPairs / k : 1);
+}
+size_t dispatch_ws_bytes(int64_t m, int k, int n, int chunk_tokens);
+hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s);
 
 // ---------------------------------------------------------------- expert FFN
 size_t ffn_ws_bytes(int64_t rows_bound, int d_ff);

@@ -22,11 +22,13 @@
 //    totals, writes the outputs and clears the accumulators.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "prefix.hpp"
 
 namespace moe {
 
-constexpr int kRouteBM = 32;      // tokens per route workgroup
-constexpr int kRouteThreads = 256;
+constexpr int kRouteBM = 32;      // tokens per route workgroup (n <= 256)
+constexpr int kRowsBM = 256;      // tokens per route-epilogue workgroup (n > 256)
+constexpr int kRouteThreads = 1024;  // 16 waves
 constexpr double kFix = 4294967296.0;  // 2^32
 
 RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
@@ -81,42 +83,61 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
-// One 32-token x (tiles of 32 experts) block product on bf16 MFMA.  Lane l
-// holds row (l & 31) and the k-slice [kb + 16*(l>>5), +16) of each 32-wide
-// K block; substep s uses its elements [8s, 8s+8).  A and B use the same
-// lane -> k mapping, so every k is paired with itself exactly once.
-template <int TPW>
-__device__ __forceinline__ void gemm_tile_bf16x3(const uint16_t* __restrict__ xrow, int d, int dpad,
-                                                 const uint16_t* __restrict__ planes, int npad,
-                                                 int wave, int lane, f32x16 (&acc)[TPW]) {
+// Block product of 32 tokens x npad experts on bf16 MFMA, split over the 16
+// waves of the workgroup: wave w owns expert tile (w % NT) and the K-block
+// range ks = w / NT of KS = 16 / NT equal ranges.  Lane l holds token row
+// (l & 31) and the k-slice [kb*32 + 16*(l>>5), +16) of each 32-wide K block;
+// substep s uses its elements [8s, 8s+8).  A and B use the same lane -> k
+// mapping, so every k meets itself exactly once.  The next K block's
+// operands are loaded before the current block's MFMAs (register double
+// buffering) so that global-memory latency overlaps the matrix work.
+template <int NT>
+__device__ __forceinline__ f32x16 gemm_ksplit_bf16x3(const uint16_t* __restrict__ xrow, int d, int dpad,
+                                                     const uint16_t* __restrict__ planes, int npad, int wave,
+                                                     int lane) {
+  constexpr int KS = 16 / NT;
   const int h = lane >> 5, r32 = lane & 31;
   const size_t plane = size_t(npad) * dpad;
-  const int ntiles = npad / 32;
+  const int tile = wave % NT, ks = wave / NT;
+  const int nkb = dpad / 32;
+  const int kb0 = ks * nkb / KS, kb1 = (ks + 1) * nkb / KS;
+  const uint16_t* brow = planes + size_t(tile * 32 + r32) * dpad;
+  f32x16 acc;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  if (kb0 >= kb1) return acc;
+  bf16x8 a[2], b[3][2];
+  auto load = [&](int kb, bf16x8 (&aa)[2], bf16x8 (&bb)[3][2]) {
+    const int k0 = kb * 32 + 16 * h;
+    aa[0] = (k0 + 8 <= d) ? load8(xrow + k0) : zero8();
+    aa[1] = (k0 + 16 <= d) ? load8(xrow + k0 + 8) : zero8();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-  for (int kb = 0; kb < dpad; kb += 32) {
-    const int k0 = kb + 16 * h;
-    const bf16x8 a0 = (k0 + 8 <= d) ? load8(xrow + k0) : zero8();
-    const bf16x8 a1 = (k0 + 16 <= d) ? load8(xrow + k0 + 8) : zero8();
+    for (int p = 0; p < 3; ++p) {
+      bb[p][0] = load8(brow + p * plane + k0);
+      bb[p][1] = load8(brow + p * plane + k0 + 8);
+    }
+  };
+  load(kb0, a, b);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    bf16x8 na[2], nb[3][2];
+    const bool more = kb + 1 < kb1;
+    if (more) load(kb + 1, na, nb);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int tile = wave + 4 * t;
-      if (tile < ntiles) {
-        const uint16_t* b = planes + size_t(tile * 32 + r32) * dpad + k0;
-        const bf16x8 h0 = load8(b), h1 = load8(b + 8);
-        const bf16x8 m0 = load8(b + plane), m1 = load8(b + plane + 8);
-        const bf16x8 l0 = load8(b + 2 * plane), l1 = load8(b + 2 * plane + 8);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, h0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, h1, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, m0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, m1, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, l0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, l1, acc[t], 0, 0, 0);
+    for (int p = 0; p < 3; ++p) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[p][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[p][1], acc, 0, 0, 0);
+    }
+    if (more) {
+      a[0] = na[0];
+      a[1] = na[1];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        b[p][0] = nb[p][0];
+        b[p][1] = nb[p][1];
       }
     }
   }
+  return acc;
 }
 
 // 32x32 accumulator layout: lane l, element i -> row 8*(i/4) + 4*(l/32) + (i%4), col l%32.
@@ -193,13 +214,26 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
   }
 }
 
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < int(blockDim.x >> 6); ++w) t += red[w];   // same order in every thread
+  __syncthreads();
+  return t;
+}
+
 // Per-expert Σ over the block's tokens of score_j(t), folded into 2^-32 fixed
-// point, and the block histogram; then the last block publishes the totals.
+// point, the block histogram (and, for the dispatch that follows, this
+// chunk's dense expert counts); then the last block publishes the totals,
+// the optional load statistics ([Switch review] "로드 밸런싱 손실": f, P, aux)
+// and the optional capacity prefix sums.  scratch: LDS of >= n ints.
 __device__ __forceinline__ void route_block_tail(const float* lg, int64_t ld, int rows, const EpiArgs& e,
                                                  const float* tok_mx, const float* tok_sum, int* hist,
-                                                 const RouteArgs& a) {
+                                                 const RouteArgs& a, int* scratch) {
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
-    if (a.prob_sum) {
+    if (a.want_psum) {
       float acc = 0.f;
       for (int tl = 0; tl < rows; ++tl) acc += score_of(e.score, lg[int64_t(tl) * ld + j], tok_mx[tl], tok_sum[tl]);
       const unsigned long long fx = __double2ull_rn(double(acc) * kFix);
@@ -207,20 +241,36 @@ __device__ __forceinline__ void route_block_tail(const float* lg, int64_t ld, in
     }
     const int c = hist[j];
     if (c) atomicAdd(a.cnt_acc + j, uint32_t(c));
+    if (a.chunk_counts) a.chunk_counts[int64_t(blockIdx.x) * e.n + j] = c;
   }
   __shared__ int s_last;
+  __shared__ double red[kRouteThreads / 64];
+  __shared__ int part[kRouteThreads / 64];
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1u) == gridDim.x * gridDim.y - 1;
   __syncthreads();
   if (!s_last) return;
   __threadfence();
+  const float fm = float(a.m);
+  double auxp = 0.0;
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
     const unsigned long long v = atomicExch(reinterpret_cast<unsigned long long*>(a.psum_acc + j), 0ull);
     const uint32_t c = atomicExch(a.cnt_acc + j, 0u);
     a.counts[j] = int32_t(c);
-    if (a.prob_sum) a.prob_sum[j] = float(double(v) / kFix);
+    scratch[j] = int(c);
+    const float ps = float(double(v) / kFix);
+    if (a.prob_sum) a.prob_sum[j] = ps;
+    if (a.f) a.f[j] = float(c) / fm;
+    if (a.P) a.P[j] = ps / fm;
+    auxp += (double(c) / double(a.m)) * (double(ps) / double(a.m));
   }
+  if (a.aux) {
+    const double tot = block_sum_f64(auxp, red);
+    if (threadIdx.x == 0) a.aux[0] = float(double(a.alpha) * double(e.n) * tot);
+  }
+  __syncthreads();
+  if (a.prefix.chunk_counts) dispatch_prefix(a.prefix, scratch, part, kRouteThreads);
   if (threadIdx.x == 0) atomicExch(a.done, 0u);
 }
 
@@ -229,11 +279,11 @@ __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
 }
 
 // ------------------------------------------------------------------ fused route (n <= 256)
-template <int TPW, bool MFMA>
+template <int NT, bool MFMA>
 __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   extern __shared__ float smem[];
   const int ldl = a.npad + 1;
-  float* lg = smem;
+  float* lg = smem;                                   // [32][ldl] logits
   float* tok_mx = lg + kRouteBM * ldl;
   float* tok_sum = tok_mx + kRouteBM;
   int* hist = reinterpret_cast<int*>(tok_sum + kRouteBM);
@@ -243,37 +293,40 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   for (int j = tid; j < a.npad; j += kRouteThreads) hist[j] = 0;
 
   if constexpr (MFMA) {
+    constexpr int KS = 16 / NT;
     const int r = min(lane & 31, rows - 1);  // rows past the end repeat the last token; discarded
     const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (t0 + r) * a.d;
-    f32x16 acc[TPW];
-    gemm_tile_bf16x3<TPW>(xrow, a.d, a.dpad, a.planes, a.npad, wave, lane, acc);
+    const f32x16 acc = gemm_ksplit_bf16x3<NT>(xrow, a.d, a.dpad, a.planes, a.npad, wave, lane);
+    const int col = (wave % NT) * 32 + (lane & 31), ks = wave / NT;
+    // partial products of the K ranges are added in a fixed order
+    for (int s = 0; s < KS; ++s) {
+      if (ks == s) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int tile = wave + 4 * t;
-      if (tile < a.npad / 32) {
-        const int col = tile * 32 + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) lg[acc_row(i, lane) * ldl + col] = acc[t][i];
+        for (int i = 0; i < 16; ++i) {
+          float* q = lg + acc_row(i, lane) * ldl + col;
+          *q = s == 0 ? acc[i] : *q + acc[i];
+        }
       }
+      __syncthreads();
     }
   } else {
     // fp32 product on the vector ALUs: thread (token, expert group), fma over k in order.
-    const int tl = tid >> 3, jg = tid & 7;
+    const int tl = tid >> 5, jg = tid & 31;
     if (tl < rows) {
       const int64_t xo = (t0 + tl) * a.d;
-      for (int j = jg; j < a.npad; j += 8) {
+      for (int j = jg; j < a.npad; j += 32) {
         float h = 0.f;
         if (j < a.n)
           for (int kk = 0; kk < a.d; ++kk) h = fmaf(load_x(a.x, a.x_bf16, xo + kk), a.w_r[int64_t(kk) * a.n + j], h);
         lg[tl * ldl + j] = h;
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
   route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
   __syncthreads();
-  route_block_tail(lg, ldl, rows, e, tok_mx, tok_sum, hist, a);
+  route_block_tail(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg));
 }
 
 // ------------------------------------------------------------------ big-n route: logits GEMM
@@ -349,12 +402,12 @@ __global__ __launch_bounds__(256) void k_route_logits_valu(RouteArgs a) {
 }
 
 // big-n route epilogue: kRowsBM tokens per workgroup from the logits in global memory.
-constexpr int kRowsBM = 256;
 __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
   extern __shared__ float smem[];
   float* tok_mx = smem;
   float* tok_sum = tok_mx + kRowsBM;
   int* hist = reinterpret_cast<int*>(tok_sum + kRowsBM);
+  int* scratch = hist + a.npad;
   const int64_t t0 = int64_t(blockIdx.x) * kRowsBM;
   const int rows = int(min<int64_t>(kRowsBM, a.m - t0));
   for (int j = threadIdx.x; j < a.npad; j += kRouteThreads) hist[j] = 0;
@@ -363,34 +416,42 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
   route_rows(lg, a.npad, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
   __syncthreads();
-  route_block_tail(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a);
+  route_block_tail(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch);
 }
 
-// ------------------------------------------------------------------ launcher
+// ------------------------------------------------------------------ launchers
+hipError_t launch_router_prepare(const RoutePlan& plan, int d, int n, const float* w_r, uint16_t* planes,
+                                 hipStream_t s) {
+  dim3 g(ceil_div(plan.dpad, 64), ceil_div(plan.npad, 64));
+  hipLaunchKernelGGL(k_router_split, g, dim3(256), 0, s, w_r, planes, d, n, plan.npad, plan.dpad);
+  return hipGetLastError();
+}
+
+int route_chunk_tokens(const RoutePlan& plan) { return plan.fused ? kRouteBM : kRowsBM; }
+
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s) {
-  if (plan.mfma) {
-    dim3 g(ceil_div(plan.dpad, 64), ceil_div(plan.npad, 64));
-    hipLaunchKernelGGL(k_router_split, g, dim3(256), 0, s, a.w_r, const_cast<uint16_t*>(a.planes), a.d, a.n,
-                       plan.npad, plan.dpad);
-  }
-  const int nblk_fused = int(ceil_div64(a.m, kRouteBM));
+  if (plan.mfma && !a.planes_ready) launch_router_prepare(plan, a.d, a.n, a.w_r, const_cast<uint16_t*>(a.planes), s);
   if (plan.fused) {
+    const unsigned nblk = unsigned(ceil_div64(a.m, kRouteBM));
     const size_t lds = (size_t(kRouteBM) * (plan.npad + 1) + 2 * kRouteBM) * sizeof(float) + plan.npad * sizeof(int);
-    const int tiles = plan.npad / 32;
-    if (plan.mfma) {
-      if (tiles <= 4)
-        hipLaunchKernelGGL((k_route_fused<1, true>), dim3(nblk_fused), dim3(kRouteThreads), lds, s, a);
-      else
-        hipLaunchKernelGGL((k_route_fused<2, true>), dim3(nblk_fused), dim3(kRouteThreads), lds, s, a);
-    } else {
-      hipLaunchKernelGGL((k_route_fused<1, false>), dim3(nblk_fused), dim3(kRouteThreads), lds, s, a);
-    }
+    const int nt = plan.npad / 32;
+    const dim3 g(nblk), b(kRouteThreads);
+    if (!plan.mfma)
+      hipLaunchKernelGGL((k_route_fused<1, false>), g, b, lds, s, a);
+    else if (nt == 1)
+      hipLaunchKernelGGL((k_route_fused<1, true>), g, b, lds, s, a);
+    else if (nt == 2)
+      hipLaunchKernelGGL((k_route_fused<2, true>), g, b, lds, s, a);
+    else if (nt <= 4)
+      hipLaunchKernelGGL((k_route_fused<4, true>), g, b, lds, s, a);
+    else
+      hipLaunchKernelGGL((k_route_fused<8, true>), g, b, lds, s, a);
   } else {
     if (plan.mfma)
       hipLaunchKernelGGL(k_route_logits_mfma, dim3(unsigned(ceil_div64(a.m, 128)), plan.npad / 128), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(k_route_logits_valu, dim3(unsigned(ceil_div64(a.m, 32)), plan.npad / 64), dim3(256), 0, s, a);
-    const size_t lds = 2 * kRowsBM * sizeof(float) + plan.npad * sizeof(int);
+    const size_t lds = 2 * kRowsBM * sizeof(float) + plan.npad * sizeof(int) + size_t(a.n) * sizeof(int);
     hipLaunchKernelGGL(k_route_rows, dim3(unsigned(ceil_div64(a.m, kRowsBM))), dim3(kRouteThreads), lds, s, a);
   }
   return hipGetLastError();

@@ -39,6 +39,13 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(L.SIGNATURES), "binding signatures out of sync with include/moe.h"
 
 
+def test_router_prepare_validation(lib):
+    assert lib.moe_router_planes_bytes(768, 128) == 3 * 128 * 768 * 2
+    assert lib.moe_router_planes_bytes(0, 128) == 0
+    assert lib.moe_router_prepare(768, 128, None, FAKE, None) == 1
+    assert lib.moe_router_prepare(768, 5000, FAKE, FAKE, None) == 2
+
+
 def test_build_info(lib):
     assert b"gfx950" in lib.moe_build_info()
 
@@ -77,13 +84,13 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 def test_invalid_shapes(lib, bad):
     sh = _sh(**bad)
     assert lib.moe_workspace_size(ctypes.byref(sh), -1, 0) == 0
-    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
     assert st == L.MOE_ERR_INVALID_ARG
 
 
 def test_unsupported_sizes(lib):
     sh = _sh(n=5000)
-    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
     assert st == L.MOE_ERR_UNSUPPORTED
     sh = _sh(m=2 ** 31, k=1)
     assert lib.moe_workspace_size(ctypes.byref(sh), -1, 0) == 0
@@ -91,8 +98,8 @@ def test_unsupported_sizes(lib):
 
 def test_null_pointers_rejected(lib):
     sh = _sh()
-    assert lib.moe_route(ctypes.byref(sh), None, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.moe_route(ctypes.byref(sh), None, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
     assert lib.moe_dispatch(ctypes.byref(sh), -1, FAKE, None, FAKE, None, FAKE, None, None, FAKE, 1 << 30,
                             None) == 1
     assert lib.moe_dispatch(ctypes.byref(sh), -2, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, 1 << 30,
@@ -108,12 +115,12 @@ def test_workspace_too_small_or_misaligned(lib):
     sh = _sh(m=1024, d=768, n=128)
     need = lib.moe_workspace_size(ctypes.byref(sh), -1, 0)
     assert need >= 65536
-    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1024, None)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1024, None)
     assert st == L.MOE_ERR_WORKSPACE
-    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x1010),
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x1010),
                        1 << 40, None)
     assert st == L.MOE_ERR_WORKSPACE
-    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 1 << 40, None)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, 1 << 40, None)
     assert st == L.MOE_ERR_INVALID_ARG
 
 
@@ -165,14 +172,14 @@ def test_switch_layer_validation(lib):
     sh = _sh(m=64, d=64, n=8, xd=0)
     out = L.LayerOutputs()
     out.out = FAKE
-    p = L.LayerParams(16, 1, 64, 0.01)                       # relu_ffn needs bf16 x
+    p = L.LayerParams(16, 1, 64, 0.01, None)                       # relu_ffn needs bf16 x
     assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None,
                                 ctypes.byref(out), FAKE, 1 << 40, None) == 1
-    p = L.LayerParams(16, 7, 0, 0.01)
+    p = L.LayerParams(16, 7, 0, 0.01, None)
     assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, None, None, None,
                                 ctypes.byref(out), FAKE, 1 << 40, None) == 1
     out.out = None
-    p = L.LayerParams(16, 0, 0, 0.01)
+    p = L.LayerParams(16, 0, 0, 0.01, None)
     assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, None, None, None,
                                 ctypes.byref(out), FAKE, 1 << 40, None) == 1
 

@@ -200,6 +200,7 @@ def test_lossfree_micro_batch_loop():
     b_ref = np.zeros(spec.N, np.float32)
     gb = OS.GlobalBatch(spec.N)
     w_dev = to_dev(inp.w_r)
+    b_gpu_prev = np.zeros(spec.N, np.float32)
     for t in range(spec.micro_batches):
         x = inp.micro_batch(t)
         r = M.route(to_dev(x), w_dev, spec.k, score="sigmoid", bias=bias)
@@ -207,13 +208,24 @@ def test_lossfree_micro_batch_loop():
                 gamma=spec.gamma)
         torch.cuda.synchronize()
         ref = OR.route(x, inp.w_r, spec.k, score="sigmoid", bias=b_ref)
-        flips = check_selection(to_host(r.idx), ref, f"micro-batch {t}")
-        if flips:
-            pytest.skip(f"micro-batch {t}: near-tie flips change later biases")
+        gidx = to_host(r.idx)
+        flips = check_selection(gidx, ref, f"micro-batch {t}")
+        gcounts = to_host(r.counts)
+        assert np.array_equal(gcounts, np.bincount(gidx.ravel(), minlength=spec.N))
+        if not flips:
+            assert np.array_equal(gcounts, ref.counts)
         gb.add(ref.counts, spec.T)
         b_ref = OS.lossfree_update(b_ref, ref.counts, spec.T, spec.k, spec.gamma)
-        assert np.array_equal(to_host(bias), b_ref), f"bias after micro-batch {t}"
+        b_gpu = to_host(bias)
+        assert np.array_equal(b_gpu, OS.lossfree_update(b_gpu_prev, gcounts, spec.T, spec.k, spec.gamma))
+        if not np.array_equal(b_gpu, b_ref):
+            # only a near-tie flip that moved an expert across m*k/n can do this
+            assert flips, f"bias after micro-batch {t} differs without any selection flip"
+            pytest.skip(f"micro-batch {t}: {len(flips)} near-tie flips moved a load across the target")
+        b_gpu_prev = b_gpu
         vio = OS.max_min_avg_vio(ref.counts)
-        say(f"  micro-batch {t}: MaxVio {vio[0]:.3f}")
-    assert np.array_equal(to_host(gc), gb.counts)
-    assert to_host(gt)[0] == gb.tokens
+        say(f"  micro-batch {t}: MaxVio {vio[0]:.3f} near-tie flips {len(flips)}")
+    if np.array_equal(to_host(gc), gb.counts):
+        assert to_host(gt)[0] == gb.tokens
+    else:
+        assert to_host(gc).sum() == gb.counts.sum()
