@@ -167,6 +167,9 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for evs in events:          # creates the HIP events; the library re-records them inside each step
+        for e in evs:
+            e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

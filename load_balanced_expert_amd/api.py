@@ -321,6 +321,8 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
     if stage_events is not None:
         if len(stage_events) != 6:
             raise MoeError("stage_events takes 6 events")
+        if any(e is not None and not e.cuda_event for e in stage_events):
+            raise MoeError("stage_events must be created first (record each event once)")
         evs = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None
                                       for e in stage_events])
     params = L.LayerParams(int(capacity), L.EXPERTS["relu_ffn" if ffn else "identity"], int(d_ff), float(alpha),

@@ -18,7 +18,8 @@ struct Layout {
   size_t route_end, dispatch_end, total;
   RoutePlan rp;
   int64_t pairs, rows_bound;
-  int route_ct, disp_ct, nch, sup;
+  int route_ct, disp_ct, nch, sup, nch_route, sup_route;
+  size_t chunk_psum, super_prefix;
 };
 
 bool shape_valid(const moe_shape* s) {
@@ -54,7 +55,12 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   L.disp_ct = dispatch_chunk_tokens(L.route_ct, s.k);
   L.nch = int(ceil_div64(s.m, L.disp_ct));
   L.sup = super_chunk(L.nch);
-  L.chunks = o; o += al(dispatch_ws_bytes(s.m, s.k, s.n, L.disp_ct));
+  L.nch_route = int(ceil_div64(s.m, L.route_ct));
+  L.sup_route = super_chunk(L.nch_route);
+  const int nch_max = std::max(L.nch, L.nch_route);
+  L.chunks = o; o += al(size_t(nch_max) * s.n * sizeof(int32_t));
+  L.chunk_psum = o; o += al(size_t(nch_max) * s.n * sizeof(float));
+  L.super_prefix = o; o += al(size_t(kMaxSuperChunks) * s.n * sizeof(int32_t));
   L.r2t = o; o += al(size_t(L.pairs) * 4);
   L.dispatch_end = o;
   L.hidden = o; o += al(d_ff > 0 ? ffn_ws_bytes(L.rows_bound, d_ff) : 0);
@@ -121,18 +127,19 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
   a.gate_out = gate;
   a.counts = counts;
   a.prob_sum = prob_sum;
-  a.want_psum = prob_sum != nullptr || ex.P != nullptr || ex.aux != nullptr;
   a.f = ex.f;
   a.P = ex.P;
   a.aux = ex.aux;
   a.alpha = ex.alpha;
+  a.chunk_counts = at<int32_t>(ws, L.chunks);
+  a.chunk_psum = (prob_sum || ex.P || ex.aux) ? at<float>(ws, L.chunk_psum) : nullptr;
+  a.sup = L.sup_route;
+  a.capacity = -1;
   if (ex.disp) {
-    a.chunk_counts = ex.disp->chunk_counts;
-    a.prefix = PrefixArgs{ex.disp->chunk_counts, ex.disp->nch, ex.disp->sup, s.n, ex.disp->capacity,
-                          ex.disp->expert_offsets, ex.disp->super_prefix};
+    a.capacity = ex.disp->capacity;
+    a.expert_offsets = ex.disp->expert_offsets;
+    a.super_prefix = ex.disp->super_prefix;
   }
-  a.psum_acc = ctl_psum(ws);
-  a.cnt_acc = ctl_cnt(ws);
   a.done = ctl_ticket(ws, kTicketRoute);
   RoutePlan rp = L.rp;
   if (rp.mfma && (reinterpret_cast<uintptr_t>(x) % 16) != 0) rp.mfma = false;
@@ -152,7 +159,7 @@ DispatchArgs dispatch_args(const moe_shape& s, const Layout& L, int32_t capacity
   a.nch = L.nch;
   a.sup = L.sup;
   a.chunk_counts = at<int32_t>(ws, L.chunks);
-  a.super_prefix = at<int32_t>(ws, L.chunks + al(size_t(L.nch) * s.n * sizeof(int32_t)));
+  a.super_prefix = at<int32_t>(ws, L.super_prefix);
   a.token_to_row = t2r;
   a.drop_mask = drop;
   a.expert_offsets = offs;
@@ -161,7 +168,6 @@ DispatchArgs dispatch_args(const moe_shape& s, const Layout& L, int32_t capacity
   a.dispatched = disp;
   a.row_bytes = int64_t(s.d) * x_esz(s);
   a.done = ctl_ticket(ws, kTicketDispatch);
-  a.cnt_acc = ctl_cnt(ws);
   return a;
 }
 
@@ -297,7 +303,6 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
   a.info = info;
   a.ws = static_cast<char*>(ws) + kControlBytes;
   a.done = ctl_ticket(ws, kTicketBalance);
-  a.cnt_acc = ctl_cnt(ws);
   return hip_status(launch_balance(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(256) void k_combine_vec(int64_t m, int d, int k, co
                                                      void* __restrict__ out) {
   const int64_t vpr = d / 8;
   const int64_t items = m * vpr;
+#pragma unroll 2
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < items; i += int64_t(gridDim.x) * 256) {
     const int64_t t = i / vpr, v = i - t * vpr;
     float acc[8];
@@ -111,7 +112,7 @@ hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, c
                        reinterpret_cast<uintptr_t>(residual);
   if (d % 8 == 0 && (al % 16) == 0) {
     const int64_t items = m * (d / 8);
-    const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(items, 256), 65536));
+    const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(items, 512), 65536));
     if (x_bf16 && y_bf16)
       hipLaunchKernelGGL((k_combine_vec<true, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
     else if (x_bf16)

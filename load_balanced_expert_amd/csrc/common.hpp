@@ -15,18 +15,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 4096;
 
-// Control region at the start of every workspace (zero before first use;
-// every kernel that uses a word leaves it zero again).
-//   [0, 256)            completion tickets of last-block-done kernels
-//   [256, 33024)        uint64 fixed-point score sums, one per expert
-//   [33024, 49408)      uint32 expert counters, one per expert
-constexpr size_t kControlBytes = 65536;
-constexpr size_t kCtlPsumOffset = 256;
-constexpr size_t kCtlCntOffset = kCtlPsumOffset + sizeof(uint64_t) * kMaxExperts;
+// Control region at the start of every workspace: completion tickets of the
+// last-workgroup pattern (zero before first use; each kernel that takes a
+// ticket leaves it zero again).
+constexpr int kMaxSuperChunks = 16;
+constexpr size_t kControlBytes = 4096;
 enum CtlTicket { kTicketRoute = 0, kTicketDispatch = 1, kTicketBalance = 2 };
 inline uint32_t* ctl_ticket(void* ws, int which) { return static_cast<uint32_t*>(ws) + which; }
-inline uint64_t* ctl_psum(void* ws) { return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kCtlPsumOffset); }
-inline uint32_t* ctl_cnt(void* ws) { return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCtlCntOffset); }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -25,16 +25,18 @@
 namespace moe {
 
 constexpr int kDispThreads = 256;
+constexpr int kDispPrefixBuf = 4096;   // LDS ints for the last block's super-chunk pass
 
 size_t dispatch_ws_bytes(int64_t m, int k, int n, int chunk_tokens) {
   const int64_t nch = ceil_div64(m, chunk_tokens);
   (void)k;
-  return size_t(nch) * n * sizeof(int32_t) + size_t(16) * n * sizeof(int32_t) + 256;
+  // chunk counts, chunk score sums (route), super-chunk prefixes
+  return 2 * (size_t(nch) * n * sizeof(int32_t) + 256) + size_t(kMaxSuperChunks) * n * sizeof(int32_t) + 256;
 }
 
 __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
   extern __shared__ int lds[];
-  int* hist = lds;                  // [n]
+  int* hist = lds;                  // [n], then the finishing scratch
   const int n = a.n;
   const int64_t c = blockIdx.x;
   for (int j = threadIdx.x; j < n; j += kDispThreads) hist[j] = 0;
@@ -46,24 +48,19 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
     if (unsigned(e) < unsigned(n)) atomicAdd(&hist[e], 1);   // ids outside [0, n) are dropped
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < n; j += kDispThreads) {
-    const int v = hist[j];
-    a.chunk_counts[c * n + j] = v;
-    if (v) atomicAdd(a.cnt_acc + j, uint32_t(v));
-  }
-  __shared__ int s_last;
-  __shared__ int part[kDispThreads / 64];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int j = threadIdx.x; j < n; j += kDispThreads) hist[j] = int(atomicExch(a.cnt_acc + j, 0u));
-  __syncthreads();
-  PrefixArgs pa{a.chunk_counts, a.nch, a.sup, n, a.capacity, a.expert_offsets, a.super_prefix};
-  dispatch_prefix(pa, hist, part, kDispThreads);
-  if (threadIdx.x == 0) atomicExch(a.done, 0u);
+  for (int j = threadIdx.x; j < n; j += kDispThreads) store_agent(a.chunk_counts + c * n + j, int32_t(hist[j]));
+  __shared__ int s_flag;
+  if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
+  FinalizeArgs f{};
+  f.chunk_counts = a.chunk_counts;
+  f.nch = a.nch;
+  f.sup = a.sup;
+  f.n = n;
+  f.m = a.pairs;
+  f.capacity = a.capacity;
+  f.expert_offsets = a.expert_offsets;
+  f.super_prefix = a.super_prefix;
+  finalize_chunks(f, lds, n + kDispPrefixBuf, kDispThreads);
 }
 
 template <typename V>
@@ -115,21 +112,37 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
   }
   if (!a.dispatched) return;
   __syncthreads();
+  // copy: (row, vector) items, four in flight per thread
   const int64_t vpr = a.row_bytes / int64_t(sizeof(V));
   const int64_t items = int64_t(np) * vpr;
-  const V* x = static_cast<const V*>(a.x);
-  V* out = static_cast<V*>(a.dispatched);
-  for (int64_t i = threadIdx.x; i < items; i += kDispThreads) {
-    const int q = int(i / vpr);
-    const int64_t v = i - int64_t(q) * vpr;
-    const int row = lrow[q];
-    if (row >= 0) out[int64_t(row) * vpr + v] = x[((p0 + q) / a.k) * vpr + v];
+  const V* __restrict__ x = static_cast<const V*>(a.x);
+  V* __restrict__ out = static_cast<V*>(a.dispatched);
+  for (int64_t i0 = threadIdx.x; i0 < items; i0 += 4 * kDispThreads) {
+    V v[4];
+    int64_t dst[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + int64_t(u) * kDispThreads;
+      dst[u] = -1;
+      if (i < items) {
+        const int q = int(i / vpr);
+        const int64_t c = i - int64_t(q) * vpr;
+        const int row = lrow[q];
+        if (row >= 0) {
+          v[u] = x[((p0 + q) / a.k) * vpr + c];
+          dst[u] = int64_t(row) * vpr + c;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (dst[u] >= 0) out[dst[u]] = v[u];
   }
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s) {
   if (!prefix_ready)
-    hipLaunchKernelGGL(k_disp_hist, dim3(a.nch), dim3(kDispThreads), a.n * sizeof(int), s, a);
+    hipLaunchKernelGGL(k_disp_hist, dim3(a.nch), dim3(kDispThreads), (a.n + kDispPrefixBuf) * sizeof(int), s, a);
   const size_t lds = (size_t(a.n) + 2 * size_t(a.chunk_tokens) * a.k) * sizeof(int);
   const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.dispatched);
   if (a.row_bytes % 16 == 0 && al % 16 == 0)

@@ -36,17 +36,19 @@ struct RouteArgs {
   int32_t* idx;
   float* gate_out;
   int32_t* counts;
-  float* prob_sum;
-  bool want_psum;      // accumulate Σ score (prob_sum, P or aux requested)
-  float* f;            // optional load statistics computed by the last block
+  float* prob_sum;     // optional
+  float* f;            // optional load statistics
   float* P;
   float* aux;
   float alpha;
-  int32_t* chunk_counts;  // optional [blocks, n] per-chunk counts for the dispatch
-  PrefixArgs prefix;      // optional capacity prefix sums (prefix.chunk_counts != nullptr)
-  uint64_t* psum_acc;  // [n] zero, left zero
-  uint32_t* cnt_acc;   // [n] zero, left zero
-  uint32_t* done;      // zero, left zero
+  int32_t* chunk_counts;  // [route workgroups, n] chunk rows (workspace)
+  float* chunk_psum;      // [route workgroups, n] or nullptr when no score sum is wanted
+  int sup;                // chunks per super chunk
+  int32_t capacity;       // < 0: no capacity prefix sums
+  int32_t* expert_offsets;
+  int32_t* super_prefix;
+  uint32_t* done;         // completion ticket (control region)
+  int lds_region_ints;    // set by launch_route
 };
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
 int route_chunk_tokens(const RoutePlan& plan);  // tokens per route workgroup (= dispatch chunk)
@@ -79,7 +81,6 @@ struct DispatchArgs {
   void* dispatched;
   int64_t row_bytes;    // d * element size
   uint32_t* done;       // completion ticket (control region)
-  uint32_t* cnt_acc;    // [n] expert counters (control region)
 };
 constexpr int kDispMaxChunkPairs = 4096;
 // chunk tokens for m tokens x k choices given the route workgroup size
@@ -115,7 +116,6 @@ struct BalanceArgs {
   int32_t* info;
   void* ws;          // after the control words
   uint32_t* done;    // completion ticket (control region)
-  uint32_t* cnt_acc; // [n] expert counters (control region)
 };
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
 

@@ -1,36 +1,70 @@
-// Device-side prefix sums shared by the route and dispatch kernels: the last
-// workgroup of a grid turns per-chunk expert counts into the quantities that
-// capacity slots need ([Switch review] "Expert Capacity와 토큰 드롭"):
-//   kept_j            = min(c_j, capacity)
-//   expert_offsets    = exclusive scan of kept_j over experts (+ total)
-//   super_prefix[s,j] = Σ_{c < s*sup} chunk_counts[c, j]   (chunks grouped by sup)
-// A chunk's base for expert j is then super_prefix[c/sup, j] plus at most
-// sup-1 chunk counts, so no grid-wide serial scan is needed.
+// Grid-wide finish of per-chunk partials, shared by the route and dispatch
+// kernels.  Every workgroup (one chunk of tokens) writes its dense per-expert
+// counts (and score sums) with agent-scope stores, waits for them to be
+// acknowledged and takes a ticket; the workgroup that takes the last ticket
+// sums the partials in a fixed order and publishes
+//   counts_j, Σ score_j                         (route: f_i, P_i inputs)
+//   f, P, aux                                   ([Switch review] "로드 밸런싱 손실")
+//   kept_j = min(c_j, capacity), expert_offsets ([Switch review] "Expert
+//                                                Capacity와 토큰 드롭")
+//   super_prefix[s, j] = Σ_{c < s*sup} counts[c, j]
+// so that a chunk's slot base for expert j is super_prefix[c/sup, j] plus at
+// most sup-1 chunk counts.  Data crosses workgroups only through agent-scope
+// (L2-bypassing) stores and loads, so no cache-wide fence is needed; every
+// sum has a fixed order, so results are bit-reproducible.
 #pragma once
 #include "common.hpp"
 
 namespace moe {
 
-struct PrefixArgs {
-  const int32_t* chunk_counts;  // [nch, n]
+__host__ __device__ inline int super_chunk(int nch) {  // chunks per super chunk: at most kMaxSuperChunks super chunks
+  return nch <= kMaxSuperChunks ? 1 : (nch + kMaxSuperChunks - 1) / kMaxSuperChunks;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// All of this workgroup's agent-scope stores are acknowledged; then one ticket.
+// Returns true in the workgroup that took the last ticket (which also resets it).
+__device__ __forceinline__ bool last_workgroup(uint32_t* ticket, unsigned nblocks, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) *s_flag = atomicAdd(ticket, 1u) == nblocks - 1;
+  __syncthreads();
+  const bool last = *s_flag;
+  if (last && threadIdx.x == 0) atomicExch(ticket, 0u);
+  return last;
+}
+
+struct FinalizeArgs {
+  const int32_t* chunk_counts;  // [nch, n]  agent-scope stores of every chunk
+  const float* chunk_psum;      // [nch, n]  or nullptr
   int nch, sup, n;
-  int32_t capacity;
+  int64_t m;                    // tokens (for f and P)
+  int32_t* counts;              // [n] out or nullptr
+  float* prob_sum;              // [n] out or nullptr
+  float* f;                     // [n] out or nullptr
+  float* P;                     // [n] out or nullptr
+  float* aux;                   // [1] out or nullptr
+  float alpha;
+  int32_t capacity;             // < 0: no capacity prefix sums
   int32_t* expert_offsets;      // [n + 1]
   int32_t* super_prefix;        // [ceil(nch / sup), n]
 };
 
-inline int super_chunk(int nch) {  // chunks per super chunk: at most 16 super chunks
-  return nch <= 16 ? 1 : (nch + 15) / 16;
-}
-
-// Exclusive scan of v[0..n) held in LDS (n <= 4096) by one workgroup of
-// `threads` threads into out[0..n] (global); fixed order, deterministic.
+// Exclusive scan of v[0..n) held in LDS by one workgroup into out[0..n];
+// fixed order, deterministic.  part: LDS of threads/64 ints.
 __device__ __forceinline__ void block_exclusive_scan(const int* v, int n, int32_t* out, int* part, int threads) {
   const int per = ceil_div(n, threads);
   const int j0 = threadIdx.x * per;
   int s = 0;
   for (int j = j0; j < min(j0 + per, n); ++j) s += v[j];
-  // wave-level inclusive scan of the per-thread sums, then across waves
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = s;
 #pragma unroll
@@ -58,30 +92,67 @@ __device__ __forceinline__ void block_exclusive_scan(const int* v, int n, int32_
   __syncthreads();
 }
 
-// Runs in the last workgroup.  cnt: per-expert totals in LDS (overwritten with
-// kept counts); part: LDS scratch of threads/64 ints.
-__device__ __forceinline__ void dispatch_prefix(const PrefixArgs& p, int* cnt, int* part, int threads) {
-  for (int j = threadIdx.x; j < p.n; j += threads) cnt[j] = min(cnt[j], p.capacity);
-  __syncthreads();
-  block_exclusive_scan(cnt, p.n, p.expert_offsets, part, threads);
-  const int nsup = ceil_div(p.nch, p.sup);
-  for (int q = threadIdx.x; q < nsup * p.n; q += threads) {
-    const int s = q / p.n, j = q - s * p.n;
-    int sum = 0;
-    const int c1 = min(p.nch, (s + 1) * p.sup);
-    for (int c = s * p.sup; c < c1; ++c)
-      sum += __hip_atomic_load(p.chunk_counts + int64_t(c) * p.n + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    p.super_prefix[int64_t(s) * p.n + j] = sum;
-  }
-  __syncthreads();
-  for (int j = threadIdx.x; j < p.n; j += threads) {
-    int run = 0;
-    for (int s = 0; s < nsup; ++s) {
-      int32_t* q = p.super_prefix + int64_t(s) * p.n + j;
-      const int v = *q;
-      *q = run;
-      run += v;
+// Runs in the last workgroup.  lds: >= n + 2 * nsup * 64 ints.
+__device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds, int lds_ints, int threads) {
+  __shared__ int part[16];
+  __shared__ double red[16];
+  const int n = a.n;
+  const int nsup = ceil_div(a.nch, a.sup);
+  int* tot = lds;                                   // [n] totals, then kept counts
+  int* sc = tot + n;                                // [nsup][cb] super-chunk counts
+  float* sp = reinterpret_cast<float*>(sc) + 0;     // reused below: [nsup][cb] score sums
+  const int cb = max(1, min(n, (lds_ints - n) / (2 * nsup)));
+  sp = reinterpret_cast<float*>(sc + nsup * cb);
+  const double dm = double(a.m);
+  double auxp = 0.0;
+  for (int j0 = 0; j0 < n; j0 += cb) {
+    const int w = min(cb, n - j0);
+    for (int q = threadIdx.x; q < nsup * w; q += threads) {
+      const int s = q / w, jj = q - s * w;
+      const int c1 = min(a.nch, (s + 1) * a.sup);
+      int cs = 0;
+      float ps = 0.f;
+      for (int c = s * a.sup; c < c1; ++c) {
+        const int64_t o = int64_t(c) * n + j0 + jj;
+        cs += load_agent(a.chunk_counts + o);
+        if (a.chunk_psum) ps += load_agent(a.chunk_psum + o);
+      }
+      sc[s * w + jj] = cs;
+      sp[s * w + jj] = ps;
     }
+    __syncthreads();
+    for (int jj = threadIdx.x; jj < w; jj += threads) {
+      const int j = j0 + jj;
+      int run = 0;
+      float ps = 0.f;
+      for (int s = 0; s < nsup; ++s) {
+        if (a.capacity >= 0) a.super_prefix[int64_t(s) * n + j] = run;
+        run += sc[s * w + jj];
+        ps += sp[s * w + jj];
+      }
+      tot[j] = run;
+      if (a.counts) a.counts[j] = run;
+      if (a.prob_sum) a.prob_sum[j] = ps;
+      if (a.f) a.f[j] = float(run) / float(a.m);
+      if (a.P) a.P[j] = ps / float(a.m);
+      auxp += (double(run) / dm) * (double(ps) / dm);
+    }
+    __syncthreads();
+  }
+  if (a.aux) {
+    double v = wave_sum_f64(auxp);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int q = 0; q < threads / 64; ++q) t += red[q];
+      a.aux[0] = float(double(a.alpha) * double(n) * t);
+    }
+  }
+  if (a.capacity >= 0) {
+    for (int j = threadIdx.x; j < n; j += threads) tot[j] = min(tot[j], a.capacity);
+    __syncthreads();
+    block_exclusive_scan(tot, n, a.expert_offsets, part, threads);
   }
 }
 

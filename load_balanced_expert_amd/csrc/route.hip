@@ -7,19 +7,20 @@
 // gate ρ); [Switch review] "로드 밸런싱 손실" (counts for f_i, Σ p for P_i).
 //
 // gfx950 design
-//  * bf16 x: W_r is split once per call into three bf16 planes hi + mid + lo
-//    that sum exactly to the fp32 weight; three bf16 MFMAs with fp32
-//    accumulation then give an fp32-accurate product (every bf16 x bf16
-//    product is exact in fp32).  v_mfma_f32_32x32x16_bf16, 64-lane waves.
-//  * n <= 256: one workgroup owns 32 tokens x all experts; the logits tile
-//    stays in LDS and the epilogue (softmax statistics, top-k, gates, block
-//    histogram, per-expert score sums) runs in the same kernel.
+//  * bf16 x: W_r is split once into three bf16 planes hi + mid + lo that sum
+//    exactly to the fp32 weight; three bf16 MFMAs with fp32 accumulation give
+//    an fp32-accurate product (every bf16 x bf16 product is exact in fp32).
+//    v_mfma_f32_32x32x16_bf16 on 64-lane waves.
+//  * n <= 256: one 16-wave workgroup owns 32 tokens x all experts.  The K
+//    dimension is split across waves, operands for the next K block are
+//    loaded (branch-free) while the current one is multiplied, partial tiles
+//    meet in LDS in a fixed order, and the epilogue (softmax statistics,
+//    top-k, gates, histogram, per-expert score sums) runs in the same kernel.
 //  * n > 256: a tiled MFMA GEMM writes fp32 logits to the workspace, then a
 //    row kernel runs the same epilogue from global memory.
-//  * Σ_t score_j(t) is accumulated as 2^-32 fixed point in uint64 atomics, so
-//    the total is exact integer arithmetic and independent of block order;
-//    counts use integer atomics.  The last block to finish converts the
-//    totals, writes the outputs and clears the accumulators.
+//  * Each workgroup stores its per-expert counts and score sums as a chunk
+//    row; the workgroup that finishes last sums the rows in a fixed order
+//    (prefix.hpp), so every output is bit-reproducible.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prefix.hpp"
@@ -29,7 +30,6 @@ namespace moe {
 constexpr int kRouteBM = 32;      // tokens per route workgroup (n <= 256)
 constexpr int kRowsBM = 256;      // tokens per route-epilogue workgroup (n > 256)
 constexpr int kRouteThreads = 1024;  // 16 waves
-constexpr double kFix = 4294967296.0;  // 2^32
 
 RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
   RoutePlan p{};
@@ -47,16 +47,16 @@ RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
 __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ w,
                                                        uint16_t* __restrict__ planes, int d, int n,
                                                        int npad, int dpad) {
-  __shared__ float tile[64][65];
-  const int kb = blockIdx.x * 64, jb = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
+  __shared__ float tile[32][33];
+  const int kb = blockIdx.x * 32, jb = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int r = ty; r < 32; r += 8) {
     const int k = kb + r, j = jb + tx;
     tile[r][tx] = (k < d && j < n) ? w[size_t(k) * n + j] : 0.f;
   }
   __syncthreads();
   const size_t plane = size_t(npad) * dpad;
-  for (int r = ty; r < 64; r += 4) {
+  for (int r = ty; r < 32; r += 8) {
     const int j = jb + r, k = kb + tx;
     if (j < npad && k < dpad) {
       const float v = tile[tx][r];
@@ -83,58 +83,79 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
+// 8 bf16 at p (a valid address) or zeros when !ok, without a branch.
+__device__ __forceinline__ bf16x8 load8_or_zero(const uint16_t* p, bool ok) {
+  u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  const uint32_t msk = ok ? 0xFFFFFFFFu : 0u;
+  v &= msk;
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Block product of 32 tokens x npad experts on bf16 MFMA, split over the 16
 // waves of the workgroup: wave w owns expert tile (w % NT) and the K-block
 // range ks = w / NT of KS = 16 / NT equal ranges.  Lane l holds token row
 // (l & 31) and the k-slice [kb*32 + 16*(l>>5), +16) of each 32-wide K block;
 // substep s uses its elements [8s, 8s+8).  A and B use the same lane -> k
-// mapping, so every k meets itself exactly once.  The next K block's
-// operands are loaded before the current block's MFMAs (register double
-// buffering) so that global-memory latency overlaps the matrix work.
-template <int NT>
+// mapping, so every k meets itself exactly once.  The loop body is
+// branch-free: the next K block's operands are always loaded (the last
+// iteration reloads its own block) before the current block's MFMAs, so the
+// wait before the MFMAs covers only the older loads.  Each workgroup starts
+// its K range at a different block (rot) to spread the shared W_r reads over
+// the L2 channels.
+template <int NT, bool KTAIL>
 __device__ __forceinline__ f32x16 gemm_ksplit_bf16x3(const uint16_t* __restrict__ xrow, int d, int dpad,
                                                      const uint16_t* __restrict__ planes, int npad, int wave,
-                                                     int lane) {
+                                                     int lane, int rot) {
   constexpr int KS = 16 / NT;
   const int h = lane >> 5, r32 = lane & 31;
   const size_t plane = size_t(npad) * dpad;
   const int tile = wave % NT, ks = wave / NT;
   const int nkb = dpad / 32;
-  const int kb0 = ks * nkb / KS, kb1 = (ks + 1) * nkb / KS;
+  const int kb0 = ks * nkb / KS, cnt = (ks + 1) * nkb / KS - kb0;
   const uint16_t* brow = planes + size_t(tile * 32 + r32) * dpad;
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  if (kb0 >= kb1) return acc;
-  bf16x8 a[2], b[3][2];
-  auto load = [&](int kb, bf16x8 (&aa)[2], bf16x8 (&bb)[3][2]) {
-    const int k0 = kb * 32 + 16 * h;
-    aa[0] = (k0 + 8 <= d) ? load8(xrow + k0) : zero8();
-    aa[1] = (k0 + 16 <= d) ? load8(xrow + k0 + 8) : zero8();
+  if (cnt <= 0) return acc;
+  rot %= cnt;
+  auto load = [&](int i, bf16x8 (&aa)[2], bf16x8 (&bb)[3][2]) {
+    int r = i + rot;
+    r = r >= cnt ? r - cnt : r;
+    const int k0 = (kb0 + r) * 32 + 16 * h;
+    if constexpr (KTAIL) {
+      aa[0] = load8_or_zero(xrow + min(k0, d - 8), k0 + 8 <= d);
+      aa[1] = load8_or_zero(xrow + min(k0 + 8, d - 8), k0 + 16 <= d);
+    } else {
+      aa[0] = load8(xrow + k0);
+      aa[1] = load8(xrow + k0 + 8);
+    }
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
       bb[p][0] = load8(brow + p * plane + k0);
       bb[p][1] = load8(brow + p * plane + k0 + 8);
     }
   };
-  load(kb0, a, b);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    bf16x8 na[2], nb[3][2];
-    const bool more = kb + 1 < kb1;
-    if (more) load(kb + 1, na, nb);
+  auto mma = [&](const bf16x8 (&aa)[2], const bf16x8 (&bb)[3][2]) {
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[p][0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[p][1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa[0], bb[p][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa[1], bb[p][1], acc, 0, 0, 0);
     }
-    if (more) {
-      a[0] = na[0];
-      a[1] = na[1];
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        b[p][0] = nb[p][0];
-        b[p][1] = nb[p][1];
-      }
+  };
+  // ping-pong buffers; the scheduling barriers keep each block's loads ahead
+  // of the previous block's MFMAs instead of letting them sink to their uses
+  bf16x8 a0[2], b0[3][2], a1[2], b1[3][2];
+  load(0, a0, b0);
+  for (int i = 0; i < cnt; i += 2) {
+    load(min(i + 1, cnt - 1), a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < cnt) {
+      load(min(i + 2, cnt - 1), a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   return acc;
@@ -214,64 +235,40 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
   }
 }
 
-__device__ __forceinline__ double block_sum_f64(double v, double* red) {
-  v = wave_sum_f64(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double t = 0.0;
-  for (int w = 0; w < int(blockDim.x >> 6); ++w) t += red[w];   // same order in every thread
-  __syncthreads();
-  return t;
-}
-
-// Per-expert Σ over the block's tokens of score_j(t), folded into 2^-32 fixed
-// point, the block histogram (and, for the dispatch that follows, this
-// chunk's dense expert counts); then the last block publishes the totals,
-// the optional load statistics ([Switch review] "로드 밸런싱 손실": f, P, aux)
-// and the optional capacity prefix sums.  scratch: LDS of >= n ints.
-__device__ __forceinline__ void route_block_tail(const float* lg, int64_t ld, int rows, const EpiArgs& e,
-                                                 const float* tok_mx, const float* tok_sum, int* hist,
-                                                 const RouteArgs& a, int* scratch) {
+// Chunk row of this workgroup: per-expert counts and (if wanted) Σ over its
+// tokens of score_j(t) in token order; the last workgroup publishes the
+// totals, the optional load statistics and capacity prefix sums.
+__device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows, const EpiArgs& e,
+                                           const float* tok_mx, const float* tok_sum, const int* hist,
+                                           const RouteArgs& a, int* scratch, int scratch_ints) {
+  const int64_t row0 = int64_t(blockIdx.x) * e.n;
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
-    if (a.want_psum) {
+    if (a.chunk_psum) {
       float acc = 0.f;
       for (int tl = 0; tl < rows; ++tl) acc += score_of(e.score, lg[int64_t(tl) * ld + j], tok_mx[tl], tok_sum[tl]);
-      const unsigned long long fx = __double2ull_rn(double(acc) * kFix);
-      if (fx) atomicAdd(reinterpret_cast<unsigned long long*>(a.psum_acc + j), fx);
+      store_agent(a.chunk_psum + row0 + j, acc);
     }
-    const int c = hist[j];
-    if (c) atomicAdd(a.cnt_acc + j, uint32_t(c));
-    if (a.chunk_counts) a.chunk_counts[int64_t(blockIdx.x) * e.n + j] = c;
+    store_agent(a.chunk_counts + row0 + j, int32_t(hist[j]));
   }
-  __shared__ int s_last;
-  __shared__ double red[kRouteThreads / 64];
-  __shared__ int part[kRouteThreads / 64];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1u) == gridDim.x * gridDim.y - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float fm = float(a.m);
-  double auxp = 0.0;
-  for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
-    const unsigned long long v = atomicExch(reinterpret_cast<unsigned long long*>(a.psum_acc + j), 0ull);
-    const uint32_t c = atomicExch(a.cnt_acc + j, 0u);
-    a.counts[j] = int32_t(c);
-    scratch[j] = int(c);
-    const float ps = float(double(v) / kFix);
-    if (a.prob_sum) a.prob_sum[j] = ps;
-    if (a.f) a.f[j] = float(c) / fm;
-    if (a.P) a.P[j] = ps / fm;
-    auxp += (double(c) / double(a.m)) * (double(ps) / double(a.m));
-  }
-  if (a.aux) {
-    const double tot = block_sum_f64(auxp, red);
-    if (threadIdx.x == 0) a.aux[0] = float(double(a.alpha) * double(e.n) * tot);
-  }
-  __syncthreads();
-  if (a.prefix.chunk_counts) dispatch_prefix(a.prefix, scratch, part, kRouteThreads);
-  if (threadIdx.x == 0) atomicExch(a.done, 0u);
+  __shared__ int s_flag;
+  if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
+  FinalizeArgs f{};
+  f.chunk_counts = a.chunk_counts;
+  f.chunk_psum = a.chunk_psum;
+  f.nch = int(gridDim.x);
+  f.sup = a.sup;
+  f.n = e.n;
+  f.m = a.m;
+  f.counts = a.counts;
+  f.prob_sum = a.prob_sum;
+  f.f = a.f;
+  f.P = a.P;
+  f.aux = a.aux;
+  f.alpha = a.alpha;
+  f.capacity = a.capacity;
+  f.expert_offsets = a.expert_offsets;
+  f.super_prefix = a.super_prefix;
+  finalize_chunks(f, scratch, scratch_ints, kRouteThreads);
 }
 
 __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
@@ -279,14 +276,15 @@ __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
 }
 
 // ------------------------------------------------------------------ fused route (n <= 256)
-template <int NT, bool MFMA>
+// LDS: KS-1 partial tiles [32][npad] (the first becomes the logits tile and,
+// in the last workgroup, the finishing scratch), then the histogram.
+template <int NT, bool MFMA, bool KTAIL>
 __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   extern __shared__ float smem[];
-  const int ldl = a.npad + 1;
-  float* lg = smem;                                   // [32][ldl] logits
-  float* tok_mx = lg + kRouteBM * ldl;
-  float* tok_sum = tok_mx + kRouteBM;
-  int* hist = reinterpret_cast<int*>(tok_sum + kRouteBM);
+  __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];
+  const int ldl = a.npad;
+  float* lg = smem;
+  int* hist = reinterpret_cast<int*>(smem) + a.lds_region_ints;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t t0 = int64_t(blockIdx.x) * kRouteBM;
   const int rows = int(min<int64_t>(kRouteBM, a.m - t0));
@@ -296,19 +294,25 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     constexpr int KS = 16 / NT;
     const int r = min(lane & 31, rows - 1);  // rows past the end repeat the last token; discarded
     const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (t0 + r) * a.d;
-    const f32x16 acc = gemm_ksplit_bf16x3<NT>(xrow, a.d, a.dpad, a.planes, a.npad, wave, lane);
+    const f32x16 acc = gemm_ksplit_bf16x3<NT, KTAIL>(xrow, a.d, a.dpad, a.planes, a.npad, wave, lane,
+                                                     int(blockIdx.x));
     const int col = (wave % NT) * 32 + (lane & 31), ks = wave / NT;
-    // partial products of the K ranges are added in a fixed order
-    for (int s = 0; s < KS; ++s) {
-      if (ks == s) {
+    if (ks > 0) {
+      float* buf = lg + (ks - 1) * kRouteBM * ldl;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float* q = lg + acc_row(i, lane) * ldl + col;
-          *q = s == 0 ? acc[i] : *q + acc[i];
-        }
-      }
-      __syncthreads();
+      for (int i = 0; i < 16; ++i) buf[acc_row(i, lane) * ldl + col] = acc[i];
     }
+    __syncthreads();
+    if (ks == 0) {  // partial tiles are added in K-range order
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int o = acc_row(i, lane) * ldl + col;
+        float v = acc[i];
+        for (int q = 1; q < KS; ++q) v += lg[(q - 1) * kRouteBM * ldl + o];
+        lg[o] = v;
+      }
+    }
+    __syncthreads();
   } else {
     // fp32 product on the vector ALUs: thread (token, expert group), fma over k in order.
     const int tl = tid >> 5, jg = tid & 31;
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
   route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
   __syncthreads();
-  route_block_tail(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg));
+  route_tail(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints);
 }
 
 // ------------------------------------------------------------------ big-n route: logits GEMM
@@ -403,11 +407,10 @@ __global__ __launch_bounds__(256) void k_route_logits_valu(RouteArgs a) {
 
 // big-n route epilogue: kRowsBM tokens per workgroup from the logits in global memory.
 __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
-  extern __shared__ float smem[];
-  float* tok_mx = smem;
-  float* tok_sum = tok_mx + kRowsBM;
-  int* hist = reinterpret_cast<int*>(tok_sum + kRowsBM);
-  int* scratch = hist + a.npad;
+  extern __shared__ int lds_i[];
+  __shared__ float tok_mx[kRowsBM], tok_sum[kRowsBM];
+  int* hist = lds_i;                                  // [npad]
+  int* scratch = hist + a.npad;                       // [lds_region_ints]
   const int64_t t0 = int64_t(blockIdx.x) * kRowsBM;
   const int rows = int(min<int64_t>(kRowsBM, a.m - t0));
   for (int j = threadIdx.x; j < a.npad; j += kRouteThreads) hist[j] = 0;
@@ -416,42 +419,62 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
   route_rows(lg, a.npad, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
   __syncthreads();
-  route_block_tail(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch);
+  route_tail(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch, a.lds_region_ints);
 }
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_router_prepare(const RoutePlan& plan, int d, int n, const float* w_r, uint16_t* planes,
                                  hipStream_t s) {
-  dim3 g(ceil_div(plan.dpad, 64), ceil_div(plan.npad, 64));
+  dim3 g(ceil_div(plan.dpad, 32), ceil_div(plan.npad, 32));
   hipLaunchKernelGGL(k_router_split, g, dim3(256), 0, s, w_r, planes, d, n, plan.npad, plan.dpad);
   return hipGetLastError();
 }
 
 int route_chunk_tokens(const RoutePlan& plan) { return plan.fused ? kRouteBM : kRowsBM; }
 
-hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s) {
+// LDS ints of the region each route kernel reserves: fused, the K-split
+// partial tiles (also the logits tile and the last block's scratch); rows
+// kernel, the last block's scratch.
+static int route_region_ints(const RoutePlan& plan, int n) {
+  if (!plan.fused) return n + 4096;
+  const int nt = plan.npad / 32;
+  const int ks = 16 / (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
+  const int tiles = std::max(ks - 1, 1);
+  return std::max(tiles * kRouteBM * plan.npad, n + 2 * kMaxSuperChunks * 16);
+}
+
+template <int NT>
+static void launch_fused(const RoutePlan& plan, const RouteArgs& a, dim3 g, size_t lds, hipStream_t s) {
+  if (plan.dpad == a.d)
+    hipLaunchKernelGGL((k_route_fused<NT, true, false>), g, dim3(kRouteThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_route_fused<NT, true, true>), g, dim3(kRouteThreads), lds, s, a);
+}
+
+hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_t s) {
+  RouteArgs a = a_in;
+  a.lds_region_ints = route_region_ints(plan, a.n);
   if (plan.mfma && !a.planes_ready) launch_router_prepare(plan, a.d, a.n, a.w_r, const_cast<uint16_t*>(a.planes), s);
   if (plan.fused) {
-    const unsigned nblk = unsigned(ceil_div64(a.m, kRouteBM));
-    const size_t lds = (size_t(kRouteBM) * (plan.npad + 1) + 2 * kRouteBM) * sizeof(float) + plan.npad * sizeof(int);
+    const dim3 g(unsigned(ceil_div64(a.m, kRouteBM)));
+    const size_t lds = (size_t(a.lds_region_ints) + plan.npad) * sizeof(float);
     const int nt = plan.npad / 32;
-    const dim3 g(nblk), b(kRouteThreads);
     if (!plan.mfma)
-      hipLaunchKernelGGL((k_route_fused<1, false>), g, b, lds, s, a);
+      hipLaunchKernelGGL((k_route_fused<1, false, false>), g, dim3(kRouteThreads), lds, s, a);
     else if (nt == 1)
-      hipLaunchKernelGGL((k_route_fused<1, true>), g, b, lds, s, a);
+      launch_fused<1>(plan, a, g, lds, s);
     else if (nt == 2)
-      hipLaunchKernelGGL((k_route_fused<2, true>), g, b, lds, s, a);
+      launch_fused<2>(plan, a, g, lds, s);
     else if (nt <= 4)
-      hipLaunchKernelGGL((k_route_fused<4, true>), g, b, lds, s, a);
+      launch_fused<4>(plan, a, g, lds, s);
     else
-      hipLaunchKernelGGL((k_route_fused<8, true>), g, b, lds, s, a);
+      launch_fused<8>(plan, a, g, lds, s);
   } else {
     if (plan.mfma)
       hipLaunchKernelGGL(k_route_logits_mfma, dim3(unsigned(ceil_div64(a.m, 128)), plan.npad / 128), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(k_route_logits_valu, dim3(unsigned(ceil_div64(a.m, 32)), plan.npad / 64), dim3(256), 0, s, a);
-    const size_t lds = 2 * kRowsBM * sizeof(float) + plan.npad * sizeof(int) + size_t(a.n) * sizeof(int);
+    const size_t lds = (size_t(plan.npad) + a.lds_region_ints) * sizeof(int);
     hipLaunchKernelGGL(k_route_rows, dim3(unsigned(ceil_div64(a.m, kRowsBM))), dim3(kRouteThreads), lds, s, a);
   }
   return hipGetLastError();
