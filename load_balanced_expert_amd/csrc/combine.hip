@@ -50,34 +50,47 @@ __device__ __forceinline__ void store_vec(void* p, int64_t i, const float (&v)[8
   }
 }
 
+// One wave per token: the token's (row, gate) pairs are wave-uniform, so the
+// expert rows it gathers are addressed right after one scalar load; lanes
+// stream the d/8 16-byte vectors of the row.
 template <bool XB, bool YB>
 __global__ __launch_bounds__(256) void k_combine_vec(int64_t m, int d, int k, const void* __restrict__ y,
                                                      const float* __restrict__ gate,
                                                      const int32_t* __restrict__ t2r, const void* __restrict__ res,
                                                      void* __restrict__ out) {
-  const int64_t vpr = d / 8;
-  const int64_t items = m * vpr;
-#pragma unroll 2
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < items; i += int64_t(gridDim.x) * 256) {
-    const int64_t t = i / vpr, v = i - t * vpr;
-    float acc[8];
-    if (res) {
-      load_vec<XB>(res, i, acc);
-    } else {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + wave;
+  if (t >= m) return;
+  const int vpr = d / 8;
+  for (int v0 = 0; v0 < vpr; v0 += 128) {
+    float acc[2][8];
+    const int vv[2] = {v0 + lane, v0 + 64 + lane};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      if (res && vv[u] < vpr) {
+        load_vec<XB>(res, t * vpr + vv[u], acc[u]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
+      }
     }
     for (int r = 0; r < k; ++r) {
       const int32_t row = t2r[t * k + r];
       if (row >= 0) {
         const float g = gate[t * k + r];
-        float yv[8];
-        load_vec<YB>(y, int64_t(row) * vpr + v, yv);
+        float yv[2][8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, yv[q], acc[q]);
+        for (int u = 0; u < 2; ++u)
+          if (vv[u] < vpr) load_vec<YB>(y, int64_t(row) * vpr + vv[u], yv[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[u][q] = fmaf(g, yv[u][q], acc[u][q]);
       }
     }
-    store_vec<XB>(out, i, acc);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (vv[u] < vpr) store_vec<XB>(out, t * vpr + vv[u], acc[u]);
   }
 }
 
@@ -111,8 +124,7 @@ hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, c
   const uintptr_t al = reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(out) |
                        reinterpret_cast<uintptr_t>(residual);
   if (d % 8 == 0 && (al % 16) == 0) {
-    const int64_t items = m * (d / 8);
-    const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(items, 512), 65536));
+    const unsigned blocks = unsigned(ceil_div64(m, 4));
     if (x_bf16 && y_bf16)
       hipLaunchKernelGGL((k_combine_vec<true, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
     else if (x_bf16)

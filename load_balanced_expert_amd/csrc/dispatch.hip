@@ -101,7 +101,14 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
     if (ls >= 0) {
       const int e = a.idx[p];
       int base = a.super_prefix[int64_t(s) * n + e];
-      for (int cc = s * a.sup; cc < c; ++cc) base += a.chunk_counts[int64_t(cc) * n + e];
+      for (int cc = s * a.sup; cc < c; cc += 16) {   // independent loads in batches of 16
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = a.chunk_counts[int64_t(min(cc + u, c - 1)) * n + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (cc + u < c) base += v[u];
+      }
       const int slot = base + ls;
       if (slot < a.capacity) row = a.expert_offsets[e] + slot;
     }

@@ -112,10 +112,23 @@ __device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds,
       const int c1 = min(a.nch, (s + 1) * a.sup);
       int cs = 0;
       float ps = 0.f;
-      for (int c = s * a.sup; c < c1; ++c) {
-        const int64_t o = int64_t(c) * n + j0 + jj;
-        cs += load_agent(a.chunk_counts + o);
-        if (a.chunk_psum) ps += load_agent(a.chunk_psum + o);
+      // 16 independent loads in flight per batch (these bypass the L2), then a fixed-order sum
+      for (int c = s * a.sup; c < c1; c += 16) {
+        int vc[16];
+        float vp[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int64_t o = int64_t(min(c + u, c1 - 1)) * n + j0 + jj;
+          vc[u] = load_agent(a.chunk_counts + o);
+          vp[u] = a.chunk_psum ? load_agent(a.chunk_psum + o) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (c + u < c1) {
+            cs += vc[u];
+            ps += vp[u];
+          }
+        }
       }
       sc[s * w + jj] = cs;
       sp[s * w + jj] = ps;
