@@ -31,45 +31,83 @@ constexpr int kRouteBM = 32;      // tokens per route workgroup (n <= 256)
 constexpr int kRowsBM = 256;      // tokens per route-epilogue workgroup (n > 256)
 constexpr int kRouteThreads = 1024;  // 16 waves
 
+// LDS ints of the region each route kernel reserves: fused, the x tile (if
+// staged), the K-split partial tiles (also the logits tile) and the last
+// block's scratch, which share one region; rows kernel, the scratch.
+constexpr int kFusedLdsBudgetInts = 15360;   // 60 KiB for the region (+ histogram, statics < 64 KiB)
+static int fused_partial_ints(const RoutePlan& plan, int n) {
+  const int nt = plan.npad / 32;
+  const int ks = 16 / (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
+  return std::max(std::max(ks - 1, 1) * kRouteBM * plan.npad, n + 2 * kMaxSuperChunks * 16);
+}
+static int x_tile_ints(const RoutePlan& plan) { return kRouteBM * (plan.dpad + 8) / 2; }
+static bool stage_x(const RoutePlan& plan, int n) {
+  return std::max(x_tile_ints(plan), fused_partial_ints(plan, n)) + plan.npad <= kFusedLdsBudgetInts + 256;
+}
+static int route_region_ints(const RoutePlan& plan, int n) {
+  if (!plan.fused) return n + 4096;
+  const int part = fused_partial_ints(plan, n);
+  return stage_x(plan, n) ? std::max(part, x_tile_ints(plan)) : part;
+}
+
 RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
   RoutePlan p{};
   p.fused = n <= kFusedMaxN;
+  // matrix cores need d % 8 == 0 (16-byte rows); without the LDS x tile also d % 32 == 0
   p.mfma = x_bf16 && (d % 8 == 0);
   p.npad = p.fused ? round_up(n, 32) : round_up(n, 128);
   p.dpad = round_up(d, 32);
+  if (p.fused && p.mfma && p.dpad != d && !stage_x(p, n)) p.mfma = false;   // global x rows need d % 32 == 0
   p.planes_bytes = p.mfma ? size_t(3) * p.npad * p.dpad * sizeof(uint16_t) : 0;
   p.logits_bytes = p.fused ? 0 : size_t(m) * p.npad * sizeof(float);
   return p;
 }
 
 // ------------------------------------------------------------------ W_r split
-// planes[p][j][k], p = 0 (hi), 1 (mid), 2 (lo); zero for j >= n or k >= d.
+// The three planes are stored fragment-major: for expert tile t (32 experts),
+// K block kb (32 inputs), plane p and MFMA substep s, the 64 lanes' 8-element
+// B fragments are contiguous (1 KiB), so every fragment load of the GEMM is
+// one fully coalesced 16-byte-per-lane access.  Lane l = r + 32h holds expert
+// t*32 + r and inputs kb*32 + 16h + 8s + [0, 8).
+__host__ __device__ inline size_t frag_off(int t, int kb, int p, int s, int nkb) {
+  return ((((size_t(t) * nkb + kb) * 3 + p) * 2 + s) * 64) * 8;
+}
+
+// One workgroup per (expert tile, K block): transpose through LDS, split each
+// fp32 weight into hi + mid + lo bf16 (exact), write the fragments.
 __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ w,
                                                        uint16_t* __restrict__ planes, int d, int n,
                                                        int npad, int dpad) {
   __shared__ float tile[32][33];
-  const int kb = blockIdx.x * 32, jb = blockIdx.y * 32;
+  const int t = blockIdx.x, kb = blockIdx.y, nkb = dpad / 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int r = ty; r < 32; r += 8) {
-    const int k = kb + r, j = jb + tx;
+    const int k = kb * 32 + r, j = t * 32 + tx;
     tile[r][tx] = (k < d && j < n) ? w[size_t(k) * n + j] : 0.f;
   }
   __syncthreads();
-  const size_t plane = size_t(npad) * dpad;
-  for (int r = ty; r < 32; r += 8) {
-    const int j = jb + r, k = kb + tx;
-    if (j < npad && k < dpad) {
-      const float v = tile[tx][r];
-      const uint16_t hi = f32_to_bf16(v);
-      const float r1 = v - bf16_to_f32(hi);     // exact: |r1| <= half a bf16 ulp of v
-      const uint16_t mid = f32_to_bf16(r1);
-      const float r2 = r1 - bf16_to_f32(mid);   // exact, at most 8 significant bits
-      const uint16_t lo = f32_to_bf16(r2);      // exact
-      const size_t o = size_t(j) * dpad + k;
-      planes[o] = hi;
-      planes[plane + o] = mid;
-      planes[2 * plane + o] = lo;
-    }
+  // 1024 (s, lane, e) slots per plane, 4 consecutive per thread
+  uint16_t out[3][4];
+  const int o0 = threadIdx.x * 4;
+  const int s = o0 >> 9, lane = (o0 >> 3) & 63, e0 = o0 & 7;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float v = tile[16 * h + 8 * s + e0 + q][r];
+    const uint16_t hi = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi);     // exact: |r1| <= half a bf16 ulp of v
+    const uint16_t mid = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid);   // exact, at most 8 significant bits
+    out[0][q] = hi;
+    out[1][q] = mid;
+    out[2][q] = f32_to_bf16(r2);               // exact
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    uint16_t* dst = planes + frag_off(t, kb, p, s, nkb) + lane * 8 + e0;
+    const uint64_t v = uint64_t(out[p][0]) | (uint64_t(out[p][1]) << 16) | (uint64_t(out[p][2]) << 32) |
+                       (uint64_t(out[p][3]) << 48);
+    *reinterpret_cast<uint64_t*>(dst) = v;
   }
 }
 
@@ -83,36 +121,27 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
-// 8 bf16 at p (a valid address) or zeros when !ok, without a branch.
-__device__ __forceinline__ bf16x8 load8_or_zero(const uint16_t* p, bool ok) {
-  u32x4 v = *reinterpret_cast<const u32x4*>(p);
-  const uint32_t msk = ok ? 0xFFFFFFFFu : 0u;
-  v &= msk;
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // Block product of 32 tokens x npad experts on bf16 MFMA, split over the 16
 // waves of the workgroup: wave w owns expert tile (w % NT) and the K-block
-// range ks = w / NT of KS = 16 / NT equal ranges.  Lane l holds token row
-// (l & 31) and the k-slice [kb*32 + 16*(l>>5), +16) of each 32-wide K block;
-// substep s uses its elements [8s, 8s+8).  A and B use the same lane -> k
-// mapping, so every k meets itself exactly once.  The loop body is
-// branch-free: the next K block's operands are always loaded (the last
-// iteration reloads its own block) before the current block's MFMAs, so the
-// wait before the MFMAs covers only the older loads.  Each workgroup starts
-// its K range at a different block (rot) to spread the shared W_r reads over
-// the L2 channels.
-template <int NT, bool KTAIL>
-__device__ __forceinline__ f32x16 gemm_ksplit_bf16x3(const uint16_t* __restrict__ xrow, int d, int dpad,
-                                                     const uint16_t* __restrict__ planes, int npad, int wave,
+// range ks = w / NT of KS = 16 / NT equal ranges.  Lane l = r + 32h holds
+// token row r and, in substep s of K block kb, inputs kb*32 + 16h + 8s +
+// [0, 8) — the same lane -> k mapping as the W_r fragments, so every k meets
+// itself exactly once.  arow points at lane (r, h)'s row r, input 16h, in an
+// LDS copy of the x tile or in global memory; B fragments are one coalesced
+// 1 KiB load each.  The loop body is branch-free with ping-pong
+// operand buffers: the next K block's fragments are in flight while the
+// current block is multiplied (scheduling barriers keep the loads ahead of
+// the MFMAs).  Each workgroup starts its K range at a different block (rot)
+// to spread the shared W_r reads over the L2 channels.
+template <int NT>
+__device__ __forceinline__ f32x16 gemm_ksplit_bf16x3(const uint16_t* __restrict__ arow,
+                                                     const uint16_t* __restrict__ planes, int dpad, int wave,
                                                      int lane, int rot) {
   constexpr int KS = 16 / NT;
-  const int h = lane >> 5, r32 = lane & 31;
-  const size_t plane = size_t(npad) * dpad;
   const int tile = wave % NT, ks = wave / NT;
   const int nkb = dpad / 32;
   const int kb0 = ks * nkb / KS, cnt = (ks + 1) * nkb / KS - kb0;
-  const uint16_t* brow = planes + size_t(tile * 32 + r32) * dpad;
+  const uint16_t* bt = planes + frag_off(tile, 0, 0, 0, nkb) + lane * 8;
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -121,18 +150,13 @@ __device__ __forceinline__ f32x16 gemm_ksplit_bf16x3(const uint16_t* __restrict_
   auto load = [&](int i, bf16x8 (&aa)[2], bf16x8 (&bb)[3][2]) {
     int r = i + rot;
     r = r >= cnt ? r - cnt : r;
-    const int k0 = (kb0 + r) * 32 + 16 * h;
-    if constexpr (KTAIL) {
-      aa[0] = load8_or_zero(xrow + min(k0, d - 8), k0 + 8 <= d);
-      aa[1] = load8_or_zero(xrow + min(k0 + 8, d - 8), k0 + 16 <= d);
-    } else {
-      aa[0] = load8(xrow + k0);
-      aa[1] = load8(xrow + k0 + 8);
-    }
+    const int kb = kb0 + r;
+    aa[0] = load8(arow + kb * 32);
+    aa[1] = load8(arow + kb * 32 + 8);
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
-      bb[p][0] = load8(brow + p * plane + k0);
-      bb[p][1] = load8(brow + p * plane + k0 + 8);
+      bb[p][0] = load8(bt + (size_t(kb) * 3 + p) * 1024);
+      bb[p][1] = load8(bt + (size_t(kb) * 3 + p) * 1024 + 512);
     }
   };
   auto mma = [&](const bf16x8 (&aa)[2], const bf16x8 (&bb)[3][2]) {
@@ -276,9 +300,11 @@ __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
 }
 
 // ------------------------------------------------------------------ fused route (n <= 256)
-// LDS: KS-1 partial tiles [32][npad] (the first becomes the logits tile and,
-// in the last workgroup, the finishing scratch), then the histogram.
-template <int NT, bool MFMA, bool KTAIL>
+// LDS region (lds_region_ints): first the bf16 x tile [32][dpad + 8] (XLDS),
+// then, after the product, the KS-1 partial tiles [32][npad]; the first of
+// them becomes the logits tile and, in the last workgroup, the finishing
+// scratch.  The histogram follows the region.
+template <int NT, bool MFMA, bool XLDS>
 __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   extern __shared__ float smem[];
   __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];
@@ -292,11 +318,26 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
 
   if constexpr (MFMA) {
     constexpr int KS = 16 / NT;
-    const int r = min(lane & 31, rows - 1);  // rows past the end repeat the last token; discarded
-    const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (t0 + r) * a.d;
-    const f32x16 acc = gemm_ksplit_bf16x3<NT, KTAIL>(xrow, a.d, a.dpad, a.planes, a.npad, wave, lane,
-                                                     int(blockIdx.x));
+    const uint16_t* x = static_cast<const uint16_t*>(a.x);
+    const uint16_t* arow;
+    if constexpr (XLDS) {
+      // stage the 32 x rows in LDS with coalesced 16-byte loads (zero padding past the end)
+      uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+      const int ldx = a.dpad + 8, cpr = a.dpad / 8;
+      for (int c = tid; c < kRouteBM * cpr; c += kRouteThreads) {
+        const int r = c / cpr, k = (c - r * cpr) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < rows && k < a.d) v = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
+        *reinterpret_cast<u32x4*>(xs + r * ldx + k) = v;
+      }
+      __syncthreads();
+      arow = xs + (lane & 31) * ldx + 16 * (lane >> 5);
+    } else {
+      arow = x + (t0 + min(lane & 31, rows - 1)) * a.d + 16 * (lane >> 5);  // requires d == dpad
+    }
+    const f32x16 acc = gemm_ksplit_bf16x3<NT>(arow, a.planes, a.dpad, wave, lane, int(blockIdx.x));
     const int col = (wave % NT) * 32 + (lane & 31), ks = wave / NT;
+    if constexpr (XLDS) __syncthreads();   // the x tile is dead before partials overwrite it
     if (ks > 0) {
       float* buf = lg + (ks - 1) * kRouteBM * ldl;
 #pragma unroll
@@ -340,14 +381,14 @@ __global__ __launch_bounds__(256) void k_route_logits_mfma(RouteArgs a) {
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
   const int64_t tb = int64_t(blockIdx.x) * 128 + 64 * wm;
   const int jb = blockIdx.y * 128 + 64 * wn;
-  const size_t plane = size_t(a.npad) * a.dpad;
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* xr[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) xr[mt] = x + min<int64_t>(tb + 32 * mt + r32, a.m - 1) * a.d;
+  const int nkb = a.dpad / 32;
   const uint16_t* br[2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) br[nt] = a.planes + size_t(jb + 32 * nt + r32) * a.dpad;
+  for (int nt = 0; nt < 2; ++nt) br[nt] = a.planes + frag_off((jb + 32 * nt) / 32, 0, 0, 0, nkb) + lane * 8;
   f32x16 acc[2][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -355,8 +396,8 @@ __global__ __launch_bounds__(256) void k_route_logits_mfma(RouteArgs a) {
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
-  for (int kb = 0; kb < a.dpad; kb += 32) {
-    const int k0 = kb + 16 * h;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * 32 + 16 * h;
     bf16x8 av[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -367,7 +408,8 @@ __global__ __launch_bounds__(256) void k_route_logits_mfma(RouteArgs a) {
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
       for (int p = 0; p < 3; ++p) {
-        const bf16x8 b0 = load8(br[nt] + p * plane + k0), b1 = load8(br[nt] + p * plane + k0 + 8);
+        const uint16_t* f = br[nt] + (size_t(kb) * 3 + p) * 1024;
+        const bf16x8 b0 = load8(f), b1 = load8(f + 512);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt][0], b0, acc[mt][nt], 0, 0, 0);
@@ -425,30 +467,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
 // ------------------------------------------------------------------ launchers
 hipError_t launch_router_prepare(const RoutePlan& plan, int d, int n, const float* w_r, uint16_t* planes,
                                  hipStream_t s) {
-  dim3 g(ceil_div(plan.dpad, 32), ceil_div(plan.npad, 32));
+  if (!plan.mfma) return hipSuccess;   // the vector-ALU product reads W_r directly
+  const dim3 g(plan.npad / 32, plan.dpad / 32);   // (expert tile, K block)
   hipLaunchKernelGGL(k_router_split, g, dim3(256), 0, s, w_r, planes, d, n, plan.npad, plan.dpad);
   return hipGetLastError();
 }
 
 int route_chunk_tokens(const RoutePlan& plan) { return plan.fused ? kRouteBM : kRowsBM; }
 
-// LDS ints of the region each route kernel reserves: fused, the K-split
-// partial tiles (also the logits tile and the last block's scratch); rows
-// kernel, the last block's scratch.
-static int route_region_ints(const RoutePlan& plan, int n) {
-  if (!plan.fused) return n + 4096;
-  const int nt = plan.npad / 32;
-  const int ks = 16 / (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
-  const int tiles = std::max(ks - 1, 1);
-  return std::max(tiles * kRouteBM * plan.npad, n + 2 * kMaxSuperChunks * 16);
-}
-
 template <int NT>
 static void launch_fused(const RoutePlan& plan, const RouteArgs& a, dim3 g, size_t lds, hipStream_t s) {
-  if (plan.dpad == a.d)
-    hipLaunchKernelGGL((k_route_fused<NT, true, false>), g, dim3(kRouteThreads), lds, s, a);
-  else
+  if (stage_x(plan, a.n))
     hipLaunchKernelGGL((k_route_fused<NT, true, true>), g, dim3(kRouteThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_route_fused<NT, true, false>), g, dim3(kRouteThreads), lds, s, a);
 }
 
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_t s) {
