@@ -19,7 +19,7 @@ struct Layout {
   RoutePlan rp;
   int64_t pairs, rows_bound;
   int route_ct, disp_ct, nch, sup, nch_route, sup_route;
-  size_t chunk_psum, super_prefix;
+  size_t super_prefix;
 };
 
 bool shape_valid(const moe_shape* s) {
@@ -58,8 +58,7 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   L.nch_route = int(ceil_div64(s.m, L.route_ct));
   L.sup_route = super_chunk(L.nch_route);
   const int nch_max = std::max(L.nch, L.nch_route);
-  L.chunks = o; o += al(size_t(nch_max) * s.n * sizeof(int32_t));
-  L.chunk_psum = o; o += al(size_t(nch_max) * s.n * sizeof(float));
+  L.chunks = o; o += al(size_t(nch_max) * s.n * sizeof(uint64_t));
   L.super_prefix = o; o += al(size_t(kMaxSuperChunks) * s.n * sizeof(int32_t));
   L.r2t = o; o += al(size_t(L.pairs) * 4);
   L.dispatch_end = o;
@@ -131,8 +130,8 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
   a.P = ex.P;
   a.aux = ex.aux;
   a.alpha = ex.alpha;
-  a.chunk_counts = at<int32_t>(ws, L.chunks);
-  a.chunk_psum = (prob_sum || ex.P || ex.aux) ? at<float>(ws, L.chunk_psum) : nullptr;
+  a.chunks = at<uint64_t>(ws, L.chunks);
+  a.want_psum = prob_sum || ex.P || ex.aux;
   a.sup = L.sup_route;
   a.capacity = -1;
   if (ex.disp) {
@@ -158,7 +157,7 @@ DispatchArgs dispatch_args(const moe_shape& s, const Layout& L, int32_t capacity
   a.chunk_tokens = L.disp_ct;
   a.nch = L.nch;
   a.sup = L.sup;
-  a.chunk_counts = at<int32_t>(ws, L.chunks);
+  a.chunks = at<uint64_t>(ws, L.chunks);
   a.super_prefix = at<int32_t>(ws, L.super_prefix);
   a.token_to_row = t2r;
   a.drop_mask = drop;

@@ -31,7 +31,7 @@ static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 size_t balance_ws_bytes(int64_t m, int n, int k, bool exact) {
   size_t b = al256(size_t(m) * n * sizeof(float));   // s transposed
   b += al256(size_t(m) * sizeof(float));              // alpha
-  b += al256(size_t(ceil_div64(m, kQbRowsPerBlock)) * n * sizeof(int32_t));  // per-workgroup counts
+  b += al256(size_t(ceil_div64(m, kQbRowsPerBlock)) * n * sizeof(uint64_t));  // per-workgroup chunk rows
   if (exact) b += 2 * al256(size_t(m) * k * sizeof(int32_t));  // assignment, per-expert token lists
   return b;
 }
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_qb_transpose(const float* __restrict__ 
 // ------------------------------------------------------------------ rows: top-k and α
 template <bool IDX, bool ALPHA>
 __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __restrict__ beta,
-                                                 float* __restrict__ alpha, int32_t* __restrict__ chunk_counts) {
+                                                 float* __restrict__ alpha, uint64_t* __restrict__ chunks) {
   extern __shared__ int hist[];   // [n], then the finishing scratch
   const int n = a.n, k = a.k;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -97,11 +97,11 @@ __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __r
   }
   if (!IDX) return;
   __syncthreads();
-  for (int j = threadIdx.x; j < n; j += 256) store_agent(chunk_counts + int64_t(blockIdx.x) * n + j, int32_t(hist[j]));
+  for (int j = threadIdx.x; j < n; j += 256) store_agent(chunks + int64_t(blockIdx.x) * n + j, pack_chunk(hist[j], 0.f));
   __shared__ int s_flag;
   if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
   FinalizeArgs f{};
-  f.chunk_counts = chunk_counts;
+  f.chunks = chunks;
   f.nch = int(gridDim.x);
   f.sup = super_chunk(f.nch);
   f.n = n;
@@ -386,8 +386,8 @@ hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
   ws += al256(size_t(a.m) * a.n * sizeof(float));
   float* alpha_int = reinterpret_cast<float*>(ws);
   ws += al256(size_t(a.m) * sizeof(float));
-  int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);
-  ws += al256(size_t(ceil_div64(a.m, kQbRowsPerBlock)) * a.n * sizeof(int32_t));
+  uint64_t* chunks = reinterpret_cast<uint64_t*>(ws);
+  ws += al256(size_t(ceil_div64(a.m, kQbRowsPerBlock)) * a.n * sizeof(uint64_t));
   int32_t* xi = reinterpret_cast<int32_t*>(ws);
   float* alpha = a.alpha_out ? a.alpha_out : alpha_int;
 
@@ -397,18 +397,18 @@ hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_qb_transpose, dim3(unsigned(ceil_div64(a.m, 64)), ceil_div(a.n, 64)), dim3(256), 0, s, a.s,
                      sT, a.m, a.n);
   if (a.mode == 1) {  // online: route with the old β, then one α and one β step
-    hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunk_counts);
+    hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
     hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q);
     return hipGetLastError();
   }
   for (int it = 0; it < a.iters; ++it) {
-    hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, a.beta, alpha, chunk_counts);
+    hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, a.beta, alpha, chunks);
     hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q);
   }
   if (a.exact)
     hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi);
   else
-    hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunk_counts);
+    hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
   return hipGetLastError();
 }
 

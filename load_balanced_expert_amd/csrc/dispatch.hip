@@ -30,8 +30,8 @@ constexpr int kDispPrefixBuf = 4096;   // LDS ints for the last block's super-ch
 size_t dispatch_ws_bytes(int64_t m, int k, int n, int chunk_tokens) {
   const int64_t nch = ceil_div64(m, chunk_tokens);
   (void)k;
-  // chunk counts, chunk score sums (route), super-chunk prefixes
-  return 2 * (size_t(nch) * n * sizeof(int32_t) + 256) + size_t(kMaxSuperChunks) * n * sizeof(int32_t) + 256;
+  // packed chunk rows (count, route score sum), super-chunk prefixes
+  return size_t(nch) * n * sizeof(uint64_t) + 256 + size_t(kMaxSuperChunks) * n * sizeof(int32_t) + 256;
 }
 
 __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
@@ -48,11 +48,11 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
     if (unsigned(e) < unsigned(n)) atomicAdd(&hist[e], 1);   // ids outside [0, n) are dropped
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < n; j += kDispThreads) store_agent(a.chunk_counts + c * n + j, int32_t(hist[j]));
+  for (int j = threadIdx.x; j < n; j += kDispThreads) store_agent(a.chunks + c * n + j, pack_chunk(hist[j], 0.f));
   __shared__ int s_flag;
   if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
   FinalizeArgs f{};
-  f.chunk_counts = a.chunk_counts;
+  f.chunks = a.chunks;
   f.nch = a.nch;
   f.sup = a.sup;
   f.n = n;
@@ -101,10 +101,12 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
     if (ls >= 0) {
       const int e = a.idx[p];
       int base = a.super_prefix[int64_t(s) * n + e];
-      for (int cc = s * a.sup; cc < c; cc += 16) {   // independent loads in batches of 16
+      // counts are the low words of the chunk rows; independent loads in batches of 16
+      const int32_t* cw = reinterpret_cast<const int32_t*>(a.chunks);
+      for (int cc = s * a.sup; cc < c; cc += 16) {
         int v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = a.chunk_counts[int64_t(min(cc + u, c - 1)) * n + e];
+        for (int u = 0; u < 16; ++u) v[u] = cw[2 * (int64_t(min(cc + u, c - 1)) * n + e)];
 #pragma unroll
         for (int u = 0; u < 16; ++u)
           if (cc + u < c) base += v[u];

@@ -41,8 +41,8 @@ struct RouteArgs {
   float* P;
   float* aux;
   float alpha;
-  int32_t* chunk_counts;  // [route workgroups, n] chunk rows (workspace)
-  float* chunk_psum;      // [route workgroups, n] or nullptr when no score sum is wanted
+  uint64_t* chunks;       // [route workgroups, n] packed (count, score sum) chunk rows (workspace)
+  bool want_psum;         // score sums wanted (prob_sum, P or aux)
   int sup;                // chunks per super chunk
   int32_t capacity;       // < 0: no capacity prefix sums
   int32_t* expert_offsets;
@@ -71,7 +71,7 @@ struct DispatchArgs {
   int32_t capacity;     // >= 0 (unlimited is passed as pairs)
   int chunk_tokens;     // tokens per chunk (== route workgroup tokens when the route made the counts)
   int nch, sup;         // chunks, chunks per super chunk
-  int32_t* chunk_counts;  // [nch, n]
+  uint64_t* chunks;       // [nch, n] packed chunk rows (count in the low word)
   int32_t* super_prefix;  // [ceil(nch / sup), n]
   int32_t* token_to_row;
   uint8_t* drop_mask;

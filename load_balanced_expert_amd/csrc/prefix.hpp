@@ -42,9 +42,15 @@ __device__ __forceinline__ bool last_workgroup(uint32_t* ticket, unsigned nblock
   return last;
 }
 
+// A chunk row entry: count in the low 32 bits, fp32 score sum in the high 32.
+__device__ __forceinline__ uint64_t pack_chunk(int count, float psum) {
+  return uint64_t(uint32_t(count)) | (uint64_t(__float_as_uint(psum)) << 32);
+}
+__device__ __forceinline__ int chunk_count(uint64_t v) { return int(uint32_t(v)); }
+__device__ __forceinline__ float chunk_psum(uint64_t v) { return __uint_as_float(uint32_t(v >> 32)); }
+
 struct FinalizeArgs {
-  const int32_t* chunk_counts;  // [nch, n]  agent-scope stores of every chunk
-  const float* chunk_psum;      // [nch, n]  or nullptr
+  const uint64_t* chunks;       // [nch, n]  agent-scope stores of every chunk (pack_chunk)
   int nch, sup, n;
   int64_t m;                    // tokens (for f and P)
   int32_t* counts;              // [n] out or nullptr
@@ -114,19 +120,14 @@ __device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds,
       float ps = 0.f;
       // 16 independent loads in flight per batch (these bypass the L2), then a fixed-order sum
       for (int c = s * a.sup; c < c1; c += 16) {
-        int vc[16];
-        float vp[16];
+        uint64_t v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int64_t o = int64_t(min(c + u, c1 - 1)) * n + j0 + jj;
-          vc[u] = load_agent(a.chunk_counts + o);
-          vp[u] = a.chunk_psum ? load_agent(a.chunk_psum + o) : 0.f;
-        }
+        for (int u = 0; u < 16; ++u) v[u] = load_agent(a.chunks + int64_t(min(c + u, c1 - 1)) * n + j0 + jj);
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           if (c + u < c1) {
-            cs += vc[u];
-            ps += vp[u];
+            cs += chunk_count(v[u]);
+            ps += chunk_psum(v[u]);
           }
         }
       }

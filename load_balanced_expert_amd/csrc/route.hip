@@ -259,26 +259,136 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
   }
 }
 
-// Chunk row of this workgroup: per-expert counts and (if wanted) Σ over its
-// tokens of score_j(t) in token order; the last workgroup publishes the
-// totals, the optional load statistics and capacity prefix sums.
+// Half-wave (32 lanes) reductions; every lane of the half gets the result.
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 32));
+  return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 32);
+  return v;
+}
+__device__ __forceinline__ void half_argbest(float& key, int& ix) {
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    const float ok = __shfl_xor(key, off, 32);
+    const int oi = __shfl_xor(ix, off, 32);
+    if (better(ok, oi, key, ix)) {
+      key = ok;
+      ix = oi;
+    }
+  }
+}
+
+// Fused-route epilogue for k <= 32: one half-wave per token, NV = npad/32
+// logits per lane in registers (expert j = lane + 32u).  Computes the scores
+// (softmax or sigmoid), the top-k by key (logit, or score + bias), the gates
+// and the histogram, then overwrites the token's LDS row with its scores so
+// that the per-expert score sums are plain column sums.
+template <int NV>
+__device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int64_t t0, const EpiArgs& e,
+                                                int32_t* __restrict__ idx, float* __restrict__ gate_out,
+                                                int* hist) {
+  const int half = threadIdx.x >> 5, l = threadIdx.x & 31;
+  const int nhalf = kRouteThreads / 32;
+  for (int tl = half; tl < rows; tl += nhalf) {
+    float* row = lg + tl * ld;
+    float h[NV], sc[NV], bv[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int j = l + 32 * u;
+      h[u] = j < e.n ? row[j] : -INFINITY;
+      bv[u] = (e.bias && j < e.n) ? e.bias[j] : 0.f;
+    }
+    if (e.score == 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) mx = fmaxf(mx, h[u]);
+      mx = half_max(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        sc[u] = l + 32 * u < e.n ? expf(h[u] - mx) : 0.f;
+        sum += sc[u];
+      }
+      sum = half_sum(sum);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) sc[u] = sc[u] / sum;
+    } else {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) sc[u] = l + 32 * u < e.n ? sigm(h[u]) : 0.f;
+    }
+    // k rounds: each picks the best (key, j) strictly after the previous pick
+    float last_key = INFINITY;
+    int last_j = -1, my_j = 0;
+    float my_score = 0.f, total = 0.f;
+    for (int r = 0; r < e.k; ++r) {
+      float bk = -INFINITY;
+      int bj = 0x7FFFFFFF;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int j = l + 32 * u;
+        if (j < e.n) {
+          const float key = e.bias ? sc[u] + bv[u] : h[u];
+          if (better(last_key, last_j, key, j) && better(key, j, bk, bj)) {
+            bk = key;
+            bj = j;
+          }
+        }
+      }
+      half_argbest(bk, bj);
+      last_key = bk;
+      last_j = bj;
+      // the chosen expert's score, from the lane that holds it
+      float mine = 0.f;
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (l + 32 * u == bj) mine = sc[u];
+      const float sc_b = __shfl(mine, bj & 31, 32);
+      total += sc_b;
+      if (l == r) {
+        my_j = bj;
+        my_score = sc_b;
+      }
+      if (l == 0) atomicAdd(&hist[bj], 1);
+    }
+    if (l < e.k) {
+      const int64_t o = (t0 + tl) * e.k + l;
+      idx[o] = my_j;
+      gate_out[o] = e.gate == 1 ? my_score / total : my_score;
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      if (l + 32 * u < ld) row[l + 32 * u] = sc[u];
+  }
+}
+
+// Chunk row of this workgroup: per expert, its count and (if wanted) Σ over
+// its tokens of score_j(t) in token order, packed into one 64-bit word; the
+// last workgroup publishes the totals, the optional load statistics and the
+// capacity prefix sums.  SCORES: lg rows already hold the scores (fused
+// epilogue); otherwise they hold logits and the scores are recomputed.
+template <bool SCORES>
 __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows, const EpiArgs& e,
                                            const float* tok_mx, const float* tok_sum, const int* hist,
                                            const RouteArgs& a, int* scratch, int scratch_ints) {
   const int64_t row0 = int64_t(blockIdx.x) * e.n;
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
-    if (a.chunk_psum) {
-      float acc = 0.f;
-      for (int tl = 0; tl < rows; ++tl) acc += score_of(e.score, lg[int64_t(tl) * ld + j], tok_mx[tl], tok_sum[tl]);
-      store_agent(a.chunk_psum + row0 + j, acc);
+    float acc = 0.f;
+    if (a.want_psum) {
+      for (int tl = 0; tl < rows; ++tl) {
+        const float v = lg[int64_t(tl) * ld + j];
+        acc += SCORES ? v : score_of(e.score, v, tok_mx[tl], tok_sum[tl]);
+      }
     }
-    store_agent(a.chunk_counts + row0 + j, int32_t(hist[j]));
+    store_agent(a.chunks + row0 + j, pack_chunk(hist[j], acc));
   }
   __shared__ int s_flag;
   if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
   FinalizeArgs f{};
-  f.chunk_counts = a.chunk_counts;
-  f.chunk_psum = a.chunk_psum;
+  f.chunks = a.chunks;
   f.nch = int(gridDim.x);
   f.sup = a.sup;
   f.n = e.n;
@@ -307,7 +417,7 @@ __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
 template <int NT, bool MFMA, bool XLDS>
 __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   extern __shared__ float smem[];
-  __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];
+  __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];   // softmax statistics (k > 32 epilogue)
   const int ldl = a.npad;
   float* lg = smem;
   int* hist = reinterpret_cast<int*>(smem) + a.lds_region_ints;
@@ -369,9 +479,15 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     __syncthreads();
   }
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
-  route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
-  __syncthreads();
-  route_tail(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints);
+  if (a.k <= 32) {
+    route_rows_half<NT>(lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
+    __syncthreads();
+    route_tail<true>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints);
+  } else {
+    route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
+    __syncthreads();
+    route_tail<false>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints);
+  }
 }
 
 // ------------------------------------------------------------------ big-n route: logits GEMM
@@ -461,7 +577,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
   route_rows(lg, a.npad, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
   __syncthreads();
-  route_tail(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch, a.lds_region_ints);
+  route_tail<false>(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch, a.lds_region_ints);
 }
 
 // ------------------------------------------------------------------ launchers

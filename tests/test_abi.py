@@ -114,7 +114,7 @@ def test_null_pointers_rejected(lib):
 def test_workspace_too_small_or_misaligned(lib):
     sh = _sh(m=1024, d=768, n=128)
     need = lib.moe_workspace_size(ctypes.byref(sh), -1, 0)
-    assert need >= 327680
+    assert need >= 4096 + 3 * 128 * 768 * 2     # control words + router weight planes
     st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1024, None)
     assert st == L.MOE_ERR_WORKSPACE
     st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x1010),

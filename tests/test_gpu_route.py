@@ -89,6 +89,15 @@ def test_softmax_with_bias():
     check_route(inp.x, inp.w_r, 2, "softmax + bias (key = p + b)", bias=bias)
 
 
+@pytest.mark.parametrize("k,score,bias", [(32, "softmax", False), (40, "softmax", False), (33, "sigmoid", True)])
+def test_many_picks(k, score, bias):
+    # k = 32 is the largest pick count of the half-wave epilogue; larger k takes the wave-per-token one
+    spec = W.SwitchSpec("manyk", T=300, d=64, N=64, w_r_std=0.1)
+    inp = W.switch_inputs(spec, 12)
+    b = np.linspace(-0.01, 0.01, 64).astype(np.float32)[::-1].copy() if bias else None
+    check_route(inp.x, inp.w_r, k, f"top-{k} of 64 ({score})", score=score, gate="renorm", bias=b)
+
+
 def test_bf16_x_with_d_not_multiple_of_8():
     spec = W.SwitchSpec("oddd", T=200, d=36, N=16, w_r_std=0.1)
     inp = W.switch_inputs(spec, 6)
