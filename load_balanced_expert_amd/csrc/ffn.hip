@@ -103,14 +103,153 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(const uint16_t* __restrict
   }
 }
 
+// ------------------------------------------------------------------ streaming path
+// For K % 256 == 0 and N % 128 == 0.  One workgroup (4 waves) owns one expert
+// and 128 output columns; wave w owns 32 of them.  The expert's rows (up to
+// 128 per pass) are staged through LDS in K chunks of 128 (register
+// prefetch of the next chunk, one LDS buffer), and each wave streams its 32
+// weight rows from HBM with 12 16-byte loads in flight: for K step s (64
+// inputs) lane (c, h) reads 64 contiguous bytes of weight row c, inputs
+// 64 s + 32 h + [0, 32), and the A fragments use the same K order.  The
+// workgroup order puts all column blocks of an expert on one XCD, so the
+// expert's rows are fetched into that XCD's L2 once.
+constexpr int kFfnKA = 128;            // K per staged A chunk
+constexpr int kFfnLdA = kFfnKA + 8;    // LDS row stride (bf16), 16 bytes of padding
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int MT, bool RELU>
+__device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                uint16_t* __restrict__ C, uint16_t* As, int r0, int r_end, int K,
+                                                int N, int col0, int tid) {
+  const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
+  const int nks = K / 64, nch = K / kFfnKA;
+  // A chunk: 32 MT rows x 16 segments of 16 bytes, 2 MT per thread
+  constexpr int AL = 2 * MT;
+  const uint16_t* ap[AL];
+  int lo[AL];
+#pragma unroll
+  for (int u = 0; u < AL; ++u) {
+    const int item = tid + 256 * u, row = item >> 4, seg = item & 15;
+    ap[u] = A + size_t(min(r0 + row, r_end - 1)) * K + seg * 8;
+    lo[u] = row * kFfnLdA + seg * 8;
+  }
+  u32x4 areg[AL];
+  auto a_fetch = [&](int c) {
+    c = min(c, nch - 1);
+#pragma unroll
+    for (int u = 0; u < AL; ++u) areg[u] = *reinterpret_cast<const u32x4*>(ap[u] + c * kFfnKA);
+  };
+  auto a_store = [&]() {
+#pragma unroll
+    for (int u = 0; u < AL; ++u) *reinterpret_cast<u32x4*>(As + lo[u]) = areg[u];
+  };
+  const uint16_t* bp = B + size_t(col0 + r32) * K + 32 * h;
+  auto b_fetch = [&](bf16x8 (&b)[4], int s) {
+    s = min(s, nks - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = ld8(bp + 64 * s + 8 * q);
+  };
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+  const uint16_t* arow = As + r32 * kFfnLdA + 32 * h;
+  auto step = [&](const bf16x8 (&b)[4], int t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * mt * kFfnLdA + 64 * t + 8 * q);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[q], acc[mt], 0, 0, 0);
+      }
+    }
+  };
+  bf16x8 b0[4], b1[4], b2[4], b3[4];
+  a_fetch(0);
+  a_store();
+  a_fetch(1);
+  b_fetch(b0, 0);
+  b_fetch(b1, 1);
+  b_fetch(b2, 2);
+  lds_barrier();
+  for (int c = 0; c < nch; c += 2) {
+    const int s0 = 2 * c;
+    b_fetch(b3, s0 + 3);
+    step(b0, 0);
+    b_fetch(b0, s0 + 4);
+    step(b1, 1);
+    lds_barrier();
+    a_store();
+    a_fetch(c + 2);
+    lds_barrier();
+    b_fetch(b1, s0 + 5);
+    step(b2, 0);
+    b_fetch(b2, s0 + 6);
+    step(b3, 1);
+    lds_barrier();
+    a_store();
+    a_fetch(c + 3);
+    lds_barrier();
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = r0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (row < r_end) {
+        float v = acc[mt][i];
+        if (RELU) v = fmaxf(v, 0.f);
+        C[size_t(row) * N + col0 + r32] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+template <bool RELU>
+__global__ __launch_bounds__(256) void k_grouped_gemm_stream(const uint16_t* __restrict__ A,
+                                                             const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+                                                             const int32_t* __restrict__ offsets, int n, int K, int N,
+                                                             int row_limit) {
+  __shared__ __align__(16) uint16_t As[128 * kFfnLdA];
+  const int ncb = N / 128;
+  const unsigned G = unsigned(n) * ncb, b = blockIdx.x;
+  // XCD-major order: workgroup b runs on XCD b % 8; give each XCD a contiguous range of (expert, block)
+  const unsigned L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int e = int(L / ncb), cb = int(L % ncb);
+  const int r_begin = min(offsets[e], row_limit), r_end = min(offsets[e + 1], row_limit);
+  const int wave = threadIdx.x >> 6;
+  const int col0 = cb * 128 + wave * 32;
+  const uint16_t* Be = B + size_t(e) * N * K;
+  for (int r0 = r_begin; r0 < r_end; r0 += 128) {
+    switch (ceil_div(min(128, r_end - r0), 32)) {
+      case 1: ffn_stream_rows<1, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 2: ffn_stream_rows<2, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 3: ffn_stream_rows<3, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
+      default: ffn_stream_rows<4, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
+    }
+  }
+}
+
+static bool ffn_streams(int K, int N) { return K % 256 == 0 && N % 128 == 0; }
+
 hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets, const uint16_t* D,
                              const uint16_t* w1, const uint16_t* w2, uint16_t* hidden, uint16_t* y,
                              hipStream_t s) {
   const int row_limit = int(std::min<int64_t>(int64_t(n) * rows_max, 0x7FFFFFFF));
-  hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(ceil_div(d_ff, 128), n), dim3(256), 0, s, D, w1, hidden, offsets,
-                     d, d_ff, row_limit);
-  hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(ceil_div(d, 128), n), dim3(256), 0, s, hidden, w2, y, offsets,
-                     d_ff, d, row_limit);
+  if (ffn_streams(d, d_ff))
+    hipLaunchKernelGGL(k_grouped_gemm_stream<true>, dim3(unsigned(n) * (d_ff / 128)), dim3(256), 0, s, D, w1, hidden,
+                       offsets, n, d, d_ff, row_limit);
+  else
+    hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(ceil_div(d_ff, 128), n), dim3(256), 0, s, D, w1, hidden, offsets,
+                       d, d_ff, row_limit);
+  if (ffn_streams(d_ff, d))
+    hipLaunchKernelGGL(k_grouped_gemm_stream<false>, dim3(unsigned(n) * (d / 128)), dim3(256), 0, s, hidden, w2, y,
+                       offsets, n, d_ff, d, row_limit);
+  else
+    hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(ceil_div(d, 128), n), dim3(256), 0, s, hidden, w2, y, offsets,
+                       d_ff, d, row_limit);
   return hipGetLastError();
 }
 

@@ -110,7 +110,8 @@ def test_combine_without_residual():
 
 # ------------------------------------------------------------------ expert FFN
 @pytest.mark.parametrize("rows_per_expert,d,d_ff", [([80, 37, 0, 130, 64, 1, 33, 96], 768, 3072),
-                                                    ([5, 40, 17, 0], 1024, 4096), ([3, 200], 128, 96)])
+                                                    ([5, 40, 17, 0], 1024, 4096), ([3, 200], 128, 96),
+                                                    ([128, 129, 0, 256, 31], 256, 512)])
 def test_expert_ffn(rows_per_expert, d, d_ff):
     n = len(rows_per_expert)
     spec = W.SwitchSpec("ffn", T=1, d=d, N=n, d_ff=d_ff, w_std=np.sqrt(1.0 / d))
