@@ -104,52 +104,64 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ streaming path
-// For K % 256 == 0 and N % 128 == 0.  One workgroup (4 waves) owns one expert
-// and 128 output columns; wave w owns 32 of them.  The expert's rows (up to
+// For K % 256 == 0 and N % 128 == 0.  One workgroup (W = 4 or 8 waves) owns
+// one expert and 32 W output columns; wave w owns 32 of them.  The expert's rows (up to
 // 128 per pass) are staged through LDS in K chunks of 128 (register
-// prefetch of the next chunk, one LDS buffer), and each wave streams its 32
-// weight rows from HBM with 12 16-byte loads in flight: for K step s (64
-// inputs) lane (c, h) reads 64 contiguous bytes of weight row c, inputs
-// 64 s + 32 h + [0, 32), and the A fragments use the same K order.  The
-// workgroup order puts all column blocks of an expert on one XCD, so the
-// expert's rows are fetched into that XCD's L2 once.
+// prefetch of the next chunk, one LDS buffer) and shared by the W waves.
+// Each wave streams its 32 weight rows with coalesced 16-byte loads (eight
+// lanes per 128-byte line), kFfnRing - 1 K steps of 64 ahead, and turns each
+// step into MFMA fragments through its own LDS slab; the A fragments use the
+// same K order.  The workgroup order puts all column blocks of an expert on
+// one XCD, so the expert's rows are fetched into that XCD's L2 once.
 constexpr int kFfnKA = 128;            // K per staged A chunk
 constexpr int kFfnLdA = kFfnKA + 8;    // LDS row stride (bf16), 16 bytes of padding
+constexpr int kFfnLdB = 72;            // per-wave weight slab row stride (bf16): 64 + 16 bytes of padding
+constexpr int kFfnRing = 4;            // weight K steps in flight + 1 (even)
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int MT, bool RELU>
+template <int W, int MT, bool RELU>   // W waves per workgroup, 32 output columns each
 __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                uint16_t* __restrict__ C, uint16_t* As, int r0, int r_end, int K,
+                                                uint16_t* __restrict__ C, uint16_t* As, uint16_t* Bs, int r0, int r_end, int K,
                                                 int N, int col0, int tid) {
   const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
   const int nks = K / 64, nch = K / kFfnKA;
-  // A chunk: 32 MT rows x 16 segments of 16 bytes, 2 MT per thread
-  constexpr int AL = 2 * MT;
-  const uint16_t* ap[AL];
-  int lo[AL];
-#pragma unroll
-  for (int u = 0; u < AL; ++u) {
-    const int item = tid + 256 * u, row = item >> 4, seg = item & 15;
-    ap[u] = A + size_t(min(r0 + row, r_end - 1)) * K + seg * 8;
-    lo[u] = row * kFfnLdA + seg * 8;
-  }
+  // A chunk: 32 MT rows x 16 segments of 16 bytes over the workgroup
+  constexpr int AL = 8 * MT / W;
+  // thread's A items: rows row0 + 16 u (clamped to the last row), 16-byte segment seg
+  const int row0 = tid >> 4, seg = tid & 15;
+  static_assert(W == 4 || W == 8, "A item mapping");
+  constexpr int kRowStep = 64 * W / 16;
+  const int lo0 = row0 * kFfnLdA + seg * 8;
   u32x4 areg[AL];
   auto a_fetch = [&](int c) {
     c = min(c, nch - 1);
 #pragma unroll
-    for (int u = 0; u < AL; ++u) areg[u] = *reinterpret_cast<const u32x4*>(ap[u] + c * kFfnKA);
+    for (int u = 0; u < AL; ++u) {
+      const uint32_t off = uint32_t(min(r0 + row0 + kRowStep * u, r_end - 1)) * uint32_t(K) + c * kFfnKA + seg * 8;
+      areg[u] = *reinterpret_cast<const u32x4*>(A + off);
+    }
   };
   auto a_store = [&]() {
 #pragma unroll
-    for (int u = 0; u < AL; ++u) *reinterpret_cast<u32x4*>(As + lo[u]) = areg[u];
+    for (int u = 0; u < AL; ++u) *reinterpret_cast<u32x4*>(As + lo0 + u * kRowStep * kFfnLdA) = areg[u];
   };
-  const uint16_t* bp = B + size_t(col0 + r32) * K + 32 * h;
+  // weight K step s: load q brings rows 8q + lane / 8 of the wave's 32, 16 bytes each
+  // (eight lanes cover one 128-byte line), coalesced; the wave then transposes
+  // the step through its own LDS slab into MFMA fragments.
+  const uint16_t* bp = B + size_t(col0 + (lane >> 3)) * K + 8 * (lane & 7);
+  const size_t bq = size_t(8) * K;
   auto b_fetch = [&](bf16x8 (&b)[4], int s) {
     s = min(s, nks - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = ld8(bp + 64 * s + 8 * q);
+    for (int q = 0; q < 4; ++q) b[q] = ld8(bp + q * bq + 64 * s);
   };
+  uint16_t* bw = Bs + (tid >> 6) * (32 * kFfnLdB);
+  auto b_stage = [&](const bf16x8 (&b)[4]) {   // same-wave LDS accesses stay in order
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<bf16x8*>(bw + (8 * q + (lane >> 3)) * kFfnLdB + 8 * (lane & 7)) = b[q];
+  };
+  const uint16_t* brow = bw + r32 * kFfnLdB + 32 * h;
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -157,41 +169,39 @@ __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, 
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
   const uint16_t* arow = As + r32 * kFfnLdA + 32 * h;
   auto step = [&](const bf16x8 (&b)[4], int t) {
+    b_stage(b);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(brow + 8 * q);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * mt * kFfnLdA + 64 * t + 8 * q);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[q], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf, acc[mt], 0, 0, 0);
       }
     }
   };
-  bf16x8 b0[4], b1[4], b2[4], b3[4];
+  // weight ring: step s lives in slot s % kFfnRing and is fetched kFfnRing - 1 steps ahead
+  bf16x8 ring[kFfnRing][4];
   a_fetch(0);
   a_store();
   a_fetch(1);
-  b_fetch(b0, 0);
-  b_fetch(b1, 1);
-  b_fetch(b2, 2);
+#pragma unroll
+  for (int u = 0; u < kFfnRing - 1; ++u) b_fetch(ring[u], u);
   lds_barrier();
-  for (int c = 0; c < nch; c += 2) {
-    const int s0 = 2 * c;
-    b_fetch(b3, s0 + 3);
-    step(b0, 0);
-    b_fetch(b0, s0 + 4);
-    step(b1, 1);
-    lds_barrier();
-    a_store();
-    a_fetch(c + 2);
-    lds_barrier();
-    b_fetch(b1, s0 + 5);
-    step(b2, 0);
-    b_fetch(b2, s0 + 6);
-    step(b3, 1);
-    lds_barrier();
-    a_store();
-    a_fetch(c + 3);
-    lds_barrier();
+  for (int s0 = 0; s0 < nks; s0 += kFfnRing) {
+#pragma unroll
+    for (int u = 0; u < kFfnRing; ++u) {
+      if (s0 + u < nks) {
+        b_fetch(ring[(u + kFfnRing - 1) % kFfnRing], s0 + u + kFfnRing - 1);
+        step(ring[u], u & 1);
+        if (u & 1) {  // chunk (s0 + u) / 2 consumed: stage the next one, prefetch the one after
+          lds_barrier();
+          a_store();
+          a_fetch((s0 + u) / 2 + 2);
+          lds_barrier();
+        }
+      }
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -207,46 +217,61 @@ __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, 
   }
 }
 
-template <bool RELU>
-__global__ __launch_bounds__(256) void k_grouped_gemm_stream(const uint16_t* __restrict__ A,
+template <int W, bool RELU>
+__global__ __launch_bounds__(64 * W) void k_grouped_gemm_stream(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
                                                              const int32_t* __restrict__ offsets, int n, int K, int N,
                                                              int row_limit) {
   __shared__ __align__(16) uint16_t As[128 * kFfnLdA];
-  const int ncb = N / 128;
+  __shared__ __align__(16) uint16_t Bs[W * 32 * kFfnLdB];
+  const int ncb = N / (32 * W);
   const unsigned G = unsigned(n) * ncb, b = blockIdx.x;
   // XCD-major order: workgroup b runs on XCD b % 8; give each XCD a contiguous range of (expert, block)
   const unsigned L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
   const int e = int(L / ncb), cb = int(L % ncb);
   const int r_begin = min(offsets[e], row_limit), r_end = min(offsets[e + 1], row_limit);
   const int wave = threadIdx.x >> 6;
-  const int col0 = cb * 128 + wave * 32;
+  const int col0 = cb * (32 * W) + wave * 32;
   const uint16_t* Be = B + size_t(e) * N * K;
   for (int r0 = r_begin; r0 < r_end; r0 += 128) {
     switch (ceil_div(min(128, r_end - r0), 32)) {
-      case 1: ffn_stream_rows<1, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
-      case 2: ffn_stream_rows<2, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
-      case 3: ffn_stream_rows<3, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
-      default: ffn_stream_rows<4, RELU>(A, Be, C, As, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 1: ffn_stream_rows<W, 1, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 2: ffn_stream_rows<W, 2, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 3: ffn_stream_rows<W, 3, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      default: ffn_stream_rows<W, 4, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
     }
   }
 }
 
-static bool ffn_streams(int K, int N) { return K % 256 == 0 && N % 128 == 0; }
+// the streaming kernel addresses the activations with 32-bit element offsets
+static bool ffn_streams(int K, int N, int row_limit) {
+  return K % 256 == 0 && N % 128 == 0 && int64_t(row_limit) * K < (int64_t(1) << 32);
+}
+
+// 8-wave workgroups (256 columns: twice the reuse of each staged row chunk)
+// where N allows, else 4-wave workgroups (128 columns).
+template <bool RELU>
+static void launch_stream(int n, int K, int N, int row_limit, const int32_t* offsets, const uint16_t* A,
+                          const uint16_t* B, uint16_t* C, hipStream_t s) {
+  if (N % 256 == 0)
+    hipLaunchKernelGGL((k_grouped_gemm_stream<8, RELU>), dim3(unsigned(n) * (N / 256)), dim3(512), 0, s, A, B, C,
+                       offsets, n, K, N, row_limit);
+  else
+    hipLaunchKernelGGL((k_grouped_gemm_stream<4, RELU>), dim3(unsigned(n) * (N / 128)), dim3(256), 0, s, A, B, C,
+                       offsets, n, K, N, row_limit);
+}
 
 hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets, const uint16_t* D,
                              const uint16_t* w1, const uint16_t* w2, uint16_t* hidden, uint16_t* y,
                              hipStream_t s) {
   const int row_limit = int(std::min<int64_t>(int64_t(n) * rows_max, 0x7FFFFFFF));
-  if (ffn_streams(d, d_ff))
-    hipLaunchKernelGGL(k_grouped_gemm_stream<true>, dim3(unsigned(n) * (d_ff / 128)), dim3(256), 0, s, D, w1, hidden,
-                       offsets, n, d, d_ff, row_limit);
+  if (ffn_streams(d, d_ff, row_limit))
+    launch_stream<true>(n, d, d_ff, row_limit, offsets, D, w1, hidden, s);
   else
     hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(ceil_div(d_ff, 128), n), dim3(256), 0, s, D, w1, hidden, offsets,
                        d, d_ff, row_limit);
-  if (ffn_streams(d_ff, d))
-    hipLaunchKernelGGL(k_grouped_gemm_stream<false>, dim3(unsigned(n) * (d / 128)), dim3(256), 0, s, hidden, w2, y,
-                       offsets, n, d_ff, d, row_limit);
+  if (ffn_streams(d_ff, d, row_limit))
+    launch_stream<false>(n, d_ff, d, row_limit, offsets, hidden, w2, y, s);
   else
     hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(ceil_div(d, 128), n), dim3(256), 0, s, hidden, w2, y, offsets,
                        d_ff, d, row_limit);
