@@ -139,7 +139,7 @@ moe_status moe_router_prepare(int32_t d, int32_t n, const float* w_r, void* plan
  * counts   [n]      int32 out: c_j = number of (token, choice) pairs on expert j
  * prob_sum [n]      fp32 out or NULL: Σ_t score_j(t) (softmax p or sigmoid ρ),
  *                   the numerator of P_j ([Switch review] "로드 밸런싱 손실")
- * Limits: 1 <= k <= n <= 4096, d >= 1, m >= 1. */
+ * Limits: 1 <= k <= n <= 4096, 1 <= d <= 65536, m >= 1. */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
                      const float* bias, int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
                      void* ws, size_t ws_bytes, void* stream);

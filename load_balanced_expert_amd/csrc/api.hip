@@ -30,7 +30,7 @@ bool shape_valid(const moe_shape* s) {
 }
 
 bool shape_supported(const moe_shape* s) {
-  return s->n <= kMaxExperts && s->m <= 0x7FFFFFFFll && s->m * s->k <= 0x7FFFFFFFll;
+  return s->n <= kMaxExperts && s->d <= kMaxD && s->m <= 0x7FFFFFFFll && s->m * s->k <= 0x7FFFFFFFll;
 }
 
 moe_status check_shape(const moe_shape* s) {
@@ -387,8 +387,8 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   const bool fused_prefix = L.disp_ct == L.route_ct;
   if (fused_prefix) ex.disp = &da;
   mark(0);
-  const void* planes = nullptr;
-  if (L.rp.mfma && (reinterpret_cast<uintptr_t>(x) % 16) == 0) {
+  const void* planes = nullptr;   // else the route kernel splits W_r itself
+  if (L.rp.mfma && !route_direct(L.rp, sh.d, sh.n) && (reinterpret_cast<uintptr_t>(x) % 16) == 0) {
     if ((st = hip_status(launch_router_prepare(L.rp, sh.d, sh.n, w_r, at<uint16_t>(ws, L.planes), s))) != MOE_OK)
       return st;
     planes = at<void>(ws, L.planes);

@@ -19,6 +19,7 @@ constexpr int kMaxExperts = 4096;
 // last-workgroup pattern (zero before first use; each kernel that takes a
 // ticket leaves it zero again).
 constexpr int kMaxSuperChunks = 16;
+constexpr int kMaxD = 65536;   // keeps per-chunk copy item counts within 32 bits
 constexpr size_t kControlBytes = 4096;
 enum CtlTicket { kTicketRoute = 0, kTicketDispatch = 1, kTicketBalance = 2 };
 inline uint32_t* ctl_ticket(void* ws, int which) { return static_cast<uint32_t*>(ws) + which; }

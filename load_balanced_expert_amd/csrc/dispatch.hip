@@ -16,15 +16,16 @@
 //   2. one workgroup per chunk: wave 0 ranks the chunk's pairs in order with
 //      a match-any built from ballots over the expert-id bits and per-expert
 //      LDS counters; every pair adds its chunk base (a super-chunk prefix plus
-//      at most sup-1 chunk counts) and, if kept, its expert offset; then the
-//      whole workgroup copies the chunk's kept rows with 16-byte accesses.
+//      at most sup-1 chunk counts) and, if kept, its expert offset.  The other
+//      waves read the chunk's source rows meanwhile and write the kept ones
+//      with 16-byte accesses once the rows are known.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prefix.hpp"
 
 namespace moe {
 
-constexpr int kDispThreads = 256;
+constexpr int kDispThreads = 1024;
 constexpr int kDispPrefixBuf = 4096;   // LDS ints for the last block's super-chunk pass
 
 size_t dispatch_ws_bytes(int64_t m, int k, int n, int chunk_tokens) {
@@ -63,21 +64,41 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
   finalize_chunks(f, lds, n + kDispPrefixBuf, kDispThreads);
 }
 
+// Wave 0 ranks the chunk and computes its slots while the other 15 waves read
+// the chunk's source rows (only their destinations depend on the slots): up
+// to kDispPrefetch 16-byte items per thread of those waves, the rest after.
+constexpr int kDispPrefetch = 4;
+constexpr int kDispCopyThreads = kDispThreads - 64;
+
 template <typename V>
 __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a) {
   extern __shared__ int lds[];
   const int n = a.n;
   const int cp = a.chunk_tokens * a.k;          // pairs per chunk
   int* cnt = lds;                                // [n] running counts inside the chunk
-  int* lslot = cnt + n;                          // [cp] slot inside the chunk (-1: invalid id)
-  int* lrow = lslot + cp;                        // [cp] dispatched row (-1: dropped)
+  int* lrow = cnt + n;                           // [cp] dispatched row (-1: dropped)
   const int c = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t p0 = int64_t(c) * cp;
   const int np = int(min<int64_t>(cp, a.pairs - p0));
-  for (int j = threadIdx.x; j < n; j += kDispThreads) cnt[j] = 0;
-  __syncthreads();
+  // copy items i = q * vpr + v (pair q, vector v) are walked with (q, v) stepped
+  // incrementally: no integer division per item (np * vpr < 2^31 by the API limits)
+  const int vpr = int(a.row_bytes / int64_t(sizeof(V)));
+  const int qend = a.dispatched ? np : 0;
+  const V* __restrict__ x = static_cast<const V*>(a.x);
+  V* __restrict__ out = static_cast<V*>(a.dispatched);
+  auto src_row = [&](int q) -> int64_t {   // token of pair p0 + q
+    return a.k == 1 ? p0 + q : int64_t(uint32_t(p0 + q) / uint32_t(a.k));
+  };
+  const int ct = threadIdx.x - 64;   // copy thread index (waves 1-3)
+  const int q0 = ct / vpr, v0 = ct - q0 * vpr;
+  const int dq = kDispCopyThreads / vpr, dv = kDispCopyThreads - dq * vpr;
+  V pv[kDispPrefetch];
   if (wave == 0) {
+    for (int j = lane; j < n; j += 64) cnt[j] = 0;
+    __builtin_amdgcn_wave_barrier();
+    const int s = c / a.sup;
+    const int32_t* cw = reinterpret_cast<const int32_t*>(a.chunks);   // counts: low words of the chunk rows
     for (int g = 0; g < np; g += 64) {
       const bool inside = g + lane < np;
       const int e0 = inside ? a.idx[p0 + g + lane] : 0;
@@ -89,70 +110,94 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
       // every lane has read cnt[e] before the group's first lane advances it
       __builtin_amdgcn_wave_barrier();
       if (valid && (pr & lanemask_lt()) == 0) cnt[e] = before + __popcll(pr);
-      if (inside) lslot[g + lane] = valid ? before + __popcll(pr & lanemask_lt()) : -1;
-    }
-  }
-  __syncthreads();
-  const int s = c / a.sup;
-  for (int q = threadIdx.x; q < np; q += kDispThreads) {
-    const int64_t p = p0 + q;
-    const int ls = lslot[q];
-    int row = -1;
-    if (ls >= 0) {
-      const int e = a.idx[p];
-      int base = a.super_prefix[int64_t(s) * n + e];
-      // counts are the low words of the chunk rows; independent loads in batches of 16
-      const int32_t* cw = reinterpret_cast<const int32_t*>(a.chunks);
-      for (int cc = s * a.sup; cc < c; cc += 16) {
-        int v[16];
+      if (!inside) continue;
+      int row = -1;
+      if (valid) {
+        // chunk base of expert e: its super-chunk prefix plus the earlier chunks of the super chunk
+        int base = a.super_prefix[int64_t(s) * n + e];
+        const int off = a.expert_offsets[e];
+        for (int cc = s * a.sup; cc < c; cc += 16) {
+          int v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = cw[2 * (int64_t(min(cc + u, c - 1)) * n + e)];
+          for (int u = 0; u < 16; ++u) v[u] = cw[2 * (int64_t(min(cc + u, c - 1)) * n + e)];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (cc + u < c) base += v[u];
+          for (int u = 0; u < 16; ++u)
+            if (cc + u < c) base += v[u];
+        }
+        const int slot = base + before + __popcll(pr & lanemask_lt());
+        if (slot < a.capacity) row = off + slot;
       }
-      const int slot = base + ls;
-      if (slot < a.capacity) row = a.expert_offsets[e] + slot;
+      const int64_t p = p0 + g + lane;
+      lrow[g + lane] = row;
+      a.token_to_row[p] = row;
+      if (a.drop_mask) a.drop_mask[p] = row < 0 ? 1 : 0;
+      if (row >= 0 && a.row_to_token) a.row_to_token[row] = int32_t(src_row(g + lane));
     }
-    lrow[q] = row;
-    a.token_to_row[p] = row;
-    if (a.drop_mask) a.drop_mask[p] = row < 0 ? 1 : 0;
-    if (row >= 0 && a.row_to_token) a.row_to_token[row] = int32_t(p / a.k);
+  } else {
+    int q = q0, v = v0;
+#pragma unroll
+    for (int u = 0; u < kDispPrefetch; ++u) {
+      if (q < qend) pv[u] = x[src_row(q) * vpr + v];
+      q += dq;
+      v += dv;
+      if (v >= vpr) {
+        v -= vpr;
+        ++q;
+      }
+    }
   }
   if (!a.dispatched) return;
   __syncthreads();
-  // copy: (row, vector) items, four in flight per thread
-  const int64_t vpr = a.row_bytes / int64_t(sizeof(V));
-  const int64_t items = int64_t(np) * vpr;
-  const V* __restrict__ x = static_cast<const V*>(a.x);
-  V* __restrict__ out = static_cast<V*>(a.dispatched);
-  for (int64_t i0 = threadIdx.x; i0 < items; i0 += 4 * kDispThreads) {
-    V v[4];
+  if (wave != 0) {
+    int q = q0, v = v0;
+#pragma unroll
+    for (int u = 0; u < kDispPrefetch; ++u) {
+      if (q < qend) {
+        const int row = lrow[q];
+        if (row >= 0) out[int64_t(row) * vpr + v] = pv[u];
+      }
+      q += dq;
+      v += dv;
+      if (v >= vpr) {
+        v -= vpr;
+        ++q;
+      }
+    }
+  }
+  // items past the prefetched ones (long rows or many pairs): every thread, stride kDispThreads
+  const int first = kDispPrefetch * kDispCopyThreads + threadIdx.x;
+  int q = first / vpr, v = first - (first / vpr) * vpr;
+  const int sq = kDispThreads / vpr, sv = kDispThreads - sq * vpr;
+  while (q < qend) {
+    V val[4];
     int64_t dst[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + int64_t(u) * kDispThreads;
       dst[u] = -1;
-      if (i < items) {
-        const int q = int(i / vpr);
-        const int64_t c = i - int64_t(q) * vpr;
+      if (q < qend) {
         const int row = lrow[q];
         if (row >= 0) {
-          v[u] = x[((p0 + q) / a.k) * vpr + c];
-          dst[u] = int64_t(row) * vpr + c;
+          val[u] = x[src_row(q) * vpr + v];
+          dst[u] = int64_t(row) * vpr + v;
         }
+      }
+      q += sq;
+      v += sv;
+      if (v >= vpr) {
+        v -= vpr;
+        ++q;
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (dst[u] >= 0) out[dst[u]] = v[u];
+      if (dst[u] >= 0) out[dst[u]] = val[u];
   }
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s) {
   if (!prefix_ready)
     hipLaunchKernelGGL(k_disp_hist, dim3(a.nch), dim3(kDispThreads), (a.n + kDispPrefixBuf) * sizeof(int), s, a);
-  const size_t lds = (size_t(a.n) + 2 * size_t(a.chunk_tokens) * a.k) * sizeof(int);
+  const size_t lds = (size_t(a.n) + size_t(a.chunk_tokens) * a.k) * sizeof(int);
   const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.dispatched);
   if (a.row_bytes % 16 == 0 && al % 16 == 0)
     hipLaunchKernelGGL(k_disp_rank_copy<u32x4>, dim3(a.nch), dim3(kDispThreads), lds, s, a);

@@ -52,6 +52,8 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
 int route_chunk_tokens(const RoutePlan& plan);  // tokens per route workgroup (= dispatch chunk)
+// whether the route kernel reads W_r directly (no prepared planes needed)
+bool route_direct(const RoutePlan& plan, int d, int n);
 hipError_t launch_router_prepare(const RoutePlan& plan, int d, int n, const float* w_r, uint16_t* planes,
                                  hipStream_t s);
 

@@ -113,26 +113,40 @@ __device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds,
   double auxp = 0.0;
   for (int j0 = 0; j0 < n; j0 += cb) {
     const int w = min(cb, n - j0);
-    for (int q = threadIdx.x; q < nsup * w; q += threads) {
-      const int s = q / w, jj = q - s * w;
-      const int c1 = min(a.nch, (s + 1) * a.sup);
-      int cs = 0;
-      float ps = 0.f;
-      // 16 independent loads in flight per batch (these bypass the L2), then a fixed-order sum
-      for (int c = s * a.sup; c < c1; c += 16) {
-        uint64_t v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = load_agent(a.chunks + int64_t(min(c + u, c1 - 1)) * n + j0 + jj);
+    // two (super chunk, expert) pairs per thread per pass, 32 independent loads
+    // in flight (these bypass the L2), then fixed-order sums
+    for (int q0 = threadIdx.x; q0 < nsup * w; q0 += 2 * threads) {
+      const int q1 = min(q0 + threads, nsup * w - 1);
+      const bool two = q0 + threads < nsup * w;
+      const int s0 = q0 / w, j0q = q0 - s0 * w, s1 = q1 / w, j1q = q1 - s1 * w;
+      const int b0 = s0 * a.sup, e0 = min(a.nch, b0 + a.sup), b1 = s1 * a.sup, e1 = min(a.nch, b1 + a.sup);
+      int cs0 = 0, cs1 = 0;
+      float ps0 = 0.f, ps1 = 0.f;
+      for (int o = 0; o < a.sup; o += 16) {
+        uint64_t v0[16], v1[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          if (c + u < c1) {
-            cs += chunk_count(v[u]);
-            ps += chunk_psum(v[u]);
+          v0[u] = load_agent(a.chunks + int64_t(min(b0 + o + u, e0 - 1)) * n + j0 + j0q);
+          v1[u] = load_agent(a.chunks + int64_t(min(b1 + o + u, e1 - 1)) * n + j0 + j1q);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (b0 + o + u < e0) {
+            cs0 += chunk_count(v0[u]);
+            ps0 += chunk_psum(v0[u]);
+          }
+          if (b1 + o + u < e1) {
+            cs1 += chunk_count(v1[u]);
+            ps1 += chunk_psum(v1[u]);
           }
         }
       }
-      sc[s * w + jj] = cs;
-      sp[s * w + jj] = ps;
+      sc[s0 * w + j0q] = cs0;
+      sp[s0 * w + j0q] = ps0;
+      if (two) {
+        sc[s1 * w + j1q] = cs1;
+        sp[s1 * w + j1q] = ps1;
+      }
     }
     __syncthreads();
     for (int jj = threadIdx.x; jj < w; jj += threads) {

@@ -185,6 +185,106 @@ __device__ __forceinline__ f32x16 gemm_ksplit_bf16x3(const uint16_t* __restrict_
   return acc;
 }
 
+// Exact three-way split of 8 fp32 weights into bf16 fragments: hi = w with
+// the low 16 bits cleared, mid = (w - hi) likewise, lo = w - hi - mid (at
+// most 8 significant bits, so exact in bf16); hi + mid + lo == w.
+__device__ __forceinline__ void split3(const float* v, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  u32x4 wh, wm, wl;
+  constexpr uint32_t kHigh = 0x07060302u;   // v_perm selector: high halves of (src1, src0) -> (lo, hi)
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t u0 = __float_as_uint(v[2 * p]), u1 = __float_as_uint(v[2 * p + 1]);
+    const float r0 = v[2 * p] - __uint_as_float(u0 & 0xFFFF0000u);
+    const float r1 = v[2 * p + 1] - __uint_as_float(u1 & 0xFFFF0000u);
+    const uint32_t s0 = __float_as_uint(r0), s1 = __float_as_uint(r1);
+    const float q0 = r0 - __uint_as_float(s0 & 0xFFFF0000u);
+    const float q1 = r1 - __uint_as_float(s1 & 0xFFFF0000u);
+    wh[p] = __builtin_amdgcn_perm(u1, u0, kHigh);
+    wm[p] = __builtin_amdgcn_perm(s1, s0, kHigh);
+    wl[p] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), kHigh);
+  }
+  hi = __builtin_bit_cast(bf16x8, wh);
+  mid = __builtin_bit_cast(bf16x8, wm);
+  lo = __builtin_bit_cast(bf16x8, wl);
+}
+
+// The same block product taking W_r [d, n] fp32 straight from global memory:
+// lane (r, h) loads the 16 weights of expert 32 tile + r it needs per K block
+// (each load instruction reads two 128-byte rows of W_r) and splits them in
+// registers, so no prepared planes are needed.  Three weight buffers rotate,
+// two K blocks ahead of the multiply; the first two are requested before the
+// x tile is staged (init), so both latencies overlap.  Used when d % 32 == 0
+// and n == 32 NT: the row stride is then a compile-time constant and every
+// address is in range.
+template <int NT>
+struct DirectGemm {
+  static constexpr int kStride = 32 * NT;   // n
+  const float* wcol;
+  int kb0, cnt, rot, h;
+  float r0[16], r1[16], r2[16];
+
+  __device__ __forceinline__ void init(const float* w, int dpad, int wave, int lane, int rot_) {
+    constexpr int KS = 16 / NT;
+    const int tile = wave % NT, ks = wave / NT;
+    const int nkb = dpad / 32;
+    kb0 = ks * nkb / KS;
+    cnt = (ks + 1) * nkb / KS - kb0;
+    rot = cnt > 0 ? rot_ % cnt : 0;
+    h = lane >> 5;
+    wcol = w + tile * 32 + (lane & 31);
+    if (cnt > 0) {
+      load(r0, 0);
+      load(r1, 1);
+    }
+  }
+  __device__ __forceinline__ int kb(int i) const {
+    i = min(i, cnt - 1);
+    const int r = i + rot;
+    return kb0 + (r >= cnt ? r - cnt : r);
+  }
+  __device__ __forceinline__ void load(float (&bb)[16], int i) {
+    const float* p = wcol + (kb(i) * 32 + 16 * h) * kStride;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) bb[q] = p[q * kStride];
+  }
+  __device__ __forceinline__ void step(f32x16& acc, const uint16_t* arow, const float (&bb)[16], int i) {
+    const int k = kb(i) * 32;
+    const bf16x8 a0 = load8(arow + k), a1 = load8(arow + k + 8);
+    bf16x8 f[3][2];
+    split3(bb, f[0][0], f[1][0], f[2][0]);
+    split3(bb + 8, f[0][1], f[1][1], f[2][1]);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, f[p][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, f[p][1], acc, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ f32x16 run(const uint16_t* arow) {
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int i = 0; i < cnt; i += 3) {
+      load(r2, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      step(acc, arow, r0, i);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < cnt) {
+        load(r0, i + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        step(acc, arow, r1, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i + 2 < cnt) {
+        load(r1, i + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        step(acc, arow, r2, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return acc;
+  }
+};
+
 // 32x32 accumulator layout: lane l, element i -> row 8*(i/4) + 4*(l/32) + (i%4), col l%32.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
@@ -414,7 +514,7 @@ __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
 // then, after the product, the KS-1 partial tiles [32][npad]; the first of
 // them becomes the logits tile and, in the last workgroup, the finishing
 // scratch.  The histogram follows the region.
-template <int NT, bool MFMA, bool XLDS>
+template <int NT, bool MFMA, bool XLDS, bool DIRECT>
 __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   extern __shared__ float smem[];
   __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];   // softmax statistics (k > 32 epilogue)
@@ -430,22 +530,34 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     constexpr int KS = 16 / NT;
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     const uint16_t* arow;
+    DirectGemm<NT> dg;
+    if constexpr (DIRECT) dg.init(a.w_r, a.dpad, wave, lane, int(blockIdx.x));
     if constexpr (XLDS) {
       // stage the 32 x rows in LDS with coalesced 16-byte loads (zero padding past the end)
       uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
       const int ldx = a.dpad + 8, cpr = a.dpad / 8;
-      for (int c = tid; c < kRouteBM * cpr; c += kRouteThreads) {
-        const int r = c / cpr, k = (c - r * cpr) * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < rows && k < a.d) v = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
-        *reinterpret_cast<u32x4*>(xs + r * ldx + k) = v;
+      // four loads in flight per thread before the LDS stores (one pass for d <= 1024)
+      for (int c0 = tid; c0 < kRouteBM * cpr; c0 += 4 * kRouteThreads) {
+        u32x4 v[4];
+        int dst[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * kRouteThreads;
+          const int r = c / cpr, k = (c - r * cpr) * 8;
+          v[u] = u32x4{0u, 0u, 0u, 0u};
+          dst[u] = c < kRouteBM * cpr ? r * ldx + k : -1;
+          if (c < kRouteBM * cpr && r < rows && k < a.d) v[u] = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xs + dst[u]) = v[u];
       }
       __syncthreads();
       arow = xs + (lane & 31) * ldx + 16 * (lane >> 5);
     } else {
       arow = x + (t0 + min(lane & 31, rows - 1)) * a.d + 16 * (lane >> 5);  // requires d == dpad
     }
-    const f32x16 acc = gemm_ksplit_bf16x3<NT>(arow, a.planes, a.dpad, wave, lane, int(blockIdx.x));
+    const f32x16 acc = DIRECT ? dg.run(arow) : gemm_ksplit_bf16x3<NT>(arow, a.planes, a.dpad, wave, lane, int(blockIdx.x));
     const int col = (wave % NT) * 32 + (lane & 31), ks = wave / NT;
     if constexpr (XLDS) __syncthreads();   // the x tile is dead before partials overwrite it
     if (ks > 0) {
@@ -591,24 +703,41 @@ hipError_t launch_router_prepare(const RoutePlan& plan, int d, int n, const floa
 
 int route_chunk_tokens(const RoutePlan& plan) { return plan.fused ? kRouteBM : kRowsBM; }
 
+bool route_direct(const RoutePlan& plan, int d, int n) {
+  return plan.fused && plan.mfma && d % 32 == 0 && (n == 32 || n == 64 || n == 128 || n == 256);
+}
+
+// Without prepared planes the fused kernel splits W_r in registers when d is a
+// multiple of 32 and n one of 32, 64, 128, 256 (else the planes are prepared).
 template <int NT>
 static void launch_fused(const RoutePlan& plan, const RouteArgs& a, dim3 g, size_t lds, hipStream_t s) {
-  if (stage_x(plan, a.n))
-    hipLaunchKernelGGL((k_route_fused<NT, true, true>), g, dim3(kRouteThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL((k_route_fused<NT, true, false>), g, dim3(kRouteThreads), lds, s, a);
+  const bool x_lds = stage_x(plan, a.n);
+  if (a.planes_ready || !route_direct(plan, a.d, a.n)) {
+    if (x_lds)
+      hipLaunchKernelGGL((k_route_fused<NT, true, true, false>), g, dim3(kRouteThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((k_route_fused<NT, true, false, false>), g, dim3(kRouteThreads), lds, s, a);
+  } else {
+    if (x_lds)
+      hipLaunchKernelGGL((k_route_fused<NT, true, true, true>), g, dim3(kRouteThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((k_route_fused<NT, true, false, true>), g, dim3(kRouteThreads), lds, s, a);
+  }
 }
 
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_t s) {
   RouteArgs a = a_in;
   a.lds_region_ints = route_region_ints(plan, a.n);
-  if (plan.mfma && !a.planes_ready) launch_router_prepare(plan, a.d, a.n, a.w_r, const_cast<uint16_t*>(a.planes), s);
+  if (plan.mfma && !a.planes_ready && !route_direct(plan, a.d, a.n)) {
+    const hipError_t err = launch_router_prepare(plan, a.d, a.n, a.w_r, const_cast<uint16_t*>(a.planes), s);
+    if (err != hipSuccess) return err;
+  }
   if (plan.fused) {
     const dim3 g(unsigned(ceil_div64(a.m, kRouteBM)));
     const size_t lds = (size_t(a.lds_region_ints) + plan.npad) * sizeof(float);
     const int nt = plan.npad / 32;
     if (!plan.mfma)
-      hipLaunchKernelGGL((k_route_fused<1, false, false>), g, dim3(kRouteThreads), lds, s, a);
+      hipLaunchKernelGGL((k_route_fused<1, false, false, false>), g, dim3(kRouteThreads), lds, s, a);
     else if (nt == 1)
       launch_fused<1>(plan, a, g, lds, s);
     else if (nt == 2)

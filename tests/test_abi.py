@@ -94,6 +94,9 @@ def test_unsupported_sizes(lib):
     assert st == L.MOE_ERR_UNSUPPORTED
     sh = _sh(m=2 ** 31, k=1)
     assert lib.moe_workspace_size(ctypes.byref(sh), -1, 0) == 0
+    sh = _sh(d=65537)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == L.MOE_ERR_UNSUPPORTED
 
 
 def test_null_pointers_rejected(lib):

@@ -131,17 +131,17 @@ def test_global_aux():
 
 
 # ------------------------------------------------------------------ whole layer
-def _layer_check(spec, seed, cf, ffn):
+def _layer_check(spec, seed, cf, ffn, k=1):
     inp = W.switch_inputs(spec, seed)
     cap = OD.capacity(spec.T, spec.N, cf)
     w1 = w2 = None
     if ffn:
         w1, w2 = W.all_expert_weights(spec, seed)
-    say(f"[layer] {spec.name} T={spec.T} cf={cf} cap={cap} ffn={ffn}")
-    o = M.switch_layer(to_dev(inp.x), to_dev(inp.w_r), k=1, capacity=cap, alpha=spec.alpha,
+    say(f"[layer] {spec.name} T={spec.T} k={k} cf={cf} cap={cap} ffn={ffn}")
+    o = M.switch_layer(to_dev(inp.x), to_dev(inp.w_r), k=k, capacity=cap, alpha=spec.alpha,
                        w1=None if w1 is None else to_dev(w1), w2=None if w2 is None else to_dev(w2))
     torch.cuda.synchronize()
-    ref = OR.route(inp.x, inp.w_r, 1)
+    ref = OR.route(inp.x, inp.w_r, k)
     idx = to_host(o.idx)
     flips = check_selection(idx, ref, f"{spec.name} layer")
     f, P, aux = OS.switch_stats(ref.counts, ref.prob_sum, spec.T, spec.alpha)
@@ -172,8 +172,9 @@ def _layer_check(spec, seed, cf, ffn):
     err = row_rel_err(got, out_ref)
     say(f"[layer] worst row error {err.max():.3e} (tol {tol:.1e})")
     assert err.max() <= tol
-    dropped = dm.drop_mask[:, 0] == 1
+    dropped = np.all(dm.drop_mask == 1, axis=1)
     assert np.array_equal(to_host(o.out)[dropped], inp.x[dropped])
+    return o
 
 
 def test_tiny_switch_layer():
@@ -187,6 +188,39 @@ def test_switch_base_layer_with_ffn(cf):
 
 def test_switch_base_layer_identity_ragged():
     _layer_check(W.SWITCH_BASE.scaled(T=1234, d_ff=None), 1, 1.25, ffn=False)
+
+
+def test_layer_large_batch():
+    _layer_check(W.SWITCH_BASE.scaled(T=12000, d_ff=None), 2, 1.0, ffn=False)
+
+
+@pytest.mark.parametrize("T,cf", [(2048, 1.0), (333, 1.5)])
+def test_top2_layer(T, cf):
+    spec = W.SwitchSpec("top2", T=T, d=256, N=64, w_r_std=0.05)
+    _layer_check(spec, 3, cf, ffn=False, k=2)
+
+
+def test_layer_maps_equal_separate_calls():
+    # the layer (route kernel that also finishes the capacity prefix) against route + dispatch as separate calls
+    spec = W.SWITCH_BASE.scaled(T=4000, d_ff=None)
+    inp = W.switch_inputs(spec, 4)
+    cap = OD.capacity(spec.T, spec.N, 1.0)
+    x, w = to_dev(inp.x), to_dev(inp.w_r)
+    o = M.switch_layer(x, w, k=1, capacity=cap)
+    r = M.route(x, w, 1)
+    dsp = M.dispatch(x, r.idx, spec.N, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(o.idx, r.idx)
+    assert torch.equal(o.token_to_row, dsp.token_to_row)
+    assert torch.equal(o.drop_mask, dsp.drop_mask)
+    assert torch.equal(o.expert_offsets, dsp.expert_offsets)
+    rows = int(dsp.expert_offsets[-1].item())
+    assert torch.equal(o.row_to_token[:rows], dsp.row_to_token[:rows])
+    assert torch.equal(o.dispatched[:rows], dsp.dispatched[:rows])
+    # a second layer call on the same workspace: the control words were left zero
+    o2 = M.switch_layer(x, w, k=1, capacity=cap)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.token_to_row, o.token_to_row) and torch.equal(o2.dispatched[:rows], o.dispatched[:rows])
 
 
 def test_lossfree_micro_batch_loop():
