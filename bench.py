@@ -10,11 +10,14 @@ slots + permute-dispatch, grouped expert FFN, gate-scaled inverse-permute
 combine with the residual.  All inputs are resident in HBM before the timed
 region.
 
-value = T / (time of prepare + route + dispatch + combine) per step, the
-"routed tokens/s (route + dispatch + combine)" metric; the expert FFN runs
-inside every step but is excluded from that time and reported separately.
-Stage times come from HIP events that the library records on its stream at
-the stage boundaries (moe_layer_params.stage_events).
+value = T / (time of route + dispatch + combine) per step, the "routed
+tokens/s (route + dispatch + combine)" metric; the expert FFN runs inside
+every step but is excluded from that time and reported separately.  Times
+come from HIP events (created without the system-scope fence, so recording
+them does not write back the caches) that the library records on its stream
+after the dispatch and after the FFN of every step: the metric region of a
+step is the span from its FFN end to the next step's dispatch end.  A short
+extra run with all six stage events gives the per-stage breakdown.
 
 Also printed (same JSON line):
   roofline      the dominant kernel of the metric region against its MI355X
@@ -119,6 +122,46 @@ def cpu_baseline(spec, inp, cap, seconds: float):
                       f"host affinity cores={len(os.sched_getaffinity(0))}"}
 
 
+class HipEvents:
+    """Timing events from the HIP runtime torch already loaded, created with
+    hipEventDisableSystemFence: recording them skips the system-scope cache
+    writeback and invalidation that a default event performs, which would
+    otherwise add several microseconds to every measured span."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so[.\d]*)", open("/proc/self/maps").read())))
+        if not paths:
+            raise RuntimeError("HIP runtime not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(paths[0])
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.ct.c_uint(self.DISABLE_SYSTEM_FENCE)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return _Ev(e.value)
+
+    def record(self, e, stream):
+        self.hip.hipEventRecord(self.ct.c_void_p(e.cuda_event), self.ct.c_void_p(stream))
+
+    def ms(self, a, b):
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), self.ct.c_void_p(a.cuda_event),
+                                        self.ct.c_void_p(b.cuda_event)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+
+class _Ev:
+    """A raw hipEvent_t in the shape the binding's stage_events expects."""
+    def __init__(self, handle):
+        self.cuda_event = handle
+
+
 def copy_calibration():
     import torch
     n = 256 << 20
@@ -176,28 +219,65 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for evs in events:          # creates the HIP events; the library re-records them inside each step
-        for e in evs:
-            e.record()
+    he = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # Timed run: per step only two events, after dispatch ([3]) and after the
+    # expert FFN ([4]).  The metric region of step i is then the span from its
+    # FFN end to the dispatch end of step i + 1 (combine of step i, then route
+    # and dispatch of the next step, the same work on the same inputs), so one
+    # event sits inside each measured region; the FFN is e3(i) -> e4(i).
+    n_run = args.steps + 1
+    ev3 = [he.create() for _ in range(n_run)]
+    ev4 = [he.create() for _ in range(n_run)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for i in range(n_run):
+        step([None, None, None, ev3[i], ev4[i], None])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    st = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(5)]
-                   for i in range(args.steps)])  # ms
-    names = ["router_prepare", "route", "dispatch", "expert_ffn", "combine"]
-    stage_ms = {n: float(np.mean(st[:, j])) for j, n in enumerate(names)}
-    metric_ms = stage_ms["router_prepare"] + stage_ms["route"] + stage_ms["dispatch"] + stage_ms["combine"]
+    region = np.array([he.ms(ev4[i], ev3[i + 1]) for i in range(args.steps)])   # ms
+    ffn = np.array([he.ms(ev3[i], ev4[i]) for i in range(args.steps)])
+    metric_ms = float(np.mean(region))
     value = T / (metric_ms * 1e-3)
     rows = int(lo.expert_offsets[N].item())
 
-    # dominant single-kernel stage of the metric region
+    # Stage breakdown: a separate short run with all six stage events (each
+    # span also carries one event's own cost, so these add up to more than
+    # the metric region above).
+    nb = min(args.steps, 20)
+    evs = [[he.create() for _ in range(6)] for _ in range(nb)]
+    for i in range(nb):
+        step(evs[i])
+    torch.cuda.synchronize()
+    st = np.array([[he.ms(evs[i][j], evs[i][j + 1]) for j in range(5)] for i in range(nb)])
+    names = ["router_prepare", "route", "dispatch", "expert_ffn", "combine"]
+    stage_ms = {n_: float(np.mean(st[:, j])) for j, n_ in enumerate(names)}
+
+    def per_launch_ms(fn, reps=30):
+        """Average of `reps` back-to-back launches between two events."""
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a_, b_ = he.create(), he.create()
+        he.record(a_, stream)
+        for _ in range(reps):
+            fn()
+        he.record(b_, stream)
+        torch.cuda.synchronize()
+        return he.ms(a_, b_) / reps
+
+    # dominant kernel of the metric region (by its event span), timed on its own:
+    # route and combine are the same kernels as inside the layer, launched back to back
     dom = max(("route", "dispatch", "combine"), key=lambda s_: stage_ms[s_])
-    t_s = stage_ms[dom] * 1e-3
+    if dom == "route":
+        r_out = M.route(x, w_r, k)
+        t_s = per_launch_ms(lambda: M.route(x, w_r, k, out=r_out)) * 1e-3
+    elif dom == "combine":
+        c_out = torch.empty_like(x)
+        t_s = per_launch_ms(lambda: M.combine(lo.y, lo.gate, lo.token_to_row, x, out=c_out)) * 1e-3
+    else:
+        t_s = stage_ms[dom] * 1e-3
     if dom == "route":
         flops = 3 * 2.0 * T * d * N                    # bf16x3 products on bf16 matrix cores
         alg_bytes = T * d * 2 + 3 * N * d * 2 + T * k * 8 + N * 8
@@ -226,7 +306,7 @@ def main():
 
     # the expert FFN stage (outside the metric): weight streaming from HBM bounds it
     d_ff = spec.d_ff
-    t_ffn = stage_ms["expert_ffn"] * 1e-3
+    t_ffn = float(np.mean(ffn)) * 1e-3
     ffn_bytes = 2 * N * d * d_ff * 2 + 2 * rows * (d + d_ff) * 2
     ffn_flops = 2 * 2.0 * rows * d * d_ff
     t1 = committed_traffic("ffn1", "switch_base", kernel_source_hash(KERNEL_SOURCES["ffn"]))
@@ -249,7 +329,9 @@ def main():
         "config": {"workload": "switch_base: T=8192 (16x512), d_model=768, N=128 experts, top-1 softmax, "
                                f"capacity factor {args.cf} (capacity {cap}), ReLU expert FFN d_ff=3072",
                    "global_batch": T, "capacity": cap, "parallelism": "single GPU"},
-        "metric_ms_per_step": metric_ms, "stage_ms": stage_ms,
+        "metric_ms_per_step": metric_ms, "metric_ms_p10_p90": [float(np.percentile(region, 10)),
+                                                               float(np.percentile(region, 90))],
+        "expert_ffn_ms": t_ffn * 1e3, "stage_ms_event_spans": stage_ms,
         "hbm_roofline_frac_of_metric_region": alg_metric_bytes / (metric_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes_metric_region": alg_metric_bytes,
         "dropped_tokens": int(lo.drop_mask.sum().item()), "aux_loss": float(lo.aux.item()),
