@@ -101,6 +101,7 @@ struct RouteExtras {
   float* aux = nullptr;
   float alpha = 0.f;
   const DispatchArgs* disp = nullptr;   // capacity prefix sums for this dispatch
+  bool defer_finish = false;            // chunk rows only; the dispatch derives everything else
 };
 
 moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const float* w_r, const void* w_planes,
@@ -140,6 +141,7 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
     a.super_prefix = ex.disp->super_prefix;
   }
   a.done = ctl_ticket(ws, kTicketRoute);
+  a.finish = !ex.defer_finish;
   RoutePlan rp = L.rp;
   if (rp.mfma && (reinterpret_cast<uintptr_t>(x) % 16) != 0) rp.mfma = false;
   return hip_status(launch_route(rp, a, st));
@@ -378,14 +380,27 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   };
   // route (+ load statistics + per-chunk counts and capacity prefix sums in its last workgroup), then
   // slots + permute-dispatch in one kernel
-  const DispatchArgs da = dispatch_args(sh, L, p->capacity, x, idx, t2r, drop, offs, o->row_to_token, disp, ws);
+  DispatchArgs da = dispatch_args(sh, L, p->capacity, x, idx, t2r, drop, offs, o->row_to_token, disp, ws);
   RouteExtras ex;
   ex.f = f;
   ex.P = P;
   ex.aux = aux;
   ex.alpha = p->alpha;
   const bool fused_prefix = L.disp_ct == L.route_ct;
-  if (fused_prefix) ex.disp = &da;
+  if (fused_prefix && L.rp.fused && dispatch_self_prefix_ok(L.nch, sh.n)) {
+    // the route kernel stops after its chunk rows; the dispatch workgroups derive
+    // the totals, slot bases and offsets, and publish the load statistics
+    ex.defer_finish = true;
+    da.self_prefix = true;
+    da.counts = counts;
+    da.prob_sum = psum;
+    da.f = f;
+    da.P = P;
+    da.aux = aux;
+    da.alpha = p->alpha;
+  } else if (fused_prefix) {
+    ex.disp = &da;
+  }
   mark(0);
   const void* planes = nullptr;   // else the route kernel splits W_r itself
   if (L.rp.mfma && !route_direct(L.rp, sh.d, sh.n) && (reinterpret_cast<uintptr_t>(x) % 16) == 0) {

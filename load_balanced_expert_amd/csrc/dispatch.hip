@@ -70,13 +70,123 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
 constexpr int kDispPrefetch = 4;
 constexpr int kDispCopyThreads = kDispThreads - 64;
 
-template <typename V>
+// Self prefix (n <= 256, n % 4 == 0): the route kernel left split chunk rows
+// (counts [nch][n] int32, then score sums [nch][n] fp32).  Every workgroup
+// reads all count rows with 16-byte loads (a thread owns 4 experts and a
+// contiguous range of chunks) and keeps per expert the total and the count
+// of the chunks before its own (its slot base); workgroup 0 also sums the
+// score rows.  Sums run in a fixed order.  Wave 0 scans the kept counts into
+// the expert offsets; workgroup 0 publishes counts, f, P, aux and the
+// offsets.  part: 3 arrays of G n = 4 kDispThreads ints.
+__device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int* part, int* lbase, int* loff) {
+  const int n = a.n, t = threadIdx.x, nq = n / 4;
+  const int G = kDispThreads / nq;
+  const bool stats = c == 0;
+  int* pc = part;                                                  // [G][n] counts
+  int* pb = part + 4 * kDispThreads;                               // [G][n] counts before chunk c
+  float* pp = reinterpret_cast<float*>(part + 8 * kDispThreads);   // [G][n] score sums (workgroup 0)
+  const int32_t* ccnt = reinterpret_cast<const int32_t*>(a.chunks);
+  const float* cps = reinterpret_cast<const float*>(ccnt + int64_t(a.nch) * n);
+  if (t < G * nq) {
+    const int e4 = (t % nq) * 4, g = t / nq;
+    const int lo = g * a.nch / G, hi = (g + 1) * a.nch / G;
+    int cs[4] = {0, 0, 0, 0}, cb[4] = {0, 0, 0, 0};
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int cc = lo; cc < hi; cc += 8) {
+      u32x4 v[8];
+      f32x4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t o = int64_t(min(cc + u, hi - 1)) * n + e4;
+        v[u] = *reinterpret_cast<const u32x4*>(ccnt + o);
+        if (stats) w[u] = *reinterpret_cast<const f32x4*>(cps + o);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (cc + u < hi) {
+          const bool before = cc + u < c;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            cs[q] += int(v[u][q]);
+            cb[q] += before ? int(v[u][q]) : 0;
+            if (stats) ps[q] += w[u][q];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pc[g * n + e4 + q] = cs[q];
+      pb[g * n + e4 + q] = cb[q];
+      pp[g * n + e4 + q] = ps[q];
+    }
+  }
+  __syncthreads();
+  int* ltot = loff + n + 1;   // kept counts, then scanned by wave 0
+  double auxp = 0.0;
+  if (t < n) {
+    int tot = 0, base = 0;
+    float ps = 0.f;
+    for (int g = 0; g < G; ++g) {
+      tot += pc[g * n + t];
+      base += pb[g * n + t];
+      ps += pp[g * n + t];
+    }
+    lbase[t] = base;
+    ltot[t] = min(tot, a.capacity);
+    if (stats) {
+      const int64_t m = a.pairs / a.k;
+      if (a.counts) a.counts[t] = tot;
+      if (a.prob_sum) a.prob_sum[t] = ps;
+      if (a.f) a.f[t] = float(tot) / float(m);
+      if (a.P) a.P[t] = ps / float(m);
+      auxp = (double(tot) / double(m)) * (double(ps) / double(m));
+    }
+  }
+  if (stats && a.aux) {   // fixed-order fp64 sum over the experts
+    __shared__ double red[kDispThreads / 64];
+    const double v = wave_sum_f64(auxp);
+    if ((t & 63) == 0) red[t >> 6] = v;
+    __syncthreads();
+    if (t == 0) {
+      double s = 0.0;
+      for (int w = 0; w < (n + 63) / 64; ++w) s += red[w];
+      a.aux[0] = float(double(a.alpha) * double(n) * s);
+    }
+  }
+  __syncthreads();
+  if (t < 64) {   // exclusive scan of the kept counts: lane l owns a contiguous run
+    const int per = (n + 63) / 64, j0 = t * per, j1 = min(j0 + per, n);
+    int sum = 0;
+    for (int j = j0; j < j1; ++j) sum += ltot[j];
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (t >= off) incl += o;
+    }
+    int run = incl - sum;
+    for (int j = j0; j < j1; ++j) {
+      loff[j] = run;
+      run += ltot[j];
+    }
+    if (t == 63) loff[n] = incl;
+  }
+  __syncthreads();
+  if (stats)
+    for (int j = t; j <= n; j += kDispThreads) a.expert_offsets[j] = loff[j];
+}
+
+template <typename V, bool SELF>
 __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a) {
   extern __shared__ int lds[];
   const int n = a.n;
   const int cp = a.chunk_tokens * a.k;          // pairs per chunk
   int* cnt = lds;                                // [n] running counts inside the chunk
   int* lrow = cnt + n;                           // [cp] dispatched row (-1: dropped)
+  int* lbase = lrow + cp;                        // SELF: [n] slot base of this chunk
+  int* loff = lbase + n;                         // SELF: [n + 1] expert offsets, then [n] kept counts
+  int* part = loff + 2 * n + 1;                  // SELF: [3][4 kDispThreads]
   const int c = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t p0 = int64_t(c) * cp;
@@ -94,6 +204,20 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
   const int q0 = ct / vpr, v0 = ct - q0 * vpr;
   const int dq = kDispCopyThreads / vpr, dv = kDispCopyThreads - dq * vpr;
   V pv[kDispPrefetch];
+  if (wave != 0) {   // the chunk's source rows: their destinations come later
+    int q = q0, v = v0;
+#pragma unroll
+    for (int u = 0; u < kDispPrefetch; ++u) {
+      if (q < qend) pv[u] = x[src_row(q) * vpr + v];
+      q += dq;
+      v += dv;
+      if (v >= vpr) {
+        v -= vpr;
+        ++q;
+      }
+    }
+  }
+  if constexpr (SELF) derive_prefix(a, c, part, lbase, loff);
   if (wave == 0) {
     for (int j = lane; j < n; j += 64) cnt[j] = 0;
     __builtin_amdgcn_wave_barrier();
@@ -113,16 +237,22 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
       if (!inside) continue;
       int row = -1;
       if (valid) {
-        // chunk base of expert e: its super-chunk prefix plus the earlier chunks of the super chunk
-        int base = a.super_prefix[int64_t(s) * n + e];
-        const int off = a.expert_offsets[e];
-        for (int cc = s * a.sup; cc < c; cc += 16) {
-          int v[16];
+        int base, off;
+        if constexpr (SELF) {
+          base = lbase[e];
+          off = loff[e];
+        } else {
+          // chunk base of expert e: its super-chunk prefix plus the earlier chunks of the super chunk
+          base = a.super_prefix[int64_t(s) * n + e];
+          off = a.expert_offsets[e];
+          for (int cc = s * a.sup; cc < c; cc += 16) {
+            int v[16];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = cw[2 * (int64_t(min(cc + u, c - 1)) * n + e)];
+            for (int u = 0; u < 16; ++u) v[u] = cw[2 * (int64_t(min(cc + u, c - 1)) * n + e)];
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            if (cc + u < c) base += v[u];
+            for (int u = 0; u < 16; ++u)
+              if (cc + u < c) base += v[u];
+          }
         }
         const int slot = base + before + __popcll(pr & lanemask_lt());
         if (slot < a.capacity) row = off + slot;
@@ -132,18 +262,6 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
       a.token_to_row[p] = row;
       if (a.drop_mask) a.drop_mask[p] = row < 0 ? 1 : 0;
       if (row >= 0 && a.row_to_token) a.row_to_token[row] = int32_t(src_row(g + lane));
-    }
-  } else {
-    int q = q0, v = v0;
-#pragma unroll
-    for (int u = 0; u < kDispPrefetch; ++u) {
-      if (q < qend) pv[u] = x[src_row(q) * vpr + v];
-      q += dq;
-      v += dv;
-      if (v >= vpr) {
-        v -= vpr;
-        ++q;
-      }
     }
   }
   if (!a.dispatched) return;
@@ -194,17 +312,32 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
   }
 }
 
+template <bool SELF>
+static void launch_rank_copy(const DispatchArgs& a, size_t lds, hipStream_t s) {
+  const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.dispatched);
+  if (a.row_bytes % 16 == 0 && al % 16 == 0)
+    hipLaunchKernelGGL((k_disp_rank_copy<u32x4, SELF>), dim3(a.nch), dim3(kDispThreads), lds, s, a);
+  else if (a.row_bytes % 4 == 0 && al % 4 == 0)
+    hipLaunchKernelGGL((k_disp_rank_copy<uint32_t, SELF>), dim3(a.nch), dim3(kDispThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_disp_rank_copy<uint16_t, SELF>), dim3(a.nch), dim3(kDispThreads), lds, s, a);
+}
+
+bool dispatch_self_prefix_ok(int nch, int n) {
+  return n <= 256 && n % 4 == 0 && int64_t(nch) * n * int64_t(sizeof(int32_t)) <= kDispSelfPrefixBytes;
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s) {
+  if (a.self_prefix) {
+    // cnt [n], lrow [cp], lbase [n], loff [n + 1] + kept [n], part [12 kDispThreads]
+    const size_t lds = (4 * size_t(a.n) + 1 + size_t(a.chunk_tokens) * a.k + 12 * size_t(kDispThreads)) * sizeof(int);
+    launch_rank_copy<true>(a, lds, s);
+    return hipGetLastError();
+  }
   if (!prefix_ready)
     hipLaunchKernelGGL(k_disp_hist, dim3(a.nch), dim3(kDispThreads), (a.n + kDispPrefixBuf) * sizeof(int), s, a);
   const size_t lds = (size_t(a.n) + size_t(a.chunk_tokens) * a.k) * sizeof(int);
-  const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.dispatched);
-  if (a.row_bytes % 16 == 0 && al % 16 == 0)
-    hipLaunchKernelGGL(k_disp_rank_copy<u32x4>, dim3(a.nch), dim3(kDispThreads), lds, s, a);
-  else if (a.row_bytes % 4 == 0 && al % 4 == 0)
-    hipLaunchKernelGGL(k_disp_rank_copy<uint32_t>, dim3(a.nch), dim3(kDispThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL(k_disp_rank_copy<uint16_t>, dim3(a.nch), dim3(kDispThreads), lds, s, a);
+  launch_rank_copy<false>(a, lds, s);
   return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ struct RouteArgs {
   int32_t* super_prefix;
   uint32_t* done;         // completion ticket (control region)
   int lds_region_ints;    // set by launch_route
+  bool finish;            // false: store the chunk rows only (the dispatch finishes)
 };
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
 int route_chunk_tokens(const RoutePlan& plan);  // tokens per route workgroup (= dispatch chunk)
@@ -83,7 +84,19 @@ struct DispatchArgs {
   void* dispatched;
   int64_t row_bytes;    // d * element size
   uint32_t* done;       // completion ticket (control region)
+  // self_prefix: the route kernel left only its chunk rows; every dispatch
+  // workgroup derives the expert totals, its chunk bases and the offsets from
+  // them, and workgroup 0 publishes the load statistics (nullptr: not wanted)
+  bool self_prefix;
+  int32_t* counts;
+  float* prob_sum;
+  float* f;
+  float* P;
+  float* aux;
+  float alpha;
 };
+// chunk-row bytes up to which the dispatch derives the prefix itself
+constexpr int64_t kDispSelfPrefixBytes = 512 << 10;
 constexpr int kDispMaxChunkPairs = 4096;
 // chunk tokens for m tokens x k choices given the route workgroup size
 inline int dispatch_chunk_tokens(int route_tokens, int k) {
@@ -91,6 +104,8 @@ inline int dispatch_chunk_tokens(int route_tokens, int k) {
 }
 size_t dispatch_ws_bytes(int64_t m, int k, int n, int chunk_tokens);
 hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s);
+// whether the dispatch can derive the prefix from nch chunk rows of n experts
+bool dispatch_self_prefix_ok(int nch, int n);
 
 // ---------------------------------------------------------------- expert FFN
 size_t ffn_ws_bytes(int64_t rows_bound, int d_ff);

@@ -483,8 +483,16 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
         acc += SCORES ? v : score_of(e.score, v, tok_mx[tl], tok_sum[tl]);
       }
     }
-    store_agent(a.chunks + row0 + j, pack_chunk(hist[j], acc));
+    if (a.finish) {
+      store_agent(a.chunks + row0 + j, pack_chunk(hist[j], acc));
+    } else {   // split rows for the next kernel: counts [chunks][n] int32, then score sums [chunks][n] fp32
+      int32_t* cc = reinterpret_cast<int32_t*>(a.chunks);
+      float* cps = reinterpret_cast<float*>(cc + int64_t(gridDim.x) * e.n);
+      cc[row0 + j] = hist[j];
+      cps[row0 + j] = acc;
+    }
   }
+  if (!a.finish) return;
   __shared__ int s_flag;
   if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
   FinalizeArgs f{};
