@@ -15,7 +15,7 @@
  *     owned by the caller.  The library allocates no device memory: scratch
  *     space is the caller's workspace `ws` of at least moe_workspace_size()
  *     bytes, 256-byte aligned.
- *   - The first 4096 bytes of a workspace are control words that must be
+ *   - The first 53248 bytes of a workspace are control words that must be
  *     zero before the workspace is first used (moe_workspace_init(), or any
  *     zero fill).  Every call leaves them zero again.  Two calls that run at
  *     the same time (different streams) must not share a workspace.

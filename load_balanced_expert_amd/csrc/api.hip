@@ -142,6 +142,8 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
   }
   a.done = ctl_ticket(ws, kTicketRoute);
   a.finish = !ex.defer_finish;
+  a.sup_counts = at<int32_t>(ws, kSupCountsOff);
+  a.sup_psum = at<unsigned long long>(ws, kSupPsumOff);
   RoutePlan rp = L.rp;
   if (rp.mfma && (reinterpret_cast<uintptr_t>(x) % 16) != 0) rp.mfma = false;
   return hip_status(launch_route(rp, a, st));
@@ -392,6 +394,8 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
     // the totals, slot bases and offsets, and publish the load statistics
     ex.defer_finish = true;
     da.self_prefix = true;
+    da.sup_counts = at<int32_t>(ws, kSupCountsOff);
+    da.sup_psum = at<unsigned long long>(ws, kSupPsumOff);
     da.counts = counts;
     da.prob_sum = psum;
     da.f = f;
@@ -421,8 +425,10 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
       return st;
   }
   mark(4);
+  // the combine also clears the per-super-chunk sums for the next layer call
   st = hip_status(launch_combine(sh.m, sh.d, sh.k, y, ffn ? true : sh.x_dtype == MOE_BF16, gate, t2r, x, o->out,
-                                 sh.x_dtype == MOE_BF16, s));
+                                 sh.x_dtype == MOE_BF16, s, da.self_prefix ? at<void>(ws, kSupCountsOff) : nullptr,
+                                 kControlBytes - kSupCountsOff));
   mark(5);
   return st;
 }

@@ -57,7 +57,9 @@ template <bool XB, bool YB>
 __global__ __launch_bounds__(256) void k_combine_vec(int64_t m, int d, int k, const void* __restrict__ y,
                                                      const float* __restrict__ gate,
                                                      const int32_t* __restrict__ t2r, const void* __restrict__ res,
-                                                     void* __restrict__ out) {
+                                                     void* __restrict__ out, u32x4* clear, int clear_vecs) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < clear_vecs; i += 256) clear[i] = u32x4{0u, 0u, 0u, 0u};
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + wave;
   if (t >= m) return;
@@ -98,7 +100,10 @@ __global__ __launch_bounds__(256) void k_combine_vec(int64_t m, int d, int k, co
 __global__ __launch_bounds__(256) void k_combine_scalar(int64_t m, int d, int k, const void* __restrict__ y, int yb,
                                                         const float* __restrict__ gate,
                                                         const int32_t* __restrict__ t2r,
-                                                        const void* __restrict__ res, void* __restrict__ out, int xb) {
+                                                        const void* __restrict__ res, void* __restrict__ out, int xb,
+                                                        u32x4* clear, int clear_vecs) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < clear_vecs; i += 256) clear[i] = u32x4{0u, 0u, 0u, 0u};
   const int64_t items = m * d;
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < items; i += int64_t(gridDim.x) * 256) {
     const int64_t t = i / d, c = i - t * d;
@@ -120,23 +125,30 @@ __global__ __launch_bounds__(256) void k_combine_scalar(int64_t m, int d, int k,
 }
 
 hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, const float* gate,
-                          const int32_t* t2r, const void* residual, void* out, bool x_bf16, hipStream_t s) {
+                          const int32_t* t2r, const void* residual, void* out, bool x_bf16, hipStream_t s,
+                          void* clear, size_t clear_bytes) {
+  u32x4* cv = static_cast<u32x4*>(clear);
+  const int cn = clear ? int(clear_bytes / sizeof(u32x4)) : 0;
   const uintptr_t al = reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(out) |
                        reinterpret_cast<uintptr_t>(residual);
   if (d % 8 == 0 && (al % 16) == 0) {
     const unsigned blocks = unsigned(ceil_div64(m, 4));
     if (x_bf16 && y_bf16)
-      hipLaunchKernelGGL((k_combine_vec<true, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+      hipLaunchKernelGGL((k_combine_vec<true, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out,
+                         cv, cn);
     else if (x_bf16)
-      hipLaunchKernelGGL((k_combine_vec<true, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+      hipLaunchKernelGGL((k_combine_vec<true, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual,
+                         out, cv, cn);
     else if (y_bf16)
-      hipLaunchKernelGGL((k_combine_vec<false, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+      hipLaunchKernelGGL((k_combine_vec<false, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual,
+                         out, cv, cn);
     else
-      hipLaunchKernelGGL((k_combine_vec<false, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out);
+      hipLaunchKernelGGL((k_combine_vec<false, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual,
+                         out, cv, cn);
   } else {
     const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(m * d, 256), 65536));
     hipLaunchKernelGGL(k_combine_scalar, dim3(blocks), dim3(256), 0, s, m, d, k, y, int(y_bf16), gate, t2r, residual,
-                       out, int(x_bf16));
+                       out, int(x_bf16), cv, cn);
   }
   return hipGetLastError();
 }

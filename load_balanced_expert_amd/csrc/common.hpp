@@ -20,7 +20,14 @@ constexpr int kMaxExperts = 4096;
 // ticket leaves it zero again).
 constexpr int kMaxSuperChunks = 16;
 constexpr int kMaxD = 65536;   // keeps per-chunk copy item counts within 32 bits
-constexpr size_t kControlBytes = 4096;
+// Control region: tickets in the first 4096 bytes, then the per-super-chunk
+// expert counts [16][256] int32 and fixed-point score sums [16][256] uint64
+// that the Switch layer's route kernel accumulates and its combine clears.
+constexpr size_t kSupCountsOff = 4096;
+constexpr size_t kSupPsumOff = kSupCountsOff + size_t(kMaxSuperChunks) * 256 * sizeof(int32_t);
+constexpr size_t kControlBytes = kSupPsumOff + size_t(kMaxSuperChunks) * 256 * sizeof(uint64_t);
+constexpr int kSelfPrefixMaxN = 256;
+constexpr float kPsumScale = 4294967296.0f;   // 2^32: fixed-point score sums
 enum CtlTicket { kTicketRoute = 0, kTicketDispatch = 1, kTicketBalance = 2 };
 inline uint32_t* ctl_ticket(void* ws, int which) { return static_cast<uint32_t*>(ws) + which; }
 

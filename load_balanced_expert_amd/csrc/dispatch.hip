@@ -64,83 +64,57 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
   finalize_chunks(f, lds, n + kDispPrefixBuf, kDispThreads);
 }
 
-// Wave 0 ranks the chunk and computes its slots while the other 15 waves read
-// the chunk's source rows (only their destinations depend on the slots): up
-// to kDispPrefetch 16-byte items per thread of those waves, the rest after.
+// Wave 0 loads the chunk's expert ids and ranks them, waves 1-2 load the
+// prefix data, and waves 3-15 read the chunk's source rows (only their
+// destinations depend on the slots), all at once: up to kDispPrefetch
+// 16-byte items per thread of those waves, the rest after the slots.
 constexpr int kDispPrefetch = 4;
-constexpr int kDispCopyThreads = kDispThreads - 64;
+constexpr int kDispCopyWave0 = 3;
+constexpr int kDispCopyThreads = kDispThreads - 64 * kDispCopyWave0;
 
-// Self prefix (n <= 256, n % 4 == 0): the route kernel left split chunk rows
-// (counts [nch][n] int32, then score sums [nch][n] fp32).  Every workgroup
-// reads all count rows with 16-byte loads (a thread owns 4 experts and a
-// contiguous range of chunks) and keeps per expert the total and the count
-// of the chunks before its own (its slot base); workgroup 0 also sums the
-// score rows.  Sums run in a fixed order.  Wave 0 scans the kept counts into
-// the expert offsets; workgroup 0 publishes counts, f, P, aux and the
-// offsets.  part: 3 arrays of G n = 4 kDispThreads ints.
-__device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int* part, int* lbase, int* loff) {
-  const int n = a.n, t = threadIdx.x, nq = n / 4;
-  const int G = kDispThreads / nq;
+// Self prefix (n <= 256): the route kernel left per-chunk count rows
+// [nch][n] int32 and, per super chunk of `sup` chunks, the expert counts and
+// fixed-point score sums (integer atomics, so order-free).  Per expert, a
+// thread adds the super-chunk counts (the total) and those before this
+// chunk's super chunk plus the count rows of the earlier chunks inside it
+// (this chunk's slot base); wave 0 scans the kept counts into the expert
+// offsets.  Workgroup 0 publishes counts, f, P, aux and the offsets.
+__device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int* lbase, int* loff) {
+  const int n = a.n, t = threadIdx.x;
+  const int nsup = ceil_div(a.nch, a.sup), sc = c / a.sup;
   const bool stats = c == 0;
-  int* pc = part;                                                  // [G][n] counts
-  int* pb = part + 4 * kDispThreads;                               // [G][n] counts before chunk c
-  float* pp = reinterpret_cast<float*>(part + 8 * kDispThreads);   // [G][n] score sums (workgroup 0)
-  const int32_t* ccnt = reinterpret_cast<const int32_t*>(a.chunks);
-  const float* cps = reinterpret_cast<const float*>(ccnt + int64_t(a.nch) * n);
-  if (t < G * nq) {
-    const int e4 = (t % nq) * 4, g = t / nq;
-    const int lo = g * a.nch / G, hi = (g + 1) * a.nch / G;
-    int cs[4] = {0, 0, 0, 0}, cb[4] = {0, 0, 0, 0};
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int cc = lo; cc < hi; cc += 8) {
-      u32x4 v[8];
-      f32x4 w[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t o = int64_t(min(cc + u, hi - 1)) * n + e4;
-        v[u] = *reinterpret_cast<const u32x4*>(ccnt + o);
-        if (stats) w[u] = *reinterpret_cast<const f32x4*>(cps + o);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (cc + u < hi) {
-          const bool before = cc + u < c;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            cs[q] += int(v[u][q]);
-            cb[q] += before ? int(v[u][q]) : 0;
-            if (stats) ps[q] += w[u][q];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      pc[g * n + e4 + q] = cs[q];
-      pb[g * n + e4 + q] = cb[q];
-      pp[g * n + e4 + q] = ps[q];
-    }
-  }
-  __syncthreads();
   int* ltot = loff + n + 1;   // kept counts, then scanned by wave 0
+  const int32_t* crow = reinterpret_cast<const int32_t*>(a.chunks);
   double auxp = 0.0;
-  if (t < n) {
-    int tot = 0, base = 0;
-    float ps = 0.f;
-    for (int g = 0; g < G; ++g) {
-      tot += pc[g * n + t];
-      base += pb[g * n + t];
-      ps += pp[g * n + t];
+  const int pt = t - 64;   // waves 1-2 load the prefix data while wave 0 ranks
+  for (int e = pt; pt >= 0 && pt < 128 && e < n; e += 128) {
+    int v[kMaxSuperChunks], w[kMaxSuperChunks];
+#pragma unroll
+    for (int q = 0; q < kMaxSuperChunks; ++q) {
+      v[q] = q < nsup ? a.sup_counts[q * n + e] : 0;
+      const int cc = sc * a.sup + q;   // earlier chunks of this super chunk (up to 16 per pass)
+      w[q] = cc < c ? crow[int64_t(cc) * n + e] : 0;
     }
-    lbase[t] = base;
-    ltot[t] = min(tot, a.capacity);
+    int tot = 0, base = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxSuperChunks; ++q) {
+      tot += v[q];
+      base += q < sc ? v[q] : 0;
+      base += w[q];
+    }
+    for (int cc = sc * a.sup + kMaxSuperChunks; cc < c; ++cc) base += crow[int64_t(cc) * n + e];
+    lbase[e] = base;
+    ltot[e] = min(tot, a.capacity);
     if (stats) {
+      unsigned long long ps = 0;
+      for (int q = 0; q < nsup; ++q) ps += a.sup_psum[q * n + e];
+      const double psum = double(ps) / double(kPsumScale);
       const int64_t m = a.pairs / a.k;
-      if (a.counts) a.counts[t] = tot;
-      if (a.prob_sum) a.prob_sum[t] = ps;
-      if (a.f) a.f[t] = float(tot) / float(m);
-      if (a.P) a.P[t] = ps / float(m);
-      auxp = (double(tot) / double(m)) * (double(ps) / double(m));
+      if (a.counts) a.counts[e] = tot;
+      if (a.prob_sum) a.prob_sum[e] = float(psum);
+      if (a.f) a.f[e] = float(tot) / float(m);
+      if (a.P) a.P[e] = float(psum / double(m));
+      auxp += (double(tot) / double(m)) * (psum / double(m));
     }
   }
   if (stats && a.aux) {   // fixed-order fp64 sum over the experts
@@ -150,7 +124,7 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int*
     __syncthreads();
     if (t == 0) {
       double s = 0.0;
-      for (int w = 0; w < (n + 63) / 64; ++w) s += red[w];
+      for (int w = 0; w < kDispThreads / 64; ++w) s += red[w];
       a.aux[0] = float(double(a.alpha) * double(n) * s);
     }
   }
@@ -183,10 +157,10 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
   const int n = a.n;
   const int cp = a.chunk_tokens * a.k;          // pairs per chunk
   int* cnt = lds;                                // [n] running counts inside the chunk
-  int* lrow = cnt + n;                           // [cp] dispatched row (-1: dropped)
-  int* lbase = lrow + cp;                        // SELF: [n] slot base of this chunk
+  int* lrow = cnt + n;                           // [cp] expert id, then dispatched row (-1: dropped)
+  int* lslot = lrow + cp;                        // [cp] slot inside the chunk
+  int* lbase = lslot + cp;                       // SELF: [n] slot base of this chunk
   int* loff = lbase + n;                         // SELF: [n + 1] expert offsets, then [n] kept counts
-  int* part = loff + 2 * n + 1;                  // SELF: [3][4 kDispThreads]
   const int c = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t p0 = int64_t(c) * cp;
@@ -200,11 +174,11 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
   auto src_row = [&](int q) -> int64_t {   // token of pair p0 + q
     return a.k == 1 ? p0 + q : int64_t(uint32_t(p0 + q) / uint32_t(a.k));
   };
-  const int ct = threadIdx.x - 64;   // copy thread index (waves 1-3)
+  const int ct = threadIdx.x - 64 * kDispCopyWave0;   // copy thread index (waves 3-15)
   const int q0 = ct / vpr, v0 = ct - q0 * vpr;
   const int dq = kDispCopyThreads / vpr, dv = kDispCopyThreads - dq * vpr;
   V pv[kDispPrefetch];
-  if (wave != 0) {   // the chunk's source rows: their destinations come later
+  if (wave >= kDispCopyWave0) {
     int q = q0, v = v0;
 #pragma unroll
     for (int u = 0; u < kDispPrefetch; ++u) {
@@ -217,12 +191,9 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
       }
     }
   }
-  if constexpr (SELF) derive_prefix(a, c, part, lbase, loff);
-  if (wave == 0) {
+  if (wave == 0) {   // rank the chunk's pairs in token-major order
     for (int j = lane; j < n; j += 64) cnt[j] = 0;
     __builtin_amdgcn_wave_barrier();
-    const int s = c / a.sup;
-    const int32_t* cw = reinterpret_cast<const int32_t*>(a.chunks);   // counts: low words of the chunk rows
     for (int g = 0; g < np; g += 64) {
       const bool inside = g + lane < np;
       const int e0 = inside ? a.idx[p0 + g + lane] : 0;
@@ -234,39 +205,50 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
       // every lane has read cnt[e] before the group's first lane advances it
       __builtin_amdgcn_wave_barrier();
       if (valid && (pr & lanemask_lt()) == 0) cnt[e] = before + __popcll(pr);
-      if (!inside) continue;
-      int row = -1;
-      if (valid) {
-        int base, off;
-        if constexpr (SELF) {
-          base = lbase[e];
-          off = loff[e];
-        } else {
-          // chunk base of expert e: its super-chunk prefix plus the earlier chunks of the super chunk
-          base = a.super_prefix[int64_t(s) * n + e];
-          off = a.expert_offsets[e];
-          for (int cc = s * a.sup; cc < c; cc += 16) {
-            int v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = cw[2 * (int64_t(min(cc + u, c - 1)) * n + e)];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-              if (cc + u < c) base += v[u];
-          }
-        }
-        const int slot = base + before + __popcll(pr & lanemask_lt());
-        if (slot < a.capacity) row = off + slot;
+      if (inside) {
+        lrow[g + lane] = valid ? e : -1;
+        lslot[g + lane] = before + __popcll(pr & lanemask_lt());
       }
-      const int64_t p = p0 + g + lane;
-      lrow[g + lane] = row;
-      a.token_to_row[p] = row;
-      if (a.drop_mask) a.drop_mask[p] = row < 0 ? 1 : 0;
-      if (row >= 0 && a.row_to_token) a.row_to_token[row] = int32_t(src_row(g + lane));
     }
+  }
+  if constexpr (SELF) derive_prefix(a, c, lbase, loff);   // has barriers
+  else __syncthreads();
+  // slots -> rows and maps, one thread per pair
+  const int s = c / a.sup;
+  const int32_t* cw = reinterpret_cast<const int32_t*>(a.chunks);   // counts: low words of the chunk rows
+  for (int q = threadIdx.x; q < np; q += kDispThreads) {
+    const int e = lrow[q];
+    int row = -1;
+    if (e >= 0) {
+      int base, off;
+      if constexpr (SELF) {
+        base = lbase[e];
+        off = loff[e];
+      } else {
+        // chunk base of expert e: its super-chunk prefix plus the earlier chunks of the super chunk
+        base = a.super_prefix[int64_t(s) * n + e];
+        off = a.expert_offsets[e];
+        for (int cc = s * a.sup; cc < c; cc += 16) {
+          int v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = cw[2 * (int64_t(min(cc + u, c - 1)) * n + e)];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (cc + u < c) base += v[u];
+        }
+      }
+      const int slot = base + lslot[q];
+      if (slot < a.capacity) row = off + slot;
+    }
+    const int64_t p = p0 + q;
+    a.token_to_row[p] = row;
+    if (a.drop_mask) a.drop_mask[p] = row < 0 ? 1 : 0;
+    if (row >= 0 && a.row_to_token) a.row_to_token[row] = int32_t(src_row(q));
+    lrow[q] = row;
   }
   if (!a.dispatched) return;
   __syncthreads();
-  if (wave != 0) {
+  if (wave >= kDispCopyWave0) {
     int q = q0, v = v0;
 #pragma unroll
     for (int u = 0; u < kDispPrefetch; ++u) {
@@ -324,19 +306,19 @@ static void launch_rank_copy(const DispatchArgs& a, size_t lds, hipStream_t s) {
 }
 
 bool dispatch_self_prefix_ok(int nch, int n) {
-  return n <= 256 && n % 4 == 0 && int64_t(nch) * n * int64_t(sizeof(int32_t)) <= kDispSelfPrefixBytes;
+  return n <= kSelfPrefixMaxN && super_chunk(nch) <= 64;   // at most 63 in-super count rows per expert
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s) {
   if (a.self_prefix) {
-    // cnt [n], lrow [cp], lbase [n], loff [n + 1] + kept [n], part [12 kDispThreads]
-    const size_t lds = (4 * size_t(a.n) + 1 + size_t(a.chunk_tokens) * a.k + 12 * size_t(kDispThreads)) * sizeof(int);
+    // cnt [n], lrow [cp], lslot [cp], lbase [n], loff [n + 1] + kept [n]
+    const size_t lds = (4 * size_t(a.n) + 1 + 2 * size_t(a.chunk_tokens) * a.k) * sizeof(int);
     launch_rank_copy<true>(a, lds, s);
     return hipGetLastError();
   }
   if (!prefix_ready)
     hipLaunchKernelGGL(k_disp_hist, dim3(a.nch), dim3(kDispThreads), (a.n + kDispPrefixBuf) * sizeof(int), s, a);
-  const size_t lds = (size_t(a.n) + size_t(a.chunk_tokens) * a.k) * sizeof(int);
+  const size_t lds = (size_t(a.n) + 2 * size_t(a.chunk_tokens) * a.k) * sizeof(int);
   launch_rank_copy<false>(a, lds, s);
   return hipGetLastError();
 }

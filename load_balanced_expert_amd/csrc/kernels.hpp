@@ -50,6 +50,8 @@ struct RouteArgs {
   uint32_t* done;         // completion ticket (control region)
   int lds_region_ints;    // set by launch_route
   bool finish;            // false: store the chunk rows only (the dispatch finishes)
+  int32_t* sup_counts;            // finish == false: per-super-chunk sums (atomics)
+  unsigned long long* sup_psum;
 };
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
 int route_chunk_tokens(const RoutePlan& plan);  // tokens per route workgroup (= dispatch chunk)
@@ -84,10 +86,13 @@ struct DispatchArgs {
   void* dispatched;
   int64_t row_bytes;    // d * element size
   uint32_t* done;       // completion ticket (control region)
-  // self_prefix: the route kernel left only its chunk rows; every dispatch
-  // workgroup derives the expert totals, its chunk bases and the offsets from
-  // them, and workgroup 0 publishes the load statistics (nullptr: not wanted)
+  // self_prefix: the route kernel left only its chunk count rows and the
+  // per-super-chunk sums; every dispatch workgroup derives the expert totals,
+  // its chunk bases and the offsets, and workgroup 0 publishes the load
+  // statistics (nullptr: not wanted)
   bool self_prefix;
+  const int32_t* sup_counts;            // [nsup][n] (control region)
+  const unsigned long long* sup_psum;   // [nsup][n] fixed point, 2^-32
   int32_t* counts;
   float* prob_sum;
   float* f;
@@ -95,8 +100,6 @@ struct DispatchArgs {
   float* aux;
   float alpha;
 };
-// chunk-row bytes up to which the dispatch derives the prefix itself
-constexpr int64_t kDispSelfPrefixBytes = 512 << 10;
 constexpr int kDispMaxChunkPairs = 4096;
 // chunk tokens for m tokens x k choices given the route workgroup size
 inline int dispatch_chunk_tokens(int route_tokens, int k) {
@@ -114,9 +117,10 @@ hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t
                              uint16_t* hidden, uint16_t* y, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
+// clear (optional): bytes of device memory the first workgroup zeroes (16-byte multiple)
 hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, const float* gate,
                           const int32_t* token_to_row, const void* residual, void* out,
-                          bool x_bf16, hipStream_t s);
+                          bool x_bf16, hipStream_t s, void* clear = nullptr, size_t clear_bytes = 0);
 
 // ---------------------------------------------------------------- balanced assignment
 size_t balance_ws_bytes(int64_t m, int n, int k, bool exact);

@@ -485,11 +485,13 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
     }
     if (a.finish) {
       store_agent(a.chunks + row0 + j, pack_chunk(hist[j], acc));
-    } else {   // split rows for the next kernel: counts [chunks][n] int32, then score sums [chunks][n] fp32
-      int32_t* cc = reinterpret_cast<int32_t*>(a.chunks);
-      float* cps = reinterpret_cast<float*>(cc + int64_t(gridDim.x) * e.n);
-      cc[row0 + j] = hist[j];
-      cps[row0 + j] = acc;
+    } else {
+      // count rows [chunks][n] int32 for the next kernel, and this chunk's share
+      // of its super chunk's totals: integer adds, so their order does not matter
+      const int64_t so = int64_t(blockIdx.x / a.sup) * e.n + j;
+      reinterpret_cast<int32_t*>(a.chunks)[row0 + j] = hist[j];
+      if (hist[j]) atomicAdd(a.sup_counts + so, hist[j]);
+      if (a.want_psum) atomicAdd(a.sup_psum + so, __float2ull_rn(acc * kPsumScale));
     }
   }
   if (!a.finish) return;
