@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (HBM counter calibration)")
+    p.add_argument("--workload", default="switch_base",
+                   choices=["switch_base", "lossfree", "balanced", "switch_c"],
+                   help="switch_base (default) is the headline; the others report the other configurations")
     return p.parse_args()
 
 
@@ -190,6 +193,10 @@ def main():
 
     import load_balanced_expert_amd as M
     import workloads as W
+
+    if args.workload != "switch_base":
+        {"lossfree": bench_lossfree, "balanced": bench_balanced, "switch_c": bench_switch_c}[args.workload](args)
+        return
 
     dev = "cuda:0"
     spec = W.SWITCH_BASE
@@ -342,6 +349,237 @@ def main():
         out["cpu_baseline"] = cpu_baseline(spec, inp, cap, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# The other configurations (one JSON line each; not the headline)
+def _dev(a, torch, np, dev="cuda:0"):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def _timed(he, stream, fn, steps, warmup, torch):
+    """ms per call of fn over `steps` back-to-back calls between two events."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = he.create(), he.create()
+    t0 = time.perf_counter()
+    he.record(a, stream)
+    for _ in range(steps):
+        fn()
+    he.record(b, stream)
+    torch.cuda.synchronize()
+    return he.ms(a, b) / steps, (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def bench_lossfree(args):
+    """16 micro-batches of 4096 tokens, d=2048, n=256, k=8, sigmoid: route with the Loss-Free bias,
+    then counts/P, global-batch accumulation and the bias update, micro-batch after micro-batch."""
+    import numpy as np
+    import torch
+    import load_balanced_expert_amd as M
+    import workloads as W
+    spec = W.LOSSFREE
+    inp = W.lossfree_inputs(spec, args.seed)
+    T, d, n, k = spec.T, spec.d, spec.N, spec.k
+    xs = [_dev(inp.micro_batch(t), torch, np) for t in range(spec.micro_batches)]
+    w_r = _dev(inp.w_r, torch, np)
+    dev = "cuda:0"
+    bias = torch.zeros(n, dtype=torch.float32, device=dev)
+    gc = torch.zeros(n, dtype=torch.int64, device=dev)
+    gt = torch.zeros(1, dtype=torch.int64, device=dev)
+    routs = [M.route(xs[0], w_r, k, score="sigmoid", bias=bias) for _ in range(spec.micro_batches)]
+    souts = [M.stats(T, k, routs[0].counts, routs[0].prob_sum) for _ in range(spec.micro_batches)]
+    torch.cuda.synchronize()
+    he = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def one_pass():
+        for t in range(spec.micro_batches):
+            r = M.route(xs[t], w_r, k, score="sigmoid", bias=bias, out=routs[t])
+            M.stats(T, k, r.counts, r.prob_sum, global_counts=gc, global_tokens=gt, bias=bias, gamma=spec.gamma,
+                    out=souts[t])
+
+    steps = max(1, args.steps // 10)
+    ms, wall_ms = _timed(he, stream, one_pass, steps, max(1, args.warmup // 5), torch)
+    tokens = spec.micro_batches * T
+    value = tokens / (ms * 1e-3)
+    # the route kernel alone, back to back
+    r0 = routs[0]
+    t_route = _timed(he, stream, lambda: M.route(xs[0], w_r, k, score="sigmoid", bias=bias, out=r0), 30, 3, torch)[0]
+    flops = 3 * 2.0 * T * d * n
+    alg_bytes = T * d * 2 + d * n * 4 + T * k * 8 + n * 8
+    out = {
+        "metric": "routed tokens/sec (Loss-Free biased top-k route + stats + global batch + bias update)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": max(1, args.warmup // 5),
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 x, fp32-accurate router (bf16x3 MFMA), fp32 bias state",
+        "data": "synthetic (4 cluster means ~N(0,4) per dim + N(0,1) noise, one cluster per micro-batch)",
+        "config": {"workload": "lossfree: 16 micro-batches x 4096 tokens, d_model=2048, n=256, k=8, sigmoid, "
+                               "gamma=1e-3", "global_batch": tokens, "parallelism": "single GPU"},
+        "roofline": {"kernel": "k_route_fused (bf16x3 MFMA router, sigmoid, biased top-8, histogram, score sums)",
+                     "bound": "mfma", "achieved": flops / (t_route * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / (t_route * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "traffic": None, "avg_launch_us": t_route * 1e3, "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "hbm_frac_of_same_launch": alg_bytes / (t_route * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "final_bias_range": [float(bias.min().item()), float(bias.max().item())],
+    }
+    if not args.no_cpu_baseline:
+        from oracle import router as OR
+        from oracle import stats as OS
+        t0 = time.perf_counter()
+        b = np.zeros(n, np.float32)
+        done = 0
+        while time.perf_counter() - t0 < args.cpu_seconds and done < spec.micro_batches:
+            x = inp.micro_batch(done)
+            r = OR.route(x, inp.w_r, k, score="sigmoid", bias=b)
+            b = OS.lossfree_update(b, r.counts, T, k, spec.gamma)
+            done += 1
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": done * T / el, "unit": "tokens/s", "cores": int(_cpu_threads()),
+                               "kind": "oracle", "sample": f"{done} micro-batches of 4096 tokens in {el:.1f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_balanced(args):
+    """m=4096, n=64, k=4: QB duals (5 iterations from beta = 0) then the exact completion."""
+    import numpy as np
+    import torch
+    import load_balanced_expert_amd as M
+    import workloads as W
+    spec = W.BALANCED
+    s_np = W.balanced_scores(spec, args.seed)
+    m, n, k = spec.m, spec.n, spec.k
+    s = _dev(s_np, torch, np)
+    beta = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    he = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+
+    def solve(iters, exact):
+        beta.zero_()
+        return M.balance_duals(s, k, beta, iters=iters, exact=exact)
+
+    t_exact = _timed(he, stream, lambda: solve(5, True), 20, 3, torch)[0]
+    info = solve(5, True).info
+    torch.cuda.synchronize()
+    t_qb20 = _timed(he, stream, lambda: solve(20, False), 20, 3, torch)[0]
+    t_qb1 = _timed(he, stream, lambda: solve(1, False), 20, 3, torch)[0]
+    per_iter = (t_qb20 - t_qb1) / 19
+    bytes_iter = 2 * m * n * 4
+    out = {
+        "metric": "balanced assignments/sec (QB duals, 5 iterations, + exact completion to the LP optimum)",
+        "value": m / (t_exact * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": 20, "warmup": 3,
+        "ms_per_step": t_exact, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 scores and duals, fp64 completion potentials",
+        "data": "synthetic (s = per-expert offset ~N(0,1.5^2) + N(0,1) noise)",
+        "config": {"workload": "balanced: m=4096, n=64, k=4, exactly 256 tokens per expert",
+                   "parallelism": "single GPU"},
+        "augmentations": int(info[1].item()), "qb_iteration_us": per_iter * 1e3,
+        "roofline": {"kernel": "k_qb_rows + k_qb_cols (one QB iteration)", "bound": "hbm",
+                     "achieved": bytes_iter / (per_iter * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": bytes_iter / (per_iter * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": bytes_iter, "avg_launch_us": per_iter * 1e3,
+                     "note": "s (1 MiB) stays in the caches; the iteration is latency-bound"},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import balance as OB
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            _, beta0, _ = OB.qb_solve(s_np, k, 5)
+            OB.ssp_complete(s_np, k, beta0)
+            done += 1
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": done * m / el, "unit": "tokens/s", "cores": int(_cpu_threads()),
+                               "kind": "oracle", "sample": f"{done} full solves (QB 5 + SSP completion) in {el:.1f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_switch_c(args):
+    """T=65536, d=1024, N=2048, top-1, cf 1.25, ReLU FFN d_ff=4096 (34.4 GB of bf16 expert weights, drawn on
+    the GPU from a seeded generator), timed like the headline."""
+    import numpy as np
+    import torch
+    import load_balanced_expert_amd as M
+    import workloads as W
+    spec = W.SWITCH_C
+    T, d, N, k, d_ff = spec.T, spec.d, spec.N, 1, spec.d_ff
+    cap = M.capacity(T, N, args.cf)
+    inp = W.switch_inputs(spec, args.seed)
+    x = _dev(inp.x, torch, np)
+    w_r = _dev(inp.w_r, torch, np)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(args.seed)
+    W1 = torch.empty((N, d_ff, d), dtype=torch.bfloat16, device="cuda:0")
+    W2 = torch.empty((N, d, d_ff), dtype=torch.bfloat16, device="cuda:0")
+    for w in (W1, W2):
+        for e0 in range(0, N, 256):   # in slices, to bound the fp32 temporary
+            w[e0:e0 + 256] = (torch.randn(w[e0:e0 + 256].shape, generator=g, device="cuda:0") * spec.w_std).to(
+                torch.bfloat16)
+    rows_bound = min(T * k, cap * N)
+    lo = M.allocate_layer_outputs(T, d, N, k, rows_bound, x.dtype, True, "cuda:0")
+    torch.cuda.synchronize()
+    he = HipEvents()
+
+    def step(ev=None):
+        M.switch_layer(x, w_r, k=k, capacity=cap, alpha=spec.alpha, w1=W1, w2=W2, outputs=lo, stage_events=ev)
+
+    steps = max(2, min(args.steps, 10))
+    for _ in range(max(1, min(args.warmup, 3))):
+        step()
+    torch.cuda.synchronize()
+    ev3 = [he.create() for _ in range(steps + 1)]
+    ev4 = [he.create() for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    for i in range(steps + 1):
+        step([None, None, None, ev3[i], ev4[i], None])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region = np.array([he.ms(ev4[i], ev3[i + 1]) for i in range(steps)])
+    ffn = np.array([he.ms(ev3[i], ev4[i]) for i in range(steps)])
+    metric_ms = float(np.mean(region))
+    rows = int(lo.expert_offsets[N].item())
+    alg_metric_bytes = (T * d * 2 + N * d * 4 + T * k * 8) + (T * k * 4 * 3) + 2 * rows * d * 2 + \
+        (rows * d * 2 + 2 * T * d * 2 + T * k * 8)
+    flops = 3 * 2.0 * T * d * N
+    t_ffn = float(np.mean(ffn)) * 1e-3
+    ffn_bytes = 2 * N * d * d_ff * 2 + 2 * rows * (d + d_ff) * 2
+    out = {
+        "metric": "routed tokens/sec (route+dispatch+combine) at T=65536,N=2048; % HBM roofline",
+        "value": T / (metric_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(1, min(args.warmup, 3)), "ms_per_step": wall * 1e3 / (steps + 1), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x, fp32-accurate router (bf16x3 MFMA), bf16 expert FFN",
+        "data": "synthetic (seeded normals; expert weights drawn on the GPU)",
+        "config": {"workload": "switch_c: T=65536, d_model=1024, N=2048 experts, top-1 softmax, capacity factor "
+                               f"{args.cf} (capacity {cap}), ReLU expert FFN d_ff=4096", "global_batch": T,
+                   "capacity": cap, "parallelism": "single GPU"},
+        "metric_ms_per_step": metric_ms, "expert_ffn_ms": t_ffn * 1e3,
+        "hbm_roofline_frac_of_metric_region": alg_metric_bytes / (metric_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "router_tflops_if_metric_were_router_only": flops / (metric_ms * 1e-3) / 1e12,
+        "dropped_tokens": int(lo.drop_mask.sum().item()),
+        "expert_ffn_roofline": {"bound": "hbm", "achieved": ffn_bytes / t_ffn / 1e9, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": ffn_bytes / t_ffn / 1e9 / HBM_PEAK_GBS,
+                                "algorithmic_bytes_per_stage": ffn_bytes},
+        "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -32,7 +32,10 @@ size_t balance_ws_bytes(int64_t m, int n, int k, bool exact) {
   size_t b = al256(size_t(m) * n * sizeof(float));   // s transposed
   b += al256(size_t(m) * sizeof(float));              // alpha
   b += al256(size_t(ceil_div64(m, kQbRowsPerBlock)) * n * sizeof(uint64_t));  // per-workgroup chunk rows
-  if (exact) b += 2 * al256(size_t(m) * k * sizeof(int32_t));  // assignment, per-expert token lists
+  if (exact) {
+    b += 2 * al256(size_t(m) * k * sizeof(int32_t));   // assignment, list positions
+    b += al256(size_t(n) * m * sizeof(int32_t));       // per-expert token lists
+  }
   return b;
 }
 
@@ -195,11 +198,75 @@ __device__ __forceinline__ void wave_argbest64(double& key, int& ix) {
   }
 }
 
-__global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __restrict__ xi) {
+// Move costs of one source expert e (one row of M): for every target j, the
+// cheapest s_te − s_tj over the tokens t that hold e but not j, ties to the
+// lower token index.  Thread (slice, j) scans every 16th token of e's list
+// (batches of 8 tokens, loads first); slices meet in LDS.
+__device__ __forceinline__ void qb_row_costs(const BalanceArgs& a, const int32_t* __restrict__ xi,
+                                             const int32_t* __restrict__ lst, int e, int cnt_e,
+                                             unsigned long long* Mk, int* arg, unsigned long long* pk, int* pi_) {
+  const int n = a.n, k = a.k, tid = threadIdx.x, j = tid & 63, sl = tid >> 6;
+  const int64_t m = a.m;
+  unsigned long long bk = ~0ull;
+  int bt = 0x7FFFFFFF;
+  const int32_t* L = lst + int64_t(e) * m;
+  for (int b0 = sl * 8; b0 < cnt_e; b0 += 16 * 8) {
+    int t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = L[min(b0 + u, cnt_e - 1)];
+    float se[8], sj[8];
+    bool has[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* sr = a.s + int64_t(t[u]) * n;
+      se[u] = sr[e];
+      sj[u] = j < n ? sr[j] : 0.f;
+      has[u] = false;
+      for (int r = 0; r < k; ++r) has[u] |= xi[int64_t(t[u]) * k + r] == j;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (b0 + u < cnt_e && j < n && !has[u]) {
+        const unsigned long long key = f64_key(double(se[u]) - double(sj[u]));
+        if (key < bk || (key == bk && t[u] < bt)) {
+          bk = key;
+          bt = t[u];
+        }
+      }
+    }
+  }
+  pk[sl * 64 + j] = bk;
+  pi_[sl * 64 + j] = bt;
+  __syncthreads();
+  if (tid < 64) {
+    for (int q = 1; q < 16; ++q) {
+      const unsigned long long ok = pk[q * 64 + tid];
+      const int ot = pi_[q * 64 + tid];
+      if (ok < bk || (ok == bk && ot < bt)) {
+        bk = ok;
+        bt = ot;
+      }
+    }
+    if (tid < n) {
+      Mk[e * n + tid] = bk;
+      arg[e * n + tid] = bt;
+    }
+  }
+  __syncthreads();
+}
+
+// Exact completion by successive shortest paths.  xi: [m][k] assignment,
+// pos: [m][k] position of token i in the list of its r-th expert, lst:
+// [n][m] token lists.  M is kept in LDS and only the rows of the experts a
+// moved token held before or after its move are recomputed.
+__global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __restrict__ xi,
+                                                      int32_t* __restrict__ pos, int32_t* __restrict__ lst) {
   __shared__ unsigned long long Mk[kCompleteMaxN * kCompleteMaxN];
   __shared__ int arg[kCompleteMaxN * kCompleteMaxN];
+  __shared__ unsigned long long pk[1024];
+  __shared__ int pt[1024];
   __shared__ double pi[kCompleteMaxN], dist[kCompleteMaxN];
-  __shared__ int cnt[kCompleteMaxN], pred[kCompleteMaxN], vis[kCompleteMaxN];
+  __shared__ int cnt[kCompleteMaxN], pred[kCompleteMaxN], vis[kCompleteMaxN], dirty[kCompleteMaxN];
   __shared__ int s_go, s_target, s_fail;
   __shared__ double s_D;
   const int n = a.n, k = a.k;
@@ -210,9 +277,12 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
   for (int j = tid; j < n; j += 1024) {
     pi[j] = double(a.beta[j]);
     cnt[j] = 0;
+    dirty[j] = 1;
   }
   __syncthreads();
-  // initial assignment: top-k of the exact keys s_ij − β_j (lower index on ties)
+  // initial assignment: top-k of the exact keys s_ij − β_j (lower index on ties),
+  // and the per-expert token lists (their order does not matter: every row
+  // minimum breaks ties by token index)
   for (int64_t i = wave; i < m; i += 16) {
     double last = INFINITY;
     int lj = -1;
@@ -231,48 +301,32 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
       lj = bj;
       if (lane == 0) {
         xi[i * k + r] = bj;
-        atomicAdd(&cnt[bj], 1);
+        const int slot = atomicAdd(&cnt[bj], 1);
+        lst[int64_t(bj) * m + slot] = int(i);
+        pos[i * k + r] = slot;
       }
     }
   }
+  __threadfence_block();
+  __syncthreads();
   int aug = 0;
   const int max_aug = int(min<int64_t>(m * k, 0x7FFFFFFF));
   for (;;) {
+    // refresh the rows of M whose source expert changed
+    for (int e = 0; e < n; ++e)
+      if (dirty[e]) qb_row_costs(a, xi, lst, e, cnt[e], Mk, arg, pk, pt);
     __syncthreads();
     if (tid == 0) {
       int go = 0;
-      for (int j = 0; j < n; ++j) go |= cnt[j] > q;
+      for (int j = 0; j < n; ++j) {
+        go |= cnt[j] > q;
+        dirty[j] = 0;
+      }
       s_go = go && aug < max_aug;
       s_fail = 0;
     }
     __syncthreads();
     if (!s_go) break;
-    for (int e = tid; e < n * n; e += 1024) {
-      Mk[e] = ~0ull;
-      arg[e] = 0x7FFFFFFF;
-    }
-    __syncthreads();
-    // move costs: token i holding a but not j offers s_ia − s_ij for a -> j
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int64_t c = tid; c < m * n; c += 1024) {
-        const int64_t i = c / n;
-        const int j = int(c - i * n);
-        const int32_t* xr = xi + i * k;
-        bool has = false;
-        for (int r = 0; r < k; ++r) has |= xr[r] == j;
-        if (has) continue;
-        const double sij = double(s[i * n + j]);
-        for (int r = 0; r < k; ++r) {
-          const int aa = xr[r];
-          const uint64_t key = f64_key(double(s[i * n + aa]) - sij);
-          if (pass == 0)
-            atomicMin(&Mk[aa * n + j], (unsigned long long)key);
-          else if (Mk[aa * n + j] == key)
-            atomicMin(&arg[aa * n + j], int(i));
-        }
-      }
-      __syncthreads();
-    }
     // Dijkstra from every over-full expert to the first under-full one reached
     if (wave == 0) {
       double dv = (lane < n && cnt[lane] > q) ? 0.0 : INFINITY;
@@ -320,19 +374,66 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
       const double D = s_D;
       pi[tid] -= vis[tid] ? fmin(dist[tid], D) : D;
     }
-    if (tid == 0) {
+    if (wave == 0) {
+      // move one token along every edge of the path (target back to source).
+      // M stays exact: the source row is rescanned next round; token i joining
+      // j adds it as a candidate to row j; for the other experts a of token i,
+      // (a -> aa) gains candidate i and (a -> j) loses it (a rescan only if i
+      // was its cheapest token).
       int j = s_target;
       while (pred[j] >= 0) {
         const int aa = pred[j];
         const int i = arg[aa * n + j];
         int32_t* xr = xi + int64_t(i) * k;
-        for (int r = 0; r < k; ++r)
-          if (xr[r] == aa) xr[r] = j;
+        int r = 0;
+        for (int rr = 0; rr < k; ++rr)
+          if (xr[rr] == aa) r = rr;
+        const float* si = s + int64_t(i) * n;
+        // row j gains candidate i for every l the token will not hold
+        if (lane < n) {
+          bool held = lane == j;
+          for (int rr = 0; rr < k; ++rr) held |= rr != r && xr[rr] == lane;
+          if (!held) {
+            const unsigned long long key = f64_key(double(si[j]) - double(si[lane]));
+            const int o = j * n + lane;
+            if (key < Mk[o] || (key == Mk[o] && i < arg[o])) {
+              Mk[o] = key;
+              arg[o] = i;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) {
+          for (int rr = 0; rr < k; ++rr) {
+            const int e = xr[rr];
+            if (rr == r) continue;
+            const unsigned long long key = f64_key(double(si[e]) - double(si[aa]));
+            const int o = e * n + aa;
+            if (key < Mk[o] || (key == Mk[o] && i < arg[o])) {
+              Mk[o] = key;
+              arg[o] = i;
+            }
+            if (arg[e * n + j] == i) dirty[e] = 1;
+          }
+          dirty[aa] = 1;
+          // leave aa's list (the last entry fills the hole), join j's
+          const int p = pos[int64_t(i) * k + r];
+          const int last = lst[int64_t(aa) * m + cnt[aa] - 1];
+          lst[int64_t(aa) * m + p] = last;
+          for (int rr = 0; rr < k; ++rr)
+            if (xi[int64_t(last) * k + rr] == aa) pos[int64_t(last) * k + rr] = p;
+          cnt[aa] -= 1;
+          lst[int64_t(j) * m + cnt[j]] = i;
+          pos[int64_t(i) * k + r] = cnt[j];
+          cnt[j] += 1;
+          xr[r] = j;
+        }
+        __builtin_amdgcn_wave_barrier();
         j = aa;
       }
-      cnt[j] -= 1;
-      cnt[s_target] += 1;
     }
+    __threadfence_block();
+    __syncthreads();
     ++aug;
   }
   __syncthreads();
@@ -389,6 +490,10 @@ hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
   uint64_t* chunks = reinterpret_cast<uint64_t*>(ws);
   ws += al256(size_t(ceil_div64(a.m, kQbRowsPerBlock)) * a.n * sizeof(uint64_t));
   int32_t* xi = reinterpret_cast<int32_t*>(ws);
+  ws += al256(size_t(a.m) * a.k * sizeof(int32_t));
+  int32_t* pos = reinterpret_cast<int32_t*>(ws);
+  ws += al256(size_t(a.m) * a.k * sizeof(int32_t));
+  int32_t* lst = reinterpret_cast<int32_t*>(ws);
   float* alpha = a.alpha_out ? a.alpha_out : alpha_int;
 
   if (a.info) hipLaunchKernelGGL(k_qb_info, dim3(1), dim3(64), 0, s, a.info, a.iters);
@@ -406,7 +511,7 @@ hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q);
   }
   if (a.exact)
-    hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi);
+    hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi, pos, lst);
   else
     hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
   return hipGetLastError();
