@@ -13,7 +13,7 @@ using namespace moe;
 size_t al(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t planes, logits, chunks, r2t, hidden;
+  size_t planes, logits, kpart, chunks, r2t, hidden;
   size_t idx, gate, counts, psum, f, P, aux, t2r, drop, offs, disp, y;
   size_t route_end, dispatch_end, total;
   RoutePlan rp;
@@ -50,6 +50,7 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   size_t o = kControlBytes;
   L.planes = o; o += al(L.rp.planes_bytes);
   L.logits = o; o += al(L.rp.logits_bytes);
+  L.kpart = o; o += al(L.rp.kpart_bytes);
   L.route_end = o;
   L.route_ct = route_chunk_tokens(L.rp);
   L.disp_ct = dispatch_chunk_tokens(L.route_ct, s.k);
@@ -141,6 +142,8 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
     a.super_prefix = ex.disp->super_prefix;
   }
   a.done = ctl_ticket(ws, kTicketRoute);
+  a.kpart = at<float>(ws, L.kpart);
+  a.tile_tickets = at<uint32_t>(ws, kTileTicketsOff);
   a.finish = !ex.defer_finish;
   a.sup_counts = at<int32_t>(ws, kSupCountsOff);
   a.sup_psum = at<unsigned long long>(ws, kSupPsumOff);

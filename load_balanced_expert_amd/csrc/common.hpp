@@ -29,6 +29,8 @@ constexpr size_t kControlBytes = kSupPsumOff + size_t(kMaxSuperChunks) * 256 * s
 constexpr int kSelfPrefixMaxN = 256;
 constexpr float kPsumScale = 4294967296.0f;   // 2^32: fixed-point score sums
 enum CtlTicket { kTicketRoute = 0, kTicketDispatch = 1, kTicketBalance = 2 };
+constexpr int kTileTicketsOff = 1024;   // bytes: per-token-tile tickets of the K-split route
+constexpr int kMaxKgTiles = 128;        // token tiles up to which the route splits K over workgroups
 inline uint32_t* ctl_ticket(void* ws, int which) { return static_cast<uint32_t*>(ws) + which; }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -17,6 +17,8 @@ struct RoutePlan {
   int dpad;        // d padded to a multiple of 32 (mfma)
   size_t planes_bytes;
   size_t logits_bytes;
+  int kg;          // fused route: workgroups (K ranges) per 32-token tile
+  size_t kpart_bytes;   // kg > 1: per-K-group logit tiles
 };
 constexpr int kFusedMaxN = 256;
 RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16);
@@ -50,6 +52,9 @@ struct RouteArgs {
   uint32_t* done;         // completion ticket (control region)
   int lds_region_ints;    // set by launch_route
   bool finish;            // false: store the chunk rows only (the dispatch finishes)
+  int kg;                         // workgroups per token tile (RoutePlan::kg)
+  float* kpart;                   // kg > 1: [tiles][kg][32][npad] partial logits (workspace)
+  uint32_t* tile_tickets;         // kg > 1: [tiles] (control region)
   int32_t* sup_counts;            // finish == false: per-super-chunk sums (atomics)
   unsigned long long* sup_psum;
 };

@@ -50,6 +50,14 @@ static int route_region_ints(const RoutePlan& plan, int n) {
   return stage_x(plan, n) ? std::max(part, x_tile_ints(plan)) : part;
 }
 
+// Reading fp32 W_r (4 bytes per weight per workgroup) and splitting it in
+// registers measured faster than loading prepared planes (6 bytes per weight)
+// both at d x n = 768 x 128 and at 2048 x 256, and it needs no preparation
+// kernel.
+bool route_direct(const RoutePlan& plan, int d, int n) {
+  return plan.fused && plan.mfma && d % 32 == 0 && (n == 32 || n == 64 || n == 128 || n == 256);
+}
+
 RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
   RoutePlan p{};
   p.fused = n <= kFusedMaxN;
@@ -60,6 +68,16 @@ RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
   if (p.fused && p.mfma && p.dpad != d && !stage_x(p, n)) p.mfma = false;   // global x rows need d % 32 == 0
   p.planes_bytes = p.mfma ? size_t(3) * p.npad * p.dpad * sizeof(uint16_t) : 0;
   p.logits_bytes = p.fused ? 0 : size_t(m) * p.npad * sizeof(float);
+  // Few token tiles (small batches): split each tile's K range over 2 or 4
+  // workgroups so that the whole chip works; the last of them adds the parts.
+  p.kg = 1;
+  const int64_t tiles = ceil_div64(m, kRouteBM);
+  if (route_direct(p, d, n) && tiles <= kMaxKgTiles) {
+    const int nt = p.npad / 32, ks = 16 / (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
+    p.kg = tiles <= 64 ? 4 : 2;
+    while (p.kg > 1 && p.dpad / 32 < p.kg * ks) p.kg /= 2;
+  }
+  p.kpart_bytes = p.kg > 1 ? size_t(tiles) * p.kg * kRouteBM * p.npad * sizeof(float) : 0;
   return p;
 }
 
@@ -223,12 +241,13 @@ struct DirectGemm {
   int kb0, cnt, rot, h;
   float r0[16], r1[16], r2[16];
 
-  __device__ __forceinline__ void init(const float* w, int dpad, int wave, int lane, int rot_) {
+  // K blocks [kbA, kbB) of the workgroup, split over its KS wave groups
+  __device__ __forceinline__ void init(const float* w, int kbA, int kbB, int wave, int lane, int rot_) {
     constexpr int KS = 16 / NT;
     const int tile = wave % NT, ks = wave / NT;
-    const int nkb = dpad / 32;
-    kb0 = ks * nkb / KS;
-    cnt = (ks + 1) * nkb / KS - kb0;
+    const int nkb = kbB - kbA;
+    kb0 = kbA + ks * nkb / KS;
+    cnt = kbA + (ks + 1) * nkb / KS - kb0;
     rot = cnt > 0 ? rot_ % cnt : 0;
     h = lane >> 5;
     wcol = w + tile * 32 + (lane & 31);
@@ -473,8 +492,9 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
 template <bool SCORES>
 __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows, const EpiArgs& e,
                                            const float* tok_mx, const float* tok_sum, const int* hist,
-                                           const RouteArgs& a, int* scratch, int scratch_ints) {
-  const int64_t row0 = int64_t(blockIdx.x) * e.n;
+                                           const RouteArgs& a, int* scratch, int scratch_ints, int chunk,
+                                           int nchunks) {
+  const int64_t row0 = int64_t(chunk) * e.n;
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
     float acc = 0.f;
     if (a.want_psum) {
@@ -488,7 +508,7 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
     } else {
       // count rows [chunks][n] int32 for the next kernel, and this chunk's share
       // of its super chunk's totals: integer adds, so their order does not matter
-      const int64_t so = int64_t(blockIdx.x / a.sup) * e.n + j;
+      const int64_t so = int64_t(chunk / a.sup) * e.n + j;
       reinterpret_cast<int32_t*>(a.chunks)[row0 + j] = hist[j];
       if (hist[j]) atomicAdd(a.sup_counts + so, hist[j]);
       if (a.want_psum) atomicAdd(a.sup_psum + so, __float2ull_rn(acc * kPsumScale));
@@ -496,10 +516,10 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
   }
   if (!a.finish) return;
   __shared__ int s_flag;
-  if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
+  if (!last_workgroup(a.done, unsigned(nchunks), &s_flag)) return;
   FinalizeArgs f{};
   f.chunks = a.chunks;
-  f.nch = int(gridDim.x);
+  f.nch = nchunks;
   f.sup = a.sup;
   f.n = e.n;
   f.m = a.m;
@@ -532,7 +552,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   float* lg = smem;
   int* hist = reinterpret_cast<int*>(smem) + a.lds_region_ints;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t t0 = int64_t(blockIdx.x) * kRouteBM;
+  // a token tile may be split over a.kg workgroups by K range (direct path only)
+  const int tile = int(blockIdx.x) / a.kg, g = int(blockIdx.x) % a.kg, ntiles = int(gridDim.x) / a.kg;
+  const int nkb = a.dpad / 32, kbA = g * nkb / a.kg, kbB = (g + 1) * nkb / a.kg;
+  const int64_t t0 = int64_t(tile) * kRouteBM;
   const int rows = int(min<int64_t>(kRouteBM, a.m - t0));
   for (int j = tid; j < a.npad; j += kRouteThreads) hist[j] = 0;
 
@@ -541,11 +564,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     const uint16_t* arow;
     DirectGemm<NT> dg;
-    if constexpr (DIRECT) dg.init(a.w_r, a.dpad, wave, lane, int(blockIdx.x));
+    if constexpr (DIRECT) dg.init(a.w_r, kbA, kbB, wave, lane, tile);
     if constexpr (XLDS) {
       // stage the 32 x rows in LDS with coalesced 16-byte loads (zero padding past the end)
       uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-      const int ldx = a.dpad + 8, cpr = a.dpad / 8;
+      // only this workgroup's K range [32 kbA, 32 kbB) of the tile is staged
+      const int ldx = a.dpad + 8, cpr = (kbB - kbA) * 4, kx = kbA * 32;
       // four loads in flight per thread before the LDS stores (one pass for d <= 1024)
       for (int c0 = tid; c0 < kRouteBM * cpr; c0 += 4 * kRouteThreads) {
         u32x4 v[4];
@@ -553,7 +577,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int c = c0 + u * kRouteThreads;
-          const int r = c / cpr, k = (c - r * cpr) * 8;
+          const int r = c / cpr, k = kx + (c - r * cpr) * 8;
           v[u] = u32x4{0u, 0u, 0u, 0u};
           dst[u] = c < kRouteBM * cpr ? r * ldx + k : -1;
           if (c < kRouteBM * cpr && r < rows && k < a.d) v[u] = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
@@ -586,6 +610,22 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
       }
     }
     __syncthreads();
+    if (a.kg > 1) {
+      // publish this K group's tile; the group that arrives last adds all of
+      // them in K-group order and goes on with the epilogue
+      const int tsz = kRouteBM * ldl;
+      float* mine = a.kpart + (int64_t(tile) * a.kg + g) * tsz;
+      for (int o = tid; o < tsz; o += kRouteThreads) store_agent(mine + o, lg[o]);
+      __shared__ int s_last;
+      if (!last_workgroup(a.tile_tickets + tile, unsigned(a.kg), &s_last)) return;
+      for (int o = tid; o < tsz; o += kRouteThreads) {
+        float v = 0.f;
+        for (int q = 0; q < a.kg; ++q)
+          v += q == g ? lg[o] : load_agent(a.kpart + (int64_t(tile) * a.kg + q) * tsz + o);
+        lg[o] = v;
+      }
+      __syncthreads();
+    }
   } else {
     // fp32 product on the vector ALUs: thread (token, expert group), fma over k in order.
     const int tl = tid >> 5, jg = tid & 31;
@@ -604,11 +644,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   if (a.k <= 32) {
     route_rows_half<NT>(lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
     __syncthreads();
-    route_tail<true>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints);
+    route_tail<true>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints,
+                     tile, ntiles);
   } else {
     route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
     __syncthreads();
-    route_tail<false>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints);
+    route_tail<false>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints,
+                      tile, ntiles);
   }
 }
 
@@ -699,7 +741,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
   route_rows(lg, a.npad, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
   __syncthreads();
-  route_tail<false>(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch, a.lds_region_ints);
+  route_tail<false>(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch, a.lds_region_ints, int(blockIdx.x),
+                    int(gridDim.x));
 }
 
 // ------------------------------------------------------------------ launchers
@@ -713,20 +756,13 @@ hipError_t launch_router_prepare(const RoutePlan& plan, int d, int n, const floa
 
 int route_chunk_tokens(const RoutePlan& plan) { return plan.fused ? kRouteBM : kRowsBM; }
 
-// Reading fp32 W_r (4 bytes per weight per workgroup) and splitting it in
-// registers measured faster than loading prepared planes (6 bytes per weight)
-// both at d x n = 768 x 128 and at 2048 x 256, and it needs no preparation
-// kernel.
-bool route_direct(const RoutePlan& plan, int d, int n) {
-  return plan.fused && plan.mfma && d % 32 == 0 && (n == 32 || n == 64 || n == 128 || n == 256);
-}
 
-// Without prepared planes the fused kernel splits W_r in registers when
-// route_direct allows it (else the planes are prepared first).
+// The fused kernel splits W_r in registers whenever route_direct allows it
+// (prepared planes are then not needed); otherwise it reads the planes.
 template <int NT>
 static void launch_fused(const RoutePlan& plan, const RouteArgs& a, dim3 g, size_t lds, hipStream_t s) {
   const bool x_lds = stage_x(plan, a.n);
-  if (a.planes_ready || !route_direct(plan, a.d, a.n)) {
+  if (!route_direct(plan, a.d, a.n)) {
     if (x_lds)
       hipLaunchKernelGGL((k_route_fused<NT, true, true, false>), g, dim3(kRouteThreads), lds, s, a);
     else
@@ -746,8 +782,9 @@ hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_
     const hipError_t err = launch_router_prepare(plan, a.d, a.n, a.w_r, const_cast<uint16_t*>(a.planes), s);
     if (err != hipSuccess) return err;
   }
+  a.kg = plan.kg;
   if (plan.fused) {
-    const dim3 g(unsigned(ceil_div64(a.m, kRouteBM)));
+    const dim3 g(unsigned(ceil_div64(a.m, kRouteBM) * plan.kg));
     const size_t lds = (size_t(a.lds_region_ints) + plan.npad) * sizeof(float);
     const int nt = plan.npad / 32;
     if (!plan.mfma)
