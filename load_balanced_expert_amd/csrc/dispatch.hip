@@ -88,10 +88,13 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int*
   double auxp = 0.0;
   const int pt = t - 64;   // waves 1-2 load the prefix data while wave 0 ranks
   for (int e = pt; pt >= 0 && pt < 128 && e < n; e += 128) {
+    // every load of the pass is issued before the first use (no serial round trips)
     int v[kMaxSuperChunks], w[kMaxSuperChunks];
+    unsigned long long pq[kMaxSuperChunks];
 #pragma unroll
     for (int q = 0; q < kMaxSuperChunks; ++q) {
       v[q] = q < nsup ? a.sup_counts[q * n + e] : 0;
+      pq[q] = stats && q < nsup ? a.sup_psum[q * n + e] : 0ull;
       const int cc = sc * a.sup + q;   // earlier chunks of this super chunk (up to 16 per pass)
       w[q] = cc < c ? crow[int64_t(cc) * n + e] : 0;
     }
@@ -102,12 +105,18 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int*
       base += q < sc ? v[q] : 0;
       base += w[q];
     }
-    for (int cc = sc * a.sup + kMaxSuperChunks; cc < c; ++cc) base += crow[int64_t(cc) * n + e];
+    for (int cc0 = sc * a.sup + kMaxSuperChunks; cc0 < c; cc0 += kMaxSuperChunks) {
+#pragma unroll
+      for (int q = 0; q < kMaxSuperChunks; ++q) w[q] = cc0 + q < c ? crow[int64_t(cc0 + q) * n + e] : 0;
+#pragma unroll
+      for (int q = 0; q < kMaxSuperChunks; ++q) base += w[q];
+    }
     lbase[e] = base;
     ltot[e] = min(tot, a.capacity);
     if (stats) {
       unsigned long long ps = 0;
-      for (int q = 0; q < nsup; ++q) ps += a.sup_psum[q * n + e];
+#pragma unroll
+      for (int q = 0; q < kMaxSuperChunks; ++q) ps += pq[q];   // integer sum: order-free
       const double psum = double(ps) / double(kPsumScale);
       const int64_t m = a.pairs / a.k;
       if (a.counts) a.counts[e] = tot;

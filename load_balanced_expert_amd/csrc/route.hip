@@ -226,80 +226,129 @@ __device__ __forceinline__ void split3(const float* v, bf16x8& hi, bf16x8& mid, 
   lo = __builtin_bit_cast(bf16x8, wl);
 }
 
+// Exact three-way split of 8 fp32 weights (raw bits) into bf16 fragments, as above.
+__device__ __forceinline__ void split8(const uint32_t* u, bf16x8 (&f)[3]) {
+  u32x4 wh, wm, wl;
+  constexpr uint32_t kHigh = 0x07060302u;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t u0 = u[2 * p], u1 = u[2 * p + 1];
+    const float r0 = __uint_as_float(u0) - __uint_as_float(u0 & 0xFFFF0000u);
+    const float r1 = __uint_as_float(u1) - __uint_as_float(u1 & 0xFFFF0000u);
+    const uint32_t s0 = __float_as_uint(r0), s1 = __float_as_uint(r1);
+    const float q0 = r0 - __uint_as_float(s0 & 0xFFFF0000u);
+    const float q1 = r1 - __uint_as_float(s1 & 0xFFFF0000u);
+    wh[p] = __builtin_amdgcn_perm(u1, u0, kHigh);
+    wm[p] = __builtin_amdgcn_perm(s1, s0, kHigh);
+    wl[p] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), kHigh);
+  }
+  f[0] = __builtin_bit_cast(bf16x8, wh);
+  f[1] = __builtin_bit_cast(bf16x8, wm);
+  f[2] = __builtin_bit_cast(bf16x8, wl);
+}
+
 // The same block product taking W_r [d, n] fp32 straight from global memory:
 // lane (r, h) loads the 16 weights of expert 32 tile + r it needs per K block
 // (each load instruction reads two 128-byte rows of W_r) and splits them in
-// registers, so no prepared planes are needed.  Three weight buffers rotate,
-// two K blocks ahead of the multiply; the first two are requested before the
-// x tile is staged (init), so both latencies overlap.  Used when d % 32 == 0
-// and n == 32 NT: the row stride is then a compile-time constant and every
-// address is in range.
+// registers, so no prepared planes are needed.  Used when d % 32 == 0 and
+// n == 32 NT (compile-time row stride).
+//
+// Software pipeline in half blocks (8 weights per lane, three MFMAs): while
+// the matrix core runs the three products of one half, the vector ALUs split
+// the next half, so the split and the products overlap inside every wave.
+// Raw weights are loaded two K blocks ahead through a buffer resource: a load
+// for a block past the wave's range is given an offset past the end of W_r,
+// which returns zero without reading memory, so the load sequence has no
+// branches and every wait counts exactly the loads it needs.
 template <int NT>
 struct DirectGemm {
-  static constexpr int kStride = 32 * NT;   // n
-  const float* wcol;
-  int kb0, cnt, rot, h;
-  float r0[16], r1[16], r2[16];
+  static constexpr int kRow = 4 * 32 * NT;          // bytes per W_r row
+  static constexpr uint32_t kOut = 0x7FFF0000u;      // beyond num_records
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t vbase;                                    // lane's byte offset inside a K block
+  int kb0, cnt, rot;
+  uint32_t ra[16], rb[16];
+  bf16x8 g0[3], g1[3];
 
   // K blocks [kbA, kbB) of the workgroup, split over its KS wave groups
-  __device__ __forceinline__ void init(const float* w, int kbA, int kbB, int wave, int lane, int rot_) {
+  __device__ __forceinline__ void init(const float* w, int d, int kbA, int kbB, int wave, int lane, int rot_) {
     constexpr int KS = 16 / NT;
     const int tile = wave % NT, ks = wave / NT;
     const int nkb = kbB - kbA;
     kb0 = kbA + ks * nkb / KS;
     cnt = kbA + (ks + 1) * nkb / KS - kb0;
     rot = cnt > 0 ? rot_ % cnt : 0;
-    h = lane >> 5;
-    wcol = w + tile * 32 + (lane & 31);
-    if (cnt > 0) {
-      load(r0, 0);
-      load(r1, 1);
-    }
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w), 0, d * kRow, 0x00020000);
+    vbase = uint32_t((tile * 32 + (lane & 31)) * 4 + 16 * (lane >> 5) * kRow);
+    load(ra, 0);
+    load(rb, 1);
   }
-  __device__ __forceinline__ int kb(int i) const {
-    i = min(i, cnt - 1);
+  __device__ __forceinline__ int kb(int i) const {   // i < cnt
     const int r = i + rot;
     return kb0 + (r >= cnt ? r - cnt : r);
   }
-  __device__ __forceinline__ void load(float (&bb)[16], int i) {
-    const float* p = wcol + (kb(i) * 32 + 16 * h) * kStride;
+  __device__ __forceinline__ void load(uint32_t (&b)[16], int i) {
+    const uint32_t o = i < cnt ? vbase + uint32_t(kb(i)) * uint32_t(32 * kRow) : kOut;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) bb[q] = p[q * kStride];
+    for (int q = 0; q < 16; ++q) b[q] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, int(o + q * kRow), 0, 0);
   }
-  __device__ __forceinline__ void step(f32x16& acc, const uint16_t* arow, const float (&bb)[16], int i) {
-    const int k = kb(i) * 32;
-    const bf16x8 a0 = load8(arow + k), a1 = load8(arow + k + 8);
-    bf16x8 f[3][2];
-    split3(bb, f[0][0], f[1][0], f[2][0]);
-    split3(bb + 8, f[0][1], f[1][1], f[2][1]);
+  // first half of block 0, split while the x tile is still being staged
+  __device__ __forceinline__ void prime() {
+    if (cnt > 0) split8(ra, g0);
+  }
+  // three products of one half (fragments g, A operand a) with the split of
+  // the next half (raw u -> gn) interleaved: MFMA, then a share of the split
+  __device__ __forceinline__ static void half(f32x16& acc, const bf16x8& a, const bf16x8 (&g)[3],
+                                              const uint32_t* u, bf16x8 (&gn)[3]) {
+    split8(u, gn);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, g[p], acc, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // the next half's A operand read first
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, f[p][0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, f[p][1], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 15, 0);   // then vector ALU work
     }
   }
   __device__ __forceinline__ f32x16 run(const uint16_t* arow) {
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    for (int i = 0; i < cnt; i += 3) {
-      load(r2, i + 2);
+    if (cnt == 0) return acc;
+    int i = 0;
+    bf16x8 a0 = load8(arow + kb(0) * 32), a1;
+    // blocks i (raw in ra) and i + 1 (rb) per pass; block i + 2 exists, so its
+    // first half is split in the pass and its load is always in range
+    for (; i + 2 < cnt; i += 2) {
+      a1 = load8(arow + kb(i) * 32 + 8);
+      half(acc, a0, g0, ra + 8, g1);
+      load(ra, i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      step(acc, arow, r0, i);
+      a0 = load8(arow + kb(i + 1) * 32);
+      half(acc, a1, g1, rb, g0);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < cnt) {
-        load(r0, i + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        step(acc, arow, r1, i + 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (i + 2 < cnt) {
-        load(r1, i + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        step(acc, arow, r2, i + 2);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      a1 = load8(arow + kb(i + 1) * 32 + 8);
+      half(acc, a0, g0, rb + 8, g1);
+      load(rb, i + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      a0 = load8(arow + kb(i + 2) * 32);
+      half(acc, a1, g1, ra, g0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // one or two blocks left: i (ra) and possibly i + 1 (rb)
+    a1 = load8(arow + kb(i) * 32 + 8);
+    half(acc, a0, g0, ra + 8, g1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < cnt) {
+      a0 = load8(arow + kb(i + 1) * 32);
+      half(acc, a1, g1, rb, g0);
+      __builtin_amdgcn_sched_barrier(0);
+      a1 = load8(arow + kb(i + 1) * 32 + 8);
+      half(acc, a0, g0, rb + 8, g1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, g1[p], acc, 0, 0, 0);
     return acc;
   }
 };
@@ -313,7 +362,8 @@ struct EpiArgs {
   const float* bias;
 };
 
-__device__ __forceinline__ float sigm(float h) { return 1.0f / (1.0f + expf(-h)); }
+// Logistic score; the reciprocal is the hardware one (within 1 ulp; 1 + e^-h >= 1).
+__device__ __forceinline__ float sigm(float h) { return __builtin_amdgcn_rcpf(1.0f + expf(-h)); }
 
 // Score of expert j for a token with softmax statistics (mx, sum).
 __device__ __forceinline__ float score_of(int score, float h, float mx, float sum) {
@@ -378,27 +428,65 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
   }
 }
 
-// Half-wave (32 lanes) reductions; every lane of the half gets the result.
+// Half-wave (32 lanes) all-reductions without the LDS crossbar: partners at
+// lane xor 1 and xor 2 (quad permutes), the mirrored quad and the mirrored
+// half-row (row_half_mirror, row_mirror DPP), then the other 16-lane row of
+// the half (gfx950 v_permlane16_swap).  Each step combines a lane with a
+// partner that already holds the same partial, so every lane of the half ends
+// with the same bits.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppMirror = 0x140, kDppHalfMirror = 0x141;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// (value of the even row, value of the odd row) of this lane's 32-lane half
+__device__ __forceinline__ void row_pair(uint32_t v, uint32_t& even, uint32_t& odd) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  even = r[0];
+  odd = r[1];
+}
 __device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 32));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  uint32_t a, b;
+  row_pair(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 __device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 32);
-  return v;
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  uint32_t a, b;
+  row_pair(__float_as_uint(v), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+template <int CTRL>
+__device__ __forceinline__ void argbest_step(float& key, int& ix) {
+  const float ok = dpp_f<CTRL>(key);
+  const int oi = dpp_i<CTRL>(ix);
+  if (better(ok, oi, key, ix)) {
+    key = ok;
+    ix = oi;
+  }
 }
 __device__ __forceinline__ void half_argbest(float& key, int& ix) {
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) {
-    const float ok = __shfl_xor(key, off, 32);
-    const int oi = __shfl_xor(ix, off, 32);
-    if (better(ok, oi, key, ix)) {
-      key = ok;
-      ix = oi;
-    }
-  }
+  argbest_step<kDppXor1>(key, ix);
+  argbest_step<kDppXor2>(key, ix);
+  argbest_step<kDppHalfMirror>(key, ix);
+  argbest_step<kDppMirror>(key, ix);
+  uint32_t ka, kb, ia, ib;
+  row_pair(__float_as_uint(key), ka, kb);
+  row_pair(uint32_t(ix), ia, ib);
+  const bool second = better(__uint_as_float(kb), int(ib), __uint_as_float(ka), int(ia));
+  key = __uint_as_float(second ? kb : ka);
+  ix = int(second ? ib : ia);
 }
 
 // Fused-route epilogue for k <= 32: one half-wave per token, NV = npad/32
@@ -432,9 +520,9 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
         sc[u] = l + 32 * u < e.n ? expf(h[u] - mx) : 0.f;
         sum += sc[u];
       }
-      sum = half_sum(sum);
+      const float inv = 1.0f / half_sum(sum);
 #pragma unroll
-      for (int u = 0; u < NV; ++u) sc[u] = sc[u] / sum;
+      for (int u = 0; u < NV; ++u) sc[u] *= inv;
     } else {
 #pragma unroll
       for (int u = 0; u < NV; ++u) sc[u] = l + 32 * u < e.n ? sigm(h[u]) : 0.f;
@@ -498,9 +586,14 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
     float acc = 0.f;
     if (a.want_psum) {
-      for (int tl = 0; tl < rows; ++tl) {
-        const float v = lg[int64_t(tl) * ld + j];
-        acc += SCORES ? v : score_of(e.score, v, tok_mx[tl], tok_sum[tl]);
+      // token order; eight reads in flight
+      for (int tl0 = 0; tl0 < rows; tl0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = tl0 + u < rows ? lg[int64_t(tl0 + u) * ld + j] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (tl0 + u < rows) acc += SCORES ? v[u] : score_of(e.score, v[u], tok_mx[tl0 + u], tok_sum[tl0 + u]);
       }
     }
     if (a.finish) {
@@ -551,7 +644,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   const int ldl = a.npad;
   float* lg = smem;
   int* hist = reinterpret_cast<int*>(smem) + a.lds_region_ints;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and every K-block index derived from it) in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // a token tile may be split over a.kg workgroups by K range (direct path only)
   const int tile = int(blockIdx.x) / a.kg, g = int(blockIdx.x) % a.kg, ntiles = int(gridDim.x) / a.kg;
   const int nkb = a.dpad / 32, kbA = g * nkb / a.kg, kbB = (g + 1) * nkb / a.kg;
@@ -564,14 +658,15 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     const uint16_t* arow;
     DirectGemm<NT> dg;
-    if constexpr (DIRECT) dg.init(a.w_r, kbA, kbB, wave, lane, tile);
+    if constexpr (DIRECT) dg.init(a.w_r, a.d, kbA, kbB, wave, lane, tile);
     if constexpr (XLDS) {
       // stage the 32 x rows in LDS with coalesced 16-byte loads (zero padding past the end)
       uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
       // only this workgroup's K range [32 kbA, 32 kbB) of the tile is staged
       const int ldx = a.dpad + 8, cpr = (kbB - kbA) * 4, kx = kbA * 32;
-      // four loads in flight per thread before the LDS stores (one pass for d <= 1024)
-      for (int c0 = tid; c0 < kRouteBM * cpr; c0 += 4 * kRouteThreads) {
+      // four loads in flight per thread before the LDS stores (one pass for d <= 1024);
+      // the first pass runs in every thread (its items are range-checked)
+      for (int c0 = tid; c0 == tid || c0 < kRouteBM * cpr; c0 += 4 * kRouteThreads) {
         u32x4 v[4];
         int dst[4];
 #pragma unroll
@@ -582,6 +677,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
           dst[u] = c < kRouteBM * cpr ? r * ldx + k : -1;
           if (c < kRouteBM * cpr && r < rows && k < a.d) v[u] = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
         }
+        if constexpr (DIRECT) {   // split the first weights while the x loads are in flight
+          if (c0 == tid) dg.prime();
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xs + dst[u]) = v[u];
@@ -590,6 +688,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
       arow = xs + (lane & 31) * ldx + 16 * (lane >> 5);
     } else {
       arow = x + (t0 + min(lane & 31, rows - 1)) * a.d + 16 * (lane >> 5);  // requires d == dpad
+      if constexpr (DIRECT) dg.prime();
     }
     const f32x16 acc = DIRECT ? dg.run(arow) : gemm_ksplit_bf16x3<NT>(arow, a.planes, a.dpad, wave, lane, int(blockIdx.x));
     const int col = (wave % NT) * 32 + (lane & 31), ks = wave / NT;
@@ -600,14 +699,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
       for (int i = 0; i < 16; ++i) buf[acc_row(i, lane) * ldl + col] = acc[i];
     }
     __syncthreads();
-    if (ks == 0) {  // partial tiles are added in K-range order
+    if (ks == 0) {  // partial tiles are added in K-range order (every read issued before the first write)
+      float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int o = acc_row(i, lane) * ldl + col;
-        float v = acc[i];
-        for (int q = 1; q < KS; ++q) v += lg[(q - 1) * kRouteBM * ldl + o];
-        lg[o] = v;
-      }
+      for (int i = 0; i < 16; ++i) v[i] = acc[i];
+#pragma unroll
+      for (int q = 1; q < KS; ++q)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] += lg[(q - 1) * kRouteBM * ldl + acc_row(i, lane) * ldl + col];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lg[acc_row(i, lane) * ldl + col] = v[i];
     }
     __syncthreads();
     if (a.kg > 1) {
