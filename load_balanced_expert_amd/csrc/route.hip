@@ -31,23 +31,26 @@ constexpr int kRouteBM = 32;      // tokens per route workgroup (n <= 256)
 constexpr int kRowsBM = 256;      // tokens per route-epilogue workgroup (n > 256)
 constexpr int kRouteThreads = 1024;  // 16 waves
 
-// LDS ints of the region each route kernel reserves: fused, the x tile (if
-// staged), the K-split partial tiles (also the logits tile) and the last
-// block's scratch, which share one region; rows kernel, the scratch.
-constexpr int kFusedLdsBudgetInts = 15360;   // 60 KiB for the region (+ histogram, statics < 64 KiB)
-static int fused_partial_ints(const RoutePlan& plan, int n) {
+// LDS ints of the region each route kernel reserves.  Fused: the x tile (if
+// staged, at most 60 KiB) and, once the product is done, the partial logit
+// tiles [KS][32][npad + 8] (one per K group; the first becomes the logits
+// tile), which share one region; the last workgroup's finishing scratch
+// reuses it.  Rows kernel: the scratch.  The padding of 8 columns puts the
+// two lane halves of an accumulator store on different banks.
+constexpr int kXStageMaxInts = 15360;
+static int fused_parts(const RoutePlan& plan) {
   const int nt = plan.npad / 32;
-  const int ks = 16 / (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
-  return std::max(std::max(ks - 1, 1) * kRouteBM * plan.npad, n + 2 * kMaxSuperChunks * 16);
+  return plan.mfma ? 16 / (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8) : 1;
+}
+static int fused_partial_ints(const RoutePlan& plan, int n) {
+  return std::max(fused_parts(plan) * kRouteBM * (plan.npad + 8), n + 2 * kMaxSuperChunks * 16);
 }
 static int x_tile_ints(const RoutePlan& plan) { return kRouteBM * (plan.dpad + 8) / 2; }
-static bool stage_x(const RoutePlan& plan, int n) {
-  return std::max(x_tile_ints(plan), fused_partial_ints(plan, n)) + plan.npad <= kFusedLdsBudgetInts + 256;
-}
+static bool stage_x(const RoutePlan& plan, int) { return x_tile_ints(plan) + plan.npad <= kXStageMaxInts + 256; }
 static int route_region_ints(const RoutePlan& plan, int n) {
   if (!plan.fused) return n + 4096;
   const int part = fused_partial_ints(plan, n);
-  return stage_x(plan, n) ? std::max(part, x_tile_ints(plan)) : part;
+  return plan.mfma && stage_x(plan, n) ? std::max(part, x_tile_ints(plan)) : part;
 }
 
 // Reading fp32 W_r (4 bytes per weight per workgroup) and splitting it in
@@ -63,7 +66,9 @@ RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
   p.fused = n <= kFusedMaxN;
   // matrix cores need d % 8 == 0 (16-byte rows); without the LDS x tile also d % 32 == 0
   p.mfma = x_bf16 && (d % 8 == 0);
-  p.npad = p.fused ? round_up(n, 32) : round_up(n, 128);
+  // fused: 32, 64, 128 or 256 columns, one 32-expert tile per wave column and
+  // npad / 32 experts per lane in the epilogue; big n: 128-column GEMM tiles
+  p.npad = p.fused ? (n <= 32 ? 32 : n <= 64 ? 64 : n <= 128 ? 128 : 256) : round_up(n, 128);
   p.dpad = round_up(d, 32);
   if (p.fused && p.mfma && p.dpad != d && !stage_x(p, n)) p.mfma = false;   // global x rows need d % 32 == 0
   p.planes_bytes = p.mfma ? size_t(3) * p.npad * p.dpad * sizeof(uint16_t) : 0;
@@ -77,7 +82,7 @@ RoutePlan route_plan(int64_t m, int d, int n, bool x_bf16) {
     p.kg = tiles <= 64 ? 4 : 2;
     while (p.kg > 1 && p.dpad / 32 < p.kg * ks) p.kg /= 2;
   }
-  p.kpart_bytes = p.kg > 1 ? size_t(tiles) * p.kg * kRouteBM * p.npad * sizeof(float) : 0;
+  p.kpart_bytes = p.kg > 1 ? size_t(tiles) * p.kg * kRouteBM * (p.npad + 8) * sizeof(float) : 0;
   return p;
 }
 
@@ -493,13 +498,17 @@ __device__ __forceinline__ void half_argbest(float& key, int& ix) {
 // logits per lane in registers (expert j = lane + 32u).  Computes the scores
 // (softmax or sigmoid), the top-k by key (logit, or score + bias), the gates
 // and the histogram, then overwrites the token's LDS row with its scores so
-// that the per-expert score sums are plain column sums.
+// that the per-expert score sums are plain column sums.  Top-1 softmax
+// without bias (the Switch router) takes a shorter path: one arg-max
+// reduction gives both the softmax maximum and the pick, whose score is
+// exp(0) / sum = 1 / sum.
 template <int NV>
 __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int64_t t0, const EpiArgs& e,
                                                 int32_t* __restrict__ idx, float* __restrict__ gate_out,
                                                 int* hist) {
   const int half = threadIdx.x >> 5, l = threadIdx.x & 31;
   const int nhalf = kRouteThreads / 32;
+  const bool fast = e.k == 1 && e.score == 0 && !e.bias;
   for (int tl = half; tl < rows; tl += nhalf) {
     float* row = lg + tl * ld;
     float h[NV], sc[NV], bv[NV];
@@ -507,8 +516,35 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
     for (int u = 0; u < NV; ++u) {
       const int j = l + 32 * u;
       h[u] = j < e.n ? row[j] : -INFINITY;
-      bv[u] = (e.bias && j < e.n) ? e.bias[j] : 0.f;
     }
+    if (fast) {
+      float bk = -INFINITY;
+      int bj = 0x7FFFFFFF;
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (l + 32 * u < e.n && better(h[u], l + 32 * u, bk, bj)) {
+          bk = h[u];
+          bj = l + 32 * u;
+        }
+      half_argbest(bk, bj);   // bk: the softmax maximum; bj: its lowest expert
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        sc[u] = l + 32 * u < e.n ? expf(h[u] - bk) : 0.f;
+        sum += sc[u];
+      }
+      const float inv = 1.0f / half_sum(sum);
+      if (l == 0) {
+        atomicAdd(&hist[bj], 1);
+        idx[t0 + tl] = bj;
+        gate_out[t0 + tl] = e.gate == 1 ? 1.0f : inv;
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) row[l + 32 * u] = sc[u] * inv;
+      continue;
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) bv[u] = (e.bias && l + 32 * u < e.n) ? e.bias[l + 32 * u] : 0.f;
     if (e.score == 0) {
       float mx = -INFINITY;
 #pragma unroll
@@ -628,6 +664,15 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
   finalize_chunks(f, scratch, scratch_ints, kRouteThreads);
 }
 
+// The epilogue above with NV = npad / 32 chosen at run time (vector-ALU product path).
+__device__ __forceinline__ void route_rows_half_nv(int nv, float* lg, int ld, int rows, int64_t t0, const EpiArgs& e,
+                                                   int32_t* idx, float* gate_out, int* hist) {
+  if (nv == 1) route_rows_half<1>(lg, ld, rows, t0, e, idx, gate_out, hist);
+  else if (nv == 2) route_rows_half<2>(lg, ld, rows, t0, e, idx, gate_out, hist);
+  else if (nv == 4) route_rows_half<4>(lg, ld, rows, t0, e, idx, gate_out, hist);
+  else route_rows_half<8>(lg, ld, rows, t0, e, idx, gate_out, hist);
+}
+
 __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
   return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i]) : static_cast<const float*>(x)[i];
 }
@@ -641,7 +686,7 @@ template <int NT, bool MFMA, bool XLDS, bool DIRECT>
 __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   extern __shared__ float smem[];
   __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];   // softmax statistics (k > 32 epilogue)
-  const int ldl = a.npad;
+  const int ldl = a.npad + 8;   // logit and partial tile row stride
   float* lg = smem;
   int* hist = reinterpret_cast<int*>(smem) + a.lds_region_ints;
   // the wave index is uniform: keep it (and every K-block index derived from it) in scalar registers
@@ -693,22 +738,24 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     const f32x16 acc = DIRECT ? dg.run(arow) : gemm_ksplit_bf16x3<NT>(arow, a.planes, a.dpad, wave, lane, int(blockIdx.x));
     const int col = (wave % NT) * 32 + (lane & 31), ks = wave / NT;
     if constexpr (XLDS) __syncthreads();   // the x tile is dead before partials overwrite it
-    if (ks > 0) {
-      float* buf = lg + (ks - 1) * kRouteBM * ldl;
+    {
+      float* buf = lg + ks * kRouteBM * ldl;
 #pragma unroll
       for (int i = 0; i < 16; ++i) buf[acc_row(i, lane) * ldl + col] = acc[i];
     }
     __syncthreads();
-    if (ks == 0) {  // partial tiles are added in K-range order (every read issued before the first write)
-      float v[16];
+    // the KS partial tiles added in K-range order, every thread owning npad / 32 elements
+    // (the sum lands in the first tile, element by element)
+    constexpr int NPAD = 32 * NT;   // = npad on the matrix-core path
+    for (int o = tid; o < kRouteBM * NPAD; o += kRouteThreads) {
+      const int li = (o / NPAD) * ldl + o % NPAD;
+      float p[KS];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = acc[i];
+      for (int q = 0; q < KS; ++q) p[q] = lg[q * kRouteBM * ldl + li];
+      float v = p[0];
 #pragma unroll
-      for (int q = 1; q < KS; ++q)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] += lg[(q - 1) * kRouteBM * ldl + acc_row(i, lane) * ldl + col];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) lg[acc_row(i, lane) * ldl + col] = v[i];
+      for (int q = 1; q < KS; ++q) v += p[q];
+      lg[li] = v;
     }
     __syncthreads();
     if (a.kg > 1) {
@@ -743,7 +790,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   }
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
   if (a.k <= 32) {
-    route_rows_half<NT>(lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
+    if constexpr (MFMA) route_rows_half<NT>(lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
+    else route_rows_half_nv(a.npad / 32, lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
     __syncthreads();
     route_tail<true>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints,
                      tile, ntiles);

@@ -98,6 +98,28 @@ def test_many_picks(k, score, bias):
     check_route(inp.x, inp.w_r, k, f"top-{k} of 64 ({score})", score=score, gate="renorm", bias=b)
 
 
+@pytest.mark.parametrize("n,k", [(96, 1), (96, 3), (200, 2), (160, 1)])
+def test_expert_counts_between_tile_sizes(n, k):
+    # n not in {32, 64, 128, 256}: padded to the next of them (prepared planes, masked columns)
+    spec = W.SwitchSpec(f"n{n}", T=300, d=128, N=n, w_r_std=0.05)
+    inp = W.switch_inputs(spec, 13)
+    check_route(inp.x, inp.w_r, k, f"N={n} top-{k}")
+
+
+def test_fp32_x_fused_many_experts():
+    # vector-ALU product with more experts than one lane group: four experts per lane in the epilogue
+    spec = W.SwitchSpec("f32n100", T=150, d=40, N=100, x_dtype="f32", w_r_std=0.05)
+    inp = W.switch_inputs(spec, 14)
+    check_route(inp.x, inp.w_r, 3, "fp32 x, N=100 top-3 (vector-ALU product)")
+
+
+def test_top1_renorm_gate_is_one():
+    spec = W.SwitchSpec("renorm1", T=200, d=64, N=64, w_r_std=0.1)
+    inp = W.switch_inputs(spec, 15)
+    _, g, *_ = check_route(inp.x, inp.w_r, 1, "top-1 renormalised gate", gate="renorm")
+    assert np.all(g == 1.0)
+
+
 def test_bf16_x_with_d_not_multiple_of_8():
     spec = W.SwitchSpec("oddd", T=200, d=36, N=16, w_r_std=0.1)
     inp = W.switch_inputs(spec, 6)
