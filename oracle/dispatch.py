@@ -14,8 +14,13 @@ Follows
   and capacity slot.
 
 Readings: capacity = floor(T·cf / N) on the exact value of cf; slots are
-given in token-major order (token t before t+1, then choice r before r+1);
-the dispatched buffer is compact and expert-major with row offsets.
+given in token-major order (token t before t+1, then choice r before r+1).
+Two buffer layouts, both expert-major: compact (expert j's kept rows follow
+expert j-1's, offsets are prefix sums of the kept counts — the grouping the
+permute example on [Switch impl] draws), and capacity-padded (expert j owns
+rows [j·C, (j+1)·C) and fills the first kept_j of them — the per-expert
+capacity buffer of [Switch review] "Expert Capacity와 토큰 드롭").  Slots,
+kept / dropped pairs and the row order inside an expert are the same in both.
 Plain Python loops: fine at the sizes the oracle runs.
 """
 from __future__ import annotations
@@ -41,14 +46,26 @@ class Dispatch:
     row_to_token: np.ndarray    # [rows] int32 (token index of each dispatched row)
     row_to_pair: np.ndarray     # [rows] int64 (flat t*k + r of each row)
     counts: np.ndarray          # [n] selections
-    kept_counts: np.ndarray     # [n] min(counts, capacity)
+    kept_counts: np.ndarray     # [n] min(counts, capacity) = rows filled per expert
+    padded: bool = False        # capacity-padded layout (expert j owns rows [j·C, (j+1)·C))
 
     @property
     def rows(self) -> int:
+        """Rows of the dispatched buffer (padded: n·C, some of them unfilled)."""
         return int(self.expert_offsets[-1])
 
+    @property
+    def expert_rows(self) -> np.ndarray:
+        """[n] int32: filled rows of each expert, from its offset on."""
+        return self.kept_counts.astype(np.int32)
 
-def dispatch_maps(idx: np.ndarray, n: int, cap: int) -> Dispatch:
+    def filled_rows(self) -> np.ndarray:
+        """Indices of the dispatched rows that hold a token."""
+        return np.nonzero(self.row_to_token >= 0)[0]
+
+
+def dispatch_maps(idx: np.ndarray, n: int, cap: int, padded: bool = False) -> Dispatch:
+    """Slots in token order and the permute maps; padded needs cap >= 0."""
     idx = np.asarray(idx)
     T, k = idx.shape
     slot = np.zeros((T, k), dtype=np.int64)
@@ -62,7 +79,11 @@ def dispatch_maps(idx: np.ndarray, n: int, cap: int) -> Dispatch:
     kept = slot < cap
     kept_counts = np.minimum(counts, cap)
     offsets = np.zeros(n + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(kept_counts)
+    if padded:
+        assert cap >= 0, "the padded layout needs a capacity"
+        offsets[:] = np.arange(n + 1) * cap
+    else:
+        offsets[1:] = np.cumsum(kept_counts)
     token_to_row = np.full((T, k), -1, dtype=np.int64)
     rows = int(offsets[-1])
     row_to_token = np.full(rows, -1, dtype=np.int64)
@@ -76,9 +97,14 @@ def dispatch_maps(idx: np.ndarray, n: int, cap: int) -> Dispatch:
                 row_to_pair[row] = t * k + r
     return Dispatch(slot, kept, token_to_row.astype(np.int32), (~kept).astype(np.uint8),
                     offsets.astype(np.int32), row_to_token.astype(np.int32), row_to_pair,
-                    counts, kept_counts)
+                    counts, kept_counts, padded)
 
 
 def dispatch_rows(x: np.ndarray, dm: Dispatch) -> np.ndarray:
-    """Dispatched buffer: row r holds the (bit-identical) hidden state of its token."""
-    return np.asarray(x)[dm.row_to_token]
+    """Dispatched buffer: row r holds the (bit-identical) hidden state of its
+    token; unfilled rows of the padded layout are zero."""
+    x = np.asarray(x)
+    out = np.zeros((dm.rows,) + x.shape[1:], dtype=x.dtype)
+    filled = dm.filled_rows()
+    out[filled] = x[dm.row_to_token[filled]]
+    return out

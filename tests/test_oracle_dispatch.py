@@ -103,6 +103,47 @@ def test_all_tokens_to_one_expert_drops_T_minus_C():
     assert dm.expert_offsets.tolist() == [0, cap, cap, cap, cap]
 
 
+def test_padded_permute_worked_example():
+    # the permute example, each expert's group placed at the start of its capacity region
+    g = _read_golden("permute_example.txt")
+    experts = np.array([int(v) - 1 for v in g["experts"][0]], np.int32)[:, None]
+    cap = 6
+    dm = D.dispatch_maps(experts, 4, cap, padded=True)
+    compact = [int(v) for v in g["dispatched_tokens"][0]]
+    off = [int(v) for v in g["expert_offsets"][0]]
+    assert dm.expert_offsets.tolist() == [e * cap for e in range(5)]
+    for e in range(4):
+        group = compact[off[e]:off[e + 1]]
+        region = (dm.row_to_token[e * cap:(e + 1) * cap] + 1).tolist()
+        assert region == group + [0] * (cap - len(group))
+        assert dm.expert_rows[e] == len(group)
+
+
+@pytest.mark.parametrize("k,skew,cf", [(1, 0.0, 1.0), (1, 1.2, 1.25), (2, 0.5, 1.0), (4, 2.0, 0.5), (2, 1.0, 0.0)])
+def test_padded_layout_matches_compact(k, skew, cf):
+    T, n = 400, 16
+    idx = W.random_assignment(T, n, k, seed=11, skew=skew)
+    cap = D.capacity(T * k, n, cf)
+    c = D.dispatch_maps(idx, n, cap)
+    p = D.dispatch_maps(idx, n, cap, padded=True)
+    for a in ("slot", "kept", "drop_mask", "counts", "kept_counts"):
+        assert np.array_equal(getattr(c, a), getattr(p, a)), a
+    assert p.rows == n * cap and len(p.filled_rows()) == c.rows
+    kept = p.token_to_row >= 0
+    assert np.array_equal(p.token_to_row[kept], (idx * cap + p.slot)[kept])
+    assert np.all(p.token_to_row[~kept] == -1)
+    for e in range(n):
+        lo, hi = c.expert_offsets[e], c.expert_offsets[e + 1]
+        assert np.array_equal(p.row_to_token[e * cap:e * cap + hi - lo], c.row_to_token[lo:hi])
+        assert np.all(p.row_to_token[e * cap + hi - lo:(e + 1) * cap] == -1)
+    # the dispatched buffers agree on every filled row
+    x = np.arange(T * 3, dtype=np.float32).reshape(T, 3)
+    bc, bp = D.dispatch_rows(x, c), D.dispatch_rows(x, p)
+    for e in range(n):
+        lo, hi = c.expert_offsets[e], c.expert_offsets[e + 1]
+        assert np.array_equal(bp[e * cap:e * cap + hi - lo], bc[lo:hi])
+
+
 # ---------------------------------------------------------------- expert FFN + combine
 def test_bf16_round_matches_torch_rne_on_fp32_values():
     g = np.random.default_rng(0)
