@@ -216,7 +216,7 @@ def main():
     W1 = dev_t(w1)
     W2 = dev_t(w2)
     del w1, w2
-    rows_bound = min(T * k, cap * N)
+    rows_bound = M.dispatch_rows(T, k, N, cap)   # capacity-padded buffer
     lo = M.allocate_layer_outputs(T, d, N, k, rows_bound, x.dtype, True, dev)
     torch.cuda.synchronize()
 
@@ -247,7 +247,7 @@ def main():
     ffn = np.array([he.ms(ev3[i], ev4[i]) for i in range(args.steps)])
     metric_ms = float(np.mean(region))
     value = T / (metric_ms * 1e-3)
-    rows = int(lo.expert_offsets[N].item())
+    rows = int(lo.expert_rows.sum().item())   # kept rows
 
     # Stage breakdown: a separate short run with all six stage events (each
     # span also carries one event's own cost, so these add up to more than
@@ -516,7 +516,7 @@ def bench_switch_c(args):
         for e0 in range(0, N, 256):   # in slices, to bound the fp32 temporary
             w[e0:e0 + 256] = (torch.randn(w[e0:e0 + 256].shape, generator=g, device="cuda:0") * spec.w_std).to(
                 torch.bfloat16)
-    rows_bound = min(T * k, cap * N)
+    rows_bound = M.dispatch_rows(T, k, N, cap)   # capacity-padded buffer
     lo = M.allocate_layer_outputs(T, d, N, k, rows_bound, x.dtype, True, "cuda:0")
     torch.cuda.synchronize()
     he = HipEvents()
@@ -538,7 +538,7 @@ def bench_switch_c(args):
     region = np.array([he.ms(ev4[i], ev3[i + 1]) for i in range(steps)])
     ffn = np.array([he.ms(ev3[i], ev4[i]) for i in range(steps)])
     metric_ms = float(np.mean(region))
-    rows = int(lo.expert_offsets[N].item())
+    rows = int(lo.expert_rows.sum().item())   # kept rows
     alg_metric_bytes = (T * d * 2 + N * d * 4 + T * k * 8) + (T * k * 4 * 3) + 2 * rows * d * 2 + \
         (rows * d * 2 + 2 * T * d * 2 + T * k * 8)
     flops = 3 * 2.0 * T * d * N

@@ -208,18 +208,26 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
  *   slot(t, r) = number of earlier pairs (t', r') < (t, r) in token-major order
  *   with the same expert; kept ⇔ slot < capacity ([Switch review] "Expert
  *   Capacity와 토큰 드롭": overflow tokens skip the expert and reach the next
- *   layer through the residual).  Kept pairs are gathered expert-major and
- *   contiguous ([Switch impl] "forward pass에서는 토큰 순서를 두 번 변경한다").
+ *   layer through the residual).  Kept pairs are gathered expert-major, in
+ *   token order inside each expert ([Switch impl] "forward pass에서는 토큰
+ *   순서를 두 번 변경한다").
+ * Buffer layout (rows of `dispatched`, `row_to_token`):
+ *   capacity >= 0: capacity-padded, the per-expert capacity buffer — expert j
+ *     owns rows [j·C, (j+1)·C) and fills the first expert_rows[j] of them;
+ *     n·C rows in all, unfilled rows untouched;
+ *   capacity = -1 (unlimited): compact — expert j's rows follow expert j-1's;
+ *     m·k rows at most.
  * capacity: -1 = unlimited, else >= 0.
  * x [m, d] (x_dtype) or NULL when dispatched is NULL; idx [m, k] int32 in;
  * token_to_row [m, k] int32 out (-1 = dropped); drop_mask [m, k] uint8 out or NULL;
- * expert_offsets [n + 1] int32 out: rows of expert j are
- *   [expert_offsets[j], expert_offsets[j+1]);
- * row_to_token [m·k] int32 out or NULL (entries >= expert_offsets[n] untouched);
- * dispatched [m·k, d] (x_dtype) out or NULL: row r = x[row_to_token[r]], bit copy. */
+ * expert_offsets [n + 1] int32 out: expert j's rows start at expert_offsets[j]
+ *   (padded: j·C; compact: the prefix sums, [n] = rows in use);
+ * expert_rows [n] int32 out or NULL: rows of expert j (= min(count_j, C));
+ * row_to_token [rows] int32 out or NULL (unfilled rows untouched);
+ * dispatched [rows, d] (x_dtype) out or NULL: row r = x[row_to_token[r]], bit copy. */
 moe_status moe_dispatch(const moe_shape* shape, int32_t capacity, const void* x, const int32_t* idx,
                         int32_t* token_to_row, uint8_t* drop_mask, int32_t* expert_offsets,
-                        int32_t* row_to_token, void* dispatched,
+                        int32_t* expert_rows, int32_t* row_to_token, void* dispatched,
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ expert FFN */
@@ -228,13 +236,17 @@ moe_status moe_dispatch(const moe_shape* shape, int32_t capacity, const void* x,
  * "Switch Layer의 구조": FFN(x) = max(0, x·W1)·W2, one weight set per expert;
  * no biases).  bf16 operands, fp32 accumulation, the hidden activation and
  * the output rounded to bf16 (nearest even).
- * rows_max: a host-known bound on any expert's row count (e.g. the capacity).
- * expert_offsets [n + 1] int32 (device, from moe_dispatch);
+ * rows_max: a host-known bound on any expert's row count (e.g. the capacity);
+ *   the buffers hold n·rows_max rows.
+ * expert_offsets [n + 1], expert_rows [n] or NULL, int32 (device, from
+ *   moe_dispatch): expert j's rows are [offsets[j], offsets[j] + rows[j]), or
+ *   [offsets[j], offsets[j+1]) when expert_rows is NULL (compact layout);
  * dispatched [rows, d] bf16; w1 [n, d_ff, d] bf16 (row f feeds hidden unit f);
- * w2 [n, d, d_ff] bf16 (row c feeds output channel c); y [rows, d] bf16 out.
+ * w2 [n, d, d_ff] bf16 (row c feeds output channel c); y [rows, d] bf16 out
+ *   (rows outside every expert's range untouched).
  * Limits: d and d_ff multiples of 32. */
 moe_status moe_expert_ffn(int32_t n, int32_t d, int32_t d_ff, int32_t rows_max,
-                          const int32_t* expert_offsets, const void* dispatched,
+                          const int32_t* expert_offsets, const int32_t* expert_rows, const void* dispatched,
                           const void* w1, const void* w2, void* y,
                           void* ws, size_t ws_bytes, void* stream);
 
@@ -279,9 +291,10 @@ typedef struct {
   int32_t* token_to_row;   /* [m, k] */
   uint8_t* drop_mask;      /* [m, k] */
   int32_t* expert_offsets; /* [n + 1] */
-  int32_t* row_to_token;   /* [m·k] */
-  void* dispatched;        /* [m·k, d] x_dtype */
-  void* y;                 /* [m·k, d] bf16 expert outputs (relu_ffn; ignored for
+  int32_t* expert_rows;    /* [n] */
+  int32_t* row_to_token;   /* [rows] (rows as for moe_dispatch: n·C, or m·k without capacity) */
+  void* dispatched;        /* [rows, d] x_dtype */
+  void* y;                 /* [rows, d] bf16 expert outputs (relu_ffn; ignored for
                               the identity expert, whose output is `dispatched`) */
   void* out;               /* [m, d] x_dtype */
 } moe_layer_outputs;

@@ -30,7 +30,7 @@ class LayerParams(ctypes.Structure):
 class LayerOutputs(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in (
         "idx", "gate", "counts", "prob_sum", "f", "P", "aux", "token_to_row", "drop_mask",
-        "expert_offsets", "row_to_token", "dispatched", "y", "out")]
+        "expert_offsets", "expert_rows", "row_to_token", "dispatched", "y", "out")]
 
 
 _P = c_void_p
@@ -49,8 +49,8 @@ SIGNATURES = {
     "moe_global_aux": (c_int32, [c_int32, _P, _P, _P, c_int32, c_float, _P, _P, _P, _P]),
     "moe_balance_duals": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_int32, c_int32, c_int32,
                                     _P, _P, _P, _P, _P, c_size_t, _P]),
-    "moe_dispatch": (c_int32, [POINTER(MoeShape), c_int32, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
-    "moe_expert_ffn": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_dispatch": (c_int32, [POINTER(MoeShape), c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_expert_ffn": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_combine": (c_int32, [POINTER(MoeShape), _P, c_int32, _P, _P, _P, _P, _P]),
     "moe_switch_layer": (c_int32, [POINTER(MoeShape), POINTER(LayerParams), _P, _P, _P, _P, _P,
                                    POINTER(LayerOutputs), _P, c_size_t, _P]),

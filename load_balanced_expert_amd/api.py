@@ -207,8 +207,14 @@ class DispatchOut:
     token_to_row: torch.Tensor
     drop_mask: torch.Tensor
     expert_offsets: torch.Tensor
+    expert_rows: torch.Tensor
     row_to_token: torch.Tensor
     dispatched: Optional[torch.Tensor]
+
+
+def dispatch_rows(m: int, k: int, n: int, capacity: int) -> int:
+    """Rows of the dispatched buffer: capacity-padded n * C, or m * k without a capacity."""
+    return m * k if capacity < 0 else capacity * n
 
 
 def dispatch(x: Optional[torch.Tensor], idx: torch.Tensor, n: int, capacity: int = -1, d: Optional[int] = None,
@@ -222,34 +228,38 @@ def dispatch(x: Optional[torch.Tensor], idx: torch.Tensor, n: int, capacity: int
     else:
         xd = L.MOE_BF16
     sh = shape(m, d or 1, n, k, x_dtype=xd)
-    rows_bound = m * k if capacity < 0 else min(m * k, capacity * n)
+    rows_bound = dispatch_rows(m, k, n, capacity)
     if out is not None:
-        t2r, drop, offs, r2t, disp = (out.token_to_row, out.drop_mask, out.expert_offsets, out.row_to_token,
-                                      out.dispatched)
+        t2r, drop, offs, rows, r2t, disp = (out.token_to_row, out.drop_mask, out.expert_offsets, out.expert_rows,
+                                            out.row_to_token, out.dispatched)
     else:
         t2r = torch.empty((m, k), dtype=torch.int32, device=dev)
         drop = torch.empty((m, k), dtype=torch.uint8, device=dev)
         offs = torch.empty(n + 1, dtype=torch.int32, device=dev)
-        r2t = torch.full((m * k,), -1, dtype=torch.int32, device=dev)
-        disp = (torch.empty((rows_bound, d), dtype=x.dtype, device=dev)
+        rows = torch.empty(n, dtype=torch.int32, device=dev)
+        r2t = torch.full((rows_bound,), -1, dtype=torch.int32, device=dev)
+        disp = (torch.zeros((rows_bound, d), dtype=x.dtype, device=dev)
                 if (x is not None and copy_rows) else None)
     ws, wsb = _ws_args(workspace_size(sh, capacity), dev)
     _check(_lib().moe_dispatch(ctypes.byref(sh), int(capacity), _ptr(x), _ptr(idx), _ptr(t2r), _ptr(drop),
-                               _ptr(offs), _ptr(r2t), _ptr(disp), ws, wsb, _stream(dev)), "moe_dispatch")
-    return DispatchOut(t2r, drop, offs, r2t, disp)
+                               _ptr(offs), _ptr(rows), _ptr(r2t), _ptr(disp), ws, wsb, _stream(dev)), "moe_dispatch")
+    return DispatchOut(t2r, drop, offs, rows, r2t, disp)
 
 
 # ------------------------------------------------------------------ expert FFN
 def expert_ffn(dispatched: torch.Tensor, expert_offsets: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
-               rows_max: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    _on_device(dispatched, expert_offsets, w1, w2)
+               rows_max: int, out: Optional[torch.Tensor] = None,
+               expert_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """expert_rows: rows per expert (capacity-padded layout); None: compact offsets."""
+    _on_device(dispatched, expert_offsets, w1, w2, expert_rows)
     n, d_ff, d = w1.shape
     dev = dispatched.device
     y = out if out is not None else torch.empty((dispatched.shape[0], d), dtype=torch.bfloat16, device=dev)
     need = int(_lib().moe_expert_ffn_workspace_size(int(n), int(rows_max), int(d_ff)))
     ws, wsb = _ws_args(need, dev)
-    _check(_lib().moe_expert_ffn(int(n), int(d), int(d_ff), int(rows_max), _ptr(expert_offsets), _ptr(dispatched),
-                                 _ptr(w1), _ptr(w2), _ptr(y), ws, wsb, _stream(dev)), "moe_expert_ffn")
+    _check(_lib().moe_expert_ffn(int(n), int(d), int(d_ff), int(rows_max), _ptr(expert_offsets), _ptr(expert_rows),
+                                 _ptr(dispatched), _ptr(w1), _ptr(w2), _ptr(y), ws, wsb, _stream(dev)),
+           "moe_expert_ffn")
     return y
 
 
@@ -282,6 +292,7 @@ class LayerOut:
     token_to_row: torch.Tensor
     drop_mask: torch.Tensor
     expert_offsets: torch.Tensor
+    expert_rows: torch.Tensor
     row_to_token: torch.Tensor
     dispatched: torch.Tensor
     y: Optional[torch.Tensor]
@@ -294,8 +305,8 @@ def allocate_layer_outputs(m, d, n, k, rows_bound, x_dtype, ffn: bool, device) -
         idx=e(m, k, dt=torch.int32), gate=e(m, k, dt=torch.float32), counts=e(n, dt=torch.int32),
         prob_sum=e(n, dt=torch.float32), f=e(n, dt=torch.float32), P=e(n, dt=torch.float32),
         aux=e(1, dt=torch.float32), token_to_row=e(m, k, dt=torch.int32), drop_mask=e(m, k, dt=torch.uint8),
-        expert_offsets=e(n + 1, dt=torch.int32),
-        row_to_token=torch.full((m * k,), -1, dtype=torch.int32, device=device),
+        expert_offsets=e(n + 1, dt=torch.int32), expert_rows=e(n, dt=torch.int32),
+        row_to_token=torch.full((rows_bound,), -1, dtype=torch.int32, device=device),
         dispatched=e(rows_bound, d, dt=x_dtype), y=e(rows_bound, d, dt=torch.bfloat16) if ffn else None,
         out=e(m, d, dt=x_dtype))
 
@@ -313,7 +324,7 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
     ffn = w1 is not None
     d_ff = w1.shape[1] if ffn else 0
     sh = shape(m, d, n, k, score, gate, _dtype_code(x))
-    rows_bound = m * k if capacity < 0 else min(m * k, capacity * n)
+    rows_bound = dispatch_rows(m, k, n, capacity)
     o = outputs or allocate_layer_outputs(m, d, n, k, rows_bound, x.dtype, ffn, dev)
     lo = L.LayerOutputs(*[(_ptr(getattr(o, f)) if getattr(o, f) is not None else None)
                           for f, _ in L.LayerOutputs._fields_])

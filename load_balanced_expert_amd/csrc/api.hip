@@ -14,7 +14,7 @@ size_t al(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct Layout {
   size_t planes, logits, kpart, chunks, r2t, hidden;
-  size_t idx, gate, counts, psum, f, P, aux, t2r, drop, offs, disp, y;
+  size_t idx, gate, counts, psum, f, P, aux, t2r, drop, offs, rowsn, disp, y;
   size_t route_end, dispatch_end, total;
   RoutePlan rp;
   int64_t pairs, rows_bound;
@@ -45,7 +45,8 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   Layout L{};
   L.rp = route_plan(s.m, s.d, s.n, s.x_dtype == MOE_BF16);
   L.pairs = s.m * s.k;
-  L.rows_bound = capacity < 0 ? L.pairs : std::min<int64_t>(L.pairs, int64_t(capacity) * s.n);
+  // dispatched rows: capacity-padded n * C, or compact m * k without a capacity
+  L.rows_bound = capacity < 0 ? L.pairs : int64_t(capacity) * s.n;
   const size_t esz = x_esz(s);
   size_t o = kControlBytes;
   L.planes = o; o += al(L.rp.planes_bytes);
@@ -61,7 +62,7 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   const int nch_max = std::max(L.nch, L.nch_route);
   L.chunks = o; o += al(size_t(nch_max) * s.n * sizeof(uint64_t));
   L.super_prefix = o; o += al(size_t(kMaxSuperChunks) * s.n * sizeof(int32_t));
-  L.r2t = o; o += al(size_t(L.pairs) * 4);
+  L.r2t = o; o += al(size_t(L.rows_bound) * 4);
   L.dispatch_end = o;
   L.hidden = o; o += al(d_ff > 0 ? ffn_ws_bytes(L.rows_bound, d_ff) : 0);
   L.idx = o; o += al(size_t(L.pairs) * 4);
@@ -74,6 +75,7 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   L.t2r = o; o += al(size_t(L.pairs) * 4);
   L.drop = o; o += al(size_t(L.pairs));
   L.offs = o; o += al(size_t(s.n + 1) * 4);
+  L.rowsn = o; o += al(size_t(s.n) * 4);
   L.disp = o; o += al(size_t(L.rows_bound) * s.d * esz);
   L.y = o; o += al(size_t(L.rows_bound) * s.d * (d_ff > 0 ? 2 : esz));
   L.total = o;
@@ -139,6 +141,8 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
   if (ex.disp) {
     a.capacity = ex.disp->capacity;
     a.expert_offsets = ex.disp->expert_offsets;
+    a.expert_rows = ex.disp->expert_rows;
+    a.padded = ex.disp->padded;
     a.super_prefix = ex.disp->super_prefix;
   }
   a.done = ctl_ticket(ws, kTicketRoute);
@@ -153,7 +157,8 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
 }
 
 DispatchArgs dispatch_args(const moe_shape& s, const Layout& L, int32_t capacity, const void* x, const int32_t* idx,
-                           int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* r2t, void* disp, void* ws) {
+                           int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* rows, int32_t* r2t, void* disp,
+                           void* ws) {
   DispatchArgs a{};
   a.idx = idx;
   a.pairs = L.pairs;
@@ -169,6 +174,8 @@ DispatchArgs dispatch_args(const moe_shape& s, const Layout& L, int32_t capacity
   a.token_to_row = t2r;
   a.drop_mask = drop;
   a.expert_offsets = offs;
+  a.expert_rows = rows;
+  a.padded = capacity >= 0;
   a.row_to_token = r2t;
   a.x = x;
   a.dispatched = disp;
@@ -178,9 +185,9 @@ DispatchArgs dispatch_args(const moe_shape& s, const Layout& L, int32_t capacity
 }
 
 moe_status do_dispatch(const moe_shape& s, const Layout& L, int32_t capacity, const void* x, const int32_t* idx,
-                       int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* r2t, void* disp, void* ws,
+                       int32_t* t2r, uint8_t* drop, int32_t* offs, int32_t* rows, int32_t* r2t, void* disp, void* ws,
                        bool prefix_ready, hipStream_t st) {
-  const DispatchArgs a = dispatch_args(s, L, capacity, x, idx, t2r, drop, offs, r2t, disp, ws);
+  const DispatchArgs a = dispatch_args(s, L, capacity, x, idx, t2r, drop, offs, rows, r2t, disp, ws);
   return hip_status(launch_dispatch(a, prefix_ready, st));
 }
 
@@ -313,16 +320,16 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
 }
 
 moe_status moe_dispatch(const moe_shape* shape, int32_t capacity, const void* x, const int32_t* idx,
-                        int32_t* token_to_row, uint8_t* drop_mask, int32_t* expert_offsets, int32_t* row_to_token,
-                        void* dispatched, void* ws, size_t ws_bytes, void* stream) {
+                        int32_t* token_to_row, uint8_t* drop_mask, int32_t* expert_offsets, int32_t* expert_rows,
+                        int32_t* row_to_token, void* dispatched, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (capacity < -1 || !idx || !token_to_row || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (dispatched && !x) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape, capacity, 0);
   if (!ws_ok(ws, ws_bytes, L.dispatch_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
-  return do_dispatch(*shape, L, capacity, x, idx, token_to_row, drop_mask, expert_offsets, row_to_token, dispatched,
-                     ws, false, static_cast<hipStream_t>(stream));
+  return do_dispatch(*shape, L, capacity, x, idx, token_to_row, drop_mask, expert_offsets, expert_rows, row_to_token,
+                     dispatched, ws, false, static_cast<hipStream_t>(stream));
 }
 
 size_t moe_expert_ffn_workspace_size(int32_t n, int32_t rows_max, int32_t d_ff) {
@@ -331,14 +338,15 @@ size_t moe_expert_ffn_workspace_size(int32_t n, int32_t rows_max, int32_t d_ff) 
 }
 
 moe_status moe_expert_ffn(int32_t n, int32_t d, int32_t d_ff, int32_t rows_max, const int32_t* expert_offsets,
-                          const void* dispatched, const void* w1, const void* w2, void* y, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const int32_t* expert_rows, const void* dispatched, const void* w1, const void* w2, void* y,
+                          void* ws, size_t ws_bytes, void* stream) {
   if (n < 1 || d < 1 || d_ff < 1 || rows_max < 0 || !expert_offsets || !dispatched || !w1 || !w2 || !y)
     return MOE_ERR_INVALID_ARG;
   if (d % 32 != 0 || d_ff % 32 != 0 || n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (!ws_ok(ws, ws_bytes, moe_expert_ffn_workspace_size(n, rows_max, d_ff)))
     return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
-  return hip_status(launch_expert_ffn(n, d, d_ff, rows_max, expert_offsets, static_cast<const uint16_t*>(dispatched),
+  return hip_status(launch_expert_ffn(n, d, d_ff, rows_max, expert_offsets, expert_rows,
+                                      static_cast<const uint16_t*>(dispatched),
                                       static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
                                       at<uint16_t>(ws, kControlBytes), static_cast<uint16_t*>(y),
                                       static_cast<hipStream_t>(stream)));
@@ -377,6 +385,7 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   int32_t* t2r = o->token_to_row ? o->token_to_row : at<int32_t>(ws, L.t2r);
   uint8_t* drop = o->drop_mask ? o->drop_mask : at<uint8_t>(ws, L.drop);
   int32_t* offs = o->expert_offsets ? o->expert_offsets : at<int32_t>(ws, L.offs);
+  int32_t* rowsn = o->expert_rows ? o->expert_rows : at<int32_t>(ws, L.rowsn);
   void* disp = o->dispatched ? o->dispatched : at<void>(ws, L.disp);
   void* y = ffn ? (o->y ? o->y : at<void>(ws, L.y)) : disp;
 
@@ -385,7 +394,7 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   };
   // route (+ load statistics + per-chunk counts and capacity prefix sums in its last workgroup), then
   // slots + permute-dispatch in one kernel
-  DispatchArgs da = dispatch_args(sh, L, p->capacity, x, idx, t2r, drop, offs, o->row_to_token, disp, ws);
+  DispatchArgs da = dispatch_args(sh, L, p->capacity, x, idx, t2r, drop, offs, rowsn, o->row_to_token, disp, ws);
   RouteExtras ex;
   ex.f = f;
   ex.P = P;
@@ -422,7 +431,8 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   mark(3);
   if (ffn) {
     const int32_t rows_max = effective_capacity(p->capacity, L.pairs);
-    if ((st = hip_status(launch_expert_ffn(sh.n, sh.d, p->d_ff, rows_max, offs, static_cast<const uint16_t*>(disp),
+    if ((st = hip_status(launch_expert_ffn(sh.n, sh.d, p->d_ff, rows_max, offs, da.padded ? rowsn : nullptr,
+                                           static_cast<const uint16_t*>(disp),
                                            static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
                                            at<uint16_t>(ws, L.hidden), static_cast<uint16_t*>(y), s))) != MOE_OK)
       return st;

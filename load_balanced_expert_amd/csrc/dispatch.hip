@@ -61,6 +61,8 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_hist(DispatchArgs a) {
   f.capacity = a.capacity;
   f.expert_offsets = a.expert_offsets;
   f.super_prefix = a.super_prefix;
+  f.expert_rows = a.expert_rows;
+  f.padded = a.padded;
   finalize_chunks(f, lds, n + kDispPrefixBuf, kDispThreads);
 }
 
@@ -113,6 +115,7 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int*
     }
     lbase[e] = base;
     ltot[e] = min(tot, a.capacity);
+    if (stats && a.expert_rows) a.expert_rows[e] = ltot[e];
     if (stats) {
       unsigned long long ps = 0;
 #pragma unroll
@@ -138,7 +141,9 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int*
     }
   }
   __syncthreads();
-  if (t < 64) {   // exclusive scan of the kept counts: lane l owns a contiguous run
+  if (a.padded) {   // capacity regions: expert j starts at row j * capacity
+    for (int j = t; j <= n; j += kDispThreads) loff[j] = j * a.capacity;
+  } else if (t < 64) {   // exclusive scan of the kept counts: lane l owns a contiguous run
     const int per = (n + 63) / 64, j0 = t * per, j1 = min(j0 + per, n);
     int sum = 0;
     for (int j = j0; j < j1; ++j) sum += ltot[j];

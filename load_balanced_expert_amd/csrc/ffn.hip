@@ -82,16 +82,21 @@ __device__ __forceinline__ void ffn_tile(const uint16_t* __restrict__ A, const u
   }
 }
 
+// End row of expert e: offsets[e] + rows[e] (capacity-padded layout) or offsets[e + 1].
+__device__ __forceinline__ int expert_end(const int32_t* offsets, const int32_t* rows, int e) {
+  return rows ? offsets[e] + rows[e] : offsets[e + 1];
+}
+
 template <bool RELU>
 __global__ __launch_bounds__(256) void k_grouped_gemm(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                       uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
-                                                      int K, int N, int row_limit) {
+                                                      const int32_t* __restrict__ rows, int K, int N, int row_limit) {
   const int e = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col0 = blockIdx.x * 128 + wave * 32;
   if (col0 >= N) return;
   // rows at or past row_limit (the hidden buffer's size) are never touched
-  const int r_begin = min(offsets[e], row_limit), r_end = min(offsets[e + 1], row_limit);
+  const int r_begin = min(offsets[e], row_limit), r_end = min(expert_end(offsets, rows, e), row_limit);
   const uint16_t* Bw = B + (size_t(e) * N + col0 + (lane & 31)) * K;
   for (int mb = r_begin; mb < r_end; mb += 128) {
     switch (ceil_div(min(128, r_end - mb), 32)) {
@@ -220,7 +225,8 @@ __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, 
 template <int W, bool RELU>
 __global__ __launch_bounds__(64 * W) void k_grouped_gemm_stream(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-                                                             const int32_t* __restrict__ offsets, int n, int K, int N,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ rows, int n, int K, int N,
                                                              int row_limit) {
   __shared__ __align__(16) uint16_t As[128 * kFfnLdA];
   __shared__ __align__(16) uint16_t Bs[W * 32 * kFfnLdB];
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(64 * W) void k_grouped_gemm_stream(const uint16_t* 
   // XCD-major order: workgroup b runs on XCD b % 8; give each XCD a contiguous range of (expert, block)
   const unsigned L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
   const int e = int(L / ncb), cb = int(L % ncb);
-  const int r_begin = min(offsets[e], row_limit), r_end = min(offsets[e + 1], row_limit);
+  const int r_begin = min(offsets[e], row_limit), r_end = min(expert_end(offsets, rows, e), row_limit);
   const int wave = threadIdx.x >> 6;
   const int col0 = cb * (32 * W) + wave * 32;
   const uint16_t* Be = B + size_t(e) * N * K;
@@ -251,30 +257,30 @@ static bool ffn_streams(int K, int N, int row_limit) {
 // 8-wave workgroups (256 columns: twice the reuse of each staged row chunk)
 // where N allows, else 4-wave workgroups (128 columns).
 template <bool RELU>
-static void launch_stream(int n, int K, int N, int row_limit, const int32_t* offsets, const uint16_t* A,
-                          const uint16_t* B, uint16_t* C, hipStream_t s) {
+static void launch_stream(int n, int K, int N, int row_limit, const int32_t* offsets, const int32_t* rows,
+                          const uint16_t* A, const uint16_t* B, uint16_t* C, hipStream_t s) {
   if (N % 256 == 0)
     hipLaunchKernelGGL((k_grouped_gemm_stream<8, RELU>), dim3(unsigned(n) * (N / 256)), dim3(512), 0, s, A, B, C,
-                       offsets, n, K, N, row_limit);
+                       offsets, rows, n, K, N, row_limit);
   else
     hipLaunchKernelGGL((k_grouped_gemm_stream<4, RELU>), dim3(unsigned(n) * (N / 128)), dim3(256), 0, s, A, B, C,
-                       offsets, n, K, N, row_limit);
+                       offsets, rows, n, K, N, row_limit);
 }
 
-hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets, const uint16_t* D,
-                             const uint16_t* w1, const uint16_t* w2, uint16_t* hidden, uint16_t* y,
+hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets, const int32_t* rows,
+                             const uint16_t* D, const uint16_t* w1, const uint16_t* w2, uint16_t* hidden, uint16_t* y,
                              hipStream_t s) {
   const int row_limit = int(std::min<int64_t>(int64_t(n) * rows_max, 0x7FFFFFFF));
   if (ffn_streams(d, d_ff, row_limit))
-    launch_stream<true>(n, d, d_ff, row_limit, offsets, D, w1, hidden, s);
+    launch_stream<true>(n, d, d_ff, row_limit, offsets, rows, D, w1, hidden, s);
   else
     hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(ceil_div(d_ff, 128), n), dim3(256), 0, s, D, w1, hidden, offsets,
-                       d, d_ff, row_limit);
+                       rows, d, d_ff, row_limit);
   if (ffn_streams(d_ff, d, row_limit))
-    launch_stream<false>(n, d_ff, d, row_limit, offsets, hidden, w2, y, s);
+    launch_stream<false>(n, d_ff, d, row_limit, offsets, rows, hidden, w2, y, s);
   else
     hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(ceil_div(d, 128), n), dim3(256), 0, s, hidden, w2, y, offsets,
-                       d_ff, d, row_limit);
+                       rows, d_ff, d, row_limit);
   return hipGetLastError();
 }
 

@@ -48,6 +48,8 @@ struct RouteArgs {
   int sup;                // chunks per super chunk
   int32_t capacity;       // < 0: no capacity prefix sums
   int32_t* expert_offsets;
+  int32_t* expert_rows;   // [n] kept rows per expert, or nullptr
+  bool padded;            // capacity-padded layout
   int32_t* super_prefix;
   uint32_t* done;         // completion ticket (control region)
   int lds_region_ints;    // set by launch_route
@@ -86,6 +88,8 @@ struct DispatchArgs {
   int32_t* token_to_row;
   uint8_t* drop_mask;
   int32_t* expert_offsets;
+  int32_t* expert_rows;   // [n] kept rows per expert, or nullptr
+  bool padded;            // capacity-padded layout: expert j owns rows [j C, (j + 1) C)
   int32_t* row_to_token;
   const void* x;
   void* dispatched;
@@ -117,7 +121,9 @@ bool dispatch_self_prefix_ok(int nch, int n);
 
 // ---------------------------------------------------------------- expert FFN
 size_t ffn_ws_bytes(int64_t rows_bound, int d_ff);
-hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets,
+// rows (nullable): rows of expert j = rows[j] from offsets[j] (capacity-padded
+// layout); else offsets[j + 1] - offsets[j]
+hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets, const int32_t* rows,
                              const uint16_t* D, const uint16_t* w1, const uint16_t* w2,
                              uint16_t* hidden, uint16_t* y, hipStream_t s);
 

@@ -62,6 +62,8 @@ struct FinalizeArgs {
   int32_t capacity;             // < 0: no capacity prefix sums
   int32_t* expert_offsets;      // [n + 1]
   int32_t* super_prefix;        // [ceil(nch / sup), n]
+  int32_t* expert_rows;         // [n] kept rows per expert, or nullptr
+  bool padded;                  // capacity-padded layout: expert j starts at row j * capacity
 };
 
 // Exclusive scan of v[0..n) held in LDS by one workgroup into out[0..n];
@@ -178,9 +180,16 @@ __device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds,
     }
   }
   if (a.capacity >= 0) {
-    for (int j = threadIdx.x; j < n; j += threads) tot[j] = min(tot[j], a.capacity);
+    for (int j = threadIdx.x; j < n; j += threads) {
+      tot[j] = min(tot[j], a.capacity);
+      if (a.expert_rows) a.expert_rows[j] = tot[j];
+    }
     __syncthreads();
-    block_exclusive_scan(tot, n, a.expert_offsets, part, threads);
+    if (a.padded) {
+      for (int j = threadIdx.x; j <= n; j += threads) a.expert_offsets[j] = j * a.capacity;
+    } else {
+      block_exclusive_scan(tot, n, a.expert_offsets, part, threads);
+    }
   }
 }
 

@@ -661,6 +661,8 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
   f.capacity = a.capacity;
   f.expert_offsets = a.expert_offsets;
   f.super_prefix = a.super_prefix;
+  f.expert_rows = a.expert_rows;
+  f.padded = a.padded;
   finalize_chunks(f, scratch, scratch_ints, kRouteThreads);
 }
 

@@ -103,12 +103,12 @@ def test_null_pointers_rejected(lib):
     sh = _sh()
     assert lib.moe_route(ctypes.byref(sh), None, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
     assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert lib.moe_dispatch(ctypes.byref(sh), -1, FAKE, None, FAKE, None, FAKE, None, None, FAKE, 1 << 30,
+    assert lib.moe_dispatch(ctypes.byref(sh), -1, FAKE, None, FAKE, None, FAKE, None, None, None, FAKE, 1 << 30,
                             None) == 1
-    assert lib.moe_dispatch(ctypes.byref(sh), -2, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, 1 << 30,
+    assert lib.moe_dispatch(ctypes.byref(sh), -2, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, 1 << 30,
                             None) == 1
     # dispatched rows requested without x
-    assert lib.moe_dispatch(ctypes.byref(sh), -1, None, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 30,
+    assert lib.moe_dispatch(ctypes.byref(sh), -1, None, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, 1 << 30,
                             None) == 1
     assert lib.moe_combine(ctypes.byref(sh), None, 1, FAKE, FAKE, None, FAKE, None) == 1
     assert lib.moe_combine(ctypes.byref(sh), FAKE, 7, FAKE, FAKE, None, FAKE, None) == 1
@@ -166,9 +166,9 @@ def test_balance_validation(lib):
 
 def test_expert_ffn_validation(lib):
     big = 1 << 40
-    assert lib.moe_expert_ffn(8, 48, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 2
-    assert lib.moe_expert_ffn(8, 64, 64, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 1
-    assert lib.moe_expert_ffn(8, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == 3
+    assert lib.moe_expert_ffn(8, 48, 64, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 2
+    assert lib.moe_expert_ffn(8, 64, 64, 10, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 1
+    assert lib.moe_expert_ffn(8, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == 3
 
 
 def test_switch_layer_validation(lib):

@@ -150,22 +150,25 @@ def _layer_check(spec, seed, cf, ffn, k=1):
     if flips:
         pytest.skip(f"{len(flips)} near-tie flips: downstream maps legitimately differ")
     assert np.array_equal(to_host(o.f), f.astype(np.float32))
-    dm = OD.dispatch_maps(ref.idx, spec.N, cap)
+    dm = OD.dispatch_maps(ref.idx, spec.N, cap, padded=True)   # the layer's layout with a capacity
     assert np.array_equal(to_host(o.token_to_row), dm.token_to_row)
     assert np.array_equal(to_host(o.drop_mask), dm.drop_mask)
     assert np.array_equal(to_host(o.expert_offsets), dm.expert_offsets)
-    assert np.array_equal(to_host(o.dispatched)[:dm.rows], OD.dispatch_rows(inp.x, dm))
+    assert np.array_equal(to_host(o.expert_rows), dm.expert_rows)
+    filled = dm.filled_rows()
+    assert np.array_equal(to_host(o.row_to_token)[filled], dm.row_to_token[filled])
+    assert np.array_equal(to_host(o.dispatched)[filled], OD.dispatch_rows(inp.x, dm)[filled])
     x64 = OR.decode_hidden(inp.x)
-    D64 = x64[dm.row_to_token]
+    Y = np.zeros((dm.rows, spec.d))
+    D64 = x64[dm.row_to_token[filled]]
     if ffn:
-        Y = np.zeros_like(D64)
         for e in range(spec.N):
-            lo, hi = dm.expert_offsets[e], dm.expert_offsets[e + 1]
+            lo, hi = dm.expert_offsets[e], dm.expert_offsets[e] + dm.expert_rows[e]
             if hi > lo:
-                Y[lo:hi] = OE.relu_ffn(D64[lo:hi], w1[e], w2[e])
+                Y[lo:hi] = OE.relu_ffn(x64[dm.row_to_token[lo:hi]], w1[e], w2[e])
         tol = 2e-2
     else:
-        Y = D64
+        Y[filled] = D64
         tol = 1e-5 if spec.x_dtype == "f32" else 2.0 ** -8 + 1e-5
     out_ref = OE.combine(x64, Y, ref.gate, dm.token_to_row)
     got = OR.decode_hidden(to_host(o.out))
@@ -214,13 +217,14 @@ def test_layer_maps_equal_separate_calls():
     assert torch.equal(o.token_to_row, dsp.token_to_row)
     assert torch.equal(o.drop_mask, dsp.drop_mask)
     assert torch.equal(o.expert_offsets, dsp.expert_offsets)
-    rows = int(dsp.expert_offsets[-1].item())
-    assert torch.equal(o.row_to_token[:rows], dsp.row_to_token[:rows])
-    assert torch.equal(o.dispatched[:rows], dsp.dispatched[:rows])
+    assert torch.equal(o.expert_rows, dsp.expert_rows)
+    assert torch.equal(o.row_to_token, dsp.row_to_token)
+    filled = dsp.row_to_token >= 0
+    assert torch.equal(o.dispatched[filled], dsp.dispatched[filled])
     # a second layer call on the same workspace: the control words were left zero
     o2 = M.switch_layer(x, w, k=1, capacity=cap)
     torch.cuda.synchronize()
-    assert torch.equal(o2.token_to_row, o.token_to_row) and torch.equal(o2.dispatched[:rows], o.dispatched[:rows])
+    assert torch.equal(o2.token_to_row, o.token_to_row) and torch.equal(o2.dispatched[filled], o.dispatched[filled])
 
 
 def test_lossfree_micro_batch_loop():

@@ -24,10 +24,12 @@ def check_dispatch(T, n, k, d, cf, skew, seed, x_dtype="bf16", copy_rows=True):
     xs = W.switch_inputs(W.SwitchSpec("d", T=T, d=d, N=n, x_dtype=x_dtype), seed).x
     out = M.dispatch(to_dev(xs), to_dev(idx), n, capacity=cap, copy_rows=copy_rows)
     torch.cuda.synchronize()
-    ref = OD.dispatch_maps(idx, n, cap if cap >= 0 else T * k)
+    # capacity-padded layout with a capacity, compact without
+    ref = OD.dispatch_maps(idx, n, cap if cap >= 0 else T * k, padded=cap >= 0)
     assert np.array_equal(to_host(out.token_to_row), ref.token_to_row)
     assert np.array_equal(to_host(out.drop_mask), ref.drop_mask)
     assert np.array_equal(to_host(out.expert_offsets), ref.expert_offsets)
+    assert np.array_equal(to_host(out.expert_rows), ref.expert_rows)
     rows = ref.rows
     assert np.array_equal(to_host(out.row_to_token)[:rows], ref.row_to_token)
     if copy_rows:
@@ -65,7 +67,8 @@ def test_all_tokens_one_expert():
     out = M.dispatch(None, to_dev(idx), n, capacity=cap, d=16)
     torch.cuda.synchronize()
     assert int(to_host(out.drop_mask).sum()) == T - cap
-    assert to_host(out.expert_offsets).tolist() == [0] + [cap] * n
+    assert to_host(out.expert_offsets).tolist() == [j * cap for j in range(n + 1)]
+    assert to_host(out.expert_rows).tolist() == [cap] + [0] * (n - 1)
     assert np.array_equal(to_host(out.token_to_row)[:cap, 0], np.arange(cap))
 
 
@@ -108,6 +111,10 @@ def test_combine_without_residual():
     check_combine(512, 8, 2, 128, 100, "bf16", seed=5, residual=False)
 
 
+def test_dispatch_capacity_zero():
+    check_dispatch(300, 8, 2, 32, 0.0, 0.5, seed=8)
+
+
 # ------------------------------------------------------------------ expert FFN
 @pytest.mark.parametrize("rows_per_expert,d,d_ff", [([80, 37, 0, 130, 64, 1, 33, 96], 768, 3072),
                                                     ([5, 40, 17, 0], 1024, 4096), ([3, 200], 128, 96),
@@ -127,6 +134,29 @@ def test_expert_ffn(rows_per_expert, d, d_ff):
     D64 = OR.decode_hidden(D)
     for e in range(n):
         lo, hi = offs[e], offs[e + 1]
+        if hi == lo:
+            continue
+        ref = OE.relu_ffn(D64[lo:hi], w1[e], w2[e])
+        err = row_rel_err(got[lo:hi], ref)
+        assert err.max() <= 2e-2, f"expert {e}: worst row error {err.max():.3e}"
+
+
+def test_expert_ffn_padded_layout():
+    # capacity-padded rows: expert j's rows start at j * C, rows_j of them filled
+    rows_per_expert, C, d, d_ff = [80, 0, 17, 80, 1, 64], 80, 256, 512
+    n = len(rows_per_expert)
+    spec = W.SwitchSpec("ffnp", T=1, d=d, N=n, d_ff=d_ff, w_std=np.sqrt(1.0 / d))
+    offs = (np.arange(n + 1) * C).astype(np.int32)
+    rows = np.array(rows_per_expert, np.int32)
+    D = W.random_rows(n * C, d, seed=9, bf16=True)
+    w1, w2 = W.all_expert_weights(spec, 9)
+    say(f"[ffn padded] n={n} C={C} rows={rows_per_expert}")
+    y = M.expert_ffn(to_dev(D), to_dev(offs), to_dev(w1), to_dev(w2), rows_max=C, expert_rows=to_dev(rows))
+    torch.cuda.synchronize()
+    got = OR.decode_hidden(to_host(y))
+    D64 = OR.decode_hidden(D)
+    for e in range(n):
+        lo, hi = offs[e], offs[e] + rows[e]
         if hi == lo:
             continue
         ref = OE.relu_ffn(D64[lo:hi], w1[e], w2[e])
