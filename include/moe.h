@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,   /* bad size, null required pointer, inconsistent options */
-  MOE_ERR_UNSUPPORTED = 2,   /* valid but beyond this build's limits (e.g. n > 4096) */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but beyond the library's limits (e.g. n > 4096) */
   MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_size() */
   MOE_ERR_HIP = 4            /* a kernel launch failed */
 } moe_status;
@@ -139,7 +139,7 @@ moe_status moe_router_prepare(int32_t d, int32_t n, const float* w_r, void* plan
  * counts   [n]      int32 out: c_j = number of (token, choice) pairs on expert j
  * prob_sum [n]      fp32 out or NULL: Σ_t score_j(t) (softmax p or sigmoid ρ),
  *                   the numerator of P_j ([Switch review] "로드 밸런싱 손실")
- * Limits: 1 <= k <= n <= 4096, 1 <= d <= 65536, m >= 1. */
+ * Limits: 1 <= k <= min(n, 64), n <= 4096, 1 <= d <= 65536, m >= 1. */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
                      const float* bias, int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
                      void* ws, size_t ws_bytes, void* stream);

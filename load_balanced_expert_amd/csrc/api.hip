@@ -30,7 +30,8 @@ bool shape_valid(const moe_shape* s) {
 }
 
 bool shape_supported(const moe_shape* s) {
-  return s->n <= kMaxExperts && s->d <= kMaxD && s->m <= 0x7FFFFFFFll && s->m * s->k <= 0x7FFFFFFFll;
+  return s->n <= kMaxExperts && s->k <= kMaxK && s->d <= kMaxD && s->m <= 0x7FFFFFFFll &&
+         s->m * s->k <= 0x7FFFFFFFll;
 }
 
 moe_status check_shape(const moe_shape* s) {

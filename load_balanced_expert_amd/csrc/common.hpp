@@ -14,6 +14,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 4096;
+constexpr int kMaxK = 64;   // picks per token (one wave lane per pick in the epilogues)
 
 // Control region at the start of every workspace: completion tickets of the
 // last-workgroup pattern (zero before first use; each kernel that takes a

@@ -97,6 +97,9 @@ def test_unsupported_sizes(lib):
     sh = _sh(d=65537)
     st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
     assert st == L.MOE_ERR_UNSUPPORTED
+    sh = _sh(n=128, k=65)   # more picks per token than wave lanes
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == L.MOE_ERR_UNSUPPORTED
 
 
 def test_null_pointers_rejected(lib):
