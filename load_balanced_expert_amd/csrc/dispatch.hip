@@ -76,57 +76,84 @@ constexpr int kDispCopyThreads = kDispThreads - 64 * kDispCopyWave0;
 
 // Self prefix (n <= 256): the route kernel left per-chunk count rows
 // [nch][n] int32 and, per super chunk of `sup` chunks, the expert counts and
-// fixed-point score sums (integer atomics, so order-free).  Per expert, a
-// thread adds the super-chunk counts (the total) and those before this
-// chunk's super chunk plus the count rows of the earlier chunks inside it
-// (this chunk's slot base); wave 0 scans the kept counts into the expert
-// offsets.  Workgroup 0 publishes counts, f, P, aux and the offsets.
-__device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, int* lbase, int* loff) {
-  const int n = a.n, t = threadIdx.x;
-  const int nsup = ceil_div(a.nch, a.sup), sc = c / a.sup;
-  const bool stats = c == 0;
-  int* ltot = loff + n + 1;   // kept counts, then scanned by wave 0
+// fixed-point score sums (integer atomics, so order-free).  Expert e's total
+// is the sum of its super-chunk counts; this chunk's slot base adds the
+// super-chunk counts before this chunk's super chunk and the count rows of
+// the earlier chunks inside it.  Those sources are spread over the whole
+// workgroup, every thread loading its share first thing (before the row
+// reads, so the prefix loads are not queued behind them): thread t takes
+// expert t % n and every (1024 / n)-th source.  The partial sums meet in LDS
+// through integer atomics (order-free); then the offsets follow, and
+// workgroup 0 publishes counts, f, P, aux, the kept counts and the offsets.
+constexpr int kPrefixBatch = 8;   // sources per thread loaded up front
+struct PrefixPart {
+  int e, sl, slices, nsrc, nsup, sc;
+  int v[kPrefixBatch];
+  unsigned long long pq[kPrefixBatch];
+};
+__device__ __forceinline__ int prefix_source(const DispatchArgs& a, const PrefixPart& P, int c, int i) {
   const int32_t* crow = reinterpret_cast<const int32_t*>(a.chunks);
+  return i < P.nsup ? a.sup_counts[i * a.n + P.e] : crow[int64_t(P.sc * a.sup + (i - P.nsup)) * a.n + P.e];
+}
+__device__ __forceinline__ void prefix_issue(const DispatchArgs& a, int c, PrefixPart& P) {
+  const int n = a.n, t = threadIdx.x;
+  P.nsup = ceil_div(a.nch, a.sup);
+  P.sc = c / a.sup;
+  P.nsrc = P.nsup + (c - P.sc * a.sup);
+  P.slices = kDispThreads / n;
+  P.e = t % n;
+  P.sl = t / n;
+  const bool stats = c == 0;
+#pragma unroll
+  for (int u = 0; u < kPrefixBatch; ++u) {
+    const int i = P.sl + u * P.slices;
+    const bool in = P.sl < P.slices && i < P.nsrc;
+    P.v[u] = in ? prefix_source(a, P, c, i) : 0;
+    P.pq[u] = stats && P.sl < P.slices && i < P.nsup ? a.sup_psum[i * n + P.e] : 0ull;
+  }
+}
+__device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, PrefixPart& P, int* lbase, int* loff,
+                                              int* ltot_raw, unsigned long long* lps) {
+  const int n = a.n, t = threadIdx.x;
+  const bool stats = c == 0;
+  int* ltot = loff + n + 1;   // kept counts
+  // partial sums of this thread's sources (the batch loaded up front, then any rest)
+  int tot = 0, base = 0;
+  unsigned long long ps = 0;
+  if (P.sl < P.slices) {
+#pragma unroll
+    for (int u = 0; u < kPrefixBatch; ++u) {
+      const int i = P.sl + u * P.slices;
+      tot += i < P.nsup ? P.v[u] : 0;
+      base += i < P.sc || i >= P.nsup ? P.v[u] : 0;
+      ps += P.pq[u];
+    }
+    for (int i = P.sl + kPrefixBatch * P.slices; i < P.nsrc; i += P.slices) {
+      const int v = prefix_source(a, P, c, i);
+      tot += i < P.nsup ? v : 0;
+      base += i < P.sc || i >= P.nsup ? v : 0;
+    }
+  }
+  __syncthreads();   // the LDS sums were zeroed before the row reads
+  if (P.sl < P.slices) {
+    if (tot) atomicAdd(ltot_raw + P.e, tot);
+    if (base) atomicAdd(lbase + P.e, base);
+    if (stats && ps) atomicAdd(lps + P.e, ps);
+  }
+  __syncthreads();
   double auxp = 0.0;
-  const int pt = t - 64;   // waves 1-2 load the prefix data while wave 0 ranks
-  for (int e = pt; pt >= 0 && pt < 128 && e < n; e += 128) {
-    // every load of the pass is issued before the first use (no serial round trips)
-    int v[kMaxSuperChunks], w[kMaxSuperChunks];
-    unsigned long long pq[kMaxSuperChunks];
-#pragma unroll
-    for (int q = 0; q < kMaxSuperChunks; ++q) {
-      v[q] = q < nsup ? a.sup_counts[q * n + e] : 0;
-      pq[q] = stats && q < nsup ? a.sup_psum[q * n + e] : 0ull;
-      const int cc = sc * a.sup + q;   // earlier chunks of this super chunk (up to 16 per pass)
-      w[q] = cc < c ? crow[int64_t(cc) * n + e] : 0;
-    }
-    int tot = 0, base = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxSuperChunks; ++q) {
-      tot += v[q];
-      base += q < sc ? v[q] : 0;
-      base += w[q];
-    }
-    for (int cc0 = sc * a.sup + kMaxSuperChunks; cc0 < c; cc0 += kMaxSuperChunks) {
-#pragma unroll
-      for (int q = 0; q < kMaxSuperChunks; ++q) w[q] = cc0 + q < c ? crow[int64_t(cc0 + q) * n + e] : 0;
-#pragma unroll
-      for (int q = 0; q < kMaxSuperChunks; ++q) base += w[q];
-    }
-    lbase[e] = base;
-    ltot[e] = min(tot, a.capacity);
-    if (stats && a.expert_rows) a.expert_rows[e] = ltot[e];
+  for (int e = t; e < n; e += kDispThreads) {
+    const int tt = ltot_raw[e];
+    ltot[e] = min(tt, a.capacity);
     if (stats) {
-      unsigned long long ps = 0;
-#pragma unroll
-      for (int q = 0; q < kMaxSuperChunks; ++q) ps += pq[q];   // integer sum: order-free
-      const double psum = double(ps) / double(kPsumScale);
+      if (a.expert_rows) a.expert_rows[e] = ltot[e];
+      const double psum = double(lps[e]) / double(kPsumScale);   // integer sum: order-free
       const int64_t m = a.pairs / a.k;
-      if (a.counts) a.counts[e] = tot;
+      if (a.counts) a.counts[e] = tt;
       if (a.prob_sum) a.prob_sum[e] = float(psum);
-      if (a.f) a.f[e] = float(tot) / float(m);
+      if (a.f) a.f[e] = float(tt) / float(m);
       if (a.P) a.P[e] = float(psum / double(m));
-      auxp += (double(tot) / double(m)) * (psum / double(m));
+      auxp += (double(tt) / double(m)) * (psum / double(m));
     }
   }
   if (stats && a.aux) {   // fixed-order fp64 sum over the experts
@@ -175,7 +202,18 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
   int* lslot = lrow + cp;                        // [cp] slot inside the chunk
   int* lbase = lslot + cp;                       // SELF: [n] slot base of this chunk
   int* loff = lbase + n;                         // SELF: [n + 1] expert offsets, then [n] kept counts
+  int* ltot_raw = loff + 2 * n + 1;              // SELF: [n] expert totals
   const int c = blockIdx.x;
+  PrefixPart pp;
+  __shared__ unsigned long long lps[kSelfPrefixMaxN];   // SELF, workgroup 0: score sums
+  if constexpr (SELF) {
+    prefix_issue(a, c, pp);
+    for (int j = threadIdx.x; j < n; j += kDispThreads) {
+      lbase[j] = 0;
+      ltot_raw[j] = 0;
+      lps[j] = 0ull;
+    }
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t p0 = int64_t(c) * cp;
   const int np = int(min<int64_t>(cp, a.pairs - p0));
@@ -225,7 +263,7 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
       }
     }
   }
-  if constexpr (SELF) derive_prefix(a, c, lbase, loff);   // has barriers
+  if constexpr (SELF) derive_prefix(a, c, pp, lbase, loff, ltot_raw, lps);   // has barriers
   else __syncthreads();
   // slots -> rows and maps, one thread per pair
   const int s = c / a.sup;
@@ -262,13 +300,14 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
   }
   if (!a.dispatched) return;
   __syncthreads();
+  // rows are stored non-temporally: nothing in this kernel reads them again
   if (wave >= kDispCopyWave0) {
     int q = q0, v = v0;
 #pragma unroll
     for (int u = 0; u < kDispPrefetch; ++u) {
       if (q < qend) {
         const int row = lrow[q];
-        if (row >= 0) out[int64_t(row) * vpr + v] = pv[u];
+        if (row >= 0) __builtin_nontemporal_store(pv[u], &out[int64_t(row) * vpr + v]);
       }
       q += dq;
       v += dv;
@@ -304,7 +343,7 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (dst[u] >= 0) out[dst[u]] = val[u];
+      if (dst[u] >= 0) __builtin_nontemporal_store(val[u], &out[dst[u]]);
   }
 }
 
@@ -325,8 +364,8 @@ bool dispatch_self_prefix_ok(int nch, int n) {
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool prefix_ready, hipStream_t s) {
   if (a.self_prefix) {
-    // cnt [n], lrow [cp], lslot [cp], lbase [n], loff [n + 1] + kept [n]
-    const size_t lds = (4 * size_t(a.n) + 1 + 2 * size_t(a.chunk_tokens) * a.k) * sizeof(int);
+    // cnt [n], lrow [cp], lslot [cp], lbase [n], loff [n + 1] + kept [n], totals [n]
+    const size_t lds = (5 * size_t(a.n) + 1 + 2 * size_t(a.chunk_tokens) * a.k) * sizeof(int);
     launch_rank_copy<true>(a, lds, s);
     return hipGetLastError();
   }
