@@ -167,10 +167,13 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, Pref
       a.aux[0] = float(double(a.alpha) * double(n) * s);
     }
   }
+  if (a.padded) {   // capacity regions: expert j starts at row j * capacity (no scan, no barrier)
+    if (stats)
+      for (int j = t; j <= n; j += kDispThreads) a.expert_offsets[j] = j * a.capacity;
+    return;
+  }
   __syncthreads();
-  if (a.padded) {   // capacity regions: expert j starts at row j * capacity
-    for (int j = t; j <= n; j += kDispThreads) loff[j] = j * a.capacity;
-  } else if (t < 64) {   // exclusive scan of the kept counts: lane l owns a contiguous run
+  if (t < 64) {   // exclusive scan of the kept counts: lane l owns a contiguous run
     const int per = (n + 63) / 64, j0 = t * per, j1 = min(j0 + per, n);
     int sum = 0;
     for (int j = j0; j < j1; ++j) sum += ltot[j];
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a)
       int base, off;
       if constexpr (SELF) {
         base = lbase[e];
-        off = loff[e];
+        off = a.padded ? e * a.capacity : loff[e];
       } else {
         // chunk base of expert e: its super-chunk prefix plus the earlier chunks of the super chunk
         base = a.super_prefix[int64_t(s) * n + e];
