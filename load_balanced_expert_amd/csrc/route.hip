@@ -472,6 +472,15 @@ __device__ __forceinline__ float half_sum(float v) {
   row_pair(__float_as_uint(v), a, b);
   return __uint_as_float(a) + __uint_as_float(b);
 }
+__device__ __forceinline__ int half_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  v = min(v, dpp_i<kDppMirror>(v));
+  uint32_t a, b;
+  row_pair(uint32_t(v), a, b);
+  return min(int(a), int(b));
+}
 template <int CTRL>
 __device__ __forceinline__ void argbest_step(float& key, int& ix) {
   const float ok = dpp_f<CTRL>(key);
@@ -499,9 +508,12 @@ __device__ __forceinline__ void half_argbest(float& key, int& ix) {
 // (softmax or sigmoid), the top-k by key (logit, or score + bias), the gates
 // and the histogram, then overwrites the token's LDS row with its scores so
 // that the per-expert score sums are plain column sums.  Top-1 softmax
-// without bias (the Switch router) takes a shorter path: one arg-max
-// reduction gives both the softmax maximum and the pick, whose score is
-// exp(0) / sum = 1 / sum.
+// without bias (the Switch router) takes a shorter path: a max reduction
+// gives the softmax maximum, a min reduction over the lanes holding it the
+// pick (the lowest such expert), whose score is exp(0) / sum = 1 / sum; the
+// exponentials and that reciprocal use the hardware exp2 (argument scaled by
+// log2 e) and reciprocal, about 1e-6 relative, well inside the fp32 tolerance
+// the scores are checked to.
 template <int NV>
 __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int64_t t0, const EpiArgs& e,
                                                 int32_t* __restrict__ idx, float* __restrict__ gate_out,
@@ -518,24 +530,25 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
       h[u] = j < e.n ? row[j] : -INFINITY;
     }
     if (fast) {
-      float bk = -INFINITY;
-      int bj = 0x7FFFFFFF;
+      // the maximum, then the lowest expert attaining it (ties to the lower index)
+      float mx = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < NV; ++u)
-        if (l + 32 * u < e.n && better(h[u], l + 32 * u, bk, bj)) {
-          bk = h[u];
-          bj = l + 32 * u;
-        }
-      half_argbest(bk, bj);   // bk: the softmax maximum; bj: its lowest expert
+      for (int u = 0; u < NV; ++u) mx = fmaxf(mx, h[u]);
+      mx = half_max(mx);
+      int cand = 0x7FFFFFFF;
+#pragma unroll
+      for (int u = NV - 1; u >= 0; --u)
+        if (l + 32 * u < e.n && h[u] == mx) cand = l + 32 * u;
+      const int bj = half_min_i(cand);
       float sum = 0.f;
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        sc[u] = l + 32 * u < e.n ? expf(h[u] - bk) : 0.f;
+        sc[u] = l + 32 * u < e.n ? __expf(h[u] - mx) : 0.f;   // hardware exp2 of the scaled argument
         sum += sc[u];
       }
-      const float inv = 1.0f / half_sum(sum);
+      const float inv = __builtin_amdgcn_rcpf(half_sum(sum));   // sum >= 1 (the maximum's term is 1)
       if (l == 0) {
-        atomicAdd(&hist[bj], 1);
+        if (bj < e.n) atomicAdd(&hist[bj], 1);   // out of range only for a row without a finite maximum
         idx[t0 + tl] = bj;
         gate_out[t0 + tl] = e.gate == 1 ? 1.0f : inv;
       }
@@ -622,13 +635,13 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
     float acc = 0.f;
     if (a.want_psum) {
-      // token order; eight reads in flight
-      for (int tl0 = 0; tl0 < rows; tl0 += 8) {
-        float v[8];
+      // token order; 32 reads in flight
+      for (int tl0 = 0; tl0 < rows; tl0 += 32) {
+        float v[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = tl0 + u < rows ? lg[int64_t(tl0 + u) * ld + j] : 0.f;
+        for (int u = 0; u < 32; ++u) v[u] = tl0 + u < rows ? lg[int64_t(tl0 + u) * ld + j] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 32; ++u)
           if (tl0 + u < rows) acc += SCORES ? v[u] : score_of(e.score, v[u], tok_mx[tl0 + u], tok_sum[tl0 + u]);
       }
     }
