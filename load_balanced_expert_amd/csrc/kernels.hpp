@@ -34,6 +34,7 @@ struct RouteArgs {
   const float* bias;
   const uint16_t* planes;
   bool planes_ready;  // planes already hold the split of w_r
+  bool parts_apart;   // set by launch_route: partial tiles after the x tile
   float* logits;   // big-n path only
   int32_t* idx;
   float* gate_out;

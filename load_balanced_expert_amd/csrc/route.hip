@@ -37,7 +37,7 @@ constexpr int kRouteThreads = 1024;  // 16 waves
 // tile), which share one region; the last workgroup's finishing scratch
 // reuses it.  Rows kernel: the scratch.  The padding of 8 columns puts the
 // two lane halves of an accumulator store on different banks.
-constexpr int kXStageMaxInts = 15360;
+constexpr int kXStageMaxInts = 32768;
 static int fused_parts(const RoutePlan& plan) {
   const int nt = plan.npad / 32;
   return plan.mfma ? 16 / (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8) : 1;
@@ -45,11 +45,25 @@ static int fused_parts(const RoutePlan& plan) {
 static int fused_partial_ints(const RoutePlan& plan, int n) {
   return std::max(fused_parts(plan) * kRouteBM * (plan.npad + 8), n + 2 * kMaxSuperChunks * 16);
 }
-static int x_tile_ints(const RoutePlan& plan) { return kRouteBM * (plan.dpad + 8) / 2; }
+// width of the staged x tile: the K range of one workgroup (the whole of d
+// unless the tile's K range is split over kg workgroups)
+static int x_tile_cols(const RoutePlan& plan) {
+  const int nkb = plan.dpad / 32;
+  return (plan.kg > 1 ? (nkb + plan.kg - 1) / plan.kg : nkb) * 32;
+}
+static int x_tile_ints(const RoutePlan& plan) { return kRouteBM * (x_tile_cols(plan) + 8) / 2; }
 static bool stage_x(const RoutePlan& plan, int) { return x_tile_ints(plan) + plan.npad <= kXStageMaxInts + 256; }
+// whether the partial tiles get a region of their own after the x tile (it
+// fits in LDS), so that each wave stores its partial tile as soon as its
+// product is done instead of waiting until every wave has read the x tile
+static bool partials_apart(const RoutePlan& plan, int n) {
+  return plan.fused && plan.mfma && stage_x(plan, n) &&
+         x_tile_ints(plan) + fused_partial_ints(plan, n) + plan.npad + 1024 <= 40960;
+}
 static int route_region_ints(const RoutePlan& plan, int n) {
   if (!plan.fused) return n + 4096;
   const int part = fused_partial_ints(plan, n);
+  if (partials_apart(plan, n)) return x_tile_ints(plan) + part;
   return plan.mfma && stage_x(plan, n) ? std::max(part, x_tile_ints(plan)) : part;
 }
 
@@ -702,7 +716,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   extern __shared__ float smem[];
   __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];   // softmax statistics (k > 32 epilogue)
   const int ldl = a.npad + 8;   // logit and partial tile row stride
-  float* lg = smem;
+  // the staged x tile holds one workgroup's K range: xcols columns, row stride xcols + 8
+  // (x_tile_cols on the host); partials apart: the partial (and logit) tiles follow it
+  const int xcols = ((a.dpad / 32 + a.kg - 1) / a.kg) * 32;
+  const int lg_off = XLDS && a.parts_apart ? kRouteBM * (xcols + 8) / 2 : 0;
+  float* lg = smem + lg_off;
   int* hist = reinterpret_cast<int*>(smem) + a.lds_region_ints;
   // the wave index is uniform: keep it (and every K-block index derived from it) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -723,7 +741,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
       // stage the 32 x rows in LDS with coalesced 16-byte loads (zero padding past the end)
       uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
       // only this workgroup's K range [32 kbA, 32 kbB) of the tile is staged
-      const int ldx = a.dpad + 8, cpr = (kbB - kbA) * 4, kx = kbA * 32;
+      // columns [kx, kx + 32 (kbB - kbA)) of x land at tile columns from 0 (row stride ldx)
+      const int ldx = xcols + 8, cpr = (kbB - kbA) * 4, kx = kbA * 32;
       // four loads in flight per thread before the LDS stores (one pass for d <= 1024);
       // the first pass runs in every thread (its items are range-checked)
       for (int c0 = tid; c0 == tid || c0 < kRouteBM * cpr; c0 += 4 * kRouteThreads) {
@@ -734,7 +753,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
           const int c = c0 + u * kRouteThreads;
           const int r = c / cpr, k = kx + (c - r * cpr) * 8;
           v[u] = u32x4{0u, 0u, 0u, 0u};
-          dst[u] = c < kRouteBM * cpr ? r * ldx + k : -1;
+          dst[u] = c < kRouteBM * cpr ? r * ldx + (k - kx) : -1;
           if (c < kRouteBM * cpr && r < rows && k < a.d) v[u] = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
         }
         if constexpr (DIRECT) {   // split the first weights while the x loads are in flight
@@ -745,14 +764,15 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
           if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xs + dst[u]) = v[u];
       }
       __syncthreads();
-      arow = xs + (lane & 31) * ldx + 16 * (lane >> 5);
+      // the product indexes x by absolute K block: shift the row start back by kx
+      arow = xs + (lane & 31) * ldx + 16 * (lane >> 5) - kx;
     } else {
       arow = x + (t0 + min(lane & 31, rows - 1)) * a.d + 16 * (lane >> 5);  // requires d == dpad
       if constexpr (DIRECT) dg.prime();
     }
     const f32x16 acc = DIRECT ? dg.run(arow) : gemm_ksplit_bf16x3<NT>(arow, a.planes, a.dpad, wave, lane, int(blockIdx.x));
     const int col = (wave % NT) * 32 + (lane & 31), ks = wave / NT;
-    if constexpr (XLDS) __syncthreads();   // the x tile is dead before partials overwrite it
+    if (XLDS && !a.parts_apart) __syncthreads();   // the x tile is dead before partials overwrite it
     {
       float* buf = lg + ks * kRouteBM * ldl;
 #pragma unroll
@@ -781,11 +801,29 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
       for (int o = tid; o < tsz; o += kRouteThreads) store_agent(mine + o, lg[o]);
       __shared__ int s_last;
       if (!last_workgroup(a.tile_tickets + tile, unsigned(a.kg), &s_last)) return;
-      for (int o = tid; o < tsz; o += kRouteThreads) {
-        float v = 0.f;
-        for (int q = 0; q < a.kg; ++q)
-          v += q == g ? lg[o] : load_agent(a.kpart + (int64_t(tile) * a.kg + q) * tsz + o);
-        lg[o] = v;
+      // every other group's elements of this thread loaded first (no serial round trips),
+      // then added in K-group order
+      constexpr int kBatch = 8;
+      for (int o0 = tid; o0 < tsz; o0 += kBatch * kRouteThreads) {
+        float w[kBatch][4];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int o = o0 + u * kRouteThreads;
+            w[u][q] = q < a.kg && q != g && o < tsz ? load_agent(a.kpart + (int64_t(tile) * a.kg + q) * tsz + o) : 0.f;
+          }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int o = o0 + u * kRouteThreads;
+          if (o < tsz) {
+            float v = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (q < a.kg) v += q == g ? lg[o] : w[u][q];
+            lg[o] = v;
+          }
+        }
       }
       __syncthreads();
     }
@@ -808,12 +846,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     if constexpr (MFMA) route_rows_half<NT>(lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
     else route_rows_half_nv(a.npad / 32, lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
     __syncthreads();
-    route_tail<true>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints,
+    route_tail<true>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints - lg_off,
                      tile, ntiles);
   } else {
     route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
     __syncthreads();
-    route_tail<false>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints,
+    route_tail<false>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints - lg_off,
                       tile, ntiles);
   }
 }
@@ -942,6 +980,7 @@ static void launch_fused(const RoutePlan& plan, const RouteArgs& a, dim3 g, size
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_t s) {
   RouteArgs a = a_in;
   a.lds_region_ints = route_region_ints(plan, a.n);
+  a.parts_apart = partials_apart(plan, a.n);
   if (plan.mfma && !a.planes_ready && !route_direct(plan, a.d, a.n)) {
     const hipError_t err = launch_router_prepare(plan, a.d, a.n, a.w_r, const_cast<uint16_t*>(a.planes), s);
     if (err != hipSuccess) return err;
