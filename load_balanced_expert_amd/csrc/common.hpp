@@ -34,6 +34,15 @@ constexpr int kTileTicketsOff = 1024;   // bytes: per-token-tile tickets of the 
 constexpr int kMaxKgTiles = 128;        // token tiles up to which the route splits K over workgroups
 inline uint32_t* ctl_ticket(void* ws, int which) { return static_cast<uint32_t*>(ws) + which; }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it does
+// not wait for the wave's global loads and stores, so loads issued before it
+// (a prefetch) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

@@ -123,8 +123,6 @@ constexpr int kFfnLdA = kFfnKA + 8;    // LDS row stride (bf16), 16 bytes of pad
 constexpr int kFfnLdB = 72;            // per-wave weight slab row stride (bf16): 64 + 16 bytes of padding
 constexpr int kFfnRing = 4;            // weight K steps in flight + 1 (even)
 
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 template <int W, int MT, bool RELU>   // W waves per workgroup, 32 output columns each
 __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                 uint16_t* __restrict__ C, uint16_t* As, uint16_t* Bs, int r0, int r_end, int K,

@@ -56,6 +56,7 @@ struct RouteArgs {
   int lds_region_ints;    // set by launch_route
   bool finish;            // false: store the chunk rows only (the dispatch finishes)
   int kg;                         // workgroups per token tile (RoutePlan::kg)
+  int rows_sub;                   // big-n epilogue: tokens per LDS sub-tile (set by launch_route)
   float* kpart;                   // kg > 1: [tiles][kg][32][npad] partial logits (workspace)
   uint32_t* tile_tickets;         // kg > 1: [tiles] (control region)
   int32_t* sup_counts;            // finish == false: per-super-chunk sums (atomics)

@@ -384,9 +384,10 @@ struct EpiArgs {
 // Logistic score; the reciprocal is the hardware one (within 1 ulp; 1 + e^-h >= 1).
 __device__ __forceinline__ float sigm(float h) { return __builtin_amdgcn_rcpf(1.0f + expf(-h)); }
 
-// Score of expert j for a token with softmax statistics (mx, sum).
+// Score of expert j for a token with softmax statistics (mx, sum); the softmax
+// exponential is the hardware exp2 of the scaled argument (about 1e-6 relative).
 __device__ __forceinline__ float score_of(int score, float h, float mx, float sum) {
-  return score == 0 ? expf(h - mx) / sum : sigm(h);
+  return score == 0 ? __expf(h - mx) / sum : sigm(h);
 }
 
 // Per-token selection for the `rows` tokens of one block, wave w taking
@@ -405,7 +406,7 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
       for (int j = lane; j < n; j += 64) mx = fmaxf(mx, row[j]);
       mx = wave_max(mx);
       float s = 0.f;
-      for (int j = lane; j < n; j += 64) s += expf(row[j] - mx);
+      for (int j = lane; j < n; j += 64) s += __expf(row[j] - mx);
       sum = wave_sum(s);
     }
     if (lane == 0) {
@@ -640,12 +641,29 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
 // last workgroup publishes the totals, the optional load statistics and the
 // capacity prefix sums.  SCORES: lg rows already hold the scores (fused
 // epilogue); otherwise they hold logits and the scores are recomputed.
+// Expert j's entry of this chunk's row: count and score sum.
+__device__ __forceinline__ void chunk_row_out(const RouteArgs& a, const EpiArgs& e, int chunk, int j, int count,
+                                              float acc) {
+  const int64_t row0 = int64_t(chunk) * e.n;
+  if (a.finish) {
+    store_agent(a.chunks + row0 + j, pack_chunk(count, acc));
+  } else {
+    // count rows [chunks][n] int32 for the next kernel, and this chunk's share
+    // of its super chunk's totals: integer adds, so their order does not matter
+    const int64_t so = int64_t(chunk / a.sup) * e.n + j;
+    reinterpret_cast<int32_t*>(a.chunks)[row0 + j] = count;
+    if (count) atomicAdd(a.sup_counts + so, count);
+    if (a.want_psum) atomicAdd(a.sup_psum + so, __float2ull_rn(acc * kPsumScale));
+  }
+}
+__device__ __forceinline__ void route_finish(const RouteArgs& a, const EpiArgs& e, int* scratch, int scratch_ints,
+                                             int nchunks);
+
 template <bool SCORES>
 __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows, const EpiArgs& e,
                                            const float* tok_mx, const float* tok_sum, const int* hist,
                                            const RouteArgs& a, int* scratch, int scratch_ints, int chunk,
                                            int nchunks) {
-  const int64_t row0 = int64_t(chunk) * e.n;
   for (int j = threadIdx.x; j < e.n; j += kRouteThreads) {
     float acc = 0.f;
     if (a.want_psum) {
@@ -659,17 +677,14 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
           if (tl0 + u < rows) acc += SCORES ? v[u] : score_of(e.score, v[u], tok_mx[tl0 + u], tok_sum[tl0 + u]);
       }
     }
-    if (a.finish) {
-      store_agent(a.chunks + row0 + j, pack_chunk(hist[j], acc));
-    } else {
-      // count rows [chunks][n] int32 for the next kernel, and this chunk's share
-      // of its super chunk's totals: integer adds, so their order does not matter
-      const int64_t so = int64_t(chunk / a.sup) * e.n + j;
-      reinterpret_cast<int32_t*>(a.chunks)[row0 + j] = hist[j];
-      if (hist[j]) atomicAdd(a.sup_counts + so, hist[j]);
-      if (a.want_psum) atomicAdd(a.sup_psum + so, __float2ull_rn(acc * kPsumScale));
-    }
+    chunk_row_out(a, e, chunk, j, hist[j], acc);
   }
+  route_finish(a, e, scratch, scratch_ints, nchunks);
+}
+
+// The workgroup that finishes last (stand-alone route) sums the chunk rows.
+__device__ __forceinline__ void route_finish(const RouteArgs& a, const EpiArgs& e, int* scratch, int scratch_ints,
+                                             int nchunks) {
   if (!a.finish) return;
   __shared__ int s_flag;
   if (!last_workgroup(a.done, unsigned(nchunks), &s_flag)) return;
@@ -929,22 +944,149 @@ __global__ __launch_bounds__(256) void k_route_logits_valu(RouteArgs a) {
   }
 }
 
-// big-n route epilogue: kRowsBM tokens per workgroup from the logits in global memory.
+// Top-1 softmax without bias (the Switch router) for n > 256: one wave per
+// token, lane l taking experts l + 64 u; a max reduction, a min
+// reduction over the lanes holding the maximum (the lowest such expert), and
+// the sum of the exponentials; the pick's score is exp(0) / sum.  Writes what
+// route_rows writes.
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = half_max(v);
+  return fmaxf(lane_value(v, 0), lane_value(v, 32));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = half_sum(v);
+  return lane_value(v, 0) + lane_value(v, 32);
+}
+__device__ __forceinline__ int wave_min_i_dpp(int v) {
+  v = half_min_i(v);
+  return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+}
+__device__ __forceinline__ void route_rows_top1(float* lg, int ld, int rows, int64_t t0, const EpiArgs& e,
+                                                int32_t* __restrict__ idx, float* __restrict__ gate_out,
+                                                float* tok_mx, float* tok_sum, int* hist) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nv = ld / 64;   // ld = npad, a multiple of 128: every lane reads nv in-row values
+  for (int tl = wave; tl < rows; tl += kRouteThreads / 64) {
+    float* row = lg + tl * ld;
+    // three passes over the LDS row (padded experts hold -inf in the tile, so
+    // nothing is masked; few registers: the prefetch of the next sub-tile stays live):
+    // maximum, lowest expert holding it, then the exponentials, which replace
+    // the logits in the row for the score column sums
+    float mx = -INFINITY;
+#pragma unroll 8
+    for (int u = 0; u < nv; ++u) mx = fmaxf(mx, row[lane + 64 * u]);
+    mx = wave_max_dpp(mx);
+    int cand = 0x7FFFFFFF;
+#pragma unroll 8
+    for (int u = 0; u < nv; ++u) cand = min(cand, row[lane + 64 * u] == mx ? lane + 64 * u : 0x7FFFFFFF);
+    const int bj = wave_min_i_dpp(cand);
+    float s = 0.f;
+#pragma unroll 8
+    for (int u = 0; u < nv; ++u) {
+      const float ex = __expf(row[lane + 64 * u] - mx);
+      row[lane + 64 * u] = ex;
+      s += ex;
+    }
+    const float sum = wave_sum_dpp(s);
+    if (lane == 0) {
+      tok_mx[tl] = mx;
+      tok_sum[tl] = sum;
+      if (bj < e.n) atomicAdd(&hist[bj], 1);   // out of range only for a row without a finite maximum
+      idx[t0 + tl] = bj;
+      gate_out[t0 + tl] = e.gate == 1 ? 1.0f : __builtin_amdgcn_rcpf(sum);   // sum >= 1
+    }
+  }
+}
+
+// big-n route epilogue: kRowsBM tokens per workgroup (one chunk) from the
+// logits in global memory, read once: sub-tiles of `rows_sub` tokens are staged
+// in LDS (the next one loaded into registers while the current one is routed),
+// each routed one wave per token, then its scores added into per-thread
+// column sums in token order.  The barriers order LDS only, so the prefetch
+// stays in flight while a sub-tile is routed.  NV = logits per lane of the top-1 path (npad <= 64 NV).
+constexpr int kRowsLdsFloats = 32768;   // LDS floats for a staged sub-tile (128 KiB)
+constexpr int kRowsMaxSub = 16;
+constexpr int kRowsLoadItems = 8;       // 16-byte loads per thread and sub-tile (at most)
+template <int NV>
 __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
+  constexpr int NQ = NV * 64 > kRouteThreads ? NV * 64 / kRouteThreads : 1;   // experts per thread
   extern __shared__ int lds_i[];
-  __shared__ float tok_mx[kRowsBM], tok_sum[kRowsBM];
-  int* hist = lds_i;                                  // [npad]
-  int* scratch = hist + a.npad;                       // [lds_region_ints]
+  __shared__ float tok_mx[kRowsMaxSub], tok_sum[kRowsMaxSub], tok_inv[kRowsMaxSub];
+  int* hist = lds_i;                                             // [npad]
+  float* tile = reinterpret_cast<float*>(lds_i + a.npad);        // [rows_sub][npad]
+  int* scratch = lds_i + a.npad;                                 // finishing scratch, after the last sub-tile
+  const int tid = threadIdx.x, npad = a.npad, sub = a.rows_sub;
   const int64_t t0 = int64_t(blockIdx.x) * kRowsBM;
   const int rows = int(min<int64_t>(kRowsBM, a.m - t0));
-  for (int j = threadIdx.x; j < a.npad; j += kRouteThreads) hist[j] = 0;
-  __syncthreads();
-  const float* lg = a.logits + t0 * a.npad;
+  const int nsub = (rows + sub - 1) / sub;
+  const int vpr = npad / 4, items = sub * vpr;                   // 16-byte items per sub-tile
+  const f32x4* lg4 = reinterpret_cast<const f32x4*>(a.logits + t0 * npad);
+  for (int j = tid; j < npad; j += kRouteThreads) hist[j] = 0;
   EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
-  route_rows(lg, a.npad, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
-  __syncthreads();
-  route_tail<false>(lg, a.npad, rows, e, tok_mx, tok_sum, hist, a, scratch, a.lds_region_ints, int(blockIdx.x),
-                    int(gridDim.x));
+  f32x4 v[kRowsLoadItems];
+  auto load = [&](int s) {
+#pragma unroll
+    for (int u = 0; u < kRowsLoadItems; ++u) {
+      const int i = tid + u * kRouteThreads;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < items && s * sub + i / vpr < rows) v[u] = lg4[int64_t(s) * items + i];
+    }
+  };
+  float acc[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) acc[q] = 0.f;
+  load(0);
+  for (int s = 0; s < nsub; ++s) {
+    lds_barrier();   // the previous sub-tile is read (and hist zeroed)
+#pragma unroll
+    for (int u = 0; u < kRowsLoadItems; ++u) {
+      const int i = tid + u * kRouteThreads;
+      if (i < items) {
+        if (a.n < npad) {   // padded experts become -inf in the LDS tile
+          const int c = (i % vpr) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (c + q >= a.n) v[u][q] = -INFINITY;
+        }
+        reinterpret_cast<f32x4*>(tile)[i] = v[u];
+      }
+    }
+    lds_barrier();
+    if (s + 1 < nsub) load(s + 1);
+    const int r = min(sub, rows - s * sub);
+    const bool top1 = e.k == 1 && e.score == 0 && !e.bias;
+    if (top1)
+      route_rows_top1(tile, npad, r, t0 + int64_t(s) * sub, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
+    else
+      route_rows(tile, npad, r, t0 + int64_t(s) * sub, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
+    lds_barrier();
+    if (a.want_psum) {
+      if (tid < r) tok_inv[tid] = 1.0f / tok_sum[tid];
+      lds_barrier();
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int j = tid + q * kRouteThreads;
+        if (j < a.n) {
+          if (top1)   // the row holds exp(h - max) already
+            for (int tl = 0; tl < r; ++tl) acc[q] += tile[tl * npad + j] * tok_inv[tl];
+          else if (e.score == 0)
+            for (int tl = 0; tl < r; ++tl) acc[q] += __expf(tile[tl * npad + j] - tok_mx[tl]) * tok_inv[tl];
+          else
+            for (int tl = 0; tl < r; ++tl) acc[q] += sigm(tile[tl * npad + j]);
+        }
+      }
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int j = tid + q * kRouteThreads;
+    if (j < a.n) chunk_row_out(a, e, int(blockIdx.x), j, hist[j], acc[q]);
+  }
+  route_finish(a, e, scratch, a.lds_region_ints, int(gridDim.x));
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1005,8 +1147,19 @@ hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_
       hipLaunchKernelGGL(k_route_logits_mfma, dim3(unsigned(ceil_div64(a.m, 128)), plan.npad / 128), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(k_route_logits_valu, dim3(unsigned(ceil_div64(a.m, 32)), plan.npad / 64), dim3(256), 0, s, a);
+    // sub-tiles of the logits staged in LDS; the finishing scratch reuses that region
+    a.rows_sub = std::min(kRowsMaxSub, kRowsLdsFloats / plan.npad);
+    a.lds_region_ints = std::max(a.lds_region_ints, a.rows_sub * plan.npad);
     const size_t lds = (size_t(plan.npad) + a.lds_region_ints) * sizeof(int);
-    hipLaunchKernelGGL(k_route_rows, dim3(unsigned(ceil_div64(a.m, kRowsBM))), dim3(kRouteThreads), lds, s, a);
+    const dim3 g(unsigned(ceil_div64(a.m, kRowsBM)));
+    if (plan.npad <= 512)
+      hipLaunchKernelGGL(k_route_rows<8>, g, dim3(kRouteThreads), lds, s, a);
+    else if (plan.npad <= 1024)
+      hipLaunchKernelGGL(k_route_rows<16>, g, dim3(kRouteThreads), lds, s, a);
+    else if (plan.npad <= 2048)
+      hipLaunchKernelGGL(k_route_rows<32>, g, dim3(kRouteThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL(k_route_rows<64>, g, dim3(kRouteThreads), lds, s, a);
   }
   return hipGetLastError();
 }

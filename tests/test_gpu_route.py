@@ -54,6 +54,19 @@ def test_switch_base_full():
     check_route(inp.x, inp.w_r, 1, "switch-base T=8192 d=768 N=128")
 
 
+@pytest.mark.parametrize("T,d,n,k,score", [(1000, 800, 128, 1, "softmax"), (3000, 800, 128, 2, "softmax"),
+                                          (2500, 2080, 256, 8, "sigmoid")])
+def test_k_split_uneven_ranges(T, d, n, k, score):
+    # few token tiles: each tile's K range is split over 2 or 4 workgroups; d / 32 K blocks that do
+    # not divide evenly give ranges of two sizes, each staged in LDS at its own width
+    spec = W.SwitchSpec("ksplit", T=T, d=d, N=n, w_r_std=0.1 / np.sqrt(d))
+    inp = W.switch_inputs(spec, 7)
+    bias = None
+    if score == "sigmoid":
+        bias = np.random.default_rng(7).normal(0.0, 0.01, n).astype(np.float32)
+    check_route(inp.x, inp.w_r, k, f"K split, d={d} n={n} T={T}", score=score, bias=bias)
+
+
 def test_padded_expert_count_and_odd_tokens():
     spec = W.SwitchSpec("odd", T=333, d=96, N=40, w_r_std=0.05)
     inp = W.switch_inputs(spec, 3)
@@ -130,6 +143,15 @@ def test_large_expert_count_path():
     spec = W.SwitchSpec("bign", T=777, d=256, N=600, w_r_std=0.05)
     inp = W.switch_inputs(spec, 7)
     check_route(inp.x, inp.w_r, 2, "N=600 (logits GEMM + row kernel)")
+
+
+@pytest.mark.parametrize("T,d,n,gate", [(1000, 256, 1000, "prob"), (700, 128, 3000, "prob"), (530, 96, 520, "renorm")])
+def test_large_expert_count_top1(T, d, n, gate):
+    # top-1 softmax without bias on the big-n path: LDS sub-tiles of 32768 / npad tokens (10 at
+    # n = 3000, so the last sub-tile of a workgroup is short), padded experts masked in the tile
+    spec = W.SwitchSpec("bign1", T=T, d=d, N=n, w_r_std=0.05)
+    inp = W.switch_inputs(spec, 9)
+    check_route(inp.x, inp.w_r, 1, f"N={n} top-1 (logits GEMM + row kernel)", gate=gate)
 
 
 def test_large_expert_count_fp32():
