@@ -102,7 +102,8 @@ def test_softmax_with_bias():
     check_route(inp.x, inp.w_r, 2, "softmax + bias (key = p + b)", bias=bias)
 
 
-@pytest.mark.parametrize("k,score,bias", [(32, "softmax", False), (40, "softmax", False), (33, "sigmoid", True)])
+@pytest.mark.parametrize("k,score,bias", [(32, "softmax", False), (40, "softmax", False), (33, "sigmoid", True),
+                                          (64, "softmax", True)])
 def test_many_picks(k, score, bias):
     # k = 32 is the largest pick count of the half-wave epilogue; larger k takes the wave-per-token one
     spec = W.SwitchSpec("manyk", T=300, d=64, N=64, w_r_std=0.1)
