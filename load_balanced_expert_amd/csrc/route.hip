@@ -591,9 +591,10 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
 #pragma unroll
       for (int u = 0; u < NV; ++u) sc[u] = l + 32 * u < e.n ? sigm(h[u]) : 0.f;
     }
-    // k rounds: each picks the best (key, j) strictly after the previous pick
-    float last_key = INFINITY;
-    int last_j = -1, my_j = 0;
+    // k rounds: each picks the best (key, j) not picked yet (bit u of `taken`
+    // marks this lane's expert l + 32 u as picked)
+    uint32_t taken = 0;
+    int my_j = 0;
     float my_score = 0.f, total = 0.f;
     for (int r = 0; r < e.k; ++r) {
       float bk = -INFINITY;
@@ -601,17 +602,16 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
         const int j = l + 32 * u;
-        if (j < e.n) {
+        if (j < e.n && !((taken >> u) & 1u)) {
           const float key = e.bias ? sc[u] + bv[u] : h[u];
-          if (better(last_key, last_j, key, j) && better(key, j, bk, bj)) {
+          if (better(key, j, bk, bj)) {
             bk = key;
             bj = j;
           }
         }
       }
       half_argbest(bk, bj);
-      last_key = bk;
-      last_j = bj;
+      if ((bj & 31) == l) taken |= 1u << (bj >> 5);
       // the chosen expert's score, from the lane that holds it
       float mine = 0.f;
 #pragma unroll
