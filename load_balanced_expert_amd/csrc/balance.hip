@@ -186,6 +186,45 @@ __device__ __forceinline__ double key_f64(uint64_t k) {
 __device__ __forceinline__ bool better64(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
+// Wave-wide minima without the LDS crossbar: DPP within 16-lane rows (xor 1, xor 2,
+// the mirrored quad, the mirrored row), the other row of the half
+// (v_permlane16_swap), then the two halves (lanes 0 and 32 read as scalars).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return (uint64_t(dpp32<CTRL>(uint32_t(v >> 32))) << 32) | dpp32<CTRL>(uint32_t(v));
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  uint64_t o = dpp64<0xB1>(v);
+  v = o < v ? o : v;
+  o = dpp64<0x4E>(v);
+  v = o < v ? o : v;
+  o = dpp64<0x141>(v);
+  v = o < v ? o : v;
+  o = dpp64<0x140>(v);
+  v = o < v ? o : v;
+  const auto lo = __builtin_amdgcn_permlane16_swap(uint32_t(v), uint32_t(v), false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(uint32_t(v >> 32), uint32_t(v >> 32), false, false);
+  const uint64_t p = (uint64_t(hi[0]) << 32) | lo[0], q = (uint64_t(hi[1]) << 32) | lo[1];
+  v = p < q ? p : q;
+  const uint64_t a = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 0))) << 32) |
+                     uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 0));
+  const uint64_t b = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 32))) << 32) |
+                     uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 32));
+  return a < b ? a : b;
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, int(dpp32<0xB1>(uint32_t(v))));
+  v = min(v, int(dpp32<0x4E>(uint32_t(v))));
+  v = min(v, int(dpp32<0x141>(uint32_t(v))));
+  v = min(v, int(dpp32<0x140>(uint32_t(v))));
+  const auto r = __builtin_amdgcn_permlane16_swap(uint32_t(v), uint32_t(v), false, false);
+  v = min(int(r[0]), int(r[1]));
+  return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+}
 __device__ __forceinline__ void wave_argbest64(double& key, int& ix) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -334,21 +373,30 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
       bool done = lane >= n;
       int target = -1;
       double D = 0.0;
+      // potentials and counts in registers; expert u's read back with readlane
+      const double pil = lane < n ? pi[lane] : 0.0;
+      const int cntl = lane < n ? cnt[lane] : 0;
       for (int it = 0; it < n; ++it) {
-        double bk = done ? -INFINITY : -dv;   // arg-best of -dist == arg-min of dist
-        int bj = done ? 0x7FFFFFFF : lane;
-        wave_argbest64(bk, bj);
-        if (bj == 0x7FFFFFFF || bk == -INFINITY) break;
-        const int u = bj;
-        const double du = -bk;
+        // the unfinished expert of least distance, the lower index on ties
+        // (dist >= 0, so its order-preserving key orders like the distance)
+        const uint64_t dk = done ? ~0ull : f64_key(dv);
+        const uint64_t mk = wave_min_u64(dk);
+        if (mk == ~0ull) break;
+        const double du = key_f64(mk);
+        if (du == INFINITY) break;
+        const int u = wave_min_i32(dk == mk ? lane : 64);
         if (lane == u) done = true;
-        if (cnt[u] < q) {
+        if (__builtin_amdgcn_readlane(cntl, u) < q) {
           target = u;
           D = du;
           break;
         }
         if (!done) {
-          double w = key_f64(Mk[u * n + lane]) - pi[u] + pi[lane];
+          const uint64_t pb = uint64_t(__double_as_longlong(pil));
+          const double piu = __longlong_as_double(
+              int64_t((uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(pb >> 32)), u))) << 32) |
+                      uint32_t(__builtin_amdgcn_readlane(int(uint32_t(pb)), u))));
+          double w = key_f64(Mk[u * n + lane]) - piu + pil;
           w = fmax(w, 0.0);
           const double nd = du + w;
           if (nd < dv) {
