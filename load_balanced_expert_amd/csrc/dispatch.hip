@@ -197,7 +197,7 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, Pref
 
 template <typename V, bool SELF>
 __global__ __launch_bounds__(kDispThreads) void k_disp_rank_copy(DispatchArgs a) {
-  extern __shared__ int lds[];
+  extern __shared__ __attribute__((aligned(16))) int lds[];
   const int n = a.n;
   const int cp = a.chunk_tokens * a.k;          // pairs per chunk
   int* cnt = lds;                                // [n] running counts inside the chunk

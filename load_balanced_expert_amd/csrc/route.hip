@@ -728,7 +728,7 @@ __device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
 // scratch.  The histogram follows the region.
 template <int NT, bool MFMA, bool XLDS, bool DIRECT>
 __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];   // 16-byte LDS vectors need a 16-byte base
   __shared__ float tok_mx[kRouteBM], tok_sum[kRouteBM];   // softmax statistics (k > 32 epilogue)
   const int ldl = a.npad + 8;   // logit and partial tile row stride
   // the staged x tile holds one workgroup's K range: xcols columns, row stride xcols + 8
@@ -1013,7 +1013,7 @@ constexpr int kRowsLoadItems = 8;       // 16-byte loads per thread and sub-tile
 template <int NV>
 __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
   constexpr int NQ = NV * 64 > kRouteThreads ? NV * 64 / kRouteThreads : 1;   // experts per thread
-  extern __shared__ int lds_i[];
+  extern __shared__ __attribute__((aligned(16))) int lds_i[];   // 16-byte LDS vectors need a 16-byte base
   __shared__ float tok_mx[kRowsMaxSub], tok_sum[kRowsMaxSub], tok_inv[kRowsMaxSub];
   int* hist = lds_i;                                             // [npad]
   float* tile = reinterpret_cast<float*>(lds_i + a.npad);        // [rows_sub][npad]
