@@ -193,6 +193,15 @@ def test_switch_base_layer_identity_ragged():
     _layer_check(W.SWITCH_BASE.scaled(T=1234, d_ff=None), 1, 1.25, ffn=False)
 
 
+@pytest.mark.parametrize("T,n,k,cf", [(5000, 200, 2, 1.1), (20000, 256, 1, 1.25)])
+def test_layer_uneven_slices(T, n, k, cf):
+    # the dispatch spreads each expert's slot-base sources over 1024 / n threads: n = 200 leaves
+    # threads idle, and T = 20000 (625 chunks, 40 per super chunk) at n = 256 has more sources per
+    # thread than its first batch of loads holds
+    spec = W.SwitchSpec("uneven", T=T, d=128, N=n, w_r_std=0.05)
+    _layer_check(spec, 5, cf, ffn=False, k=k)
+
+
 def test_layer_large_batch():
     _layer_check(W.SWITCH_BASE.scaled(T=12000, d_ff=None), 2, 1.0, ffn=False)
 
