@@ -17,10 +17,13 @@
 //    meet in LDS in a fixed order, and the epilogue (softmax statistics,
 //    top-k, gates, histogram, per-expert score sums) runs in the same kernel.
 //  * n > 256: a tiled MFMA GEMM writes fp32 logits to the workspace, then a
-//    row kernel runs the same epilogue from global memory.
+//    row kernel reads them once through LDS sub-tiles and runs the same
+//    epilogue (one wave per token).
 //  * Each workgroup stores its per-expert counts and score sums as a chunk
 //    row; the workgroup that finishes last sums the rows in a fixed order
-//    (prefix.hpp), so every output is bit-reproducible.
+//    (prefix.hpp), so every output is bit-reproducible.  In the Switch layer
+//    the route stops after its chunk rows and per-super-chunk sums, and the
+//    dispatch derives the rest.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prefix.hpp"
@@ -32,11 +35,13 @@ constexpr int kRowsBM = 256;      // tokens per route-epilogue workgroup (n > 25
 constexpr int kRouteThreads = 1024;  // 16 waves
 
 // LDS ints of the region each route kernel reserves.  Fused: the x tile (if
-// staged, at most 60 KiB) and, once the product is done, the partial logit
-// tiles [KS][32][npad + 8] (one per K group; the first becomes the logits
-// tile), which share one region; the last workgroup's finishing scratch
-// reuses it.  Rows kernel: the scratch.  The padding of 8 columns puts the
-// two lane halves of an accumulator store on different banks.
+// staged, at most 128 KiB: the workgroup's K range of 32 rows) and the partial
+// logit tiles [KS][32][npad + 8] (one per K group; the first becomes the
+// logits tile), which either follow the x tile or, when both do not fit,
+// reuse its region once the product is done; the last workgroup's finishing
+// scratch reuses the tiles.  Rows kernel: the logit sub-tiles, then the
+// scratch.  The padding of 8 columns puts the two lane halves of an
+// accumulator store on different banks.
 constexpr int kXStageMaxInts = 32768;
 static int fused_parts(const RoutePlan& plan) {
   const int nt = plan.npad / 32;
@@ -391,7 +396,7 @@ __device__ __forceinline__ float score_of(int score, float h, float mx, float su
 }
 
 // Per-token selection for the `rows` tokens of one block, wave w taking
-// tokens w, w+4, ...; writes idx/gate, per-token softmax statistics to
+// tokens w, w+16, ...; writes idx/gate, per-token softmax statistics to
 // tok_mx/tok_sum (shared) and counts selections into hist (shared).
 __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows, int64_t t0,
                                            const EpiArgs& e, int32_t* __restrict__ idx,
