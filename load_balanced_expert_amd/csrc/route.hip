@@ -881,8 +881,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
 __global__ __launch_bounds__(256) void k_route_logits_mfma(RouteArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
-  const int64_t tb = int64_t(blockIdx.x) * 128 + 64 * wm;
-  const int jb = blockIdx.y * 128 + 64 * wn;
+  // expert tiles fastest: the tiles of one token block run together (its x rows read once)
+  const int64_t tb = int64_t(blockIdx.y) * 128 + 64 * wm;
+  const int jb = blockIdx.x * 128 + 64 * wn;
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* xr[2];
 #pragma unroll
@@ -1149,7 +1150,7 @@ hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_
       launch_fused<8>(plan, a, g, lds, s);
   } else {
     if (plan.mfma)
-      hipLaunchKernelGGL(k_route_logits_mfma, dim3(unsigned(ceil_div64(a.m, 128)), plan.npad / 128), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_route_logits_mfma, dim3(plan.npad / 128, unsigned(ceil_div64(a.m, 128))), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(k_route_logits_valu, dim3(unsigned(ceil_div64(a.m, 32)), plan.npad / 64), dim3(256), 0, s, a);
     // sub-tiles of the logits staged in LDS; the finishing scratch reuses that region
