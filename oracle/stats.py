@@ -9,7 +9,11 @@ Follows
   the fraction of tokens that selected expert i (a reading; the page is top-1).
 * [Qwen global] "글로벌-배치 로드 밸런스 구현": f_i is gathered over the whole
   global batch (all micro-batches), the loss is then formed per micro-batch
-  with that global f, and the per-micro-batch losses are averaged.
+  with that global f, and the per-micro-batch losses are averaged.  The same
+  page's hybrid ("효율성과 효과성의 균형"): the micro-batch balance loss
+  (the Switch loss of each micro-batch on its own f) is added to the global
+  one with a constant weight (0.01 on the page); read as
+  L_hybrid^(t) = L_global^(t) + w · L_micro^(t), averaged like the global one.
 * [MoE tour 6] "방법 회고" eq. (2): b ← b − γ·sign(F − 1/n), F = observed load
   share; applied after routing with the old b ("함정에 주의").  The bias is fp32
   state, so this update is computed in fp32: F_j − 1/n has the sign of
@@ -52,11 +56,14 @@ class GlobalBatch:
         if self.counts is None:
             self.counts = np.zeros(self.n, dtype=np.int64)
 
+    micro_f: List[np.ndarray] = field(default_factory=list)
+
     def add(self, c: np.ndarray, m: int, prob_sum: np.ndarray = None):
         self.counts = self.counts + np.asarray(c, dtype=np.int64)
         self.tokens += int(m)
         if prob_sum is not None:
             self.prob_means.append(np.asarray(prob_sum, dtype=np.float64) / m)
+            self.micro_f.append(np.asarray(c, dtype=np.float64) / m)
 
     def f(self) -> np.ndarray:
         return self.counts.astype(np.float64) / self.tokens
@@ -68,6 +75,17 @@ class GlobalBatch:
 
     def loss(self, alpha: float) -> float:
         return float(np.mean(self.losses(alpha)))
+
+    def micro_losses(self, alpha: float) -> np.ndarray:
+        """The Switch loss of each micro-batch with its own f: α·N·Σ_i f_i^(t) · P_i^(t)."""
+        return np.array([alpha * self.n * float(np.sum(f * P)) for f, P in zip(self.micro_f, self.prob_means)])
+
+    def hybrid_losses(self, alpha: float, weight: float) -> np.ndarray:
+        """L_global^(t) + weight · L_micro^(t) for each micro-batch t."""
+        return self.losses(alpha) + weight * self.micro_losses(alpha)
+
+    def hybrid_loss(self, alpha: float, weight: float) -> float:
+        return float(np.mean(self.hybrid_losses(alpha, weight)))
 
 
 def lossfree_update(bias: np.ndarray, c: np.ndarray, m: int, k: int, gamma: float) -> np.ndarray:

@@ -84,6 +84,24 @@ def test_global_batch_differs_from_micro_when_domains_skew():
     assert np.mean(micro) == pytest.approx(0.015)
 
 
+def test_hybrid_loss_closed_forms():
+    """Hybrid = global + w·micro: on the skewed pair above each micro loss is 0.015
+    (each micro-batch loads one expert, whose P is 0.75), the global ones 0.01; one
+    micro-batch alone has L_global = L_micro = the Switch loss, so hybrid = (1 + w)·aux."""
+    gb = S.GlobalBatch(2)
+    gb.add(np.array([4, 0]), 4, np.array([3.0, 1.0]))
+    gb.add(np.array([0, 4]), 4, np.array([1.0, 3.0]))
+    np.testing.assert_allclose(gb.micro_losses(1e-2), [0.015, 0.015], rtol=1e-14)   # 0.01·2·(1·0.75)
+    np.testing.assert_allclose(gb.hybrid_losses(1e-2, 0.01), [0.01 + 0.01 * 0.015] * 2, rtol=1e-14)
+    inp = W.switch_inputs(W.TINY_SWITCH, 6)
+    rt = R.route(inp.x, inp.w_r, 1)
+    one = S.GlobalBatch(8)
+    one.add(rt.counts, 1024, rt.prob_sum)
+    aux = S.switch_stats(rt.counts, rt.prob_sum, 1024, 1e-2)[2]
+    assert one.hybrid_loss(1e-2, 0.01) == pytest.approx(1.01 * aux, rel=1e-13)
+    assert one.hybrid_loss(1e-2, 0.0) == pytest.approx(aux, rel=1e-14)
+
+
 def test_lossfree_update_signs_and_fp32_rounding():
     b = np.array([1.0, 0.0, -0.25, 3.0], np.float32)
     c = np.array([9, 8, 7, 8])                            # m*k/n = 8 per expert
