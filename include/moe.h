@@ -171,11 +171,18 @@ moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, con
  * 밸런스 구현": synchronise f over the global batch, form each micro-batch's loss
  * with it, aggregate).  f^g_j = global_counts_j / global_tokens;
  * losses[t] = α · n · Σ_j f^g_j · P[t, j]; loss_mean = mean_t losses[t].
+ * Hybrid ([Qwen global] "효율성과 효과성의 균형": the micro-batch balance loss
+ * added with a constant weight, 0.01 on the page): hybrid[t] = losses[t] +
+ * micro_weight · micro_aux[t], hybrid_mean = mean_t hybrid[t], where micro_aux[t]
+ * is micro-batch t's own Switch loss (moe_stats' aux).  Sums in fp64.
  * P [nb, n] fp32 (each row a micro-batch's P); f_global [n], losses [nb],
- * loss_mean [1] fp32 out (each may be NULL). */
+ * loss_mean [1] fp32 out (each may be NULL); micro_aux [nb] fp32 in, needed
+ * only for hybrid [nb] / hybrid_mean [1] fp32 out (each may be NULL). */
 moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t* global_tokens,
                           const float* P, int32_t nb, float alpha,
-                          float* f_global, float* losses, float* loss_mean, void* stream);
+                          float* f_global, float* losses, float* loss_mean,
+                          const float* micro_aux, float micro_weight, float* hybrid, float* hybrid_mean,
+                          void* stream);
 
 /* ------------------------------------------------------------------ balanced assignment */
 

@@ -46,7 +46,7 @@ SIGNATURES = {
     "moe_router_prepare": (c_int32, [c_int32, c_int32, _P, _P, _P]),
     "moe_route": (c_int32, [POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_stats": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_float, _P, _P, _P, _P, _P, _P, c_float, _P]),
-    "moe_global_aux": (c_int32, [c_int32, _P, _P, _P, c_int32, c_float, _P, _P, _P, _P]),
+    "moe_global_aux": (c_int32, [c_int32, _P, _P, _P, c_int32, c_float, _P, _P, _P, _P, c_float, _P, _P, _P]),
     "moe_balance_duals": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_int32, c_int32, c_int32,
                                     _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_dispatch": (c_int32, [POINTER(MoeShape), c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),

@@ -170,8 +170,26 @@ def global_aux(global_counts: torch.Tensor, global_tokens: torch.Tensor, P_rows:
     losses = torch.empty(max(nb, 1), dtype=torch.float32, device=dev)
     mean = torch.empty(1, dtype=torch.float32, device=dev)
     _check(_lib().moe_global_aux(int(n), _ptr(global_counts), _ptr(global_tokens), _ptr(P_rows), int(nb),
-                                 float(alpha), _ptr(fg), _ptr(losses), _ptr(mean), _stream(dev)), "moe_global_aux")
+                                 float(alpha), _ptr(fg), _ptr(losses), _ptr(mean), None, 0.0, None, None,
+                                 _stream(dev)), "moe_global_aux")
     return fg, losses[:nb], mean
+
+
+def global_aux_hybrid(global_counts: torch.Tensor, global_tokens: torch.Tensor, P_rows: torch.Tensor,
+                      micro_aux: torch.Tensor, alpha: float = 1e-2, weight: float = 1e-2):
+    """(global losses [nb], hybrid losses [nb], hybrid mean [1]): each micro-batch's global-batch
+    loss plus `weight` times its own Switch loss (micro_aux[t], as moe_stats returns it)."""
+    _on_device(global_counts, global_tokens, P_rows, micro_aux)
+    n = global_counts.shape[0]
+    nb = P_rows.shape[0]
+    dev = global_counts.device
+    losses = torch.empty(max(nb, 1), dtype=torch.float32, device=dev)
+    hybrid = torch.empty(max(nb, 1), dtype=torch.float32, device=dev)
+    hmean = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(_lib().moe_global_aux(int(n), _ptr(global_counts), _ptr(global_tokens), _ptr(P_rows), int(nb),
+                                 float(alpha), None, _ptr(losses), None, _ptr(micro_aux), float(weight),
+                                 _ptr(hybrid), _ptr(hmean), _stream(dev)), "moe_global_aux")
+    return losses[:nb], hybrid[:nb], hmean
 
 
 # ------------------------------------------------------------------ balanced assignment

@@ -278,11 +278,15 @@ moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, con
 }
 
 moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t* global_tokens, const float* P,
-                          int32_t nb, float alpha, float* f_global, float* losses, float* loss_mean, void* stream) {
+                          int32_t nb, float alpha, float* f_global, float* losses, float* loss_mean,
+                          const float* micro_aux, float micro_weight, float* hybrid, float* hybrid_mean,
+                          void* stream) {
   if (n < 1 || nb < 0 || !global_counts || !global_tokens) return MOE_ERR_INVALID_ARG;
   if (nb > 0 && !P) return MOE_ERR_INVALID_ARG;
+  if (nb > 0 && (hybrid || hybrid_mean) && !micro_aux) return MOE_ERR_INVALID_ARG;
   if (n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_global_aux(n, global_counts, global_tokens, P, nb, alpha, f_global, losses, loss_mean,
+                                      micro_aux, micro_weight, hybrid, hybrid_mean,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -75,6 +75,7 @@ hipError_t launch_stats(int64_t m, int n, int k, const int32_t* counts, const fl
                         int64_t* gtokens, float* bias, float gamma, hipStream_t s);
 hipError_t launch_global_aux(int n, const int64_t* gcounts, const int64_t* gtokens, const float* P,
                              int nb, float alpha, float* fg, float* losses, float* loss_mean,
+                             const float* micro_aux, float micro_weight, float* hybrid, float* hybrid_mean,
                              hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch

@@ -148,8 +148,10 @@ def test_stats_validation(lib):
     # aux requested without prob_sum
     assert lib.moe_stats(8, 8, 1, FAKE, None, 0.01, None, None, FAKE, None, None, None, 0.001, None) == 1
     assert lib.moe_stats(8, 5000, 1, FAKE, None, 0.01, None, None, None, None, None, None, 0.001, None) == 2
-    assert lib.moe_global_aux(8, None, FAKE, FAKE, 1, 0.01, None, None, None, None) == 1
-    assert lib.moe_global_aux(8, FAKE, FAKE, None, 2, 0.01, None, None, None, None) == 1
+    assert lib.moe_global_aux(8, None, FAKE, FAKE, 1, 0.01, None, None, None, None, 0.0, None, None, None) == 1
+    assert lib.moe_global_aux(8, FAKE, FAKE, None, 2, 0.01, None, None, None, None, 0.0, None, None, None) == 1
+    # a hybrid output needs the micro-batch losses
+    assert lib.moe_global_aux(8, FAKE, FAKE, FAKE, 2, 0.01, None, None, None, None, 0.01, FAKE, None, None) == 1
 
 
 def test_balance_validation(lib):

@@ -130,6 +130,32 @@ def test_global_aux():
     assert_rel(to_host(mean), [gb.loss(1e-2)], 1e-5, "global loss")
 
 
+def test_global_aux_hybrid():
+    # the global-batch loss plus 0.01 times each micro-batch's own Switch loss, the micro-batch
+    # losses taken from moe_stats on the GPU (counts and score sums of each micro-batch)
+    n, nb, m = 64, 8, 2048
+    rng = np.random.default_rng(2)
+    gb = OS.GlobalBatch(n)
+    micro_gpu, P_rows = [], []
+    for t in range(nb):
+        c = rng.multinomial(m, rng.dirichlet(np.full(n, 0.5))).astype(np.int32)
+        ps = (rng.dirichlet(np.ones(n)) * m).astype(np.float32)
+        gb.add(c, m, ps.astype(np.float64))
+        st = M.stats(m, 1, to_dev(c), to_dev(ps), alpha=1e-2)
+        micro_gpu.append(st.aux)
+        P_rows.append(to_host(st.P))
+    P_rows = np.stack(P_rows)
+    gb.prob_means = [p.astype(np.float64) for p in P_rows]   # the P rows the kernel sees (fp32)
+    micro = torch.cat(micro_gpu)
+    losses, hybrid, hmean = M.global_aux_hybrid(to_dev(gb.counts), to_dev(np.array([gb.tokens], np.int64)),
+                                                to_dev(P_rows), micro, alpha=1e-2, weight=1e-2)
+    torch.cuda.synchronize()
+    assert_rel(to_host(losses), gb.losses(1e-2), 1e-5, "global losses")
+    assert_rel(to_host(micro), gb.micro_losses(1e-2), 1e-5, "micro-batch losses (moe_stats)")
+    assert_rel(to_host(hybrid), gb.hybrid_losses(1e-2, 1e-2), 1e-5, "hybrid losses")
+    assert_rel(to_host(hmean), [gb.hybrid_loss(1e-2, 1e-2)], 1e-5, "hybrid mean")
+
+
 # ------------------------------------------------------------------ whole layer
 def _layer_check(spec, seed, cf, ffn, k=1):
     inp = W.switch_inputs(spec, seed)
