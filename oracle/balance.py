@@ -21,7 +21,12 @@ Follows [MoE tour 6]:
 Precision: the Quantile-Balancing duals are exact order statistics of fp32
 differences (fl32(s − β), fl32(s − α)), so ``qb_*`` work in fp32 and are
 bit-reproducible.  ``qb_*`` take the exact order statistic of the algorithm
-box, not the linearly interpolated quantile of the page's demo code.
+box.  ``qb_*_quantile`` follow the page's demo code ("데모 코드") instead: the
+1 − k/n quantile of each row and of each column with linear interpolation
+between the two neighbouring order statistics (the same quantile on both
+axes, "교대 반복"), numpy's quantile on the fp32 differences (so in fp32
+arithmetic); ``bip`` adds the clip of α and β at 0 that the demo's comments
+attribute to BIP.
 
 Exact balance (reading): the alternating iteration stalls short of exact
 column counts on skewed scores, while the pages' target is exactly q per
@@ -83,6 +88,32 @@ def qb_online(s: np.ndarray, k: int, beta_old: np.ndarray):
     alpha = qb_alpha(s, beta_old, k)
     beta = qb_beta(s, alpha, q)
     return idx, beta, alpha
+
+
+# ------------------------------------------------------------------ QB, the demo's quantile form
+def qb_alpha_quantile(s: np.ndarray, beta: np.ndarray, k: int, bip: bool = False) -> np.ndarray:
+    n = s.shape[1]
+    v = (s.astype(np.float32) - beta.astype(np.float32)[None, :]).astype(np.float32)
+    a = np.quantile(v, 1 - k / n, axis=1).astype(np.float32)
+    return np.maximum(a, np.float32(0)) if bip else a
+
+
+def qb_beta_quantile(s: np.ndarray, alpha: np.ndarray, k: int, bip: bool = False) -> np.ndarray:
+    n = s.shape[1]
+    w = (s.astype(np.float32) - alpha.astype(np.float32)[:, None]).astype(np.float32)
+    b = np.quantile(w, 1 - k / n, axis=0).astype(np.float32)
+    return np.maximum(b, np.float32(0)) if bip else b
+
+
+def qb_solve_quantile(s: np.ndarray, k: int, iters: int, bip: bool = False, beta0: Optional[np.ndarray] = None):
+    """The demo's alternating quantiles, T = iters rounds from β = 0.  Returns (idx, beta, alpha)."""
+    m, n = s.shape
+    beta = np.zeros(n, np.float32) if beta0 is None else np.asarray(beta0, np.float32).copy()
+    alpha = np.zeros(m, np.float32)
+    for _ in range(iters):
+        alpha = qb_alpha_quantile(s, beta, k, bip)
+        beta = qb_beta_quantile(s, alpha, k, bip)
+    return topk_biased(s, beta, k), beta, alpha
 
 
 # ------------------------------------------------------------------ assignments

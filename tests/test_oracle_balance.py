@@ -150,6 +150,46 @@ def test_qb_improves_balance_on_demo_workload():
     assert after[0] < 0.25 * before[0] and after[2] < 0.25 * before[2]
 
 
+def test_qb_quantile_is_the_type7_sample_quantile():
+    """The demo's quantile on each axis is the order statistic at position (N − 1)(1 − k/n)
+    linearly interpolated with the next one: checked against np.interp over the sorted values
+    (float64), to fp32 rounding, and against the exact-mode neighbours it lies between."""
+    s = W.uniform_offset_scores(3008, 64, 3)   # m k / n = 188 whole, so the column bracket is (q+1)-th, q-th
+    k, n = 4, 64
+    beta = np.linspace(-0.2, 0.3, n).astype(np.float32)
+    a = B.qb_alpha_quantile(s, beta, k)
+    v = (s - beta[None, :]).astype(np.float32).astype(np.float64)
+    p = (n - 1) * (1 - k / n)
+    ref = np.array([np.interp(p, np.arange(n), np.sort(r)) for r in v])
+    np.testing.assert_allclose(a, ref, rtol=2e-7, atol=1e-7)
+    lo, hi = B.qb_alpha(s, beta, k), B.qb_alpha(s, beta, k - 1)     # (k+1)-th and k-th largest
+    assert np.all((a >= lo) & (a <= hi))
+    b = B.qb_beta_quantile(s, a, k)
+    w = (s - a[:, None]).astype(np.float32).astype(np.float64)
+    m, q = s.shape[0], s.shape[0] * k // n
+    pc = (m - 1) * (1 - k / n)
+    refc = np.array([np.interp(pc, np.arange(m), np.sort(w[:, j])) for j in range(n)])
+    np.testing.assert_allclose(b, refc, rtol=2e-7, atol=1e-7)
+    assert np.all((b >= B.qb_beta(s, a, q)) & (b <= B.qb_beta(s, a, q - 1)))
+
+
+def test_qb_quantile_balances_the_demo_workload_and_bip_clips():
+    """The demo itself at m = 100000, n = 256, k = 8, T = 5: the max and mean violation of the
+    biased top-k fall far below those of the plain top-k; the BIP clip keeps α, β >= 0 and
+    changes nothing where they are positive anyway."""
+    m, n, k = 100000, 256, 8
+    s = W.uniform_offset_scores(m, n, 0)
+    top = np.argsort(-s, axis=1)[:, :k]
+    before = S.max_min_avg_vio(np.bincount(top.ravel(), minlength=n))
+    idx, beta, alpha = B.qb_solve_quantile(s, k, 5)
+    after = S.max_min_avg_vio(np.bincount(idx.ravel(), minlength=n))
+    assert before[0] > 0.5 and after[0] < 0.05 * before[0] and after[2] < 0.05 * before[2]
+    _, bb, ab = B.qb_solve_quantile(s, k, 5, bip=True)
+    assert np.all(bb >= 0) and np.all(ab >= 0)
+    if np.all(alpha > 0) and np.all(beta > 0):
+        assert np.array_equal(bb, beta)
+
+
 @pytest.mark.slow
 def test_full_size_completion_matches_highs():
     """The balanced-LP workload at full size (m=4096, n=64, k=4)."""
