@@ -61,8 +61,13 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
  * "Shazeer et al. (2017)의 MoE Layer"). */
 typedef enum { MOE_GATE_PROB = 0, MOE_GATE_RENORM = 1 } moe_gate;
 
-/* Balanced-assignment modes ([MoE tour 6] "교대 반복" and "함정에 주의"). */
+/* Balanced-assignment modes ([MoE tour 6] "교대 반복" and "함정에 주의"), with
+ * optional flags OR-ed in: MOE_QB_QUANTILE, the quantile form of the page's
+ * demo code ("데모 코드": each α and β the 1 − k/n quantile of its row / column
+ * with linear interpolation, as numpy computes it on fp32 data); MOE_QB_BIP,
+ * α and β clipped at 0 after every step (the demo's comment on BIP). */
 typedef enum { MOE_QB_SOLVE = 0, MOE_QB_ONLINE = 1 } moe_qb_mode;
+enum { MOE_QB_QUANTILE = 0x10, MOE_QB_BIP = 0x20 };
 
 typedef enum { MOE_EXPERT_IDENTITY = 0, MOE_EXPERT_RELU_FFN = 1 } moe_expert_kind;
 
@@ -195,6 +200,10 @@ moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t
  *     idx = top-k of fl32(s_i − β) (ties: lower index).
  *   mode ONLINE ("함정에 주의"): idx = top-k of fl32(s_i − β_old) FIRST, then one
  *     QB step updates beta (iters must be 1, exact must be 0).
+ *   | MOE_QB_QUANTILE: α_i and β_j are the 1 − k/n quantiles of fl32(s_i − β) and
+ *     fl32(s_·j − α), interpolated linearly between the two neighbouring order
+ *     statistics (fp32 arithmetic, numpy's rule; bit-reproducible).
+ *   | MOE_QB_BIP: α and β clipped at 0 after each step.
  *   exact = 1 (SOLVE only): finish with successive shortest paths (min-cost
  *     flow on the expert graph, fp64) from x = top-k(s − β) until every expert
  *     holds exactly q tokens; idx is then the LP optimum (eq. (4), which has an

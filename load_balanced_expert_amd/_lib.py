@@ -14,6 +14,7 @@ MOE_F32, MOE_BF16 = 0, 1
 SCORES = {"softmax": 0, "sigmoid": 1}
 GATES = {"prob": 0, "renorm": 1}
 QB_MODES = {"solve": 0, "online": 1}
+QB_QUANTILE, QB_BIP = 0x10, 0x20
 EXPERTS = {"identity": 0, "relu_ffn": 1}
 
 

@@ -202,8 +202,9 @@ class BalanceOut:
 
 
 def balance_duals(s: torch.Tensor, k: int, beta: torch.Tensor, iters: int = 5, mode: str = "solve",
-                  exact: bool = False) -> BalanceOut:
-    """beta is updated in place."""
+                  exact: bool = False, quantile: bool = False, bip: bool = False) -> BalanceOut:
+    """beta is updated in place.  quantile: the demo code's interpolated 1 - k/n quantiles;
+    bip: α and β clipped at 0 after every step."""
     _on_device(s, beta)
     m, n = s.shape
     dev = s.device
@@ -213,7 +214,8 @@ def balance_duals(s: torch.Tensor, k: int, beta: torch.Tensor, iters: int = 5, m
     info = torch.zeros(4, dtype=torch.int32, device=dev)
     need = int(_lib().moe_balance_workspace_size(int(m), int(n), int(k), int(exact)))
     ws, wsb = _ws_args(need, dev)
-    _check(_lib().moe_balance_duals(int(m), int(n), int(k), _ptr(s), _ptr(beta), int(iters), L.QB_MODES[mode],
+    flags = (L.QB_QUANTILE if quantile else 0) | (L.QB_BIP if bip else 0)
+    _check(_lib().moe_balance_duals(int(m), int(n), int(k), _ptr(s), _ptr(beta), int(iters), L.QB_MODES[mode] | flags,
                                     int(exact), _ptr(idx), _ptr(counts), _ptr(alpha), _ptr(info), ws, wsb,
                                     _stream(dev)), "moe_balance_duals")
     return BalanceOut(idx, counts, alpha, info)

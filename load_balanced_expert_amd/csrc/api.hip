@@ -300,6 +300,8 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
                              int32_t* info, void* ws, size_t ws_bytes, void* stream) {
   if (m < 1 || n < 2 || k < 1 || k >= n || !s || !beta || !idx || !counts) return MOE_ERR_INVALID_ARG;
   if ((m * int64_t(k)) % n != 0) return MOE_ERR_INVALID_ARG;
+  const bool quantile = (mode & MOE_QB_QUANTILE) != 0, bip = (mode & MOE_QB_BIP) != 0;
+  mode &= ~(MOE_QB_QUANTILE | MOE_QB_BIP);
   if (mode != MOE_QB_SOLVE && mode != MOE_QB_ONLINE) return MOE_ERR_INVALID_ARG;
   if (iters < 0 || (mode == MOE_QB_ONLINE && (iters != 1 || exact))) return MOE_ERR_INVALID_ARG;
   if (n > kMaxExperts || m > 0x7FFFFFFFll || m * k > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
@@ -315,6 +317,8 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
   a.iters = mode == MOE_QB_ONLINE ? 1 : iters;
   a.mode = mode;
   a.exact = exact;
+  a.quantile = quantile;
+  a.bip = bip;
   a.idx = idx;
   a.counts = counts;
   a.alpha_out = alpha;

@@ -59,6 +59,14 @@ __global__ __launch_bounds__(256) void k_qb_transpose(const float* __restrict__ 
   }
 }
 
+// numpy's linear interpolation of two neighbouring order statistics, in fp32
+// with no contraction (the demo's quantile of fp32 differences is computed so)
+__device__ __forceinline__ float lerp_np(float a, float b, float t) {
+#pragma clang fp contract(off)
+  const float d = b - a;
+  return t >= 0.5f ? b - d * (1.0f - t) : a + d * t;
+}
+
 // ------------------------------------------------------------------ rows: top-k and α
 template <bool IDX, bool ALPHA>
 __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __restrict__ beta,
@@ -74,9 +82,12 @@ __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __r
     const int64_t i = int64_t(blockIdx.x) * kQbRowsPerBlock + rr;
     if (i >= a.m) break;
     const float* row = a.s + i * n;
-    float last_key = INFINITY;
+    float last_key = INFINITY, hi_key = INFINITY, lo_key = INFINITY;
     int last_j = -1, my_j = 0;
-    const int rounds = ALPHA ? k + 1 : k;
+    // α: the (k+1)-th largest (exact form), or the order statistics of descending
+    // ranks rank_row and rank_row - 1 (quantile form)
+    const int arank = a.quantile ? a.rank_row : k;
+    const int rounds = ALPHA ? max(k, arank + 1) : k;
     for (int r = 0; r < rounds; ++r) {
       float bk = -INFINITY;
       int bj = 0x7FFFFFFF;
@@ -90,12 +101,19 @@ __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __r
       wave_argbest(bk, bj);
       last_key = bk;
       last_j = bj;
+      if (r == arank - 1) hi_key = bk;
+      if (r == arank) lo_key = bk;
       if (IDX && r < k) {
         if (lane == r) my_j = bj;
         if (lane == 0) atomicAdd(&hist[bj], 1);
       }
     }
-    if (ALPHA && lane == 0) alpha[i] = last_key;
+    if (ALPHA && lane == 0) {
+      float al = lo_key;
+      if (a.quantile) al = lerp_np(lo_key, arank >= 1 ? hi_key : lo_key, a.g_row);
+      if (a.bip) al = fmaxf(al, 0.f);
+      alpha[i] = al;
+    }
     if (IDX && lane < k) a.idx[i * k + lane] = my_j;
   }
   if (!IDX) return;
@@ -122,15 +140,20 @@ __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __r
 }
 
 // ------------------------------------------------------------------ columns: (q+1)-th largest
+// Quantile form: the order statistic of descending rank r = rank_col and the
+// next larger one, d_{r-1} = the least key above d_r if exactly r keys lie
+// above it, else d_r itself; interpolated with weight g_col.
 __global__ __launch_bounds__(256) void k_qb_cols(const float* __restrict__ sT, const float* __restrict__ alpha,
-                                                 float* __restrict__ beta, int64_t m, int64_t q) {
+                                                 float* __restrict__ beta, int64_t m, int64_t q, BalanceArgs a) {
   __shared__ int hist[256];
-  __shared__ uint32_t s_prefix;
+  __shared__ uint32_t s_prefix, s_min;
   __shared__ int64_t s_rank;
+  __shared__ unsigned long long s_above;
   const int j = blockIdx.x;
   const float* col = sT + int64_t(j) * m;
   uint32_t prefix = 0, mask = 0;
-  int64_t rank = q;  // 0-based rank in descending order
+  int64_t rank = a.quantile ? a.rank_col : q;  // 0-based rank in descending order
+  const int64_t rank0 = rank;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     hist[threadIdx.x] = 0;
@@ -171,7 +194,30 @@ __global__ __launch_bounds__(256) void k_qb_cols(const float* __restrict__ sT, c
     mask |= 255u << shift;
     __syncthreads();
   }
-  if (threadIdx.x == 0) beta[j] = key_f32(prefix);
+  float bv = key_f32(prefix);
+  if (a.quantile) {
+    if (threadIdx.x == 0) {
+      s_min = 0xFFFFFFFFu;
+      s_above = 0;
+    }
+    __syncthreads();
+    uint32_t mn = 0xFFFFFFFFu;
+    unsigned long long above = 0;
+    for (int64_t i = threadIdx.x; i < m; i += 256) {
+      const uint32_t u = f32_key(col[i] - alpha[i]);
+      if (u > prefix) {
+        ++above;
+        mn = min(mn, u);
+      }
+    }
+    atomicMin(&s_min, mn);
+    atomicAdd(&s_above, above);
+    __syncthreads();
+    const float hi = rank0 >= 1 && int64_t(s_above) == rank0 ? key_f32(s_min) : bv;
+    bv = lerp_np(bv, hi, a.g_col);
+  }
+  if (a.bip) bv = fmaxf(bv, 0.f);
+  if (threadIdx.x == 0) beta[j] = bv;
 }
 
 // ------------------------------------------------------------------ exact completion (n <= 64)
@@ -529,7 +575,25 @@ __global__ void k_qb_info(int32_t* info, int iters) {
 }
 
 // ------------------------------------------------------------------ launcher
-hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
+// numpy's linear quantile of N values at 1 - k/n (the level and the index in
+// fp32, as numpy computes them for fp32 data): the lower neighbour's 0-based
+// descending rank and the interpolation weight
+static void quantile_pos(int64_t N, int k, int n, int64_t& rank, float& g) {
+  const float lev = float(1.0 - double(k) / double(n));
+  const float vi = float(N - 1) * lev;
+  const float lo = std::floor(vi);
+  rank = N - 1 - int64_t(lo);
+  g = vi - lo;
+}
+
+hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
+  BalanceArgs a = a_in;
+  if (a.quantile) {
+    int64_t rr = 0;
+    quantile_pos(a.n, a.k, a.n, rr, a.g_row);
+    a.rank_row = int(rr);
+    quantile_pos(a.m, a.k, a.n, a.rank_col, a.g_col);
+  }
   char* ws = static_cast<char*>(a.ws);
   float* sT = reinterpret_cast<float*>(ws);
   ws += al256(size_t(a.m) * a.n * sizeof(float));
@@ -551,12 +615,12 @@ hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
                      sT, a.m, a.n);
   if (a.mode == 1) {  // online: route with the old β, then one α and one β step
     hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
-    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q);
+    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q, a);
     return hipGetLastError();
   }
   for (int it = 0; it < a.iters; ++it) {
     hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, a.beta, alpha, chunks);
-    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q);
+    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q, a);
   }
   if (a.exact)
     hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi, pos, lst);

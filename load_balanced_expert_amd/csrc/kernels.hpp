@@ -145,6 +145,14 @@ struct BalanceArgs {
   const float* s;
   float* beta;
   int iters, mode, exact;
+  // quantile form (the demo code's 1 - k/n quantile with linear interpolation):
+  // the lower order statistic's 0-based descending rank and the weight of the
+  // next larger one, per axis (set by launch_balance); bip clips α and β at 0
+  bool quantile, bip;
+  int rank_row;
+  float g_row;
+  int64_t rank_col;
+  float g_col;
   int32_t* idx;
   int32_t* counts;
   float* alpha_out;

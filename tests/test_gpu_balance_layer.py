@@ -49,6 +49,34 @@ def test_qb_solve_other_shapes(m, n, k):
     assert np.array_equal(to_host(out.idx), idx_r)
 
 
+@pytest.mark.parametrize("m,n,k,iters,bip", [(4096, 64, 4, 5, False), (3200, 256, 8, 5, False),
+                                             (3200, 256, 8, 5, True), (1000, 8, 2, 3, False), (96, 32, 3, 2, True)])
+def test_qb_quantile_bit_exact(m, n, k, iters, bip):
+    # the demo code's interpolated quantiles on both axes, against numpy's quantile in the oracle
+    s = W.uniform_offset_scores(m, n, 11)
+    say(f"[qb] quantile m={m} n={n} k={k} iters={iters} bip={bip}")
+    beta = torch.zeros(n, dtype=torch.float32, device=DEV)
+    out = M.balance_duals(to_dev(s), k, beta, iters=iters, quantile=True, bip=bip)
+    torch.cuda.synchronize()
+    idx_r, beta_r, alpha_r = OB.qb_solve_quantile(s, k, iters, bip=bip)
+    assert np.array_equal(to_host(out.alpha), alpha_r)
+    assert np.array_equal(to_host(beta), beta_r)
+    assert np.array_equal(to_host(out.idx), idx_r)
+
+
+def test_qb_quantile_demo_full_size():
+    # the page's demo: m = 100000, n = 256, k = 8, s = U(0,1) + U(0,1)_n, T = 5
+    m, n, k = 100000, 256, 8
+    s = W.uniform_offset_scores(m, n, 0)
+    say(f"[qb] quantile demo m={m} n={n} k={k}")
+    beta = torch.zeros(n, dtype=torch.float32, device=DEV)
+    out = M.balance_duals(to_dev(s), k, beta, iters=5, quantile=True)
+    torch.cuda.synchronize()
+    idx_r, beta_r, _ = OB.qb_solve_quantile(s, k, 5)
+    assert np.array_equal(to_host(beta), beta_r)
+    assert np.array_equal(to_host(out.counts), np.bincount(idx_r.ravel(), minlength=n))
+
+
 def test_qb_online_routes_before_update():
     spec = W.BALANCED
     s = W.balanced_scores(spec, 2)
