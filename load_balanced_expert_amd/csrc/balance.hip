@@ -6,18 +6,22 @@
 //   "함정에 주의": the online form routes with the old β, then updates it.
 //
 // Kernels
-//  * row kernel: one wave per token row; k+1 rounds of a wave-wide arg-best
-//    over fl32(s_i − β) give the top-k (idx) and the (k+1)-th value (α).
-//  * column kernel: one workgroup per expert; the (q+1)-th largest of
-//    fl32(s_·j − α) by an exact 4-pass radix select (8 bits per pass) over
-//    order-preserving uint32 keys, on a transposed copy of s so that each
-//    column is contiguous.
+//  * row kernel: one wave per token row.  For n <= 256 the lanes keep their
+//    experts sorted in registers and each of the k+1 rounds pops the wave's
+//    best head (DPP max); wider rows take k+1 rounds of a wave-wide arg-best
+//    over fl32(s_i − β).  The rounds give the top-k (idx) and the (k+1)-th
+//    value (α).
+//  * column kernel: one 1024-thread workgroup per expert on a transposed copy
+//    of s (each column contiguous): the (q+1)-th largest of fl32(s_·j − α) by
+//    an exact radix select over order-preserving uint32 keys (12 + 12 + 8
+//    bits), the last two digits over the keys of the chosen bin held in LDS.
 //  * exact completion: one persistent workgroup runs successive shortest
 //    paths on the expert graph in fp64 (the move cost a -> j is the cheapest
 //    s_ia − s_ij over tokens holding a but not j, kept in LDS; Dijkstra runs
 //    on one wave with one expert per lane) until every expert has q tokens.
 //    Requires n <= 64.
 #include "common.hpp"
+#include "dpp.hpp"
 #include "kernels.hpp"
 #include "prefix.hpp"
 
@@ -139,85 +143,311 @@ __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __r
   if (threadIdx.x == 0 && a.info) a.info[2] = s_bal;
 }
 
-// ------------------------------------------------------------------ columns: (q+1)-th largest
-// Quantile form: the order statistic of descending rank r = rank_col and the
-// next larger one, d_{r-1} = the least key above d_r if exactly r keys lie
-// above it, else d_r itself; interpolated with weight g_col.
-__global__ __launch_bounds__(256) void k_qb_cols(const float* __restrict__ sT, const float* __restrict__ alpha,
-                                                 float* __restrict__ beta, int64_t m, int64_t q, BalanceArgs a) {
-  __shared__ int hist[256];
-  __shared__ uint32_t s_prefix, s_min;
-  __shared__ int64_t s_rank;
-  __shared__ unsigned long long s_above;
-  const int j = blockIdx.x;
-  const float* col = sT + int64_t(j) * m;
-  uint32_t prefix = 0, mask = 0;
-  int64_t rank = a.quantile ? a.rank_col : q;  // 0-based rank in descending order
-  const int64_t rank0 = rank;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[threadIdx.x] = 0;
+// ------------------------------------------------------------------ rows, n <= 256
+// Lane l holds experts l + 64u (u < NPL) in registers, sorted by (value
+// descending, index ascending); each round the wave's best head (a DPP max, and
+// among equal heads the lowest expert) is popped by the lane that holds it, so a
+// round costs a few DPP steps instead of a pass over the row.
+// compare-exchange into (value desc, index asc) order; by value alone when the
+// indices are not wanted
+template <bool USEJ, int NPL>
+__device__ __forceinline__ void ce_desc(float (&v)[NPL], int (&j)[NPL], int p, int q) {
+  if (!USEJ) {
+    const float hi = fmaxf(v[p], v[q]), lo = fminf(v[p], v[q]);
+    v[p] = hi;
+    v[q] = lo;
+    return;
+  }
+  if (better(v[q], j[q], v[p], j[p])) {
+    const float tv = v[p];
+    v[p] = v[q];
+    v[q] = tv;
+    const int tj = j[p];
+    j[p] = j[q];
+    j[q] = tj;
+  }
+}
+
+constexpr int kRowsRegThreads = 1024;
+template <bool IDX, bool ALPHA, int NPL>
+__global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_reg(BalanceArgs a, const float* __restrict__ beta,
+                                                     float* __restrict__ alpha, uint64_t* __restrict__ chunks) {
+  extern __shared__ __attribute__((aligned(16))) int hist[];   // [n], then the finishing scratch
+  const int n = a.n, k = a.k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (IDX) {
+    for (int j = threadIdx.x; j < n; j += kRowsRegThreads) hist[j] = 0;
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < m; i += 256) {
-      const uint32_t u = f32_key(col[i] - alpha[i]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+  }
+  const int arank = a.quantile ? a.rank_row : k;
+  const int rounds = ALPHA ? max(k, arank + 1) : k;
+  float bl[NPL];
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) bl[u] = lane + 64 * u < n ? beta[lane + 64 * u] : 0.f;
+  constexpr int kWaves = kRowsRegThreads / 64;
+  const int64_t stride = int64_t(gridDim.x) * kWaves;
+  int64_t i = int64_t(blockIdx.x) * kWaves + wave;
+  float nx[NPL];
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) nx[u] = i < a.m && lane + 64 * u < n ? a.s[i * n + lane + 64 * u] : 0.f;
+  for (; i < a.m; i += stride) {
+    float v[NPL];
+    int jj[NPL];
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) {
+      const int j = lane + 64 * u;
+      v[u] = j < n ? nx[u] - bl[u] : -INFINITY;
+      jj[u] = j < n ? j : 0x7FFFFFFF;
     }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l holds digits 255-4l .. 252-4l (descending digit order across lanes)
-      const int lane = threadIdx.x;
-      int hv[4], tot = 0;
+    const int64_t i2 = i + stride;   // next row of this wave, loaded while this one is ranked
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        hv[u] = hist[255 - 4 * lane - u];
-        tot += hv[u];
-      }
-      int incl = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-      }
-      int64_t cum = incl - tot;  // count of keys in higher digits
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (cum <= rank && rank < cum + hv[u]) {
-          s_prefix = prefix | (uint32_t(255 - 4 * lane - u) << shift);
-          s_rank = rank - cum;
+    for (int u = 0; u < NPL; ++u) nx[u] = i2 < a.m && lane + 64 * u < n ? a.s[i2 * n + lane + 64 * u] : 0.f;
+    if (NPL == 2) ce_desc<IDX, NPL>(v, jj, 0, 1 % NPL);
+    if (NPL == 4) {
+      ce_desc<IDX, NPL>(v, jj, 0, 1 % NPL);
+      ce_desc<IDX, NPL>(v, jj, 2 % NPL, 3 % NPL);
+      ce_desc<IDX, NPL>(v, jj, 0, 2 % NPL);
+      ce_desc<IDX, NPL>(v, jj, 1 % NPL, 3 % NPL);
+      ce_desc<IDX, NPL>(v, jj, 1 % NPL, 2 % NPL);
+    }
+    float hi_key = INFINITY, lo_key = INFINITY;
+    int my_j = 0;
+    for (int r = 0; r < rounds; ++r) {
+      const float h = v[0];
+      const float mx = wave_max_dpp(h);
+      const bool top = h == mx;
+      const uint64_t tied = __ballot(top);
+      int win = tied ? __ffsll((unsigned long long)tied) - 1 : 0;
+      if (IDX && r < k) {
+        if (__popcll(tied) > 1) {   // equal heads: the lowest expert goes first
+          const int mj = wave_min_i_dpp(top ? jj[0] : 0x7FFFFFFF);
+          const uint64_t w = __ballot(top && jj[0] == mj);
+          win = w ? __ffsll((unsigned long long)w) - 1 : 0;
         }
-        cum += hv[u];
+        const int bj = __builtin_amdgcn_readlane(jj[0], win);
+        if (lane == r) my_j = bj;
+        if (lane == 0) atomicAdd(&hist[bj], 1);
+      }
+      if (r == arank - 1) hi_key = mx;
+      if (r == arank) lo_key = mx;
+      if (lane == win) {
+#pragma unroll
+        for (int u = 0; u + 1 < NPL; ++u) {
+          v[u] = v[u + 1];
+          if (IDX) jj[u] = jj[u + 1];
+        }
+        v[NPL - 1] = -INFINITY;
+        if (IDX) jj[NPL - 1] = 0x7FFFFFFF;
       }
     }
+    if (ALPHA && lane == 0) {
+      float al = lo_key;
+      if (a.quantile) al = lerp_np(lo_key, arank >= 1 ? hi_key : lo_key, a.g_row);
+      if (a.bip) al = fmaxf(al, 0.f);
+      alpha[i] = al;
+    }
+    if (IDX && lane < k) a.idx[i * k + lane] = my_j;
+  }
+  if (!IDX) return;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += kRowsRegThreads) store_agent(chunks + int64_t(blockIdx.x) * n + j, pack_chunk(hist[j], 0.f));
+  __shared__ int s_flag;
+  if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
+  FinalizeArgs f{};
+  f.chunks = chunks;
+  f.nch = int(gridDim.x);
+  f.sup = super_chunk(f.nch);
+  f.n = n;
+  f.m = a.m;
+  f.counts = a.counts;
+  f.capacity = -1;
+  finalize_chunks(f, hist, n + 4096, kRowsRegThreads);
+  __shared__ int s_bal;
+  if (threadIdx.x == 0) s_bal = 1;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += kRowsRegThreads)
+    if (int64_t(hist[j]) != a.q) atomicAnd(&s_bal, 0);
+  __syncthreads();
+  if (threadIdx.x == 0 && a.info) a.info[2] = s_bal;
+}
+
+// ------------------------------------------------------------------ columns: an order statistic per expert
+// One 1024-thread workgroup per expert on the transposed copy of s.  Keys are
+// the order-preserving uint32 images of fl32(s_ij - α_i).  Pass 1 histograms
+// the top 12 key bits; pass 2 copies the keys of the bin that holds the wanted
+// rank into LDS (when they fit), and the remaining 12 + 8 bits are selected
+// there; otherwise those two digits take further passes over the column.
+// Histogram adds are merged per wave for the lanes that share the first
+// active lane's digit (the column's keys crowd into few top-bit bins).
+constexpr int kColThreads = 1024;
+constexpr int kColBins = 4096;
+constexpr int kColCap = 24576;
+constexpr size_t kColLds = (size_t(kColBins) + kColCap) * sizeof(int);
+
+__device__ __forceinline__ void hist_add(int* hist, uint32_t d, bool act) {
+  const uint64_t am = __ballot(act);
+  if (!am) return;
+  const uint32_t lead = uint32_t(__builtin_amdgcn_readlane(int(d), __ffsll((unsigned long long)am) - 1));
+  const uint64_t peers = __ballot(act && d == lead);
+  if (!act) return;
+  if (d != lead) {
+    atomicAdd(&hist[d], 1);
+  } else if ((threadIdx.x & 63) == __ffsll((unsigned long long)peers) - 1) {
+    atomicAdd(&hist[lead], __popcll(peers));
+  }
+}
+
+// The bin of hist[0..nb) (taken in descending digit order) holding descending
+// rank `rank`, and the rank within it.
+__device__ __forceinline__ void col_select(const int* hist, int nb, int rank, int* s_wsum, int* s_bin,
+                                           int* s_rank) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = ceil_div(nb, kColThreads);
+  int hv[4], tot = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int b = nb - 1 - (tid * per + u);
+    hv[u] = u < per && b >= 0 ? hist[b] : 0;
+    tot += hv[u];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int cum = incl - tot;
+  for (int w = 0; w < wave; ++w) cum += s_wsum[w];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u < per && cum <= rank && rank < cum + hv[u]) {
+      *s_bin = nb - 1 - (tid * per + u);
+      *s_rank = rank - cum;
+    }
+    cum += hv[u];
+  }
+  __syncthreads();
+}
+
+// f(key, active) over the column, four loads in flight per thread
+template <typename F>
+__device__ __forceinline__ void col_scan(const float* __restrict__ col, const float* __restrict__ alpha, int64_t m,
+                                         F f) {
+  for (int64_t b = threadIdx.x; b < m; b += 4 * kColThreads) {
+    float x[4], al[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = b + int64_t(u) * kColThreads;
+      x[u] = i < m ? col[i] : 0.f;
+      al[u] = i < m ? alpha[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f(f32_key(x[u] - al[u]), b + int64_t(u) * kColThreads < m);
+  }
+}
+
+__global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict__ sT,
+                                                         const float* __restrict__ alpha, float* __restrict__ beta,
+                                                         BalanceArgs a) {
+  extern __shared__ __attribute__((aligned(16))) int hist[];   // [kColBins], then [kColCap] keys
+  uint32_t* keys = reinterpret_cast<uint32_t*>(hist + kColBins);
+  __shared__ int s_wsum[kColThreads / 64], s_bin, s_rank, s_nk;
+  __shared__ uint32_t s_min;
+  const int j = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int64_t m = a.m;
+  const float* col = sT + int64_t(j) * m;
+  const int rank0 = int(a.quantile ? a.rank_col : a.q);   // 0-based rank in descending order
+  for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
+  if (tid == 0) {
+    s_nk = 0;
+    s_min = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  col_scan(col, alpha, m, [&](uint32_t u, bool act) { hist_add(hist, u >> 20, act); });
+  __syncthreads();
+  col_select(hist, kColBins, rank0, s_wsum, &s_bin, &s_rank);
+  const uint32_t b1 = uint32_t(s_bin);
+  int rank = s_rank;
+  const bool in_lds = hist[b1] <= kColCap;
+  uint32_t mn = 0xFFFFFFFFu;   // least key in a higher first-digit bin
+  __syncthreads();
+  for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
+  __syncthreads();
+  uint32_t prefix;
+  if (in_lds) {
+    col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+      const bool take = act && (u >> 20) == b1;
+      if (act && (u >> 20) > b1) mn = min(mn, u);
+      const uint64_t bm = __ballot(take);
+      if (!bm) return;
+      const int lead = __ffsll((unsigned long long)bm) - 1;
+      int base = 0;
+      if (lane == lead) base = atomicAdd(&s_nk, __popcll(bm));
+      base = __builtin_amdgcn_readlane(base, lead);
+      if (take) keys[base + __popcll(bm & lanemask_lt())] = u;
+    });
     __syncthreads();
-    prefix = s_prefix;
+    const int nk = s_nk;
+    for (int t = tid; t - tid < nk; t += kColThreads) {
+      const bool act = t < nk;
+      hist_add(hist, act ? (keys[t] >> 8) & 0xFFFu : 0u, act);
+    }
+    __syncthreads();
+    col_select(hist, kColBins, rank, s_wsum, &s_bin, &s_rank);
+    const uint32_t p2 = (b1 << 12) | uint32_t(s_bin);   // key >> 8
     rank = s_rank;
-    mask |= 255u << shift;
     __syncthreads();
+    for (int b = tid; b < 256; b += kColThreads) hist[b] = 0;
+    __syncthreads();
+    for (int t = tid; t - tid < nk; t += kColThreads) {
+      const bool act = t < nk && (keys[t] >> 8) == p2;
+      hist_add(hist, act ? keys[t] & 0xFFu : 0u, act);
+    }
+    __syncthreads();
+    col_select(hist, 256, rank, s_wsum, &s_bin, &s_rank);
+    prefix = (p2 << 8) | uint32_t(s_bin);
+    rank = s_rank;
+    if (a.quantile && rank == 0)
+      for (int t = tid; t < nk; t += kColThreads)
+        if (keys[t] > prefix) mn = min(mn, keys[t]);
+  } else {
+    col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+      const bool take = act && (u >> 20) == b1;
+      hist_add(hist, take ? (u >> 8) & 0xFFFu : 0u, take);
+    });
+    __syncthreads();
+    col_select(hist, kColBins, rank, s_wsum, &s_bin, &s_rank);
+    const uint32_t p2 = (b1 << 12) | uint32_t(s_bin);
+    rank = s_rank;
+    __syncthreads();
+    for (int b = tid; b < 256; b += kColThreads) hist[b] = 0;
+    __syncthreads();
+    col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+      const bool take = act && (u >> 8) == p2;
+      hist_add(hist, take ? u & 0xFFu : 0u, take);
+    });
+    __syncthreads();
+    col_select(hist, 256, rank, s_wsum, &s_bin, &s_rank);
+    prefix = (p2 << 8) | uint32_t(s_bin);
+    rank = s_rank;
+    if (a.quantile && rank == 0)
+      col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+        if (act && u > prefix) mn = min(mn, u);
+      });
   }
   float bv = key_f32(prefix);
   if (a.quantile) {
-    if (threadIdx.x == 0) {
-      s_min = 0xFFFFFFFFu;
-      s_above = 0;
-    }
-    __syncthreads();
-    uint32_t mn = 0xFFFFFFFFu;
-    unsigned long long above = 0;
-    for (int64_t i = threadIdx.x; i < m; i += 256) {
-      const uint32_t u = f32_key(col[i] - alpha[i]);
-      if (u > prefix) {
-        ++above;
-        mn = min(mn, u);
-      }
-    }
+    // descending rank rank0 - 1: the least key above when exactly rank0 keys
+    // lie above this one (rank within equal keys is 0), else this key again
     atomicMin(&s_min, mn);
-    atomicAdd(&s_above, above);
     __syncthreads();
-    const float hi = rank0 >= 1 && int64_t(s_above) == rank0 ? key_f32(s_min) : bv;
+    const float hi = rank0 >= 1 && rank == 0 ? key_f32(s_min) : bv;
     bv = lerp_np(bv, hi, a.g_col);
   }
   if (a.bip) bv = fmaxf(bv, 0.f);
-  if (threadIdx.x == 0) beta[j] = bv;
+  if (tid == 0) beta[j] = bv;
 }
 
 // ------------------------------------------------------------------ exact completion (n <= 64)
@@ -611,21 +841,52 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
   if (a.info) hipLaunchKernelGGL(k_qb_info, dim3(1), dim3(64), 0, s, a.info, a.iters);
   const unsigned rblocks = unsigned(ceil_div64(a.m, kQbRowsPerBlock));
   const size_t rlds = (size_t(a.n) + 4096) * sizeof(int);
+  // register rows: grid-stride waves; the counting form keeps at most 512
+  // per-workgroup count rows (ceil(m/16) are allocated) for the last workgroup to fold
+  const int npl = a.n <= 64 ? 1 : a.n <= 128 ? 2 : a.n <= 256 ? 4 : 0;
+  const unsigned gidx = unsigned(std::min<int64_t>(ceil_div64(a.m, 64), 512));
+  const unsigned galpha = unsigned(std::min<int64_t>(ceil_div64(a.m, 64), 1024));
+  auto rows = [&](bool idx, bool al) {
+#define MOE_QB_ROWS(NPL)                                                                                      \
+  if (idx && al)                                                                                           \
+    hipLaunchKernelGGL((k_qb_rows_reg<true, true, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
+  else if (idx)                                                                                            \
+    hipLaunchKernelGGL((k_qb_rows_reg<true, false, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
+  else                                                                                                     \
+    hipLaunchKernelGGL((k_qb_rows_reg<false, true, NPL>), dim3(galpha), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha, chunks);
+    if (npl == 1) {
+      MOE_QB_ROWS(1)
+    } else if (npl == 2) {
+      MOE_QB_ROWS(2)
+    } else if (npl == 4) {
+      MOE_QB_ROWS(4)
+    } else if (idx && al) {
+      hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
+    } else if (idx) {
+      hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
+    } else {
+      hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, a.beta, alpha, chunks);
+    }
+#undef MOE_QB_ROWS
+  };
+  auto cols = [&]() {
+    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(kColThreads), kColLds, s, sT, alpha, a.beta, a);
+  };
   hipLaunchKernelGGL(k_qb_transpose, dim3(unsigned(ceil_div64(a.m, 64)), ceil_div(a.n, 64)), dim3(256), 0, s, a.s,
                      sT, a.m, a.n);
   if (a.mode == 1) {  // online: route with the old β, then one α and one β step
-    hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
-    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q, a);
+    rows(true, true);
+    cols();
     return hipGetLastError();
   }
   for (int it = 0; it < a.iters; ++it) {
-    hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, a.beta, alpha, chunks);
-    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(256), 0, s, sT, alpha, a.beta, a.m, a.q, a);
+    rows(false, true);
+    cols();
   }
   if (a.exact)
     hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi, pos, lst);
   else
-    hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
+    rows(true, false);
   return hipGetLastError();
 }
 

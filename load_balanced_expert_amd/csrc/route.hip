@@ -25,6 +25,7 @@
 //    the route stops after its chunk rows and per-super-chunk sums, and the
 //    dispatch derives the rest.
 #include "common.hpp"
+#include "dpp.hpp"
 #include "kernels.hpp"
 #include "prefix.hpp"
 
@@ -453,54 +454,6 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
   }
 }
 
-// Half-wave (32 lanes) all-reductions without the LDS crossbar: partners at
-// lane xor 1 and xor 2 (quad permutes), the mirrored quad and the mirrored
-// half-row (row_half_mirror, row_mirror DPP), then the other 16-lane row of
-// the half (gfx950 v_permlane16_swap).  Each step combines a lane with a
-// partner that already holds the same partial, so every lane of the half ends
-// with the same bits.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppMirror = 0x140, kDppHalfMirror = 0x141;
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-// (value of the even row, value of the odd row) of this lane's 32-lane half
-__device__ __forceinline__ void row_pair(uint32_t v, uint32_t& even, uint32_t& odd) {
-  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  even = r[0];
-  odd = r[1];
-}
-__device__ __forceinline__ float half_max(float v) {
-  v = fmaxf(v, dpp_f<kDppXor1>(v));
-  v = fmaxf(v, dpp_f<kDppXor2>(v));
-  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_f<kDppMirror>(v));
-  uint32_t a, b;
-  row_pair(__float_as_uint(v), a, b);
-  return fmaxf(__uint_as_float(a), __uint_as_float(b));
-}
-__device__ __forceinline__ float half_sum(float v) {
-  v += dpp_f<kDppXor1>(v);
-  v += dpp_f<kDppXor2>(v);
-  v += dpp_f<kDppHalfMirror>(v);
-  v += dpp_f<kDppMirror>(v);
-  uint32_t a, b;
-  row_pair(__float_as_uint(v), a, b);
-  return __uint_as_float(a) + __uint_as_float(b);
-}
-__device__ __forceinline__ int half_min_i(int v) {
-  v = min(v, dpp_i<kDppXor1>(v));
-  v = min(v, dpp_i<kDppXor2>(v));
-  v = min(v, dpp_i<kDppHalfMirror>(v));
-  v = min(v, dpp_i<kDppMirror>(v));
-  uint32_t a, b;
-  row_pair(uint32_t(v), a, b);
-  return min(int(a), int(b));
-}
 template <int CTRL>
 __device__ __forceinline__ void argbest_step(float& key, int& ix) {
   const float ok = dpp_f<CTRL>(key);
@@ -955,21 +908,6 @@ __global__ __launch_bounds__(256) void k_route_logits_valu(RouteArgs a) {
 // reduction over the lanes holding the maximum (the lowest such expert), and
 // the sum of the exponentials; the pick's score is exp(0) / sum.  Writes what
 // route_rows writes.
-__device__ __forceinline__ float lane_value(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = half_max(v);
-  return fmaxf(lane_value(v, 0), lane_value(v, 32));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = half_sum(v);
-  return lane_value(v, 0) + lane_value(v, 32);
-}
-__device__ __forceinline__ int wave_min_i_dpp(int v) {
-  v = half_min_i(v);
-  return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
-}
 __device__ __forceinline__ void route_rows_top1(float* lg, int ld, int rows, int64_t t0, const EpiArgs& e,
                                                 int32_t* __restrict__ idx, float* __restrict__ gate_out,
                                                 float* tok_mx, float* tok_sum, int* hist) {
