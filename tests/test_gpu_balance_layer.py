@@ -64,6 +64,31 @@ def test_qb_quantile_bit_exact(m, n, k, iters, bip):
     assert np.array_equal(to_host(out.idx), idx_r)
 
 
+@pytest.mark.parametrize("m,n,k,levels", [
+    (2000, 100, 5, 0),       # 65..128 experts: two experts per lane in the row kernel
+    (1600, 320, 4, 0),       # more than 256 experts: the row kernel's arg-best rounds
+    (4096, 64, 4, 4),        # scores on a grid of 4 values: equal heads, lowest expert first
+    (120000, 8, 2, 2),       # two score values: the column bin overflows LDS, selected in global passes
+])
+@pytest.mark.parametrize("quantile", [False, True])
+def test_qb_kernel_paths(m, n, k, levels, quantile):
+    s = W.uniform_offset_scores(m, n, 5)
+    if levels:
+        s = (np.floor(s * (levels / 2.0)) / levels).astype(np.float32)
+    say(f"[qb] paths m={m} n={n} k={k} levels={levels} quantile={quantile}")
+    beta = torch.zeros(n, dtype=torch.float32, device=DEV)
+    out = M.balance_duals(to_dev(s), k, beta, iters=3, quantile=quantile)
+    torch.cuda.synchronize()
+    if quantile:
+        idx_r, beta_r, alpha_r = OB.qb_solve_quantile(s, k, 3)
+    else:
+        idx_r, beta_r, alpha_r = OB.qb_solve(s, k, 3)
+    assert np.array_equal(to_host(out.alpha), alpha_r)
+    assert np.array_equal(to_host(beta), beta_r)
+    assert np.array_equal(to_host(out.idx), idx_r)
+    assert np.array_equal(to_host(out.counts), np.bincount(idx_r.ravel(), minlength=n))
+
+
 def test_qb_quantile_demo_full_size():
     # the page's demo: m = 100000, n = 256, k = 8, s = U(0,1) + U(0,1)_n, T = 5
     m, n, k = 100000, 256, 8
