@@ -170,7 +170,7 @@ __device__ __forceinline__ void ce_desc(float (&v)[NPL], int (&j)[NPL], int p, i
 
 constexpr int kRowsRegThreads = 1024;
 template <bool IDX, bool ALPHA, int NPL>
-__global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_reg(BalanceArgs a, const float* __restrict__ beta,
+__global__ __launch_bounds__(kRowsRegThreads, 8) void k_qb_rows_reg(BalanceArgs a, const float* __restrict__ beta,
                                                      float* __restrict__ alpha, uint64_t* __restrict__ chunks) {
   extern __shared__ __attribute__((aligned(16))) int hist[];   // [n], then the finishing scratch
   const int n = a.n, k = a.k;
@@ -269,6 +269,75 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_reg(BalanceArgs a, 
     if (int64_t(hist[j]) != a.q) atomicAnd(&s_bal, 0);
   __syncthreads();
   if (threadIdx.x == 0 && a.info) a.info[2] = s_bal;
+}
+
+// α only (no indices), n <= 256: two rows per wave, one per 32-lane half; lane
+// l of a half holds experts l + 32u (u < NPL) sorted by value in registers,
+// and each round every half pops its best head (half-wave DPP max).  Equal
+// values need no order here, since only the values of the order statistics are
+// kept.
+template <int NPL>
+__device__ __forceinline__ void sort_desc(float (&v)[NPL]) {
+  auto ce = [&](int p, int q) {
+    const float hi = fmaxf(v[p], v[q]), lo = fminf(v[p], v[q]);
+    v[p] = hi;
+    v[q] = lo;
+  };
+  if constexpr (NPL == 2) ce(0, 1);
+  if constexpr (NPL == 4) {
+    ce(0, 1), ce(2, 3), ce(0, 2), ce(1, 3), ce(1, 2);
+  }
+  if constexpr (NPL == 8) {   // Batcher's odd-even merge network, 19 exchanges
+    ce(0, 1), ce(2, 3), ce(4, 5), ce(6, 7), ce(0, 2), ce(1, 3), ce(4, 6), ce(5, 7), ce(1, 2), ce(5, 6);
+    ce(0, 4), ce(1, 5), ce(2, 6), ce(3, 7), ce(2, 4), ce(3, 5), ce(1, 2), ce(3, 4), ce(5, 6);
+  }
+}
+
+template <int NPL>
+__global__ __launch_bounds__(kRowsRegThreads) void k_qb_alpha_half(BalanceArgs a, const float* __restrict__ beta,
+                                                                   float* __restrict__ alpha) {
+  const int n = a.n;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hl = lane & 31, half = lane >> 5;
+  const int arank = a.quantile ? a.rank_row : a.k;
+  float bl[NPL];
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) bl[u] = hl + 32 * u < n ? beta[hl + 32 * u] : 0.f;
+  constexpr int kWaves = kRowsRegThreads / 64;
+  const int64_t stride = int64_t(gridDim.x) * kWaves * 2;
+  int64_t i = (int64_t(blockIdx.x) * kWaves + wave) * 2 + half;
+  float nx[NPL];
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) nx[u] = i < a.m && hl + 32 * u < n ? a.s[i * n + hl + 32 * u] : 0.f;
+  // both halves run the same number of iterations (the wave's first row decides)
+  for (int64_t i0 = i - half; i0 < a.m; i0 += stride, i += stride) {
+    float v[NPL];
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) v[u] = hl + 32 * u < n && i < a.m ? nx[u] - bl[u] : -INFINITY;
+    const int64_t i2 = i + stride;
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) nx[u] = i2 < a.m && hl + 32 * u < n ? a.s[i2 * n + hl + 32 * u] : 0.f;
+    sort_desc<NPL>(v);
+    float hi_key = INFINITY, lo_key = INFINITY;
+    for (int r = 0; r <= arank; ++r) {
+      const float mx = half_max(v[0]);
+      const uint64_t tied = __ballot(v[0] == mx);
+      const uint32_t tlo = uint32_t(tied), thi = uint32_t(tied >> 32);
+      const int wlo = tlo ? __ffs(tlo) - 1 : 0, whi = thi ? __ffs(thi) + 31 : 32;
+      if (r == arank - 1) hi_key = mx;
+      if (r == arank) lo_key = mx;
+      if (lane == (half ? whi : wlo)) {
+#pragma unroll
+        for (int u = 0; u + 1 < NPL; ++u) v[u] = v[u + 1];
+        v[NPL - 1] = -INFINITY;
+      }
+    }
+    if (hl == 0 && i < a.m) {
+      float al = lo_key;
+      if (a.quantile) al = lerp_np(lo_key, arank >= 1 ? hi_key : lo_key, a.g_row);
+      if (a.bip) al = fmaxf(al, 0.f);
+      alpha[i] = al;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ columns: an order statistic per expert
@@ -845,16 +914,20 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
   // per-workgroup count rows (ceil(m/16) are allocated) for the last workgroup to fold
   const int npl = a.n <= 64 ? 1 : a.n <= 128 ? 2 : a.n <= 256 ? 4 : 0;
   const unsigned gidx = unsigned(std::min<int64_t>(ceil_div64(a.m, 64), 512));
-  const unsigned galpha = unsigned(std::min<int64_t>(ceil_div64(a.m, 64), 1024));
   auto rows = [&](bool idx, bool al) {
 #define MOE_QB_ROWS(NPL)                                                                                      \
-  if (idx && al)                                                                                           \
+  if (al)                                                                                                  \
     hipLaunchKernelGGL((k_qb_rows_reg<true, true, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
-  else if (idx)                                                                                            \
-    hipLaunchKernelGGL((k_qb_rows_reg<true, false, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
   else                                                                                                     \
-    hipLaunchKernelGGL((k_qb_rows_reg<false, true, NPL>), dim3(galpha), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha, chunks);
-    if (npl == 1) {
+    hipLaunchKernelGGL((k_qb_rows_reg<true, false, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+    if (!idx && a.n <= 256) {
+      const int nh = a.n <= 32 ? 1 : a.n <= 64 ? 2 : a.n <= 128 ? 4 : 8;
+      const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), 1024));
+      if (nh == 1) hipLaunchKernelGGL(k_qb_alpha_half<1>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
+      if (nh == 2) hipLaunchKernelGGL(k_qb_alpha_half<2>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
+      if (nh == 4) hipLaunchKernelGGL(k_qb_alpha_half<4>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
+      if (nh == 8) hipLaunchKernelGGL(k_qb_alpha_half<8>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
+    } else if (npl == 1) {
       MOE_QB_ROWS(1)
     } else if (npl == 2) {
       MOE_QB_ROWS(2)
