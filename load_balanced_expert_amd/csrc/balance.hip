@@ -170,7 +170,7 @@ __device__ __forceinline__ void ce_desc(float (&v)[NPL], int (&j)[NPL], int p, i
 
 constexpr int kRowsRegThreads = 1024;
 template <bool IDX, bool ALPHA, int NPL>
-__global__ __launch_bounds__(kRowsRegThreads, 8) void k_qb_rows_reg(BalanceArgs a, const float* __restrict__ beta,
+__global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_reg(BalanceArgs a, const float* __restrict__ beta,
                                                      float* __restrict__ alpha, uint64_t* __restrict__ chunks) {
   extern __shared__ __attribute__((aligned(16))) int hist[];   // [n], then the finishing scratch
   const int n = a.n, k = a.k;
@@ -249,40 +249,19 @@ __global__ __launch_bounds__(kRowsRegThreads, 8) void k_qb_rows_reg(BalanceArgs 
     if (IDX && lane < k) a.idx[i * k + lane] = my_j;
   }
   if (!IDX) return;
-  __syncthreads();
-  for (int j = threadIdx.x; j < n; j += kRowsRegThreads) store_agent(chunks + int64_t(blockIdx.x) * n + j, pack_chunk(hist[j], 0.f));
-  __shared__ int s_flag;
-  if (!last_workgroup(a.done, gridDim.x, &s_flag)) return;
-  FinalizeArgs f{};
-  f.chunks = chunks;
-  f.nch = int(gridDim.x);
-  f.sup = super_chunk(f.nch);
-  f.n = n;
-  f.m = a.m;
-  f.counts = a.counts;
-  f.capacity = -1;
-  finalize_chunks(f, hist, n + 4096, kRowsRegThreads);
-  __shared__ int s_bal;
-  if (threadIdx.x == 0) s_bal = 1;
-  __syncthreads();
-  for (int j = threadIdx.x; j < n; j += kRowsRegThreads)
-    if (int64_t(hist[j]) != a.q) atomicAnd(&s_bal, 0);
-  __syncthreads();
-  if (threadIdx.x == 0 && a.info) a.info[2] = s_bal;
+  __syncthreads();   // this workgroup's count row; k_qb_count_finish folds them
+  for (int j = threadIdx.x; j < n; j += kRowsRegThreads) chunks[int64_t(blockIdx.x) * n + j] = pack_chunk(hist[j], 0.f);
 }
 
-// α only (no indices), n <= 256: two rows per wave, one per 32-lane half; lane
-// l of a half holds experts l + 32u (u < NPL) sorted by value in registers,
-// and each round every half pops its best head (half-wave DPP max).  Equal
-// values need no order here, since only the values of the order statistics are
-// kept.
-template <int NPL>
-__device__ __forceinline__ void sort_desc(float (&v)[NPL]) {
-  auto ce = [&](int p, int q) {
-    const float hi = fmaxf(v[p], v[q]), lo = fminf(v[p], v[q]);
-    v[p] = hi;
-    v[q] = lo;
-  };
+// n <= 256 (and k <= 32 when counting): two rows per wave, one per 32-lane
+// half; lane l of a half holds experts l + 32u (u < NPL) sorted in registers
+// (by value, and by index among equal values when the picks are wanted), and
+// each round every half pops its best head (half-wave DPP max; among equal
+// heads the lowest expert).  Without picks equal values need no order, since
+// only the values of the order statistics are kept.
+template <bool USEJ, int NPL>
+__device__ __forceinline__ void sort_desc(float (&v)[NPL], int (&j)[NPL]) {
+  auto ce = [&](int p, int q) { ce_desc<USEJ, NPL>(v, j, p, q); };
   if constexpr (NPL == 2) ce(0, 1);
   if constexpr (NPL == 4) {
     ce(0, 1), ce(2, 3), ce(0, 2), ce(1, 3), ce(1, 2);
@@ -293,12 +272,19 @@ __device__ __forceinline__ void sort_desc(float (&v)[NPL]) {
   }
 }
 
-template <int NPL>
-__global__ __launch_bounds__(kRowsRegThreads) void k_qb_alpha_half(BalanceArgs a, const float* __restrict__ beta,
-                                                                   float* __restrict__ alpha) {
-  const int n = a.n;
+template <bool IDX, bool ALPHA, int NPL>
+__global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_half(BalanceArgs a, const float* __restrict__ beta,
+                                                                     float* __restrict__ alpha,
+                                                                     uint64_t* __restrict__ chunks) {
+  extern __shared__ __attribute__((aligned(16))) int hist[];   // [n], then the finishing scratch
+  const int n = a.n, k = a.k;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hl = lane & 31, half = lane >> 5;
-  const int arank = a.quantile ? a.rank_row : a.k;
+  if (IDX) {
+    for (int j = threadIdx.x; j < n; j += kRowsRegThreads) hist[j] = 0;
+    __syncthreads();
+  }
+  const int arank = a.quantile ? a.rank_row : k;
+  const int rounds = ALPHA ? (IDX ? max(k, arank + 1) : arank + 1) : k;
   float bl[NPL];
 #pragma unroll
   for (int u = 0; u < NPL; ++u) bl[u] = hl + 32 * u < n ? beta[hl + 32 * u] : 0.f;
@@ -310,34 +296,85 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_alpha_half(BalanceArgs a
   for (int u = 0; u < NPL; ++u) nx[u] = i < a.m && hl + 32 * u < n ? a.s[i * n + hl + 32 * u] : 0.f;
   // both halves run the same number of iterations (the wave's first row decides)
   for (int64_t i0 = i - half; i0 < a.m; i0 += stride, i += stride) {
+    const bool live = i < a.m;
     float v[NPL];
+    int jj[NPL];
 #pragma unroll
-    for (int u = 0; u < NPL; ++u) v[u] = hl + 32 * u < n && i < a.m ? nx[u] - bl[u] : -INFINITY;
+    for (int u = 0; u < NPL; ++u) {
+      const int j = hl + 32 * u;
+      v[u] = j < n && live ? nx[u] - bl[u] : -INFINITY;
+      jj[u] = j < n ? j : 0x7FFFFFFF;
+    }
     const int64_t i2 = i + stride;
 #pragma unroll
     for (int u = 0; u < NPL; ++u) nx[u] = i2 < a.m && hl + 32 * u < n ? a.s[i2 * n + hl + 32 * u] : 0.f;
-    sort_desc<NPL>(v);
+    sort_desc<IDX, NPL>(v, jj);
     float hi_key = INFINITY, lo_key = INFINITY;
-    for (int r = 0; r <= arank; ++r) {
+    int my_j = 0;
+    for (int r = 0; r < rounds; ++r) {
       const float mx = half_max(v[0]);
-      const uint64_t tied = __ballot(v[0] == mx);
+      bool top = v[0] == mx;
+      uint64_t tied = __ballot(top);
+      if (IDX && r < k && (__popc(uint32_t(tied)) > 1 || __popc(uint32_t(tied >> 32)) > 1)) {
+        // equal heads: the lowest expert goes first
+        const int mj = half_min_i(top ? jj[0] : 0x7FFFFFFF);
+        top = top && jj[0] == mj;
+        tied = __ballot(top);
+      }
       const uint32_t tlo = uint32_t(tied), thi = uint32_t(tied >> 32);
       const int wlo = tlo ? __ffs(tlo) - 1 : 0, whi = thi ? __ffs(thi) + 31 : 32;
+      const int win = half ? whi : wlo;
+      if (IDX && r < k) {
+        const int bj = __shfl(jj[0], win, 64);
+        if (hl == r) my_j = bj;
+        if (hl == 0 && live) atomicAdd(&hist[bj], 1);
+      }
       if (r == arank - 1) hi_key = mx;
       if (r == arank) lo_key = mx;
-      if (lane == (half ? whi : wlo)) {
+      if (lane == win) {
 #pragma unroll
-        for (int u = 0; u + 1 < NPL; ++u) v[u] = v[u + 1];
+        for (int u = 0; u + 1 < NPL; ++u) {
+          v[u] = v[u + 1];
+          if (IDX) jj[u] = jj[u + 1];
+        }
         v[NPL - 1] = -INFINITY;
+        if (IDX) jj[NPL - 1] = 0x7FFFFFFF;
       }
     }
-    if (hl == 0 && i < a.m) {
+    if (ALPHA && hl == 0 && live) {
       float al = lo_key;
       if (a.quantile) al = lerp_np(lo_key, arank >= 1 ? hi_key : lo_key, a.g_row);
       if (a.bip) al = fmaxf(al, 0.f);
       alpha[i] = al;
     }
+    if (IDX && hl < k && live) a.idx[i * k + hl] = my_j;
   }
+  if (!IDX) return;
+  __syncthreads();   // this workgroup's count row; k_qb_count_finish folds them
+  for (int j = threadIdx.x; j < n; j += kRowsRegThreads) chunks[int64_t(blockIdx.x) * n + j] = pack_chunk(hist[j], 0.f);
+}
+
+// Counts of the final top-k from the register row kernels' count rows, and
+// whether every expert holds exactly q tokens.  One 1024-thread workgroup.
+__global__ __launch_bounds__(kRowsRegThreads) void k_qb_count_finish(BalanceArgs a, const uint64_t* __restrict__ chunks,
+                                                                     int nch) {
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  FinalizeArgs f{};
+  f.chunks = chunks;
+  f.nch = nch;
+  f.sup = super_chunk(nch);
+  f.n = a.n;
+  f.m = a.m;
+  f.counts = a.counts;
+  f.capacity = -1;
+  finalize_chunks(f, lds, a.n + 4096, kRowsRegThreads);
+  __shared__ int s_bal;
+  if (threadIdx.x == 0) s_bal = 1;
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.n; j += kRowsRegThreads)
+    if (int64_t(lds[j]) != a.q) atomicAnd(&s_bal, 0);
+  __syncthreads();
+  if (threadIdx.x == 0 && a.info) a.info[2] = s_bal;
 }
 
 // ------------------------------------------------------------------ columns: an order statistic per expert
@@ -920,19 +957,38 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
     hipLaunchKernelGGL((k_qb_rows_reg<true, true, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
   else                                                                                                     \
     hipLaunchKernelGGL((k_qb_rows_reg<true, false, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
-    if (!idx && a.n <= 256) {
+    // (the counting form with 8 experts per lane needs too many registers: whole-wave rows above 128)
+    if (a.n <= 256 && (!idx || (a.k <= 32 && a.n <= 128))) {
       const int nh = a.n <= 32 ? 1 : a.n <= 64 ? 2 : a.n <= 128 ? 4 : 8;
-      const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), 1024));
-      if (nh == 1) hipLaunchKernelGGL(k_qb_alpha_half<1>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
-      if (nh == 2) hipLaunchKernelGGL(k_qb_alpha_half<2>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
-      if (nh == 4) hipLaunchKernelGGL(k_qb_alpha_half<4>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
-      if (nh == 8) hipLaunchKernelGGL(k_qb_alpha_half<8>, dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha);
+      // two rows per wave; the counting form keeps at most 512 count rows
+      const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), idx ? 512 : 1024));
+#define MOE_QB_HALF(NH)                                                                                        \
+  if (idx && al)                                                                                            \
+    hipLaunchKernelGGL((k_qb_rows_half<true, true, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
+  else if (idx)                                                                                             \
+    hipLaunchKernelGGL((k_qb_rows_half<true, false, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
+  else                                                                                                      \
+    hipLaunchKernelGGL((k_qb_rows_half<false, true, NH>), dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha, chunks);
+      if (nh == 1) {
+        MOE_QB_HALF(1)
+      } else if (nh == 2) {
+        MOE_QB_HALF(2)
+      } else if (nh == 4) {
+        MOE_QB_HALF(4)
+      } else {
+        MOE_QB_HALF(8)
+      }
+#undef MOE_QB_HALF
+      if (idx) hipLaunchKernelGGL(k_qb_count_finish, dim3(1), dim3(kRowsRegThreads), rlds, s, a, chunks, int(gh));
     } else if (npl == 1) {
       MOE_QB_ROWS(1)
+      hipLaunchKernelGGL(k_qb_count_finish, dim3(1), dim3(kRowsRegThreads), rlds, s, a, chunks, int(gidx));
     } else if (npl == 2) {
       MOE_QB_ROWS(2)
+      hipLaunchKernelGGL(k_qb_count_finish, dim3(1), dim3(kRowsRegThreads), rlds, s, a, chunks, int(gidx));
     } else if (npl == 4) {
       MOE_QB_ROWS(4)
+      hipLaunchKernelGGL(k_qb_count_finish, dim3(1), dim3(kRowsRegThreads), rlds, s, a, chunks, int(gidx));
     } else if (idx && al) {
       hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
     } else if (idx) {
