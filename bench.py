@@ -65,7 +65,7 @@ def parse():
 # Sources that decide each kernel's code and launch shape; a committed counter
 # profile is used only while these are unchanged.
 KERNEL_SOURCES = {
-    "route": ("route.hip", "common.hpp", "prefix.hpp", "kernels.hpp", "api.hip"),
+    "route": ("route.hip", "common.hpp", "dpp.hpp", "prefix.hpp", "kernels.hpp", "api.hip"),
     "dispatch": ("dispatch.hip", "common.hpp", "prefix.hpp", "kernels.hpp", "api.hip"),
     "combine": ("combine.hip", "common.hpp", "kernels.hpp", "api.hip"),
     "ffn": ("ffn.hip", "common.hpp", "kernels.hpp", "api.hip"),
