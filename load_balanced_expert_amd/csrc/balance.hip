@@ -437,11 +437,37 @@ __device__ __forceinline__ void col_select(const int* hist, int nb, int rank, in
   __syncthreads();
 }
 
-// f(key, active) over the column, four loads in flight per thread
+// f(key, active) over the column in no particular order.  A column whose
+// length is a multiple of 4, with α 16-byte aligned (the transposed copy starts
+// on 256 bytes in an aligned workspace), is read as float4 pairs (8 keys per
+// thread per step); otherwise four scalar loads at a time.
 template <typename F>
 __device__ __forceinline__ void col_scan(const float* __restrict__ col, const float* __restrict__ alpha, int64_t m,
                                          F f) {
-  for (int64_t b = threadIdx.x; b < m; b += 4 * kColThreads) {
+  if ((m & 3) == 0 && ((reinterpret_cast<uintptr_t>(col) | reinterpret_cast<uintptr_t>(alpha)) & 15) == 0) {
+    const int64_t nv = m >> 2;
+    const f32x4* c4 = reinterpret_cast<const f32x4*>(col);
+    const f32x4* a4 = reinterpret_cast<const f32x4*>(alpha);
+    for (int64_t b = threadIdx.x; b - threadIdx.x < nv; b += 2 * kColThreads) {   // uniform trip count
+      f32x4 x[2], al[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t v = b + int64_t(u) * kColThreads;
+        x[u] = v < nv ? c4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+        al[u] = v < nv ? a4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool act = b + int64_t(u) * kColThreads < nv;
+        f(f32_key(x[u][0] - al[u][0]), act);
+        f(f32_key(x[u][1] - al[u][1]), act);
+        f(f32_key(x[u][2] - al[u][2]), act);
+        f(f32_key(x[u][3] - al[u][3]), act);
+      }
+    }
+    return;
+  }
+  for (int64_t b = threadIdx.x; b - threadIdx.x < m; b += 4 * kColThreads) {   // uniform trip count
     float x[4], al[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -454,94 +480,190 @@ __device__ __forceinline__ void col_scan(const float* __restrict__ col, const fl
   }
 }
 
+// Radix select of descending rank `rank` over keys[0..nk) in LDS (12 + 12 + 8
+// bits): the key, and its rank among the keys equal to it.
+__device__ __forceinline__ void lds_select(const uint32_t* keys, int nk, int rank, int* hist, int* s_wsum, int* s_bin,
+                                           int* s_rank, uint32_t& key, int& rank_out) {
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
+  __syncthreads();
+  for (int t = tid; t - tid < nk; t += kColThreads) {
+    const bool act = t < nk;
+    hist_add(hist, act ? keys[t] >> 20 : 0u, act);
+  }
+  __syncthreads();
+  col_select(hist, kColBins, rank, s_wsum, s_bin, s_rank);
+  const uint32_t b1 = uint32_t(*s_bin);
+  rank = *s_rank;
+  __syncthreads();
+  for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
+  __syncthreads();
+  for (int t = tid; t - tid < nk; t += kColThreads) {
+    const bool act = t < nk && (keys[t] >> 20) == b1;
+    hist_add(hist, act ? (keys[t] >> 8) & 0xFFFu : 0u, act);
+  }
+  __syncthreads();
+  col_select(hist, kColBins, rank, s_wsum, s_bin, s_rank);
+  const uint32_t p2 = (b1 << 12) | uint32_t(*s_bin);   // key >> 8
+  rank = *s_rank;
+  __syncthreads();
+  for (int b = tid; b < 256; b += kColThreads) hist[b] = 0;
+  __syncthreads();
+  for (int t = tid; t - tid < nk; t += kColThreads) {
+    const bool act = t < nk && (keys[t] >> 8) == p2;
+    hist_add(hist, act ? keys[t] & 0xFFu : 0u, act);
+  }
+  __syncthreads();
+  col_select(hist, 256, rank, s_wsum, s_bin, s_rank);
+  key = (p2 << 8) | uint32_t(*s_bin);
+  rank_out = *s_rank;
+  __syncthreads();
+}
+
+// Appends the keys with take == true to keys[] (wave-aggregated slots);
+// slots past the capacity set *ovf instead.
+__device__ __forceinline__ void lds_append(uint32_t* keys, int* s_nk, int* s_ovf, uint32_t u, bool take) {
+  const uint64_t bm = __ballot(take);
+  if (!bm) return;
+  const int lead = __ffsll((unsigned long long)bm) - 1;
+  int base = 0;
+  if ((threadIdx.x & 63) == lead) base = atomicAdd(s_nk, __popcll(bm));
+  base = __builtin_amdgcn_readlane(base, lead);
+  const int at = base + __popcll(bm & lanemask_lt());
+  if (take && at < kColCap) keys[at] = u;
+  if (take && at >= kColCap) *s_ovf = 1;
+}
+
+// Column order statistic.  Columns that fit in LDS are copied there whole.
+// Longer ones: a sample of about 4096 keys in 32-key segments (one segment per
+// 512 keys or sparser) is copied to LDS and two of its order statistics bound a
+// key window expected to hold the wanted rank (4 standard deviations of the
+// sample rank plus 8); one pass over the column then counts the keys above the
+// window and copies the window's keys to LDS, and the rank is selected there.
+// When the window misses the rank or overflows LDS, the exact radix passes
+// over the column run instead.
 __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict__ sT,
                                                          const float* __restrict__ alpha, float* __restrict__ beta,
                                                          BalanceArgs a) {
   extern __shared__ __attribute__((aligned(16))) int hist[];   // [kColBins], then [kColCap] keys
   uint32_t* keys = reinterpret_cast<uint32_t*>(hist + kColBins);
-  __shared__ int s_wsum[kColThreads / 64], s_bin, s_rank, s_nk;
+  __shared__ int s_wsum[kColThreads / 64], s_bin, s_rank, s_nk, s_ovf, s_above;
   __shared__ uint32_t s_min;
-  const int j = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int j = blockIdx.x, tid = threadIdx.x;
   const int64_t m = a.m;
   const float* col = sT + int64_t(j) * m;
   const int rank0 = int(a.quantile ? a.rank_col : a.q);   // 0-based rank in descending order
-  for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
   if (tid == 0) {
     s_nk = 0;
+    s_ovf = 0;
+    s_above = 0;
     s_min = 0xFFFFFFFFu;
   }
   __syncthreads();
-  col_scan(col, alpha, m, [&](uint32_t u, bool act) { hist_add(hist, u >> 20, act); });
+  // ---- key window [k_lo, k_hi]
+  uint32_t k_lo = 0, k_hi = 0xFFFFFFFFu;
+  if (m > kColCap) {
+    // at most 128 segments of 32 keys: 4096 samples, within kColCap
+    const int64_t period = 32 * std::max<int64_t>(16, ceil_div64(m, 4096));
+    const int64_t nseg = ceil_div64(m, period);
+    for (int64_t t = tid; t - tid < nseg * 32; t += kColThreads) {   // uniform trip count
+      const int64_t i = (t >> 5) * period + (t & 31);
+      const bool act = t < nseg * 32 && i < m;
+      const uint32_t u = act ? f32_key(col[i] - alpha[i]) : 0u;
+      lds_append(keys, &s_nk, &s_ovf, u, act);
+    }
+    __syncthreads();
+    const int ns = min(s_nk, kColCap);
+    const bool sampled = !s_ovf && ns > 0;
+    __syncthreads();   // every thread has read the counters
+    if (sampled) {
+      const double rs = double(rank0) * double(ns) / double(m);
+      const int dev = int(4.0 * sqrt(fmax(rs * (1.0 - rs / double(ns)), 0.0))) + 8;
+      const int r_hi = int(rs) - dev, r_lo = int(rs) + dev;
+      int rr;
+      if (r_hi > 0) lds_select(keys, ns, r_hi, hist, s_wsum, &s_bin, &s_rank, k_hi, rr);
+      if (r_lo < ns - 1) lds_select(keys, ns, r_lo, hist, s_wsum, &s_bin, &s_rank, k_lo, rr);
+    }
+    if (tid == 0) {
+      s_nk = 0;
+      s_ovf = 0;
+    }
+    __syncthreads();
+  }
+  // ---- one pass: keys above the window counted, the window's keys to LDS
+  int above = 0;
+  uint32_t mn = 0xFFFFFFFFu;   // least key above the window
+  col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+    if (act && u > k_hi) {
+      ++above;
+      mn = min(mn, u);
+    }
+    lds_append(keys, &s_nk, &s_ovf, u, act && u >= k_lo && u <= k_hi);
+  });
+  atomicAdd(&s_above, above);
   __syncthreads();
-  col_select(hist, kColBins, rank0, s_wsum, &s_bin, &s_rank);
-  const uint32_t b1 = uint32_t(s_bin);
-  int rank = s_rank;
-  const bool in_lds = hist[b1] <= kColCap;
-  uint32_t mn = 0xFFFFFFFFu;   // least key in a higher first-digit bin
-  __syncthreads();
-  for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
-  __syncthreads();
+  const int nabove = s_above, nk = s_nk;
+  const bool hit = !s_ovf && nabove <= rank0 && rank0 < nabove + nk;
+  __syncthreads();   // every thread has read the counters
   uint32_t prefix;
-  if (in_lds) {
-    col_scan(col, alpha, m, [&](uint32_t u, bool act) {
-      const bool take = act && (u >> 20) == b1;
-      if (act && (u >> 20) > b1) mn = min(mn, u);
-      const uint64_t bm = __ballot(take);
-      if (!bm) return;
-      const int lead = __ffsll((unsigned long long)bm) - 1;
-      int base = 0;
-      if (lane == lead) base = atomicAdd(&s_nk, __popcll(bm));
-      base = __builtin_amdgcn_readlane(base, lead);
-      if (take) keys[base + __popcll(bm & lanemask_lt())] = u;
-    });
-    __syncthreads();
-    const int nk = s_nk;
-    for (int t = tid; t - tid < nk; t += kColThreads) {
-      const bool act = t < nk;
-      hist_add(hist, act ? (keys[t] >> 8) & 0xFFFu : 0u, act);
-    }
-    __syncthreads();
-    col_select(hist, kColBins, rank, s_wsum, &s_bin, &s_rank);
-    const uint32_t p2 = (b1 << 12) | uint32_t(s_bin);   // key >> 8
-    rank = s_rank;
-    __syncthreads();
-    for (int b = tid; b < 256; b += kColThreads) hist[b] = 0;
-    __syncthreads();
-    for (int t = tid; t - tid < nk; t += kColThreads) {
-      const bool act = t < nk && (keys[t] >> 8) == p2;
-      hist_add(hist, act ? keys[t] & 0xFFu : 0u, act);
-    }
-    __syncthreads();
-    col_select(hist, 256, rank, s_wsum, &s_bin, &s_rank);
-    prefix = (p2 << 8) | uint32_t(s_bin);
-    rank = s_rank;
+  int rank;
+  if (hit) {
+    lds_select(keys, nk, rank0 - nabove, hist, s_wsum, &s_bin, &s_rank, prefix, rank);
     if (a.quantile && rank == 0)
       for (int t = tid; t < nk; t += kColThreads)
         if (keys[t] > prefix) mn = min(mn, keys[t]);
   } else {
-    col_scan(col, alpha, m, [&](uint32_t u, bool act) {
-      const bool take = act && (u >> 20) == b1;
-      hist_add(hist, take ? (u >> 8) & 0xFFFu : 0u, take);
-    });
+    // exact radix passes over the column: 12 top bits, then the chosen bin's
+    // keys in LDS when they fit, else two more passes (12 and 8 bits)
+    mn = 0xFFFFFFFFu;
+    for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
+    if (tid == 0) s_nk = 0;
     __syncthreads();
-    col_select(hist, kColBins, rank, s_wsum, &s_bin, &s_rank);
-    const uint32_t p2 = (b1 << 12) | uint32_t(s_bin);
+    col_scan(col, alpha, m, [&](uint32_t u, bool act) { hist_add(hist, u >> 20, act); });
+    __syncthreads();
+    col_select(hist, kColBins, rank0, s_wsum, &s_bin, &s_rank);
+    const uint32_t b1 = uint32_t(s_bin);
     rank = s_rank;
+    const bool in_lds = hist[b1] <= kColCap;
     __syncthreads();
-    for (int b = tid; b < 256; b += kColThreads) hist[b] = 0;
-    __syncthreads();
-    col_scan(col, alpha, m, [&](uint32_t u, bool act) {
-      const bool take = act && (u >> 8) == p2;
-      hist_add(hist, take ? u & 0xFFu : 0u, take);
-    });
-    __syncthreads();
-    col_select(hist, 256, rank, s_wsum, &s_bin, &s_rank);
-    prefix = (p2 << 8) | uint32_t(s_bin);
-    rank = s_rank;
-    if (a.quantile && rank == 0)
+    if (in_lds) {
       col_scan(col, alpha, m, [&](uint32_t u, bool act) {
-        if (act && u > prefix) mn = min(mn, u);
+        if (act && (u >> 20) > b1) mn = min(mn, u);
+        lds_append(keys, &s_nk, &s_ovf, u, act && (u >> 20) == b1);
       });
+      __syncthreads();
+      const int nb = s_nk;
+      lds_select(keys, nb, rank, hist, s_wsum, &s_bin, &s_rank, prefix, rank);
+      if (a.quantile && rank == 0)
+        for (int t = tid; t < nb; t += kColThreads)
+          if (keys[t] > prefix) mn = min(mn, keys[t]);
+    } else {
+      for (int b = tid; b < kColBins; b += kColThreads) hist[b] = 0;
+      __syncthreads();
+      col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+        const bool take = act && (u >> 20) == b1;
+        hist_add(hist, take ? (u >> 8) & 0xFFFu : 0u, take);
+      });
+      __syncthreads();
+      col_select(hist, kColBins, rank, s_wsum, &s_bin, &s_rank);
+      const uint32_t p2 = (b1 << 12) | uint32_t(s_bin);
+      rank = s_rank;
+      __syncthreads();
+      for (int b = tid; b < 256; b += kColThreads) hist[b] = 0;
+      __syncthreads();
+      col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+        const bool take = act && (u >> 8) == p2;
+        hist_add(hist, take ? u & 0xFFu : 0u, take);
+      });
+      __syncthreads();
+      col_select(hist, 256, rank, s_wsum, &s_bin, &s_rank);
+      prefix = (p2 << 8) | uint32_t(s_bin);
+      rank = s_rank;
+      if (a.quantile && rank == 0)
+        col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+          if (act && u > prefix) mn = min(mn, u);
+        });
+    }
   }
   float bv = key_f32(prefix);
   if (a.quantile) {

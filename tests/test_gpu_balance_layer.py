@@ -69,6 +69,7 @@ def test_qb_quantile_bit_exact(m, n, k, iters, bip):
     (1600, 320, 4, 0),       # more than 256 experts: the row kernel's arg-best rounds
     (4096, 64, 4, 4),        # scores on a grid of 4 values: equal heads, lowest expert first
     (120000, 8, 2, 2),       # two score values: the column bin overflows LDS, selected in global passes
+    (30002, 6, 3, 0),        # columns longer than LDS holds, length not a multiple of 4: sampled window, scalar loads
 ])
 @pytest.mark.parametrize("quantile", [False, True])
 def test_qb_kernel_paths(m, n, k, levels, quantile):
