@@ -388,6 +388,8 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_count_finish(BalanceArgs
 constexpr int kColThreads = 1024;
 constexpr int kColBins = 4096;
 constexpr int kColCap = 24576;
+constexpr int kColWaveSlots = 1024;                       // per-wave window slots (long columns)
+constexpr int kColPackOff = kColWaveSlots * (kColThreads / 64);   // packed window keys after them
 constexpr size_t kColLds = (size_t(kColBins) + kColCap) * sizeof(int);
 
 __device__ __forceinline__ void hist_add(int* hist, uint32_t d, bool act) {
@@ -539,7 +541,8 @@ __device__ __forceinline__ void lds_append(uint32_t* keys, int* s_nk, int* s_ovf
 // 512 keys or sparser) is copied to LDS and two of its order statistics bound a
 // key window expected to hold the wanted rank (4 standard deviations of the
 // sample rank plus 8); one pass over the column then counts the keys above the
-// window and copies the window's keys to LDS, and the rank is selected there.
+// window and copies the window's keys to LDS (per-wave slots, then packed),
+// and the rank is selected there.
 // When the window misses the rank or overflows LDS, the exact radix passes
 // over the column run instead.
 __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict__ sT,
@@ -547,7 +550,7 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
                                                          BalanceArgs a) {
   extern __shared__ __attribute__((aligned(16))) int hist[];   // [kColBins], then [kColCap] keys
   uint32_t* keys = reinterpret_cast<uint32_t*>(hist + kColBins);
-  __shared__ int s_wsum[kColThreads / 64], s_bin, s_rank, s_nk, s_ovf, s_above;
+  __shared__ int s_wsum[kColThreads / 64], s_wcnt[kColThreads / 64], s_bin, s_rank, s_nk, s_ovf, s_above;
   __shared__ uint32_t s_min;
   const int j = blockIdx.x, tid = threadIdx.x;
   const int64_t m = a.m;
@@ -593,25 +596,60 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
   // ---- one pass: keys above the window counted, the window's keys to LDS
   int above = 0;
   uint32_t mn = 0xFFFFFFFFu;   // least key above the window
-  col_scan(col, alpha, m, [&](uint32_t u, bool act) {
-    if (act && u > k_hi) {
-      ++above;
-      mn = min(mn, u);
+  uint32_t* wk = keys;         // the window's keys, contiguous
+  int nk;
+  bool w_ovf;
+  if (m <= kColCap) {   // the whole column: one shared append counter
+    col_scan(col, alpha, m, [&](uint32_t u, bool act) { lds_append(keys, &s_nk, &s_ovf, u, act); });
+    __syncthreads();
+    nk = s_nk;
+    w_ovf = s_ovf;
+  } else {
+    // each wave appends to slots of its own (no shared counter in the loop),
+    // then the waves' keys are packed after those slots
+    const int wave = tid >> 6, lane = tid & 63;
+    uint32_t* slots = keys + wave * kColWaveSlots;
+    int wcnt = 0;
+    col_scan(col, alpha, m, [&](uint32_t u, bool act) {
+      if (act && u > k_hi) {
+        ++above;
+        mn = min(mn, u);
+      }
+      const bool take = act && u >= k_lo && u <= k_hi;
+      const uint64_t bm = __ballot(take);
+      if (!bm) return;
+      const int at = wcnt + __popcll(bm & lanemask_lt());
+      if (take && at < kColWaveSlots) slots[at] = u;
+      wcnt += __popcll(bm);
+    });
+    if (lane == 0) s_wcnt[wave] = wcnt;
+    __syncthreads();
+    int off = 0, tot = 0;
+    w_ovf = false;
+    for (int v = 0; v < kColThreads / 64; ++v) {
+      const int c = s_wcnt[v];
+      w_ovf |= c > kColWaveSlots;
+      off += v < wave ? c : 0;
+      tot += c;
     }
-    lds_append(keys, &s_nk, &s_ovf, u, act && u >= k_lo && u <= k_hi);
-  });
+    w_ovf |= tot > kColCap - kColPackOff;
+    wk = keys + kColPackOff;
+    if (!w_ovf)
+      for (int q = lane; q < wcnt; q += 64) wk[off + q] = slots[q];
+    nk = tot;
+  }
   atomicAdd(&s_above, above);
   __syncthreads();
-  const int nabove = s_above, nk = s_nk;
-  const bool hit = !s_ovf && nabove <= rank0 && rank0 < nabove + nk;
+  const int nabove = s_above;
+  const bool hit = !w_ovf && nabove <= rank0 && rank0 < nabove + nk;
   __syncthreads();   // every thread has read the counters
   uint32_t prefix;
   int rank;
   if (hit) {
-    lds_select(keys, nk, rank0 - nabove, hist, s_wsum, &s_bin, &s_rank, prefix, rank);
+    lds_select(wk, nk, rank0 - nabove, hist, s_wsum, &s_bin, &s_rank, prefix, rank);
     if (a.quantile && rank == 0)
       for (int t = tid; t < nk; t += kColThreads)
-        if (keys[t] > prefix) mn = min(mn, keys[t]);
+        if (wk[t] > prefix) mn = min(mn, wk[t]);
   } else {
     // exact radix passes over the column: 12 top bits, then the chosen bin's
     // keys in LDS when they fit, else two more passes (12 and 8 bits)
