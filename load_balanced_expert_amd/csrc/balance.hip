@@ -1117,8 +1117,8 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
     hipLaunchKernelGGL((k_qb_rows_reg<true, true, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
   else                                                                                                     \
     hipLaunchKernelGGL((k_qb_rows_reg<true, false, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
-    // (the counting form with 8 experts per lane needs too many registers: whole-wave rows above 128)
-    if (a.n <= 256 && (!idx || (a.k <= 32 && a.n <= 128))) {
+    // (half-wave rows; the counting form needs a lane per pick in each half: k <= 32)
+    if (a.n <= 256 && (!idx || a.k <= 32)) {
       const int nh = a.n <= 32 ? 1 : a.n <= 64 ? 2 : a.n <= 128 ? 4 : 8;
       // two rows per wave; the counting form keeps at most 512 count rows
       const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), idx ? 512 : 1024));
