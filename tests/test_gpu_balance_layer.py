@@ -70,6 +70,7 @@ def test_qb_quantile_bit_exact(m, n, k, iters, bip):
     (4096, 64, 4, 4),        # scores on a grid of 4 values: equal heads, lowest expert first
     (120000, 8, 2, 2),       # two score values: the column bin overflows LDS, selected in global passes
     (30002, 6, 3, 0),        # columns longer than LDS holds, length not a multiple of 4: sampled window, scalar loads
+    (1000, 80, 40, 0),       # more than 32 picks: the counting top-k on whole-wave rows
 ])
 @pytest.mark.parametrize("quantile", [False, True])
 def test_qb_kernel_paths(m, n, k, levels, quantile):
