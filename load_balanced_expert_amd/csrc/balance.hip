@@ -1120,8 +1120,9 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
     // (half-wave rows; the counting form needs a lane per pick in each half: k <= 32)
     if (a.n <= 256 && (!idx || a.k <= 32)) {
       const int nh = a.n <= 32 ? 1 : a.n <= 64 ? 2 : a.n <= 128 ? 4 : 8;
-      // two rows per wave; the counting form keeps at most 512 count rows
-      const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), idx ? 512 : 1024));
+      // two rows per wave; the counting form keeps at most 256 count rows (one
+      // workgroup per CU: its registers allow no more) for k_qb_count_finish to fold
+      const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), idx ? 256 : 1024));
 #define MOE_QB_HALF(NH)                                                                                        \
   if (idx && al)                                                                                            \
     hipLaunchKernelGGL((k_qb_rows_half<true, true, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
