@@ -116,6 +116,35 @@ def qb_solve_quantile(s: np.ndarray, k: int, iters: int, bip: bool = False, beta
     return topk_biased(s, beta, k), beta, alpha
 
 
+# ------------------------------------------------------------------ SignSGD on β
+def dual_of_beta(s: np.ndarray, beta: np.ndarray, k: int) -> float:
+    """ℓ(β) = Σ_i (sum of the k largest of s_i − β) + q Σ_j β_j in float64: eq. (8)
+    with α at its best value for β ("분할정복"), which the gradient steps descend."""
+    m, n = s.shape
+    q = m * k // n
+    v = s.astype(np.float64) - np.asarray(beta, np.float64)[None, :]
+    top = -np.sort(-v, axis=1)[:, :k]
+    return float(top.sum() + q * np.asarray(beta, np.float64).sum())
+
+
+def signsgd_solve(s: np.ndarray, k: int, iters: int, gamma: float, beta0: Optional[np.ndarray] = None):
+    """[MoE tour 6] "경사하강" eq. (15)-(17): β_j ← β_j − γ·sign(∂ℓ/∂β_j) with
+    ∂ℓ/∂β_j = q − c_j, c_j the number of tokens whose top-k of fl32(s_i − β)
+    holds j (reading: the page counts s_ij − α_i − β_j > 0 with α_i the
+    (k+1)-th largest, the same set whenever a row's k-th and (k+1)-th values
+    differ; ties go to the lower expert as in the routing).  fp32 update
+    fl32(β_j + γ·sign(c_j − q)).  Returns (idx of the final β, beta, counts)."""
+    m, n = s.shape
+    q = m * k // n
+    beta = np.zeros(n, np.float32) if beta0 is None else np.asarray(beta0, np.float32).copy()
+    g = np.float32(gamma)
+    for _ in range(iters):
+        c = np.bincount(topk_biased(s, beta, k).ravel(), minlength=n)
+        beta = (beta + g * np.sign(c - q).astype(np.float32)).astype(np.float32)
+    idx = topk_biased(s, beta, k)
+    return idx, beta, np.bincount(idx.ravel(), minlength=n).astype(np.int32)
+
+
 # ------------------------------------------------------------------ assignments
 def idx_to_x(idx: np.ndarray, n: int) -> np.ndarray:
     m = idx.shape[0]

@@ -200,3 +200,35 @@ def test_full_size_completion_matches_highs():
     xl, obj = B.lp_highs(s, spec.k)
     assert np.array_equal(comp.x, xl > 0.5)
     assert B.objective(s, comp.x) == pytest.approx(obj, rel=1e-12)
+
+
+# ------------------------------------------------------------------ SignSGD on β (eq. (15)-(17))
+def test_signsgd_gradient_is_dual_slope():
+    # ∂ℓ/∂β_j = q − c_j: central differences of the dual ℓ(β) at a generic β, small
+    # enough that no row's top-k changes, equal q − c_j exactly (ℓ is piecewise linear)
+    rng = np.random.default_rng(3)
+    m, n, k = 240, 12, 3
+    s = rng.standard_normal((m, n)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(n)).astype(np.float32)
+    c = np.bincount(B.topk_biased(s, beta, k).ravel(), minlength=n)
+    q = m * k // n
+    for j in range(n):
+        e = np.zeros(n)
+        e[j] = 1e-7
+        d = (B.dual_of_beta(s, beta + e, k) - B.dual_of_beta(s, beta - e, k)) / 2e-7
+        assert abs(d - (q - c[j])) < 1e-3
+
+
+def test_signsgd_step_and_progress():
+    rng = np.random.default_rng(4)
+    m, n, k, gamma = 4096, 32, 2, 0.01
+    s = (rng.random((m, n)) + rng.random(n)[None, :]).astype(np.float32)
+    q = m * k // n
+    _, b1, _ = B.signsgd_solve(s, k, 1, gamma)
+    c0 = np.bincount(B.topk_biased(s, np.zeros(n, np.float32), k).ravel(), minlength=n)
+    # one step from 0: overloaded experts up by γ, underloaded down, balanced ones unchanged
+    assert np.array_equal(b1, (np.float32(gamma) * np.sign(c0 - q)).astype(np.float32))
+    # many steps: the violation falls well below the plain top-k's
+    vio = lambda c: (c / c.sum() * n - 1).max()
+    _, _, c200 = B.signsgd_solve(s, k, 200, gamma)
+    assert vio(c200) < 0.25 * vio(c0)
