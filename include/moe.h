@@ -218,6 +218,20 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
                              int32_t* idx, int32_t* counts, float* alpha, int32_t* info,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* moe_balance_signsgd — sign-gradient steps on the balancing duals ([MoE tour 6]
+ * "경사하강" eq. (15)-(17)): the dual's slope in β_j is q − c_j, so each step
+ * takes c_j = the number of tokens whose top-k of fl32(s_i − β) holds expert j
+ * (ties: lower index) and sets β_j ← fl32(β_j + γ·sign(c_j − q)).  After
+ * `iters` steps, idx = top-k of fl32(s_i − β) and counts its histogram.
+ * (c_j is the page's count of s_ij − α_i − β_j > 0 whenever a row's k-th and
+ * (k+1)-th values differ.)
+ * s [m, n] fp32; beta [n] fp32 in/out; gamma >= 0 finite; idx [m, k] int32
+ * out; counts [n] int32 out; ws: moe_balance_workspace_size(m, n, k, 0) bytes.
+ * Requires (m·k) % n == 0, 1 <= k < n, n <= 256 (else MOE_ERR_UNSUPPORTED). */
+moe_status moe_balance_signsgd(int64_t m, int32_t n, int32_t k, const float* s, float* beta, float gamma,
+                               int32_t iters, int32_t* idx, int32_t* counts, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* ------------------------------------------------------------------ capacity + dispatch */
 
 /* moe_dispatch — capacity slots in token order and permute-dispatch.

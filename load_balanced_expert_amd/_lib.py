@@ -50,6 +50,8 @@ SIGNATURES = {
     "moe_global_aux": (c_int32, [c_int32, _P, _P, _P, c_int32, c_float, _P, _P, _P, _P, c_float, _P, _P, _P]),
     "moe_balance_duals": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_int32, c_int32, c_int32,
                                     _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_balance_signsgd": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_float, c_int32, _P, _P, _P, c_size_t,
+                                      _P]),
     "moe_dispatch": (c_int32, [POINTER(MoeShape), c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_expert_ffn": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_combine": (c_int32, [POINTER(MoeShape), _P, c_int32, _P, _P, _P, _P, _P]),

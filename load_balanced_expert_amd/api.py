@@ -221,6 +221,20 @@ def balance_duals(s: torch.Tensor, k: int, beta: torch.Tensor, iters: int = 5, m
     return BalanceOut(idx, counts, alpha, info)
 
 
+def balance_signsgd(s: torch.Tensor, k: int, beta: torch.Tensor, gamma: float, iters: int):
+    """Sign-gradient steps on β (updated in place); returns (idx, counts) of the final β."""
+    _on_device(s, beta)
+    m, n = s.shape
+    dev = s.device
+    idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    need = int(_lib().moe_balance_workspace_size(int(m), int(n), int(k), 0))
+    ws, wsb = _ws_args(need, dev)
+    _check(_lib().moe_balance_signsgd(int(m), int(n), int(k), _ptr(s), _ptr(beta), float(gamma), int(iters),
+                                      _ptr(idx), _ptr(counts), ws, wsb, _stream(dev)), "moe_balance_signsgd")
+    return idx, counts
+
+
 # ------------------------------------------------------------------ dispatch
 @dataclass
 class DispatchOut:

@@ -328,6 +328,28 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
   return hip_status(launch_balance(a, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_balance_signsgd(int64_t m, int32_t n, int32_t k, const float* s, float* beta, float gamma,
+                               int32_t iters, int32_t* idx, int32_t* counts, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (m < 1 || n < 2 || k < 1 || k >= n || !s || !beta || !idx || !counts) return MOE_ERR_INVALID_ARG;
+  if ((m * int64_t(k)) % n != 0 || iters < 0 || !(gamma >= 0.f) || !isfinite(gamma)) return MOE_ERR_INVALID_ARG;
+  if (n > 256 || k > kMaxK || m > 0x7FFFFFFFll || m * k > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
+  if (!ws_ok(ws, ws_bytes, moe_balance_workspace_size(m, n, k, 0))) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  BalanceArgs a{};
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.q = m * k / n;
+  a.s = s;
+  a.beta = beta;
+  a.iters = iters;
+  a.idx = idx;
+  a.counts = counts;
+  a.ws = static_cast<char*>(ws) + kControlBytes;
+  a.done = ctl_ticket(ws, kTicketBalance);
+  return hip_status(launch_signsgd(a, gamma, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_dispatch(const moe_shape* shape, int32_t capacity, const void* x, const int32_t* idx,
                         int32_t* token_to_row, uint8_t* drop_mask, int32_t* expert_offsets, int32_t* expert_rows,
                         int32_t* row_to_token, void* dispatched, void* ws, size_t ws_bytes, void* stream) {

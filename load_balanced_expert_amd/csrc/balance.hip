@@ -377,6 +377,27 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_count_finish(BalanceArgs
   if (threadIdx.x == 0 && a.info) a.info[2] = s_bal;
 }
 
+// One SignSGD step on β ([MoE tour 6] "경사하강" eq. (15)-(17)): the counts of the
+// counting top-k (folded from its count rows) against q, β_j ← fl32(β_j + γ·sign(c_j − q)).
+__global__ __launch_bounds__(kRowsRegThreads) void k_qb_signsgd_step(BalanceArgs a, const uint64_t* __restrict__ chunks,
+                                                                     int nch, float gamma) {
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  FinalizeArgs f{};
+  f.chunks = chunks;
+  f.nch = nch;
+  f.sup = super_chunk(nch);
+  f.n = a.n;
+  f.m = a.m;
+  f.capacity = -1;
+  finalize_chunks(f, lds, a.n + 4096, kRowsRegThreads);
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.n; j += kRowsRegThreads) {
+    const int64_t c = lds[j];
+    const float sg = c > a.q ? 1.f : (c < a.q ? -1.f : 0.f);
+    a.beta[j] = a.beta[j] + gamma * sg;
+  }
+}
+
 // ------------------------------------------------------------------ columns: an order statistic per expert
 // One 1024-thread workgroup per expert on the transposed copy of s.  Keys are
 // the order-preserving uint32 images of fl32(s_ij - α_i).  Pass 1 histograms
@@ -1177,6 +1198,40 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
     hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi, pos, lst);
   else
     rows(true, false);
+  return hipGetLastError();
+}
+
+hipError_t launch_signsgd(const BalanceArgs& a, float gamma, hipStream_t s) {
+  // the counting top-k of launch_balance's register paths (n <= 256) and its count rows
+  char* ws = static_cast<char*>(a.ws);
+  ws += al256(size_t(a.m) * a.n * sizeof(float));
+  ws += al256(size_t(a.m) * sizeof(float));
+  uint64_t* chunks = reinterpret_cast<uint64_t*>(ws);
+  const size_t rlds = (size_t(a.n) + 4096) * sizeof(int);
+  float* alpha = nullptr;
+  const bool half = a.k <= 32;
+  const int nh = a.n <= 32 ? 1 : a.n <= 64 ? 2 : a.n <= 128 ? 4 : 8;
+  const int npl = a.n <= 64 ? 1 : a.n <= 128 ? 2 : 4;
+  const unsigned grid = half ? unsigned(std::min<int64_t>(ceil_div64(a.m, 128), 256))
+                             : unsigned(std::min<int64_t>(ceil_div64(a.m, 64), 512));
+  auto count = [&]() {
+    if (half) {
+      if (nh == 1) hipLaunchKernelGGL((k_qb_rows_half<true, false, 1>), dim3(grid), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+      if (nh == 2) hipLaunchKernelGGL((k_qb_rows_half<true, false, 2>), dim3(grid), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+      if (nh == 4) hipLaunchKernelGGL((k_qb_rows_half<true, false, 4>), dim3(grid), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+      if (nh == 8) hipLaunchKernelGGL((k_qb_rows_half<true, false, 8>), dim3(grid), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+    } else {
+      if (npl == 1) hipLaunchKernelGGL((k_qb_rows_reg<true, false, 1>), dim3(grid), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+      if (npl == 2) hipLaunchKernelGGL((k_qb_rows_reg<true, false, 2>), dim3(grid), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+      if (npl == 4) hipLaunchKernelGGL((k_qb_rows_reg<true, false, 4>), dim3(grid), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+    }
+  };
+  for (int it = 0; it < a.iters; ++it) {
+    count();
+    hipLaunchKernelGGL(k_qb_signsgd_step, dim3(1), dim3(kRowsRegThreads), rlds, s, a, chunks, int(grid), gamma);
+  }
+  count();
+  hipLaunchKernelGGL(k_qb_count_finish, dim3(1), dim3(kRowsRegThreads), rlds, s, a, chunks, int(grid));
   return hipGetLastError();
 }
 

@@ -161,5 +161,7 @@ struct BalanceArgs {
   uint32_t* done;    // completion ticket (control region)
 };
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
+// SignSGD steps on β (n <= 256), then the counting top-k of the final β
+hipError_t launch_signsgd(const BalanceArgs& a, float gamma, hipStream_t s);
 
 }  // namespace moe

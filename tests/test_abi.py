@@ -196,3 +196,13 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(M.MoeError):
         M.route(torch.zeros(4, 8), torch.zeros(8, 2), 1)
+
+
+def test_signsgd_limits(lib):
+    # more than 256 experts, or k >= n, are refused before any device work
+    assert lib.moe_balance_signsgd(600, 300, 3, FAKE, FAKE, 0.01, 1, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_balance_signsgd(64, 8, 8, FAKE, FAKE, 0.01, 1, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        L.MOE_ERR_INVALID_ARG
+    assert lib.moe_balance_signsgd(64, 8, 2, FAKE, FAKE, -1.0, 1, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        L.MOE_ERR_INVALID_ARG

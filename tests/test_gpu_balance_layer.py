@@ -91,6 +91,21 @@ def test_qb_kernel_paths(m, n, k, levels, quantile):
     assert np.array_equal(to_host(out.counts), np.bincount(idx_r.ravel(), minlength=n))
 
 
+@pytest.mark.parametrize("m,n,k,gamma,iters", [(4096, 32, 2, 0.01, 20), (3200, 256, 8, 1e-3, 10),
+                                               (1000, 80, 40, 0.01, 5), (2000, 100, 5, 0.02, 0)])
+def test_signsgd_bit_exact(m, n, k, gamma, iters):
+    # sign-gradient steps on β against the oracle: β bit-exact, the final top-k and counts exact
+    s = W.uniform_offset_scores(m, n, 21)
+    say(f"[qb] signsgd m={m} n={n} k={k} gamma={gamma} iters={iters}")
+    beta = torch.zeros(n, dtype=torch.float32, device=DEV)
+    idx, counts = M.balance_signsgd(to_dev(s), k, beta, gamma, iters)
+    torch.cuda.synchronize()
+    idx_r, beta_r, counts_r = OB.signsgd_solve(s, k, iters, gamma)
+    assert np.array_equal(to_host(beta), beta_r)
+    assert np.array_equal(to_host(idx), idx_r)
+    assert np.array_equal(to_host(counts), counts_r)
+
+
 def test_qb_quantile_demo_full_size():
     # the page's demo: m = 100000, n = 256, k = 8, s = U(0,1) + U(0,1)_n, T = 5
     m, n, k = 100000, 256, 8
