@@ -21,12 +21,24 @@ Follows [MoE tour 6]:
 Precision: the Quantile-Balancing duals are exact order statistics of fp32
 differences (fl32(s − β), fl32(s − α)), so ``qb_*`` work in fp32 and are
 bit-reproducible.  ``qb_*`` take the exact order statistic of the algorithm
-box.  ``qb_*_quantile`` follow the page's demo code ("데모 코드") instead: the
-1 − k/n quantile of each row and of each column with linear interpolation
-between the two neighbouring order statistics (the same quantile on both
-axes, "교대 반복"), numpy's quantile on the fp32 differences (so in fp32
-arithmetic); ``bip`` adds the clip of α and β at 0 that the demo's comments
-attribute to BIP.
+box.  With ``bip`` they take the BIP variant of "관련 연구" (eqs. (12)-(14)):
+the inequality-constrained problem gives the same steps with each dual
+truncated at zero, α ← max(0, ·) and β ← max(0, ·).
+
+The quantile form (``quantile_*``) reads the last paragraph of "교대 반복":
+the (k+1)-th largest of n and the (mk/n+1)-th largest of m are both the
+1 − k/n quantile of their axis, and a framework quantile function may replace
+the sort.  The demo ("데모 코드") uses numpy's default quantile, which places
+the level at fractional position (N − 1)·level of the ascending values and
+interpolates linearly between the two neighbours; on fp32 data numpy does
+that arithmetic in fp32.  ``_interp_quantile_fp32`` states that rule.
+
+Mini-batch β ("함정에 주의", last paragraph): when one column selection over
+all m tokens is too expensive, the tokens are split into mini-batches, β is
+computed on each by the same formula and the results are averaged.
+``minibatch_beta`` takes contiguous row blocks and averages in fp64 in block
+order, rounding once to fp32 (a reading: the page fixes neither the split
+nor the precision of the mean).
 
 Exact balance (reading): the alternating iteration stalls short of exact
 column counts on skewed scores, while the pages' target is exactly q per
@@ -52,14 +64,19 @@ def _kth_largest_rows(v: np.ndarray, k: int) -> np.ndarray:
     return -np.sort(-v, axis=1)[:, k]
 
 
-def qb_alpha(s: np.ndarray, beta: np.ndarray, k: int) -> np.ndarray:
+def _truncate(v: np.ndarray, bip: bool) -> np.ndarray:
+    """eq. (14): the BIP duals are kept non-negative, max(0, ·)."""
+    return np.maximum(v, np.float32(0)).astype(np.float32) if bip else v
+
+
+def qb_alpha(s: np.ndarray, beta: np.ndarray, k: int, bip: bool = False) -> np.ndarray:
     v = (s.astype(np.float32) - beta.astype(np.float32)[None, :]).astype(np.float32)
-    return _kth_largest_rows(v, k).astype(np.float32)
+    return _truncate(_kth_largest_rows(v, k).astype(np.float32), bip)
 
 
-def qb_beta(s: np.ndarray, alpha: np.ndarray, q: int) -> np.ndarray:
+def qb_beta(s: np.ndarray, alpha: np.ndarray, q: int, bip: bool = False) -> np.ndarray:
     w = (s.astype(np.float32) - alpha.astype(np.float32)[:, None]).astype(np.float32)
-    return (-np.sort(-w, axis=0)[q, :]).astype(np.float32)
+    return _truncate((-np.sort(-w, axis=0)[q, :]).astype(np.float32), bip)
 
 
 def topk_biased(s: np.ndarray, beta: np.ndarray, k: int) -> np.ndarray:
@@ -68,51 +85,105 @@ def topk_biased(s: np.ndarray, beta: np.ndarray, k: int) -> np.ndarray:
     return np.argsort(-v, axis=1, kind="stable")[:, :k].astype(np.int32)
 
 
-def qb_solve(s: np.ndarray, k: int, iters: int, beta0: Optional[np.ndarray] = None):
-    """Quantile Balancing, solve form.  Returns (idx [m,k], beta [n], alpha [m])."""
+def qb_solve(s: np.ndarray, k: int, iters: int, beta0: Optional[np.ndarray] = None, bip: bool = False):
+    """Quantile Balancing, solve form (BIP's truncated steps with ``bip``).
+    Returns (idx [m,k], beta [n], alpha [m])."""
     m, n = s.shape
     q = m * k // n
     beta = np.zeros(n, np.float32) if beta0 is None else np.asarray(beta0, np.float32).copy()
     alpha = np.zeros(m, np.float32)
     for _ in range(iters):
-        alpha = qb_alpha(s, beta, k)
-        beta = qb_beta(s, alpha, q)
+        alpha = qb_alpha(s, beta, k, bip)
+        beta = qb_beta(s, alpha, q, bip)
     return topk_biased(s, beta, k), beta, alpha
 
 
-def qb_online(s: np.ndarray, k: int, beta_old: np.ndarray):
+def qb_online(s: np.ndarray, k: int, beta_old: np.ndarray, bip: bool = False):
     """Online form: route with the old β, then one α and one β update."""
     m, n = s.shape
     q = m * k // n
     idx = topk_biased(s, beta_old, k)
-    alpha = qb_alpha(s, beta_old, k)
-    beta = qb_beta(s, alpha, q)
+    alpha = qb_alpha(s, beta_old, k, bip)
+    beta = qb_beta(s, alpha, q, bip)
     return idx, beta, alpha
 
 
-# ------------------------------------------------------------------ QB, the demo's quantile form
-def qb_alpha_quantile(s: np.ndarray, beta: np.ndarray, k: int, bip: bool = False) -> np.ndarray:
+def bip_reduced_assignment(s: np.ndarray, alpha: np.ndarray, beta: np.ndarray) -> np.ndarray:
+    """eq. (7) at BIP duals: x_ij = 1 exactly where s_ij − α_i − β_j > 0 (float64).
+    With α_i = 0 a row may hold fewer than k experts: the inequality form of eq. (12)
+    lets a token leave a slot empty."""
+    r = s.astype(np.float64) - np.asarray(alpha, np.float64)[:, None] - np.asarray(beta, np.float64)[None, :]
+    return r > 0
+
+
+def minibatch_beta(s: np.ndarray, k: int, iters: int, batch_rows: int, beta0: Optional[np.ndarray] = None,
+                   bip: bool = False) -> np.ndarray:
+    """"함정에 주의", last paragraph: β computed on each mini-batch of ``batch_rows``
+    consecutive tokens (its own q_b = batch_rows·k/n, ``iters`` QB steps from
+    beta0), then averaged over the mini-batches.  Needs m % batch_rows == 0 and
+    batch_rows·k % n == 0.  The mean is an fp64 sum in block order, divided by the
+    number of blocks, rounded once to fp32."""
+    m, n = s.shape
+    if m % batch_rows or (batch_rows * k) % n:
+        raise ValueError("mini-batches must tile the tokens and hold whole quotas")
+    acc = np.zeros(n, np.float64)
+    nb = m // batch_rows
+    for b in range(nb):
+        _, beta_b, _ = qb_solve(s[b * batch_rows:(b + 1) * batch_rows], k, iters, beta0, bip)
+        acc = acc + beta_b.astype(np.float64)
+    return (acc / nb).astype(np.float32)
+
+
+# ------------------------------------------------------------------ QB, quantile form
+def _interp_quantile_fp32(ascending: np.ndarray, level: np.float32) -> np.ndarray:
+    """Linear-interpolation quantile along axis 0 of values sorted ascending, in fp32:
+    position p = (N − 1)·level; below it the value at floor(p), above it the next one,
+    weight g = p − floor(p).  The blend is a + (b − a)·g, or b − (b − a)·(1 − g) once
+    g ≥ 1/2 (the form that stays exact at g = 1); at p ≥ N − 1 it is the maximum."""
+    N = ascending.shape[0]
+    pos = np.float32(N - 1) * np.float32(level)
+    lo = int(np.floor(pos))
+    if lo >= N - 1:
+        return ascending[N - 1].astype(np.float32)
+    g = np.float32(pos - np.float32(lo))
+    a = ascending[lo].astype(np.float32)
+    b = ascending[lo + 1].astype(np.float32)
+    diff = (b - a).astype(np.float32)
+    if g >= np.float32(0.5):
+        return (b - (diff * np.float32(np.float32(1) - g)).astype(np.float32)).astype(np.float32)
+    return (a + (diff * g).astype(np.float32)).astype(np.float32)
+
+
+def _level(k: int, n: int) -> np.float32:
+    """The common level 1 − k/n of both axes ("교대 반복"), as an fp32 number."""
+    return np.float32(1.0 - k / n)
+
+
+def quantile_alpha(s: np.ndarray, beta: np.ndarray, k: int, bip: bool = False) -> np.ndarray:
+    """α_i = the 1 − k/n quantile of the row fl32(s_i − β) (rows sorted ascending)."""
     n = s.shape[1]
     v = (s.astype(np.float32) - beta.astype(np.float32)[None, :]).astype(np.float32)
-    a = np.quantile(v, 1 - k / n, axis=1).astype(np.float32)
-    return np.maximum(a, np.float32(0)) if bip else a
+    a = _interp_quantile_fp32(np.sort(v, axis=1).T, _level(k, n))
+    return _truncate(a, bip)
 
 
-def qb_beta_quantile(s: np.ndarray, alpha: np.ndarray, k: int, bip: bool = False) -> np.ndarray:
+def quantile_beta(s: np.ndarray, alpha: np.ndarray, k: int, bip: bool = False) -> np.ndarray:
+    """β_j = the 1 − k/n quantile of the column fl32(s_·j − α)."""
     n = s.shape[1]
     w = (s.astype(np.float32) - alpha.astype(np.float32)[:, None]).astype(np.float32)
-    b = np.quantile(w, 1 - k / n, axis=0).astype(np.float32)
-    return np.maximum(b, np.float32(0)) if bip else b
+    b = _interp_quantile_fp32(np.sort(w, axis=0), _level(k, n))
+    return _truncate(b, bip)
 
 
-def qb_solve_quantile(s: np.ndarray, k: int, iters: int, bip: bool = False, beta0: Optional[np.ndarray] = None):
-    """The demo's alternating quantiles, T = iters rounds from β = 0.  Returns (idx, beta, alpha)."""
+def qb_quantile_solve(s: np.ndarray, k: int, iters: int, bip: bool = False, beta0: Optional[np.ndarray] = None):
+    """Alternating quantiles, iters rounds from β = 0 (or beta0); then the biased top-k.
+    Returns (idx, beta, alpha)."""
     m, n = s.shape
     beta = np.zeros(n, np.float32) if beta0 is None else np.asarray(beta0, np.float32).copy()
     alpha = np.zeros(m, np.float32)
     for _ in range(iters):
-        alpha = qb_alpha_quantile(s, beta, k, bip)
-        beta = qb_beta_quantile(s, alpha, k, bip)
+        alpha = quantile_alpha(s, beta, k, bip)
+        beta = quantile_beta(s, alpha, k, bip)
     return topk_biased(s, beta, k), beta, alpha
 
 
@@ -281,6 +352,25 @@ def lp_highs(s: np.ndarray, k: int):
     b = np.concatenate([np.full(m, k, np.float64), np.full(n, q, np.float64)])
     res = linprog(-s.astype(np.float64).reshape(-1), A_eq=A, b_eq=b, bounds=(0.0, 1.0),
                   method="highs")
+    if res.status != 0:
+        raise RuntimeError(res.message)
+    return res.x.reshape(m, n), -res.fun
+
+
+def lp_highs_leq(s: np.ndarray, k: int):
+    """The relaxation of BIP's problem eq. (12) ("관련 연구": Σ_j x_ij ≤ k and Σ_i x_ij ≤ mk/n,
+    0 ≤ x ≤ 1) solved by scipy's HiGHS.  Returns (x, objective)."""
+    from scipy.optimize import linprog
+    from scipy.sparse import coo_matrix, vstack
+
+    m, n = s.shape
+    q = m * k // n
+    cols = np.arange(m * n)
+    A_row = coo_matrix((np.ones(m * n), (np.repeat(np.arange(m), n), cols)), shape=(m, m * n))
+    A_col = coo_matrix((np.ones(m * n), (np.tile(np.arange(n), m), cols)), shape=(n, m * n))
+    A = vstack([A_row, A_col]).tocsr()
+    b = np.concatenate([np.full(m, k, np.float64), np.full(n, q, np.float64)])
+    res = linprog(-s.astype(np.float64).reshape(-1), A_ub=A, b_ub=b, bounds=(0.0, 1.0), method="highs")
     if res.status != 0:
         raise RuntimeError(res.message)
     return res.x.reshape(m, n), -res.fun

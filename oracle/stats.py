@@ -12,15 +12,21 @@ Follows
   with that global f, and the per-micro-batch losses are averaged.  The same
   page's hybrid ("효율성과 효과성의 균형"): the micro-batch balance loss
   (the Switch loss of each micro-batch on its own f) is added to the global
-  one with a constant weight (0.01 on the page); read as
-  L_hybrid^(t) = L_global^(t) + w · L_micro^(t), averaged like the global one.
+  one with a constant weight 0.01.  The page's parenthetical attaches that
+  weight to the global-batch loss; the sentence it sits in adds the
+  micro-batch loss.  Both readings are kept by taking two weights:
+  L_hybrid^(t) = w_g · L_global^(t) + w_m · L_micro^(t), averaged like the
+  global one; reading A (micro-batch loss weighted) is (w_g, w_m) = (1, 0.01),
+  reading B (global loss weighted) is (0.01, 1).
 * [MoE tour 6] "방법 회고" eq. (2): b ← b − γ·sign(F − 1/n), F = observed load
   share; applied after routing with the old b ("함정에 주의").  The bias is fp32
   state, so this update is computed in fp32: F_j − 1/n has the sign of
   c_j·n − m·k, evaluated exactly in integers, and b_j − fl32(γ)·s_j is one fp32
   operation.
-* [MoE tour 6] "데모 코드": max/min/avg violation of the load
-  f = c / Σc · n − 1 (all three are 0 when balanced).
+* [MoE tour 6] "방법 회고" and "데모 코드": the load share F_j = c_j / Σ c
+  against its expected value 1/n; the violation of expert j is the relative
+  excess F_j / (1/n) − 1, and the page reports its maximum (MaxVio, ≥ 0), its
+  minimum (≥ −1) and its mean absolute value, all 0 when perfectly balanced.
 """
 from __future__ import annotations
 
@@ -80,12 +86,12 @@ class GlobalBatch:
         """The Switch loss of each micro-batch with its own f: α·N·Σ_i f_i^(t) · P_i^(t)."""
         return np.array([alpha * self.n * float(np.sum(f * P)) for f, P in zip(self.micro_f, self.prob_means)])
 
-    def hybrid_losses(self, alpha: float, weight: float) -> np.ndarray:
-        """L_global^(t) + weight · L_micro^(t) for each micro-batch t."""
-        return self.losses(alpha) + weight * self.micro_losses(alpha)
+    def hybrid_losses(self, alpha: float, w_global: float, w_micro: float) -> np.ndarray:
+        """w_global · L_global^(t) + w_micro · L_micro^(t) for each micro-batch t."""
+        return w_global * self.losses(alpha) + w_micro * self.micro_losses(alpha)
 
-    def hybrid_loss(self, alpha: float, weight: float) -> float:
-        return float(np.mean(self.hybrid_losses(alpha, weight)))
+    def hybrid_loss(self, alpha: float, w_global: float, w_micro: float) -> float:
+        return float(np.mean(self.hybrid_losses(alpha, w_global, w_micro)))
 
 
 def lossfree_update(bias: np.ndarray, c: np.ndarray, m: int, k: int, gamma: float) -> np.ndarray:
@@ -96,8 +102,11 @@ def lossfree_update(bias: np.ndarray, c: np.ndarray, m: int, k: int, gamma: floa
     return (b - np.float32(gamma) * s).astype(np.float32)
 
 
-def max_min_avg_vio(c: np.ndarray):
-    """(max, min, mean |·|) of f = c/Σc·n − 1 ([MoE tour 6] "데모 코드")."""
+def load_violation(c: np.ndarray):
+    """(MaxVio, min, mean |·|) of each expert's relative excess load F_j·n − 1, where
+    F_j = c_j / Σ c is its load share and 1/n the balanced share."""
     c = np.asarray(c, dtype=np.float64)
-    f = c / c.sum() * c.shape[0] - 1.0
-    return float(f.max()), float(f.min()), float(np.abs(f).mean())
+    n = c.shape[0]
+    share = c / c.sum()
+    excess = share / (1.0 / n) - 1.0
+    return float(excess.max()), float(excess.min()), float(np.mean(np.abs(excess)))

@@ -58,7 +58,7 @@ def test_qb_quantile_bit_exact(m, n, k, iters, bip):
     beta = torch.zeros(n, dtype=torch.float32, device=DEV)
     out = M.balance_duals(to_dev(s), k, beta, iters=iters, quantile=True, bip=bip)
     torch.cuda.synchronize()
-    idx_r, beta_r, alpha_r = OB.qb_solve_quantile(s, k, iters, bip=bip)
+    idx_r, beta_r, alpha_r = OB.qb_quantile_solve(s, k, iters, bip=bip)
     assert np.array_equal(to_host(out.alpha), alpha_r)
     assert np.array_equal(to_host(beta), beta_r)
     assert np.array_equal(to_host(out.idx), idx_r)
@@ -82,7 +82,7 @@ def test_qb_kernel_paths(m, n, k, levels, quantile):
     out = M.balance_duals(to_dev(s), k, beta, iters=3, quantile=quantile)
     torch.cuda.synchronize()
     if quantile:
-        idx_r, beta_r, alpha_r = OB.qb_solve_quantile(s, k, 3)
+        idx_r, beta_r, alpha_r = OB.qb_quantile_solve(s, k, 3)
     else:
         idx_r, beta_r, alpha_r = OB.qb_solve(s, k, 3)
     assert np.array_equal(to_host(out.alpha), alpha_r)
@@ -114,7 +114,7 @@ def test_qb_quantile_demo_full_size():
     beta = torch.zeros(n, dtype=torch.float32, device=DEV)
     out = M.balance_duals(to_dev(s), k, beta, iters=5, quantile=True)
     torch.cuda.synchronize()
-    idx_r, beta_r, _ = OB.qb_solve_quantile(s, k, 5)
+    idx_r, beta_r, _ = OB.qb_quantile_solve(s, k, 5)
     assert np.array_equal(to_host(beta), beta_r)
     assert np.array_equal(to_host(out.counts), np.bincount(idx_r.ravel(), minlength=n))
 
@@ -366,7 +366,7 @@ def test_lossfree_micro_batch_loop():
             assert flips, f"bias after micro-batch {t} differs without any selection flip"
             pytest.skip(f"micro-batch {t}: {len(flips)} near-tie flips moved a load across the target")
         b_gpu_prev = b_gpu
-        vio = OS.max_min_avg_vio(ref.counts)
+        vio = OS.load_violation(ref.counts)
         say(f"  micro-batch {t}: MaxVio {vio[0]:.3f} near-tie flips {len(flips)}")
     if np.array_equal(to_host(gc), gb.counts):
         assert to_host(gt)[0] == gb.tokens

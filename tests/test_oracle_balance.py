@@ -144,9 +144,9 @@ def test_qb_improves_balance_on_demo_workload():
     s = W.uniform_offset_scores(4000, 64, 0)
     k = 4
     top = np.argsort(-s, axis=1)[:, :k]
-    before = S.max_min_avg_vio(np.bincount(top.ravel(), minlength=64))
+    before = S.load_violation(np.bincount(top.ravel(), minlength=64))
     idx, beta, _ = B.qb_solve(s, k, 5)
-    after = S.max_min_avg_vio(np.bincount(idx.ravel(), minlength=64))
+    after = S.load_violation(np.bincount(idx.ravel(), minlength=64))
     assert after[0] < 0.25 * before[0] and after[2] < 0.25 * before[2]
 
 
@@ -157,14 +157,14 @@ def test_qb_quantile_is_the_type7_sample_quantile():
     s = W.uniform_offset_scores(3008, 64, 3)   # m k / n = 188 whole, so the column bracket is (q+1)-th, q-th
     k, n = 4, 64
     beta = np.linspace(-0.2, 0.3, n).astype(np.float32)
-    a = B.qb_alpha_quantile(s, beta, k)
+    a = B.quantile_alpha(s, beta, k)
     v = (s - beta[None, :]).astype(np.float32).astype(np.float64)
     p = (n - 1) * (1 - k / n)
     ref = np.array([np.interp(p, np.arange(n), np.sort(r)) for r in v])
     np.testing.assert_allclose(a, ref, rtol=2e-7, atol=1e-7)
     lo, hi = B.qb_alpha(s, beta, k), B.qb_alpha(s, beta, k - 1)     # (k+1)-th and k-th largest
     assert np.all((a >= lo) & (a <= hi))
-    b = B.qb_beta_quantile(s, a, k)
+    b = B.quantile_beta(s, a, k)
     w = (s - a[:, None]).astype(np.float32).astype(np.float64)
     m, q = s.shape[0], s.shape[0] * k // n
     pc = (m - 1) * (1 - k / n)
@@ -180,11 +180,11 @@ def test_qb_quantile_balances_the_demo_workload_and_bip_clips():
     m, n, k = 100000, 256, 8
     s = W.uniform_offset_scores(m, n, 0)
     top = np.argsort(-s, axis=1)[:, :k]
-    before = S.max_min_avg_vio(np.bincount(top.ravel(), minlength=n))
-    idx, beta, alpha = B.qb_solve_quantile(s, k, 5)
-    after = S.max_min_avg_vio(np.bincount(idx.ravel(), minlength=n))
+    before = S.load_violation(np.bincount(top.ravel(), minlength=n))
+    idx, beta, alpha = B.qb_quantile_solve(s, k, 5)
+    after = S.load_violation(np.bincount(idx.ravel(), minlength=n))
     assert before[0] > 0.5 and after[0] < 0.05 * before[0] and after[2] < 0.05 * before[2]
-    _, bb, ab = B.qb_solve_quantile(s, k, 5, bip=True)
+    _, bb, ab = B.qb_quantile_solve(s, k, 5, bip=True)
     assert np.all(bb >= 0) and np.all(ab >= 0)
     if np.all(alpha > 0) and np.all(beta > 0):
         assert np.array_equal(bb, beta)
@@ -232,3 +232,102 @@ def test_signsgd_step_and_progress():
     vio = lambda c: (c / c.sum() * n - 1).max()
     _, _, c200 = B.signsgd_solve(s, k, 200, gamma)
     assert vio(c200) < 0.25 * vio(c0)
+
+
+# ------------------------------------------------------------------ BIP (eqs. (12)-(14))
+def test_bip_hand_example():
+    """m=4, n=2, k=1, q=2 worked by hand.  Row differences from β = 0: the second largest of
+    each row is the negative expert-1 score, so every α is truncated to 0.  Column 0 then
+    holds 1, 2, 3, 4: its 3rd largest is 2.  Column 1 holds −3, −2, −1, −4: its 3rd largest
+    is −3, truncated to β_1 = 0 exactly.  A second step changes nothing (the second largest
+    of each row of s − β is still negative).  Without the truncation α = s_·1 and
+    β = (4, 0).  The inequality LP assigns tokens 2 and 3 to expert 0 and leaves 0 and 1
+    empty; the reduced-cost rule of eq. (7) at the BIP duals gives the same."""
+    s = np.array([[1, -3], [2, -2], [3, -1], [4, -4]], np.float32)
+    for iters in (1, 2):
+        idx, beta, alpha = B.qb_solve(s, 1, iters, bip=True)
+        assert alpha.tolist() == [0, 0, 0, 0]
+        assert beta.tolist() == [2, 0]
+    _, beta_eq, alpha_eq = B.qb_solve(s, 1, 1)
+    assert alpha_eq.tolist() == [-3, -2, -1, -4] and beta_eq.tolist() == [4, 0]
+    x = B.bip_reduced_assignment(s, np.zeros(4), np.array([2.0, 0.0]))
+    assert x.astype(int).tolist() == [[0, 0], [0, 0], [1, 0], [1, 0]]
+    xl, obj = B.lp_highs_leq(s, 1)
+    assert np.array_equal(xl > 0.5, x) and obj == pytest.approx(7.0)
+    # the online form takes the same truncated steps after routing with the old β
+    idx_o, beta_o, alpha_o = B.qb_online(s, 1, np.zeros(2, np.float32), bip=True)
+    assert beta_o.tolist() == [2, 0] and idx_o[:, 0].tolist() == [0, 0, 0, 0]
+
+
+def test_bip_fixed_point_is_inequality_lp_optimum():
+    """Where the truncated iteration stops moving and its eq. (7) assignment satisfies the
+    conditions of the inequality LP (row sums ≤ k, column sums ≤ q, rows with α_i > 0 full,
+    columns with β_j > 0 full), that assignment is the optimum of eq. (12)'s relaxation, as
+    HiGHS finds it.  Scores of mixed sign make the truncation bite (many zero duals and rows
+    left empty)."""
+    hits = clipped = 0
+    for seed in range(60):
+        rng = np.random.default_rng(seed)
+        m, n, k = 16, 4, 1
+        q = m * k // n
+        s = (rng.standard_normal((m, n)) + rng.standard_normal(n) - 0.5).astype(np.float32)
+        beta = np.zeros(n, np.float32)
+        alpha = np.zeros(m, np.float32)
+        for _ in range(60):
+            a2 = B.qb_alpha(s, beta, k, bip=True)
+            b2 = B.qb_beta(s, a2, q, bip=True)
+            if np.array_equal(a2, alpha) and np.array_equal(b2, beta):
+                break
+            alpha, beta = a2, b2
+        else:
+            continue
+        assert np.all(alpha >= 0) and np.all(beta >= 0)
+        x = B.bip_reduced_assignment(s, alpha, beta)
+        r, c = x.sum(axis=1), x.sum(axis=0)
+        if not (np.all(r <= k) and np.all(c <= q) and np.all(r[alpha > 0] == k) and np.all(c[beta > 0] == q)):
+            continue
+        hits += 1
+        clipped += int(np.any(alpha == 0) and r.sum() < m * k)
+        xl, _ = B.lp_highs_leq(s, k)
+        assert np.array_equal(x, xl > 0.5)
+    assert hits >= 10 and clipped >= 10
+
+
+# ------------------------------------------------------------------ mini-batch β ("함정에 주의")
+def test_minibatch_beta_hand_example():
+    """Two mini-batches of two tokens, n=2, k=1 (q_b = 1), one step from β = 0.
+    Batch A = [[5, 1], [4, 0]]: α = (1, 0), columns of s − α are (4, 4) and (0, 0), so
+    β_A = (4, 0).  Batch B = [[1, 3], [2, 7]]: α = (1, 2), columns (0, 0) and (2, 5), so
+    β_B = (0, 2).  The mean is (2, 1).  One selection over all four tokens (q = 2) gives
+    (0, 0) instead."""
+    s = np.array([[5, 1], [4, 0], [1, 3], [2, 7]], np.float32)
+    assert B.minibatch_beta(s, 1, 1, 2).tolist() == [2.0, 1.0]
+    assert B.qb_solve(s, 1, 1)[1].tolist() == [0.0, 0.0]
+    with pytest.raises(ValueError):
+        B.minibatch_beta(s, 1, 1, 3)
+
+
+@pytest.mark.parametrize("iters,bip", [(1, False), (3, False), (2, True)])
+def test_minibatch_beta_reductions(iters, bip):
+    """One mini-batch is the plain solve; identical mini-batches average to that block's β."""
+    spec = W.BalancedSpec(m=256, n=16, k=2)
+    s = W.balanced_scores(spec, 8)
+    beta0 = np.linspace(-0.3, 0.3, 16).astype(np.float32)
+    assert np.array_equal(B.minibatch_beta(s, 2, iters, 256, beta0, bip), B.qb_solve(s, 2, iters, beta0, bip)[1])
+    block = s[:64]
+    tiled = np.concatenate([block] * 4)
+    assert np.array_equal(B.minibatch_beta(tiled, 2, iters, 64, beta0, bip), B.qb_solve(block, 2, iters, beta0, bip)[1])
+
+
+def test_quantile_helper_equals_numpy_on_fp32():
+    """The interpolation rule written out in _interp_quantile_fp32 reproduces numpy's quantile
+    on fp32 data bit for bit (a library routine; levels with weight below and above 1/2, and
+    a level at the top)."""
+    rng = np.random.default_rng(9)
+    for N, level in [(256, 1 - 8 / 256), (100000, 1 - 8 / 256), (64, 1 - 4 / 64), (7, 0.3), (10, 0.95),
+                     (5, 1.0), (33, 0.5)]:
+        v = rng.standard_normal((N, 3)).astype(np.float32)
+        got = B._interp_quantile_fp32(np.sort(v, axis=0), np.float32(level))
+        ref = np.quantile(v, level, axis=0)
+        assert ref.dtype == np.float32
+        assert np.array_equal(got, ref), (N, level)

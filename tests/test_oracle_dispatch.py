@@ -36,6 +36,22 @@ def test_permute_worked_example():
     assert np.array_equal(dm.token_to_row[:, 0], order)
 
 
+def test_permute_worked_example_row_contents():
+    """dispatch_rows on the same example, against the hand-written buffers: compact, and
+    capacity-padded with capacity 2 (unfilled rows zero)."""
+    g = _read_golden("permute_example.txt")
+    experts = np.array([int(v) - 1 for v in g["experts"][0]], np.int32)[:, None]
+    x = np.array([[t, 10 * t] for t in range(1, 7)], np.float32)
+    compact = np.array([[float(v) for v in r] for r in g["dispatched_row"]], np.float32)
+    padded = np.array([[float(v) for v in r] for r in g["padded_row"]], np.float32)
+    dm = D.dispatch_maps(experts, 4, cap=6)
+    assert np.array_equal(D.dispatch_rows(x, dm), compact)
+    dp = D.dispatch_maps(experts, 4, cap=2, padded=True)
+    assert np.array_equal(D.dispatch_rows(x, dp), padded)
+    # inverse permute of the compact buffer restores x
+    assert np.array_equal(D.dispatch_rows(x, dm)[dm.token_to_row[:, 0]], x)
+
+
 def _capacity_example_idx(counts, seed):
     T = sum(counts)
     idx = np.concatenate([np.full(c, e) for e, c in enumerate(counts)])

@@ -85,21 +85,28 @@ def test_global_batch_differs_from_micro_when_domains_skew():
 
 
 def test_hybrid_loss_closed_forms():
-    """Hybrid = global + w·micro: on the skewed pair above each micro loss is 0.015
-    (each micro-batch loads one expert, whose P is 0.75), the global ones 0.01; one
-    micro-batch alone has L_global = L_micro = the Switch loss, so hybrid = (1 + w)·aux."""
+    """Hybrid = w_g·global + w_m·micro, both readings of the 0.01 weight.  On the skewed pair
+    above each micro loss is 0.015 (each micro-batch loads one expert, whose P is 0.75) and
+    each global loss 0.01.  Reading A (micro loss weighted 0.01): 0.01 + 0.01·0.015 = 0.01015.
+    Reading B (global loss weighted 0.01): 0.01·0.01 + 0.015 = 0.0151.  One micro-batch alone
+    has L_global = L_micro = the Switch loss, so hybrid = (w_g + w_m)·aux."""
     gb = S.GlobalBatch(2)
     gb.add(np.array([4, 0]), 4, np.array([3.0, 1.0]))
     gb.add(np.array([0, 4]), 4, np.array([1.0, 3.0]))
     np.testing.assert_allclose(gb.micro_losses(1e-2), [0.015, 0.015], rtol=1e-14)   # 0.01·2·(1·0.75)
-    np.testing.assert_allclose(gb.hybrid_losses(1e-2, 0.01), [0.01 + 0.01 * 0.015] * 2, rtol=1e-14)
+    np.testing.assert_allclose(gb.hybrid_losses(1e-2, 1.0, 0.01), [0.01015, 0.01015], rtol=1e-13)
+    np.testing.assert_allclose(gb.hybrid_losses(1e-2, 0.01, 1.0), [0.0151, 0.0151], rtol=1e-13)
+    assert gb.hybrid_loss(1e-2, 1.0, 0.01) == pytest.approx(0.01015, rel=1e-13)
+    assert gb.hybrid_loss(1e-2, 0.01, 1.0) == pytest.approx(0.0151, rel=1e-13)
     inp = W.switch_inputs(W.TINY_SWITCH, 6)
     rt = R.route(inp.x, inp.w_r, 1)
     one = S.GlobalBatch(8)
     one.add(rt.counts, 1024, rt.prob_sum)
     aux = S.switch_stats(rt.counts, rt.prob_sum, 1024, 1e-2)[2]
-    assert one.hybrid_loss(1e-2, 0.01) == pytest.approx(1.01 * aux, rel=1e-13)
-    assert one.hybrid_loss(1e-2, 0.0) == pytest.approx(aux, rel=1e-14)
+    assert one.hybrid_loss(1e-2, 1.0, 0.01) == pytest.approx(1.01 * aux, rel=1e-13)
+    assert one.hybrid_loss(1e-2, 0.01, 1.0) == pytest.approx(1.01 * aux, rel=1e-13)
+    assert one.hybrid_loss(1e-2, 1.0, 0.0) == pytest.approx(aux, rel=1e-14)
+    assert one.hybrid_loss(1e-2, 0.0, 1.0) == pytest.approx(aux, rel=1e-14)
 
 
 def test_lossfree_update_signs_and_fp32_rounding():
@@ -127,11 +134,14 @@ def test_lossfree_sign_is_exact_for_huge_batches():
     assert nb.tolist() == [-np.float32(1e-3), 0.0, np.float32(1e-3)]
 
 
-def test_max_min_avg_vio():
-    assert S.max_min_avg_vio(np.full(8, 5)) == (0.0, 0.0, 0.0)
+def test_load_violation():
+    # balanced: every share is exactly 1/n
+    assert S.load_violation(np.full(8, 5)) == (0.0, 0.0, 0.0)
+    # hand example: counts 6, 2, 0, 0 -> shares 3/4, 1/4, 0, 0 -> excess 2, 0, -1, -1
+    assert S.load_violation(np.array([6, 2, 0, 0])) == (2.0, -1.0, 1.0)
     n, k = 8, 2
     c = np.zeros(n)
     c[:k] = 100
-    mx, mn, av = S.max_min_avg_vio(c)
+    mx, mn, av = S.load_violation(c)
     assert mx == pytest.approx(n / k - 1) and mn == -1.0
     assert av == pytest.approx((k * (n / k - 1) + (n - k)) / n)
