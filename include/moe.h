@@ -17,7 +17,10 @@
  *     bytes, 256-byte aligned.
  *   - The first 53248 bytes of a workspace are control words that must be
  *     zero before the workspace is first used (moe_workspace_init(), or any
- *     zero fill).  Every call leaves them zero again.  Two calls that run at
+ *     zero fill).  Every call leaves them zero again; a call that returns
+ *     MOE_ERR_HIP after enqueueing kernels clears them with an asynchronous
+ *     fill on its stream (should the stream itself be broken, re-initialise
+ *     with moe_workspace_init before reusing the workspace).  Two calls that run at
  *     the same time (different streams) must not share a workspace.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work; they never synchronise with the host.  Results are ready
@@ -176,18 +179,20 @@ moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, con
  * 밸런스 구현": synchronise f over the global batch, form each micro-batch's loss
  * with it, aggregate).  f^g_j = global_counts_j / global_tokens;
  * losses[t] = α · n · Σ_j f^g_j · P[t, j]; loss_mean = mean_t losses[t].
- * Hybrid ([Qwen global] "효율성과 효과성의 균형": the micro-batch balance loss
- * added with a constant weight, 0.01 on the page): hybrid[t] = losses[t] +
+ * Hybrid ([Qwen global] "효율성과 효과성의 균형": the micro-batch balance loss is
+ * added to the global-batch one, with a constant weight of 0.01 that the page's
+ * wording can attach to either term): hybrid[t] = global_weight · losses[t] +
  * micro_weight · micro_aux[t], hybrid_mean = mean_t hybrid[t], where micro_aux[t]
- * is micro-batch t's own Switch loss (moe_stats' aux).  Sums in fp64.
+ * is micro-batch t's own Switch loss (moe_stats' aux).  (1, 0.01) weights the
+ * micro-batch loss, (0.01, 1) the global one.  Sums in fp64.
  * P [nb, n] fp32 (each row a micro-batch's P); f_global [n], losses [nb],
  * loss_mean [1] fp32 out (each may be NULL); micro_aux [nb] fp32 in, needed
  * only for hybrid [nb] / hybrid_mean [1] fp32 out (each may be NULL). */
 moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t* global_tokens,
                           const float* P, int32_t nb, float alpha,
                           float* f_global, float* losses, float* loss_mean,
-                          const float* micro_aux, float micro_weight, float* hybrid, float* hybrid_mean,
-                          void* stream);
+                          const float* micro_aux, float global_weight, float micro_weight,
+                          float* hybrid, float* hybrid_mean, void* stream);
 
 /* ------------------------------------------------------------------ balanced assignment */
 
@@ -217,6 +222,34 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
                              int32_t iters, int32_t mode, int32_t exact,
                              int32_t* idx, int32_t* counts, float* alpha, int32_t* info,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_balance_duals_minibatch; 0 for invalid sizes. */
+size_t moe_balance_minibatch_workspace_size(int64_t m, int32_t n, int32_t k, int64_t batch_rows);
+
+/* moe_balance_duals_minibatch — β from mini-batches ([MoE tour 6] "함정에 주의",
+ * last paragraph: one column selection over all m tokens is too expensive, so the
+ * tokens are split into mini-batches, β is computed on each by the same rule and
+ * the results are averaged).  The mini-batches are the m / batch_rows blocks of
+ * batch_rows consecutive tokens; block b has quota q_b = batch_rows·k/n and its
+ * own β, and all blocks run in the same kernel launches.
+ *   mode SOLVE: every block starts from the given beta and runs `iters` QB
+ *     steps (as moe_balance_duals, on its own tokens); beta ← the mean of the
+ *     blocks' β (sum in fp64 in block order, divided by the block count,
+ *     rounded once to fp32); then idx = top-k of fl32(s_i − β).
+ *   mode ONLINE: idx = top-k of fl32(s_i − β_old) first, then one QB step per
+ *     block from β_old and beta ← their mean (iters must be 1).
+ *   MOE_QB_QUANTILE / MOE_QB_BIP as for moe_balance_duals (each block's column
+ *   quantile is taken over its batch_rows keys).  No exact completion.
+ * s [m, n] fp32; beta [n] fp32 in/out; idx [m, k], counts [n] int32 out (the
+ * top-k above and its histogram); alpha [m] fp32 out or NULL (the last α, each
+ * row's from its own block's β); info [4] int32 out or NULL: {QB steps, 0,
+ * 1 if every count == m·k/n else 0, 0}.
+ * Requires m % batch_rows == 0, (batch_rows·k) % n == 0, 1 <= k < n; at most
+ * 65535 blocks (else MOE_ERR_UNSUPPORTED). */
+moe_status moe_balance_duals_minibatch(int64_t m, int32_t n, int32_t k, const float* s, float* beta,
+                                       int32_t iters, int32_t mode, int64_t batch_rows,
+                                       int32_t* idx, int32_t* counts, float* alpha, int32_t* info,
+                                       void* ws, size_t ws_bytes, void* stream);
 
 /* moe_balance_signsgd — sign-gradient steps on the balancing duals ([MoE tour 6]
  * "경사하강" eq. (15)-(17)): the dual's slope in β_j is q − c_j, so each step

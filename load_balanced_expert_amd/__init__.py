@@ -4,10 +4,11 @@ The compute lives in libmoe.so (HIP kernels for gfx950 behind the C ABI of
 include/moe.h); this package is its Python binding.  There is no CPU
 fallback: every call needs the built library and a GPU.
 """
-from .api import (MoeError, balance_duals, balance_signsgd, capacity, combine, dispatch, dispatch_rows, expert_ffn,  # noqa: F401
-                  global_aux, global_aux_hybrid, route, router_prepare, stats, switch_layer, workspace_size, allocate_layer_outputs,
-                  shape)
+from .api import (MoeError, allocate_layer_outputs, balance_duals, balance_duals_minibatch,  # noqa: F401
+                  balance_signsgd, capacity, combine, dispatch, dispatch_rows, expert_ffn, global_aux,
+                  global_aux_hybrid, route, router_prepare, shape, stats, switch_layer, workspace_size)
 from ._lib import LIB_PATH, load  # noqa: F401
 
-__all__ = ["route", "router_prepare", "stats", "global_aux", "global_aux_hybrid", "balance_duals", "balance_signsgd", "dispatch", "dispatch_rows", "expert_ffn", "combine", "switch_layer",
-           "capacity", "MoeError", "load", "LIB_PATH"]
+__all__ = ["route", "router_prepare", "stats", "global_aux", "global_aux_hybrid", "balance_duals",
+           "balance_duals_minibatch", "balance_signsgd", "dispatch", "dispatch_rows", "expert_ffn", "combine",
+           "switch_layer", "capacity", "MoeError", "load", "LIB_PATH"]

@@ -67,13 +67,17 @@ _ws = {}
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-initialised uint8 device buffer of at least nbytes, cached per device.
-    Calls on one stream may share it (the library leaves its control words zero)."""
+    """A zero-initialised uint8 device buffer of at least nbytes, cached per (device, current
+    stream): calls on one stream run in order and may share it (the library leaves its control
+    words zero), calls on different streams may overlap and get buffers of their own."""
     dev = torch.device(device)
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream)
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(int(nbytes), 1 << 16) + 256, dtype=torch.uint8, device=dev)
+        if buf is not None:
+            torch.cuda.current_stream(index).synchronize()   # the old buffer may still be in use
+        buf = torch.zeros(max(int(nbytes), 1 << 16) + 256, dtype=torch.uint8, device=torch.device("cuda", index))
         _ws[key] = buf
     return buf
 
@@ -170,15 +174,17 @@ def global_aux(global_counts: torch.Tensor, global_tokens: torch.Tensor, P_rows:
     losses = torch.empty(max(nb, 1), dtype=torch.float32, device=dev)
     mean = torch.empty(1, dtype=torch.float32, device=dev)
     _check(_lib().moe_global_aux(int(n), _ptr(global_counts), _ptr(global_tokens), _ptr(P_rows), int(nb),
-                                 float(alpha), _ptr(fg), _ptr(losses), _ptr(mean), None, 0.0, None, None,
+                                 float(alpha), _ptr(fg), _ptr(losses), _ptr(mean), None, 0.0, 0.0, None, None,
                                  _stream(dev)), "moe_global_aux")
     return fg, losses[:nb], mean
 
 
 def global_aux_hybrid(global_counts: torch.Tensor, global_tokens: torch.Tensor, P_rows: torch.Tensor,
-                      micro_aux: torch.Tensor, alpha: float = 1e-2, weight: float = 1e-2):
-    """(global losses [nb], hybrid losses [nb], hybrid mean [1]): each micro-batch's global-batch
-    loss plus `weight` times its own Switch loss (micro_aux[t], as moe_stats returns it)."""
+                      micro_aux: torch.Tensor, alpha: float = 1e-2, global_weight: float = 1.0,
+                      micro_weight: float = 1e-2):
+    """(global losses [nb], hybrid losses [nb], hybrid mean [1]): global_weight times each
+    micro-batch's global-batch loss plus micro_weight times its own Switch loss (micro_aux[t],
+    as moe_stats returns it)."""
     _on_device(global_counts, global_tokens, P_rows, micro_aux)
     n = global_counts.shape[0]
     nb = P_rows.shape[0]
@@ -187,7 +193,8 @@ def global_aux_hybrid(global_counts: torch.Tensor, global_tokens: torch.Tensor, 
     hybrid = torch.empty(max(nb, 1), dtype=torch.float32, device=dev)
     hmean = torch.empty(1, dtype=torch.float32, device=dev)
     _check(_lib().moe_global_aux(int(n), _ptr(global_counts), _ptr(global_tokens), _ptr(P_rows), int(nb),
-                                 float(alpha), None, _ptr(losses), None, _ptr(micro_aux), float(weight),
+                                 float(alpha), None, _ptr(losses), None, _ptr(micro_aux), float(global_weight),
+                                 float(micro_weight),
                                  _ptr(hybrid), _ptr(hmean), _stream(dev)), "moe_global_aux")
     return losses[:nb], hybrid[:nb], hmean
 
@@ -218,6 +225,26 @@ def balance_duals(s: torch.Tensor, k: int, beta: torch.Tensor, iters: int = 5, m
     _check(_lib().moe_balance_duals(int(m), int(n), int(k), _ptr(s), _ptr(beta), int(iters), L.QB_MODES[mode] | flags,
                                     int(exact), _ptr(idx), _ptr(counts), _ptr(alpha), _ptr(info), ws, wsb,
                                     _stream(dev)), "moe_balance_duals")
+    return BalanceOut(idx, counts, alpha, info)
+
+
+def balance_duals_minibatch(s: torch.Tensor, k: int, beta: torch.Tensor, batch_rows: int, iters: int = 5,
+                            mode: str = "solve", quantile: bool = False, bip: bool = False) -> BalanceOut:
+    """β from mini-batches of batch_rows consecutive tokens, averaged (beta updated in place)."""
+    _on_device(s, beta)
+    m, n = s.shape
+    dev = s.device
+    idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    alpha = torch.empty(m, dtype=torch.float32, device=dev)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    need = int(_lib().moe_balance_minibatch_workspace_size(int(m), int(n), int(k), int(batch_rows)))
+    ws, wsb = _ws_args(need, dev)
+    flags = (L.QB_QUANTILE if quantile else 0) | (L.QB_BIP if bip else 0)
+    _check(_lib().moe_balance_duals_minibatch(int(m), int(n), int(k), _ptr(s), _ptr(beta), int(iters),
+                                              L.QB_MODES[mode] | flags, int(batch_rows), _ptr(idx), _ptr(counts),
+                                              _ptr(alpha), _ptr(info), ws, wsb, _stream(dev)),
+           "moe_balance_duals_minibatch")
     return BalanceOut(idx, counts, alpha, info)
 
 

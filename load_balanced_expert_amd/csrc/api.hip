@@ -279,14 +279,14 @@ moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, con
 
 moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t* global_tokens, const float* P,
                           int32_t nb, float alpha, float* f_global, float* losses, float* loss_mean,
-                          const float* micro_aux, float micro_weight, float* hybrid, float* hybrid_mean,
-                          void* stream) {
+                          const float* micro_aux, float global_weight, float micro_weight, float* hybrid,
+                          float* hybrid_mean, void* stream) {
   if (n < 1 || nb < 0 || !global_counts || !global_tokens) return MOE_ERR_INVALID_ARG;
   if (nb > 0 && !P) return MOE_ERR_INVALID_ARG;
   if (nb > 0 && (hybrid || hybrid_mean) && !micro_aux) return MOE_ERR_INVALID_ARG;
   if (n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_global_aux(n, global_counts, global_tokens, P, nb, alpha, f_global, losses, loss_mean,
-                                      micro_aux, micro_weight, hybrid, hybrid_mean,
+                                      micro_aux, global_weight, micro_weight, hybrid, hybrid_mean,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -328,6 +328,47 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
   return hip_status(launch_balance(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_balance_minibatch_workspace_size(int64_t m, int32_t n, int32_t k, int64_t batch_rows) {
+  if (m < 1 || n < 2 || k < 1 || k >= n || batch_rows < 1 || m % batch_rows != 0) return 0;
+  return kControlBytes + balance_ws_bytes(m, n, k, false) + al(size_t(m / batch_rows) * n * sizeof(float));
+}
+
+moe_status moe_balance_duals_minibatch(int64_t m, int32_t n, int32_t k, const float* s, float* beta, int32_t iters,
+                                       int32_t mode, int64_t batch_rows, int32_t* idx, int32_t* counts, float* alpha,
+                                       int32_t* info, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 1 || n < 2 || k < 1 || k >= n || !s || !beta || !idx || !counts) return MOE_ERR_INVALID_ARG;
+  if ((m * int64_t(k)) % n != 0 || batch_rows < 1 || m % batch_rows != 0 || (batch_rows * k) % n != 0)
+    return MOE_ERR_INVALID_ARG;
+  const bool quantile = (mode & MOE_QB_QUANTILE) != 0, bip = (mode & MOE_QB_BIP) != 0;
+  mode &= ~(MOE_QB_QUANTILE | MOE_QB_BIP);
+  if (mode != MOE_QB_SOLVE && mode != MOE_QB_ONLINE) return MOE_ERR_INVALID_ARG;
+  if (iters < 0 || (mode == MOE_QB_ONLINE && iters != 1)) return MOE_ERR_INVALID_ARG;
+  if (n > kMaxExperts || m > 0x7FFFFFFFll || m * k > 0x7FFFFFFFll || m / batch_rows > 65535)
+    return MOE_ERR_UNSUPPORTED;
+  if (!ws_ok(ws, ws_bytes, moe_balance_minibatch_workspace_size(m, n, k, batch_rows)))
+    return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  BalanceArgs a{};
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.q = m * k / n;
+  a.s = s;
+  a.beta = beta;
+  a.iters = mode == MOE_QB_ONLINE ? 1 : iters;
+  a.mode = mode;
+  a.quantile = quantile;
+  a.bip = bip;
+  a.idx = idx;
+  a.counts = counts;
+  a.alpha_out = alpha;
+  a.info = info;
+  a.ws = static_cast<char*>(ws) + kControlBytes;
+  a.done = ctl_ticket(ws, kTicketBalance);
+  a.beta_rows = batch_rows;
+  a.nblocks = int(m / batch_rows);
+  return hip_status(launch_balance_minibatch(a, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_balance_signsgd(int64_t m, int32_t n, int32_t k, const float* s, float* beta, float gamma,
                                int32_t iters, int32_t* idx, int32_t* counts, void* ws, size_t ws_bytes,
                                void* stream) {
@@ -347,6 +388,8 @@ moe_status moe_balance_signsgd(int64_t m, int32_t n, int32_t k, const float* s, 
   a.counts = counts;
   a.ws = static_cast<char*>(ws) + kControlBytes;
   a.done = ctl_ticket(ws, kTicketBalance);
+  a.nblocks = 1;
+  a.beta_rows = m;
   return hip_status(launch_signsgd(a, gamma, static_cast<hipStream_t>(stream)));
 }
 
@@ -456,9 +499,16 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
     planes = at<void>(ws, L.planes);
   }
   mark(1);
-  if ((st = do_route(sh, L, x, w_r, planes, bias, idx, gate, counts, psum, ws, s, ex)) != MOE_OK) return st;
+  // After the route kernel has added into the per-super-chunk control words, only the
+  // combine clears them: a launch that fails before it clears them here, so that the
+  // workspace stays usable for the next call.
+  auto fail = [&](moe_status e) {
+    if (da.self_prefix) hipMemsetAsync(at<char>(ws, kSupCountsOff), 0, kControlBytes - kSupCountsOff, s);
+    return e;
+  };
+  if ((st = do_route(sh, L, x, w_r, planes, bias, idx, gate, counts, psum, ws, s, ex)) != MOE_OK) return fail(st);
   mark(2);
-  if ((st = hip_status(launch_dispatch(da, fused_prefix, s))) != MOE_OK) return st;
+  if ((st = hip_status(launch_dispatch(da, fused_prefix, s))) != MOE_OK) return fail(st);
   mark(3);
   if (ffn) {
     const int32_t rows_max = effective_capacity(p->capacity, L.pairs);
@@ -466,13 +516,14 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
                                            static_cast<const uint16_t*>(disp),
                                            static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
                                            at<uint16_t>(ws, L.hidden), static_cast<uint16_t*>(y), s))) != MOE_OK)
-      return st;
+      return fail(st);
   }
   mark(4);
   // the combine also clears the per-super-chunk sums for the next layer call
   st = hip_status(launch_combine(sh.m, sh.d, sh.k, y, ffn ? true : sh.x_dtype == MOE_BF16, gate, t2r, x, o->out,
                                  sh.x_dtype == MOE_BF16, s, da.self_prefix ? at<void>(ws, kSupCountsOff) : nullptr,
                                  kControlBytes - kSupCountsOff));
+  if (st != MOE_OK) return fail(st);
   mark(5);
   return st;
 }

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __r
     const int64_t i = int64_t(blockIdx.x) * kQbRowsPerBlock + rr;
     if (i >= a.m) break;
     const float* row = a.s + i * n;
+    const float* bi = a.nblocks > 1 ? beta + (i / a.beta_rows) * n : beta;   // the row's β block
     float last_key = INFINITY, hi_key = INFINITY, lo_key = INFINITY;
     int last_j = -1, my_j = 0;
     // α: the (k+1)-th largest (exact form), or the order statistics of descending
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256) void k_qb_rows(BalanceArgs a, const float* __r
       float bk = -INFINITY;
       int bj = 0x7FFFFFFF;
       for (int j = lane; j < n; j += 64) {
-        const float v = row[j] - beta[j];
+        const float v = row[j] - bi[j];
         if (better(last_key, last_j, v, j) && better(v, j, bk, bj)) {
           bk = v;
           bj = j;
@@ -285,18 +286,25 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_half(BalanceArgs a,
   }
   const int arank = a.quantile ? a.rank_row : k;
   const int rounds = ALPHA ? (IDX ? max(k, arank + 1) : arank + 1) : k;
-  float bl[NPL];
-#pragma unroll
-  for (int u = 0; u < NPL; ++u) bl[u] = hl + 32 * u < n ? beta[hl + 32 * u] : 0.f;
   constexpr int kWaves = kRowsRegThreads / 64;
   const int64_t stride = int64_t(gridDim.x) * kWaves * 2;
   int64_t i = (int64_t(blockIdx.x) * kWaves + wave) * 2 + half;
+  // this half's β row: block 0, or the block of its current row (mini-batch duals)
+  int64_t cur_b = a.nblocks > 1 && i < a.m ? i / a.beta_rows : 0;
+  float bl[NPL];
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) bl[u] = hl + 32 * u < n ? beta[cur_b * n + hl + 32 * u] : 0.f;
   float nx[NPL];
 #pragma unroll
   for (int u = 0; u < NPL; ++u) nx[u] = i < a.m && hl + 32 * u < n ? a.s[i * n + hl + 32 * u] : 0.f;
   // both halves run the same number of iterations (the wave's first row decides)
   for (int64_t i0 = i - half; i0 < a.m; i0 += stride, i += stride) {
     const bool live = i < a.m;
+    if (a.nblocks > 1 && live && i / a.beta_rows != cur_b) {
+      cur_b = i / a.beta_rows;
+#pragma unroll
+      for (int u = 0; u < NPL; ++u) bl[u] = hl + 32 * u < n ? beta[cur_b * n + hl + 32 * u] : 0.f;
+    }
     float v[NPL];
     int jj[NPL];
 #pragma unroll
@@ -574,8 +582,11 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
   __shared__ int s_wsum[kColThreads / 64], s_wcnt[kColThreads / 64], s_bin, s_rank, s_nk, s_ovf, s_above;
   __shared__ uint32_t s_min;
   const int j = blockIdx.x, tid = threadIdx.x;
-  const int64_t m = a.m;
-  const float* col = sT + int64_t(j) * m;
+  // block blockIdx.y's segment of column j: beta_rows keys from row blockIdx.y * beta_rows
+  const int64_t m = a.beta_rows, r0 = int64_t(blockIdx.y) * m;
+  const float* col = sT + int64_t(j) * a.m + r0;
+  alpha += r0;
+  beta += int64_t(blockIdx.y) * a.n;
   const int rank0 = int(a.quantile ? a.rank_col : a.q);   // 0-based rank in descending order
   if (tid == 0) {
     s_nk = 0;
@@ -1103,41 +1114,39 @@ static void quantile_pos(int64_t N, int k, int n, int64_t& rank, float& g) {
   g = vi - lo;
 }
 
-hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
-  BalanceArgs a = a_in;
-  if (a.quantile) {
-    int64_t rr = 0;
-    quantile_pos(a.n, a.k, a.n, rr, a.g_row);
-    a.rank_row = int(rr);
-    quantile_pos(a.m, a.k, a.n, a.rank_col, a.g_col);
-  }
-  char* ws = static_cast<char*>(a.ws);
-  float* sT = reinterpret_cast<float*>(ws);
-  ws += al256(size_t(a.m) * a.n * sizeof(float));
-  float* alpha_int = reinterpret_cast<float*>(ws);
-  ws += al256(size_t(a.m) * sizeof(float));
-  uint64_t* chunks = reinterpret_cast<uint64_t*>(ws);
-  ws += al256(size_t(ceil_div64(a.m, kQbRowsPerBlock)) * a.n * sizeof(uint64_t));
-  int32_t* xi = reinterpret_cast<int32_t*>(ws);
-  ws += al256(size_t(a.m) * a.k * sizeof(int32_t));
-  int32_t* pos = reinterpret_cast<int32_t*>(ws);
-  ws += al256(size_t(a.m) * a.k * sizeof(int32_t));
-  int32_t* lst = reinterpret_cast<int32_t*>(ws);
-  float* alpha = a.alpha_out ? a.alpha_out : alpha_int;
+// β of every block set to the incoming β (mini-batch solve)
+__global__ __launch_bounds__(256) void k_qb_beta_fill(const float* __restrict__ beta, float* __restrict__ blk, int n,
+                                                      int nb) {
+  for (int64_t o = int64_t(blockIdx.x) * 256 + threadIdx.x; o < int64_t(n) * nb; o += int64_t(gridDim.x) * 256)
+    blk[o] = beta[o % n];
+}
 
-  if (a.info) hipLaunchKernelGGL(k_qb_info, dim3(1), dim3(64), 0, s, a.info, a.iters);
+// β_j = fl32((Σ_b β_b,j) / nb), the sum in fp64 in block order
+__global__ __launch_bounds__(256) void k_qb_beta_mean(const float* __restrict__ blk, int n, int nb,
+                                                      float* __restrict__ beta) {
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < n; j += gridDim.x * 256) {
+    double acc = 0.0;
+    for (int b = 0; b < nb; ++b) acc += double(blk[int64_t(b) * n + j]);
+    beta[j] = float(acc / double(nb));
+  }
+}
+
+// Row pass: α (al) and / or the top-k with its counts (idx) of fl32(s_i − β) for every
+// token, on the kernel that fits n and k; beta is one row, or one row per block of
+// a.beta_rows tokens (α only).
+static void launch_rows(const BalanceArgs& a, const float* beta, float* alpha, uint64_t* chunks, bool idx, bool al,
+                        hipStream_t s) {
   const unsigned rblocks = unsigned(ceil_div64(a.m, kQbRowsPerBlock));
   const size_t rlds = (size_t(a.n) + 4096) * sizeof(int);
   // register rows: grid-stride waves; the counting form keeps at most 512
   // per-workgroup count rows (ceil(m/16) are allocated) for the last workgroup to fold
   const int npl = a.n <= 64 ? 1 : a.n <= 128 ? 2 : a.n <= 256 ? 4 : 0;
   const unsigned gidx = unsigned(std::min<int64_t>(ceil_div64(a.m, 64), 512));
-  auto rows = [&](bool idx, bool al) {
 #define MOE_QB_ROWS(NPL)                                                                                      \
   if (al)                                                                                                  \
-    hipLaunchKernelGGL((k_qb_rows_reg<true, true, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
+    hipLaunchKernelGGL((k_qb_rows_reg<true, true, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, beta, alpha, chunks); \
   else                                                                                                     \
-    hipLaunchKernelGGL((k_qb_rows_reg<true, false, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks);
+    hipLaunchKernelGGL((k_qb_rows_reg<true, false, NPL>), dim3(gidx), dim3(kRowsRegThreads), rlds, s, a, beta, alpha, chunks);
     // (half-wave rows; the counting form needs a lane per pick in each half: k <= 32)
     if (a.n <= 256 && (!idx || a.k <= 32)) {
       const int nh = a.n <= 32 ? 1 : a.n <= 64 ? 2 : a.n <= 128 ? 4 : 8;
@@ -1146,11 +1155,11 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
       const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), idx ? 256 : 1024));
 #define MOE_QB_HALF(NH)                                                                                        \
   if (idx && al)                                                                                            \
-    hipLaunchKernelGGL((k_qb_rows_half<true, true, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
+    hipLaunchKernelGGL((k_qb_rows_half<true, true, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, beta, alpha, chunks); \
   else if (idx)                                                                                             \
-    hipLaunchKernelGGL((k_qb_rows_half<true, false, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, a.beta, alpha, chunks); \
+    hipLaunchKernelGGL((k_qb_rows_half<true, false, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, beta, alpha, chunks); \
   else                                                                                                      \
-    hipLaunchKernelGGL((k_qb_rows_half<false, true, NH>), dim3(gh), dim3(kRowsRegThreads), 0, s, a, a.beta, alpha, chunks);
+    hipLaunchKernelGGL((k_qb_rows_half<false, true, NH>), dim3(gh), dim3(kRowsRegThreads), 0, s, a, beta, alpha, chunks);
       if (nh == 1) {
         MOE_QB_HALF(1)
       } else if (nh == 2) {
@@ -1172,16 +1181,43 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
       MOE_QB_ROWS(4)
       hipLaunchKernelGGL(k_qb_count_finish, dim3(1), dim3(kRowsRegThreads), rlds, s, a, chunks, int(gidx));
     } else if (idx && al) {
-      hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
+      hipLaunchKernelGGL((k_qb_rows<true, true>), dim3(rblocks), dim3(256), rlds, s, a, beta, alpha, chunks);
     } else if (idx) {
-      hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, a.beta, alpha, chunks);
+      hipLaunchKernelGGL((k_qb_rows<true, false>), dim3(rblocks), dim3(256), rlds, s, a, beta, alpha, chunks);
     } else {
-      hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, a.beta, alpha, chunks);
+      hipLaunchKernelGGL((k_qb_rows<false, true>), dim3(rblocks), dim3(256), 0, s, a, beta, alpha, chunks);
     }
 #undef MOE_QB_ROWS
-  };
+}
+
+hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
+  BalanceArgs a = a_in;
+  a.nblocks = 1;
+  a.beta_rows = a.m;
+  if (a.quantile) {
+    int64_t rr = 0;
+    quantile_pos(a.n, a.k, a.n, rr, a.g_row);
+    a.rank_row = int(rr);
+    quantile_pos(a.m, a.k, a.n, a.rank_col, a.g_col);
+  }
+  char* ws = static_cast<char*>(a.ws);
+  float* sT = reinterpret_cast<float*>(ws);
+  ws += al256(size_t(a.m) * a.n * sizeof(float));
+  float* alpha_int = reinterpret_cast<float*>(ws);
+  ws += al256(size_t(a.m) * sizeof(float));
+  uint64_t* chunks = reinterpret_cast<uint64_t*>(ws);
+  ws += al256(size_t(ceil_div64(a.m, kQbRowsPerBlock)) * a.n * sizeof(uint64_t));
+  int32_t* xi = reinterpret_cast<int32_t*>(ws);
+  ws += al256(size_t(a.m) * a.k * sizeof(int32_t));
+  int32_t* pos = reinterpret_cast<int32_t*>(ws);
+  ws += al256(size_t(a.m) * a.k * sizeof(int32_t));
+  int32_t* lst = reinterpret_cast<int32_t*>(ws);
+  float* alpha = a.alpha_out ? a.alpha_out : alpha_int;
+
+  if (a.info) hipLaunchKernelGGL(k_qb_info, dim3(1), dim3(64), 0, s, a.info, a.iters);
+  auto rows = [&](bool idx, bool al) { launch_rows(a, a.beta, alpha, chunks, idx, al, s); };
   auto cols = [&]() {
-    hipLaunchKernelGGL(k_qb_cols, dim3(a.n), dim3(kColThreads), kColLds, s, sT, alpha, a.beta, a);
+    hipLaunchKernelGGL(k_qb_cols, dim3(a.n, 1), dim3(kColThreads), kColLds, s, sT, alpha, a.beta, a);
   };
   hipLaunchKernelGGL(k_qb_transpose, dim3(unsigned(ceil_div64(a.m, 64)), ceil_div(a.n, 64)), dim3(256), 0, s, a.s,
                      sT, a.m, a.n);
@@ -1198,6 +1234,61 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
     hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi, pos, lst);
   else
     rows(true, false);
+  return hipGetLastError();
+}
+
+// Mini-batch duals ([MoE tour 6] "함정에 주의", last paragraph): the tokens are
+// cut into blocks of a.beta_rows rows, each block runs the QB steps with its own
+// quota q_b = beta_rows·k/n and its own β row (all blocks in the same launches:
+// α rows read their block's β, the column kernel takes one segment per block),
+// and the blocks' β are averaged into a.beta.  SOLVE: every block starts from
+// the incoming β, then idx = top-k of fl32(s − mean β).  ONLINE: idx = top-k
+// of fl32(s − β_old) first, then one step per block from β_old.
+hipError_t launch_balance_minibatch(const BalanceArgs& a_in, hipStream_t s) {
+  BalanceArgs a = a_in;                 // global view: rows, final top-k, info
+  BalanceArgs b = a_in;                 // block view: α rows and column segments
+  a.nblocks = 1;
+  a.beta_rows = a.m;
+  b.q = b.beta_rows * b.k / b.n;
+  if (a.quantile) {
+    int64_t rr = 0;
+    quantile_pos(a.n, a.k, a.n, rr, a.g_row);
+    a.rank_row = int(rr);
+    b.rank_row = a.rank_row;
+    b.g_row = a.g_row;
+    quantile_pos(b.beta_rows, b.k, b.n, b.rank_col, b.g_col);
+  }
+  char* ws = static_cast<char*>(a.ws);
+  float* sT = reinterpret_cast<float*>(ws);
+  ws += al256(size_t(a.m) * a.n * sizeof(float));
+  float* alpha_int = reinterpret_cast<float*>(ws);
+  ws += al256(size_t(a.m) * sizeof(float));
+  uint64_t* chunks = reinterpret_cast<uint64_t*>(ws);
+  ws += al256(size_t(ceil_div64(a.m, kQbRowsPerBlock)) * a.n * sizeof(uint64_t));
+  float* blk = reinterpret_cast<float*>(ws);   // [nblocks, n] β rows
+  float* alpha = a.alpha_out ? a.alpha_out : alpha_int;
+  const unsigned fill_grid = unsigned(std::min<int64_t>(ceil_div64(int64_t(b.nblocks) * a.n, 256), 1024));
+
+  if (a.info) hipLaunchKernelGGL(k_qb_info, dim3(1), dim3(64), 0, s, a.info, a.iters);
+  hipLaunchKernelGGL(k_qb_transpose, dim3(unsigned(ceil_div64(a.m, 64)), ceil_div(a.n, 64)), dim3(256), 0, s, a.s,
+                     sT, a.m, a.n);
+  auto cols = [&]() {
+    hipLaunchKernelGGL(k_qb_cols, dim3(a.n, b.nblocks), dim3(kColThreads), kColLds, s, sT, alpha, blk, b);
+  };
+  if (a.mode == 1) {
+    launch_rows(a, a.beta, alpha, chunks, true, true, s);   // route with β_old; α from β_old
+    cols();
+  } else {
+    hipLaunchKernelGGL(k_qb_beta_fill, dim3(fill_grid), dim3(256), 0, s, a.beta, blk, a.n, b.nblocks);
+    for (int it = 0; it < a.iters; ++it) {
+      launch_rows(b, blk, alpha, chunks, false, true, s);
+      cols();
+    }
+  }
+  if (a.mode == 1 || a.iters > 0)
+    hipLaunchKernelGGL(k_qb_beta_mean, dim3(unsigned(ceil_div(a.n, 256))), dim3(256), 0, s, blk, a.n, b.nblocks,
+                       a.beta);
+  if (a.mode != 1) launch_rows(a, a.beta, alpha, chunks, true, false, s);
   return hipGetLastError();
 }
 

@@ -75,8 +75,8 @@ hipError_t launch_stats(int64_t m, int n, int k, const int32_t* counts, const fl
                         int64_t* gtokens, float* bias, float gamma, hipStream_t s);
 hipError_t launch_global_aux(int n, const int64_t* gcounts, const int64_t* gtokens, const float* P,
                              int nb, float alpha, float* fg, float* losses, float* loss_mean,
-                             const float* micro_aux, float micro_weight, float* hybrid, float* hybrid_mean,
-                             hipStream_t s);
+                             const float* micro_aux, float global_weight, float micro_weight, float* hybrid,
+                             float* hybrid_mean, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch
 struct DispatchArgs {
@@ -159,8 +159,16 @@ struct BalanceArgs {
   int32_t* info;
   void* ws;          // after the control words
   uint32_t* done;    // completion ticket (control region)
+  // mini-batch duals: the tokens fall into blocks of beta_rows consecutive rows,
+  // each with its own β row (row kernels: β block i / beta_rows; column kernel:
+  // one segment of beta_rows keys per block).  One block: beta_rows = m.
+  int64_t beta_rows;
+  int nblocks;
 };
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
+// mini-batch β: QB steps on every block of batch_rows tokens at once, the
+// blocks' β averaged (fp64, block order) into a.beta
+hipError_t launch_balance_minibatch(const BalanceArgs& a, hipStream_t s);
 // SignSGD steps on β (n <= 256), then the counting top-k of the final β
 hipError_t launch_signsgd(const BalanceArgs& a, float gamma, hipStream_t s);
 

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kStatsThreads) void k_global_aux(int n, const int64
                                                                const float* __restrict__ P, int nb, float alpha,
                                                                float* __restrict__ fg, float* __restrict__ losses,
                                                                float* __restrict__ loss_mean,
-                                                               const float* __restrict__ micro_aux, float micro_weight,
+                                                               const float* __restrict__ micro_aux, float global_weight,
+                                                               float micro_weight,
                                                                float* __restrict__ hybrid,
                                                                float* __restrict__ hybrid_mean) {
   __shared__ double red[kStatsThreads / 64];
@@ -93,8 +94,8 @@ __global__ __launch_bounds__(kStatsThreads) void k_global_aux(int n, const int64
     const double L = double(alpha) * double(n) * block_sum_f64(part, red);
     if (threadIdx.x == 0 && losses) losses[t] = float(L);
     mean += L;
-    if (micro_aux) {   // hybrid: the micro-batch's own loss added with a constant weight
-      const double H = L + double(micro_weight) * double(micro_aux[t]);
+    if (micro_aux) {   // hybrid: the global-batch and the micro-batch losses, each with a constant weight
+      const double H = double(global_weight) * L + double(micro_weight) * double(micro_aux[t]);
       if (threadIdx.x == 0 && hybrid) hybrid[t] = float(H);
       hmean += H;
     }
@@ -107,9 +108,10 @@ __global__ __launch_bounds__(kStatsThreads) void k_global_aux(int n, const int64
 
 hipError_t launch_global_aux(int n, const int64_t* gcounts, const int64_t* gtokens, const float* P, int nb,
                              float alpha, float* fg, float* losses, float* loss_mean, const float* micro_aux,
-                             float micro_weight, float* hybrid, float* hybrid_mean, hipStream_t s) {
+                             float global_weight, float micro_weight, float* hybrid, float* hybrid_mean,
+                             hipStream_t s) {
   hipLaunchKernelGGL(k_global_aux, dim3(1), dim3(kStatsThreads), 0, s, n, gcounts, gtokens, P, nb, alpha, fg,
-                     losses, loss_mean, micro_aux, micro_weight, hybrid, hybrid_mean);
+                     losses, loss_mean, micro_aux, global_weight, micro_weight, hybrid, hybrid_mean);
   return hipGetLastError();
 }
 

@@ -117,19 +117,23 @@ def bip_reduced_assignment(s: np.ndarray, alpha: np.ndarray, beta: np.ndarray) -
 
 
 def minibatch_beta(s: np.ndarray, k: int, iters: int, batch_rows: int, beta0: Optional[np.ndarray] = None,
-                   bip: bool = False) -> np.ndarray:
+                   bip: bool = False, quantile: bool = False) -> np.ndarray:
     """"함정에 주의", last paragraph: β computed on each mini-batch of ``batch_rows``
     consecutive tokens (its own q_b = batch_rows·k/n, ``iters`` QB steps from
-    beta0), then averaged over the mini-batches.  Needs m % batch_rows == 0 and
-    batch_rows·k % n == 0.  The mean is an fp64 sum in block order, divided by the
-    number of blocks, rounded once to fp32."""
+    beta0, exact or quantile form), then averaged over the mini-batches.  Needs
+    m % batch_rows == 0 and batch_rows·k % n == 0.  The mean is an fp64 sum in block
+    order, divided by the number of blocks, rounded once to fp32."""
     m, n = s.shape
     if m % batch_rows or (batch_rows * k) % n:
         raise ValueError("mini-batches must tile the tokens and hold whole quotas")
     acc = np.zeros(n, np.float64)
     nb = m // batch_rows
     for b in range(nb):
-        _, beta_b, _ = qb_solve(s[b * batch_rows:(b + 1) * batch_rows], k, iters, beta0, bip)
+        sb = s[b * batch_rows:(b + 1) * batch_rows]
+        if quantile:
+            _, beta_b, _ = qb_quantile_solve(sb, k, iters, bip, beta0)
+        else:
+            _, beta_b, _ = qb_solve(sb, k, iters, beta0, bip)
         acc = acc + beta_b.astype(np.float64)
     return (acc / nb).astype(np.float32)
 

@@ -148,10 +148,10 @@ def test_stats_validation(lib):
     # aux requested without prob_sum
     assert lib.moe_stats(8, 8, 1, FAKE, None, 0.01, None, None, FAKE, None, None, None, 0.001, None) == 1
     assert lib.moe_stats(8, 5000, 1, FAKE, None, 0.01, None, None, None, None, None, None, 0.001, None) == 2
-    assert lib.moe_global_aux(8, None, FAKE, FAKE, 1, 0.01, None, None, None, None, 0.0, None, None, None) == 1
-    assert lib.moe_global_aux(8, FAKE, FAKE, None, 2, 0.01, None, None, None, None, 0.0, None, None, None) == 1
+    assert lib.moe_global_aux(8, None, FAKE, FAKE, 1, 0.01, None, None, None, None, 0.0, 0.0, None, None, None) == 1
+    assert lib.moe_global_aux(8, FAKE, FAKE, None, 2, 0.01, None, None, None, None, 0.0, 0.0, None, None, None) == 1
     # a hybrid output needs the micro-batch losses
-    assert lib.moe_global_aux(8, FAKE, FAKE, FAKE, 2, 0.01, None, None, None, None, 0.01, FAKE, None, None) == 1
+    assert lib.moe_global_aux(8, FAKE, FAKE, FAKE, 2, 0.01, None, None, None, None, 1.0, 0.01, FAKE, None, None) == 1
 
 
 def test_balance_validation(lib):
@@ -206,3 +206,17 @@ def test_signsgd_limits(lib):
         L.MOE_ERR_INVALID_ARG
     assert lib.moe_balance_signsgd(64, 8, 2, FAKE, FAKE, -1.0, 1, FAKE, FAKE, FAKE, 1 << 30, None) == \
         L.MOE_ERR_INVALID_ARG
+
+
+def test_minibatch_validation(lib):
+    big = 1 << 40
+    args = lambda m, n, k, br, it=1, mode=0, wsb=big: (m, n, k, FAKE, FAKE, it, mode, br, FAKE, FAKE,  # noqa
+                                                       None, None, FAKE, wsb, None)
+    assert lib.moe_balance_duals_minibatch(*args(64, 8, 1, 24)) == 1       # blocks do not tile the tokens
+    assert lib.moe_balance_duals_minibatch(*args(64, 8, 1, 4)) == 1        # block quota 4·1/8 not whole
+    assert lib.moe_balance_duals_minibatch(*args(64, 8, 1, 0)) == 1
+    assert lib.moe_balance_duals_minibatch(*args(64, 8, 1, 16, it=2, mode=1)) == 1   # online takes one step
+    assert lib.moe_balance_duals_minibatch(*args(64, 8, 1, 16, mode=3)) == 1
+    assert lib.moe_balance_duals_minibatch(*args(64, 8, 1, 16, wsb=100)) == 3
+    assert lib.moe_balance_minibatch_workspace_size(64, 8, 1, 24) == 0
+    assert lib.moe_balance_minibatch_workspace_size(64, 8, 1, 16) > lib.moe_balance_workspace_size(64, 8, 1, 0)

@@ -187,23 +187,26 @@ def test_repeat_is_bitwise_deterministic():
         assert np.array_equal(u, v)
 
 
-@pytest.mark.parametrize("sample", [4096])
-def test_switch_c_full_size_sampled(sample):
-    """T=65536, d=1024, N=2048 at full size: every output checked on a token sample,
-    counts against the GPU's own indices, score sums against the full oracle."""
+def test_switch_c_full_size():
+    """T=65536, d=1024, N=2048 at full size: the oracle routes every token (in blocks of 8192),
+    so indices are checked on all tokens, gates on all but near-tie flips, counts against the
+    oracle's and score sums against its full sums."""
     spec = W.SWITCH_C
     inp = W.switch_inputs(spec, 0)
     say("[route] switch-C full size on GPU")
     idx, g, counts, psum = run_route(inp.x, inp.w_r, 1)
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(spec.T, sample, replace=False))
-    ref = OR.route(inp.x[toks], inp.w_r, 1)
-    flips = check_selection(idx[toks], ref, "switch-C sampled")
-    same = np.array([t not in flips for t in range(sample)])
-    assert_rel(g[toks][same], ref.gate[same], 1e-5, "switch-C gates")
-    assert np.array_equal(counts, np.bincount(idx.reshape(-1), minlength=spec.N))
-    assert counts.sum() == spec.T
     psum_ref = np.zeros(spec.N)
+    counts_ref = np.zeros(spec.N, np.int64)
+    nflips = 0
     for lo in range(0, spec.T, 8192):
-        psum_ref += OR.route(inp.x[lo:lo + 8192], inp.w_r, 1).prob_sum
+        ref = OR.route(inp.x[lo:lo + 8192], inp.w_r, 1)
+        flips = check_selection(idx[lo:lo + 8192], ref, f"switch-C tokens {lo}..{lo + 8191}")
+        nflips += len(flips)
+        same = np.array([t not in flips for t in range(8192)])
+        assert_rel(g[lo:lo + 8192][same], ref.gate[same], 1e-5, "switch-C gates")
+        psum_ref += ref.prob_sum
+        counts_ref += ref.counts
+    assert np.array_equal(counts, np.bincount(idx.reshape(-1), minlength=spec.N))
+    if nflips == 0:
+        assert np.array_equal(counts, counts_ref)
     assert_rel(psum, psum_ref, 1e-5, "switch-C prob_sum")

@@ -317,6 +317,11 @@ def test_minibatch_beta_reductions(iters, bip):
     block = s[:64]
     tiled = np.concatenate([block] * 4)
     assert np.array_equal(B.minibatch_beta(tiled, 2, iters, 64, beta0, bip), B.qb_solve(block, 2, iters, beta0, bip)[1])
+    # the quantile form likewise
+    assert np.array_equal(B.minibatch_beta(s, 2, iters, 256, beta0, bip, quantile=True),
+                          B.qb_quantile_solve(s, 2, iters, bip, beta0)[1])
+    assert np.array_equal(B.minibatch_beta(tiled, 2, iters, 64, beta0, bip, quantile=True),
+                          B.qb_quantile_solve(block, 2, iters, bip, beta0)[1])
 
 
 def test_quantile_helper_equals_numpy_on_fp32():
