@@ -53,7 +53,6 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   L.planes = o; o += al(L.rp.planes_bytes);
   L.logits = o; o += al(L.rp.logits_bytes);
   L.kpart = o; o += al(L.rp.kpart_bytes);
-  L.route_end = o;
   L.route_ct = route_chunk_tokens(L.rp);
   L.disp_ct = dispatch_chunk_tokens(L.route_ct, s.k);
   L.nch = int(ceil_div64(s.m, L.disp_ct));
@@ -62,6 +61,7 @@ Layout layout(const moe_shape& s, int32_t capacity, int32_t d_ff) {
   L.sup_route = super_chunk(L.nch_route);
   const int nch_max = std::max(L.nch, L.nch_route);
   L.chunks = o; o += al(size_t(nch_max) * s.n * sizeof(uint64_t));
+  L.route_end = o;   // the route's scratch ends with its chunk rows
   L.super_prefix = o; o += al(size_t(kMaxSuperChunks) * s.n * sizeof(int32_t));
   L.r2t = o; o += al(size_t(L.rows_bound) * 4);
   L.dispatch_end = o;
