@@ -152,6 +152,23 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, co
                      const float* bias, int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* moe_route_noalloc — moe_route for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as moe_route without ws / ws_bytes:
+ * the scratch is a static device array of moe_route_noalloc_max_bytes() bytes
+ * (16 MiB) that the library holds on each GPU it runs on until the process
+ * ends.  Shapes whose moe_route workspace exceeds that return
+ * MOE_ERR_UNSUPPORTED (for example n > 256 at large m, whose logits pass
+ * through the scratch); the Switch-Base and Loss-Free router shapes fit.  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (different streams, host threads) race; calls
+ * in order on one stream do not.  The first call on a device also enqueues a
+ * small kernel that clears the array's control words. */
+size_t moe_route_noalloc_max_bytes(void);
+moe_status moe_route_noalloc(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
+                             const float* bias, int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
+                             void* stream);
+
 /* ------------------------------------------------------------------ statistics */
 
 /* moe_stats — load statistics of one (micro-)batch, optional global-batch

@@ -140,6 +140,28 @@ def route(x: torch.Tensor, w_r: torch.Tensor, k: int, score: str = "softmax", ga
     return RouteOut(idx, g, counts, ps)
 
 
+def route_noalloc(x: torch.Tensor, w_r: torch.Tensor, k: int, score: str = "softmax", gate: str = "prob",
+                  bias: Optional[torch.Tensor] = None, prob_sum: bool = True, out: Optional[RouteOut] = None,
+                  w_planes: Optional[torch.Tensor] = None) -> RouteOut:
+    """route() through moe_route_noalloc: the library's static scratch instead of a workspace
+    (outputs are allocated here unless `out` is given)."""
+    _on_device(x, w_r, bias, w_planes)
+    m, d = x.shape
+    n = w_r.shape[1]
+    dev = x.device
+    sh = shape(m, d, n, k, score, gate, _dtype_code(x))
+    if out is not None:
+        idx, g, counts, ps = out.idx, out.gate, out.counts, out.prob_sum
+    else:
+        idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+        g = torch.empty((m, k), dtype=torch.float32, device=dev)
+        counts = torch.empty(n, dtype=torch.int32, device=dev)
+        ps = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum else None
+    _check(_lib().moe_route_noalloc(ctypes.byref(sh), _ptr(x), _ptr(w_r), _ptr(w_planes), _ptr(bias), _ptr(idx),
+                                    _ptr(g), _ptr(counts), _ptr(ps), _stream(dev)), "moe_route_noalloc")
+    return RouteOut(idx, g, counts, ps)
+
+
 # ------------------------------------------------------------------ statistics
 @dataclass
 class StatsOut:

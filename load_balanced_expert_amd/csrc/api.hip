@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -192,6 +194,39 @@ moe_status do_dispatch(const moe_shape& s, const Layout& L, int32_t capacity, co
   return hip_status(launch_dispatch(a, prefix_ready, st));
 }
 
+// ------------------------------------------------------------------ route without allocation
+// Scratch of moe_route_noalloc: one file-scope device array per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the host
+// the name only stands for the variable): its device address is looked up once per
+// device and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void k_zero_words(u32x4* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// The current device's scratch address; on its first use the control words are
+// cleared by a fill kernel on `st` (no memset node, so the call may be captured).
+moe_status noalloc_scratch(void** out, hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    hipLaunchKernelGGL(k_zero_words, dim3(ceil_div(int(kControlBytes / 16), 256)), dim3(256), 0, st,
+                       static_cast<u32x4*>(p), int(kControlBytes / 16));
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,6 +298,22 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, co
   if (!ws_ok(ws, ws_bytes, L.route_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
   return do_route(*shape, L, x, w_r, w_planes, bias, idx, gate, counts, prob_sum, ws,
                   static_cast<hipStream_t>(stream));
+}
+
+size_t moe_route_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+moe_status moe_route_noalloc(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
+                             const float* bias, int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
+                             void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !w_r || !idx || !gate || !counts) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(*shape, -1, 0);
+  if (L.route_end > kNoAllocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws, s)) != MOE_OK) return st;
+  return do_route(*shape, L, x, w_r, w_planes, bias, idx, gate, counts, prob_sum, ws, s);
 }
 
 moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, const float* prob_sum, float alpha,
