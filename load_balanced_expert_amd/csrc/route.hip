@@ -709,16 +709,38 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     const uint16_t* arow;
     DirectGemm<NT> dg;
-    if constexpr (DIRECT) dg.init(a.w_r, a.d, kbA, kbB, wave, lane, tile);
     if constexpr (XLDS) {
       // stage the 32 x rows in LDS with coalesced 16-byte loads (zero padding past the end)
       uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
       // only this workgroup's K range [32 kbA, 32 kbB) of the tile is staged
       // columns [kx, kx + 32 (kbB - kbA)) of x land at tile columns from 0 (row stride ldx)
-      const int ldx = xcols + 8, cpr = (kbB - kbA) * 4, kx = kbA * 32;
-      // four loads in flight per thread before the LDS stores (one pass for d <= 1024);
-      // the first pass runs in every thread (its items are range-checked)
-      for (int c0 = tid; c0 == tid || c0 < kRouteBM * cpr; c0 += 4 * kRouteThreads) {
+      const int ldx = xcols + 8, cpr = (kbB - kbA) * 4, kx = kbA * 32, items = kRouteBM * cpr;
+      // The first pass (all of it for d <= 1024): four unconditional 16-byte loads per
+      // thread through a buffer resource over the tile's rows (an item past the tile reads
+      // zeros without touching memory), then the W_r loads of the product's first blocks,
+      // so the LDS stores wait for the x loads alone and the weights stay in flight.
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(x + t0 * a.d), 0, rows * a.d * int(sizeof(uint16_t)), 0x00020000);
+      {
+        u32x4 v[4];
+        int dst[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = tid + u * kRouteThreads;
+          const int r = c / cpr, k = kx + (c - r * cpr) * 8;
+          const bool in = c < items && r < rows && k < a.d;
+          v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               xr, in ? (r * a.d + k) * int(sizeof(uint16_t)) : int(0x7FFF0000), 0, 0));
+          dst[u] = c < items ? r * ldx + (k - kx) : -1;
+        }
+        if constexpr (DIRECT) dg.init(a.w_r, a.d, kbA, kbB, wave, lane, tile);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xs + dst[u]) = v[u];
+        if constexpr (DIRECT) dg.prime();   // split the first weights
+      }
+      // further passes (d > 1024 without a K split)
+      for (int c0 = tid + 4 * kRouteThreads; c0 < items; c0 += 4 * kRouteThreads) {
         u32x4 v[4];
         int dst[4];
 #pragma unroll
@@ -726,20 +748,18 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
           const int c = c0 + u * kRouteThreads;
           const int r = c / cpr, k = kx + (c - r * cpr) * 8;
           v[u] = u32x4{0u, 0u, 0u, 0u};
-          dst[u] = c < kRouteBM * cpr ? r * ldx + (k - kx) : -1;
-          if (c < kRouteBM * cpr && r < rows && k < a.d) v[u] = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
-        }
-        if constexpr (DIRECT) {   // split the first weights while the x loads are in flight
-          if (c0 == tid) dg.prime();
+          dst[u] = c < items ? r * ldx + (k - kx) : -1;
+          if (c < items && r < rows && k < a.d) v[u] = *reinterpret_cast<const u32x4*>(x + (t0 + r) * a.d + k);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xs + dst[u]) = v[u];
       }
-      __syncthreads();
+      lds_barrier();   // the tile is in LDS; the weight loads stay in flight
       // the product indexes x by absolute K block: shift the row start back by kx
       arow = xs + (lane & 31) * ldx + 16 * (lane >> 5) - kx;
     } else {
+      if constexpr (DIRECT) dg.init(a.w_r, a.d, kbA, kbB, wave, lane, tile);
       arow = x + (t0 + min(lane & 31, rows - 1)) * a.d + 16 * (lane >> 5);  // requires d == dpad
       if constexpr (DIRECT) dg.prime();
     }
@@ -818,12 +838,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   if (a.k <= 32) {
     if constexpr (MFMA) route_rows_half<NT>(lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
     else route_rows_half_nv(a.npad / 32, lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
-    __syncthreads();
+    lds_barrier();   // scores and histogram in LDS (the idx / gate stores need not land first)
     route_tail<true>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints - lg_off,
                      tile, ntiles);
   } else {
     route_rows(lg, ldl, rows, t0, e, a.idx, a.gate_out, tok_mx, tok_sum, hist);
-    __syncthreads();
+    lds_barrier();
     route_tail<false>(lg, ldl, rows, e, tok_mx, tok_sum, hist, a, reinterpret_cast<int*>(lg), a.lds_region_ints - lg_off,
                       tile, ntiles);
   }
