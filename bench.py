@@ -94,6 +94,23 @@ def committed_traffic(kernel: str, workload: str, src_hash: str):
     return float(m_tr.group(1))
 
 
+def committed_trace_us(stage: str):
+    """Average duration of the stage's kernel in profiles/kernels_switch_base_trace.md, if that trace
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "kernels_switch_base_trace.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    key = {"route": "route", "dispatch": "dispatch", "combine": "combine"}[stage]
+    m_hash = re.search(r"source_sha256_16\(" + key + r"\):\s*([0-9a-f]+)", text)
+    if not m_hash or m_hash.group(1) != kernel_source_hash(KERNEL_SOURCES[key]):
+        return None
+    pat = {"route": r"k_route_fused[^|]*\|\s*\d+\s*\|\s*([0-9.]+)", "dispatch": r"k_disp_rank_copy[^|]*\|\s*\d+\s*\|\s*([0-9.]+)",
+           "combine": r"k_combine_vec[^|]*\|\s*\d+\s*\|\s*([0-9.]+)"}[stage]
+    m = re.search(pat, text)
+    return float(m.group(1)) if m else None
+
+
 def cpu_baseline(spec, inp, cap, seconds: float):
     """The oracle (float64 numpy) on full batches of the workload, repeated for ~`seconds`."""
     import numpy as np
@@ -123,6 +140,32 @@ def cpu_baseline(spec, inp, cap, seconds: float):
             "sample": f"{passes} full batches of T={spec.T} (route+stats+dispatch+combine in float64 numpy, "
                       f"identity expert output fed to combine) in {el:.1f} s; BLAS threads={threads}, "
                       f"host affinity cores={len(os.sched_getaffinity(0))}"}
+
+
+def _cpu_baseline_child(cf: float, seed: int, seconds: float):
+    """Entry of the oracle-timing child process: prints the cpu_baseline JSON object."""
+    import workloads as W
+    from oracle import dispatch as OD
+    spec = W.SWITCH_BASE
+    inp = W.switch_inputs(spec, seed)
+    print(json.dumps(cpu_baseline(spec, inp, OD.capacity(spec.T, spec.N, cf), seconds)), flush=True)
+
+
+def cpu_baseline_process(cf: float, seed: int, seconds: float, threads=None):
+    """The oracle timed in a child process; threads=1 pins every BLAS / OpenMP pool to one
+    thread through the environment, set before numpy is imported."""
+    import subprocess
+    env = dict(os.environ)
+    if threads is not None:
+        for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS",
+                  "NUMEXPR_NUM_THREADS"):
+            env[v] = str(threads)
+    code = f"import bench; bench._cpu_baseline_child({cf!r}, {seed!r}, {seconds!r})"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"oracle timing failed:\n{r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 class HipEvents:
@@ -221,8 +264,9 @@ def main():
     lo = M.allocate_layer_outputs(T, d, N, k, rows_bound, x.dtype, True, dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        M.switch_layer(x, w_r, k=k, capacity=cap, alpha=spec.alpha, w1=W1, w2=W2, outputs=lo, stage_events=ev)
+    def step(ev=None, capacity=cap, outputs=lo):
+        M.switch_layer(x, w_r, k=k, capacity=capacity, alpha=spec.alpha, w1=W1, w2=W2, outputs=outputs,
+                       stage_events=ev)
 
     for _ in range(args.warmup):
         step()
@@ -230,53 +274,99 @@ def main():
     he = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
 
-    # Timed run: per step only two events, after dispatch ([3]) and after the
-    # expert FFN ([4]).  The metric region of step i is then the span from its
-    # FFN end to the dispatch end of step i + 1 (combine of step i, then route
-    # and dispatch of the next step, the same work on the same inputs), so one
-    # event sits inside each measured region; the FFN is e3(i) -> e4(i).
-    n_run = args.steps + 1
-    ev3 = [he.create() for _ in range(n_run)]
-    ev4 = [he.create() for _ in range(n_run)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(n_run):
-        step([None, None, None, ev3[i], ev4[i], None])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    region = np.array([he.ms(ev4[i], ev3[i + 1]) for i in range(args.steps)])   # ms
-    ffn = np.array([he.ms(ev3[i], ev4[i]) for i in range(args.steps)])
+    def timed_region(nsteps, capacity, outputs):
+        """Per step only two events, after dispatch ([3]) and after the expert FFN ([4]).  The metric
+        region of step i is the span from its FFN end to the dispatch end of step i + 1 (its combine,
+        then the route and dispatch of the next step: the same work on the same inputs), so one event
+        sits inside each measured region; the FFN is e3(i) -> e4(i)."""
+        ev3 = [he.create() for _ in range(nsteps + 1)]
+        ev4 = [he.create() for _ in range(nsteps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(nsteps + 1):
+            step([None, None, None, ev3[i], ev4[i], None], capacity, outputs)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        region = np.array([he.ms(ev4[i], ev3[i + 1]) for i in range(nsteps)])   # ms
+        ffn = np.array([he.ms(ev3[i], ev4[i]) for i in range(nsteps)])
+        return region, ffn, wall
+
+    region, ffn, wall = timed_region(args.steps, cap, lo)
     metric_ms = float(np.mean(region))
     value = T / (metric_ms * 1e-3)
     rows = int(lo.expert_rows.sum().item())   # kept rows
 
-    # Stage breakdown: a separate short run with all six stage events (each
-    # span also carries one event's own cost, so these add up to more than
-    # the metric region above).
+    # Stage breakdown: a separate short run with all six stage events.  Every span also carries the
+    # cost of the event packets around it; the span between two events with nothing between them
+    # ([0] -> [1]: the router weight is prepared outside the step) measures that cost, and each
+    # kernel's time is its span minus that.
     nb = min(args.steps, 20)
     evs = [[he.create() for _ in range(6)] for _ in range(nb)]
     for i in range(nb):
         step(evs[i])
     torch.cuda.synchronize()
     st = np.array([[he.ms(evs[i][j], evs[i][j + 1]) for j in range(5)] for i in range(nb)])
-    names = ["router_prepare", "route", "dispatch", "expert_ffn", "combine"]
+    names = ["events_only", "route", "dispatch", "expert_ffn", "combine"]
     stage_ms = {n_: float(np.mean(st[:, j])) for j, n_ in enumerate(names)}
+    null_ms = stage_ms["events_only"]
 
-    # dominant kernel of the metric region: its span in the breakdown run (one
-    # kernel between two fence-free events)
+    # cold cache: every step starts after a 1 GiB write that evicts L2 and the 256 MB last-level cache;
+    # route + dispatch ([1] -> [3]) and combine ([4] -> [5]) spans, measured the same way warm
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ncold = min(args.steps, 20)
+
+    def spans(cold):
+        out_ = []
+        for i in range(ncold):
+            if cold:
+                flush.fill_(i & 0xFF)
+            ev = [he.create() for _ in range(6)]
+            step(ev)
+            torch.cuda.synchronize()
+            out_.append(he.ms(ev[1], ev[3]) + he.ms(ev[4], ev[5]))
+        return float(np.mean(out_))
+
+    warm_same = spans(False)
+    cold_ms = spans(True)
+    del flush
+
+    # capacity factor 1.0 (64 slots per expert): same timing as the headline
+    cap10 = M.capacity(T, N, 1.0)
+    lo10 = M.allocate_layer_outputs(T, d, N, k, M.dispatch_rows(T, k, N, cap10), x.dtype, True, dev)
+    for _ in range(3):
+        step(None, cap10, lo10)
+    region10, _, _ = timed_region(min(args.steps, 30), cap10, lo10)
+    rows10 = int(lo10.expert_rows.sum().item())
+
+    # a plain device copy of the metric region's byte count (half read, half written): the
+    # practical ceiling of a streaming kernel on this part
+    alg_metric_bytes = (T * d * 2 + N * d * 4 + T * k * 8) + (T * k * 4 * 3) + 2 * rows * d * 2 + \
+        (rows * d * 2 + 2 * T * d * 2 + T * k * 8)
+    csrc_t = torch.empty(alg_metric_bytes // 2, dtype=torch.uint8, device=dev)
+    cdst_t = torch.empty_like(csrc_t)
+    copy_ms = _timed(he, stream, lambda: cdst_t.copy_(csrc_t), 20, 3, torch)[0]
+    copy_gbs = alg_metric_bytes / (copy_ms * 1e-3) / 1e9
+    del csrc_t, cdst_t
+
+    # dominant kernel of the metric region: its event span minus the cost of an empty event pair
     dom = max(("route", "dispatch", "combine"), key=lambda s_: stage_ms[s_])
-    t_s = stage_ms[dom] * 1e-3
+    t_s = (stage_ms[dom] - null_ms) * 1e-3
     if dom == "route":
-        flops = 3 * 2.0 * T * d * N                    # bf16x3 products on bf16 matrix cores
+        method_flops = 2.0 * T * d * N                   # h = x . W_r, the method's fp32 product
+        issued_flops = 3 * method_flops                  # three bf16 products (exact bf16x3 split of W_r)
         nch = (T + 31) // 32
         alg_bytes = T * d * 2 + N * d * 4 + T * k * 8 + nch * N * 4
         traffic = committed_traffic("route", "switch_base", kernel_source_hash(KERNEL_SOURCES["route"]))
         roof = {"kernel": "k_route_fused (W_r split in registers, bf16x3 MFMA router, softmax, top-1, histogram, "
                           "chunk counts and super-chunk sums)",
-                "bound": "mfma", "achieved": flops / t_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": flops / t_s / 1e12 / BF16_PEAK_TFLOPS, "traffic": traffic,
-                "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes,
-                "hbm_frac_of_same_launch": alg_bytes / t_s / 1e9 / HBM_PEAK_GBS}
+                "bound": "hbm", "achieved": alg_bytes / t_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": alg_bytes / t_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+                "algorithmic_bytes_per_launch": alg_bytes,
+                "method_flops_per_launch": method_flops,
+                "mfma_frac_of_bf16_peak_on_method_flops": method_flops / t_s / 1e12 / BF16_PEAK_TFLOPS,
+                "issued_bf16x3_flops_per_launch": issued_flops,
+                "issued_bf16_tflops": issued_flops / t_s / 1e12,
+                "why_hbm": "at bf16 peak the method's flops take 0.64 us, its bytes 1.63 us at 8 TB/s"}
     elif dom == "dispatch":
         alg_bytes = T * k * 4 + 2 * rows * d * 2 + T * k * 9
         traffic = committed_traffic("dispatch", "switch_base", kernel_source_hash(KERNEL_SOURCES["dispatch"]))
@@ -292,6 +382,9 @@ def main():
                 "frac": alg_bytes / t_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": alg_bytes}
     roof["avg_launch_us"] = t_s * 1e6
+    roof["event_span_us"] = stage_ms[dom] * 1e3
+    roof["empty_event_pair_us"] = null_ms * 1e3
+    roof["trace_avg_us"] = committed_trace_us(dom)
     roof["stage"] = dom
 
     # the expert FFN stage (outside the metric): weight streaming from HBM bounds it
@@ -308,8 +401,9 @@ def main():
                 "algorithmic_bytes_per_stage": ffn_bytes, "algorithmic_flops_per_stage": ffn_flops,
                 "mfma_frac_bf16": ffn_flops / t_ffn / 1e12 / BF16_PEAK_TFLOPS, "stage_us": t_ffn * 1e6}
 
-    alg_metric_bytes = (T * d * 2 + N * d * 4 + T * k * 8) + (T * k * 4 * 3) + 2 * rows * d * 2 + \
-        (rows * d * 2 + 2 * T * d * 2 + T * k * 8)
+    alg10 = (T * d * 2 + N * d * 4 + T * k * 8) + (T * k * 4 * 3) + 2 * rows10 * d * 2 + \
+        (rows10 * d * 2 + 2 * T * d * 2 + T * k * 8)
+    ms10 = float(np.mean(region10))
     out = {
         "metric": "routed tokens/sec (route+dispatch+combine) at T=8192,N=128; % HBM roofline",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -323,13 +417,27 @@ def main():
                                                                float(np.percentile(region, 90))],
         "expert_ffn_ms": t_ffn * 1e3, "stage_ms_event_spans": stage_ms,
         "hbm_roofline_frac_of_metric_region": alg_metric_bytes / (metric_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "copy_ceiling_gbs": copy_gbs,
+        "frac_of_copy_ceiling": alg_metric_bytes / (metric_ms * 1e-3) / 1e9 / copy_gbs,
         "algorithmic_bytes_metric_region": alg_metric_bytes,
+        "cold_cache": {"value": T / (cold_ms * 1e-3), "ms_per_step": cold_ms,
+                       "warm_same_spans_value": T / (warm_same * 1e-3), "warm_same_spans_ms": warm_same,
+                       "how": "route+dispatch and combine event spans of steps that each start after a 1 GiB "
+                              "write (L2 and the 256 MB last-level cache evicted); warm_same_spans is the same "
+                              "measurement without the write"},
+        "capacity_factor_1_0": {"value": T / (ms10 * 1e-3), "metric_ms_per_step": ms10, "capacity": cap10,
+                                "hbm_roofline_frac_of_metric_region":
+                                    alg10 / (ms10 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "dropped_tokens": int(lo10.drop_mask.sum().item())},
         "dropped_tokens": int(lo.drop_mask.sum().item()), "aux_loss": float(lo.aux.item()),
         "roofline": roof,
         "expert_ffn_roofline": ffn_roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, inp, cap, args.cpu_seconds)
+        cb = cpu_baseline_process(args.cf, args.seed, args.cpu_seconds)
+        one = cpu_baseline_process(args.cf, args.seed, args.cpu_seconds / 2, threads=1)
+        cb["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+        out["cpu_baseline"] = cb
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -402,8 +510,9 @@ def bench_lossfree(args):
     # the route kernel alone, back to back
     r0 = routs[0]
     t_route = _timed(he, stream, lambda: M.route(xs[0], w_r, k, score="sigmoid", bias=bias, out=r0), 30, 3, torch)[0]
-    flops = 3 * 2.0 * T * d * n
+    method_flops = 2.0 * T * d * n       # the fp32 router product of the method
     alg_bytes = T * d * 2 + d * n * 4 + T * k * 8 + n * 8
+    t_r = t_route * 1e-3
     out = {
         "metric": "routed tokens/sec (Loss-Free biased top-k route + stats + global batch + bias update)",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": max(1, args.warmup // 5),
@@ -412,12 +521,15 @@ def bench_lossfree(args):
         "data": "synthetic (4 cluster means ~N(0,4) per dim + N(0,1) noise, one cluster per micro-batch)",
         "config": {"workload": "lossfree: 16 micro-batches x 4096 tokens, d_model=2048, n=256, k=8, sigmoid, "
                                "gamma=1e-3", "global_batch": tokens, "parallelism": "single GPU"},
+        # bound: the larger of the method's bytes at 8 TB/s (2.4 us) and its flops at bf16 peak (1.7 us)
         "roofline": {"kernel": "k_route_fused (bf16x3 MFMA router, sigmoid, biased top-8, histogram, score sums)",
-                     "bound": "mfma", "achieved": flops / (t_route * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": flops / (t_route * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                     "traffic": None, "avg_launch_us": t_route * 1e3, "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": alg_bytes,
-                     "hbm_frac_of_same_launch": alg_bytes / (t_route * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                     "bound": "hbm", "achieved": alg_bytes / t_r / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg_bytes / t_r / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": t_route * 1e3, "algorithmic_bytes_per_launch": alg_bytes,
+                     "method_flops_per_launch": method_flops,
+                     "mfma_frac_of_bf16_peak_on_method_flops": method_flops / t_r / 1e12 / BF16_PEAK_TFLOPS,
+                     "issued_bf16x3_flops_per_launch": 3 * method_flops,
+                     "timing": "stand-alone moe_route calls back to back between two events"},
         "final_bias_range": [float(bias.min().item()), float(bias.max().item())],
     }
     if not args.no_cpu_baseline:
@@ -604,7 +716,7 @@ def bench_switch_c(args):
     rows = int(lo.expert_rows.sum().item())   # kept rows
     alg_metric_bytes = (T * d * 2 + N * d * 4 + T * k * 8) + (T * k * 4 * 3) + 2 * rows * d * 2 + \
         (rows * d * 2 + 2 * T * d * 2 + T * k * 8)
-    flops = 3 * 2.0 * T * d * N
+    method_flops = 2.0 * T * d * N      # the fp32 router product of the method (issued: 3x, bf16x3)
     t_ffn = float(np.mean(ffn)) * 1e-3
     ffn_bytes = 2 * N * d * d_ff * 2 + 2 * rows * (d + d_ff) * 2
     out = {
@@ -618,7 +730,7 @@ def bench_switch_c(args):
                    "capacity": cap, "parallelism": "single GPU"},
         "metric_ms_per_step": metric_ms, "expert_ffn_ms": t_ffn * 1e3,
         "hbm_roofline_frac_of_metric_region": alg_metric_bytes / (metric_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "router_tflops_if_metric_were_router_only": flops / (metric_ms * 1e-3) / 1e12,
+        "router_method_tflops_if_metric_were_router_only": method_flops / (metric_ms * 1e-3) / 1e12,
         "dropped_tokens": int(lo.drop_mask.sum().item()),
         "expert_ffn_roofline": {"bound": "hbm", "achieved": ffn_bytes / t_ffn / 1e9, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": ffn_bytes / t_ffn / 1e9 / HBM_PEAK_GBS,
