@@ -23,3 +23,4 @@ Parity status of each part is recorded in the module docstrings.  Every
 function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*.py``.
 """
 from . import router, stats, dispatch, expert, balance  # noqa: F401
+from . import backward  # noqa: F401,E402
