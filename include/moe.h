@@ -377,6 +377,8 @@ typedef struct {
   void* y;                 /* [rows, d] bf16 expert outputs (relu_ffn; ignored for
                               the identity expert, whose output is `dispatched`) */
   void* out;               /* [m, d] x_dtype */
+  void* hidden;            /* [rows, d_ff] bf16 hidden activation max(0, D·W1) of the
+                              relu_ffn expert (kept for the backward), or NULL */
 } moe_layer_outputs;
 
 /* moe_switch_layer — route → stats → capacity + dispatch → expert → combine on one
@@ -388,6 +390,52 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* para
                             const void* x, const float* w_r, const void* w1, const void* w2,
                             const float* bias, const moe_layer_outputs* outputs,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ backward */
+
+/* Saved values of one moe_switch_layer forward (its outputs), read by the backward. */
+typedef struct {
+  const int32_t* idx;            /* [m, k] chosen experts */
+  const float* gate;             /* [m, k] gates */
+  const int32_t* counts;         /* [n] selections per expert (f_j = counts_j / m) */
+  const int32_t* token_to_row;   /* [m, k], -1 = dropped */
+  const int32_t* expert_offsets; /* [n + 1] */
+  const int32_t* expert_rows;    /* [n] (capacity layout), or NULL (compact offsets) */
+  const void* dispatched;        /* [rows, d] bf16 */
+  const void* hidden;            /* [rows, d_ff] bf16 */
+  const void* y;                 /* [rows, d] bf16 */
+} moe_layer_saved;
+
+/* Gradient outputs (device, fp32, every one required). */
+typedef struct {
+  float* dx;     /* [m, d] */
+  float* dw_r;   /* [d, n] */
+  float* dw1;    /* [n, d_ff, d] (zero for experts with no rows) */
+  float* dw2;    /* [n, d, d_ff] */
+} moe_layer_grads;
+
+/* Workspace bytes for moe_switch_layer_backward; 0 for an invalid shape. */
+size_t moe_switch_layer_backward_workspace_size(const moe_shape* shape, int32_t capacity, int32_t d_ff);
+
+/* moe_switch_layer_backward — gradients of L = Σ out ⊙ dout + aux with respect to x, W_r, W1
+ * and W2 for one moe_switch_layer forward with softmax scores, gate = the chosen expert's
+ * probability and the relu_ffn expert ([Switch review] "Switch Routing 메커니즘" Step 3: the
+ * gate multiplies the output, so W_r receives a gradient; [Switch impl] "argmax가 있어도
+ * Router를 학습할 수 있는 이유": the chosen id itself gets none; [Switch review] "로드 밸런싱
+ * 손실": f_i is constant, P_i carries the balancing loss's gradient).  At the forward's saved
+ * values: dY = g·dout (combine transpose, rounded to bf16), dg = <dout, Y>; the expert data and
+ * weight gradients on bf16 matrix cores (fp32 accumulation; the ReLU mask is H > 0); the
+ * router's logits recomputed in fp32, dh = Σ_r dg_r g_r (e_{i_r} − p) + p ⊙ (c − <p, c>) with
+ * c_j = α·n·counts_j/m², then dW_r = xᵀ·dh and dx = dout + (dispatch transpose of dD) + dh·W_rᵀ,
+ * all fp32 (the router's products on fp32 matrix cores).  Every reduction has a fixed order.
+ * params: capacity, d_ff and alpha as in the forward (expert_kind must be relu_ffn);
+ * x [m, d] bf16; w_r [d, n] fp32; w1 [n, d_ff, d], w2 [n, d, d_ff] bf16; dout [m, d] fp32.
+ * Requires softmax scores, the prob gate, bf16 x, d and d_ff multiples of 32
+ * (else MOE_ERR_UNSUPPORTED / MOE_ERR_INVALID_ARG). */
+moe_status moe_switch_layer_backward(const moe_shape* shape, const moe_layer_params* params,
+                                     const void* x, const float* w_r, const void* w1, const void* w2,
+                                     const moe_layer_saved* saved, const float* dout,
+                                     const moe_layer_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

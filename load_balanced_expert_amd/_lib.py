@@ -31,7 +31,16 @@ class LayerParams(ctypes.Structure):
 class LayerOutputs(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in (
         "idx", "gate", "counts", "prob_sum", "f", "P", "aux", "token_to_row", "drop_mask",
-        "expert_offsets", "expert_rows", "row_to_token", "dispatched", "y", "out")]
+        "expert_offsets", "expert_rows", "row_to_token", "dispatched", "y", "out", "hidden")]
+
+
+class LayerSaved(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in (
+        "idx", "gate", "counts", "token_to_row", "expert_offsets", "expert_rows", "dispatched", "hidden", "y")]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in ("dx", "dw_r", "dw1", "dw2")]
 
 
 _P = c_void_p
@@ -63,6 +72,9 @@ SIGNATURES = {
     "moe_combine": (c_int32, [POINTER(MoeShape), _P, c_int32, _P, _P, _P, _P, _P]),
     "moe_switch_layer": (c_int32, [POINTER(MoeShape), POINTER(LayerParams), _P, _P, _P, _P, _P,
                                    POINTER(LayerOutputs), _P, c_size_t, _P]),
+    "moe_switch_layer_backward_workspace_size": (c_size_t, [POINTER(MoeShape), c_int32, c_int32]),
+    "moe_switch_layer_backward": (c_int32, [POINTER(MoeShape), POINTER(LayerParams), _P, _P, _P, _P,
+                                            POINTER(LayerSaved), _P, POINTER(LayerGrads), _P, c_size_t, _P]),
 }
 
 _lib = None

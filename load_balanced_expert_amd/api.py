@@ -380,9 +380,11 @@ class LayerOut:
     dispatched: torch.Tensor
     y: Optional[torch.Tensor]
     out: torch.Tensor
+    hidden: Optional[torch.Tensor] = None   # [rows, d_ff] bf16 (relu_ffn), kept for the backward
 
 
-def allocate_layer_outputs(m, d, n, k, rows_bound, x_dtype, ffn: bool, device) -> LayerOut:
+def allocate_layer_outputs(m, d, n, k, rows_bound, x_dtype, ffn: bool, device, d_ff: Optional[int] = None) -> LayerOut:
+    """Layer output buffers; with d_ff the relu_ffn hidden activation is kept too (for the backward)."""
     e = lambda *s, dt: torch.empty(s, dtype=dt, device=device)  # noqa: E731
     return LayerOut(
         idx=e(m, k, dt=torch.int32), gate=e(m, k, dt=torch.float32), counts=e(n, dt=torch.int32),
@@ -391,7 +393,7 @@ def allocate_layer_outputs(m, d, n, k, rows_bound, x_dtype, ffn: bool, device) -
         expert_offsets=e(n + 1, dt=torch.int32), expert_rows=e(n, dt=torch.int32),
         row_to_token=torch.full((rows_bound,), -1, dtype=torch.int32, device=device),
         dispatched=e(rows_bound, d, dt=x_dtype), y=e(rows_bound, d, dt=torch.bfloat16) if ffn else None,
-        out=e(m, d, dt=x_dtype))
+        out=e(m, d, dt=x_dtype), hidden=e(rows_bound, d_ff, dt=torch.bfloat16) if (ffn and d_ff) else None)
 
 
 def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int = -1, alpha: float = 1e-2,
@@ -408,7 +410,7 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
     d_ff = w1.shape[1] if ffn else 0
     sh = shape(m, d, n, k, score, gate, _dtype_code(x))
     rows_bound = dispatch_rows(m, k, n, capacity)
-    o = outputs or allocate_layer_outputs(m, d, n, k, rows_bound, x.dtype, ffn, dev)
+    o = outputs or allocate_layer_outputs(m, d, n, k, rows_bound, x.dtype, ffn, dev, d_ff if ffn else None)
     lo = L.LayerOutputs(*[(_ptr(getattr(o, f)) if getattr(o, f) is not None else None)
                           for f, _ in L.LayerOutputs._fields_])
     evs = None
@@ -425,3 +427,42 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
     _check(_lib().moe_switch_layer(ctypes.byref(sh), ctypes.byref(params), _ptr(x), _ptr(w_r), _ptr(w1), _ptr(w2),
                                    _ptr(bias), ctypes.byref(lo), ws, wsb, _stream(dev)), "moe_switch_layer")
     return o
+
+
+# ------------------------------------------------------------------ backward
+@dataclass
+class LayerGrads:
+    dx: torch.Tensor
+    dw_r: torch.Tensor
+    dw1: torch.Tensor
+    dw2: torch.Tensor
+
+
+def switch_layer_backward(x: torch.Tensor, w_r: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, fwd: LayerOut,
+                          dout: torch.Tensor, capacity: int = -1, alpha: float = 1e-2,
+                          out: Optional[LayerGrads] = None) -> LayerGrads:
+    """Gradients of sum(out * dout) + aux for the forward `fwd` (its saved outputs, hidden included)."""
+    _on_device(x, w_r, w1, w2, dout)
+    if fwd.hidden is None or fwd.y is None:
+        raise MoeError("the backward needs the forward's hidden activation and expert outputs")
+    m, d = x.shape
+    n = w_r.shape[1]
+    k = fwd.idx.shape[1]
+    d_ff = w1.shape[1]
+    dev = x.device
+    sh = shape(m, d, n, k, "softmax", "prob", _dtype_code(x))
+    g = out or LayerGrads(torch.empty((m, d), dtype=torch.float32, device=dev),
+                          torch.empty((d, n), dtype=torch.float32, device=dev),
+                          torch.empty(tuple(w1.shape), dtype=torch.float32, device=dev),
+                          torch.empty(tuple(w2.shape), dtype=torch.float32, device=dev))
+    saved = L.LayerSaved(_ptr(fwd.idx), _ptr(fwd.gate), _ptr(fwd.counts), _ptr(fwd.token_to_row),
+                         _ptr(fwd.expert_offsets), _ptr(fwd.expert_rows) if capacity >= 0 else None,
+                         _ptr(fwd.dispatched), _ptr(fwd.hidden), _ptr(fwd.y))
+    grads = L.LayerGrads(_ptr(g.dx), _ptr(g.dw_r), _ptr(g.dw1), _ptr(g.dw2))
+    params = L.LayerParams(int(capacity), L.EXPERTS["relu_ffn"], int(d_ff), float(alpha), None)
+    need = int(_lib().moe_switch_layer_backward_workspace_size(ctypes.byref(sh), int(capacity), int(d_ff)))
+    ws, wsb = _ws_args(need, dev)
+    _check(_lib().moe_switch_layer_backward(ctypes.byref(sh), ctypes.byref(params), _ptr(x), _ptr(w_r), _ptr(w1),
+                                            _ptr(w2), ctypes.byref(saved), _ptr(dout), ctypes.byref(grads), ws, wsb,
+                                            _stream(dev)), "moe_switch_layer_backward")
+    return g

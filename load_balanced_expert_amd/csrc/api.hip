@@ -566,7 +566,8 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
     if ((st = hip_status(launch_expert_ffn(sh.n, sh.d, p->d_ff, rows_max, offs, da.padded ? rowsn : nullptr,
                                            static_cast<const uint16_t*>(disp),
                                            static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
-                                           at<uint16_t>(ws, L.hidden), static_cast<uint16_t*>(y), s))) != MOE_OK)
+                                           o->hidden ? static_cast<uint16_t*>(o->hidden) : at<uint16_t>(ws, L.hidden),
+                                           static_cast<uint16_t*>(y), s))) != MOE_OK)
       return fail(st);
   }
   mark(4);
@@ -577,6 +578,62 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   if (st != MOE_OK) return fail(st);
   mark(5);
   return st;
+}
+
+size_t moe_switch_layer_backward_workspace_size(const moe_shape* shape, int32_t capacity, int32_t d_ff) {
+  if (check_shape(shape) != MOE_OK || capacity < -1 || d_ff < 1) return 0;
+  const int64_t pairs = shape->m * shape->k;
+  const int64_t rows_bound = capacity < 0 ? pairs : int64_t(capacity) * shape->n;
+  return kControlBytes + al(backward_ws_bytes(shape->m, shape->d, shape->n, shape->k, rows_bound, d_ff));
+}
+
+moe_status moe_switch_layer_backward(const moe_shape* shape, const moe_layer_params* p, const void* x,
+                                     const float* w_r, const void* w1, const void* w2, const moe_layer_saved* sv,
+                                     const float* dout, const moe_layer_grads* gr, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!p || !x || !w_r || !w1 || !w2 || !sv || !dout || !gr || p->capacity < -1 || p->d_ff < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (!sv->idx || !sv->gate || !sv->counts || !sv->token_to_row || !sv->expert_offsets || !sv->dispatched ||
+      !sv->hidden || !sv->y || !gr->dx || !gr->dw_r || !gr->dw1 || !gr->dw2)
+    return MOE_ERR_INVALID_ARG;
+  if (p->expert_kind != MOE_EXPERT_RELU_FFN || shape->x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (shape->score != MOE_SCORE_SOFTMAX || shape->gate != MOE_GATE_PROB) return MOE_ERR_UNSUPPORTED;
+  if (shape->d % 32 != 0 || p->d_ff % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!ws_ok(ws, ws_bytes, moe_switch_layer_backward_workspace_size(shape, p->capacity, p->d_ff)))
+    return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  const int64_t pairs = shape->m * shape->k;
+  BackwardArgs b{};
+  b.m = shape->m;
+  b.d = shape->d;
+  b.n = shape->n;
+  b.k = shape->k;
+  b.d_ff = p->d_ff;
+  b.rows_bound = p->capacity < 0 ? pairs : int64_t(p->capacity) * shape->n;
+  b.rows_max = effective_capacity(p->capacity, pairs);
+  b.x_bf16 = true;
+  b.alpha = p->alpha;
+  b.x = x;
+  b.w_r = w_r;
+  b.w1 = static_cast<const uint16_t*>(w1);
+  b.w2 = static_cast<const uint16_t*>(w2);
+  b.idx = sv->idx;
+  b.gate = sv->gate;
+  b.counts = sv->counts;
+  b.t2r = sv->token_to_row;
+  b.offsets = sv->expert_offsets;
+  b.rows = sv->expert_rows;
+  b.dispatched = static_cast<const uint16_t*>(sv->dispatched);
+  b.hidden = static_cast<const uint16_t*>(sv->hidden);
+  b.y = static_cast<const uint16_t*>(sv->y);
+  b.dout = dout;
+  b.dx = gr->dx;
+  b.dw_r = gr->dw_r;
+  b.dw1 = gr->dw1;
+  b.dw2 = gr->dw2;
+  b.ws = static_cast<char*>(ws) + kControlBytes;
+  return hip_status(launch_backward(b, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

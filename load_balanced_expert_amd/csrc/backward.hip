@@ -1,0 +1,365 @@
+// Backward pass of the Switch layer: gradients of L = Σ out ⊙ dout + L_aux with respect to x,
+// W_r, W1 and W2, at one forward's saved values (selection, gates, dispatch maps, the
+// dispatched rows D, the hidden activation H and the expert outputs Y).
+//
+// [Switch review] "Switch Routing 메커니즘" Step 3: the output is scaled by the chosen
+// expert's router probability, which carries the gradient to W_r; [Switch impl] "argmax가
+// 있어도 Router를 학습할 수 있는 이유": the expert id itself gets no gradient.  [Switch review]
+// "로드 밸런싱 손실": f_i (from the argmax) is constant, P_i (mean softmax) is differentiable.
+//
+//   dY[row] = g·dout[t],  dg = <dout[t], Y[row]>              (combine transpose)  k_bwd_gate
+//   dA = (dY·W2_e) ⊙ [H > 0],  dD = dA·W1_e                    (expert data gradients)
+//   dW2_e = dYᵀ·H,  dW1_e = dAᵀ·D                              (expert weight gradients)
+//   h = x·W_r,  p = softmax(h),  c_j = α·N·f_j/T
+//   dh = Σ_r dg_r·g_r·(e_{i_r} − p) + p ⊙ (c − <p, c>)          (softmax Jacobian)  k_bwd_dh
+//   dW_r = xᵀ·dh,  dx = dout + Σ_r dD[row_r] + dh·W_rᵀ         (dispatch transpose) k_bwd_dx
+//
+// Every product is one launch of a grouped MFMA GEMM (64 x 64 output tiles, 4 waves of
+// 32 x 32, K in steps of 32 staged through LDS): bf16 operands with fp32 accumulation for the
+// expert GEMMs (v_mfma_f32_32x32x16_bf16), fp32 operands for the router's (v_mfma_f32_32x32x2_f32:
+// the router runs in fp32, [Switch review] "선택적 정밀도 캐스팅").  dW_r's long reduction over
+// the tokens is split into token ranges whose partial products are summed in a fixed order.
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kBwdTile = 64;
+constexpr int kBwdK = 32;
+constexpr int kBwdThreads = 256;
+
+// ------------------------------------------------------------------ grouped GEMM
+// C_g[M, N] = A_g[M, K] · B_g[K, N] for groups g (experts or split-K ranges).  Element (m, k) of
+// A sits at A + m·sAm + k·sAk, element (k, n) of B at B + k·sBk + n·sBn, element (m, n) of C at
+// C + m·ldc + n.  Per group: rows_dim 0 — M is the group's row count (rows of the dispatched
+// buffer from offsets[g]: A's and C's row index is offsets[g] + m); rows_dim 1 — K is the group's
+// row count (A's and B's k index is offsets[g] + k); rows_dim 2 — fixed sizes.  gA, gB, gC move
+// A, B, C by group (per-expert weights and gradients); with splits > 1 each group is a range of
+// K (split s covers [s·K/splits, (s+1)·K/splits)) and writes its own C at C + s·gC.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  int64_t sAm, sAk, sBk, sBn, ldc;
+  int64_t gA, gB, gC;
+  int M, N, K;
+  const int32_t* offsets;
+  const int32_t* rows;      // rows of each group (nullptr: offsets[g + 1] - offsets[g])
+  int rows_dim;
+  int splits;
+  const uint16_t* mask;     // out = bf16(acc · [mask > 0]) when set (C then bf16, same indexing)
+};
+
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool f32) {
+  return f32 ? static_cast<const float*>(p)[i] : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+// Operand types: TA / TB = 0 bf16, 1 fp32.  F32 selects the fp32 MFMA (operands converted to
+// fp32 in LDS); otherwise both operands are bf16.
+template <bool F32, int TA, int TB>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm(GemmArgs a) {
+  using LT = typename std::conditional<F32, float, uint16_t>::type;
+  constexpr int kPad = F32 ? 1 : 8;   // row padding of the LDS tiles (bank spread)
+  __shared__ __attribute__((aligned(16))) LT As[kBwdTile][kBwdK + kPad];   // [m][k]
+  __shared__ __attribute__((aligned(16))) LT Bs[kBwdTile][kBwdK + kPad];   // [n][k]
+  const int g = blockIdx.z;
+  const int e = a.splits > 1 ? 0 : g;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int M = a.M, K = a.K;
+  int64_t row0 = 0;
+  if (a.rows_dim < 2) {
+    row0 = a.offsets[e];
+    const int cnt = a.rows ? a.rows[e] : a.offsets[e + 1] - a.offsets[e];
+    if (a.rows_dim == 0) M = cnt; else K = cnt;
+  }
+  const int m0 = blockIdx.y * kBwdTile, n0 = blockIdx.x * kBwdTile;
+  if (m0 >= M && a.rows_dim == 0) return;   // this expert has no rows here
+  int k_begin = 0, k_end = K;
+  if (a.splits > 1) {
+    k_begin = int(int64_t(g) * K / a.splits);
+    k_end = int(int64_t(g + 1) * K / a.splits);
+  }
+  const char* Ab = static_cast<const char*>(a.A) + int64_t(e) * a.gA * (TA ? 4 : 2);
+  const char* Bb = static_cast<const char*>(a.B) + int64_t(e) * a.gB * (TB ? 4 : 2);
+  // A / B index of (m, k) / (k, n) with the group's row offset applied
+  auto a_idx = [&](int m, int k) {
+    const int64_t mm = a.rows_dim == 0 ? row0 + m : m, kk = a.rows_dim == 1 ? row0 + k : k;
+    return mm * a.sAm + kk * a.sAk;
+  };
+  auto b_idx = [&](int k, int n) {
+    const int64_t kk = a.rows_dim == 1 ? row0 + k : k;
+    return kk * a.sBk + int64_t(n) * a.sBn;
+  };
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32, r32 = lane & 31, h = lane >> 5;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int k0 = k_begin; k0 < k_end; k0 += kBwdK) {
+    // stage A [64 m][32 k] and B [64 n][32 k]: 2048 elements each, 8 per thread, every element
+    // range-checked (zeros outside)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = tid + u * kBwdThreads;
+      // A: k fastest when A is k-contiguous, else m fastest (coalesced either way)
+      int am, ak;
+      if (a.sAk == 1) { am = i >> 5; ak = i & 31; } else { ak = i >> 6; am = i & 63; }
+      const int gm = m0 + am, gk = k0 + ak;
+      float av = 0.f;
+      if (gm < M && gk < k_end) av = ld_elem(Ab, a_idx(gm, gk), TA == 1);
+      int bn, bk;
+      if (a.sBk == 1) { bn = i >> 5; bk = i & 31; } else { bk = i >> 6; bn = i & 63; }
+      const int gn = n0 + bn, gk2 = k0 + bk;
+      float bv = 0.f;
+      if (gn < a.N && gk2 < k_end) bv = ld_elem(Bb, b_idx(gk2, gn), TB == 1);
+      if constexpr (F32) {
+        As[am][ak] = av;
+        Bs[bn][bk] = bv;
+      } else {
+        As[am][ak] = f32_to_bf16(av);   // exact: av is a bf16 value
+        Bs[bn][bk] = f32_to_bf16(bv);
+      }
+    }
+    __syncthreads();
+    if constexpr (F32) {
+#pragma unroll
+      for (int s = 0; s < kBwdK / 2; ++s) {
+        const float av = As[wm + r32][2 * s + h], bv = Bs[wn + r32][2 * s + h];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kBwdK / 16; ++s) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[wm + r32][16 * s + 8 * h]);
+        const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[wn + r32][16 * s + 8 * h]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // store: element i of the accumulator is row 8 (i / 4) + 4 h + i % 4, column r32 of the 32 x 32 tile
+  const int64_t cg = int64_t(g) * a.gC;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + wm + 8 * (i >> 2) + 4 * h + (i & 3), n = n0 + wn + r32;
+    if (m < M && n < a.N) {
+      const int64_t mm = a.rows_dim == 0 ? row0 + m : m;
+      const int64_t o = cg + mm * a.ldc + n;
+      if (a.mask) {
+        const float v = a.mask[o] > 0 && (a.mask[o] & 0x8000u) == 0 ? acc[i] : 0.f;   // H > 0 (bf16 bits)
+        static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(v);
+      } else {
+        static_cast<float*>(a.C)[o] = acc[i];
+      }
+    }
+  }
+}
+
+// Fixed-order sum of split-K partials: out[i] = Σ_s part[s][i].
+__global__ __launch_bounds__(256) void k_bwd_sum_splits(const float* __restrict__ part, int splits, int64_t count,
+                                                        float* __restrict__ out) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += int64_t(gridDim.x) * 256) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += part[int64_t(s) * count + i];
+    out[i] = v;
+  }
+}
+
+// ------------------------------------------------------------------ combine transpose
+// One wave per token: for each kept pair, dg = <dout[t], Y[row]> (lane partials, then a butterfly
+// sum: a fixed order) and dY[row] = bf16(g · dout[t]); dropped pairs get dg = 0.
+__global__ __launch_bounds__(256) void k_bwd_gate(int64_t m, int d, int k, const float* __restrict__ dout,
+                                                  const uint16_t* __restrict__ y, const float* __restrict__ gate,
+                                                  const int32_t* __restrict__ t2r, uint16_t* __restrict__ dy,
+                                                  float* __restrict__ dgate) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + wave;
+  if (t >= m) return;
+  for (int r = 0; r < k; ++r) {
+    const int32_t row = t2r[t * k + r];
+    float part = 0.f;
+    if (row >= 0) {
+      const float g = gate[t * k + r];
+      for (int c = lane; c < d; c += 64) {
+        const float go = dout[t * d + c];
+        part += go * bf16_to_f32(y[int64_t(row) * d + c]);
+        dy[int64_t(row) * d + c] = f32_to_bf16(g * go);
+      }
+    }
+    const float dg = wave_sum(part);
+    if (lane == 0) dgate[t * k + r] = row >= 0 ? dg : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------ router: softmax Jacobian
+// One wave per token over its logits row h (fp32, in place): p = softmax(h),
+// dh = Σ_r dg_r·g_r·(e_{i_r} − p) + p ⊙ (c − <p, c>), c_j = α·N·counts_j / T².  g_r is the
+// chosen expert's probability recomputed here.
+__global__ __launch_bounds__(256) void k_bwd_dh(int64_t m, int n, int k, float* __restrict__ hrow,
+                                                const int32_t* __restrict__ idx, const float* __restrict__ dgate,
+                                                const int32_t* __restrict__ counts, float alpha) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + wave;
+  if (t >= m) return;
+  float* h = hrow + t * n;
+  const double cs = double(alpha) * double(n) / (double(m) * double(m));
+  float mx = -INFINITY;
+  for (int j = lane; j < n; j += 64) mx = fmaxf(mx, h[j]);
+  mx = wave_max(mx);
+  float s = 0.f;
+  for (int j = lane; j < n; j += 64) s += expf(h[j] - mx);
+  const float inv = 1.0f / wave_sum(s);
+  float pc = 0.f;   // <p, c>
+  for (int j = lane; j < n; j += 64) pc += expf(h[j] - mx) * inv * float(cs * double(counts[j]));
+  pc = wave_sum(pc);
+  // Σ_r dg_r g_r, with g_r the chosen expert's probability
+  float coef[kMaxK];
+  float csum = 0.f;
+  for (int r = 0; r < k; ++r) {
+    const int j = idx[t * k + r];
+    const float gr = expf(h[j] - mx) * inv;
+    coef[r] = dgate[t * k + r] * gr;
+    csum += coef[r];
+  }
+  __builtin_amdgcn_wave_barrier();   // every lane has read the logits it needs before any is overwritten
+  for (int j = lane; j < n; j += 64) {
+    const float p = expf(h[j] - mx) * inv;
+    float v = p * (float(cs * double(counts[j])) - pc) - csum * p;
+    for (int r = 0; r < k; ++r)
+      if (idx[t * k + r] == j) v += coef[r];
+    h[j] = v;
+  }
+}
+
+// ------------------------------------------------------------------ dx assembly
+// dx[t] = dout[t] + Σ_r dD[row(t, r)] (kept pairs, r in order) + dxr[t].
+__global__ __launch_bounds__(256) void k_bwd_dx(int64_t m, int d, int k, const float* __restrict__ dout,
+                                                const float* __restrict__ dD, const int32_t* __restrict__ t2r,
+                                                const float* __restrict__ dxr, float* __restrict__ dx) {
+  const int64_t items = m * d;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < items; i += int64_t(gridDim.x) * 256) {
+    const int64_t t = i / d, c = i - t * d;
+    float v = dout[i];
+    for (int r = 0; r < k; ++r) {
+      const int32_t row = t2r[t * k + r];
+      if (row >= 0) v += dD[int64_t(row) * d + c];
+    }
+    dx[i] = v + dxr[i];
+  }
+}
+
+// ------------------------------------------------------------------ launcher
+static size_t al256b(size_t b) { return (b + 255) / 256 * 256; }
+constexpr int kBwdRouterSplits = 32;
+
+size_t backward_ws_bytes(int64_t m, int d, int n, int k, int64_t rows_bound, int d_ff) {
+  size_t b = 0;
+  b += al256b(size_t(rows_bound) * d * sizeof(uint16_t));       // dY
+  b += al256b(size_t(m) * k * sizeof(float));                    // dgate
+  b += al256b(size_t(rows_bound) * d_ff * sizeof(uint16_t));    // dA
+  b += al256b(size_t(rows_bound) * d * sizeof(float));          // dD
+  b += al256b(size_t(m) * n * sizeof(float));                   // h, then dh
+  b += al256b(size_t(m) * d * sizeof(float));                   // dh · W_rᵀ
+  b += al256b(size_t(kBwdRouterSplits) * d * n * sizeof(float));  // dW_r partials
+  return b;
+}
+
+template <bool F32, int TA, int TB>
+static void gemm(const GemmArgs& a, int groups, int m_max, hipStream_t s) {
+  const dim3 grid(unsigned(ceil_div(a.N, kBwdTile)), unsigned(ceil_div(std::max(m_max, 1), kBwdTile)),
+                  unsigned(groups));
+  hipLaunchKernelGGL((k_bwd_gemm<F32, TA, TB>), grid, dim3(kBwdThreads), 0, s, a);
+}
+
+hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
+  char* ws = static_cast<char*>(b.ws);
+  uint16_t* dY = reinterpret_cast<uint16_t*>(ws);
+  ws += al256b(size_t(b.rows_bound) * b.d * sizeof(uint16_t));
+  float* dgate = reinterpret_cast<float*>(ws);
+  ws += al256b(size_t(b.m) * b.k * sizeof(float));
+  uint16_t* dA = reinterpret_cast<uint16_t*>(ws);
+  ws += al256b(size_t(b.rows_bound) * b.d_ff * sizeof(uint16_t));
+  float* dD = reinterpret_cast<float*>(ws);
+  ws += al256b(size_t(b.rows_bound) * b.d * sizeof(float));
+  float* hbuf = reinterpret_cast<float*>(ws);
+  ws += al256b(size_t(b.m) * b.n * sizeof(float));
+  float* dxr = reinterpret_cast<float*>(ws);
+  ws += al256b(size_t(b.m) * b.d * sizeof(float));
+  float* dwr_part = reinterpret_cast<float*>(ws);
+
+  const int n = b.n, d = b.d, d_ff = b.d_ff, k = b.k;
+  const unsigned tok_blocks = unsigned(ceil_div64(b.m, 4));
+  // 1. combine transpose: dY and the gate gradients
+  hipLaunchKernelGGL(k_bwd_gate, dim3(tok_blocks), dim3(256), 0, s, b.m, d, k, b.dout, b.y, b.gate, b.t2r, dY, dgate);
+  // 2. expert gradients, grouped by expert
+  {
+    GemmArgs g{};   // dA = (dY · W2_e) ⊙ [H > 0]: M = rows, K = d, N = d_ff
+    g.A = dY; g.sAm = d; g.sAk = 1;
+    g.B = b.w2; g.sBk = d_ff; g.sBn = 1; g.gB = int64_t(d) * d_ff;
+    g.C = dA; g.ldc = d_ff; g.mask = b.hidden;
+    g.N = d_ff; g.K = d; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 0; g.splits = 1;
+    gemm<false, 0, 0>(g, n, b.rows_max, s);
+  }
+  {
+    GemmArgs g{};   // dD = dA · W1_e: M = rows, K = d_ff, N = d
+    g.A = dA; g.sAm = d_ff; g.sAk = 1;
+    g.B = b.w1; g.sBk = d; g.sBn = 1; g.gB = int64_t(d_ff) * d;
+    g.C = dD; g.ldc = d;
+    g.N = d; g.K = d_ff; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 0; g.splits = 1;
+    gemm<false, 0, 0>(g, n, b.rows_max, s);
+  }
+  {
+    GemmArgs g{};   // dW2_e = dYᵀ · H: M = d, K = rows, N = d_ff
+    g.A = dY; g.sAm = 1; g.sAk = d;
+    g.B = b.hidden; g.sBk = d_ff; g.sBn = 1;
+    g.C = b.dw2; g.ldc = d_ff; g.gC = int64_t(d) * d_ff;
+    g.M = d; g.N = d_ff; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 1; g.splits = 1;
+    gemm<false, 0, 0>(g, n, d, s);
+  }
+  {
+    GemmArgs g{};   // dW1_e = dAᵀ · D: M = d_ff, K = rows, N = d
+    g.A = dA; g.sAm = 1; g.sAk = d_ff;
+    g.B = b.dispatched; g.sBk = d; g.sBn = 1;
+    g.C = b.dw1; g.ldc = d; g.gC = int64_t(d_ff) * d;
+    g.M = d_ff; g.N = d; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 1; g.splits = 1;
+    gemm<false, 0, 0>(g, n, d_ff, s);
+  }
+  // 3. router: h = x · W_r in fp32, then dh in place
+  {
+    GemmArgs g{};
+    g.A = b.x; g.sAm = d; g.sAk = 1;
+    g.B = b.w_r; g.sBk = n; g.sBn = 1;
+    g.C = hbuf; g.ldc = n;
+    g.M = int(b.m); g.N = n; g.K = d; g.rows_dim = 2; g.splits = 1;
+    if (b.x_bf16) gemm<true, 0, 1>(g, 1, int(b.m), s);
+    else gemm<true, 1, 1>(g, 1, int(b.m), s);
+  }
+  hipLaunchKernelGGL(k_bwd_dh, dim3(tok_blocks), dim3(256), 0, s, b.m, n, k, hbuf, b.idx, dgate, b.counts, b.alpha);
+  {
+    GemmArgs g{};   // dh · W_rᵀ: M = m, K = n, N = d; B(k = j, n = c) = W_r[c][j]
+    g.A = hbuf; g.sAm = n; g.sAk = 1;
+    g.B = b.w_r; g.sBk = 1; g.sBn = n;
+    g.C = dxr; g.ldc = d;
+    g.M = int(b.m); g.N = d; g.K = n; g.rows_dim = 2; g.splits = 1;
+    gemm<true, 1, 1>(g, 1, int(b.m), s);
+  }
+  {
+    GemmArgs g{};   // dW_r = xᵀ · dh: M = d, K = m (split in token ranges), N = n
+    g.A = b.x; g.sAm = 1; g.sAk = d;
+    g.B = hbuf; g.sBk = n; g.sBn = 1;
+    g.C = dwr_part; g.ldc = n; g.gC = int64_t(d) * n;
+    g.M = d; g.N = n; g.K = int(b.m); g.rows_dim = 2; g.splits = kBwdRouterSplits;
+    if (b.x_bf16) gemm<true, 0, 1>(g, kBwdRouterSplits, d, s);
+    else gemm<true, 1, 1>(g, kBwdRouterSplits, d, s);
+    const int64_t cnt = int64_t(d) * n;
+    hipLaunchKernelGGL(k_bwd_sum_splits, dim3(unsigned(std::min<int64_t>(ceil_div64(cnt, 256), 4096))), dim3(256), 0,
+                       s, dwr_part, kBwdRouterSplits, cnt, b.dw_r);
+  }
+  // 4. dx = dout + dispatch transpose + router path
+  hipLaunchKernelGGL(k_bwd_dx, dim3(unsigned(std::min<int64_t>(ceil_div64(b.m * d, 256), 65536))), dim3(256), 0, s,
+                     b.m, d, k, b.dout, dD, b.t2r, dxr, b.dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -172,4 +172,35 @@ hipError_t launch_balance_minibatch(const BalanceArgs& a, hipStream_t s);
 // SignSGD steps on β (n <= 256), then the counting top-k of the final β
 hipError_t launch_signsgd(const BalanceArgs& a, float gamma, hipStream_t s);
 
+// ---------------------------------------------------------------- backward
+struct BackwardArgs {
+  int64_t m;
+  int d, n, k, d_ff;
+  int64_t rows_bound;   // rows of the dispatched buffer
+  int rows_max;         // most rows any expert holds
+  bool x_bf16;
+  float alpha;
+  const void* x;
+  const float* w_r;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  const int32_t* idx;
+  const float* gate;
+  const int32_t* counts;
+  const int32_t* t2r;
+  const int32_t* offsets;
+  const int32_t* rows;   // rows per expert (capacity layout) or nullptr (compact offsets)
+  const uint16_t* dispatched;
+  const uint16_t* hidden;
+  const uint16_t* y;
+  const float* dout;
+  float* dx;
+  float* dw_r;
+  float* dw1;
+  float* dw2;
+  void* ws;
+};
+size_t backward_ws_bytes(int64_t m, int d, int n, int k, int64_t rows_bound, int d_ff);
+hipError_t launch_backward(const BackwardArgs& b, hipStream_t s);
+
 }  // namespace moe

@@ -68,9 +68,11 @@ def _expert_forward(D: np.ndarray, w1: np.ndarray, w2: np.ndarray, rounded: bool
 
 
 def switch_layer_backward(x, w_r, idx, token_to_row, expert_offsets, expert_rows, w1, w2, dout, alpha: float,
-                          counts=None, rounded: bool = True) -> LayerGrads:
+                          counts=None, rounded: bool = True, wgrad_experts=None) -> LayerGrads:
     """Gradients of L = Σ out ⊙ dout + L_aux for one Switch layer forward, given its selection
-    (idx [T, k]), its dispatch maps and the expert weights (bf16 bits or float arrays)."""
+    (idx [T, k]), its dispatch maps and the expert weights (bf16 bits or float arrays).
+    wgrad_experts: the experts whose weight gradients are returned (dw1 / dw2 then hold those,
+    in that order); None = all."""
     x64 = R.decode_hidden(x)
     T, d = x64.shape
     w_r64 = np.asarray(w_r, np.float64)
@@ -88,8 +90,10 @@ def switch_layer_backward(x, w_r, idx, token_to_row, expert_offsets, expert_rows
 
     dx = dout.copy()
     dgate = np.zeros((T, k))
-    dw1 = np.zeros((N,) + np.shape(w1)[1:])
-    dw2 = np.zeros((N,) + np.shape(w2)[1:])
+    wl = list(range(N)) if wgrad_experts is None else [int(e) for e in wgrad_experts]
+    slot = {e: i for i, e in enumerate(wl)}
+    dw1 = np.zeros((len(wl),) + np.shape(w1)[1:])
+    dw2 = np.zeros((len(wl),) + np.shape(w2)[1:])
     t2r = np.asarray(token_to_row)
     for e in range(N):
         lo, n_e = int(expert_offsets[e]), int(expert_rows[e])
@@ -107,8 +111,9 @@ def switch_layer_backward(x, w_r, idx, token_to_row, expert_offsets, expert_rows
         dH = dY @ W2
         dA = dH * (A > 0)
         dD = dA @ W1
-        dw2[e] = dY.T @ H
-        dw1[e] = dA.T @ D
+        if e in slot:
+            dw2[slot[e]] = dY.T @ H
+            dw1[slot[e]] = dA.T @ D
         np.add.at(dx, pt, dD)
     # softmax Jacobian: gate term plus the balancing-loss term
     dh = p * (c[None, :] - np.sum(p * c[None, :], axis=1, keepdims=True))
