@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (HBM counter calibration)")
     p.add_argument("--workload", default="switch_base",
-                   choices=["switch_base", "lossfree", "balanced", "switch_c", "qb_demo"],
+                   choices=["switch_base", "lossfree", "balanced", "switch_c", "qb_demo", "backward"],
                    help="switch_base (default) is the headline; the others report the other configurations")
     return p.parse_args()
 
@@ -239,7 +239,7 @@ def main():
 
     if args.workload != "switch_base":
         {"lossfree": bench_lossfree, "balanced": bench_balanced, "switch_c": bench_switch_c,
-         "qb_demo": bench_qb_demo}[args.workload](args)
+         "qb_demo": bench_qb_demo, "backward": bench_backward}[args.workload](args)
         return
 
     dev = "cuda:0"
@@ -735,6 +735,54 @@ def bench_switch_c(args):
         "expert_ffn_roofline": {"bound": "hbm", "achieved": ffn_bytes / t_ffn / 1e9, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": ffn_bytes / t_ffn / 1e9 / HBM_PEAK_GBS,
                                 "algorithmic_bytes_per_stage": ffn_bytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_backward(args):
+    """The Switch-Base layer's backward (moe_switch_layer_backward) at the forward's saved values:
+    T=8192, d=768, N=128, top-1, cf 1.25, ReLU FFN d_ff=3072, fp32 upstream gradient."""
+    import numpy as np
+    import torch
+    import load_balanced_expert_amd as M
+    import workloads as W
+    spec = W.SWITCH_BASE
+    T, d, N, d_ff = spec.T, spec.d, spec.N, spec.d_ff
+    cap = M.capacity(T, N, args.cf)
+    inp = W.switch_inputs(spec, args.seed)
+    w1, w2 = W.all_expert_weights(spec, args.seed)
+    x, w_r, W1, W2 = (_dev(a, torch, np) for a in (inp.x, inp.w_r, w1, w2))
+    del w1, w2
+    dout = torch.randn((T, d), generator=torch.Generator(device="cuda:0").manual_seed(args.seed), device="cuda:0")
+    fwd = M.switch_layer(x, w_r, k=1, capacity=cap, alpha=spec.alpha, w1=W1, w2=W2)
+    g = M.switch_layer_backward(x, w_r, W1, W2, fwd, dout, capacity=cap, alpha=spec.alpha)
+    torch.cuda.synchronize()
+    he = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    steps = max(3, min(args.steps, 20))
+    ms, wall_ms = _timed(he, stream, lambda: M.switch_layer_backward(x, w_r, W1, W2, fwd, dout, capacity=cap,
+                                                                      alpha=spec.alpha, out=g), steps, 2, torch)
+    rows = int(fwd.expert_rows.sum().item())
+    # bytes the method must move: both weight sets read (data gradients), both weight gradients
+    # written in fp32, the rows' activations and gradients, the router's operands
+    wbytes = 2 * N * d * d_ff * 2 + 2 * N * d * d_ff * 4
+    abytes = rows * (d * 2 * 3 + d_ff * 2 * 3 + d * 4 * 2) + T * d * (4 * 2 + 2 * 2) + 2 * d * N * 4 + T * N * 4 * 2
+    alg = wbytes + abytes
+    flops = 4 * 2.0 * rows * d * d_ff + 3 * 2.0 * T * d * N
+    out = {
+        "metric": "backward tokens/sec (Switch-Base layer: router, balancing loss, expert FFN, dispatch/combine)",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 2,
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32 gradients; bf16 expert operands with fp32 accumulation; fp32 router",
+        "data": "synthetic (seeded normals; upstream gradient ~N(0,1))",
+        "config": {"workload": f"backward: T=8192, d_model=768, N=128, top-1, capacity factor {args.cf} "
+                               f"(capacity {cap}), ReLU FFN d_ff=3072", "parallelism": "single GPU"},
+        "roofline": {"kernel": "whole backward (all launches)", "bound": "hbm",
+                     "achieved": alg / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_step": alg, "algorithmic_flops_per_step": flops,
+                     "mfma_frac_bf16": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

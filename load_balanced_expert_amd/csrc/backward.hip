@@ -19,7 +19,6 @@
 // expert GEMMs (v_mfma_f32_32x32x16_bf16), fp32 operands for the router's (v_mfma_f32_32x32x2_f32:
 // the router runs in fp32, [Switch review] "선택적 정밀도 캐스팅").  dW_r's long reduction over
 // the tokens is split into token ranges whose partial products are summed in a fixed order.
-#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -56,14 +55,11 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool f32) {
   return f32 ? static_cast<const float*>(p)[i] : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
 }
 
-// Operand types: TA / TB = 0 bf16, 1 fp32.  F32 selects the fp32 MFMA (operands converted to
-// fp32 in LDS); otherwise both operands are bf16.
-template <bool F32, int TA, int TB>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm(GemmArgs a) {
-  using LT = typename std::conditional<F32, float, uint16_t>::type;
-  constexpr int kPad = F32 ? 1 : 8;   // row padding of the LDS tiles (bank spread)
-  __shared__ __attribute__((aligned(16))) LT As[kBwdTile][kBwdK + kPad];   // [m][k]
-  __shared__ __attribute__((aligned(16))) LT Bs[kBwdTile][kBwdK + kPad];   // [n][k]
+// fp32 MFMA form: operands of type TA / TB (0 bf16, 1 fp32) converted to fp32 in LDS, any sizes.
+template <int TA, int TB>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm_f32(GemmArgs a) {
+  __shared__ float As[kBwdTile][kBwdK + 1];   // [m][k]
+  __shared__ float Bs[kBwdTile][kBwdK + 1];   // [n][k]
   const int g = blockIdx.z;
   const int e = a.splits > 1 ? 0 : g;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -113,32 +109,111 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm(GemmArgs a) {
       const int gn = n0 + bn, gk2 = k0 + bk;
       float bv = 0.f;
       if (gn < a.N && gk2 < k_end) bv = ld_elem(Bb, b_idx(gk2, gn), TB == 1);
-      if constexpr (F32) {
-        As[am][ak] = av;
-        Bs[bn][bk] = bv;
-      } else {
-        As[am][ak] = f32_to_bf16(av);   // exact: av is a bf16 value
-        Bs[bn][bk] = f32_to_bf16(bv);
-      }
+      As[am][ak] = av;
+      Bs[bn][bk] = bv;
     }
     __syncthreads();
-    if constexpr (F32) {
 #pragma unroll
-      for (int s = 0; s < kBwdK / 2; ++s) {
-        const float av = As[wm + r32][2 * s + h], bv = Bs[wn + r32][2 * s + h];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < kBwdK / 16; ++s) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[wm + r32][16 * s + 8 * h]);
-        const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[wn + r32][16 * s + 8 * h]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
-      }
+    for (int s = 0; s < kBwdK / 2; ++s) {
+      const float av = As[wm + r32][2 * s + h], bv = Bs[wn + r32][2 * s + h];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
     __syncthreads();
   }
   // store: element i of the accumulator is row 8 (i / 4) + 4 h + i % 4, column r32 of the 32 x 32 tile
+  const int64_t cg = int64_t(g) * a.gC;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + wm + 8 * (i >> 2) + 4 * h + (i & 3), n = n0 + wn + r32;
+    if (m < M && n < a.N) {
+      const int64_t mm = a.rows_dim == 0 ? row0 + m : m;
+      static_cast<float*>(a.C)[cg + mm * a.ldc + n] = acc[i];
+    }
+  }
+}
+
+// bf16 MFMA form (v_mfma_f32_32x32x16_bf16), both operands bf16.  Each K step of 32 puts the
+// operand tiles [64 outer][32 k] in LDS with k contiguous; each operand arrives as one 16-byte
+// vector per thread (256 vectors per tile), along k when k is contiguous in memory (written to
+// LDS whole), along the outer dimension otherwise (written element by element, transposed).  The
+// contiguous dimension of each operand is a multiple of 8; a vector past the tile's valid range
+// is zeros.  The next step's loads are issued before the current step's products.
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm_bf16(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[kBwdTile][kBwdK + 8];   // [m][k]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBwdTile][kBwdK + 8];   // [n][k]
+  const int g = blockIdx.z;
+  const int e = a.splits > 1 ? 0 : g;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int M = a.M, K = a.K;
+  int64_t row0 = 0;
+  if (a.rows_dim < 2) {
+    row0 = a.offsets[e];
+    const int cnt = a.rows ? a.rows[e] : a.offsets[e + 1] - a.offsets[e];
+    if (a.rows_dim == 0) M = cnt; else K = cnt;
+  }
+  const int m0 = blockIdx.y * kBwdTile, n0 = blockIdx.x * kBwdTile;
+  if (m0 >= M && a.rows_dim == 0) return;   // this expert has no rows here
+  int k_begin = 0, k_end = K;
+  if (a.splits > 1) {
+    k_begin = int(int64_t(g) * K / a.splits);
+    k_end = int(int64_t(g + 1) * K / a.splits);
+  }
+  const uint16_t* Ab = static_cast<const uint16_t*>(a.A) + int64_t(e) * a.gA;
+  const uint16_t* Bb = static_cast<const uint16_t*>(a.B) + int64_t(e) * a.gB;
+  auto a_idx = [&](int m, int k) {
+    const int64_t mm = a.rows_dim == 0 ? row0 + m : m, kk = a.rows_dim == 1 ? row0 + k : k;
+    return mm * a.sAm + kk * a.sAk;
+  };
+  auto b_idx = [&](int k, int n) {
+    const int64_t kk = a.rows_dim == 1 ? row0 + k : k;
+    return kk * a.sBk + int64_t(n) * a.sBn;
+  };
+  const bool a_kc = a.sAk == 1, b_kc = a.sBk == 1;
+  // the thread's vector of one operand at step k0: (outer, k .. k + 7) or (outer .. outer + 7, k)
+  auto fetch = [&](const uint16_t* base, bool kc, bool is_a, int lim, int o0, int k0) {
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (kc) {
+      const int go = o0 + (tid >> 2), gk = k0 + (tid & 3) * 8;
+      if (go < lim && gk < k_end)
+        w = *reinterpret_cast<const u32x4*>(base + (is_a ? a_idx(go, gk) : b_idx(gk, go)));
+    } else {
+      const int go = o0 + (tid & 7) * 8, gk = k0 + (tid >> 3);
+      if (go < lim && gk < k_end)
+        w = *reinterpret_cast<const u32x4*>(base + (is_a ? a_idx(go, gk) : b_idx(gk, go)));
+    }
+    return w;
+  };
+  auto put = [&](uint16_t (*S)[kBwdK + 8], bool kc, const u32x4& w) {
+    if (kc) {
+      *reinterpret_cast<u32x4*>(&S[tid >> 2][(tid & 3) * 8]) = w;
+    } else {
+      const int o = (tid & 7) * 8, kk = tid >> 3;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) S[o + j][kk] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
+    }
+  };
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32, r32 = lane & 31, h = lane >> 5;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  u32x4 ra = fetch(Ab, a_kc, true, M, m0, k_begin);
+  u32x4 rb = fetch(Bb, b_kc, false, a.N, n0, k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += kBwdK) {
+    put(As, a_kc, ra);
+    put(Bs, b_kc, rb);
+    lds_barrier();
+    if (k0 + kBwdK < k_end) {
+      ra = fetch(Ab, a_kc, true, M, m0, k0 + kBwdK);
+      rb = fetch(Bb, b_kc, false, a.N, n0, k0 + kBwdK);
+    }
+#pragma unroll
+    for (int s = 0; s < kBwdK / 16; ++s) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[wm + r32][16 * s + 8 * h]);
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[wn + r32][16 * s + 8 * h]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+    }
+    lds_barrier();
+  }
   const int64_t cg = int64_t(g) * a.gC;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -265,11 +340,17 @@ size_t backward_ws_bytes(int64_t m, int d, int n, int k, int64_t rows_bound, int
   return b;
 }
 
-template <bool F32, int TA, int TB>
-static void gemm(const GemmArgs& a, int groups, int m_max, hipStream_t s) {
-  const dim3 grid(unsigned(ceil_div(a.N, kBwdTile)), unsigned(ceil_div(std::max(m_max, 1), kBwdTile)),
-                  unsigned(groups));
-  hipLaunchKernelGGL((k_bwd_gemm<F32, TA, TB>), grid, dim3(kBwdThreads), 0, s, a);
+static dim3 gemm_grid(const GemmArgs& a, int groups, int m_max) {
+  return dim3(unsigned(ceil_div(a.N, kBwdTile)), unsigned(ceil_div(std::max(m_max, 1), kBwdTile)), unsigned(groups));
+}
+
+static void gemm_bf16(const GemmArgs& a, int groups, int m_max, hipStream_t s) {
+  hipLaunchKernelGGL(k_bwd_gemm_bf16, gemm_grid(a, groups, m_max), dim3(kBwdThreads), 0, s, a);
+}
+
+template <int TA, int TB>
+static void gemm_f32(const GemmArgs& a, int groups, int m_max, hipStream_t s) {
+  hipLaunchKernelGGL((k_bwd_gemm_f32<TA, TB>), gemm_grid(a, groups, m_max), dim3(kBwdThreads), 0, s, a);
 }
 
 hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
@@ -299,7 +380,7 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.B = b.w2; g.sBk = d_ff; g.sBn = 1; g.gB = int64_t(d) * d_ff;
     g.C = dA; g.ldc = d_ff; g.mask = b.hidden;
     g.N = d_ff; g.K = d; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 0; g.splits = 1;
-    gemm<false, 0, 0>(g, n, b.rows_max, s);
+    gemm_bf16(g, n, b.rows_max, s);
   }
   {
     GemmArgs g{};   // dD = dA · W1_e: M = rows, K = d_ff, N = d
@@ -307,7 +388,7 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.B = b.w1; g.sBk = d; g.sBn = 1; g.gB = int64_t(d_ff) * d;
     g.C = dD; g.ldc = d;
     g.N = d; g.K = d_ff; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 0; g.splits = 1;
-    gemm<false, 0, 0>(g, n, b.rows_max, s);
+    gemm_bf16(g, n, b.rows_max, s);
   }
   {
     GemmArgs g{};   // dW2_e = dYᵀ · H: M = d, K = rows, N = d_ff
@@ -315,7 +396,7 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.B = b.hidden; g.sBk = d_ff; g.sBn = 1;
     g.C = b.dw2; g.ldc = d_ff; g.gC = int64_t(d) * d_ff;
     g.M = d; g.N = d_ff; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 1; g.splits = 1;
-    gemm<false, 0, 0>(g, n, d, s);
+    gemm_bf16(g, n, d, s);
   }
   {
     GemmArgs g{};   // dW1_e = dAᵀ · D: M = d_ff, K = rows, N = d
@@ -323,7 +404,7 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.B = b.dispatched; g.sBk = d; g.sBn = 1;
     g.C = b.dw1; g.ldc = d; g.gC = int64_t(d_ff) * d;
     g.M = d_ff; g.N = d; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 1; g.splits = 1;
-    gemm<false, 0, 0>(g, n, d_ff, s);
+    gemm_bf16(g, n, d_ff, s);
   }
   // 3. router: h = x · W_r in fp32, then dh in place
   {
@@ -332,8 +413,8 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.B = b.w_r; g.sBk = n; g.sBn = 1;
     g.C = hbuf; g.ldc = n;
     g.M = int(b.m); g.N = n; g.K = d; g.rows_dim = 2; g.splits = 1;
-    if (b.x_bf16) gemm<true, 0, 1>(g, 1, int(b.m), s);
-    else gemm<true, 1, 1>(g, 1, int(b.m), s);
+    if (b.x_bf16) gemm_f32<0, 1>(g, 1, int(b.m), s);
+    else gemm_f32<1, 1>(g, 1, int(b.m), s);
   }
   hipLaunchKernelGGL(k_bwd_dh, dim3(tok_blocks), dim3(256), 0, s, b.m, n, k, hbuf, b.idx, dgate, b.counts, b.alpha);
   {
@@ -342,7 +423,7 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.B = b.w_r; g.sBk = 1; g.sBn = n;
     g.C = dxr; g.ldc = d;
     g.M = int(b.m); g.N = d; g.K = n; g.rows_dim = 2; g.splits = 1;
-    gemm<true, 1, 1>(g, 1, int(b.m), s);
+    gemm_f32<1, 1>(g, 1, int(b.m), s);
   }
   {
     GemmArgs g{};   // dW_r = xᵀ · dh: M = d, K = m (split in token ranges), N = n
@@ -350,8 +431,8 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.B = hbuf; g.sBk = n; g.sBn = 1;
     g.C = dwr_part; g.ldc = n; g.gC = int64_t(d) * n;
     g.M = d; g.N = n; g.K = int(b.m); g.rows_dim = 2; g.splits = kBwdRouterSplits;
-    if (b.x_bf16) gemm<true, 0, 1>(g, kBwdRouterSplits, d, s);
-    else gemm<true, 1, 1>(g, kBwdRouterSplits, d, s);
+    if (b.x_bf16) gemm_f32<0, 1>(g, kBwdRouterSplits, d, s);
+    else gemm_f32<1, 1>(g, kBwdRouterSplits, d, s);
     const int64_t cnt = int64_t(d) * n;
     hipLaunchKernelGGL(k_bwd_sum_splits, dim3(unsigned(std::min<int64_t>(ceil_div64(cnt, 256), 4096))), dim3(256), 0,
                        s, dwr_part, kBwdRouterSplits, cnt, b.dw_r);
