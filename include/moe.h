@@ -230,7 +230,8 @@ moe_status moe_global_aux(int32_t n, const int64_t* global_counts, const int64_t
  *     flow on the expert graph, fp64) from x = top-k(s − β) until every expert
  *     holds exactly q tokens; idx is then the LP optimum (eq. (4), which has an
  *     integral optimum, "극대-극소") and beta the final potentials, an optimal
- *     dual of eq. (8) rounded to fp32.  Requires n <= 64.
+ *     dual of eq. (8) rounded to fp32.  Requires n <= 64, or n <= 128 with
+ *     m <= 65535 and m·(16 + 2k) <= 129024 (MOE_ERR_UNSUPPORTED otherwise).
  * s [m, n] fp32; beta [n] fp32 in/out; idx [m, k] int32 out; counts [n] int32 out;
  * alpha [m] fp32 out or NULL (the last α computed); info [4] int32 out or NULL:
  * {QB steps run, augmentations, 1 if every count == q else 0, 0}.

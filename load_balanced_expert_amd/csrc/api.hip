@@ -356,7 +356,7 @@ moe_status moe_balance_duals(int64_t m, int32_t n, int32_t k, const float* s, fl
   if (mode != MOE_QB_SOLVE && mode != MOE_QB_ONLINE) return MOE_ERR_INVALID_ARG;
   if (iters < 0 || (mode == MOE_QB_ONLINE && (iters != 1 || exact))) return MOE_ERR_INVALID_ARG;
   if (n > kMaxExperts || m > 0x7FFFFFFFll || m * k > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
-  if (exact && n > 64) return MOE_ERR_UNSUPPORTED;
+  if (exact && !exact_completion_supported(m, n, k)) return MOE_ERR_UNSUPPORTED;
   if (!ws_ok(ws, ws_bytes, moe_balance_workspace_size(m, n, k, exact))) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
   BalanceArgs a{};
   a.m = m;

@@ -39,6 +39,8 @@ size_t balance_ws_bytes(int64_t m, int n, int k, bool exact) {
   if (exact) {
     b += 2 * al256(size_t(m) * k * sizeof(int32_t));   // assignment, list positions
     b += al256(size_t(n) * m * sizeof(int32_t));       // per-expert token lists
+    b += al256(size_t(n) * sizeof(double));            // final potentials
+    b += 2 * al256(size_t(128) * 128 * sizeof(double)) + al256(size_t(128) * 128 * sizeof(int));   // M, W (n > 64)
   }
   return b;
 }
@@ -880,6 +882,7 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
   __shared__ int pt[1024];
   __shared__ double pi[kCompleteMaxN], dist[kCompleteMaxN];
   __shared__ int cnt[kCompleteMaxN], pred[kCompleteMaxN], vis[kCompleteMaxN], dirty[kCompleteMaxN];
+  __shared__ int ptok[kCompleteMaxN];
   __shared__ int s_go, s_target, s_fail;
   __shared__ double s_D;
   const int n = a.n, k = a.k;
@@ -1001,11 +1004,20 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
       // M stays exact: the source row is rescanned next round; token i joining
       // j adds it as a candidate to row j; for the other experts a of token i,
       // (a -> aa) gains candidate i and (a -> j) loses it (a rescan only if i
-      // was its cheapest token).
-      int j = s_target;
+      // was its cheapest token).  Every edge moves the token its cost was taken from:
+      // the path's tokens are read before any of them moves.
+      if (lane == 0) {
+        int jj = s_target, len = 0;
+        while (pred[jj] >= 0) {
+          ptok[len++] = arg[pred[jj] * n + jj];
+          jj = pred[jj];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      int j = s_target, pe = 0;
       while (pred[j] >= 0) {
         const int aa = pred[j];
-        const int i = arg[aa * n + j];
+        const int i = __builtin_amdgcn_readfirstlane(ptok[pe++]);
         int32_t* xr = xi + int64_t(i) * k;
         int r = 0;
         for (int rr = 0; rr < k; ++rr)
@@ -1088,6 +1100,655 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
     if (a.info) {
       a.info[1] = aug;
       a.info[2] = bal && !s_fail;
+      a.info[3] = s_fail;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ exact completion, LDS-resident form
+// The same successive shortest paths for n <= 64 when the assignment fits in LDS (a 64-bit mask of
+// held experts per token, plus a 16-bit list entry per (token, slot)):
+//  * k_qbc_init (one wave per token, many workgroups): x = top-k of the exact keys s_ij − β_j;
+//  * k_qbc_solve (one workgroup): x and M (fp64 values and tokens) in LDS.  A token that leaves
+//    expert a stales only the entries of row a (and of its other experts' rows, column j) whose
+//    cheapest token it was; each round recomputes those (row, column) pairs, one wave per pair
+//    with the lanes over the row's tokens (listed from the masks), or whole rows (lanes over the
+//    columns, the row's tokens split over waves that meet in LDS) when many are stale, as at the
+//    start.  Dijkstra on one wave reads precomputed reduced costs and takes the arg-min lane
+//    from a ballot of the fp64 minimum.  The tokens of the path's edges
+//    are read before any of them moves, so every edge moves the token its cost was taken from;
+//  * k_qbc_out (one wave per token): idx by descending s_ij − π_j.
+// Candidates compare as fp64 values with the lower token index on ties.
+constexpr int kFastMaxN = 128;
+constexpr int kFastLdsLimit = 150 * 1024;   // dynamic LDS the solve kernel may take (static arrays aside)
+
+static int fast_npl(int n) { return n <= 64 ? 1 : 2; }
+// n <= 64: M (fp64), its tokens and the reduced costs; n <= 128: the wave partials; then the
+// token masks and the 16-bit token lists
+static size_t fast_lds_bytes(int npl, int64_t m, int k) {
+  const size_t fixed = npl == 1 ? size_t(64 * 64) * 20 : size_t(16 * 128) * 12;
+  return fixed + size_t(m) * 8 * npl + size_t(round_up(int(m * k) * 2, 16));
+}
+static bool fast_complete_ok(int64_t m, int n, int k) {
+  return n <= kFastMaxN && m <= 65535 && m * k <= (1 << 20) &&
+         fast_lds_bytes(fast_npl(n), m, k) <= size_t(kFastLdsLimit);
+}
+bool exact_completion_supported(int64_t m, int n, int k) { return n <= kCompleteMaxN || fast_complete_ok(m, n, k); }
+
+__global__ __launch_bounds__(256) void k_qbc_init(BalanceArgs a, int32_t* __restrict__ xi) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t i = int64_t(blockIdx.x) * 4 + wave;
+  if (i >= a.m) return;
+  const int n = a.n, k = a.k;
+  // lane holds experts lane and lane + 64
+  double v[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = lane + 64 * u;
+    v[u] = j < n ? double(a.s[i * n + j]) - double(a.beta[j]) : -INFINITY;
+  }
+  double last = INFINITY;
+  int lj = -1;
+  for (int r = 0; r < k; ++r) {
+    double bk = -INFINITY;
+    int bj = 0x7FFFFFFF;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = lane + 64 * u;
+      if (j < n && better64(last, lj, v[u], j) && better64(v[u], j, bk, bj)) {
+        bk = v[u];
+        bj = j;
+      }
+    }
+    wave_argbest64(bk, bj);
+    last = bk;
+    lj = bj;
+    if (lane == 0) xi[i * k + r] = bj;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_qbc_out(BalanceArgs a, const int32_t* __restrict__ xi,
+                                                 const double* __restrict__ pi) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t i = int64_t(blockIdx.x) * 4 + wave;
+  if (i >= a.m) return;
+  const int n = a.n, k = a.k;
+  double v = -INFINITY;
+  int jj = 0x7FFFFFFF;
+  if (lane < k) {
+    jj = xi[i * k + lane];
+    v = double(a.s[i * n + jj]) - pi[jj];
+  }
+  int rank = 0;   // rank of the lane's expert among the token's k (k <= 64)
+  for (int r = 0; r < k; ++r) {
+    const double ov = __shfl(v, r, 64);
+    const int oj = __shfl(jj, r, 64);
+    if (lane < k && better64(ov, oj, v, jj)) ++rank;
+  }
+  if (lane < k) a.idx[i * k + rank] = jj;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  return __longlong_as_double(
+      int64_t((uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l))) << 32) |
+              uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l))));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false));
+  return __longlong_as_double(int64_t((uint64_t(hi) << 32) | lo));
+}
+// Wave-wide fp64 minimum (no NaN inputs): DPP within 16-lane rows, the row swap, the two halves.
+__device__ __forceinline__ double wave_min_f64(double v) {
+  v = fmin(v, dpp_d<kDppXor1>(v));
+  v = fmin(v, dpp_d<kDppXor2>(v));
+  v = fmin(v, dpp_d<kDppHalfMirror>(v));
+  v = fmin(v, dpp_d<kDppMirror>(v));
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const auto lo = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+  v = fmin(__longlong_as_double(int64_t((uint64_t(hi[0]) << 32) | lo[0])),
+           __longlong_as_double(int64_t((uint64_t(hi[1]) << 32) | lo[1])));
+  return fmin(readlane_f64(v, 0), readlane_f64(v, 32));
+}
+
+// All-lane fp64 minimum (no NaN inputs): DPP within 16-lane rows, then the row and half swaps.
+__device__ __forceinline__ double wave_min_f64_all(double v) {
+  v = fmin(v, dpp_d<kDppXor1>(v));
+  v = fmin(v, dpp_d<kDppXor2>(v));
+  v = fmin(v, dpp_d<kDppHalfMirror>(v));
+  v = fmin(v, dpp_d<kDppMirror>(v));
+  uint64_t b = uint64_t(__double_as_longlong(v));
+  auto lo = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+  v = fmin(__longlong_as_double(int64_t((uint64_t(hi[0]) << 32) | lo[0])),
+           __longlong_as_double(int64_t((uint64_t(hi[1]) << 32) | lo[1])));
+  b = uint64_t(__double_as_longlong(v));
+  lo = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
+  hi = __builtin_amdgcn_permlane32_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+  return fmin(__longlong_as_double(int64_t((uint64_t(hi[0]) << 32) | lo[0])),
+              __longlong_as_double(int64_t((uint64_t(hi[1]) << 32) | lo[1])));
+}
+
+// All-lane u32 minimum: DPP within 16-lane rows, then the row and half swaps.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(0xFFFFFFFFu), int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_min_u32_all(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(uint32_t(r[0]), uint32_t(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(uint32_t(r[0]), uint32_t(r[1]));
+}
+
+constexpr int kPairMax = 64;   // stale (row, column) pairs recomputed one by one; more: whole rows
+
+// Experts held by one token: NPL 64-bit words (experts 64 c + bit of word c).
+template <int NPL>
+struct XMask {
+  uint64_t w[NPL];
+};
+template <int NPL>
+__device__ __forceinline__ bool xm_has(const XMask<NPL>& h, int j) {
+  if constexpr (NPL == 1) return (h.w[0] >> j) & 1ull;
+  else return ((j < 64 ? h.w[0] : h.w[1]) >> (j & 63)) & 1ull;
+}
+template <int NPL>
+__device__ __forceinline__ void xm_flip(XMask<NPL>& h, int j) {
+  if constexpr (NPL == 1) h.w[0] ^= 1ull << j;
+  else if (j < 64) h.w[0] ^= 1ull << j;
+  else h.w[1] ^= 1ull << (j - 64);
+}
+__device__ __forceinline__ uint64_t col_bits(int c, int n) {   // experts 64 c .. of n present in word c
+  const int v = n - 64 * c;
+  return v <= 0 ? 0ull : v >= 64 ? ~0ull : (1ull << v) - 1ull;
+}
+// a lane's value of expert j (uniform), the lane holding experts lane + 64 c
+template <int NPL>
+__device__ __forceinline__ float lane_of(const float (&v)[NPL], int j) {
+  if constexpr (NPL == 1) return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[0]), j));
+  else
+    return j < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[0]), j))
+                  : __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[1]), j - 64));
+}
+
+// NPL experts per lane (n <= 64 NPL).  NPL = 1: M, its tokens and the reduced costs in LDS;
+// NPL = 2: in global memory (gM, gArg, gW), the rest in LDS.
+template <int NPL>
+__global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __restrict__ xi,
+                                                    double* __restrict__ pi_out, double* __restrict__ gM,
+                                                    int* __restrict__ gArg, double* __restrict__ gW) {
+  constexpr int NN = 64 * NPL;
+  constexpr int TB = 16 / NPL;   // tokens per batch in the whole-row refresh
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  double* Md;     // [NN][NN] M (INFINITY: no token)
+  int* arg;       // [NN][NN] its tokens
+  double* W;      // [NN][NN] reduced costs (Dijkstra)
+  double* pk;     // [16][NN] wave partials (whole-row refresh)
+  int* pt;
+  unsigned char* rest;
+  if constexpr (NPL == 1) {
+    Md = reinterpret_cast<double*>(lds_raw);
+    arg = reinterpret_cast<int*>(Md + NN * NN);
+    W = reinterpret_cast<double*>(arg + NN * NN);
+    pk = W;   // the partials live only while the reduced costs are dead
+    pt = reinterpret_cast<int*>(pk + 16 * NN);
+    rest = reinterpret_cast<unsigned char*>(W + NN * NN);
+  } else {
+    Md = gM;
+    arg = gArg;
+    W = gW;
+    pk = reinterpret_cast<double*>(lds_raw);
+    pt = reinterpret_cast<int*>(pk + 16 * NN);
+    rest = reinterpret_cast<unsigned char*>(pt + 16 * NN);
+  }
+  const int n = a.n, k = a.k, m = int(a.m), q = int(a.q);
+  XMask<NPL>* hm = reinterpret_cast<XMask<NPL>*>(rest);    // [m] experts held by each token
+  uint16_t* lst = reinterpret_cast<uint16_t*>(hm + m);      // listed tokens of the rows being refreshed
+  __shared__ double pi[NN], dist[NN];
+  __shared__ uint64_t dcol[NN * NPL];   // per row of M: the columns whose cheapest token may have left
+  __shared__ int cnt[NN], pred[NN], vis[NN], roff[NN], rfill[NN], drow[NN];
+  __shared__ int path_a[NN], path_j[NN], path_t[NN];
+  __shared__ uint8_t pair_e[kPairMax], pair_j[kPairMax];
+  __shared__ uint64_t s_dm[NPL];
+  __shared__ int s_nd, s_np, s_go, s_target, s_fail, s_len;
+  __shared__ double s_D;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const float* __restrict__ s = a.s;
+
+  if (tid < NN) {
+    pi[tid] = tid < n ? double(a.beta[tid]) : 0.0;
+    cnt[tid] = 0;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) dcol[tid * NPL + c] = tid < n ? col_bits(c, n) : 0ull;
+  }
+  __syncthreads();
+  for (int t = tid; t < m; t += 1024) {
+    XMask<NPL> h{};
+    for (int r = 0; r < k; ++r) {
+      const int e = xi[int64_t(t) * k + r];
+      xm_flip(h, e);
+      atomicAdd(&cnt[e], 1);
+    }
+    hm[t] = h;
+  }
+  __syncthreads();
+  int aug = 0;
+  const int max_aug = m * k;
+  for (;;) {
+    // ---- refresh the entries of M whose cheapest token may have left
+    if (wave == 0) {
+      // rows lane + 64 c, in the order c, then lane
+      int cc[NPL], pc[NPL], ci[NPL], pi_[NPL];
+      bool dj[NPL];
+      uint64_t dmk[NPL];
+      int tot_c = 0, tot_p = 0;
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) {
+        const int r = lane + 64 * c;
+        uint64_t any = 0;
+        int pop = 0;
+#pragma unroll
+        for (int w = 0; w < NPL; ++w) {
+          const uint64_t d = r < n ? dcol[r * NPL + w] : 0ull;
+          any |= d;
+          pop += __popcll(d);
+        }
+        dj[c] = any != 0ull;
+        cc[c] = dj[c] ? cnt[r] : 0;
+        pc[c] = pop;
+        int incl = cc[c], pincl = pc[c];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off, 64), po = __shfl_up(pincl, off, 64);
+          if (lane >= off) {
+            incl += o;
+            pincl += po;
+          }
+        }
+        ci[c] = tot_c + incl - cc[c];
+        pi_[c] = tot_p + pincl - pc[c];
+        tot_c += __shfl(incl, 63, 64);
+        tot_p += __shfl(pincl, 63, 64);
+        dmk[c] = __ballot(dj[c]);
+      }
+      int dbase = 0;
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) {
+        const int r = lane + 64 * c;
+        if (dj[c]) {
+          roff[r] = ci[c];
+          rfill[r] = 0;
+          drow[dbase + __popcll(dmk[c] & ((1ull << lane) - 1ull))] = r;
+          if (tot_p <= kPairMax) {
+            int p = pi_[c];
+#pragma unroll
+            for (int w = 0; w < NPL; ++w)
+              for (uint64_t b = dcol[r * NPL + w]; b; b &= b - 1) {
+                pair_e[p] = uint8_t(r);
+                pair_j[p] = uint8_t(64 * w + __builtin_ctzll(b));
+                ++p;
+              }
+          }
+        }
+        dbase += __popcll(dmk[c]);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < NPL; ++c)
+#pragma unroll
+        for (int w = 0; w < NPL; ++w) dcol[(lane + 64 * c) * NPL + w] = 0ull;
+      if (lane == 0) {
+        s_nd = dbase;
+        s_np = tot_p;
+#pragma unroll
+        for (int c = 0; c < NPL; ++c) s_dm[c] = dmk[c];
+      }
+    }
+    __syncthreads();
+    const int D = s_nd, P = s_np;
+    if (D > 0) {
+      uint64_t dm[NPL];
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) dm[c] = s_dm[c];
+      for (int t = tid; t < m; t += 1024) {
+        const XMask<NPL> ht = hm[t];
+#pragma unroll
+        for (int c = 0; c < NPL; ++c) {
+          uint64_t h = ht.w[c] & dm[c];
+          while (h) {
+            const int e = 64 * c + __builtin_ctzll(h);
+            h &= h - 1;
+            lst[roff[e] + atomicAdd(&rfill[e], 1)] = uint16_t(t);
+          }
+        }
+      }
+      __syncthreads();
+      if (P <= kPairMax) {
+        // one wave per (row, column) pair, lanes over the row's tokens
+        for (int p = wave; p < P; p += 16) {
+          const int e = pair_e[p], j = pair_j[p];
+          const int len = cnt[e], beg = roff[e];
+          double bv = INFINITY;
+          int bt = 0x7FFFFFFF;
+          for (int c0 = 0; c0 < len; c0 += 64 * 8) {
+            int t[8];
+            float se[8], sj[8];
+            bool hj[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) t[u] = lst[beg + min(c0 + 64 * u + lane, len - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              se[u] = s[int64_t(t[u]) * n + e];
+              sj[u] = s[int64_t(t[u]) * n + j];
+              hj[u] = xm_has(hm[t[u]], j);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              if (c0 + 64 * u + lane < len && !hj[u]) {
+                const double v = double(se[u]) - double(sj[u]);
+                if (v < bv || (v == bv && t[u] < bt)) {
+                  bv = v;
+                  bt = t[u];
+                }
+              }
+            }
+          }
+          const double mv = wave_min_f64_all(bv);
+          const int mt = wave_min_i_dpp(bv == mv ? bt : 0x7FFFFFFF);
+          if (lane == 0) {
+            Md[e * NN + j] = mv;
+            arg[e * NN + j] = mt;
+          }
+        }
+        __syncthreads();
+      } else {
+        // whole rows, lanes over the columns; rounds of at most 16 rows, a row's tokens split over wpr waves
+        for (int o = tid; o < D * NN; o += 1024) {
+          const int e = drow[o / NN], j = o % NN;
+          Md[e * NN + j] = INFINITY;
+          arg[e * NN + j] = 0x7FFFFFFF;
+        }
+        for (int r0 = 0; r0 < D; r0 += 16) {
+          const int R = min(16, D - r0);
+          const int wpr = 16 / R;
+          const int ri = wave / wpr, sub = wave - ri * wpr;
+          double bv[NPL];
+          int bt[NPL];
+#pragma unroll
+          for (int c = 0; c < NPL; ++c) {
+            bv[c] = INFINITY;
+            bt[c] = 0x7FFFFFFF;
+          }
+          if (ri < R) {
+            const int e = __builtin_amdgcn_readfirstlane(drow[r0 + ri]);
+            const int len = cnt[e], beg = roff[e];
+            const int lo = beg + len * sub / wpr, hi = beg + len * (sub + 1) / wpr;
+            for (int b = lo; b < hi; b += TB) {
+              int t[TB];
+              float sv[TB][NPL];
+              XMask<NPL> hu[TB];
+#pragma unroll
+              for (int u = 0; u < TB; ++u) t[u] = lst[min(b + u, hi - 1)];
+#pragma unroll
+              for (int u = 0; u < TB; ++u)
+#pragma unroll
+                for (int c = 0; c < NPL; ++c)
+                  sv[u][c] = lane + 64 * c < n ? s[int64_t(t[u]) * n + lane + 64 * c] : 0.f;
+#pragma unroll
+              for (int u = 0; u < TB; ++u) hu[u] = hm[t[u]];
+#pragma unroll
+              for (int u = 0; u < TB; ++u) {
+                if (b + u < hi) {
+                  const float sev = lane_of<NPL>(sv[u], e);
+#pragma unroll
+                  for (int c = 0; c < NPL; ++c) {
+                    if (lane + 64 * c < n && !((hu[u].w[c] >> lane) & 1ull)) {
+                      const double v = double(sev) - double(sv[u][c]);
+                      if (v < bv[c] || (v == bv[c] && t[u] < bt[c])) {
+                        bv[c] = v;
+                        bt[c] = t[u];
+                      }
+                    }
+                  }
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < NPL; ++c) {
+            pk[wave * NN + lane + 64 * c] = bv[c];
+            pt[wave * NN + lane + 64 * c] = bt[c];
+          }
+          __syncthreads();
+          // a row's waves meet: (value, token) minimum over its wpr partials
+          for (int o = tid; o < R * NN; o += 1024) {
+            const int ri2 = o / NN, j = o % NN, e = drow[r0 + ri2];
+            double cv = INFINITY;
+            int ct = 0x7FFFFFFF;
+            for (int w = ri2 * wpr; w < (ri2 + 1) * wpr; ++w) {
+              const double ov = pk[w * NN + j];
+              const int ot = pt[w * NN + j];
+              if (ov < cv || (ov == cv && ot < ct)) {
+                cv = ov;
+                ct = ot;
+              }
+            }
+            Md[e * NN + j] = cv;
+            arg[e * NN + j] = ct;
+          }
+          __syncthreads();
+        }
+      }
+    }
+    // ---- any expert over-full?
+    if (wave == 0) {
+      bool over = false;
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) over |= lane + 64 * c < n && cnt[lane + 64 * c] > q;
+      const uint64_t ov = __ballot(over);
+      if (lane == 0) {
+        s_go = ov != 0 && aug < max_aug;
+        s_fail = 0;
+      }
+    }
+    __syncthreads();
+    if (!s_go) break;
+    // ---- reduced costs max(M(u, j) − π_u + π_j, 0)
+    for (int o = tid; o < NN * NN; o += 1024) {
+      const int u = o / NN, j = o % NN;
+      W[o] = (u < n && j < n) ? fmax(Md[o] - pi[u] + pi[j], 0.0) : INFINITY;
+    }
+    __syncthreads();
+    // ---- Dijkstra from every over-full expert to the first under-full one reached
+    if (wave == 0) {
+      uint64_t under[NPL];
+      double dv[NPL];
+      int pv[NPL];
+      bool done[NPL];
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) {
+        const int r = lane + 64 * c;
+        under[c] = __ballot(r < n && cnt[r] < q);
+        dv[c] = (r < n && cnt[r] > q) ? 0.0 : INFINITY;
+        pv[c] = -1;
+        done[c] = r >= n;
+      }
+      int target = -1;
+      double Dt = 0.0;
+      constexpr uint64_t kInfBits = 0x7FF0000000000000ull;
+      for (int it = 0; it < n; ++it) {
+        // distances are >= 0, so their raw bits order like their values: the minimum as two
+        // 32-bit reductions (high word, then the low word among the lanes holding the high one)
+        uint64_t kb[NPL];
+#pragma unroll
+        for (int c = 0; c < NPL; ++c) kb[c] = done[c] ? kInfBits : uint64_t(__double_as_longlong(dv[c]));
+        uint64_t kl = kb[0];
+#pragma unroll
+        for (int c = 1; c < NPL; ++c) kl = kb[c] < kl ? kb[c] : kl;
+        const uint32_t khi = uint32_t(kl >> 32);
+        const uint32_t mhi = wave_min_u32_all(khi);
+        const uint32_t mlo = wave_min_u32_all(khi == mhi ? uint32_t(kl) : 0xFFFFFFFFu);
+        const uint64_t mkey = (uint64_t(mhi) << 32) | mlo;
+        if (mkey >= kInfBits) break;   // every remaining expert unreachable
+        const double du = __longlong_as_double(int64_t(mkey));
+        // the unfinished expert of least distance, the lower index on ties
+        int u = -1;
+#pragma unroll
+        for (int c = 0; c < NPL; ++c) {
+          const uint64_t b = __ballot(kb[c] == mkey);
+          if (u < 0 && b) u = 64 * c + int(__builtin_ctzll(b));
+        }
+        u = __builtin_amdgcn_readfirstlane(u);
+#pragma unroll
+        for (int c = 0; c < NPL; ++c)
+          if (lane + 64 * c == u) done[c] = true;
+        if ((under[NPL == 1 ? 0 : (u >> 6)] >> (u & 63)) & 1ull) {
+          target = u;
+          Dt = du;
+          break;
+        }
+#pragma unroll
+        for (int c = 0; c < NPL; ++c) {
+          if (!done[c]) {
+            const double nd = du + W[u * NN + lane + 64 * c];
+            if (nd < dv[c]) {
+              dv[c] = nd;
+              pv[c] = u;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) {
+        const int r = lane + 64 * c;
+        if (r < n) {
+          dist[r] = dv[c];
+          pred[r] = pv[c];
+          vis[r] = done[c];
+        }
+      }
+      if (lane == 0) {
+        s_target = target;
+        s_D = Dt;
+        s_fail = target < 0;
+      }
+    }
+    __syncthreads();
+    if (s_fail) break;
+    if (tid < n) {
+      const double Dt = s_D;
+      pi[tid] -= vis[tid] ? fmin(dist[tid], Dt) : Dt;
+    }
+    if (wave == 0) {
+      // the path's edges (target back to source) and the token each one's cost came from
+      if (lane == 0) {
+        int j = s_target, len = 0;
+        while (pred[j] >= 0) {
+          const int aa = pred[j];
+          path_a[len] = aa;
+          path_j[len] = j;
+          path_t[len] = arg[aa * NN + j];
+          ++len;
+          j = aa;
+        }
+        s_len = len;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int len = __builtin_amdgcn_readfirstlane(s_len);
+      for (int p0 = 0; p0 < len; p0 += 8) {
+        float rowv[8][NPL];   // the score rows of the next 8 edges' tokens, read together
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int c = 0; c < NPL; ++c)
+            rowv[u][c] = (p0 + u < len && lane + 64 * c < n)
+                             ? s[int64_t(path_t[min(p0 + u, len - 1)]) * n + lane + 64 * c]
+                             : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (p0 + u < len) {
+            const int pe = p0 + u;
+            const int aa = __builtin_amdgcn_readfirstlane(path_a[pe]), j = __builtin_amdgcn_readfirstlane(path_j[pe]);
+            const int i = __builtin_amdgcn_readfirstlane(path_t[pe]);
+            XMask<NPL> after = hm[i];
+            xm_flip(after, aa);
+            xm_flip(after, j);
+            const float sij = lane_of<NPL>(rowv[u], j), sia = lane_of<NPL>(rowv[u], aa);
+            // row aa loses the token: the columns it was cheapest for
+            uint64_t lost[NPL];
+#pragma unroll
+            for (int c = 0; c < NPL; ++c) lost[c] = __ballot(lane + 64 * c < n && arg[aa * NN + lane + 64 * c] == i);
+#pragma unroll
+            for (int c = 0; c < NPL; ++c) {
+              const int e = lane + 64 * c;
+              if (e < n) {
+                const float sie = rowv[u][c];
+                if (!xm_has(after, e)) {
+                  // row j gains candidate i for every expert the token will not hold
+                  const double v = double(sij) - double(sie);
+                  const int o = j * NN + e;
+                  if (v < Md[o] || (v == Md[o] && i < arg[o])) {
+                    Md[o] = v;
+                    arg[o] = i;
+                  }
+                } else if (e != j) {
+                  // an expert e the token keeps: (e -> aa) gains it, (e -> j) loses it
+                  const double v = double(sie) - double(sia);
+                  const int o = e * NN + aa;
+                  if (v < Md[o] || (v == Md[o] && i < arg[o])) {
+                    Md[o] = v;
+                    arg[o] = i;
+                  }
+                  if (arg[e * NN + j] == i) dcol[e * NPL + (NPL == 1 ? 0 : (j >> 6))] |= 1ull << (j & 63);
+                }
+              }
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (lane == 0) {
+#pragma unroll
+              for (int c = 0; c < NPL; ++c) dcol[aa * NPL + c] |= lost[c];
+              hm[i] = after;
+              cnt[aa] -= 1;
+              cnt[j] += 1;
+            }
+            __builtin_amdgcn_wave_barrier();
+          }
+        }
+      }
+    }
+    __syncthreads();
+    ++aug;
+  }
+  __syncthreads();
+  for (int t = tid; t < m; t += 1024) {
+    const XMask<NPL> ht = hm[t];
+    int r = 0;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c)
+      for (uint64_t h = ht.w[c]; h && r < k; h &= h - 1) xi[int64_t(t) * k + r++] = 64 * c + __builtin_ctzll(h);
+  }
+  if (tid < n) {
+    a.counts[tid] = cnt[tid];
+    a.beta[tid] = float(pi[tid]);
+    pi_out[tid] = pi[tid];
+  }
+  if (wave == 0) {
+    bool offq = false;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) offq |= lane + 64 * c < n && cnt[lane + 64 * c] != q;
+    const uint64_t off = __ballot(offq);
+    if (lane == 0 && a.info) {
+      a.info[1] = aug;
+      a.info[2] = off == 0 && !s_fail;
       a.info[3] = s_fail;
     }
   }
@@ -1212,6 +1873,14 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
   int32_t* pos = reinterpret_cast<int32_t*>(ws);
   ws += al256(size_t(a.m) * a.k * sizeof(int32_t));
   int32_t* lst = reinterpret_cast<int32_t*>(ws);
+  ws += al256(size_t(a.n) * a.m * sizeof(int32_t));
+  double* pi_fin = reinterpret_cast<double*>(ws);
+  ws += al256(size_t(a.n) * sizeof(double));
+  double* gM = reinterpret_cast<double*>(ws);   // M, its tokens and the reduced costs for 64 < n <= 128
+  ws += al256(size_t(kFastMaxN) * kFastMaxN * sizeof(double));
+  int* gArg = reinterpret_cast<int*>(ws);
+  ws += al256(size_t(kFastMaxN) * kFastMaxN * sizeof(int));
+  double* gW = reinterpret_cast<double*>(ws);
   float* alpha = a.alpha_out ? a.alpha_out : alpha_int;
 
   if (a.info) hipLaunchKernelGGL(k_qb_info, dim3(1), dim3(64), 0, s, a.info, a.iters);
@@ -1230,7 +1899,17 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
     rows(false, true);
     cols();
   }
-  if (a.exact)
+  if (a.exact && fast_complete_ok(a.m, a.n, a.k)) {
+    const unsigned tok_blocks = unsigned(ceil_div64(a.m, 4));
+    hipLaunchKernelGGL(k_qbc_init, dim3(tok_blocks), dim3(256), 0, s, a, xi);
+    if (fast_npl(a.n) == 1)
+      hipLaunchKernelGGL(k_qbc_solve<1>, dim3(1), dim3(1024), fast_lds_bytes(1, a.m, a.k), s, a, xi, pi_fin, gM, gArg,
+                         gW);
+    else
+      hipLaunchKernelGGL(k_qbc_solve<2>, dim3(1), dim3(1024), fast_lds_bytes(2, a.m, a.k), s, a, xi, pi_fin, gM, gArg,
+                         gW);
+    hipLaunchKernelGGL(k_qbc_out, dim3(tok_blocks), dim3(256), 0, s, a, xi, pi_fin);
+  } else if (a.exact)
     hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi, pos, lst);
   else
     rows(true, false);

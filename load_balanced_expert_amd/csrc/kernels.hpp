@@ -138,6 +138,8 @@ hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, c
 
 // ---------------------------------------------------------------- balanced assignment
 size_t balance_ws_bytes(int64_t m, int n, int k, bool exact);
+// whether the exact completion handles these sizes (n <= 64, or n <= 128 within its LDS budget)
+bool exact_completion_supported(int64_t m, int n, int k);
 struct BalanceArgs {
   int64_t m;
   int n, k;

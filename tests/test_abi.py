@@ -163,7 +163,8 @@ def test_balance_validation(lib):
     assert lib.moe_balance_duals(*args(8, 4, 1, mode=2)) == 1
     assert lib.moe_balance_duals(*args(8, 4, 1, it=2, mode=1)) == 1   # online takes one step
     assert lib.moe_balance_duals(*args(8, 4, 1, mode=1, ex=1)) == 1   # exact is solve-only
-    assert lib.moe_balance_duals(*args(128, 128, 1, ex=1)) == 2      # completion limited to n <= 64
+    assert lib.moe_balance_duals(*args(256, 256, 1, ex=1)) == 2      # completion limited to n <= 128
+    assert lib.moe_balance_duals(*args(1 << 16, 128, 2, ex=1)) == 2  # n > 64: the assignment must fit in LDS
     assert lib.moe_balance_duals(*args(64, 8, 1, wsb=100)) == 3
     assert lib.moe_balance_workspace_size(64, 8, 8, 0) == 0
     assert lib.moe_balance_workspace_size(4096, 64, 4, 1) > lib.moe_balance_workspace_size(4096, 64, 4, 0)

@@ -194,7 +194,10 @@ def test_qb_online_routes_before_update():
     assert np.array_equal(to_host(out.alpha), alpha_r)
 
 
-@pytest.mark.parametrize("iters,m,n,k", [(20, 4096, 64, 4), (5, 4096, 64, 4), (0, 512, 16, 2), (3, 12, 4, 2)])
+# (5, 8192, 64, 4) exceeds the LDS-resident form and takes the global-list kernel; n > 64 takes
+# two experts per lane (96: a partial second half)
+@pytest.mark.parametrize("iters,m,n,k", [(20, 4096, 64, 4), (5, 4096, 64, 4), (0, 512, 16, 2), (3, 12, 4, 2),
+                                         (5, 8192, 64, 4), (5, 2048, 128, 4), (3, 1536, 96, 2), (2, 2048, 128, 8)])
 def test_exact_completion_is_lp_optimum(iters, m, n, k):
     spec = W.BalancedSpec(m=m, n=n, k=k)
     s = W.balanced_scores(spec, 0)
