@@ -17,9 +17,10 @@
 //    bits), the last two digits over the keys of the chosen bin held in LDS.
 //  * exact completion: one persistent workgroup runs successive shortest
 //    paths on the expert graph in fp64 (the move cost a -> j is the cheapest
-//    s_ia − s_ij over tokens holding a but not j, kept in LDS; Dijkstra runs
-//    on one wave with one expert per lane) until every expert has q tokens.
-//    Requires n <= 64.
+//    s_ia − s_ij over tokens holding a but not j; Dijkstra runs on one wave)
+//    until every expert has q tokens.  The LDS-resident form (n <= 128, the
+//    assignment within LDS) is below; k_qb_complete keeps its token lists in
+//    global memory for larger assignments (n <= 64).
 #include "common.hpp"
 #include "dpp.hpp"
 #include "kernels.hpp"
@@ -1106,17 +1107,22 @@ __global__ __launch_bounds__(1024) void k_qb_complete(BalanceArgs a, int32_t* __
 }
 
 // ------------------------------------------------------------------ exact completion, LDS-resident form
-// The same successive shortest paths for n <= 64 when the assignment fits in LDS (a 64-bit mask of
-// held experts per token, plus a 16-bit list entry per (token, slot)):
+// The same successive shortest paths for n <= 128 when the assignment fits in LDS (per token a
+// mask of the experts it holds, per expert a 16-bit token list):
 //  * k_qbc_init (one wave per token, many workgroups): x = top-k of the exact keys s_ij − β_j;
-//  * k_qbc_solve (one workgroup): x and M (fp64 values and tokens) in LDS.  A token that leaves
+//  * k_qbc_minit (one workgroup per expert): the initial M;
+//  * k_qbc_solve (one workgroup): x, the lists and, for n <= 64, M (fp64 values and tokens) in
+//    LDS (for n <= 128 M lives in global memory, two experts per lane).  A token that leaves
 //    expert a stales only the entries of row a (and of its other experts' rows, column j) whose
 //    cheapest token it was; each round recomputes those (row, column) pairs, one wave per pair
-//    with the lanes over the row's tokens (listed from the masks), or whole rows (lanes over the
-//    columns, the row's tokens split over waves that meet in LDS) when many are stale, as at the
-//    start.  Dijkstra on one wave reads precomputed reduced costs and takes the arg-min lane
-//    from a ballot of the fp64 minimum.  The tokens of the path's edges
-//    are read before any of them moves, so every edge moves the token its cost was taken from;
+//    with the lanes over the row's tokens, or whole rows (lanes over the columns, the row's
+//    tokens split over waves that meet in LDS) when many are stale.  The lists are kept across
+//    rounds when every expert's list fits its largest size (an over-full expert only shrinks, an
+//    under-full one grows to q), else the stale rows are listed anew each round.  Dijkstra on one
+//    wave reads precomputed reduced costs; its minimum is two 32-bit DPP reductions (the
+//    distances are >= 0, so their raw bits order like their values) and the arg-min lane a
+//    ballot.  The tokens of the path's edges are read before any of them moves, so every edge
+//    moves the token its cost was taken from;
 //  * k_qbc_out (one wave per token): idx by descending s_ij − π_j.
 // Candidates compare as fp64 values with the lower token index on ties.
 constexpr int kFastMaxN = 128;
@@ -1249,6 +1255,18 @@ __device__ __forceinline__ uint32_t wave_min_u32_all(uint32_t v) {
   return min(uint32_t(r[0]), uint32_t(r[1]));
 }
 
+// u32 minimum of the wave in lane 63's result (scalar): DPP within 16-lane rows, then the GFX9
+// row broadcasts (row 0's lane 15 into row 1, row 2's into row 3; then lane 31 into rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_min_u32_bcast(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x142, 0xA, 0xF, false)));   // row_bcast:15
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x143, 0xC, 0xF, false)));   // row_bcast:31
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+
 constexpr int kPairMax = 64;   // stale (row, column) pairs recomputed one by one; more: whole rows
 
 // Experts held by one token: NPL 64-bit words (experts 64 c + bit of word c).
@@ -1280,12 +1298,90 @@ __device__ __forceinline__ float lane_of(const float (&v)[NPL], int j) {
                   : __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[1]), j - 64));
 }
 
+// The initial M, one workgroup per row e (4 waves): the tokens holding e listed in LDS from x, the
+// lanes over the columns j, each wave over a quarter of the tokens, the waves meeting in LDS.
+// M[e][j] = min over tokens t holding e and not j of s_te − s_tj (lower token on ties).
+template <int NPL>
+__global__ __launch_bounds__(256) void k_qbc_minit(BalanceArgs a, const int32_t* __restrict__ xi,
+                                                   double* __restrict__ gM, int* __restrict__ gArg) {
+  constexpr int NN = 64 * NPL;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  double* pk = reinterpret_cast<double*>(lds_raw);   // [4][NN]
+  int* pt = reinterpret_cast<int*>(pk + 4 * NN);      // [4][NN]
+  int* toks = pt + 4 * NN;                            // [m] tokens holding e
+  __shared__ int s_len;
+  const int n = a.n, k = a.k, m = int(a.m), e = blockIdx.x;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  if (tid == 0) s_len = 0;
+  __syncthreads();
+  for (int o = tid; o < m * k; o += 256)
+    if (xi[o] == e) toks[atomicAdd(&s_len, 1)] = o / k;
+  __syncthreads();
+  const int len = s_len, lo = len * wave / 4, hi = len * (wave + 1) / 4;
+  double bv[NPL];
+  int bt[NPL];
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    bv[c] = INFINITY;
+    bt[c] = 0x7FFFFFFF;
+  }
+  for (int b = lo; b < hi; b += 8) {
+    int t[8];
+    float sv[8][NPL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = toks[min(b + u, hi - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) sv[u][c] = lane + 64 * c < n ? a.s[int64_t(t[u]) * n + lane + 64 * c] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (b + u < hi) {
+        const float se = lane_of<NPL>(sv[u], e);
+#pragma unroll
+        for (int c = 0; c < NPL; ++c) {
+          const int j = lane + 64 * c;
+          bool held = false;
+          for (int r = 0; r < k; ++r) held |= xi[int64_t(t[u]) * k + r] == j;
+          if (j < n && !held) {
+            const double v = double(se) - double(sv[u][c]);
+            if (v < bv[c] || (v == bv[c] && t[u] < bt[c])) {
+              bv[c] = v;
+              bt[c] = t[u];
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    pk[wave * NN + lane + 64 * c] = bv[c];
+    pt[wave * NN + lane + 64 * c] = bt[c];
+  }
+  __syncthreads();
+  if (tid < NN) {
+    double cv = INFINITY;
+    int ct = 0x7FFFFFFF;
+    for (int w = 0; w < 4; ++w) {
+      const double ov = pk[w * NN + tid];
+      const int ot = pt[w * NN + tid];
+      if (ov < cv || (ov == cv && ot < ct)) {
+        cv = ov;
+        ct = ot;
+      }
+    }
+    gM[e * NN + tid] = cv;
+    gArg[e * NN + tid] = ct;
+  }
+}
+
 // NPL experts per lane (n <= 64 NPL).  NPL = 1: M, its tokens and the reduced costs in LDS;
 // NPL = 2: in global memory (gM, gArg, gW), the rest in LDS.
 template <int NPL>
 __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __restrict__ xi,
                                                     double* __restrict__ pi_out, double* __restrict__ gM,
-                                                    int* __restrict__ gArg, double* __restrict__ gW) {
+                                                    int* __restrict__ gArg, double* __restrict__ gW, int list_cap) {
   constexpr int NN = 64 * NPL;
   constexpr int TB = 16 / NPL;   // tokens per batch in the whole-row refresh
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
@@ -1312,14 +1408,17 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
   }
   const int n = a.n, k = a.k, m = int(a.m), q = int(a.q);
   XMask<NPL>* hm = reinterpret_cast<XMask<NPL>*>(rest);    // [m] experts held by each token
-  uint16_t* lst = reinterpret_cast<uint16_t*>(hm + m);      // listed tokens of the rows being refreshed
+  // token lists: per expert, kept across rounds when every list fits its largest size (an
+  // over-full expert only shrinks, an under-full one grows to q); else the rows being refreshed,
+  // listed anew each round
+  uint16_t* lst = reinterpret_cast<uint16_t*>(hm + m);
   __shared__ double pi[NN], dist[NN];
   __shared__ uint64_t dcol[NN * NPL];   // per row of M: the columns whose cheapest token may have left
   __shared__ int cnt[NN], pred[NN], vis[NN], roff[NN], rfill[NN], drow[NN];
   __shared__ int path_a[NN], path_j[NN], path_t[NN];
   __shared__ uint8_t pair_e[kPairMax], pair_j[kPairMax];
   __shared__ uint64_t s_dm[NPL];
-  __shared__ int s_nd, s_np, s_go, s_target, s_fail, s_len;
+  __shared__ int s_nd, s_np, s_go, s_target, s_fail, s_len, s_keep;
   __shared__ double s_D;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const float* __restrict__ s = a.s;
@@ -1328,8 +1427,13 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
     pi[tid] = tid < n ? double(a.beta[tid]) : 0.0;
     cnt[tid] = 0;
 #pragma unroll
-    for (int c = 0; c < NPL; ++c) dcol[tid * NPL + c] = tid < n ? col_bits(c, n) : 0ull;
+    for (int c = 0; c < NPL; ++c) dcol[tid * NPL + c] = 0ull;   // M starts exact (k_qbc_minit)
   }
+  if constexpr (NPL == 1)
+    for (int o = tid; o < NN * NN; o += 1024) {
+      Md[o] = gM[o];
+      arg[o] = gArg[o];
+    }
   __syncthreads();
   for (int t = tid; t < m; t += 1024) {
     XMask<NPL> h{};
@@ -1341,9 +1445,52 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
     hm[t] = h;
   }
   __syncthreads();
+  // persistent lists when Σ_e max(c_e, q) fits
+  if (wave == 0) {
+    int cap[NPL], incl[NPL], tot = 0;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) {
+      const int r = lane + 64 * c;
+      cap[c] = r < n ? max(cnt[r], q) : 0;
+      incl[c] = cap[c];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl[c], off, 64);
+        if (lane >= off) incl[c] += o;
+      }
+      roff[r] = tot + incl[c] - cap[c];
+      rfill[r] = 0;
+      tot += __shfl(incl[c], 63, 64);
+    }
+    if (lane == 0) s_keep = tot <= list_cap;
+  }
+  __syncthreads();
+  const bool keep = s_keep;
+  if (keep) {
+    for (int t = tid; t < m; t += 1024) {
+      const XMask<NPL> ht = hm[t];
+#pragma unroll
+      for (int c = 0; c < NPL; ++c)
+        for (uint64_t h = ht.w[c]; h; h &= h - 1) {
+          const int e = 64 * c + __builtin_ctzll(h);
+          lst[roff[e] + atomicAdd(&rfill[e], 1)] = uint16_t(t);
+        }
+    }
+  }
   int aug = 0;
   const int max_aug = m * k;
+  auto over_full = [&]() {   // wave 0: any expert over-full (and augmentations left)?
+    bool over = false;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) over |= lane + 64 * c < n && cnt[lane + 64 * c] > q;
+    const uint64_t ov = __ballot(over);
+    if (lane == 0) s_go = ov != 0 && aug < max_aug;
+  };
+  if (wave == 0) over_full();
+  if (wave == 0 && lane == 0) s_fail = 0;
+  __syncthreads();
   for (;;) {
+    if (!s_go) break;
     // ---- refresh the entries of M whose cheapest token may have left
     if (wave == 0) {
       // rows lane + 64 c, in the order c, then lane
@@ -1385,8 +1532,10 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
       for (int c = 0; c < NPL; ++c) {
         const int r = lane + 64 * c;
         if (dj[c]) {
-          roff[r] = ci[c];
-          rfill[r] = 0;
+          if (!keep) {
+            roff[r] = ci[c];
+            rfill[r] = 0;
+          }
           drow[dbase + __popcll(dmk[c] & ((1ull << lane) - 1ull))] = r;
           if (tot_p <= kPairMax) {
             int p = pi_[c];
@@ -1419,7 +1568,7 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
       uint64_t dm[NPL];
 #pragma unroll
       for (int c = 0; c < NPL; ++c) dm[c] = s_dm[c];
-      for (int t = tid; t < m; t += 1024) {
+      for (int t = keep ? m : tid; t < m; t += 1024) {
         const XMask<NPL> ht = hm[t];
 #pragma unroll
         for (int c = 0; c < NPL; ++c) {
@@ -1549,19 +1698,6 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
         }
       }
     }
-    // ---- any expert over-full?
-    if (wave == 0) {
-      bool over = false;
-#pragma unroll
-      for (int c = 0; c < NPL; ++c) over |= lane + 64 * c < n && cnt[lane + 64 * c] > q;
-      const uint64_t ov = __ballot(over);
-      if (lane == 0) {
-        s_go = ov != 0 && aug < max_aug;
-        s_fail = 0;
-      }
-    }
-    __syncthreads();
-    if (!s_go) break;
     // ---- reduced costs max(M(u, j) − π_u + π_j, 0)
     for (int o = tid; o < NN * NN; o += 1024) {
       const int u = o / NN, j = o % NN;
@@ -1595,8 +1731,8 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
 #pragma unroll
         for (int c = 1; c < NPL; ++c) kl = kb[c] < kl ? kb[c] : kl;
         const uint32_t khi = uint32_t(kl >> 32);
-        const uint32_t mhi = wave_min_u32_all(khi);
-        const uint32_t mlo = wave_min_u32_all(khi == mhi ? uint32_t(kl) : 0xFFFFFFFFu);
+        const uint32_t mhi = wave_min_u32_bcast(khi);
+        const uint32_t mlo = wave_min_u32_bcast(khi == mhi ? uint32_t(kl) : 0xFFFFFFFFu);
         const uint64_t mkey = (uint64_t(mhi) << 32) | mlo;
         if (mkey >= kInfBits) break;   // every remaining expert unreachable
         const double du = __longlong_as_double(int64_t(mkey));
@@ -1608,6 +1744,9 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
           if (u < 0 && b) u = 64 * c + int(__builtin_ctzll(b));
         }
         u = __builtin_amdgcn_readfirstlane(u);
+        double wrow[NPL];   // u's reduced costs, read before the target test
+#pragma unroll
+        for (int c = 0; c < NPL; ++c) wrow[c] = W[u * NN + lane + 64 * c];
 #pragma unroll
         for (int c = 0; c < NPL; ++c)
           if (lane + 64 * c == u) done[c] = true;
@@ -1619,7 +1758,7 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
 #pragma unroll
         for (int c = 0; c < NPL; ++c) {
           if (!done[c]) {
-            const double nd = du + W[u * NN + lane + 64 * c];
+            const double nd = du + wrow[c];
             if (nd < dv[c]) {
               dv[c] = nd;
               pv[c] = u;
@@ -1713,6 +1852,20 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
               }
             }
             __builtin_amdgcn_wave_barrier();
+            if (keep) {
+              // the token leaves aa's list (the last entry fills its place) and joins j's
+              const int ca = cnt[aa], ba = roff[aa];
+              int where = -1;
+              for (int c0 = 0; c0 < ca && where < 0; c0 += 64) {
+                const uint64_t hit = __ballot(c0 + lane < ca && lst[ba + c0 + lane] == i);
+                if (hit) where = c0 + int(__builtin_ctzll(hit));
+              }
+              if (lane == 0) {
+                lst[ba + where] = lst[ba + ca - 1];
+                lst[roff[j] + cnt[j]] = uint16_t(i);
+              }
+            }
+            __builtin_amdgcn_wave_barrier();
             if (lane == 0) {
 #pragma unroll
               for (int c = 0; c < NPL; ++c) dcol[aa * NPL + c] |= lost[c];
@@ -1724,9 +1877,12 @@ __global__ __launch_bounds__(1024) void k_qbc_solve(BalanceArgs a, int32_t* __re
           }
         }
       }
+      ++aug;
+      over_full();
+    } else {
+      ++aug;
     }
     __syncthreads();
-    ++aug;
   }
   __syncthreads();
   for (int t = tid; t < m; t += 1024) {
@@ -1902,12 +2058,19 @@ hipError_t launch_balance(const BalanceArgs& a_in, hipStream_t s) {
   if (a.exact && fast_complete_ok(a.m, a.n, a.k)) {
     const unsigned tok_blocks = unsigned(ceil_div64(a.m, 4));
     hipLaunchKernelGGL(k_qbc_init, dim3(tok_blocks), dim3(256), 0, s, a, xi);
+    const size_t minit_lds = size_t(8) * 128 * 12 + size_t(a.m) * sizeof(int);
     if (fast_npl(a.n) == 1)
-      hipLaunchKernelGGL(k_qbc_solve<1>, dim3(1), dim3(1024), fast_lds_bytes(1, a.m, a.k), s, a, xi, pi_fin, gM, gArg,
-                         gW);
+      hipLaunchKernelGGL(k_qbc_minit<1>, dim3(a.n), dim3(256), minit_lds, s, a, xi, gM, gArg);
     else
-      hipLaunchKernelGGL(k_qbc_solve<2>, dim3(1), dim3(1024), fast_lds_bytes(2, a.m, a.k), s, a, xi, pi_fin, gM, gArg,
-                         gW);
+      hipLaunchKernelGGL(k_qbc_minit<2>, dim3(a.n), dim3(256), minit_lds, s, a, xi, gM, gArg);
+    // the token lists take all the LDS left (at least m·k entries)
+    const int npl = fast_npl(a.n);
+    const size_t fixed = fast_lds_bytes(npl, a.m, a.k) - size_t(round_up(int(a.m * a.k) * 2, 16));
+    const int list_cap = int((size_t(kFastLdsLimit) - fixed) / 2) & ~7;
+    if (npl == 1)
+      hipLaunchKernelGGL(k_qbc_solve<1>, dim3(1), dim3(1024), kFastLdsLimit, s, a, xi, pi_fin, gM, gArg, gW, list_cap);
+    else
+      hipLaunchKernelGGL(k_qbc_solve<2>, dim3(1), dim3(1024), kFastLdsLimit, s, a, xi, pi_fin, gM, gArg, gW, list_cap);
     hipLaunchKernelGGL(k_qbc_out, dim3(tok_blocks), dim3(256), 0, s, a, xi, pi_fin);
   } else if (a.exact)
     hipLaunchKernelGGL(k_qb_complete, dim3(1), dim3(1024), 0, s, a, xi, pos, lst);
