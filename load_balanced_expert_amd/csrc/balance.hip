@@ -1314,8 +1314,15 @@ __global__ __launch_bounds__(256) void k_qbc_minit(BalanceArgs a, const int32_t*
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   if (tid == 0) s_len = 0;
   __syncthreads();
-  for (int o = tid; o < m * k; o += 256)
-    if (xi[o] == e) toks[atomicAdd(&s_len, 1)] = o / k;
+  // 16 loads of x in flight per thread, then the matches appended
+  for (int o0 = tid; o0 < m * k; o0 += 256 * 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = o0 + 256 * u < m * k ? xi[o0 + 256 * u] : -1;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (v[u] == e) toks[atomicAdd(&s_len, 1)] = (o0 + 256 * u) / k;
+  }
   __syncthreads();
   const int len = s_len, lo = len * wave / 4, hi = len * (wave + 1) / 4;
   double bv[NPL];
