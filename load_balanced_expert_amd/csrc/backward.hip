@@ -55,8 +55,11 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i, bool f32) {
   return f32 ? static_cast<const float*>(p)[i] : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
 }
 
-// fp32 MFMA form: operands of type TA / TB (0 bf16, 1 fp32) converted to fp32 in LDS, any sizes.
-template <int TA, int TB>
+// fp32 MFMA form: operands of type TA / TB (0 bf16, 1 fp32) converted to fp32 in LDS.  VEC: every
+// operand's contiguous dimension (and K when k is contiguous) a multiple of 8, the tile staged
+// with 16-byte loads (the next K step's issued before the current step's products); else each
+// element is loaded and range-checked alone.
+template <int TA, int TB, bool VEC>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm_f32(GemmArgs a) {
   __shared__ float As[kBwdTile][kBwdK + 1];   // [m][k]
   __shared__ float Bs[kBwdTile][kBwdK + 1];   // [n][k]
@@ -92,33 +95,97 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm_f32(GemmArgs a) {
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int k0 = k_begin; k0 < k_end; k0 += kBwdK) {
-    // stage A [64 m][32 k] and B [64 n][32 k]: 2048 elements each, 8 per thread, every element
-    // range-checked (zeros outside)
+  if constexpr (VEC) {
+    // the thread's 8 elements of one operand tile [64 outer][32 k]: fp32 as two 16-byte vectors,
+    // bf16 as one; along k when k is contiguous, else along the outer dimension
+    auto fetch = [&](const char* base, bool fp32, bool kc, bool is_a, int lim, int o0, int k0, u32x4 (&r)[2],
+                     int& o, int& kk) {
+      const int per = fp32 ? 4 : 8;   // elements per vector
+      r[0] = r[1] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = tid + u * kBwdThreads;
-      // A: k fastest when A is k-contiguous, else m fastest (coalesced either way)
-      int am, ak;
-      if (a.sAk == 1) { am = i >> 5; ak = i & 31; } else { ak = i >> 6; am = i & 63; }
-      const int gm = m0 + am, gk = k0 + ak;
-      float av = 0.f;
-      if (gm < M && gk < k_end) av = ld_elem(Ab, a_idx(gm, gk), TA == 1);
-      int bn, bk;
-      if (a.sBk == 1) { bn = i >> 5; bk = i & 31; } else { bk = i >> 6; bn = i & 63; }
-      const int gn = n0 + bn, gk2 = k0 + bk;
-      float bv = 0.f;
-      if (gn < a.N && gk2 < k_end) bv = ld_elem(Bb, b_idx(gk2, gn), TB == 1);
-      As[am][ak] = av;
-      Bs[bn][bk] = bv;
-    }
-    __syncthreads();
+      for (int u = 0; u < 2; ++u) {
+        if (!fp32 && u == 1) break;
+        const int v = fp32 ? tid + kBwdThreads * u : tid;
+        int oo, kq;
+        if (kc) { oo = v / (32 / per); kq = (v % (32 / per)) * per; } else { kq = v / (64 / per); oo = (v % (64 / per)) * per; }
+        if (u == 0) { o = oo; kk = kq; }
+        const int go = o0 + oo, gk = k0 + kq;
+        if (go < lim && gk < k_end) {
+          const int64_t ix = is_a ? a_idx(go, gk) : b_idx(gk, go);
+          r[u] = *reinterpret_cast<const u32x4*>(base + ix * (fp32 ? 4 : 2));
+        }
+      }
+    };
+    auto put = [&](float (*S)[kBwdK + 1], bool fp32, bool kc, const u32x4 (&r)[2], int o, int kk) {
+      if (fp32) {
 #pragma unroll
-    for (int s = 0; s < kBwdK / 2; ++s) {
-      const float av = As[wm + r32][2 * s + h], bv = Bs[wn + r32][2 * s + h];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          const int v = tid + kBwdThreads * u;
+          int oo, kq;
+          if (kc) { oo = v / 8; kq = (v % 8) * 4; } else { kq = v / 16; oo = (v % 16) * 4; }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float f = __uint_as_float(r[u][j]);
+            if (kc) S[oo][kq + j] = f; else S[oo + j][kq] = f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float f = bf16_to_f32(uint16_t(r[0][j >> 1] >> (16 * (j & 1))));
+          if (kc) S[o][kk + j] = f; else S[o + j][kk] = f;
+        }
+      }
+    };
+    const bool akc = a.sAk == 1, bkc = a.sBk == 1;
+    u32x4 ra[2], rb[2];
+    int ao, ak, bo, bk;
+    fetch(Ab, TA == 1, akc, true, M, m0, k_begin, ra, ao, ak);
+    fetch(Bb, TB == 1, bkc, false, a.N, n0, k_begin, rb, bo, bk);
+    for (int k0 = k_begin; k0 < k_end; k0 += kBwdK) {
+      put(As, TA == 1, akc, ra, ao, ak);
+      put(Bs, TB == 1, bkc, rb, bo, bk);
+      lds_barrier();
+      if (k0 + kBwdK < k_end) {
+        fetch(Ab, TA == 1, akc, true, M, m0, k0 + kBwdK, ra, ao, ak);
+        fetch(Bb, TB == 1, bkc, false, a.N, n0, k0 + kBwdK, rb, bo, bk);
+      }
+#pragma unroll
+      for (int s = 0; s < kBwdK / 2; ++s) {
+        const float av = As[wm + r32][2 * s + h], bv = Bs[wn + r32][2 * s + h];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+      }
+      lds_barrier();
     }
-    __syncthreads();
+  } else {
+    for (int k0 = k_begin; k0 < k_end; k0 += kBwdK) {
+      // stage A [64 m][32 k] and B [64 n][32 k]: 2048 elements each, 8 per thread, every element
+      // range-checked (zeros outside)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = tid + u * kBwdThreads;
+        // A: k fastest when A is k-contiguous, else m fastest (coalesced either way)
+        int am, ak;
+        if (a.sAk == 1) { am = i >> 5; ak = i & 31; } else { ak = i >> 6; am = i & 63; }
+        const int gm = m0 + am, gk = k0 + ak;
+        float av = 0.f;
+        if (gm < M && gk < k_end) av = ld_elem(Ab, a_idx(gm, gk), TA == 1);
+        int bn, bk;
+        if (a.sBk == 1) { bn = i >> 5; bk = i & 31; } else { bk = i >> 6; bn = i & 63; }
+        const int gn = n0 + bn, gk2 = k0 + bk;
+        float bv = 0.f;
+        if (gn < a.N && gk2 < k_end) bv = ld_elem(Bb, b_idx(gk2, gn), TB == 1);
+        As[am][ak] = av;
+        Bs[bn][bk] = bv;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < kBwdK / 2; ++s) {
+        const float av = As[wm + r32][2 * s + h], bv = Bs[wn + r32][2 * s + h];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+      }
+      __syncthreads();
+    }
   }
   // store: element i of the accumulator is row 8 (i / 4) + 4 h + i % 4, column r32 of the 32 x 32 tile
   const int64_t cg = int64_t(g) * a.gC;
@@ -229,6 +296,260 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_gemm_bf16(GemmArgs a) {
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ data gradients: weight stream
+// dA = (dY · W2_e) ⊙ [H > 0] and dD = dA · W1_e read the weights as stored, [K][N] with N
+// contiguous (W2 [d][d_ff], W1 [d_ff][d]).  As in the forward FFN, one workgroup (W waves) owns an
+// expert and 32 W output columns and reads that weight slab once per 128 rows: the expert's rows
+// are staged through LDS in K chunks of 128 (register prefetch of the next chunk), each wave
+// streams its 64 x 32 weight block per K step of 64 (four 16-byte loads per lane, kNnRing - 1
+// steps ahead) into its own LDS slab in the stored [k][n] layout, and takes its MFMA B fragments
+// with the gfx950 LDS transpose read ds_read_b64_tr_b16: in each 16-lane group, lane L names row
+// L / 4 and columns 4 (L % 4) .. + 3 of a 4 x 16 block, and lane i receives column i's 4 values.
+// Requires K % 256 == 0 and N % (32 W) == 0.
+constexpr int kNnKA = 128;           // K per staged A chunk
+constexpr int kNnLdA = kNnKA + 8;    // LDS row stride of the A chunk (bf16)
+constexpr int kNnLdB = 40;           // per-wave slab row stride (bf16): 32 columns + 16 bytes
+constexpr int kNnRing = 4;           // weight K steps in flight + 1 (even)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
+}
+
+// BF16OUT: bf16 output times [H > 0] (omask = H, indexed as the output), else fp32 output
+template <int W, int MT, bool BF16OUT>
+__device__ __forceinline__ void nn_rows(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                        void* __restrict__ C, const uint16_t* __restrict__ omask, uint16_t* As,
+                                        uint16_t* Bs, int r0, int r_end, int K, int N, int col0, int tid) {
+  const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
+  const int nks = K / 64, nch = K / kNnKA;
+  constexpr int AL = 8 * MT / W;       // A chunk: 32 MT rows x 16 segments of 16 bytes over the workgroup
+  const int row0 = tid >> 4, seg = tid & 15;
+  constexpr int kRowStep = 64 * W / 16;
+  const int lo0 = row0 * kNnLdA + seg * 8;
+  u32x4 areg[AL];
+  auto a_fetch = [&](int c) {
+    c = min(c, nch - 1);
+#pragma unroll
+    for (int u = 0; u < AL; ++u) {
+      const uint32_t off = uint32_t(min(r0 + row0 + kRowStep * u, r_end - 1)) * uint32_t(K) + c * kNnKA + seg * 8;
+      areg[u] = *reinterpret_cast<const u32x4*>(A + off);
+    }
+  };
+  auto a_store = [&]() {
+#pragma unroll
+    for (int u = 0; u < AL; ++u)
+      *reinterpret_cast<u32x4*>(As + lo0 + u * kRowStep * kNnLdA) = areg[u];
+  };
+  // weight K step s: load q brings row 16 q + lane / 4 of the step's 64, columns 8 (lane % 4) .. + 7
+  const uint16_t* bp = B + size_t(lane >> 2) * N + col0 + 8 * (lane & 3);
+  auto b_fetch = [&](u32x4 (&b)[4], int s) {
+    s = min(s, nks - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = *reinterpret_cast<const u32x4*>(bp + size_t(64 * s + 16 * q) * N);
+  };
+  uint16_t* bw = Bs + (tid >> 6) * (64 * kNnLdB);
+  auto b_stage = [&](const u32x4 (&b)[4]) {   // same-wave LDS accesses stay in order
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(bw + (16 * q + (lane >> 2)) * kNnLdB + 8 * (lane & 3)) = b[q];
+  };
+  // B fragment of substep q: k = 32 h + 8 q + [0, 8) of column r32, two transposed 4 x 16 reads;
+  // 16-lane group g covers columns 16 (g % 2) + [0, 16) and the k rows of h = g / 2
+  const int g = lane >> 4, L = lane & 15;
+  const uint16_t* bt0 = bw + (32 * (g >> 1) + (L >> 2)) * kNnLdB + 16 * (g & 1) + 4 * (L & 3);
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+  const uint16_t* arow = As + r32 * kNnLdA + 32 * h;
+  auto step = [&](const u32x4 (&b)[4], int t) {
+    b_stage(b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const s16x4 lo = lds_read_tr16(bt0 + (8 * q) * kNnLdB);
+      const s16x4 hi = lds_read_tr16(bt0 + (8 * q + 4) * kNnLdB);
+      const bf16x8 bf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * mt * kNnLdA + 64 * t + 8 * q);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf, acc[mt], 0, 0, 0);
+      }
+    }
+  };
+  u32x4 ring[kNnRing][4];
+  a_fetch(0);
+  a_store();
+  a_fetch(1);
+#pragma unroll
+  for (int u = 0; u < kNnRing - 1; ++u) b_fetch(ring[u], u);
+  lds_barrier();
+  for (int s0 = 0; s0 < nks; s0 += kNnRing) {
+#pragma unroll
+    for (int u = 0; u < kNnRing; ++u) {
+      if (s0 + u < nks) {
+        b_fetch(ring[(u + kNnRing - 1) % kNnRing], s0 + u + kNnRing - 1);
+        step(ring[u], u & 1);
+        if (u & 1) {   // chunk (s0 + u) / 2 consumed: stage the next one, prefetch the one after
+          lds_barrier();
+          a_store();
+          a_fetch((s0 + u) / 2 + 2);
+          lds_barrier();
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    // the tile's 16 mask values read together, then its 16 outputs
+    uint16_t hv[16];
+    if constexpr (BF16OUT) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = min(r0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3), r_end - 1);
+        hv[i] = omask[size_t(row) * N + col0 + r32];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = r0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (row < r_end) {
+        const size_t o = size_t(row) * N + col0 + r32;
+        if constexpr (BF16OUT) {
+          static_cast<uint16_t*>(C)[o] = f32_to_bf16(int16_t(hv[i]) > 0 ? acc[mt][i] : 0.f);
+        } else {
+          static_cast<float*>(C)[o] = acc[mt][i];
+        }
+      }
+    }
+  }
+}
+
+template <int W, bool BF16OUT>
+__global__ __launch_bounds__(64 * W) void k_bwd_nn_stream(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                          void* __restrict__ C, const uint16_t* __restrict__ omask,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ rows, int n, int K, int N) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[128 * kNnLdA];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[W * 64 * kNnLdB];
+  const int ncb = N / (32 * W);
+  const unsigned G = unsigned(n) * ncb, b = blockIdx.x;
+  // XCD-major order: workgroup b runs on XCD b % 8; give each XCD a contiguous range of (expert, block)
+  const unsigned Lx = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int e = int(Lx / ncb), cb = int(Lx % ncb);
+  const int r_begin = offsets[e], r_end = rows ? offsets[e] + rows[e] : offsets[e + 1];
+  const int col0 = cb * (32 * W) + (threadIdx.x >> 6) * 32;
+  const uint16_t* Be = B + size_t(e) * K * N;
+  for (int r0 = r_begin; r0 < r_end; r0 += 128) {
+    switch (ceil_div(min(128, r_end - r0), 32)) {
+      case 1: nn_rows<W, 1, BF16OUT>(A, Be, C, omask, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 2: nn_rows<W, 2, BF16OUT>(A, Be, C, omask, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 3: nn_rows<W, 3, BF16OUT>(A, Be, C, omask, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      default: nn_rows<W, 4, BF16OUT>(A, Be, C, omask, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ weight gradients
+// C_e[M][N] (fp32) = Σ_r A[r][m] · B[r][n] over the rows r of expert e: dW2_e = dYᵀ·H (A = dY
+// [rows][d], B = H [rows][d_ff]) and dW1_e = dAᵀ·D (A = dA [rows][d_ff], B = D [rows][d]).  Both
+// operands are stored k-major (a row per token), so both are staged in that layout and read into
+// MFMA fragments by LDS transpose reads.  Workgroup: 128 x 256 outputs of one expert, 8 waves of
+// 64 x 64 (2 x 2 accumulators); the expert's rows in passes of 64 (the next pass's loads issued
+// before the current pass's products), rows past the expert's zero-filled.  The workgroup order
+// keeps an expert's blocks on one XCD.  Requires M % 128 == 0 and N % 256 == 0; an expert without
+// rows gets zeros.
+constexpr int kWgBM = 128, kWgBN = 256, kWgK = 64;
+constexpr int kWgLdA = kWgBM + 16, kWgLdB = kWgBN + 16;   // bf16 strides: 4 rows of a transposed read on distinct banks
+
+__global__ __launch_bounds__(512) void k_bwd_wgrad(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                   float* __restrict__ C, const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ rows, int n, int M, int N) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[kWgK * kWgLdA];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kWgK * kWgLdB];
+  const int nbm = M / kWgBM, nbn = N / kWgBN, per = nbm * nbn;
+  const unsigned G = unsigned(n) * per, b = blockIdx.x;
+  const unsigned Lx = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;   // XCD-major
+  const int e = int(Lx / per), bi = int(Lx % per), bm = bi / nbn, bn = bi % nbn;
+  const int r0 = offsets[e], K = rows ? rows[e] : offsets[e + 1] - offsets[e];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r32 = lane & 31, h = lane >> 5;
+  const int m0 = bm * kWgBM, n0 = bn * kWgBN;
+  const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
+  // staging: A pass [64 k][128 m] = 1024 vectors of 8, B pass [64 k][256 n] = 2048: 2 + 4 per thread
+  u32x4 ra[2], rb[4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int v = tid + 512 * u, k = v >> 4, mm = (v & 15) * 8;
+      ra[u] = k0 + k < K ? *reinterpret_cast<const u32x4*>(A + size_t(r0 + k0 + k) * M + m0 + mm) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = tid + 512 * u, k = v >> 5, nn = (v & 31) * 8;
+      rb[u] = k0 + k < K ? *reinterpret_cast<const u32x4*>(B + size_t(r0 + k0 + k) * N + n0 + nn) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int v = tid + 512 * u;
+      *reinterpret_cast<u32x4*>(As + (v >> 4) * kWgLdA + (v & 15) * 8) = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = tid + 512 * u;
+      *reinterpret_cast<u32x4*>(Bs + (v >> 5) * kWgLdB + (v & 31) * 8) = rb[u];
+    }
+  };
+  // transposed fragment reads: 16-lane group g covers outer 16 (g % 2) + [0, 16) and the k rows of h = g / 2
+  const int g = lane >> 4, L = lane & 15;
+  const uint16_t* at0 = As + (8 * (g >> 1) + (L >> 2)) * kWgLdA + wm + 16 * (g & 1) + 4 * (L & 3);
+  const uint16_t* bt0 = Bs + (8 * (g >> 1) + (L >> 2)) * kWgLdB + wn + 16 * (g & 1) + 4 * (L & 3);
+  auto frag = [&](const uint16_t* p, int ld) -> bf16x8 {
+    const s16x4 lo = lds_read_tr16(p);
+    const s16x4 hi = lds_read_tr16(p + 4 * ld);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
+  if (K > 0) fetch(0);
+  for (int k0 = 0; k0 < K; k0 += kWgK) {
+    put();
+    lds_barrier();
+    if (k0 + kWgK < K) fetch(k0 + kWgK);
+#pragma unroll
+    for (int st = 0; st < kWgK / 16; ++st) {
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) af[u] = frag(at0 + 16 * st * kWgLdA + 32 * u, kWgLdA);
+#pragma unroll
+      for (int v = 0; v < 2; ++v) bf[v] = frag(bt0 + 16 * st * kWgLdB + 32 * v, kWgLdB);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u], bf[v], acc[u][v], 0, 0, 0);
+    }
+    lds_barrier();
+  }
+  float* Ce = C + size_t(e) * M * N;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3), nn = n0 + wn + 32 * v + r32;
+        Ce[size_t(m) * N + nn] = acc[u][v][i];
+      }
 }
 
 // Fixed-order sum of split-K partials: out[i] = Σ_s part[s][i].
@@ -348,9 +669,19 @@ static void gemm_bf16(const GemmArgs& a, int groups, int m_max, hipStream_t s) {
   hipLaunchKernelGGL(k_bwd_gemm_bf16, gemm_grid(a, groups, m_max), dim3(kBwdThreads), 0, s, a);
 }
 
+// the vector form needs every operand's contiguous dimension, and K when k is contiguous (and
+// every split range's start), to be multiples of 8
 template <int TA, int TB>
 static void gemm_f32(const GemmArgs& a, int groups, int m_max, hipStream_t s) {
-  hipLaunchKernelGGL((k_bwd_gemm_f32<TA, TB>), gemm_grid(a, groups, m_max), dim3(kBwdThreads), 0, s, a);
+  auto contig = [](int64_t s_outer, int64_t s_k, int outer) {
+    return s_k == 1 ? (s_outer % 8 == 0) : (s_outer == 1 && s_k % 8 == 0 && outer % 8 == 0);
+  };
+  const bool k_ok = (a.sAk != 1 && a.sBk != 1) || (a.K % 8 == 0 && (a.splits <= 1 || a.K % (8 * a.splits) == 0));
+  const bool vec = a.rows_dim == 2 && k_ok && contig(a.sAm, a.sAk, a.M) && contig(a.sBn, a.sBk, a.N);
+  if (vec)
+    hipLaunchKernelGGL((k_bwd_gemm_f32<TA, TB, true>), gemm_grid(a, groups, m_max), dim3(kBwdThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_bwd_gemm_f32<TA, TB, false>), gemm_grid(a, groups, m_max), dim3(kBwdThreads), 0, s, a);
 }
 
 hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
@@ -374,7 +705,15 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
   // 1. combine transpose: dY and the gate gradients
   hipLaunchKernelGGL(k_bwd_gate, dim3(tok_blocks), dim3(256), 0, s, b.m, d, k, b.dout, b.y, b.gate, b.t2r, dY, dgate);
   // 2. expert gradients, grouped by expert
-  {
+  // the weight-stream form where the shapes allow it (and the row offsets fit 32 bits)
+  auto nn_ok = [&](int K, int N) {
+    return K % 256 == 0 && N % 256 == 0 && b.rows_bound * int64_t(K) < (int64_t(1) << 32);
+  };
+  const bool stream = nn_ok(d, d_ff) && nn_ok(d_ff, d);
+  if (stream) {   // dA = (dY · W2_e) ⊙ [H > 0]: K = d, N = d_ff
+    hipLaunchKernelGGL((k_bwd_nn_stream<8, true>), dim3(unsigned(n) * (d_ff / 256)), dim3(512), 0, s, dY,
+                       static_cast<const uint16_t*>(b.w2), dA, b.hidden, b.offsets, b.rows, n, d, d_ff);
+  } else {
     GemmArgs g{};   // dA = (dY · W2_e) ⊙ [H > 0]: M = rows, K = d, N = d_ff
     g.A = dY; g.sAm = d; g.sAk = 1;
     g.B = b.w2; g.sBk = d_ff; g.sBn = 1; g.gB = int64_t(d) * d_ff;
@@ -382,7 +721,10 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.N = d_ff; g.K = d; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 0; g.splits = 1;
     gemm_bf16(g, n, b.rows_max, s);
   }
-  {
+  if (stream) {   // dD = dA · W1_e: K = d_ff, N = d
+    hipLaunchKernelGGL((k_bwd_nn_stream<8, false>), dim3(unsigned(n) * (d / 256)), dim3(512), 0, s, dA,
+                       static_cast<const uint16_t*>(b.w1), dD, nullptr, b.offsets, b.rows, n, d_ff, d);
+  } else {
     GemmArgs g{};   // dD = dA · W1_e: M = rows, K = d_ff, N = d
     g.A = dA; g.sAm = d_ff; g.sAk = 1;
     g.B = b.w1; g.sBk = d; g.sBn = 1; g.gB = int64_t(d_ff) * d;
@@ -390,7 +732,10 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.N = d; g.K = d_ff; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 0; g.splits = 1;
     gemm_bf16(g, n, b.rows_max, s);
   }
-  {
+  if (d % kWgBM == 0 && d_ff % kWgBN == 0) {   // dW2_e = dYᵀ · H: M = d, N = d_ff
+    hipLaunchKernelGGL(k_bwd_wgrad, dim3(unsigned(n) * (d / kWgBM) * (d_ff / kWgBN)), dim3(512), 0, s, dY, b.hidden,
+                       b.dw2, b.offsets, b.rows, n, d, d_ff);
+  } else {
     GemmArgs g{};   // dW2_e = dYᵀ · H: M = d, K = rows, N = d_ff
     g.A = dY; g.sAm = 1; g.sAk = d;
     g.B = b.hidden; g.sBk = d_ff; g.sBn = 1;
@@ -398,7 +743,10 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     g.M = d; g.N = d_ff; g.offsets = b.offsets; g.rows = b.rows; g.rows_dim = 1; g.splits = 1;
     gemm_bf16(g, n, d, s);
   }
-  {
+  if (d_ff % kWgBM == 0 && d % kWgBN == 0) {   // dW1_e = dAᵀ · D: M = d_ff, N = d
+    hipLaunchKernelGGL(k_bwd_wgrad, dim3(unsigned(n) * (d_ff / kWgBM) * (d / kWgBN)), dim3(512), 0, s, dA,
+                       static_cast<const uint16_t*>(b.dispatched), b.dw1, b.offsets, b.rows, n, d_ff, d);
+  } else {
     GemmArgs g{};   // dW1_e = dAᵀ · D: M = d_ff, K = rows, N = d
     g.A = dA; g.sAm = 1; g.sAk = d_ff;
     g.B = b.dispatched; g.sBk = d; g.sBn = 1;
