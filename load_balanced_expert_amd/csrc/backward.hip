@@ -548,7 +548,7 @@ __global__ __launch_bounds__(512) void k_bwd_wgrad(const uint16_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = m0 + wm + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3), nn = n0 + wn + 32 * v + r32;
-        Ce[size_t(m) * N + nn] = acc[u][v][i];
+        __builtin_nontemporal_store(acc[u][v][i], Ce + size_t(m) * N + nn);   // written once, read by the caller
       }
 }
 
