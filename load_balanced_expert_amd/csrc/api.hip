@@ -154,6 +154,9 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
   a.finish = !ex.defer_finish;
   a.sup_counts = at<int32_t>(ws, kSupCountsOff);
   a.sup_psum = at<unsigned long long>(ws, kSupPsumOff);
+  // the stand-alone finish reads the per-super-chunk sums where they fit (the fused path, n <= 256)
+  a.fin_super = a.finish && L.rp.fused && s.n <= kSelfPrefixMaxN &&
+                (L.nch_route + L.sup_route - 1) / L.sup_route <= kMaxSuperChunks;
   RoutePlan rp = L.rp;
   if (rp.mfma && (reinterpret_cast<uintptr_t>(x) % 16) != 0) rp.mfma = false;
   return hip_status(launch_route(rp, a, st));

@@ -59,8 +59,9 @@ struct RouteArgs {
   int rows_sub;                   // big-n epilogue: tokens per LDS sub-tile (set by launch_route)
   float* kpart;                   // kg > 1: [tiles][kg][32][npad] partial logits (workspace)
   uint32_t* tile_tickets;         // kg > 1: [tiles] (control region)
-  int32_t* sup_counts;            // finish == false: per-super-chunk sums (atomics)
+  int32_t* sup_counts;            // finish == false or fin_super: per-super-chunk sums (atomics)
   unsigned long long* sup_psum;
+  bool fin_super;                 // finish from the per-super-chunk sums (n <= 256), not the chunk rows
 };
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
 int route_chunk_tokens(const RoutePlan& plan);  // tokens per route workgroup (= dispatch chunk)

@@ -193,4 +193,71 @@ __device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds,
   }
 }
 
+// Runs in the last workgroup when every workgroup added its counts and fixed-point (2^-32) score
+// sums into the per-super-chunk rows [nsup][n] with integer atomics (order-free, so deterministic):
+// reads the rows (one round of L2-bypassing loads), publishes what finalize_chunks publishes and
+// leaves the rows zero for the next call.  lds: >= n ints.
+__device__ __forceinline__ void finalize_super(const FinalizeArgs& a, int32_t* sup_counts,
+                                               unsigned long long* sup_psum, bool want_psum, int* lds,
+                                               int threads) {
+  __shared__ int part[16];
+  __shared__ double red[16];
+  const int n = a.n;
+  const int nsup = ceil_div(a.nch, a.sup);
+  int* tot = lds;
+  const double dm = double(a.m);
+  double auxp = 0.0;
+  for (int j = threadIdx.x; j < n; j += threads) {
+    int c[kMaxSuperChunks];
+    unsigned long long p[kMaxSuperChunks];
+#pragma unroll
+    for (int s = 0; s < kMaxSuperChunks; ++s) {
+      c[s] = s < nsup ? load_agent(sup_counts + s * n + j) : 0;
+      p[s] = s < nsup && want_psum ? load_agent(sup_psum + s * n + j) : 0ull;
+    }
+    int run = 0;
+    unsigned long long ps = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxSuperChunks; ++s) {
+      if (s < nsup) {
+        if (a.capacity >= 0) a.super_prefix[int64_t(s) * n + j] = run;
+        run += c[s];
+        ps += p[s];
+        store_agent(sup_counts + s * n + j, 0);
+        if (want_psum) store_agent(sup_psum + s * n + j, 0ull);
+      }
+    }
+    const float psf = float(double(ps) / double(kPsumScale));
+    tot[j] = run;
+    if (a.counts) a.counts[j] = run;
+    if (a.prob_sum) a.prob_sum[j] = psf;
+    if (a.f) a.f[j] = float(run) / float(a.m);
+    if (a.P) a.P[j] = psf / float(a.m);
+    auxp += (double(run) / dm) * (double(psf) / dm);
+  }
+  if (a.aux) {
+    double v = wave_sum_f64(auxp);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int q = 0; q < threads / 64; ++q) t += red[q];
+      a.aux[0] = float(double(a.alpha) * double(n) * t);
+    }
+  }
+  __syncthreads();
+  if (a.capacity >= 0) {
+    for (int j = threadIdx.x; j < n; j += threads) {
+      tot[j] = min(tot[j], a.capacity);
+      if (a.expert_rows) a.expert_rows[j] = tot[j];
+    }
+    __syncthreads();
+    if (a.padded) {
+      for (int j = threadIdx.x; j <= n; j += threads) a.expert_offsets[j] = j * a.capacity;
+    } else {
+      block_exclusive_scan(tot, n, a.expert_offsets, part, threads);
+    }
+  }
+}
+
 }  // namespace moe

@@ -64,7 +64,7 @@ static bool stage_x(const RoutePlan& plan, int) { return x_tile_ints(plan) + pla
 // product is done instead of waiting until every wave has read the x tile
 static bool partials_apart(const RoutePlan& plan, int n) {
   return plan.fused && plan.mfma && stage_x(plan, n) &&
-         x_tile_ints(plan) + fused_partial_ints(plan, n) + plan.npad + 1024 <= 40960;
+         x_tile_ints(plan) + fused_partial_ints(plan, n) + 2 * plan.npad + 1024 <= 40960;   // + histogram, bias
 }
 static int route_region_ints(const RoutePlan& plan, int n) {
   if (!plan.fused) return n + 4096;
@@ -385,6 +385,7 @@ __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 
 struct EpiArgs {
   int n, k, score, gate;
   const float* bias;
+  const float* bias_lds;   // the bias staged in LDS (fused kernel), or nullptr
 };
 
 // Logistic score; the reciprocal is the hardware one (within 1 ulp; 1 + e^-h >= 1).
@@ -530,7 +531,8 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
       continue;
     }
 #pragma unroll
-    for (int u = 0; u < NV; ++u) bv[u] = (e.bias && l + 32 * u < e.n) ? e.bias[l + 32 * u] : 0.f;
+    for (int u = 0; u < NV; ++u)
+      bv[u] = (e.bias && l + 32 * u < e.n) ? (e.bias_lds ? e.bias_lds[l + 32 * u] : e.bias[l + 32 * u]) : 0.f;
     if (e.score == 0) {
       float mx = -INFINITY;
 #pragma unroll
@@ -553,7 +555,6 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
     // marks this lane's expert l + 32 u as picked)
     uint32_t taken = 0;
     int my_j = 0;
-    float my_score = 0.f, total = 0.f;
     for (int r = 0; r < e.k; ++r) {
       float bk = -INFINITY;
       int bj = 0x7FFFFFFF;
@@ -570,19 +571,17 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
       }
       half_argbest(bk, bj);
       if ((bj & 31) == l) taken |= 1u << (bj >> 5);
-      // the chosen expert's score, from the lane that holds it
-      float mine = 0.f;
-#pragma unroll
-      for (int u = 0; u < NV; ++u)
-        if (l + 32 * u == bj) mine = sc[u];
-      const float sc_b = __shfl(mine, bj & 31, 32);
-      total += sc_b;
-      if (l == r) {
-        my_j = bj;
-        my_score = sc_b;
-      }
+      if (l == r) my_j = bj;
       if (l == 0) atomicAdd(&hist[bj], 1);
     }
+    // the picks' scores, after the rounds: lane r < k reads its pick's score from the lane holding it
+    float my_score = 0.f;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const float v = __shfl(sc[u], my_j & 31, 32);
+      if ((my_j >> 5) == u) my_score = v;
+    }
+    const float total = half_sum(l < e.k ? my_score : 0.f);
     if (l < e.k) {
       const int64_t o = (t0 + tl) * e.k + l;
       idx[o] = my_j;
@@ -603,13 +602,13 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
 __device__ __forceinline__ void chunk_row_out(const RouteArgs& a, const EpiArgs& e, int chunk, int j, int count,
                                               float acc) {
   const int64_t row0 = int64_t(chunk) * e.n;
-  if (a.finish) {
+  if (a.finish && !a.fin_super) {
     store_agent(a.chunks + row0 + j, pack_chunk(count, acc));
   } else {
-    // count rows [chunks][n] int32 for the next kernel, and this chunk's share
-    // of its super chunk's totals: integer adds, so their order does not matter
+    // this chunk's share of its super chunk's totals: integer adds, so their order does not
+    // matter; and (layer) count rows [chunks][n] int32 for the next kernel
     const int64_t so = int64_t(chunk / a.sup) * e.n + j;
-    reinterpret_cast<int32_t*>(a.chunks)[row0 + j] = count;
+    if (!a.finish) reinterpret_cast<int32_t*>(a.chunks)[row0 + j] = count;
     if (count) atomicAdd(a.sup_counts + so, count);
     if (a.want_psum) atomicAdd(a.sup_psum + so, __float2ull_rn(acc * kPsumScale));
   }
@@ -663,7 +662,10 @@ __device__ __forceinline__ void route_finish(const RouteArgs& a, const EpiArgs& 
   f.super_prefix = a.super_prefix;
   f.expert_rows = a.expert_rows;
   f.padded = a.padded;
-  finalize_chunks(f, scratch, scratch_ints, kRouteThreads);
+  if (a.fin_super)
+    finalize_super(f, a.sup_counts, a.sup_psum, a.want_psum, scratch, kRouteThreads);
+  else
+    finalize_chunks(f, scratch, scratch_ints, kRouteThreads);
 }
 
 // The epilogue above with NV = npad / 32 chosen at run time (vector-ALU product path).
@@ -695,6 +697,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   const int lg_off = XLDS && a.parts_apart ? kRouteBM * (xcols + 8) / 2 : 0;
   float* lg = smem + lg_off;
   int* hist = reinterpret_cast<int*>(smem) + a.lds_region_ints;
+  float* bias_l = reinterpret_cast<float*>(hist + a.npad);   // the Loss-Free bias, staged once
   // the wave index is uniform: keep it (and every K-block index derived from it) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // a token tile may be split over a.kg workgroups by K range (direct path only)
@@ -702,7 +705,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
   const int nkb = a.dpad / 32, kbA = g * nkb / a.kg, kbB = (g + 1) * nkb / a.kg;
   const int64_t t0 = int64_t(tile) * kRouteBM;
   const int rows = int(min<int64_t>(kRouteBM, a.m - t0));
-  for (int j = tid; j < a.npad; j += kRouteThreads) hist[j] = 0;
+  for (int j = tid; j < a.npad; j += kRouteThreads) {
+    hist[j] = 0;
+    if (a.bias) bias_l[j] = j < a.n ? a.bias[j] : 0.f;
+  }
 
   if constexpr (MFMA) {
     constexpr int KS = 16 / NT;
@@ -834,7 +840,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_fused(RouteArgs a) {
     }
     __syncthreads();
   }
-  EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
+  EpiArgs e{a.n, a.k, a.score, a.gate, a.bias, a.bias ? bias_l : nullptr};
   if (a.k <= 32) {
     if constexpr (MFMA) route_rows_half<NT>(lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
     else route_rows_half_nv(a.npad / 32, lg, ldl, rows, t0, e, a.idx, a.gate_out, hist);
@@ -989,7 +995,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
   const int vpr = npad / 4, items = sub * vpr;                   // 16-byte items per sub-tile
   const f32x4* lg4 = reinterpret_cast<const f32x4*>(a.logits + t0 * npad);
   for (int j = tid; j < npad; j += kRouteThreads) hist[j] = 0;
-  EpiArgs e{a.n, a.k, a.score, a.gate, a.bias};
+  EpiArgs e{a.n, a.k, a.score, a.gate, a.bias, nullptr};
   f32x4 v[kRowsLoadItems];
   auto load = [&](int s) {
 #pragma unroll
@@ -1094,7 +1100,7 @@ hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_
   a.kg = plan.kg;
   if (plan.fused) {
     const dim3 g(unsigned(ceil_div64(a.m, kRouteBM) * plan.kg));
-    const size_t lds = (size_t(a.lds_region_ints) + plan.npad) * sizeof(float);
+    const size_t lds = (size_t(a.lds_region_ints) + 2 * size_t(plan.npad)) * sizeof(float);   // + histogram, bias
     const int nt = plan.npad / 32;
     if (!plan.mfma)
       hipLaunchKernelGGL((k_route_fused<1, false, false, false>), g, dim3(kRouteThreads), lds, s, a);
