@@ -455,28 +455,6 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
   }
 }
 
-template <int CTRL>
-__device__ __forceinline__ void argbest_step(float& key, int& ix) {
-  const float ok = dpp_f<CTRL>(key);
-  const int oi = dpp_i<CTRL>(ix);
-  if (better(ok, oi, key, ix)) {
-    key = ok;
-    ix = oi;
-  }
-}
-__device__ __forceinline__ void half_argbest(float& key, int& ix) {
-  argbest_step<kDppXor1>(key, ix);
-  argbest_step<kDppXor2>(key, ix);
-  argbest_step<kDppHalfMirror>(key, ix);
-  argbest_step<kDppMirror>(key, ix);
-  uint32_t ka, kb, ia, ib;
-  row_pair(__float_as_uint(key), ka, kb);
-  row_pair(uint32_t(ix), ia, ib);
-  const bool second = better(__uint_as_float(kb), int(ib), __uint_as_float(ka), int(ia));
-  key = __uint_as_float(second ? kb : ka);
-  ix = int(second ? ib : ia);
-}
-
 // Fused-route epilogue for k <= 32: one half-wave per token, NV = npad/32
 // logits per lane in registers (expert j = lane + 32u).  Computes the scores
 // (softmax or sigmoid), the top-k by key (logit, or score + bias), the gates
@@ -551,26 +529,26 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
 #pragma unroll
       for (int u = 0; u < NV; ++u) sc[u] = l + 32 * u < e.n ? sigm(h[u]) : 0.f;
     }
-    // k rounds: each picks the best (key, j) not picked yet (bit u of `taken`
-    // marks this lane's expert l + 32 u as picked)
-    uint32_t taken = 0;
+    // k rounds: each picks the largest key not picked yet, the lowest expert among equal keys: a
+    // half-wave maximum of the keys, then a half-wave minimum of the experts holding it; a pick's
+    // key becomes -inf
+    float key[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) key[u] = l + 32 * u < e.n ? (e.bias ? sc[u] + bv[u] : h[u]) : -INFINITY;
     int my_j = 0;
     for (int r = 0; r < e.k; ++r) {
-      float bk = -INFINITY;
-      int bj = 0x7FFFFFFF;
+      float mk = key[0];
 #pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int j = l + 32 * u;
-        if (j < e.n && !((taken >> u) & 1u)) {
-          const float key = e.bias ? sc[u] + bv[u] : h[u];
-          if (better(key, j, bk, bj)) {
-            bk = key;
-            bj = j;
-          }
-        }
-      }
-      half_argbest(bk, bj);
-      if ((bj & 31) == l) taken |= 1u << (bj >> 5);
+      for (int u = 1; u < NV; ++u) mk = fmaxf(mk, key[u]);
+      mk = half_max(mk);
+      int cand = 0x7FFFFFFF;
+#pragma unroll
+      for (int u = NV - 1; u >= 0; --u)
+        if (key[u] == mk && l + 32 * u < e.n) cand = l + 32 * u;
+      const int bj = half_min_i(cand);
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (l + 32 * u == bj) key[u] = -INFINITY;
       if (l == r) my_j = bj;
       if (l == 0) atomicAdd(&hist[bj], 1);
     }
