@@ -609,22 +609,25 @@ __global__ __launch_bounds__(256) void k_bwd_dh(int64_t m, int n, int k, float* 
   float pc = 0.f;   // <p, c>
   for (int j = lane; j < n; j += 64) pc += expf(h[j] - mx) * inv * float(cs * double(counts[j]));
   pc = wave_sum(pc);
-  // Σ_r dg_r g_r, with g_r the chosen expert's probability
-  float coef[kMaxK];
-  float csum = 0.f;
-  for (int r = 0; r < k; ++r) {
-    const int j = idx[t * k + r];
-    const float gr = expf(h[j] - mx) * inv;
-    coef[r] = dgate[t * k + r] * gr;
-    csum += coef[r];
-  }
+  // lane r < k holds pick r: its expert and dg_r·g_r, with g_r the chosen expert's probability
+  // (k <= 64, one lane per pick); Σ_r dg_r g_r over the wave
+  const int my_j = lane < k ? idx[t * k + lane] : -1;
+  const float my_coef = lane < k ? dgate[t * k + lane] * (expf(h[my_j] - mx) * inv) : 0.f;
+  const float csum = wave_sum(my_coef);
   __builtin_amdgcn_wave_barrier();   // every lane has read the logits it needs before any is overwritten
-  for (int j = lane; j < n; j += 64) {
-    const float p = expf(h[j] - mx) * inv;
-    float v = p * (float(cs * double(counts[j])) - pc) - csum * p;
-    for (int r = 0; r < k; ++r)
-      if (idx[t * k + r] == j) v += coef[r];
-    h[j] = v;
+  // whole-wave passes (the shuffles read every pick's lane), the stores guarded
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    float add = 0.f;
+    for (int r = 0; r < k; ++r) {
+      const int jr = __shfl(my_j, r);
+      const float cr = __shfl(my_coef, r);
+      if (jr == j) add += cr;
+    }
+    if (j < n) {
+      const float p = expf(h[j] - mx) * inv;
+      h[j] = p * (float(cs * double(counts[j])) - pc) - csum * p + add;
+    }
   }
 }
 

@@ -591,6 +591,7 @@ __device__ __forceinline__ void chunk_row_out(const RouteArgs& a, const EpiArgs&
     if (a.want_psum) atomicAdd(a.sup_psum + so, __float2ull_rn(acc * kPsumScale));
   }
 }
+template <bool SUPER>
 __device__ __forceinline__ void route_finish(const RouteArgs& a, const EpiArgs& e, int* scratch, int scratch_ints,
                                              int nchunks);
 
@@ -614,10 +615,15 @@ __device__ __forceinline__ void route_tail(const float* lg, int64_t ld, int rows
     }
     chunk_row_out(a, e, chunk, j, hist[j], acc);
   }
-  route_finish(a, e, scratch, scratch_ints, nchunks);
+  route_finish<true>(a, e, scratch, scratch_ints, nchunks);
 }
 
-// The workgroup that finishes last (stand-alone route) sums the chunk rows.
+// The workgroup that finishes last (stand-alone route) sums the per-super-chunk
+// rows (SUPER: the fused kernel, n <= 256, whose launch always sets fin_super)
+// or the chunk rows (the n > 256 path).  Only one of the two finishes is
+// compiled into a kernel: the chunk-row one alone holds about as many
+// registers as the fused kernel's product, and both together made it spill.
+template <bool SUPER>
 __device__ __forceinline__ void route_finish(const RouteArgs& a, const EpiArgs& e, int* scratch, int scratch_ints,
                                              int nchunks) {
   if (!a.finish) return;
@@ -640,7 +646,7 @@ __device__ __forceinline__ void route_finish(const RouteArgs& a, const EpiArgs& 
   f.super_prefix = a.super_prefix;
   f.expert_rows = a.expert_rows;
   f.padded = a.padded;
-  if (a.fin_super)
+  if constexpr (SUPER)
     finalize_super(f, a.sup_counts, a.sup_psum, a.want_psum, scratch, kRouteThreads);
   else
     finalize_chunks(f, scratch, scratch_ints, kRouteThreads);
@@ -1034,7 +1040,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(RouteArgs a) {
     const int j = tid + q * kRouteThreads;
     if (j < a.n) chunk_row_out(a, e, int(blockIdx.x), j, hist[j], acc[q]);
   }
-  route_finish(a, e, scratch, a.lds_region_ints, int(gridDim.x));
+  route_finish<false>(a, e, scratch, a.lds_region_ints, int(gridDim.x));
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1077,6 +1083,7 @@ hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a_in, hipStream_
   }
   a.kg = plan.kg;
   if (plan.fused) {
+    if (a.finish && !a.fin_super) return hipErrorInvalidValue;   // the fused kernel finishes from super-chunk sums only
     const dim3 g(unsigned(ceil_div64(a.m, kRouteBM) * plan.kg));
     const size_t lds = (size_t(a.lds_region_ints) + 2 * size_t(plan.npad)) * sizeof(float);   // + histogram, bias
     const int nt = plan.npad / 32;
