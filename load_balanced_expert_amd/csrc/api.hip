@@ -9,8 +9,28 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+namespace moe {
+// Zero fill with vector stores: a kernel rather than hipMemsetAsync, so that the
+// clears a caller's stream sees can be recorded into a HIP graph.
+__global__ __launch_bounds__(256) void k_zero16(u32x4* __restrict__ p, int64_t n16) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+}  // namespace moe
+
 namespace {
 using namespace moe;
+
+static_assert(kSupCountsOff % 16 == 0 && kControlBytes % 16 == 0, "control words are cleared in 16-byte units");
+
+// Clears `bytes` bytes at p (16-byte aligned, bytes a multiple of 16) on stream s.
+hipError_t zero_bytes(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = int64_t(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const unsigned g = unsigned(std::min<int64_t>((n16 + 255) / 256, 1024));
+  hipLaunchKernelGGL(k_zero16, dim3(g), dim3(256), 0, s, static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
 
 size_t al(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -241,7 +261,7 @@ size_t moe_workspace_size(const moe_shape* shape, int32_t capacity, int32_t d_ff
 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws_ok(ws, ws_bytes, kControlBytes)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
-  return hip_status(hipMemsetAsync(ws, 0, kControlBytes, static_cast<hipStream_t>(stream)));
+  return hip_status(zero_bytes(ws, kControlBytes, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_capacity(int64_t m, int32_t n, double cf) {
@@ -557,7 +577,7 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   // combine clears them: a launch that fails before it clears them here, so that the
   // workspace stays usable for the next call.
   auto fail = [&](moe_status e) {
-    if (da.self_prefix) hipMemsetAsync(at<char>(ws, kSupCountsOff), 0, kControlBytes - kSupCountsOff, s);
+    if (da.self_prefix) zero_bytes(at<char>(ws, kSupCountsOff), kControlBytes - kSupCountsOff, s);
     return e;
   };
   if ((st = do_route(sh, L, x, w_r, planes, bias, idx, gate, counts, psum, ws, s, ex)) != MOE_OK) return fail(st);
