@@ -45,6 +45,15 @@ __device__ __forceinline__ float half_sum(float v) {
   row_pair(__float_as_uint(v), a, b);
   return __uint_as_float(a) + __uint_as_float(b);
 }
+__device__ __forceinline__ uint32_t half_max_u(uint32_t v) {
+  v = max(v, uint32_t(dpp_i<kDppXor1>(int(v))));
+  v = max(v, uint32_t(dpp_i<kDppXor2>(int(v))));
+  v = max(v, uint32_t(dpp_i<kDppHalfMirror>(int(v))));
+  v = max(v, uint32_t(dpp_i<kDppMirror>(int(v))));
+  uint32_t a, b;
+  row_pair(v, a, b);
+  return max(a, b);
+}
 __device__ __forceinline__ int half_min_i(int v) {
   v = min(v, dpp_i<kDppXor1>(v));
   v = min(v, dpp_i<kDppXor2>(v));

@@ -391,6 +391,14 @@ struct EpiArgs {
 // Logistic score; the reciprocal is the hardware one (within 1 ulp; 1 + e^-h >= 1).
 __device__ __forceinline__ float sigm(float h) { return __builtin_amdgcn_rcpf(1.0f + expf(-h)); }
 
+// Order-preserving integer image of a selection key: a > b as floats iff ord_key(a) >
+// ord_key(b) as unsigned integers, with -0 taken as +0 (equal keys stay equal) and NaN as
+// -inf.  Every key maps above 0, which is left to mark absent or already picked experts.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  const uint32_t u = __float_as_uint(f == f ? f + 0.0f : -INFINITY);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
+}
+
 // Score of expert j for a token with softmax statistics (mx, sum); the softmax
 // exponential is the hardware exp2 of the scaled argument (about 1e-6 relative).
 __device__ __forceinline__ float score_of(int score, float h, float mx, float sum) {
@@ -530,28 +538,28 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
       for (int u = 0; u < NV; ++u) sc[u] = l + 32 * u < e.n ? sigm(h[u]) : 0.f;
     }
     // k rounds: each picks the largest key not picked yet, the lowest expert among equal keys: a
-    // half-wave maximum of the keys, then a half-wave minimum of the experts holding it; a pick's
-    // key becomes -inf
-    float key[NV];
+    // half-wave maximum of the integer keys, then a half-wave minimum of the experts holding it;
+    // a pick's key becomes 0, below every expert's (k <= n, so a round always finds one)
+    uint32_t key[NV];
 #pragma unroll
-    for (int u = 0; u < NV; ++u) key[u] = l + 32 * u < e.n ? (e.bias ? sc[u] + bv[u] : h[u]) : -INFINITY;
+    for (int u = 0; u < NV; ++u) key[u] = l + 32 * u < e.n ? ord_key(e.bias ? sc[u] + bv[u] : h[u]) : 0u;
     int my_j = 0;
     for (int r = 0; r < e.k; ++r) {
-      float mk = key[0];
+      uint32_t mk = key[0];
 #pragma unroll
-      for (int u = 1; u < NV; ++u) mk = fmaxf(mk, key[u]);
-      mk = half_max(mk);
+      for (int u = 1; u < NV; ++u) mk = max(mk, key[u]);
+      mk = half_max_u(mk);
       int cand = 0x7FFFFFFF;
 #pragma unroll
       for (int u = NV - 1; u >= 0; --u)
-        if (key[u] == mk && l + 32 * u < e.n) cand = l + 32 * u;
+        if (key[u] == mk) cand = l + 32 * u;
       const int bj = half_min_i(cand);
 #pragma unroll
       for (int u = 0; u < NV; ++u)
-        if (l + 32 * u == bj) key[u] = -INFINITY;
+        if (l + 32 * u == bj) key[u] = 0u;
       if (l == r) my_j = bj;
-      if (l == 0) atomicAdd(&hist[bj], 1);
     }
+    if (l < e.k) atomicAdd(&hist[my_j], 1);   // the k picks are distinct experts
     // the picks' scores, after the rounds: lane r < k reads its pick's score from the lane holding it
     float my_score = 0.f;
 #pragma unroll
