@@ -296,6 +296,30 @@ def main():
     value = T / (metric_ms * 1e-3)
     rows = int(lo.expert_rows.sum().item())   # kept rows
 
+    # The region above holds one event record, and the GPU idles a few microseconds after each.
+    # The same work with no event inside: `nq` whole steps between two events, less `nq` runs of
+    # the same expert FFN (on the last step's dispatched rows) between two events; five
+    # alternating rounds, the median kept.
+    def no_event_region(nq, rounds=5):
+        est = []
+        for _ in range(rounds):
+            a0, a1, b0, b1 = (he.create() for _ in range(4))
+            torch.cuda.synchronize()
+            he.record(a0, stream)
+            for _ in range(nq):
+                step()
+            he.record(a1, stream)
+            torch.cuda.synchronize()
+            he.record(b0, stream)
+            for _ in range(nq):
+                M.expert_ffn(lo.dispatched, lo.expert_offsets, W1, W2, cap, out=lo.y, expert_rows=lo.expert_rows)
+            he.record(b1, stream)
+            torch.cuda.synchronize()
+            est.append((he.ms(a0, a1) - he.ms(b0, b1)) / nq)
+        return float(np.median(est)), [float(e) for e in est]
+
+    ne_ms, ne_all = no_event_region(max(args.steps, 20))
+
     # Stage breakdown: a separate short run with all six stage events.  Every span also carries the
     # cost of the event packets around it; the span between two events with nothing between them
     # ([0] -> [1]: the router weight is prepared outside the step) measures that cost, and each
@@ -415,6 +439,10 @@ def main():
                    "global_batch": T, "capacity": cap, "parallelism": "single GPU"},
         "metric_ms_per_step": metric_ms, "metric_ms_p10_p90": [float(np.percentile(region, 10)),
                                                                float(np.percentile(region, 90))],
+        "region_without_events": {"value": T / (ne_ms * 1e-3), "ms_per_step": ne_ms, "rounds_ms": ne_all,
+                                  "how": "whole steps between two events, less the same number of expert FFN runs "
+                                         "between two events (median of 5 alternating rounds); the headline region "
+                                         "also holds one event record"},
         "expert_ffn_ms": t_ffn * 1e3, "stage_ms_event_spans": stage_ms,
         "hbm_roofline_frac_of_metric_region": alg_metric_bytes / (metric_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "copy_ceiling_gbs": copy_gbs,
