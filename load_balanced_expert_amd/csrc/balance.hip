@@ -276,6 +276,24 @@ __device__ __forceinline__ void sort_desc(float (&v)[NPL], int (&j)[NPL]) {
   }
 }
 
+// The same network on order-preserving integer keys (values only): two instructions per exchange.
+template <int NPL>
+__device__ __forceinline__ void sort_desc_u(uint32_t (&v)[NPL]) {
+  auto ce = [&](int p, int q) {
+    const uint32_t hi = max(v[p], v[q]), lo = min(v[p], v[q]);
+    v[p] = hi;
+    v[q] = lo;
+  };
+  if constexpr (NPL == 2) ce(0, 1);
+  if constexpr (NPL == 4) {
+    ce(0, 1), ce(2, 3), ce(0, 2), ce(1, 3), ce(1, 2);
+  }
+  if constexpr (NPL == 8) {
+    ce(0, 1), ce(2, 3), ce(4, 5), ce(6, 7), ce(0, 2), ce(1, 3), ce(4, 6), ce(5, 7), ce(1, 2), ce(5, 6);
+    ce(0, 4), ce(1, 5), ce(2, 6), ce(3, 7), ce(2, 4), ce(3, 5), ce(1, 2), ce(3, 4), ce(5, 6);
+  }
+}
+
 template <bool IDX, bool ALPHA, int NPL>
 __global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_half(BalanceArgs a, const float* __restrict__ beta,
                                                                      float* __restrict__ alpha,
@@ -297,9 +315,16 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_half(BalanceArgs a,
   float bl[NPL];
 #pragma unroll
   for (int u = 0; u < NPL; ++u) bl[u] = hl + 32 * u < n ? beta[cur_b * n + hl + 32 * u] : 0.f;
-  float nx[NPL];
+  // the rows of this half's next PF iterations are loaded ahead (two for the value-only form,
+  // whose registers allow it)
+  constexpr int PF = IDX ? 1 : 2;
+  float nx[PF][NPL];
 #pragma unroll
-  for (int u = 0; u < NPL; ++u) nx[u] = i < a.m && hl + 32 * u < n ? a.s[i * n + hl + 32 * u] : 0.f;
+  for (int p = 0; p < PF; ++p) {
+    const int64_t ip = i + p * stride;
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) nx[p][u] = ip < a.m && hl + 32 * u < n ? a.s[ip * n + hl + 32 * u] : 0.f;
+  }
   // both halves run the same number of iterations (the wave's first row decides)
   for (int64_t i0 = i - half; i0 < a.m; i0 += stride, i += stride) {
     const bool live = i < a.m;
@@ -313,43 +338,73 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_half(BalanceArgs a,
 #pragma unroll
     for (int u = 0; u < NPL; ++u) {
       const int j = hl + 32 * u;
-      v[u] = j < n && live ? nx[u] - bl[u] : -INFINITY;
+      v[u] = j < n && live ? nx[0][u] - bl[u] : -INFINITY;
       jj[u] = j < n ? j : 0x7FFFFFFF;
     }
-    const int64_t i2 = i + stride;
 #pragma unroll
-    for (int u = 0; u < NPL; ++u) nx[u] = i2 < a.m && hl + 32 * u < n ? a.s[i2 * n + hl + 32 * u] : 0.f;
-    sort_desc<IDX, NPL>(v, jj);
+    for (int p = 0; p + 1 < PF; ++p)
+#pragma unroll
+      for (int u = 0; u < NPL; ++u) nx[p][u] = nx[p + 1][u];
+    const int64_t i2 = i + PF * stride;
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) nx[PF - 1][u] = i2 < a.m && hl + 32 * u < n ? a.s[i2 * n + hl + 32 * u] : 0.f;
     float hi_key = INFINITY, lo_key = INFINITY;
     int my_j = 0;
-    for (int r = 0; r < rounds; ++r) {
-      const float mx = half_max(v[0]);
-      bool top = v[0] == mx;
-      uint64_t tied = __ballot(top);
-      if (IDX && r < k && (__popc(uint32_t(tied)) > 1 || __popc(uint32_t(tied >> 32)) > 1)) {
-        // equal heads: the lowest expert goes first
-        const int mj = half_min_i(top ? jj[0] : 0x7FFFFFFF);
-        top = top && jj[0] == mj;
-        tied = __ballot(top);
-      }
-      const uint32_t tlo = uint32_t(tied), thi = uint32_t(tied >> 32);
-      const int wlo = tlo ? __ffs(tlo) - 1 : 0, whi = thi ? __ffs(thi) + 31 : 32;
-      const int win = half ? whi : wlo;
-      if (IDX && r < k) {
-        const int bj = __shfl(jj[0], win, 64);
-        if (hl == r) my_j = bj;
-        if (hl == 0 && live) atomicAdd(&hist[bj], 1);
-      }
-      if (r == arank - 1) hi_key = mx;
-      if (r == arank) lo_key = mx;
-      if (lane == win) {
+    if constexpr (!IDX) {
+      // values only: order-preserving integer keys, so the sort is integer max/min and each
+      // round a fused DPP integer maximum; an absent or popped entry holds the key of -inf
+      constexpr uint32_t kNegInf = 0x007FFFFFu;   // ord_bits(-inf)
+      uint32_t kv[NPL];
 #pragma unroll
-        for (int u = 0; u + 1 < NPL; ++u) {
-          v[u] = v[u + 1];
-          if (IDX) jj[u] = jj[u + 1];
+      for (int u = 0; u < NPL; ++u) kv[u] = ord_bits(v[u]);
+      sort_desc_u<NPL>(kv);
+      uint32_t hk = 0xFF800000u, lk = 0xFF800000u;   // ord_bits(+inf)
+      for (int r = 0; r < rounds; ++r) {
+        const uint32_t mk = half_max_u(kv[0]);
+        const uint64_t tied = __ballot(kv[0] == mk);
+        const uint32_t tlo = uint32_t(tied), thi = uint32_t(tied >> 32);
+        const int win = half ? (thi ? __ffs(thi) + 31 : 32) : (tlo ? __ffs(tlo) - 1 : 0);
+        if (r == arank - 1) hk = mk;
+        if (r == arank) lk = mk;
+        if (lane == win) {
+#pragma unroll
+          for (int u = 0; u + 1 < NPL; ++u) kv[u] = kv[u + 1];
+          kv[NPL - 1] = kNegInf;
         }
-        v[NPL - 1] = -INFINITY;
-        if (IDX) jj[NPL - 1] = 0x7FFFFFFF;
+      }
+      hi_key = from_ord(hk);
+      lo_key = from_ord(lk);
+    } else {
+      sort_desc<IDX, NPL>(v, jj);
+      for (int r = 0; r < rounds; ++r) {
+        const float mx = half_max(v[0]);
+        bool top = v[0] == mx;
+        uint64_t tied = __ballot(top);
+        if (IDX && r < k && (__popc(uint32_t(tied)) > 1 || __popc(uint32_t(tied >> 32)) > 1)) {
+          // equal heads: the lowest expert goes first
+          const int mj = half_min_i(top ? jj[0] : 0x7FFFFFFF);
+          top = top && jj[0] == mj;
+          tied = __ballot(top);
+        }
+        const uint32_t tlo = uint32_t(tied), thi = uint32_t(tied >> 32);
+        const int wlo = tlo ? __ffs(tlo) - 1 : 0, whi = thi ? __ffs(thi) + 31 : 32;
+        const int win = half ? whi : wlo;
+        if (IDX && r < k) {
+          const int bj = __shfl(jj[0], win, 64);
+          if (hl == r) my_j = bj;
+          if (hl == 0 && live) atomicAdd(&hist[bj], 1);
+        }
+        if (r == arank - 1) hi_key = mx;
+        if (r == arank) lo_key = mx;
+        if (lane == win) {
+#pragma unroll
+          for (int u = 0; u + 1 < NPL; ++u) {
+            v[u] = v[u + 1];
+            if (IDX) jj[u] = jj[u + 1];
+          }
+          v[NPL - 1] = -INFINITY;
+          if (IDX) jj[NPL - 1] = 0x7FFFFFFF;
+        }
       }
     }
     if (ALPHA && hl == 0 && live) {
@@ -482,14 +537,26 @@ __device__ __forceinline__ void col_scan(const float* __restrict__ col, const fl
     const int64_t nv = m >> 2;
     const f32x4* c4 = reinterpret_cast<const f32x4*>(col);
     const f32x4* a4 = reinterpret_cast<const f32x4*>(alpha);
+    // the next iteration's vectors are loaded before this one's keys are used, so two
+    // iterations of loads are in flight (a load past the column is not issued)
+    auto load = [&](int64_t b, f32x4 (&xx)[2], f32x4 (&aa)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t v = b + int64_t(u) * kColThreads;
+        xx[u] = v < nv ? c4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+        aa[u] = v < nv ? a4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    f32x4 xc[2], ac[2];
+    load(threadIdx.x, xc, ac);
     for (int64_t b = threadIdx.x; b - threadIdx.x < nv; b += 2 * kColThreads) {   // uniform trip count
       f32x4 x[2], al[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int64_t v = b + int64_t(u) * kColThreads;
-        x[u] = v < nv ? c4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
-        al[u] = v < nv ? a4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+        x[u] = xc[u];
+        al[u] = ac[u];
       }
+      load(b + 2 * kColThreads, xc, ac);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bool act = b + int64_t(u) * kColThreads < nv;
@@ -554,6 +621,88 @@ __device__ __forceinline__ void lds_select(const uint32_t* keys, int nk, int ran
   __syncthreads();
 }
 
+// The bins of hist[0..nb) (descending digit order) holding descending ranks ra and rb (-1: not
+// wanted), and the ranks within them: out = {bin of ra, rank in it, bin of rb, rank in it}.
+__device__ __forceinline__ void col_select2(const int* hist, int nb, int ra, int rb, int* s_wsum, int* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = ceil_div(nb, kColThreads);
+  int hv[4], tot = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int b = nb - 1 - (tid * per + u);
+    hv[u] = u < per && b >= 0 ? hist[b] : 0;
+    tot += hv[u];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int cum = incl - tot;
+  for (int w = 0; w < wave; ++w) cum += s_wsum[w];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u < per) {
+      const int bin = nb - 1 - (tid * per + u);
+      if (cum <= ra && ra < cum + hv[u]) {
+        out[0] = bin;
+        out[1] = ra - cum;
+      }
+      if (cum <= rb && rb < cum + hv[u]) {
+        out[2] = bin;
+        out[3] = rb - cum;
+      }
+    }
+    cum += hv[u];
+  }
+  __syncthreads();
+}
+
+// Window bounds from the nk sample keys: k_hi at least the key of descending rank rh, k_lo at
+// most the key of rank rl (rh or rl -1: that bound stays open), both ranks found together by
+// two 12-bit radix passes, so the bounds are the ranks' 24-bit key prefixes widened to whole
+// prefixes.  h2 holds two histograms [2][kColBins].
+__device__ __forceinline__ void window_bounds(const uint32_t* keys, int nk, int rh, int rl, int* h1, int* h2,
+                                              int* s_wsum, int* s_sel, uint32_t& k_hi, uint32_t& k_lo) {
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kColBins; b += kColThreads) {
+    h1[b] = 0;
+    h2[b] = 0;
+    h2[kColBins + b] = 0;
+  }
+  __syncthreads();
+  for (int t = tid; t - tid < nk; t += kColThreads) {
+    const bool act = t < nk;
+    hist_add(h1, act ? keys[t] >> 20 : 0u, act);
+  }
+  __syncthreads();
+  col_select2(h1, kColBins, rh, rl, s_wsum, s_sel);
+  const uint32_t bh = uint32_t(s_sel[0]), bl = uint32_t(s_sel[2]);
+  const int qh = s_sel[1], ql = s_sel[3];
+  __syncthreads();   // every thread has read s_sel
+  for (int t = tid; t - tid < nk; t += kColThreads) {
+    const uint32_t u = t < nk ? keys[t] : 0u;
+    const bool ah = t < nk && rh >= 0 && (u >> 20) == bh;
+    hist_add(h2, ah ? (u >> 8) & 0xFFFu : 0u, ah);
+    const bool al = t < nk && rl >= 0 && (u >> 20) == bl;
+    hist_add(h2 + kColBins, al ? (u >> 8) & 0xFFFu : 0u, al);
+  }
+  __syncthreads();
+  if (rh >= 0) {
+    col_select2(h2, kColBins, qh, -1, s_wsum, s_sel);
+    k_hi = (((bh << 12) | uint32_t(s_sel[0])) << 8) | 0xFFu;
+    __syncthreads();
+  }
+  if (rl >= 0) {
+    col_select2(h2 + kColBins, kColBins, ql, -1, s_wsum, s_sel);
+    k_lo = ((bl << 12) | uint32_t(s_sel[0])) << 8;
+    __syncthreads();
+  }
+}
+
 // Appends the keys with take == true to keys[] (wave-aggregated slots);
 // slots past the capacity set *ovf instead.
 __device__ __forceinline__ void lds_append(uint32_t* keys, int* s_nk, int* s_ovf, uint32_t u, bool take) {
@@ -582,7 +731,7 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
                                                          BalanceArgs a) {
   extern __shared__ __attribute__((aligned(16))) int hist[];   // [kColBins], then [kColCap] keys
   uint32_t* keys = reinterpret_cast<uint32_t*>(hist + kColBins);
-  __shared__ int s_wsum[kColThreads / 64], s_wcnt[kColThreads / 64], s_bin, s_rank, s_nk, s_ovf, s_above;
+  __shared__ int s_wsum[kColThreads / 64], s_wcnt[kColThreads / 64], s_bin, s_rank, s_nk, s_ovf, s_above, s_sel[4];
   __shared__ uint32_t s_min;
   const int j = blockIdx.x, tid = threadIdx.x;
   // block blockIdx.y's segment of column j: beta_rows keys from row blockIdx.y * beta_rows
@@ -618,9 +767,9 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
       const double rs = double(rank0) * double(ns) / double(m);
       const int dev = int(4.0 * sqrt(fmax(rs * (1.0 - rs / double(ns)), 0.0))) + 8;
       const int r_hi = int(rs) - dev, r_lo = int(rs) + dev;
-      int rr;
-      if (r_hi > 0) lds_select(keys, ns, r_hi, hist, s_wsum, &s_bin, &s_rank, k_hi, rr);
-      if (r_lo < ns - 1) lds_select(keys, ns, r_lo, hist, s_wsum, &s_bin, &s_rank, k_lo, rr);
+      // second-level histograms in the key area above the (at most 4096) samples
+      window_bounds(keys, ns, r_hi > 0 ? r_hi : -1, r_lo < ns - 1 ? r_lo : -1, hist,
+                    reinterpret_cast<int*>(keys + 4096), s_wsum, s_sel, k_hi, k_lo);
     }
     if (tid == 0) {
       s_nk = 0;
@@ -673,7 +822,13 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
       for (int q = lane; q < wcnt; q += 64) wk[off + q] = slots[q];
     nk = tot;
   }
-  atomicAdd(&s_above, above);
+  // per-wave totals first: one LDS atomic per wave, not per thread
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    above += __shfl_xor(above, off, 64);
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), off, 64)));
+  }
+  if ((tid & 63) == 0) atomicAdd(&s_above, above);
   __syncthreads();
   const int nabove = s_above;
   const bool hit = !w_ovf && nabove <= rank0 && rank0 < nabove + nk;
@@ -742,7 +897,9 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
   if (a.quantile) {
     // descending rank rank0 - 1: the least key above when exactly rank0 keys
     // lie above this one (rank within equal keys is 0), else this key again
-    atomicMin(&s_min, mn);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), off, 64)));
+    if ((tid & 63) == 0) atomicMin(&s_min, mn);
     __syncthreads();
     const float hi = rank0 >= 1 && rank == 0 ? key_f32(s_min) : bv;
     bv = lerp_np(bv, hi, a.g_col);
@@ -1976,7 +2133,8 @@ static void launch_rows(const BalanceArgs& a, const float* beta, float* alpha, u
       const int nh = a.n <= 32 ? 1 : a.n <= 64 ? 2 : a.n <= 128 ? 4 : 8;
       // two rows per wave; the counting form keeps at most 256 count rows (one
       // workgroup per CU: its registers allow no more) for k_qb_count_finish to fold
-      const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), idx ? 256 : 1024));
+      // (value-only form: two 1024-thread workgroups per CU, striding over the rows)
+      const unsigned gh = unsigned(std::min<int64_t>(ceil_div64(a.m, 128), idx ? 256 : 512));
 #define MOE_QB_HALF(NH)                                                                                        \
   if (idx && al)                                                                                            \
     hipLaunchKernelGGL((k_qb_rows_half<true, true, NH>), dim3(gh), dim3(kRowsRegThreads), rlds, s, a, beta, alpha, chunks); \
