@@ -353,12 +353,12 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_half(BalanceArgs a,
     if constexpr (!IDX) {
       // values only: order-preserving integer keys, so the sort is integer max/min and each
       // round a fused DPP integer maximum; an absent or popped entry holds the key of -inf
-      constexpr uint32_t kNegInf = 0x007FFFFFu;   // ord_bits(-inf)
+      constexpr uint32_t kNegInf = 0x007FFFFFu;   // f32_key(-inf)
       uint32_t kv[NPL];
 #pragma unroll
-      for (int u = 0; u < NPL; ++u) kv[u] = ord_bits(v[u]);
+      for (int u = 0; u < NPL; ++u) kv[u] = f32_key(v[u]);
       sort_desc_u<NPL>(kv);
-      uint32_t hk = 0xFF800000u, lk = 0xFF800000u;   // ord_bits(+inf)
+      uint32_t hk = 0xFF800000u, lk = 0xFF800000u;   // f32_key(+inf)
       for (int r = 0; r < rounds; ++r) {
         const uint32_t mk = half_max_u(kv[0]);
         const uint64_t tied = __ballot(kv[0] == mk);
@@ -372,8 +372,8 @@ __global__ __launch_bounds__(kRowsRegThreads) void k_qb_rows_half(BalanceArgs a,
           kv[NPL - 1] = kNegInf;
         }
       }
-      hi_key = from_ord(hk);
-      lo_key = from_ord(lk);
+      hi_key = key_f32(hk);
+      lo_key = key_f32(lk);
     } else {
       sort_desc<IDX, NPL>(v, jj);
       for (int r = 0; r < rounds; ++r) {
@@ -538,13 +538,16 @@ __device__ __forceinline__ void col_scan(const float* __restrict__ col, const fl
     const f32x4* c4 = reinterpret_cast<const f32x4*>(col);
     const f32x4* a4 = reinterpret_cast<const f32x4*>(alpha);
     // the next iteration's vectors are loaded before this one's keys are used, so two
-    // iterations of loads are in flight (a load past the column is not issued)
+    // iterations of loads are in flight; the loads are unconditional (an index past the
+    // column reads its last vector again, whose keys are then inactive), so the waits count
+    // only the loads of the keys in use
+    if (nv == 0) return;
     auto load = [&](int64_t b, f32x4 (&xx)[2], f32x4 (&aa)[2]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int64_t v = b + int64_t(u) * kColThreads;
-        xx[u] = v < nv ? c4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
-        aa[u] = v < nv ? a4[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int64_t v = min(b + int64_t(u) * kColThreads, nv - 1);
+        xx[u] = c4[v];
+        aa[u] = a4[v];
       }
     };
     f32x4 xc[2], ac[2];
@@ -557,13 +560,18 @@ __device__ __forceinline__ void col_scan(const float* __restrict__ col, const fl
         al[u] = ac[u];
       }
       load(b + 2 * kColThreads, xc, ac);
+      if (b - threadIdx.x + 2 * kColThreads <= nv) {   // a full step (uniform): every key active
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bool act = b + int64_t(u) * kColThreads < nv;
-        f(f32_key(x[u][0] - al[u][0]), act);
-        f(f32_key(x[u][1] - al[u][1]), act);
-        f(f32_key(x[u][2] - al[u][2]), act);
-        f(f32_key(x[u][3] - al[u][3]), act);
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) f(f32_key(x[u][c] - al[u][c]), true);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bool act = b + int64_t(u) * kColThreads < nv;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) f(f32_key(x[u][c] - al[u][c]), act);
+        }
       }
     }
     return;
@@ -794,15 +802,15 @@ __global__ __launch_bounds__(kColThreads) void k_qb_cols(const float* __restrict
     const int wave = tid >> 6, lane = tid & 63;
     uint32_t* slots = keys + wave * kColWaveSlots;
     int wcnt = 0;
+    const uint32_t span = k_hi - k_lo;   // k_lo <= k_hi: u is in the window iff u - k_lo <= span
     col_scan(col, alpha, m, [&](uint32_t u, bool act) {
-      if (act && u > k_hi) {
-        ++above;
-        mn = min(mn, u);
-      }
-      const bool take = act && u >= k_lo && u <= k_hi;
+      const bool up = act && u > k_hi;
+      above += up;
+      mn = min(mn, up ? u : 0xFFFFFFFFu);
+      const bool take = act && u - k_lo <= span;
       const uint64_t bm = __ballot(take);
       if (!bm) return;
-      const int at = wcnt + __popcll(bm & lanemask_lt());
+      const int at = wcnt + int(__builtin_amdgcn_mbcnt_hi(uint32_t(bm >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bm), 0u)));
       if (take && at < kColWaveSlots) slots[at] = u;
       wcnt += __popcll(bm);
     });

@@ -56,8 +56,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // Order-preserving map of fp32 onto uint32 (larger float <-> larger key).
 __device__ __forceinline__ uint32_t f32_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);   // negative: all bits flipped; else the sign bit set
 }
 __device__ __forceinline__ float key_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);

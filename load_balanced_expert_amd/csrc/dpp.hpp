@@ -45,15 +45,6 @@ __device__ __forceinline__ float half_sum(float v) {
   row_pair(__float_as_uint(v), a, b);
   return __uint_as_float(a) + __uint_as_float(b);
 }
-// Order-preserving integer image of a float: a < b as floats iff ord_bits(a) < ord_bits(b)
-// as unsigned integers (non-NaN values; -0 sorts just below +0), and its inverse.
-__device__ __forceinline__ uint32_t ord_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
-}
-__device__ __forceinline__ float from_ord(uint32_t k) {
-  return __uint_as_float(k ^ (uint32_t(int32_t(~k) >> 31) | 0x80000000u));
-}
 __device__ __forceinline__ uint32_t half_max_u(uint32_t v) {
   v = max(v, uint32_t(dpp_i<kDppXor1>(int(v))));
   v = max(v, uint32_t(dpp_i<kDppXor2>(int(v))));

@@ -394,7 +394,7 @@ __device__ __forceinline__ float sigm(float h) { return __builtin_amdgcn_rcpf(1.
 // Order-preserving integer image of a selection key: a > b as floats iff ord_key(a) >
 // ord_key(b) as unsigned integers, with -0 taken as +0 (equal keys stay equal) and NaN as
 // -inf.  Every key maps above 0, which is left to mark absent or already picked experts.
-__device__ __forceinline__ uint32_t ord_key(float f) { return ord_bits(f == f ? f + 0.0f : -INFINITY); }
+__device__ __forceinline__ uint32_t ord_key(float f) { return f32_key(f == f ? f + 0.0f : -INFINITY); }
 
 // Score of expert j for a token with softmax statistics (mx, sum); the softmax
 // exponential is the hardware exp2 of the scaled argument (about 1e-6 relative).
