@@ -466,7 +466,7 @@ __global__ __launch_bounds__(64 * W) void k_bwd_nn_stream(const uint16_t* __rest
 constexpr int kWgBM = 128, kWgBN = 256, kWgK = 64;
 constexpr int kWgLdA = kWgBM + 16, kWgLdB = kWgBN + 16;   // bf16 strides: 4 rows of a transposed read on distinct banks
 
-__global__ __launch_bounds__(512) void k_bwd_wgrad(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+__global__ __launch_bounds__(512, 4) void k_bwd_wgrad(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                    float* __restrict__ C, const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ rows, int n, int M, int N) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kWgK * kWgLdA];
