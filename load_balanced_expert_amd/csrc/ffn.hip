@@ -191,18 +191,18 @@ __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, 
 #pragma unroll
   for (int u = 0; u < kFfnRing - 1; ++u) b_fetch(ring[u], u);
   lds_barrier();
+  // K % 256 == 0 (the launcher's condition): whole groups of kFfnRing steps, so the loop body has
+  // no early exit and the waits for the weight ring keep their steady-state counts
   for (int s0 = 0; s0 < nks; s0 += kFfnRing) {
 #pragma unroll
     for (int u = 0; u < kFfnRing; ++u) {
-      if (s0 + u < nks) {
-        b_fetch(ring[(u + kFfnRing - 1) % kFfnRing], s0 + u + kFfnRing - 1);
-        step(ring[u], u & 1);
-        if (u & 1) {  // chunk (s0 + u) / 2 consumed: stage the next one, prefetch the one after
-          lds_barrier();
-          a_store();
-          a_fetch((s0 + u) / 2 + 2);
-          lds_barrier();
-        }
+      b_fetch(ring[(u + kFfnRing - 1) % kFfnRing], s0 + u + kFfnRing - 1);
+      step(ring[u], u & 1);
+      if (u & 1) {  // chunk (s0 + u) / 2 consumed: stage the next one, prefetch the one after
+        lds_barrier();
+        a_store();
+        a_fetch((s0 + u) / 2 + 2);
+        lds_barrier();
       }
     }
   }
