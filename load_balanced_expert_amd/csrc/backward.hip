@@ -388,18 +388,18 @@ __device__ __forceinline__ void nn_rows(const uint16_t* __restrict__ A, const ui
 #pragma unroll
   for (int u = 0; u < kNnRing - 1; ++u) b_fetch(ring[u], u);
   lds_barrier();
-  // K % 256 == 0 (the launcher's condition): whole groups of kNnRing steps, so the loop body has
-  // no early exit and the waits for the weight ring keep their steady-state counts
   for (int s0 = 0; s0 < nks; s0 += kNnRing) {
 #pragma unroll
     for (int u = 0; u < kNnRing; ++u) {
-      b_fetch(ring[(u + kNnRing - 1) % kNnRing], s0 + u + kNnRing - 1);
-      step(ring[u], u & 1);
-      if (u & 1) {   // chunk (s0 + u) / 2 consumed: stage the next one, prefetch the one after
-        lds_barrier();
-        a_store();
-        a_fetch((s0 + u) / 2 + 2);
-        lds_barrier();
+      if (s0 + u < nks) {
+        b_fetch(ring[(u + kNnRing - 1) % kNnRing], s0 + u + kNnRing - 1);
+        step(ring[u], u & 1);
+        if (u & 1) {   // chunk (s0 + u) / 2 consumed: stage the next one, prefetch the one after
+          lds_barrier();
+          a_store();
+          a_fetch((s0 + u) / 2 + 2);
+          lds_barrier();
+        }
       }
     }
   }
