@@ -481,16 +481,20 @@ __global__ __launch_bounds__(512, 4) void k_bwd_wgrad(const uint16_t* __restrict
   const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
   // staging: A pass [64 k][128 m] = 1024 vectors of 8, B pass [64 k][256 n] = 2048: 2 + 4 per thread
   u32x4 ra[2], rb[4];
+  // the workgroup's operand bases (uniform) and 32-bit element offsets per lane (K <= rows of one
+  // expert, so (k0 + k) · N stays far below 2^32)
+  const uint16_t* Ab = A + size_t(r0) * M + m0;
+  const uint16_t* Bb = B + size_t(r0) * N + n0;
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int v = tid + 512 * u, k = v >> 4, mm = (v & 15) * 8;
-      ra[u] = k0 + k < K ? *reinterpret_cast<const u32x4*>(A + size_t(r0 + k0 + k) * M + m0 + mm) : u32x4{0u, 0u, 0u, 0u};
+      ra[u] = k0 + k < K ? *reinterpret_cast<const u32x4*>(Ab + uint32_t((k0 + k) * M + mm)) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int v = tid + 512 * u, k = v >> 5, nn = (v & 31) * 8;
-      rb[u] = k0 + k < K ? *reinterpret_cast<const u32x4*>(B + size_t(r0 + k0 + k) * N + n0 + nn) : u32x4{0u, 0u, 0u, 0u};
+      rb[u] = k0 + k < K ? *reinterpret_cast<const u32x4*>(Bb + uint32_t((k0 + k) * N + nn)) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto put = [&]() {
@@ -540,15 +544,15 @@ __global__ __launch_bounds__(512, 4) void k_bwd_wgrad(const uint16_t* __restrict
     }
     lds_barrier();
   }
-  float* Ce = C + size_t(e) * M * N;
+  float* Cw = C + size_t(e) * M * N + size_t(m0 + wm) * N + n0 + wn;   // this wave's 64 x 64 block
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3), nn = n0 + wn + 32 * v + r32;
-        __builtin_nontemporal_store(acc[u][v][i], Ce + size_t(m) * N + nn);   // written once, read by the caller
+        const int mr = 32 * u + 8 * (i >> 2) + 4 * h + (i & 3), nc = 32 * v + r32;
+        __builtin_nontemporal_store(acc[u][v][i], Cw + uint32_t(mr * N + nc));   // written once, read by the caller
       }
 }
 
