@@ -192,6 +192,23 @@ moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, con
                      int64_t* global_counts, int64_t* global_tokens,
                      float* bias, float gamma, void* stream);
 
+/* moe_route_lossfree — one Loss-Free micro-batch step in one launch: moe_route
+ * with the bias as selection offset ([MoE tour 6] eq. (1)), then, in the
+ * route's last workgroup, the bias update of eq. (2) and the optional
+ * global-batch accumulation, exactly as moe_stats(m, n, k, counts, ...,
+ * global_counts, global_tokens, bias, gamma) would do them after the route.
+ * Every workgroup reads the bias before the last one updates it, so the
+ * update follows the routing as [MoE tour 6] "함정에 주의" requires.
+ * Arguments as moe_route, and: bias [n] fp32 in/out (required; routes with
+ * the incoming value, holds the updated one afterwards); gamma: the update
+ * rate; global_counts [n] int64 in/out and global_tokens [1] int64 in/out, both
+ * or neither.  Results (idx, gate, counts, prob_sum, bias, global counts) are
+ * bit-identical to moe_route followed by moe_stats.  Limits as moe_route. */
+moe_status moe_route_lossfree(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
+                              float* bias, float gamma, int32_t* idx, float* gate, int32_t* counts,
+                              float* prob_sum, int64_t* global_counts, int64_t* global_tokens, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* moe_global_aux — the global-batch balance loss ([Qwen global] "글로벌-배치 로드
  * 밸런스 구현": synchronise f over the global batch, form each micro-batch's loss
  * with it, aggregate).  f^g_j = global_counts_j / global_tokens;

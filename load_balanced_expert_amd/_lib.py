@@ -57,6 +57,8 @@ SIGNATURES = {
     "moe_route": (c_int32, [POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_route_noalloc_max_bytes": (c_size_t, []),
     "moe_route_noalloc": (c_int32, [POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_lossfree": (c_int32, [POINTER(MoeShape), _P, _P, _P, _P, c_float, _P, _P, _P, _P, _P, _P, _P,
+                                     c_size_t, _P]),
     "moe_stats": (c_int32, [c_int64, c_int32, c_int32, _P, _P, c_float, _P, _P, _P, _P, _P, _P, c_float, _P]),
     "moe_global_aux": (c_int32, [c_int32, _P, _P, _P, c_int32, c_float, _P, _P, _P, _P, c_float, c_float, _P, _P,
                                  _P]),

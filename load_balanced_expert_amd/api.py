@@ -140,6 +140,35 @@ def route(x: torch.Tensor, w_r: torch.Tensor, k: int, score: str = "softmax", ga
     return RouteOut(idx, g, counts, ps)
 
 
+def route_lossfree(x: torch.Tensor, w_r: torch.Tensor, k: int, bias: torch.Tensor, gamma: float,
+                   score: str = "sigmoid", gate: str = "prob", prob_sum: bool = True,
+                   global_counts: Optional[torch.Tensor] = None, global_tokens: Optional[torch.Tensor] = None,
+                   out: Optional[RouteOut] = None, w_planes: Optional[torch.Tensor] = None) -> RouteOut:
+    """One Loss-Free micro-batch step through moe_route_lossfree: route with `bias`, then update `bias`
+    in place (and add into global_counts / global_tokens when given) in the same launch; the results
+    equal route() followed by stats(..., bias=bias, gamma=gamma)."""
+    _on_device(x, w_r, bias, w_planes, global_counts, global_tokens)
+    if bias is None:
+        raise MoeError("route_lossfree needs the bias it updates")
+    m, d = x.shape
+    n = w_r.shape[1]
+    dev = x.device
+    sh = shape(m, d, n, k, score, gate, _dtype_code(x))
+    if out is not None:
+        idx, g, counts, ps = out.idx, out.gate, out.counts, out.prob_sum
+    else:
+        idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+        g = torch.empty((m, k), dtype=torch.float32, device=dev)
+        counts = torch.empty(n, dtype=torch.int32, device=dev)
+        ps = torch.empty(n, dtype=torch.float32, device=dev) if prob_sum else None
+    ws, wsb = _ws_args(workspace_size(sh), dev)
+    _check(_lib().moe_route_lossfree(ctypes.byref(sh), _ptr(x), _ptr(w_r), _ptr(w_planes), _ptr(bias),
+                                     float(gamma), _ptr(idx), _ptr(g), _ptr(counts), _ptr(ps),
+                                     _ptr(global_counts), _ptr(global_tokens), ws, wsb, _stream(dev)),
+           "moe_route_lossfree")
+    return RouteOut(idx, g, counts, ps)
+
+
 def route_noalloc(x: torch.Tensor, w_r: torch.Tensor, k: int, score: str = "softmax", gate: str = "prob",
                   bias: Optional[torch.Tensor] = None, prob_sum: bool = True, out: Optional[RouteOut] = None,
                   w_planes: Optional[torch.Tensor] = None) -> RouteOut:

@@ -128,6 +128,10 @@ struct RouteExtras {
   float alpha = 0.f;
   const DispatchArgs* disp = nullptr;   // capacity prefix sums for this dispatch
   bool defer_finish = false;            // chunk rows only; the dispatch derives everything else
+  int64_t* gcounts = nullptr;           // Loss-Free step in the finish (stand-alone route)
+  int64_t* gtokens = nullptr;
+  float* lf_bias = nullptr;
+  float gamma = 0.f;
 };
 
 moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const float* w_r, const void* w_planes,
@@ -168,6 +172,10 @@ moe_status do_route(const moe_shape& s, const Layout& L, const void* x, const fl
     a.padded = ex.disp->padded;
     a.super_prefix = ex.disp->super_prefix;
   }
+  a.gcounts = ex.gcounts;
+  a.gtokens = ex.gtokens;
+  a.lf_bias = ex.lf_bias;
+  a.gamma = ex.gamma;
   a.done = ctl_ticket(ws, kTicketRoute);
   a.kpart = at<float>(ws, L.kpart);
   a.tile_tickets = at<uint32_t>(ws, kTileTicketsOff);
@@ -321,6 +329,26 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, co
   if (!ws_ok(ws, ws_bytes, L.route_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
   return do_route(*shape, L, x, w_r, w_planes, bias, idx, gate, counts, prob_sum, ws,
                   static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_route_lossfree(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
+                              float* bias, float gamma, int32_t* idx, float* gate, int32_t* counts, float* prob_sum,
+                              int64_t* global_counts, int64_t* global_tokens, void* ws, size_t ws_bytes,
+                              void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !w_r || !bias || !idx || !gate || !counts || !isfinite(gamma) ||
+      (global_counts == nullptr) != (global_tokens == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(*shape, -1, 0);
+  if (!ws_ok(ws, ws_bytes, L.route_end)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  RouteExtras ex;
+  ex.gcounts = global_counts;
+  ex.gtokens = global_tokens;
+  ex.lf_bias = bias;
+  ex.gamma = gamma;
+  return do_route(*shape, L, x, w_r, w_planes, bias, idx, gate, counts, prob_sum, ws,
+                  static_cast<hipStream_t>(stream), ex);
 }
 
 size_t moe_route_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }

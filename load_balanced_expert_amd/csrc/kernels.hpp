@@ -62,6 +62,11 @@ struct RouteArgs {
   int32_t* sup_counts;            // finish == false or fin_super: per-super-chunk sums (atomics)
   unsigned long long* sup_psum;
   bool fin_super;                 // finish from the per-super-chunk sums (n <= 256), not the chunk rows
+  // the Loss-Free step done by the finish (stand-alone route only; all optional)
+  int64_t* gcounts;               // [n] global-batch counts += counts
+  int64_t* gtokens;               // [1] global-batch tokens += m
+  float* lf_bias;                 // [n] the bias, updated in place after it was used to route
+  float gamma;
 };
 hipError_t launch_route(const RoutePlan& plan, const RouteArgs& a, hipStream_t s);
 int route_chunk_tokens(const RoutePlan& plan);  // tokens per route workgroup (= dispatch chunk)

@@ -64,7 +64,27 @@ struct FinalizeArgs {
   int32_t* super_prefix;        // [ceil(nch / sup), n]
   int32_t* expert_rows;         // [n] kept rows per expert, or nullptr
   bool padded;                  // capacity-padded layout: expert j starts at row j * capacity
+  // the Loss-Free step of the same micro-batch, fused into the finish (all optional)
+  int k;                        // picks per token
+  int64_t* gcounts;             // [n] global-batch counts += counts
+  int64_t* gtokens;             // [1] global-batch tokens += m
+  float* lf_bias;               // [n] b_j -= gamma * sign(counts_j * n - m * k), in place
+  float gamma;
 };
+
+// Global-batch accumulation and the Loss-Free bias step for expert j with count c, as the
+// statistics kernel does them ([MoE tour 6] "방법 회고" eq. (2): b_j moves against the sign of
+// F_j - 1/n, i.e. of c·n - m·k; [Qwen global] "글로벌-배치 로드 밸런스 구현": counts summed over
+// the micro-batches).  The finishing workgroup runs after every workgroup of the launch has read
+// the bias, so the in-place update races with none of them.
+__device__ __forceinline__ void lossfree_step(const FinalizeArgs& a, int j, int c) {
+  if (a.gcounts) a.gcounts[j] += c;
+  if (a.lf_bias) {
+    const int64_t diff = int64_t(c) * a.n - a.m * a.k;
+    const float sgn = diff > 0 ? 1.f : (diff < 0 ? -1.f : 0.f);
+    a.lf_bias[j] = a.lf_bias[j] - a.gamma * sgn;
+  }
+}
 
 // Exclusive scan of v[0..n) held in LDS by one workgroup into out[0..n];
 // fixed order, deterministic.  part: LDS of threads/64 ints.
@@ -162,6 +182,7 @@ __device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds,
       }
       tot[j] = run;
       if (a.counts) a.counts[j] = run;
+      lossfree_step(a, j, run);
       if (a.prob_sum) a.prob_sum[j] = ps;
       if (a.f) a.f[j] = float(run) / float(a.m);
       if (a.P) a.P[j] = ps / float(a.m);
@@ -169,6 +190,7 @@ __device__ __forceinline__ void finalize_chunks(const FinalizeArgs& a, int* lds,
     }
     __syncthreads();
   }
+  if (a.gtokens && threadIdx.x == 0) a.gtokens[0] += a.m;
   if (a.aux) {
     double v = wave_sum_f64(auxp);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -230,11 +252,13 @@ __device__ __forceinline__ void finalize_super(const FinalizeArgs& a, int32_t* s
     const float psf = float(double(ps) / double(kPsumScale));
     tot[j] = run;
     if (a.counts) a.counts[j] = run;
+    lossfree_step(a, j, run);
     if (a.prob_sum) a.prob_sum[j] = psf;
     if (a.f) a.f[j] = float(run) / float(a.m);
     if (a.P) a.P[j] = psf / float(a.m);
     auxp += (double(run) / dm) * (double(psf) / dm);
   }
+  if (a.gtokens && threadIdx.x == 0) a.gtokens[0] += a.m;
   if (a.aux) {
     double v = wave_sum_f64(auxp);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;

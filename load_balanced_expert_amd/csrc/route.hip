@@ -651,6 +651,11 @@ __device__ __forceinline__ void route_finish(const RouteArgs& a, const EpiArgs& 
   f.super_prefix = a.super_prefix;
   f.expert_rows = a.expert_rows;
   f.padded = a.padded;
+  f.k = e.k;
+  f.gcounts = a.gcounts;
+  f.gtokens = a.gtokens;
+  f.lf_bias = a.lf_bias;
+  f.gamma = a.gamma;
   if constexpr (SUPER)
     finalize_super(f, a.sup_counts, a.sup_psum, a.want_psum, scratch, kRouteThreads);
   else

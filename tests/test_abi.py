@@ -117,6 +117,28 @@ def test_null_pointers_rejected(lib):
     assert lib.moe_combine(ctypes.byref(sh), FAKE, 7, FAKE, FAKE, None, FAKE, None) == 1
 
 
+def test_route_lossfree_validation(lib):
+    sh = _sh()
+    big = 1 << 30
+    ok = lambda **kw: dict(dict(x=FAKE, bias=FAKE, gamma=1e-3, gc=None, gt=None, ws=FAKE, wsb=big), **kw)  # noqa
+
+    def call(a):
+        return lib.moe_route_lossfree(ctypes.byref(sh), a["x"], FAKE, None, a["bias"], a["gamma"], FAKE, FAKE, FAKE,
+                                      None, a["gc"], a["gt"], a["ws"], a["wsb"], None)
+
+    assert call(ok(bias=None)) == L.MOE_ERR_INVALID_ARG          # the bias it updates is required
+    assert call(ok(x=None)) == L.MOE_ERR_INVALID_ARG
+    assert call(ok(gamma=float("nan"))) == L.MOE_ERR_INVALID_ARG
+    assert call(ok(gamma=float("inf"))) == L.MOE_ERR_INVALID_ARG
+    assert call(ok(gc=FAKE)) == L.MOE_ERR_INVALID_ARG            # global counts without global tokens
+    assert call(ok(gt=FAKE)) == L.MOE_ERR_INVALID_ARG
+    assert call(ok(wsb=1024)) == L.MOE_ERR_WORKSPACE
+    assert call(ok(ws=None)) == L.MOE_ERR_INVALID_ARG
+    bad = _sh(k=0)
+    assert lib.moe_route_lossfree(ctypes.byref(bad), FAKE, FAKE, None, FAKE, 1e-3, FAKE, FAKE, FAKE, None, None,
+                                  None, FAKE, big, None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_workspace_too_small_or_misaligned(lib):
     sh = _sh(m=1024, d=768, n=128)
     need = lib.moe_workspace_size(ctypes.byref(sh), -1, 0)

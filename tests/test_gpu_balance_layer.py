@@ -407,20 +407,27 @@ def test_layer_maps_equal_separate_calls():
     assert torch.equal(o2.token_to_row, o.token_to_row) and torch.equal(o2.dispatched[filled], o.dispatched[filled])
 
 
-def _lossfree_loop(spec, inp, batches, bias, gc, gt, b_in=None):
-    """Route micro-batches [batches] with the running bias on the GPU, each followed by moe_stats
-    (global counts, bias update).  Each micro-batch is checked against the oracle routed with the
-    bias the GPU held before it (so a near-tie flip in one micro-batch cannot cascade), and the
-    GPU's bias update against the oracle's update from the GPU's counts.  Returns the number of
-    near-tie flips."""
+def _lossfree_step(spec, x_dev, w_dev, bias, gc, gt, fused):
+    """One Loss-Free micro-batch: the single fused call, or route followed by moe_stats."""
+    if fused:
+        return M.route_lossfree(x_dev, w_dev, spec.k, bias, spec.gamma, global_counts=gc, global_tokens=gt)
+    r = M.route(x_dev, w_dev, spec.k, score="sigmoid", bias=bias)
+    M.stats(spec.T, spec.k, r.counts, r.prob_sum, global_counts=gc, global_tokens=gt, bias=bias, gamma=spec.gamma)
+    return r
+
+
+def _lossfree_loop(spec, inp, batches, bias, gc, gt, b_in=None, fused=False):
+    """Route micro-batches [batches] with the running bias on the GPU, each followed by the bias
+    update and global counts (moe_stats, or in the same launch with fused=True).  Each micro-batch
+    is checked against the oracle routed with the bias the GPU held before it (so a near-tie flip
+    in one micro-batch cannot cascade), and the GPU's bias update against the oracle's update from
+    the GPU's counts.  Returns the number of near-tie flips."""
     w_dev = to_dev(inp.w_r)
     b_prev = to_host(bias).copy() if b_in is None else b_in
     nflips = 0
     for t in batches:
         x = inp.micro_batch(t)
-        r = M.route(to_dev(x), w_dev, spec.k, score="sigmoid", bias=bias)
-        M.stats(spec.T, spec.k, r.counts, r.prob_sum, global_counts=gc, global_tokens=gt, bias=bias,
-                gamma=spec.gamma)
+        r = _lossfree_step(spec, to_dev(x), w_dev, bias, gc, gt, fused)
         torch.cuda.synchronize()
         ref = OR.route(x, inp.w_r, spec.k, score="sigmoid", bias=b_prev)
         gidx = to_host(r.idx)
@@ -438,16 +445,19 @@ def _lossfree_loop(spec, inp, batches, bias, gc, gt, b_in=None):
     return nflips
 
 
-def test_lossfree_micro_batch_loop():
+@pytest.mark.parametrize("fused", [False, True])
+def test_lossfree_micro_batch_loop(fused):
     """16 micro-batches: route with the old bias, accumulate global counts, then update the
-    bias.  Without near-tie flips the GPU's bias chain and global counts equal the oracle's own
-    chain; with them, each step is still checked on the GPU's inputs (stage isolation)."""
+    bias (route + moe_stats, or moe_route_lossfree alone).  Without near-tie flips the GPU's bias
+    chain and global counts equal the oracle's own chain; with them, each step is still checked
+    on the GPU's inputs (stage isolation)."""
     spec = W.LOSSFREE
     inp = W.lossfree_inputs(spec, 0)
+    say(f"[lossfree] 16 micro-batches fused={fused}")
     bias = torch.zeros(spec.N, dtype=torch.float32, device=DEV)
     gc = torch.zeros(spec.N, dtype=torch.int64, device=DEV)
     gt = torch.zeros(1, dtype=torch.int64, device=DEV)
-    nflips = _lossfree_loop(spec, inp, range(spec.micro_batches), bias, gc, gt)
+    nflips = _lossfree_loop(spec, inp, range(spec.micro_batches), bias, gc, gt, fused=fused)
     assert to_host(gt)[0] == spec.T * spec.micro_batches
     assert to_host(gc).sum() == spec.T * spec.k * spec.micro_batches
     if nflips == 0:   # the pure oracle chain, start to end
@@ -459,6 +469,38 @@ def test_lossfree_micro_batch_loop():
             b_ref = OS.lossfree_update(b_ref, ref.counts, spec.T, spec.k, spec.gamma)
         assert np.array_equal(to_host(bias), b_ref)
         assert np.array_equal(to_host(gc), gb.counts)
+
+
+@pytest.mark.parametrize("T,d,N,k,globals_", [(4096, 2048, 256, 8, True), (1000, 256, 64, 6, True),
+                                               (777, 128, 512, 8, True), (4096, 2048, 256, 8, False)])
+def test_route_lossfree_equals_route_then_stats(T, d, N, k, globals_):
+    """moe_route_lossfree does in the route's last workgroup what moe_stats does after it: over
+    12 micro-batches the two chains agree bit for bit in picks, gates, counts, expert
+    probability sums, bias and global counts.  N=512 takes the row kernel's finish instead of
+    the fused kernel's."""
+    spec = W.LOSSFREE.scaled(T=T, d=d, N=N, k=k, w_r_std=0.1 / np.sqrt(d))
+    inp = W.lossfree_inputs(spec, 2)
+    w_dev = to_dev(inp.w_r)
+    say(f"[lossfree] fused vs route+stats T={T} d={d} N={N} k={k} globals={globals_}")
+    state = []
+    for _ in range(2):
+        b = torch.zeros(N, dtype=torch.float32, device=DEV)
+        g = torch.zeros(N, dtype=torch.int64, device=DEV) if globals_ else None
+        t = torch.zeros(1, dtype=torch.int64, device=DEV) if globals_ else None
+        state.append((b, g, t))
+    for step in range(12):
+        x = to_dev(inp.micro_batch(step))
+        r0 = _lossfree_step(spec, x, w_dev, *state[0], fused=False)
+        r1 = _lossfree_step(spec, x, w_dev, *state[1], fused=True)
+        torch.cuda.synchronize()
+        for name in ("idx", "gate", "counts", "prob_sum"):
+            assert torch.equal(getattr(r0, name), getattr(r1, name)), f"step {step}: {name}"
+        assert torch.equal(state[0][0], state[1][0]), f"step {step}: bias"
+        if globals_:
+            assert torch.equal(state[0][1], state[1][1]) and torch.equal(state[0][2], state[1][2])
+    assert float(state[1][0].abs().max()) > 0          # the bias moved
+    if globals_:
+        assert int(state[1][2][0]) == 12 * T and int(state[1][1].sum()) == 12 * T * k
 
 
 def test_lossfree_resume_is_bit_identical():
