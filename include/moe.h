@@ -203,7 +203,9 @@ moe_status moe_stats(int64_t m, int32_t n, int32_t k, const int32_t* counts, con
  * the incoming value, holds the updated one afterwards); gamma: the update
  * rate; global_counts [n] int64 in/out and global_tokens [1] int64 in/out, both
  * or neither.  Results (idx, gate, counts, prob_sum, bias, global counts) are
- * bit-identical to moe_route followed by moe_stats.  Limits as moe_route. */
+ * bit-identical to moe_route followed by moe_stats.  Limits as moe_route.
+ * Errors: MOE_ERR_INVALID_ARG for a missing bias, a non-finite gamma or only
+ * one of the two global pointers (nothing is launched); otherwise as moe_route. */
 moe_status moe_route_lossfree(const moe_shape* shape, const void* x, const float* w_r, const void* w_planes,
                               float* bias, float gamma, int32_t* idx, float* gate, int32_t* counts,
                               float* prob_sum, int64_t* global_counts, int64_t* global_tokens, void* ws,
