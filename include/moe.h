@@ -376,6 +376,15 @@ typedef struct {
    * capacity prefix sums), [3] dispatched, [4] expert done, [5] combined.
    * Any entry may be NULL. */
   void* const* stage_events;
+  /* Loss-Free ([MoE tour 6] eqs. (1)-(2)): NULL, or the layer's `bias` argument
+   * itself, which the layer then updates in place once this batch is routed,
+   * b_j <- b_j - gamma * sign(c_j * n - m * k), as moe_stats would after it. */
+  float* update_bias;
+  float gamma;
+  /* NULL, or [n] / [1] int64 in/out: the global-batch counts and tokens
+   * ([Qwen global] "글로벌-배치 로드 밸런스 구현"), both or neither. */
+  int64_t* global_counts;
+  int64_t* global_tokens;
 } moe_layer_params;
 
 /* Device output pointers of moe_switch_layer.  `out` is required; every other

@@ -25,7 +25,8 @@ class MoeShape(ctypes.Structure):
 
 class LayerParams(ctypes.Structure):
     _fields_ = [("capacity", c_int32), ("expert_kind", c_int32), ("d_ff", c_int32), ("alpha", c_float),
-                ("stage_events", POINTER(c_void_p))]
+                ("stage_events", POINTER(c_void_p)), ("update_bias", c_void_p), ("gamma", c_float),
+                ("global_counts", c_void_p), ("global_tokens", c_void_p)]
 
 
 class LayerOutputs(ctypes.Structure):

@@ -428,10 +428,16 @@ def allocate_layer_outputs(m, d, n, k, rows_bound, x_dtype, ffn: bool, device, d
 def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int = -1, alpha: float = 1e-2,
                  w1: Optional[torch.Tensor] = None, w2: Optional[torch.Tensor] = None,
                  bias: Optional[torch.Tensor] = None, score: str = "softmax", gate: str = "prob",
-                 outputs: Optional[LayerOut] = None, stage_events=None) -> LayerOut:
+                 outputs: Optional[LayerOut] = None, stage_events=None, update_bias: bool = False,
+                 gamma: float = 1e-3, global_counts: Optional[torch.Tensor] = None,
+                 global_tokens: Optional[torch.Tensor] = None) -> LayerOut:
     """stage_events: optional list of 6 torch.cuda.Event (timing enabled) recorded at the stage
-    boundaries (start, router prepared, routed, dispatched, expert done, combined)."""
-    _on_device(x, w_r, w1, w2, bias)
+    boundaries (start, router prepared, routed, dispatched, expert done, combined).
+    update_bias: the layer routes with `bias`, then updates it in place (Loss-Free, rate gamma);
+    global_counts / global_tokens (int64, both or neither) accumulate the global batch."""
+    _on_device(x, w_r, w1, w2, bias, global_counts, global_tokens)
+    if update_bias and bias is None:
+        raise MoeError("update_bias needs the bias it updates")
     m, d = x.shape
     n = w_r.shape[1]
     dev = x.device
@@ -451,7 +457,9 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
         evs = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None
                                       for e in stage_events])
     params = L.LayerParams(int(capacity), L.EXPERTS["relu_ffn" if ffn else "identity"], int(d_ff), float(alpha),
-                           ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p)) if evs is not None else None)
+                           ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p)) if evs is not None else None,
+                           _ptr(bias) if update_bias else None, float(gamma), _ptr(global_counts),
+                           _ptr(global_tokens))
     ws, wsb = _ws_args(workspace_size(sh, capacity, d_ff), dev)
     _check(_lib().moe_switch_layer(ctypes.byref(sh), ctypes.byref(params), _ptr(x), _ptr(w_r), _ptr(w1), _ptr(w2),
                                    _ptr(bias), ctypes.byref(lo), ws, wsb, _stream(dev)), "moe_switch_layer")

@@ -547,6 +547,9 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   if (!ffn && p->expert_kind != MOE_EXPERT_IDENTITY) return MOE_ERR_INVALID_ARG;
   if (ffn && (!w1 || !w2 || p->d_ff < 1 || shape->x_dtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
   if (ffn && (shape->d % 32 != 0 || p->d_ff % 32 != 0)) return MOE_ERR_UNSUPPORTED;
+  // the bias the layer updates is the one it routes with, after the routing
+  if (p->update_bias && (p->update_bias != bias || !isfinite(p->gamma))) return MOE_ERR_INVALID_ARG;
+  if ((p->global_counts == nullptr) != (p->global_tokens == nullptr)) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape, p->capacity, ffn ? p->d_ff : 0);
   if (!ws_ok(ws, ws_bytes, L.total)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -590,8 +593,18 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
     da.P = P;
     da.aux = aux;
     da.alpha = p->alpha;
-  } else if (fused_prefix) {
-    ex.disp = &da;
+    da.gcounts = p->global_counts;
+    da.gtokens = p->global_tokens;
+    da.lf_bias = p->update_bias;
+    da.gamma = p->gamma;
+  } else {
+    // the route's last workgroup publishes the statistics: it also takes the
+    // global-batch accumulation and the bias update
+    if (fused_prefix) ex.disp = &da;
+    ex.gcounts = p->global_counts;
+    ex.gtokens = p->global_tokens;
+    ex.lf_bias = p->update_bias;
+    ex.gamma = p->gamma;
   }
   mark(0);
   const void* planes = nullptr;   // else the route kernel splits W_r itself

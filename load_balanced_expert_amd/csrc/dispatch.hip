@@ -154,8 +154,17 @@ __device__ __forceinline__ void derive_prefix(const DispatchArgs& a, int c, Pref
       if (a.f) a.f[e] = float(tt) / float(m);
       if (a.P) a.P[e] = float(psum / double(m));
       auxp += (double(tt) / double(m)) * (psum / double(m));
+      // [Qwen global] global batch; [MoE tour 6] eq. (2): the sign of F_j - 1/n taken
+      // exactly as the sign of c_j n - m k, one fp32 step of the bias
+      if (a.gcounts) a.gcounts[e] += tt;
+      if (a.lf_bias) {
+        const int64_t diff = int64_t(tt) * n - m * a.k;
+        const float sgn = diff > 0 ? 1.f : (diff < 0 ? -1.f : 0.f);
+        a.lf_bias[e] = a.lf_bias[e] - a.gamma * sgn;
+      }
     }
   }
+  if (stats && a.gtokens && t == 0) a.gtokens[0] += a.pairs / a.k;
   if (stats && a.aux) {   // fixed-order fp64 sum over the experts
     __shared__ double red[kDispThreads / 64];
     const double v = wave_sum_f64(auxp);

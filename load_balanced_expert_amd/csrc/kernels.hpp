@@ -117,6 +117,12 @@ struct DispatchArgs {
   float* P;
   float* aux;
   float alpha;
+  // self_prefix, workgroup 0: global-batch accumulation and the Loss-Free bias
+  // update from the expert totals (nullptr: not wanted)
+  int64_t* gcounts;
+  int64_t* gtokens;
+  float* lf_bias;
+  float gamma;
 };
 constexpr int kDispMaxChunkPairs = 4096;
 // chunk tokens for m tokens x k choices given the route workgroup size

@@ -215,6 +215,28 @@ def test_switch_layer_validation(lib):
                                 ctypes.byref(out), FAKE, 1 << 40, None) == 1
 
 
+def test_switch_layer_lossfree_validation(lib):
+    sh = _sh(m=64, d=64, n=8, k=2, score=1, xd=0)
+    out = L.LayerOutputs()
+    out.out = FAKE
+    other = ctypes.c_void_p(0x2000)
+
+    def call(bias, **kw):
+        p = L.LayerParams(16, 0, 0, 0.01, None)
+        for key, v in kw.items():
+            setattr(p, key, v)
+        return lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, None, None, bias,
+                                    ctypes.byref(out), FAKE, 1 << 40, None)
+
+    assert call(FAKE, update_bias=other.value, gamma=1e-3) == L.MOE_ERR_INVALID_ARG   # not the routing bias
+    assert call(None, update_bias=FAKE.value, gamma=1e-3) == L.MOE_ERR_INVALID_ARG
+    assert call(FAKE, update_bias=FAKE.value, gamma=float("nan")) == L.MOE_ERR_INVALID_ARG
+    assert call(FAKE, global_counts=FAKE.value) == L.MOE_ERR_INVALID_ARG               # without global tokens
+    assert call(FAKE, global_tokens=FAKE.value) == L.MOE_ERR_INVALID_ARG
+    assert call(FAKE, update_bias=FAKE.value, gamma=1e-3, global_counts=FAKE.value, global_tokens=None) == \
+        L.MOE_ERR_INVALID_ARG
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(M.MoeError):

@@ -503,6 +503,39 @@ def test_route_lossfree_equals_route_then_stats(T, d, N, k, globals_):
         assert int(state[1][2][0]) == 12 * T and int(state[1][1].sum()) == 12 * T * k
 
 
+@pytest.mark.parametrize("m,d,n,k,cf", [(4096, 256, 64, 4, 1.25), (2048, 128, 512, 4, 1.25), (1000, 128, 512, 32, -1)])
+def test_switch_layer_lossfree_update(m, d, n, k, cf):
+    """moe_switch_layer with the Loss-Free update (bias, global counts and tokens) equals the
+    layer routed with the same bias followed by moe_stats, bit for bit, over 3 micro-batches:
+    n = 64 has the dispatch derive the statistics, n = 512 (k = 4) the route's finish with the
+    capacity prefix, n = 512 (k = 32) the route's finish before a separate dispatch histogram.
+    Each update also equals the oracle's from the GPU's counts."""
+    spec = W.LOSSFREE.scaled(T=m, d=d, N=n, k=k, w_r_std=0.1 / np.sqrt(d))
+    inp = W.lossfree_inputs(spec, 3)
+    w_dev = to_dev(inp.w_r)
+    cap = int(cf * m * k / n) if cf > 0 else -1
+    say(f"[lossfree] layer update m={m} d={d} n={n} k={k} capacity={cap}")
+    st = [(torch.zeros(n, dtype=torch.float32, device=DEV), torch.zeros(n, dtype=torch.int64, device=DEV),
+           torch.zeros(1, dtype=torch.int64, device=DEV)) for _ in range(2)]
+    for step in range(3):
+        x = to_dev(inp.micro_batch(step))
+        b_prev = to_host(st[0][0]).copy()
+        o1 = M.switch_layer(x, w_dev, k=k, capacity=cap, bias=st[0][0], score="sigmoid", update_bias=True,
+                            gamma=spec.gamma, global_counts=st[0][1], global_tokens=st[0][2])
+        o2 = M.switch_layer(x, w_dev, k=k, capacity=cap, bias=st[1][0], score="sigmoid")
+        M.stats(m, k, o2.counts, o2.prob_sum, global_counts=st[1][1], global_tokens=st[1][2], bias=st[1][0],
+                gamma=spec.gamma)
+        torch.cuda.synchronize()
+        for name in ("idx", "gate", "counts", "token_to_row", "out"):
+            assert torch.equal(getattr(o1, name), getattr(o2, name)), f"step {step}: {name}"
+        for u, v in zip(st[0], st[1]):
+            assert torch.equal(u, v), f"step {step}: Loss-Free state"
+        counts = to_host(o1.counts)
+        assert np.array_equal(to_host(st[0][0]), OS.lossfree_update(b_prev, counts, m, k, spec.gamma))
+    assert float(st[0][0].abs().max()) > 0
+    assert int(st[0][2][0]) == 3 * m and int(st[0][1].sum()) == 3 * m * k
+
+
 def test_lossfree_resume_is_bit_identical():
     """Checkpoint / resume: 16 micro-batches straight against 8, a host copy of the caller-owned
     state (bias, global counts, global tokens) restored into fresh buffers, then the other 8.
