@@ -196,12 +196,14 @@ def test_qb_online_routes_before_update():
 
 # (5, 8192, 64, 4) exceeds the LDS-resident form and takes the global-list kernel; n > 64 takes
 # two experts per lane (96: a partial second half)
-@pytest.mark.parametrize("iters,m,n,k", [(20, 4096, 64, 4), (5, 4096, 64, 4), (0, 512, 16, 2), (3, 12, 4, 2),
-                                         (5, 8192, 64, 4), (5, 2048, 128, 4), (3, 1536, 96, 2), (2, 2048, 128, 8)])
-def test_exact_completion_is_lp_optimum(iters, m, n, k):
+@pytest.mark.parametrize("iters,m,n,k,seed", [(20, 4096, 64, 4, 0), (5, 4096, 64, 4, 0), (5, 4096, 64, 4, 1),
+                                              (5, 4096, 64, 4, 2), (0, 512, 16, 2, 0), (3, 12, 4, 2, 0),
+                                              (5, 8192, 64, 4, 0), (5, 2048, 128, 4, 0), (3, 1536, 96, 2, 0),
+                                              (2, 2048, 128, 8, 0)])
+def test_exact_completion_is_lp_optimum(iters, m, n, k, seed):
     spec = W.BalancedSpec(m=m, n=n, k=k)
-    s = W.balanced_scores(spec, 0)
-    say(f"[qb] exact m={m} n={n} k={k} iters={iters}")
+    s = W.balanced_scores(spec, seed)
+    say(f"[qb] exact m={m} n={n} k={k} iters={iters} seed={seed}")
     beta = torch.zeros(n, dtype=torch.float32, device=DEV)
     out = M.balance_duals(to_dev(s), k, beta, iters=iters, exact=True)
     torch.cuda.synchronize()
@@ -351,13 +353,14 @@ def _layer_check(spec, seed, cf, ffn, k=1):
     return o
 
 
-def test_tiny_switch_layer():
-    _layer_check(W.TINY_SWITCH, 0, 1.25, ffn=False)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_switch_layer(seed):
+    _layer_check(W.TINY_SWITCH, seed, 1.25, ffn=False)
 
 
-@pytest.mark.parametrize("cf", [1.0, 1.25])
-def test_switch_base_layer_with_ffn(cf):
-    _layer_check(W.SWITCH_BASE, 0, cf, ffn=True)
+@pytest.mark.parametrize("cf,seed", [(1.0, 0), (1.25, 0), (1.25, 1), (1.25, 2)])
+def test_switch_base_layer_with_ffn(cf, seed):
+    _layer_check(W.SWITCH_BASE, seed, cf, ffn=True)
 
 
 def test_switch_base_layer_identity_ragged():
@@ -445,15 +448,15 @@ def _lossfree_loop(spec, inp, batches, bias, gc, gt, b_in=None, fused=False):
     return nflips
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_lossfree_micro_batch_loop(fused):
+@pytest.mark.parametrize("fused,seed", [(False, 0), (True, 0), (True, 1), (True, 2)])
+def test_lossfree_micro_batch_loop(fused, seed):
     """16 micro-batches: route with the old bias, accumulate global counts, then update the
     bias (route + moe_stats, or moe_route_lossfree alone).  Without near-tie flips the GPU's bias
     chain and global counts equal the oracle's own chain; with them, each step is still checked
     on the GPU's inputs (stage isolation)."""
     spec = W.LOSSFREE
-    inp = W.lossfree_inputs(spec, 0)
-    say(f"[lossfree] 16 micro-batches fused={fused}")
+    inp = W.lossfree_inputs(spec, seed)
+    say(f"[lossfree] 16 micro-batches fused={fused} seed={seed}")
     bias = torch.zeros(spec.N, dtype=torch.float32, device=DEV)
     gc = torch.zeros(spec.N, dtype=torch.int64, device=DEV)
     gt = torch.zeros(1, dtype=torch.int64, device=DEV)

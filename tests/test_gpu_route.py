@@ -49,8 +49,9 @@ def test_switch_base_ragged(seed):
     check_route(inp.x, inp.w_r, 1, "switch-base ragged T=1000 (bf16x3 MFMA)")
 
 
-def test_switch_base_full():
-    inp = W.switch_inputs(W.SWITCH_BASE, 0)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_switch_base_full(seed):
+    inp = W.switch_inputs(W.SWITCH_BASE, seed)
     check_route(inp.x, inp.w_r, 1, "switch-base T=8192 d=768 N=128")
 
 
@@ -187,13 +188,14 @@ def test_repeat_is_bitwise_deterministic():
         assert np.array_equal(u, v)
 
 
-def test_switch_c_full_size():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_switch_c_full_size(seed):
     """T=65536, d=1024, N=2048 at full size: the oracle routes every token (in blocks of 8192),
     so indices are checked on all tokens, gates on all but near-tie flips, counts against the
     oracle's and score sums against its full sums."""
     spec = W.SWITCH_C
-    inp = W.switch_inputs(spec, 0)
-    say("[route] switch-C full size on GPU")
+    inp = W.switch_inputs(spec, seed)
+    say(f"[route] switch-C full size on GPU, seed {seed}")
     idx, g, counts, psum = run_route(inp.x, inp.w_r, 1)
     psum_ref = np.zeros(spec.N)
     counts_ref = np.zeros(spec.N, np.int64)
