@@ -435,7 +435,8 @@ __device__ __forceinline__ void route_rows(const float* lg, int64_t ld, int rows
       int bj = 0x7FFFFFFF;
       for (int j = lane; j < n; j += 64) {
         const float h = row[j];
-        const float key = e.bias ? score_of(e.score, h, mx, sum) + e.bias[j] : h;
+        const float k0 = e.bias ? score_of(e.score, h, mx, sum) + e.bias[j] : h;
+        const float key = k0 == k0 ? k0 : -INFINITY;   // NaN ranks as -inf (the order of the integer keys)
         if (better(last_key, last_j, key, j) && better(key, j, bk, bj)) {
           bk = key;
           bj = j;
@@ -496,7 +497,10 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
 #pragma unroll
       for (int u = NV - 1; u >= 0; --u)
         if (l + 32 * u < e.n && h[u] == mx) cand = l + 32 * u;
-      const int bj = half_min_i(cand);
+      // no expert holds the maximum only when every logit is NaN: NaN ranks as -inf, so all
+      // tie and the lowest expert is picked (indices stay in [0, n) for any input)
+      int bj = half_min_i(cand);
+      bj = bj < e.n ? bj : 0;
       float sum = 0.f;
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
@@ -505,7 +509,7 @@ __device__ __forceinline__ void route_rows_half(float* lg, int ld, int rows, int
       }
       const float inv = __builtin_amdgcn_rcpf(half_sum(sum));   // sum >= 1 (the maximum's term is 1)
       if (l == 0) {
-        if (bj < e.n) atomicAdd(&hist[bj], 1);   // out of range only for a row without a finite maximum
+        atomicAdd(&hist[bj], 1);
         idx[t0 + tl] = bj;
         gate_out[t0 + tl] = e.gate == 1 ? 1.0f : inv;
       }
@@ -946,7 +950,10 @@ __device__ __forceinline__ void route_rows_top1(float* lg, int ld, int rows, int
     int cand = 0x7FFFFFFF;
 #pragma unroll 8
     for (int u = 0; u < nv; ++u) cand = min(cand, row[lane + 64 * u] == mx ? lane + 64 * u : 0x7FFFFFFF);
-    const int bj = wave_min_i_dpp(cand);
+    // a padded expert or none holds the maximum only when every logit is NaN: NaN ranks as
+    // -inf, so all tie and the lowest expert is picked
+    int bj = wave_min_i_dpp(cand);
+    bj = bj < e.n ? bj : 0;
     float s = 0.f;
 #pragma unroll 8
     for (int u = 0; u < nv; ++u) {
@@ -958,7 +965,7 @@ __device__ __forceinline__ void route_rows_top1(float* lg, int ld, int rows, int
     if (lane == 0) {
       tok_mx[tl] = mx;
       tok_sum[tl] = sum;
-      if (bj < e.n) atomicAdd(&hist[bj], 1);   // out of range only for a row without a finite maximum
+      atomicAdd(&hist[bj], 1);
       idx[t0 + tl] = bj;
       gate_out[t0 + tl] = e.gate == 1 ? 1.0f : __builtin_amdgcn_rcpf(sum);   // sum >= 1
     }

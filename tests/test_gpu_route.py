@@ -212,3 +212,26 @@ def test_switch_c_full_size(seed):
     if nflips == 0:
         assert np.array_equal(counts, counts_ref)
     assert_rel(psum, psum_ref, 1e-5, "switch-C prob_sum")
+
+
+@pytest.mark.parametrize("n,k,score,bias,d", [(128, 1, "softmax", False, 768), (256, 8, "sigmoid", True, 256),
+                                              (64, 40, "softmax", False, 64), (600, 1, "softmax", False, 128),
+                                              (600, 3, "softmax", False, 128)])
+def test_nan_rows_keep_indices_in_range(n, k, score, bias, d):
+    # NaN inputs are outside the numerical contract, but indices stay in [0, n): NaN ranks as -inf,
+    # so a row whose logits are all NaN picks experts 0..k-1; every other row routes as it does
+    # without the NaN rows (tokens are routed independently), and counts follow the indices
+    spec = W.SwitchSpec("nanrows", T=300, d=d, N=n, w_r_std=0.05)
+    inp = W.switch_inputs(spec, 21)
+    b = (np.random.default_rng(3).standard_normal(n) * 0.01).astype(np.float32) if bias else None
+    say(f"[route] NaN rows: n={n} k={k} {score} bias={'yes' if bias else 'no'} d={d}")
+    clean = run_route(inp.x, inp.w_r, k, score=score, bias=b)
+    x = inp.x.copy()
+    nan_rows = [0, 5, 31, 32, 299]
+    x[nan_rows] = np.uint16(0x7FC0)   # bf16 quiet NaN
+    idx, _, counts, _ = run_route(x, inp.w_r, k, score=score, bias=b)
+    assert idx.min() >= 0 and idx.max() < n
+    keep = np.setdiff1d(np.arange(spec.T), nan_rows)
+    assert np.array_equal(idx[keep], clean[0][keep])
+    assert np.all(idx[nan_rows] == np.arange(k)[None, :])
+    assert np.array_equal(counts, np.bincount(idx.reshape(-1), minlength=n))
