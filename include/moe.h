@@ -350,6 +350,18 @@ moe_status moe_expert_ffn(int32_t n, int32_t d, int32_t d_ff, int32_t rows_max,
                           const void* w1, const void* w2, void* y,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* moe_expert_weights_pack — for callers that keep the expert weights fixed across many
+ * layer calls (inference, or the micro-batches between two weight updates): rewrites
+ * an [n][rows][cols] bf16 weight tensor in the Linear layout (w1: rows = d_ff,
+ * cols = d; w2: rows = d, cols = d_ff) into the order in which the FFN's
+ * weight-stream kernel consumes it as matrix-core operands, so that each wave reads
+ * its weights as one contiguous run.  Same values and size (n * rows * cols bf16);
+ * the FFN computes bit-identical outputs from either layout.  w and w_packed are
+ * distinct caller buffers, 16-byte aligned.  rows % 32 == 0 and cols % 64 == 0, else
+ * MOE_ERR_UNSUPPORTED. */
+moe_status moe_expert_weights_pack(int32_t n, int32_t rows, int32_t cols, const void* w, void* w_packed,
+                                   void* stream);
+
 /* ------------------------------------------------------------------ combine */
 
 /* moe_combine — inverse permute, gate scaling and residual:
@@ -385,6 +397,10 @@ typedef struct {
    * ([Qwen global] "글로벌-배치 로드 밸런스 구현"), both or neither. */
   int64_t* global_counts;
   int64_t* global_tokens;
+  /* Nonzero: w1 and w2 are in moe_expert_weights_pack's layout (relu_ffn only; the
+   * layer returns MOE_ERR_UNSUPPORTED where its FFN cannot read that layout:
+   * d % 256, d_ff % 256 or the rows bound).  The backward takes the plain layout. */
+  int32_t weights_packed;
 } moe_layer_params;
 
 /* Device output pointers of moe_switch_layer.  `out` is required; every other

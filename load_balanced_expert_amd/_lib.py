@@ -26,7 +26,7 @@ class MoeShape(ctypes.Structure):
 class LayerParams(ctypes.Structure):
     _fields_ = [("capacity", c_int32), ("expert_kind", c_int32), ("d_ff", c_int32), ("alpha", c_float),
                 ("stage_events", POINTER(c_void_p)), ("update_bias", c_void_p), ("gamma", c_float),
-                ("global_counts", c_void_p), ("global_tokens", c_void_p)]
+                ("global_counts", c_void_p), ("global_tokens", c_void_p), ("weights_packed", c_int32)]
 
 
 class LayerOutputs(ctypes.Structure):
@@ -72,6 +72,7 @@ SIGNATURES = {
                                       _P]),
     "moe_dispatch": (c_int32, [POINTER(MoeShape), c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_expert_ffn": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_expert_weights_pack": (c_int32, [c_int32, c_int32, c_int32, _P, _P, _P]),
     "moe_combine": (c_int32, [POINTER(MoeShape), _P, c_int32, _P, _P, _P, _P, _P]),
     "moe_switch_layer": (c_int32, [POINTER(MoeShape), POINTER(LayerParams), _P, _P, _P, _P, _P,
                                    POINTER(LayerOutputs), _P, c_size_t, _P]),

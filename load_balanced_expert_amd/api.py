@@ -375,6 +375,19 @@ def expert_ffn(dispatched: torch.Tensor, expert_offsets: torch.Tensor, w1: torch
     return y
 
 
+def pack_expert_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[n, rows, cols] bf16 expert weights (w1 or w2, Linear layout) rewritten in the order the FFN's
+    weight-stream kernel reads them (moe_expert_weights_pack); same shape and values."""
+    _on_device(w)
+    if w.dtype != torch.bfloat16 or w.dim() != 3 or not w.is_contiguous():
+        raise MoeError("pack_expert_weights takes a contiguous [n, rows, cols] bf16 tensor")
+    n, rows, cols = w.shape
+    p = out if out is not None else torch.empty_like(w)
+    _check(_lib().moe_expert_weights_pack(int(n), int(rows), int(cols), _ptr(w), _ptr(p), _stream(w.device)),
+           "moe_expert_weights_pack")
+    return p
+
+
 # ------------------------------------------------------------------ combine
 def combine(y: torch.Tensor, gate: torch.Tensor, token_to_row: torch.Tensor, residual: Optional[torch.Tensor],
             out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -430,11 +443,12 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
                  bias: Optional[torch.Tensor] = None, score: str = "softmax", gate: str = "prob",
                  outputs: Optional[LayerOut] = None, stage_events=None, update_bias: bool = False,
                  gamma: float = 1e-3, global_counts: Optional[torch.Tensor] = None,
-                 global_tokens: Optional[torch.Tensor] = None) -> LayerOut:
+                 global_tokens: Optional[torch.Tensor] = None, weights_packed: bool = False) -> LayerOut:
     """stage_events: optional list of 6 torch.cuda.Event (timing enabled) recorded at the stage
     boundaries (start, router prepared, routed, dispatched, expert done, combined).
     update_bias: the layer routes with `bias`, then updates it in place (Loss-Free, rate gamma);
-    global_counts / global_tokens (int64, both or neither) accumulate the global batch."""
+    global_counts / global_tokens (int64, both or neither) accumulate the global batch.
+    weights_packed: w1 and w2 come from pack_expert_weights (same shapes, packed order)."""
     _on_device(x, w_r, w1, w2, bias, global_counts, global_tokens)
     if update_bias and bias is None:
         raise MoeError("update_bias needs the bias it updates")
@@ -459,7 +473,7 @@ def switch_layer(x: torch.Tensor, w_r: torch.Tensor, k: int = 1, capacity: int =
     params = L.LayerParams(int(capacity), L.EXPERTS["relu_ffn" if ffn else "identity"], int(d_ff), float(alpha),
                            ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p)) if evs is not None else None,
                            _ptr(bias) if update_bias else None, float(gamma), _ptr(global_counts),
-                           _ptr(global_tokens))
+                           _ptr(global_tokens), int(bool(weights_packed)))
     ws, wsb = _ws_args(workspace_size(sh, capacity, d_ff), dev)
     _check(_lib().moe_switch_layer(ctypes.byref(sh), ctypes.byref(params), _ptr(x), _ptr(w_r), _ptr(w1), _ptr(w2),
                                    _ptr(bias), ctypes.byref(lo), ws, wsb, _stream(dev)), "moe_switch_layer")

@@ -513,6 +513,15 @@ size_t moe_expert_ffn_workspace_size(int32_t n, int32_t rows_max, int32_t d_ff) 
   return kControlBytes + al(ffn_ws_bytes(int64_t(n) * rows_max, d_ff));
 }
 
+moe_status moe_expert_weights_pack(int32_t n, int32_t rows, int32_t cols, const void* w, void* w_packed,
+                                   void* stream) {
+  if (n < 1 || rows < 1 || cols < 1 || !w || !w_packed || w == w_packed) return MOE_ERR_INVALID_ARG;
+  if (rows % 32 != 0 || cols % 64 != 0 || n > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(w_packed)) % 16 != 0) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack_weights(n, rows, cols, static_cast<const uint16_t*>(w),
+                                        static_cast<uint16_t*>(w_packed), static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_expert_ffn(int32_t n, int32_t d, int32_t d_ff, int32_t rows_max, const int32_t* expert_offsets,
                           const int32_t* expert_rows, const void* dispatched, const void* w1, const void* w2, void* y,
                           void* ws, size_t ws_bytes, void* stream) {
@@ -547,11 +556,16 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
   if (!ffn && p->expert_kind != MOE_EXPERT_IDENTITY) return MOE_ERR_INVALID_ARG;
   if (ffn && (!w1 || !w2 || p->d_ff < 1 || shape->x_dtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
   if (ffn && (shape->d % 32 != 0 || p->d_ff % 32 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (p->weights_packed && !ffn) return MOE_ERR_INVALID_ARG;
   // the bias the layer updates is the one it routes with, after the routing
   if (p->update_bias && (p->update_bias != bias || !isfinite(p->gamma))) return MOE_ERR_INVALID_ARG;
   if ((p->global_counts == nullptr) != (p->global_tokens == nullptr)) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape, p->capacity, ffn ? p->d_ff : 0);
   if (!ws_ok(ws, ws_bytes, L.total)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  if (p->weights_packed &&
+      (!ffn_packed_ok(shape->d, p->d_ff, effective_capacity(p->capacity, L.pairs), shape->n) ||
+       (reinterpret_cast<uintptr_t>(w1) | reinterpret_cast<uintptr_t>(w2)) % 16 != 0))
+    return MOE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe_shape& sh = *shape;
   int32_t* idx = o->idx ? o->idx : at<int32_t>(ws, L.idx);
@@ -631,7 +645,7 @@ moe_status moe_switch_layer(const moe_shape* shape, const moe_layer_params* p, c
                                            static_cast<const uint16_t*>(disp),
                                            static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
                                            o->hidden ? static_cast<uint16_t*>(o->hidden) : at<uint16_t>(ws, L.hidden),
-                                           static_cast<uint16_t*>(y), s))) != MOE_OK)
+                                           static_cast<uint16_t*>(y), s, p->weights_packed != 0))) != MOE_OK)
       return fail(st);
   }
   mark(4);
@@ -662,7 +676,8 @@ moe_status moe_switch_layer_backward(const moe_shape* shape, const moe_layer_par
   if (!sv->idx || !sv->gate || !sv->counts || !sv->token_to_row || !sv->expert_offsets || !sv->dispatched ||
       !sv->hidden || !sv->y || !gr->dx || !gr->dw_r || !gr->dw1 || !gr->dw2)
     return MOE_ERR_INVALID_ARG;
-  if (p->expert_kind != MOE_EXPERT_RELU_FFN || shape->x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->expert_kind != MOE_EXPERT_RELU_FFN || shape->x_dtype != MOE_BF16 || p->weights_packed)
+    return MOE_ERR_INVALID_ARG;
   if (shape->score != MOE_SCORE_SOFTMAX || shape->gate != MOE_GATE_PROB) return MOE_ERR_UNSUPPORTED;
   if (shape->d % 32 != 0 || p->d_ff % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!ws_ok(ws, ws_bytes, moe_switch_layer_backward_workspace_size(shape, p->capacity, p->d_ff)))

@@ -123,7 +123,16 @@ constexpr int kFfnLdA = kFfnKA + 8;    // LDS row stride (bf16), 16 bytes of pad
 constexpr int kFfnLdB = 72;            // per-wave weight slab row stride (bf16): 64 + 16 bytes of padding
 constexpr int kFfnRing = 4;            // weight K steps in flight + 1 (even)
 
-template <int W, int MT, bool RELU>   // W waves per workgroup, 32 output columns each
+// Packed weights (PACKED): an expert's [N][K] matrix stored as the MFMA B fragments this kernel
+// feeds, in the order it reads them: for 32-row block rb, K step s (64 inputs) and fragment q,
+// the 64 lanes' 8 bf16 are contiguous (1 KiB), lane l = r + 32 h holding row 32 rb + r, inputs
+// 64 s + 32 h + 8 q + [0, 8).  A wave's weight step is then four contiguous 1 KiB loads that are
+// already fragments, and its 32 rows stream as one contiguous run (moe_expert_weights_pack).
+__host__ __device__ inline size_t packed_frag_off(int64_t e, int rb, int s, int q, int N, int K) {
+  return ((((size_t(e) * (N / 32) + rb) * size_t(K / 64) + s) * 4 + q) * 64) * 8;
+}
+
+template <int W, int MT, bool RELU, bool PACKED>   // W waves per workgroup, 32 output columns each
 __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                 uint16_t* __restrict__ C, uint16_t* As, uint16_t* Bs, int r0, int r_end, int K,
                                                 int N, int col0, int tid) {
@@ -152,12 +161,14 @@ __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, 
   // weight K step s: load q brings rows 8q + lane / 8 of the wave's 32, 16 bytes each
   // (eight lanes cover one 128-byte line), coalesced; the wave then transposes
   // the step through its own LDS slab into MFMA fragments.
-  const uint16_t* bp = B + size_t(col0 + (lane >> 3)) * K + 8 * (lane & 7);
+  // (PACKED: B is the expert's packed matrix; the wave's run starts at its 32-row block)
+  const uint16_t* bp = PACKED ? B + packed_frag_off(0, col0 / 32, 0, 0, N, K) + lane * 8
+                              : B + size_t(col0 + (lane >> 3)) * K + 8 * (lane & 7);
   const size_t bq = size_t(8) * K;
   auto b_fetch = [&](bf16x8 (&b)[4], int s) {
     s = min(s, nks - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = ld8(bp + q * bq + 64 * s);
+    for (int q = 0; q < 4; ++q) b[q] = PACKED ? ld8(bp + (size_t(s) * 4 + q) * 512) : ld8(bp + q * bq + 64 * s);
   };
   uint16_t* bw = Bs + (tid >> 6) * (32 * kFfnLdB);
   auto b_stage = [&](const bf16x8 (&b)[4]) {   // same-wave LDS accesses stay in order
@@ -172,10 +183,10 @@ __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, 
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
   const uint16_t* arow = As + r32 * kFfnLdA + 32 * h;
   auto step = [&](const bf16x8 (&b)[4], int t) {
-    b_stage(b);
+    if constexpr (!PACKED) b_stage(b);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(brow + 8 * q);
+      const bf16x8 bf = PACKED ? b[q] : *reinterpret_cast<const bf16x8*>(brow + 8 * q);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * mt * kFfnLdA + 64 * t + 8 * q);
@@ -220,7 +231,7 @@ __device__ __forceinline__ void ffn_stream_rows(const uint16_t* __restrict__ A, 
   }
 }
 
-template <int W, bool RELU>
+template <int W, bool RELU, bool PACKED = false>
 __global__ __launch_bounds__(64 * W) void k_grouped_gemm_stream(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
                                                              const int32_t* __restrict__ offsets,
@@ -236,15 +247,40 @@ __global__ __launch_bounds__(64 * W) void k_grouped_gemm_stream(const uint16_t* 
   const int r_begin = min(offsets[e], row_limit), r_end = min(expert_end(offsets, rows, e), row_limit);
   const int wave = threadIdx.x >> 6;
   const int col0 = cb * (32 * W) + wave * 32;
-  const uint16_t* Be = B + size_t(e) * N * K;
+  const uint16_t* Be = B + size_t(e) * N * K;   // plain and packed matrices have the same size
   for (int r0 = r_begin; r0 < r_end; r0 += 128) {
     switch (ceil_div(min(128, r_end - r0), 32)) {
-      case 1: ffn_stream_rows<W, 1, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
-      case 2: ffn_stream_rows<W, 2, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
-      case 3: ffn_stream_rows<W, 3, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
-      default: ffn_stream_rows<W, 4, RELU>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 1: ffn_stream_rows<W, 1, RELU, PACKED>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 2: ffn_stream_rows<W, 2, RELU, PACKED>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      case 3: ffn_stream_rows<W, 3, RELU, PACKED>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
+      default: ffn_stream_rows<W, 4, RELU, PACKED>(A, Be, C, As, Bs, r0, r_end, K, N, col0, threadIdx.x); break;
     }
   }
+}
+
+// Packs [n][N][K] bf16 weights into the fragment order above: one thread per 16-byte fragment
+// slice, in the packed order, so the writes are contiguous.
+__global__ __launch_bounds__(256) void k_pack_weights(const uint16_t* __restrict__ w, uint16_t* __restrict__ p,
+                                                      int64_t n, int N, int K) {
+  const int64_t items = n * N * (K / 8);
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < items; t += int64_t(gridDim.x) * 256) {
+    const int l = int(t & 63), q = int((t >> 6) & 3);
+    const int64_t u = t >> 8;   // (e, rb, s)
+    const int nks = K / 64, nrb = N / 32;
+    const int s = int(u % nks);
+    const int64_t v = u / nks;
+    const int rb = int(v % nrb);
+    const int64_t e = v / nrb;
+    const size_t src = (size_t(e) * N + size_t(rb) * 32 + (l & 31)) * K + size_t(s) * 64 + 32 * (l >> 5) + 8 * q;
+    *reinterpret_cast<u32x4*>(p + size_t(t) * 8) = *reinterpret_cast<const u32x4*>(w + src);
+  }
+}
+
+hipError_t launch_pack_weights(int64_t n, int N, int K, const uint16_t* w, uint16_t* p, hipStream_t s) {
+  const int64_t items = n * N * (K / 8);
+  const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(items, 256), 1 << 20));
+  hipLaunchKernelGGL(k_pack_weights, dim3(blocks), dim3(256), 0, s, w, p, n, N, K);
+  return hipGetLastError();
 }
 
 // the streaming kernel addresses the activations with 32-bit element offsets
@@ -254,28 +290,38 @@ static bool ffn_streams(int K, int N, int row_limit) {
 
 // 8-wave workgroups (256 columns: twice the reuse of each staged row chunk)
 // where N allows, else 4-wave workgroups (128 columns).
-template <bool RELU>
+template <bool RELU, bool PACKED>
 static void launch_stream(int n, int K, int N, int row_limit, const int32_t* offsets, const int32_t* rows,
                           const uint16_t* A, const uint16_t* B, uint16_t* C, hipStream_t s) {
   if (N % 256 == 0)
-    hipLaunchKernelGGL((k_grouped_gemm_stream<8, RELU>), dim3(unsigned(n) * (N / 256)), dim3(512), 0, s, A, B, C,
-                       offsets, rows, n, K, N, row_limit);
+    hipLaunchKernelGGL((k_grouped_gemm_stream<8, RELU, PACKED>), dim3(unsigned(n) * (N / 256)), dim3(512), 0, s, A, B,
+                       C, offsets, rows, n, K, N, row_limit);
   else
-    hipLaunchKernelGGL((k_grouped_gemm_stream<4, RELU>), dim3(unsigned(n) * (N / 128)), dim3(256), 0, s, A, B, C,
-                       offsets, rows, n, K, N, row_limit);
+    hipLaunchKernelGGL((k_grouped_gemm_stream<4, RELU, PACKED>), dim3(unsigned(n) * (N / 128)), dim3(256), 0, s, A, B,
+                       C, offsets, rows, n, K, N, row_limit);
+}
+
+bool ffn_packed_ok(int d, int d_ff, int rows_max, int n) {
+  const int row_limit = int(std::min<int64_t>(int64_t(n) * rows_max, 0x7FFFFFFF));
+  return ffn_streams(d, d_ff, row_limit) && ffn_streams(d_ff, d, row_limit);
 }
 
 hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets, const int32_t* rows,
                              const uint16_t* D, const uint16_t* w1, const uint16_t* w2, uint16_t* hidden, uint16_t* y,
-                             hipStream_t s) {
+                             hipStream_t s, bool packed) {
   const int row_limit = int(std::min<int64_t>(int64_t(n) * rows_max, 0x7FFFFFFF));
+  if (packed) {   // the caller checked ffn_packed_ok
+    launch_stream<true, true>(n, d, d_ff, row_limit, offsets, rows, D, w1, hidden, s);
+    launch_stream<false, true>(n, d_ff, d, row_limit, offsets, rows, hidden, w2, y, s);
+    return hipGetLastError();
+  }
   if (ffn_streams(d, d_ff, row_limit))
-    launch_stream<true>(n, d, d_ff, row_limit, offsets, rows, D, w1, hidden, s);
+    launch_stream<true, false>(n, d, d_ff, row_limit, offsets, rows, D, w1, hidden, s);
   else
     hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(ceil_div(d_ff, 128), n), dim3(256), 0, s, D, w1, hidden, offsets,
                        rows, d, d_ff, row_limit);
   if (ffn_streams(d_ff, d, row_limit))
-    launch_stream<false>(n, d_ff, d, row_limit, offsets, rows, hidden, w2, y, s);
+    launch_stream<false, false>(n, d_ff, d, row_limit, offsets, rows, hidden, w2, y, s);
   else
     hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(ceil_div(d, 128), n), dim3(256), 0, s, hidden, w2, y, offsets,
                        rows, d_ff, d, row_limit);

@@ -138,9 +138,14 @@ bool dispatch_self_prefix_ok(int nch, int n);
 size_t ffn_ws_bytes(int64_t rows_bound, int d_ff);
 // rows (nullable): rows of expert j = rows[j] from offsets[j] (capacity-padded
 // layout); else offsets[j + 1] - offsets[j]
+// packed: w1 and w2 hold moe_expert_weights_pack's layout (only where ffn_packed_ok)
 hipError_t launch_expert_ffn(int n, int d, int d_ff, int rows_max, const int32_t* offsets, const int32_t* rows,
                              const uint16_t* D, const uint16_t* w1, const uint16_t* w2,
-                             uint16_t* hidden, uint16_t* y, hipStream_t s);
+                             uint16_t* hidden, uint16_t* y, hipStream_t s, bool packed = false);
+// whether both GEMMs of the FFN run on the weight-stream kernel, the only one that reads packed weights
+bool ffn_packed_ok(int d, int d_ff, int rows_max, int n);
+// [n][N][K] bf16 weights -> the stream kernel's fragment order (N % 32 == 0, K % 64 == 0)
+hipError_t launch_pack_weights(int64_t n, int N, int K, const uint16_t* w, uint16_t* p, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 // clear (optional): bytes of device memory the first workgroup zeroes (16-byte multiple)

@@ -265,3 +265,34 @@ def test_minibatch_validation(lib):
     assert lib.moe_balance_duals_minibatch(*args(64, 8, 1, 16, wsb=100)) == 3
     assert lib.moe_balance_minibatch_workspace_size(64, 8, 1, 24) == 0
     assert lib.moe_balance_minibatch_workspace_size(64, 8, 1, 16) > lib.moe_balance_workspace_size(64, 8, 1, 0)
+
+
+def test_weights_pack_validation(lib):
+    other = ctypes.c_void_p(0x2000)
+    assert lib.moe_expert_weights_pack(0, 64, 64, FAKE, other, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_weights_pack(2, 64, 64, None, other, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_weights_pack(2, 64, 64, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG       # in place
+    assert lib.moe_expert_weights_pack(2, 64, 64, ctypes.c_void_p(0x1008), other, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_weights_pack(2, 48, 64, FAKE, other, None) == L.MOE_ERR_UNSUPPORTED       # rows % 32
+    assert lib.moe_expert_weights_pack(2, 64, 96, FAKE, other, None) == L.MOE_ERR_UNSUPPORTED       # cols % 64
+
+
+def test_switch_layer_packed_weights_validation(lib):
+    out = L.LayerOutputs()
+    out.out = FAKE
+    sh = _sh(m=64, d=64, n=8, xd=1)
+    p = L.LayerParams(16, 0, 0, 0.01, None)
+    p.weights_packed = 1                                           # identity expert: no weights to pack
+    assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, None, None, None,
+                                ctypes.byref(out), FAKE, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    p = L.LayerParams(16, 1, 64, 0.01, None)
+    p.weights_packed = 1                                           # d = d_ff = 64: not on the stream kernel
+    assert lib.moe_switch_layer(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None,
+                                ctypes.byref(out), FAKE, 1 << 40, None) == L.MOE_ERR_UNSUPPORTED
+    sv = L.LayerSaved(*([FAKE.value] * len(L.LayerSaved._fields_)))
+    gr = L.LayerGrads(*([FAKE.value] * len(L.LayerGrads._fields_)))
+    sh = _sh(m=64, d=256, n=8, xd=1)
+    p = L.LayerParams(16, 1, 256, 0.01, None)
+    p.weights_packed = 1                                           # the backward reads the plain layout
+    assert lib.moe_switch_layer_backward(ctypes.byref(sh), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.byref(sv),
+                                         FAKE, ctypes.byref(gr), FAKE, 1 << 40, None) == L.MOE_ERR_INVALID_ARG

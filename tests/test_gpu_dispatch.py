@@ -162,3 +162,31 @@ def test_expert_ffn_padded_layout():
         ref = OE.relu_ffn(D64[lo:hi], w1[e], w2[e])
         err = row_rel_err(got[lo:hi], ref)
         assert err.max() <= 2e-2, f"expert {e}: worst row error {err.max():.3e}"
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+@pytest.mark.parametrize("T,d,n,k,d_ff,cf", [(8192, 768, 128, 1, 3072, 1.25), (1000, 256, 16, 2, 512, 1.25),
+                                             (300, 512, 8, 1, 256, -1.0)])
+def test_packed_expert_weights_bit_identical(T, d, n, k, d_ff, cf):
+    # the FFN reading moe_expert_weights_pack's layout runs the same products in the same order as
+    # the plain layout: every output of the layer is bit-identical
+    spec = W.SwitchSpec("packed", T=T, d=d, N=n, d_ff=d_ff, w_std=np.sqrt(1.0 / d), w_r_std=0.1 / np.sqrt(d))
+    inp = W.switch_inputs(spec, 5)
+    w1, w2 = W.all_expert_weights(spec, 5)
+    say(f"[ffn packed] T={T} d={d} n={n} k={k} d_ff={d_ff} cf={cf}")
+    x, wr, W1, W2 = to_dev(inp.x), to_dev(inp.w_r), to_dev(w1), to_dev(w2)
+    cap = M.capacity(T, n, cf) if cf > 0 else -1
+    plain = M.switch_layer(x, wr, k=k, capacity=cap, w1=W1, w2=W2)
+    P1, P2 = M.pack_expert_weights(W1), M.pack_expert_weights(W2)
+    packed = M.switch_layer(x, wr, k=k, capacity=cap, w1=P1, w2=P2, weights_packed=True)
+    torch.cuda.synchronize()
+    assert not torch.equal(_bits(P1), _bits(W1))   # the layout did change
+    for f in ("idx", "gate", "token_to_row", "expert_rows", "out"):
+        assert torch.equal(_bits(getattr(plain, f)), _bits(getattr(packed, f))), f
+    rows = plain.token_to_row.reshape(-1)
+    kept = rows[rows >= 0].long()
+    assert torch.equal(_bits(plain.y[kept]), _bits(packed.y[kept]))
+    assert torch.equal(_bits(plain.hidden[kept]), _bits(packed.hidden[kept]))
