@@ -448,7 +448,7 @@ def main():
     ffn_flops = 2 * 2.0 * rows * d * d_ff
     t1 = committed_traffic("ffn1", "switch_base", kernel_source_hash(KERNEL_SOURCES["ffn"]))
     t2 = committed_traffic("ffn2", "switch_base", kernel_source_hash(KERNEL_SOURCES["ffn"]))
-    ffn_roof = {"kernel": "k_grouped_gemm_stream<8, true> + k_grouped_gemm_stream<8, false> (bf16 MFMA grouped GEMMs; k_grouped_gemm where the shapes do not fit the stream kernel)", "bound": "hbm",
+    ffn_roof = {"kernel": "k_grouped_gemm_stream<8, true, false> + k_grouped_gemm_stream<8, false, false> (bf16 MFMA grouped GEMMs on the plain weight layout; k_grouped_gemm where the shapes do not fit the stream kernel)", "bound": "hbm",
                 "achieved": ffn_bytes / t_ffn / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ffn_bytes / t_ffn / 1e9 / HBM_PEAK_GBS,
                 "traffic": (t1 + t2) if (t1 is not None and t2 is not None) else None,
