@@ -57,15 +57,16 @@ __device__ __forceinline__ void store_vec(void* p, int64_t i, const float (&v)[8
 // One wave per token: the token's (row, gate) pairs are wave-uniform, so the
 // expert rows it gathers are addressed right after one scalar load; lanes
 // stream the d/8 16-byte vectors of the row.
+constexpr int kCombineWaves = 16;   // tokens (waves) per workgroup
 template <bool XB, bool YB>
-__global__ __launch_bounds__(256) void k_combine_vec(int64_t m, int d, int k, const void* __restrict__ y,
+__global__ __launch_bounds__(64 * kCombineWaves) void k_combine_vec(int64_t m, int d, int k, const void* __restrict__ y,
                                                      const float* __restrict__ gate,
                                                      const int32_t* __restrict__ t2r, const void* __restrict__ res,
                                                      void* __restrict__ out, u32x4* clear, int clear_vecs) {
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < clear_vecs; i += 256) clear[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < clear_vecs; i += 64 * kCombineWaves) clear[i] = u32x4{0u, 0u, 0u, 0u};
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t t = int64_t(blockIdx.x) * 4 + wave;
+  const int64_t t = int64_t(blockIdx.x) * kCombineWaves + wave;
   if (t >= m) return;
   const int vpr = d / 8;
   for (int v0 = 0; v0 < vpr; v0 += 128) {
@@ -136,18 +137,19 @@ hipError_t launch_combine(int64_t m, int d, int k, const void* y, bool y_bf16, c
   const uintptr_t al = reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(out) |
                        reinterpret_cast<uintptr_t>(residual);
   if (d % 8 == 0 && (al % 16) == 0) {
-    const unsigned blocks = unsigned(ceil_div64(m, 4));
+    const unsigned blocks = unsigned(ceil_div64(m, kCombineWaves));
+    const dim3 tb(64 * kCombineWaves);
     if (x_bf16 && y_bf16)
-      hipLaunchKernelGGL((k_combine_vec<true, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual, out,
+      hipLaunchKernelGGL((k_combine_vec<true, true>), dim3(blocks), tb, 0, s, m, d, k, y, gate, t2r, residual, out,
                          cv, cn);
     else if (x_bf16)
-      hipLaunchKernelGGL((k_combine_vec<true, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual,
+      hipLaunchKernelGGL((k_combine_vec<true, false>), dim3(blocks), tb, 0, s, m, d, k, y, gate, t2r, residual,
                          out, cv, cn);
     else if (y_bf16)
-      hipLaunchKernelGGL((k_combine_vec<false, true>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual,
+      hipLaunchKernelGGL((k_combine_vec<false, true>), dim3(blocks), tb, 0, s, m, d, k, y, gate, t2r, residual,
                          out, cv, cn);
     else
-      hipLaunchKernelGGL((k_combine_vec<false, false>), dim3(blocks), dim3(256), 0, s, m, d, k, y, gate, t2r, residual,
+      hipLaunchKernelGGL((k_combine_vec<false, false>), dim3(blocks), tb, 0, s, m, d, k, y, gate, t2r, residual,
                          out, cv, cn);
   } else {
     const unsigned blocks = unsigned(std::min<int64_t>(ceil_div64(m * d, 256), 65536));
